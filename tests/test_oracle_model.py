@@ -1,0 +1,243 @@
+"""Pins of the oracle's full passes (prefill, denoise step, block generation) — CPU only.
+
+The composition is pinned by (a) an independent dense transformer built from
+torch library routines (F.rms_norm, complex-number RoPE, SDPA with grouped KV,
+F.silu) for the single-expert special case, and (b) invariants that the method's
+masks fix: causal prefix encoding can be split anywhere, sliding-window layers
+forget tokens older than the window, the canvas is bidirectional, committed
+tokens are final and the mask count reaches zero.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import dg_oracle as O
+from discrete_diffusion_block_amd import synth
+
+
+def cfg_small(**kw):
+    base = dict(n_layers=2, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, n_experts=4,
+                top_k=2, expert_ffn=16, shared_ffn=24, vocab=64, canvas=6, window=8)
+    base.update(kw)
+    return synth.ModelConfig(**base)
+
+
+def weights(cfg, seed=0, std=0.2):
+    return O.to_numpy_weights(synth.make_weights(cfg, seed=seed, std=std))
+
+
+# ------------------------------------------------------------------ independent dense reference
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+def _rope_complex(x, pos, theta):
+    # x: [n][H][hd]; pairs (i, i+hd/2) as complex numbers rotated by pos * theta^(-2i/hd)
+    hd = x.shape[-1]
+    z = torch.complex(x[..., :hd // 2], x[..., hd // 2:])
+    freq = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2.0 / hd)
+    rot = torch.polar(torch.ones_like(freq)[None, :].expand(len(pos), -1),
+                      torch.tensor(pos, dtype=torch.float64)[:, None] * freq[None, :])
+    z = z * rot[:, None, :]
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+def _dense_block(x, pos, lw, cfg, prefix_kv, causal):
+    d, hq, hkv, hd = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n = x.shape[0]
+    h = F.rms_norm(x, (d,), _t(lw["attn_norm"]), eps=cfg.rms_eps)
+    qkv = h @ _t(lw["w_qkv"]).T
+    q = _rope_complex(qkv[:, :hq * hd].reshape(n, hq, hd), pos, cfg.rope_theta)
+    k = _rope_complex(qkv[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), pos, cfg.rope_theta)
+    v = qkv[:, (hq + hkv) * hd:].reshape(n, hkv, hd)
+    K = torch.cat([prefix_kv[0], k]) if prefix_kv is not None else k
+    V = torch.cat([prefix_kv[1], v]) if prefix_kv is not None else v
+    if causal:
+        P = K.shape[0] - n
+        mask = torch.ones(n, K.shape[0], dtype=torch.bool).tril(diagonal=P)
+    else:
+        mask = None
+    o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], K.permute(1, 0, 2)[None],
+                                       V.permute(1, 0, 2)[None], attn_mask=mask, enable_gqa=True)
+    x = x + o[0].permute(1, 0, 2).reshape(n, -1) @ _t(lw["w_o"]).T
+    h2 = F.rms_norm(x, (d,), _t(lw["ffn_norm"]), eps=cfg.rms_eps)
+    f, fs = cfg.expert_ffn, cfg.shared_ffn
+    wgu, wd = _t(lw["w_gate_up"][0]), _t(lw["w_down"][0])
+    y = (F.silu(h2 @ wgu[:f].T) * (h2 @ wgu[f:].T)) @ wd.T
+    sgu, sd = _t(lw["ws_gate_up"]), _t(lw["ws_down"])
+    y = y + (F.silu(h2 @ sgu[:fs].T) * (h2 @ sgu[fs:].T)) @ sd.T
+    return x + y, k, v
+
+
+def test_single_expert_model_matches_dense_torch_reference():
+    cfg = cfg_small(n_experts=1, top_k=1, window=64)
+    w = weights(cfg)
+    prompt = np.array([[3, 17, 60, 1, 9]])
+    canvas = np.array([[64, 64, 5, 64, 2, 64]])
+    t = 0.625
+    kv = O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, kv, prompt, rnd=False)
+    logits = O.denoise_step(cfg, w, kv, canvas, t, rnd=False)
+
+    # reference: causal pass over the prompt, then the canvas with temb at positions P..P+C-1
+    P, C = 5, 6
+    x = _t(w["embed"][prompt[0]])
+    cache = []
+    for l in range(cfg.n_layers):
+        x, k, v = _dense_block(x, list(range(P)), w["layers"][l], cfg, None, causal=True)
+        cache.append((k, v))
+    half = cfg.d_model // 2
+    f = 10000.0 ** (-torch.arange(half, dtype=torch.float64) / half)
+    temb = torch.cat([torch.sin(1000 * t * f), torch.cos(1000 * t * f)])
+    x = _t(w["embed"][canvas[0]]) + temb
+    for l in range(cfg.n_layers):
+        x, _, _ = _dense_block(x, list(range(P, P + C)), w["layers"][l], cfg, cache[l], causal=False)
+    hf = F.rms_norm(x, (cfg.d_model,), _t(w["final_norm"]), eps=cfg.rms_eps)
+    ref = hf @ _t(w["embed"][:cfg.vocab]).T
+    np.testing.assert_allclose(logits[0], ref.numpy(), rtol=1e-9, atol=1e-11)
+    for l in range(cfg.n_layers):
+        np.testing.assert_allclose(kv.k[l][0], cache[l][0].numpy(), rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(kv.v[l][0], cache[l][1].numpy(), rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------------------ mask invariants
+
+
+def test_prefill_can_be_split_anywhere():
+    cfg = cfg_small(window=5)
+    w = weights(cfg, seed=1)
+    toks = np.array([[1, 5, 9, 13, 2, 40, 41, 42, 7, 0, 63]])
+    a = O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, a, toks)
+    b = O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, b, toks[:, :4])
+    O.prefill_kv(cfg, w, b, toks[:, 4:7])
+    O.prefill_kv(cfg, w, b, toks[:, 7:])
+    assert a.len == b.len == [11]
+    for l in range(cfg.n_layers):
+        np.testing.assert_allclose(a.k[l][0], b.k[l][0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(a.v[l][0], b.v[l][0], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("global_every", [0, 1])
+def test_sliding_window_forgets_old_tokens(global_every):
+    W = 4
+    cfg = cfg_small(window=W, global_every=global_every)
+    w = weights(cfg, seed=2)
+    toks = np.array([[1, 5, 9, 13, 2, 40, 41, 42, 7, 0]])
+    toks2 = toks.copy(); toks2[0, 0] = 33
+    a = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, a, toks, rnd=False)
+    b = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, b, toks2, rnd=False)
+    # layer-1 keys of position i depend on layer-0 attention over (i-W, i]
+    d = np.abs(a.k[1][0] - b.k[1][0]).reshape(10, -1).max(axis=1)
+    assert np.all(d[:W] > 0)
+    if global_every == 0:
+        assert np.all(d[W:] == 0)
+    else:
+        assert np.all(d[W:] > 0)
+
+
+@pytest.mark.parametrize("global_every", [0, 1])
+def test_denoise_sees_last_window_of_prefix(global_every):
+    W = 4
+    cfg = cfg_small(n_layers=1, window=W, global_every=global_every)
+    w = weights(cfg, seed=3)
+    toks = np.array([[1, 5, 9, 13, 2, 40, 41, 42]])
+    canvas = np.full((1, cfg.canvas), cfg.mask_id)
+    out = []
+    for first in (1, 33):
+        t2 = toks.copy(); t2[0, 0] = first
+        kv = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, kv, t2, rnd=False)
+        out.append(O.denoise_step(cfg, w, kv, canvas, 0.5, rnd=False))
+    # with one layer the canvas reads layer-0 K/V of positions P-W..P-1 only (P = 8 > W)
+    if global_every == 0:
+        assert np.array_equal(out[0], out[1])
+    else:
+        assert not np.array_equal(out[0], out[1])
+
+
+def test_canvas_is_bidirectional_prefix_is_causal():
+    cfg = cfg_small()
+    w = weights(cfg, seed=4)
+    kv = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, kv, np.array([[1, 2, 3]]), rnd=False)
+    c1 = np.full((1, cfg.canvas), cfg.mask_id)
+    c2 = c1.copy(); c2[0, -1] = 7
+    l1 = O.denoise_step(cfg, w, kv, c1, 0.5, rnd=False)
+    l2 = O.denoise_step(cfg, w, kv, c2, 0.5, rnd=False)
+    assert np.all(np.abs(l1[0, 0] - l2[0, 0]) > 0)                 # first position sees the last
+    # causal encoder: changing the last token leaves earlier K/V untouched
+    a = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, a, np.array([[1, 2, 3, 4]]), rnd=False)
+    b = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, b, np.array([[1, 2, 3, 9]]), rnd=False)
+    for l in range(cfg.n_layers):
+        np.testing.assert_array_equal(a.k[l][0][:3], b.k[l][0][:3])
+        assert not np.array_equal(a.k[l][0][3], b.k[l][0][3])
+
+
+def test_denoise_canvas_kv_not_cached():
+    cfg = cfg_small()
+    w = weights(cfg, seed=5)
+    kv = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, kv, np.array([[1, 2, 3]]))
+    before = [x[0].copy() for x in kv.k]
+    O.denoise_step(cfg, w, kv, np.full((1, cfg.canvas), cfg.mask_id), 1.0)
+    assert kv.len == [3]
+    for l in range(cfg.n_layers):
+        np.testing.assert_array_equal(kv.k[l][0], before[l])
+
+
+def test_batch_rows_are_independent():
+    cfg = cfg_small()
+    w = weights(cfg, seed=6)
+    prompts = np.array([[1, 2, 3, 4], [9, 8, 7, 6]])
+    kv = O.KVCache(cfg, 2); O.prefill_kv(cfg, w, kv, prompts)
+    canv = np.array([[64, 3, 64, 64, 64, 64], [64, 64, 64, 10, 64, 64]])
+    both = O.denoise_step(cfg, w, kv, canv, 0.75)
+    kv1 = O.KVCache(cfg, 1); O.prefill_kv(cfg, w, kv1, prompts[1:])
+    one = O.denoise_step(cfg, w, kv1, canv[1:], 0.75)
+    np.testing.assert_array_equal(both[1], one[0])
+
+
+# ------------------------------------------------------------------ block generation
+
+
+def test_generate_block_invariants_tiny_config():
+    cfg = synth.CONFIGS["tiny"]
+    w = O.to_numpy_weights(synth.make_weights(cfg))
+    prompt = synth.make_prompt(cfg, 1, 64).numpy()
+    kv = O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, kv, prompt)
+    rec = []
+    out = O.generate_block(cfg, w, kv, 1, 4, 1.0, append=True, record=rec)
+    prev = rec[0]["canvas_in"]
+    assert np.all(prev == cfg.mask_id)
+    commits = []
+    for r in rec:
+        c_in = r["canvas_in"]
+        keep = prev != cfg.mask_id
+        np.testing.assert_array_equal(c_in[keep], prev[keep])           # committed never change
+        commits.append(len(r["committed"][0]))
+        prev = c_in
+        H = r["H"][0][c_in[0] == cfg.mask_id]
+        assert np.all(H >= 0) and np.all(H <= math.log(cfg.vocab) + 1e-6)
+    # random weights give near-uniform logits (H ~ log V >> gamma): one commit per step,
+    # and the final step commits the remainder
+    assert commits == [1, 1, 1, cfg.canvas - 3]
+    assert np.all(out != cfg.mask_id) and np.all(out < cfg.vocab)
+    assert kv.len == [64 + cfg.canvas]
+
+
+def test_precision_contract_within_logit_tolerance():
+    cfg = synth.CONFIGS["tiny"]
+    w = O.to_numpy_weights(synth.make_weights(cfg))
+    prompt = synth.make_prompt(cfg, 1, 64).numpy()
+    out = []
+    for rnd in (True, False):
+        kv = O.KVCache(cfg, 1)
+        O.prefill_kv(cfg, w, kv, prompt, rnd=rnd)
+        out.append(O.denoise_step(cfg, w, kv, np.full((1, cfg.canvas), cfg.mask_id), 1.0, rnd=rnd))
+    d = np.abs(out[0] - out[1]).max()
+    assert 0 < d < 3e-2

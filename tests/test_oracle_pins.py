@@ -1,0 +1,333 @@
+"""Pins of the oracle against what the pages and the mathematics fix (CPU only).
+
+Every check here compares the oracle with something other than itself: a library
+routine computing the same quantity a different way, a closed form, an invariant,
+brute force on tiny inputs, or a value printed on the pages (tests/golden/).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import dg_oracle as O
+from discrete_diffusion_block_amd import synth
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ bf16 rounding
+
+
+def test_bf16_matches_torch_rne():
+    x = rng(1).standard_normal(100000) * np.exp(rng(2).uniform(-20, 20, 100000))
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(O.bf16(x), ref)
+
+
+def test_bf16_ties_to_even():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even mantissa (1.0)
+    assert O.bf16(1 + 2 ** -8) == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    assert O.bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+    assert O.bf16(-(1 + 3 * 2 ** -8)) == -(1 + 2 ** -6)
+
+
+# ------------------------------------------------------------------ norm, rope, timestep
+
+
+def test_rms_norm_closed_form_and_library():
+    x = rng(3).standard_normal((7, 64)) * 3.0
+    g = 1 + 0.1 * rng(4).standard_normal(64)
+    y = O.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12)
+    ref = F.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_is_complex_rotation():
+    # textbook form: pair (x_i, x_{i+hd/2}) as the complex number x_i + i x_{i+hd/2},
+    # multiplied by exp(i * pos * theta^(-2i/hd))
+    hd, n, H = 16, 5, 3
+    x = rng(5).standard_normal((n, H, hd))
+    pos = np.array([0, 1, 7, 1000, 40000])
+    z = x[..., :hd // 2] + 1j * x[..., hd // 2:]
+    freq = 10000.0 ** (-np.arange(hd // 2) * 2.0 / hd)
+    z = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    ref = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(O.rope(x, pos, 10000.0), ref, rtol=1e-9, atol=1e-9)
+
+
+def test_rope_relative_position_property():
+    hd = 32
+    q = rng(6).standard_normal((1, 1, hd))
+    k = rng(7).standard_normal((1, 1, hd))
+
+    def dot(m, n):
+        return float(np.sum(O.rope(q, np.array([m]), 1e4) * O.rope(k, np.array([n]), 1e4)))
+    assert dot(10, 3) == pytest.approx(dot(1007, 1000), rel=1e-9, abs=1e-9)
+    assert dot(0, 0) == pytest.approx(float(np.sum(q * k)), rel=1e-12)
+    # norm preserved
+    r = O.rope(q, np.array([12345]), 1e4)
+    assert np.linalg.norm(r) == pytest.approx(np.linalg.norm(q), rel=1e-12)
+
+
+def test_timestep_embedding_closed_forms():
+    d = 64
+    e0 = O.timestep_embedding(0.0, d)
+    np.testing.assert_array_equal(e0[:d // 2], 0.0)
+    np.testing.assert_array_equal(e0[d // 2:], 1.0)
+    e = O.timestep_embedding(0.37, d)
+    np.testing.assert_allclose(e[:d // 2] ** 2 + e[d // 2:] ** 2, 1.0, rtol=1e-12)
+    assert e[0] == pytest.approx(math.sin(370.0), rel=1e-12)        # f_0 = 1
+    assert e[d // 2 - 1] == pytest.approx(math.sin(370.0 * 10000 ** (-(d // 2 - 1) / (d // 2))), rel=1e-12)
+
+
+# ------------------------------------------------------------------ attention
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    # q: [nq][Hq][hd] -> torch [1][Hq][nq][hd]; kv heads repeated explicitly
+    grp = q.shape[1] // k.shape[1]
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(np.repeat(k, grp, axis=1)).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(np.repeat(v, grp, axis=1)).permute(1, 0, 2)[None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, is_causal=causal)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_attention_bidirectional_matches_sdpa():
+    r = rng(8)
+    q = r.standard_normal((9, 4, 16)); k = r.standard_normal((9, 2, 16)); v = r.standard_normal((9, 2, 16))
+    out = O.attention(q, k, v, np.ones((9, 9), bool))
+    np.testing.assert_allclose(out, _sdpa(q, k, v), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_causal_matches_sdpa():
+    r = rng(9)
+    q = r.standard_normal((11, 4, 8)); k = r.standard_normal((11, 1, 8)); v = r.standard_normal((11, 1, 8))
+    allowed = np.tril(np.ones((11, 11), bool))
+    np.testing.assert_allclose(O.attention(q, k, v, allowed), _sdpa(q, k, v, causal=True),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_attention_brute_force_enumeration():
+    # explicit enumeration of the allowed pairs with a Python loop (tiny)
+    r = rng(10)
+    q = r.standard_normal((3, 2, 4)); k = r.standard_normal((5, 1, 4)); v = r.standard_normal((5, 1, 4))
+    allowed = np.array([[1, 0, 1, 0, 1], [0, 1, 1, 1, 0], [0, 0, 0, 0, 1]], bool)
+    out = O.attention(q, k, v, allowed)
+    for i in range(3):
+        for h in range(2):
+            ws, acc = 0.0, np.zeros(4)
+            for j in range(5):
+                if allowed[i, j]:
+                    w = math.exp(sum(q[i, h, t] * k[j, 0, t] for t in range(4)) / 2.0)
+                    ws += w
+                    acc += w * v[j, 0]
+            np.testing.assert_allclose(out[i, h], acc / ws, rtol=1e-12)
+
+
+def test_attention_identical_keys_mean_of_values():
+    r = rng(11)
+    q = r.standard_normal((4, 2, 8))
+    k = np.repeat(r.standard_normal((1, 1, 8)), 6, axis=0)
+    v = r.standard_normal((6, 1, 8))
+    out = O.attention(q, k, v, np.ones((4, 6), bool))
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=0)[None], out.shape), rtol=1e-12)
+
+
+# ------------------------------------------------------------------ FFN / router
+
+
+def test_swiglu_matches_torch():
+    r = rng(12)
+    h = r.standard_normal((5, 16)); wg = r.standard_normal((8, 16)); wu = r.standard_normal((8, 16))
+    wd = r.standard_normal((16, 8))
+    th = torch.from_numpy(h)
+    ref = (F.silu(th @ torch.from_numpy(wg).T) * (th @ torch.from_numpy(wu).T)) @ torch.from_numpy(wd).T
+    np.testing.assert_allclose(O.swiglu_ffn(h, wg, wu, wd), ref.numpy(), rtol=1e-12)
+
+
+def test_router_topk_vs_torch_topk_and_ties():
+    r = rng(13).standard_normal((50, 16))
+    ids, w = O.router_topk(r, 4)
+    tv, ti = torch.topk(torch.from_numpy(r), 4, dim=1)               # distinct values: unique order
+    np.testing.assert_array_equal(ids, ti.numpy())
+    np.testing.assert_allclose(w, torch.softmax(tv, dim=1).numpy(), rtol=1e-12)
+    # exact ties: lower expert id first
+    tie = np.array([[0.5, 1.0, 1.0, 0.5, 1.0, -2.0]])
+    ids, w = O.router_topk(tie, 4)
+    np.testing.assert_array_equal(ids[0], [1, 2, 4, 0])
+    # k = E: every expert, weights = the full softmax
+    ids, w = O.router_topk(r[:3], 16)
+    np.testing.assert_allclose(np.take_along_axis(w, np.argsort(ids, axis=1), axis=1),
+                               torch.softmax(torch.from_numpy(r[:3]), dim=1).numpy(), rtol=1e-12)
+
+
+def _tiny_cfg(**kw):
+    base = dict(n_layers=1, d_model=32, n_q_heads=4, n_kv_heads=2, head_dim=8, n_experts=4,
+                top_k=2, expert_ffn=16, shared_ffn=24, vocab=64, canvas=6, window=8)
+    base.update(kw)
+    return synth.ModelConfig(**base)
+
+
+def _np_weights(cfg, seed=0):
+    return O.to_numpy_weights(synth.make_weights(cfg, seed=seed, std=0.2))
+
+
+def test_moe_single_expert_is_dense_swiglu():
+    cfg = _tiny_cfg(n_experts=1, top_k=1)
+    lw = _np_weights(cfg)["layers"][0]
+    h = rng(14).standard_normal((7, 32))
+    y, ids, w, _ = O.moe_ffn(h, lw, cfg)
+    F_, Fs = cfg.expert_ffn, cfg.shared_ffn
+    th = torch.from_numpy(h)
+
+    def dense(wgu, wd, f):
+        wgu = torch.from_numpy(wgu.astype(np.float64)); wd = torch.from_numpy(wd.astype(np.float64))
+        return (F.silu(th @ wgu[:f].T) * (th @ wgu[f:].T)) @ wd.T
+    ref = dense(lw["w_gate_up"][0], lw["w_down"][0], F_) + dense(lw["ws_gate_up"], lw["ws_down"], Fs)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(w, 1.0)
+
+
+def test_moe_brute_force_per_token():
+    cfg = _tiny_cfg()
+    lw = _np_weights(cfg)["layers"][0]
+    h = rng(15).standard_normal((5, 32))
+    y, ids, w, r = O.moe_ffn(h, lw, cfg)
+    F_, Fs = cfg.expert_ffn, cfg.shared_ffn
+    for t in range(5):
+        logits = [float(np.dot(h[t], lw["w_router"][e])) for e in range(cfg.n_experts)]
+        best = sorted(range(cfg.n_experts), key=lambda e: (-logits[e], e))[:2]
+        z = [math.exp(logits[e] - logits[best[0]]) for e in best]
+        acc = np.zeros(32)
+        for e, zz in zip(best, z):
+            g = lw["w_gate_up"][e][:F_] @ h[t]; u = lw["w_gate_up"][e][F_:] @ h[t]
+            a = g / (1 + np.exp(-g)) * u
+            acc += (zz / sum(z)) * (lw["w_down"][e] @ a)
+        g = lw["ws_gate_up"][:Fs] @ h[t]; u = lw["ws_gate_up"][Fs:] @ h[t]
+        acc += lw["ws_down"] @ (g / (1 + np.exp(-g)) * u)
+        np.testing.assert_allclose(y[t], acc, rtol=1e-9, atol=1e-12)
+        assert list(ids[t]) == best
+
+
+# ------------------------------------------------------------------ sampler
+
+
+def test_entropy_vs_library_and_closed_forms():
+    x = rng(16).standard_normal((6, 1000)) * 3
+    H, a = O.entropy_argmax(x)
+    ref = torch.distributions.Categorical(logits=torch.from_numpy(x)).entropy().numpy()
+    np.testing.assert_allclose(H, ref, rtol=1e-10)
+    np.testing.assert_array_equal(a, np.argmax(x, axis=1))
+    # uniform -> log V; huge spike -> ~0
+    V = 262144
+    H, _ = O.entropy_argmax(np.zeros((1, V)))
+    assert H[0] == pytest.approx(math.log(V), rel=1e-12)
+    sp = np.zeros((1, V)); sp[0, 777] = 200.0
+    H, a = O.entropy_argmax(sp)
+    assert 0.0 <= H[0] < 1e-70 and a[0] == 777
+    # bounds on random rows
+    H, _ = O.entropy_argmax(rng(17).standard_normal((4, 5000)) * 4)
+    assert np.all(H >= 0) and np.all(H <= math.log(5000) + 1e-9)
+
+
+def test_argmax_lowest_id_on_exact_ties():
+    x = np.zeros((1, 50)); x[0, [7, 3, 30]] = 5.0
+    _, a = O.entropy_argmax(x)
+    assert a[0] == 3
+
+
+def test_split_vocab_merge_equals_one_pass():
+    # entropy of the full row from per-chunk (max, sum, weighted sum) partials
+    x = rng(18).standard_normal(4096) * 4
+    H, _ = O.entropy_argmax(x[None])
+    M = x.max(); S = 0.0; T = 0.0
+    for c in np.split(x, 8):
+        m = c.max(); e = np.exp(c - m)
+        S += e.sum() * math.exp(m - M); T += (e * (m - c)).sum() * math.exp(m - M) + e.sum() * math.exp(m - M) * (M - m)
+    assert H[0] == pytest.approx(math.log(S) + T / S, rel=1e-12)
+
+
+def test_eb_select_rules():
+    H = np.array([0.5, 0.5, 0.5, 0.5, 0.5, 0.5], np.float32)
+    allpos = list(range(6))
+    assert O.eb_select(H, allpos, 2.0, False) == [0, 1, 2, 3]          # 4 * 0.5 == 2.0 exactly
+    assert O.eb_select(H, allpos, 2.2, False) == [0, 1, 2, 3]
+    assert O.eb_select(H, allpos, 0.3, False) == [0]                   # at least one
+    assert O.eb_select(H, allpos, 0.0, False) == [0]
+    assert O.eb_select(H, allpos, float("inf"), False) == allpos
+    assert O.eb_select(H, allpos, 0.0, True) == allpos
+    assert O.eb_select(H, [], 1.0, False) == []
+    # ordering by (H, pos) over the masked subset only
+    H2 = np.array([3.0, 0.25, 9.0, 0.25, 1.0, 0.0], np.float32)
+    assert O.eb_select(H2, [0, 1, 3, 4], 1.5, False) == [1, 3, 4]
+    assert O.eb_select(H2, [0, 1, 2, 3, 4, 5], 0.4, False) == [5, 1]
+
+
+def test_eb_select_brute_force_maximal_prefix():
+    r = rng(19)
+    for trial in range(200):
+        n = int(r.integers(1, 9))
+        H = (r.integers(0, 6, n) * 0.25).astype(np.float32)              # many exact ties
+        pos = sorted(r.choice(20, n, replace=False).tolist())
+        Hd = np.zeros(20, np.float32); Hd[pos] = H
+        gamma = float(r.integers(0, 10) * 0.25)
+        sel = O.eb_select(Hd, pos, gamma, False)
+        # brute force: among all orderings consistent with (H asc, pos asc) there is one;
+        # the chosen set is its longest prefix with sum <= gamma, at least one element
+        order = [p for _, p in sorted((float(Hd[p]), p) for p in pos)]
+        best = 1
+        for k in range(1, n + 1):
+            if sum(float(Hd[p]) for p in order[:k]) <= gamma:
+                best = max(best, k)
+        assert sel == order[:best]
+
+
+def test_sample_eb_never_revises_committed_tokens():
+    V = 32
+    logits = rng(20).standard_normal((1, 10, V)) * 2
+    canvas = np.array([[5, V, V, 7, V, 1, V, V, 2, V]])
+    new, H, a, n_masked, com = O.sample_eb(logits, canvas, 1e9, False, V)
+    keep = canvas[0] != V
+    np.testing.assert_array_equal(new[0][keep], canvas[0][keep])
+    assert n_masked[0] == 0 and np.all(new[0] < V)
+    assert np.all(np.isnan(H[0][keep])) and np.all(a[0][keep] == -1)
+
+
+# ------------------------------------------------------------------ forward process
+
+
+def test_absorbing_forward_boundaries_and_coupling():
+    x = np.array([10, 20, 30, 40, 50])
+    u = rng(21).uniform(size=5)
+    out0, m0 = O.absorbing_forward(x, 0, 5, u, 1000)
+    np.testing.assert_array_equal(out0, x)                              # t = 0: nothing absorbed
+    outT, mT = O.absorbing_forward(x, 5, 5, u, 1000)
+    np.testing.assert_array_equal(outT, 1000)                           # t = T: all [MASK] (= vocab size)
+    prev = np.zeros(5, bool)
+    for t in range(6):
+        _, m = O.absorbing_forward(x, t, 5, u, 1000)
+        assert np.all(m >= prev)                                         # a masked token never reverts
+        prev = m
+
+
+def test_absorbing_forward_binomial_rate():
+    # count of masked positions ~ Binomial(C, t/T): chi-square over 4000 coupled draws
+    C, T, t = 16, 10, 3
+    counts = np.zeros(C + 1)
+    u_all = synth.make_uniforms(4000 * C, seed=123).numpy().reshape(4000, C)
+    for u in u_all:
+        _, m = O.absorbing_forward(np.zeros(C, int), t, T, u, 99)
+        counts[m.sum()] += 1
+    p = t / T
+    exp = np.array([math.comb(C, k) * p ** k * (1 - p) ** (C - k) for k in range(C + 1)]) * 4000
+    keep = exp > 5
+    chi2 = np.sum((counts[keep] - exp[keep]) ** 2 / exp[keep])
+    assert chi2 < 40.0                                                   # dof ~ 10; p ~ 1e-5 cutoff
