@@ -1,0 +1,78 @@
+// Internal launchers of the engine's kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+// Geometry of one transformer pass: `batch` sequences of `n` tokens each; row
+// m = b * n + i holds token i of sequence b at position len[b] + i.
+struct PassGeom {
+  int batch;
+  int n;
+  int denoise;               // 1: bidirectional canvas over the cached prefix; 0: causal encoder
+  int len[DG_MAX_BATCH];
+};
+
+// KV-cache view of one layer.
+struct KvLayer {
+  uint16_t* k;               // [max_batch][Hkv][max_ctx][hd]
+  uint16_t* vt;              // [max_batch][Hkv][hd][max_ctx]
+  int hkv, hd, max_ctx;
+  int window;                // 0 = global layer
+};
+
+// ---- embed / norm / prep ----
+void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
+                 float* temb, hipStream_t s);
+void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
+                       const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
+                       hipStream_t s);
+void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
+                    hipStream_t s);
+void launch_combine(float* x, const float* Y, const float* wts, const int32_t* inv, int M, int k,
+                    int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
+
+// ---- dense GEMMs ----
+// y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).
+void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,
+                     bool add, hipStream_t s);
+// q/k/v projection with RoPE; q -> q_out [M][Hq][hd], k/v -> cache at the pass positions.
+void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int hq,
+                     const KvLayer& kv, const PassGeom& g, const float2* rope_tab,
+                     uint16_t* q_out, hipStream_t s);
+// shared-expert gate/up projection with fused SwiGLU: a[M][F] = silu(h Wg^T) * (h Wu^T).
+void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,
+                        uint16_t* a, hipStream_t s);
+// tied LM head: logits bf16 [M][N] = h . E[0:N]^T
+void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
+                      int K, hipStream_t s);
+
+// ---- attention ----
+void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,
+                      uint16_t* o, hipStream_t s);
+
+// ---- MoE ----
+void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
+void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
+                  int32_t* perm, int32_t* inv, hipStream_t s);
+void launch_moe_gate_up(const uint16_t* h, const uint16_t* w_gate_up, const int32_t* cnt,
+                        const int32_t* offs, const int32_t* perm, int E, int F, int d,
+                        uint16_t* a, hipStream_t s);
+void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
+                     const int32_t* offs, int E, int F, int d, float* Y, hipStream_t s);
+
+// ---- sampler ----
+constexpr int kSampleChunk = 8192;   // logits per workgroup in the first sampler pass
+void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
+                            float4* part, int* part_arg, hipStream_t s);
+void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
+                      const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
+                      float gamma, int commit_all, float* H_out, int32_t* amax_out,
+                      int32_t* n_masked, hipStream_t s);
+void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,180 @@
+// Flash-style attention over the KV cache for both masks of the method:
+//  * denoise (bidirectional decoder): every canvas query of sequence b sees the
+//    cached keys [lo, len_b) — lo = max(0, len_b - W) on sliding layers, 0 on
+//    global ones — plus all canvas keys [len_b, len_b + n);
+//  * encoder (prefill / append): query at position p sees keys (p - W, p] on
+//    sliding layers, [0, p] on global ones.
+// The projection kernel has already written this pass's keys/values into the
+// cache at positions len_b .., so every key lives in one contiguous range.
+//
+// Work split: a workgroup owns 16 queries of one q head; its 4 waves take
+// interleaved 32-key chunks of the key range (split-KV) and merge their
+// (max, sum, output) partials through LDS in a fixed order.
+//
+// Layout trick: scores are computed transposed, S^T = K . Q^T, with the key
+// rows of each 16-row MFMA block permuted so that a lane ends up holding the
+// scores of 8 consecutive keys (8g .. 8g+7 of the chunk) for its query.  Those
+// 8 probabilities are exactly the lane's B fragment for O^T += V^T . P^T, and
+// V is stored transposed in the cache ([hd][pos]), so the A fragment is one
+// 16-byte load.  Softmax state and output rescaling are lane-local (the lane's
+// output rows all belong to its query); only the chunk max needs two shuffles.
+#include <math.h>
+
+#include "dg_common.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+template <int HD>
+__global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restrict__ q, int hq,
+                                                        KvLayer kv, PassGeom g,
+                                                        uint16_t* __restrict__ o) {
+  constexpr int NC = HD / 32;   // k-steps of the score MFMA
+  constexpr int NB = HD / 16;   // output blocks of 16 hd rows
+  __shared__ float Ol[4][16][HD + 4];
+  __shared__ float ml[4][16][2];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int b = blockIdx.z, head = blockIdx.y;
+  const int i0 = blockIdx.x * 16;
+  const int n = g.n, len = g.len[b];
+  const int kvh = head / (hq / kv.hkv);
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+
+  // query of this lane (clamped for the load; stores are guarded)
+  const int qi = min(i0 + r, n - 1);
+  const size_t qrow = ((size_t)b * n + qi) * hq + head;
+  u32x4 qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) qf[c] = ld16(q + qrow * HD + 32 * c + 8 * gq);
+
+  // key range of this lane's query and of the whole 16-query tile
+  int lo_q, hi_q, lo_t, hi_t;
+  if (g.denoise) {
+    lo_q = kv.window > 0 ? max(0, len - kv.window) : 0;
+    hi_q = len + n;
+    lo_t = lo_q;
+    hi_t = hi_q;
+  } else {
+    const int p = len + qi;
+    lo_q = kv.window > 0 ? max(0, p - kv.window + 1) : 0;
+    hi_q = p + 1;
+    const int pf = len + i0, pl = len + min(i0 + 15, n - 1);
+    lo_t = kv.window > 0 ? max(0, pf - kv.window + 1) : 0;
+    hi_t = pl + 1;
+  }
+  const int kc0 = lo_t & ~31;
+  const int nchunk = (hi_t - kc0 + 31) >> 5;
+
+  const uint16_t* kbase = kv.k + ((size_t)b * kv.hkv + kvh) * (size_t)kv.max_ctx * HD;
+  const uint16_t* vbase = kv.vt + ((size_t)b * kv.hkv + kvh) * (size_t)HD * kv.max_ctx;
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  for (int ch = w; ch < nchunk; ch += 4) {
+    const int kc = kc0 + 32 * ch;
+    // S^T blocks: block bb row rr <-> key kc + 8*(rr>>2) + 4*bb + (rr&3)
+    f32x4 s[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int key = kc + 8 * (r >> 2) + 4 * bb + (r & 3);
+      const uint16_t* kp = kbase + (size_t)key * HD + 8 * gq;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) a = mfma16(ld16(kp + 32 * c), qf[c], a);
+      s[bb] = a;
+    }
+    // lane holds keys kc + 8*gq + e (e = 0..7) for query r
+    float sv[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = kc + 8 * gq + e;
+      const float v = s[e >> 2][e & 3] * scale;
+      sv[e] = (key >= lo_q && key < hi_q) ? v : -INFINITY;
+      cmax = fmaxf(cmax, sv[e]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - m_new);
+      ps += p[e];
+    }
+    l_part = l_part * alpha + ps;
+    m_run = m_new;
+    u32x4 pb;
+    pb.x = pack_bf2(p[0], p[1]);
+    pb.y = pack_bf2(p[2], p[3]);
+    pb.z = pack_bf2(p[4], p[5]);
+    pb.w = pack_bf2(p[6], p[7]);
+#pragma unroll
+    for (int hb = 0; hb < NB; ++hb) {
+      acc[hb] *= alpha;
+      const u32x4 va = ld16(vbase + (size_t)(16 * hb + r) * kv.max_ctx + kc + 8 * gq);
+      acc[hb] = mfma16(va, pb, acc[hb]);
+    }
+  }
+
+  float l_row = l_part + __shfl_xor(l_part, 16, 64);
+  l_row += __shfl_xor(l_row, 32, 64);
+#pragma unroll
+  for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ol[w][r][16 * hb + 4 * gq + e] = acc[hb][e];
+  if (gq == 0) {
+    ml[w][r][0] = m_run;
+    ml[w][r][1] = l_row;
+  }
+  __syncthreads();
+
+  // merge the 4 waves: thread t -> query t/16, hd slice (t%16) * HD/16
+  const int qq = threadIdx.x >> 4;
+  const int d0 = (threadIdx.x & 15) * (HD / 16);
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, ml[ww][qq][0]);
+  float sc[4];
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const float mw = ml[ww][qq][0];
+    sc[ww] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+    L += sc[ww] * ml[ww][qq][1];
+  }
+  const float invL = L > 0.f ? 1.f / L : 0.f;
+  const int iq = i0 + qq;
+  if (iq < n) {
+    uint16_t* dst = o + (((size_t)b * n + iq) * hq + head) * HD + d0;
+#pragma unroll
+    for (int e = 0; e < HD / 16; e += 2) {
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        v0 += sc[ww] * Ol[ww][qq][d0 + e];
+        v1 += sc[ww] * Ol[ww][qq][d0 + e + 1];
+      }
+      *reinterpret_cast<uint32_t*>(dst + e) = pack_bf2(v0 * invL, v1 * invL);
+    }
+  }
+}
+
+void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,
+                      uint16_t* o, hipStream_t s) {
+  dim3 grid((g.n + 15) / 16, hq, g.batch);
+  switch (kv.hd) {
+    case 32: hipLaunchKernelGGL(attention_kernel<32>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
+    case 64: hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
+    default: hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
+  }
+}
+
+}  // namespace dg

@@ -1,0 +1,340 @@
+// Dense bf16 GEMMs on MFMA (v_mfma_f32_16x16x32_bf16), fp32 accumulation.
+//
+// Every product here is y[m][n] = sum_k x[m][k] * w[n][k] with both operands
+// K-contiguous, so a lane's MFMA fragment (8 consecutive k of one row) is a
+// single 16-byte global load and no LDS staging is needed for the operands.
+// Weight rows go to the MFMA "A" side (16 rows per block), tokens to the "B"
+// side (16 tokens per block); a lane then holds 4 consecutive output features
+// of one token, which makes every epilogue a short vector store.
+//
+// dense_gemm: a workgroup of 4 waves owns one (WN x 16) feature x (WM x 16)
+// token tile and splits K between its waves (interleaved 64-wide k steps),
+// then reduces the four partial tiles through LDS in a fixed order.  That puts
+// 4x more loads in flight per tile, which is what batch-1 shapes (M = 256,
+// K = 2816, few tiles) need to hide HBM latency.
+//
+// head_gemm: the tied LM head (N = 262144 rows of the embedding) — workgroup
+// tile 64 features x 256 tokens so the 256-token activation matrix is re-read
+// from L2 only once per 64 vocabulary rows.
+#include "dg_common.h"
+#include "dg_internal.h"
+
+namespace dg {
+
+enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+struct DenseArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  int M, N, K;      // N = weight rows addressable (loads clamp to N-1)
+  int nblk;         // 16-row blocks of the output feature space
+  float* yf;
+  uint16_t* yb;
+  int ldy;
+  int F;            // SwiGLU: gate rows [0,F), up rows [F,2F)
+  int hq, hd;       // QKV
+  KvLayer kv;
+  PassGeom g;
+  const float2* rope;
+  uint16_t* q_out;
+};
+
+// Weight row feeding A-row r of 16-row block `blk`.
+template <int EPI>
+__device__ __forceinline__ int row_of(const DenseArgs& a, int blk, int r) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // block 2t = gate rows of features 16t.., block 2t+1 = the matching up rows
+    return (blk & 1) * a.F + (blk >> 1) * 16 + r;
+  } else if constexpr (EPI == EPI_QKV) {
+    // Within a head, block j covers rotary pairs 8j..8j+7 and their partners
+    // (i, i + hd/2), arranged so that lane group g ends up holding features
+    // {p, p+1, p+hd/2, p+1+hd/2} with p = 8j + 2g: RoPE is then lane-local.
+    const int per = a.hd >> 4;
+    const int head = blk / per, j = blk - head * per;
+    return head * a.hd + 8 * j + 2 * (r >> 2) + (r & 1) + ((r >> 1) & 1) * (a.hd >> 1);
+  } else {
+    return blk * 16 + r;
+  }
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+template <int EPI, int WN>
+__device__ __forceinline__ void epilogue(const DenseArgs& a, int blk0, int m, const f32x4 (&v)[WN],
+                                         int g) {
+  if (m >= a.M) return;
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ADD_F32) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int n0 = (blk0 + i) * 16 + 4 * g;
+      float* dst = a.yf + (size_t)m * a.ldy + n0;
+      if (n0 + 3 < a.N) {
+        f32x4 o = v[i];
+        if constexpr (EPI == EPI_ADD_F32) o += *reinterpret_cast<f32x4*>(dst);
+        *reinterpret_cast<f32x4*>(dst) = o;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (n0 + e < a.N) dst[e] = (EPI == EPI_ADD_F32 ? dst[e] : 0.f) + v[i][e];
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int f0 = (blk0 >> 1) * 16 + 4 * g;
+    u32x2 o;
+    o.x = pack_bf2(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1]);
+    o.y = pack_bf2(silu(v[0][2]) * v[1][2], silu(v[0][3]) * v[1][3]);
+    *reinterpret_cast<u32x2*>(a.yb + (size_t)m * a.ldy + f0) = o;
+  } else {  // EPI_QKV
+    const int hd = a.hd, half = hd >> 1, per = hd >> 4;
+    const int b = m / a.g.n, ii = m - b * a.g.n;
+    const int pos = a.g.len[b] + ii;
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int blk = blk0 + i;
+      if (blk >= a.nblk) continue;
+      const int head = blk / per, j = blk - head * per;
+      const int p = 8 * j + 2 * g;
+      float x0 = v[i][0], x1 = v[i][1], x2 = v[i][2], x3 = v[i][3];
+      if (head < a.hq + a.kv.hkv) {
+        const float2 r0 = a.rope[(size_t)m * half + p], r1 = a.rope[(size_t)m * half + p + 1];
+        const float y0 = x0 * r0.x - x2 * r0.y, y2 = x2 * r0.x + x0 * r0.y;
+        const float y1 = x1 * r1.x - x3 * r1.y, y3 = x3 * r1.x + x1 * r1.y;
+        uint16_t* dst;
+        if (head < a.hq) {
+          dst = a.q_out + ((size_t)m * a.hq + head) * hd;
+        } else {
+          const int kh = head - a.hq;
+          dst = a.kv.k + (((size_t)b * a.kv.hkv + kh) * a.kv.max_ctx + pos) * hd;
+        }
+        *reinterpret_cast<uint32_t*>(dst + p) = pack_bf2(y0, y1);
+        *reinterpret_cast<uint32_t*>(dst + p + half) = pack_bf2(y2, y3);
+      } else {
+        const int vh = head - a.hq - a.kv.hkv;
+        uint16_t* base = a.kv.vt + ((size_t)b * a.kv.hkv + vh) * (size_t)hd * a.kv.max_ctx + pos;
+        const size_t ld = a.kv.max_ctx;
+        base[(size_t)p * ld] = f2bf(x0);
+        base[(size_t)(p + 1) * ld] = f2bf(x1);
+        base[(size_t)(p + half) * ld] = f2bf(x2);
+        base[(size_t)(p + half + 1) * ld] = f2bf(x3);
+      }
+    }
+  }
+}
+
+template <int WN, int WM, int EPI>
+__global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
+  extern __shared__ f32x4 red[];  // [4 waves][WN][WM][64 lanes]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int blk0 = blockIdx.x * WN;
+  const int m0 = blockIdx.y * 16 * WM;
+
+  const uint16_t* wp[WN];
+  const uint16_t* xp[WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const int blk = min(blk0 + i, a.nblk - 1);
+    const int row = min(row_of<EPI>(a, blk, r), a.N - 1);
+    wp[i] = a.w + (size_t)row * a.K + 16 * g;
+  }
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int m = min(m0 + 16 * j + r, a.M - 1);
+    xp[j] = a.x + (size_t)m * a.K + 16 * g;
+  }
+
+  f32x4 acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
+  auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
+    const int k = it * 64;
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      A[i][0] = ld16(wp[i] + k);
+      A[i][1] = ld16(wp[i] + k + 8);
+    }
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      B[j][0] = ld16(xp[j] + k);
+      B[j][1] = ld16(xp[j] + k + 8);
+    }
+  };
+  auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i)
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
+        acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
+      }
+  };
+
+  const int nk = a.K >> 6;
+  int it = w;
+  if (it < nk) load(A0, B0, it);
+  while (it < nk) {
+    const int it1 = it + 4;
+    if (it1 < nk) load(A1, B1, it1);
+    mma(A0, B0);
+    if (it1 >= nk) break;
+    const int it2 = it1 + 4;
+    if (it2 < nk) load(A0, B0, it2);
+    mma(A1, B1);
+    it = it2;
+  }
+
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) red[((w * WN + i) * WM + j) * 64 + lane] = acc[i][j];
+  __syncthreads();
+  for (int j = w; j < WM; j += 4) {
+    f32x4 v[WN];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      f32x4 s = red[((0 * WN + i) * WM + j) * 64 + lane];
+      s += red[((1 * WN + i) * WM + j) * 64 + lane];
+      s += red[((2 * WN + i) * WM + j) * 64 + lane];
+      s += red[((3 * WN + i) * WM + j) * 64 + lane];
+      v[i] = s;
+    }
+    epilogue<EPI, WN>(a, blk0, m0 + 16 * j + r, v, g);
+  }
+}
+
+template <int WN, int WM, int EPI>
+static void run_dense(const DenseArgs& a, hipStream_t s) {
+  dim3 grid((a.nblk + WN - 1) / WN, (a.M + 16 * WM - 1) / (16 * WM));
+  const size_t lds = sizeof(f32x4) * 4 * WN * WM * 64;
+  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI>), grid, dim3(256), lds, s, a);
+}
+
+void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,
+                     bool add, hipStream_t s) {
+  DenseArgs a{};
+  a.x = x; a.w = w; a.M = M; a.N = N; a.K = K;
+  a.nblk = (N + 15) / 16;
+  a.yf = y; a.ldy = N;
+  if (add)
+    run_dense<2, 4, EPI_ADD_F32>(a, s);
+  else
+    run_dense<2, 4, EPI_STORE_F32>(a, s);
+}
+
+void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int hq,
+                     const KvLayer& kv, const PassGeom& g, const float2* rope_tab,
+                     uint16_t* q_out, hipStream_t s) {
+  DenseArgs a{};
+  a.x = h; a.w = w_qkv; a.M = M; a.K = K;
+  a.N = (hq + 2 * kv.hkv) * kv.hd;
+  a.nblk = a.N / 16;
+  a.hq = hq; a.hd = kv.hd; a.kv = kv; a.g = g; a.rope = rope_tab; a.q_out = q_out;
+  run_dense<2, 4, EPI_QKV>(a, s);
+}
+
+void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,
+                        uint16_t* a_out, hipStream_t s) {
+  DenseArgs a{};
+  a.x = h; a.w = w_gate_up; a.M = M; a.K = K; a.N = 2 * F; a.F = F;
+  a.nblk = 2 * (F / 16);
+  a.yb = a_out; a.ldy = F;
+  run_dense<2, 4, EPI_SWIGLU>(a, s);
+}
+
+// ---------------------------------------------------------------- LM head
+
+template <int WN, int WM>
+__global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
+                                                 const uint16_t* __restrict__ w,
+                                                 uint16_t* __restrict__ y, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int wn = wv & 1, wm = wv >> 1;
+  const int n_base = blockIdx.x * 32 * WN + wn * 16 * WN;
+  const int m_base = blockIdx.y * 32 * WM + wm * 16 * WM;
+  const uint16_t* wp[WN];
+  const uint16_t* xp[WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) wp[i] = w + (size_t)min(n_base + 16 * i + r, N - 1) * K + 16 * g;
+#pragma unroll
+  for (int j = 0; j < WM; ++j) xp[j] = x + (size_t)min(m_base + 16 * j + r, M - 1) * K + 16 * g;
+  int jmax = 0;  // token blocks of this wave that hold at least one real row
+#pragma unroll
+  for (int j = 0; j < WM; ++j) jmax += (m_base + 16 * j < M) ? 1 : 0;
+
+  f32x4 acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (jmax == 0) return;
+
+  u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
+  auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
+    const int k = it * 64;
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      A[i][0] = ld16(wp[i] + k);
+      A[i][1] = ld16(wp[i] + k + 8);
+    }
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      if (j < jmax) {
+        B[j][0] = ld16(xp[j] + k);
+        B[j][1] = ld16(xp[j] + k + 8);
+      }
+    }
+  };
+  auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      if (j < jmax) {
+#pragma unroll
+        for (int i = 0; i < WN; ++i) {
+          acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
+          acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
+        }
+      }
+    }
+  };
+  const int nk = K >> 6;
+  load(A0, B0, 0);
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 1 < nk) load(A1, B1, it + 1);
+    mma(A0, B0);
+    if (it + 1 >= nk) break;
+    if (it + 2 < nk) load(A0, B0, it + 2);
+    mma(A1, B1);
+  }
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int m = m_base + 16 * j + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int n0 = n_base + 16 * i + 4 * g;
+      uint16_t* dst = y + (size_t)m * N + n0;
+      if (n0 + 3 < N) {
+        u32x2 o;
+        o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+        o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(dst) = o;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (n0 + e < N) dst[e] = f2bf(acc[i][j][e]);
+      }
+    }
+  }
+}
+
+void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
+                      int K, hipStream_t s) {
+  constexpr int WN = 2, WM = 8;
+  dim3 grid((N + 32 * WN - 1) / (32 * WN), (M + 32 * WM - 1) / (32 * WM));
+  hipLaunchKernelGGL((head_gemm<WN, WM>), grid, dim3(256), 0, s, h, embed, logits, M, N, K);
+}
+
+}  // namespace dg

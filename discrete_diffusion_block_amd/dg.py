@@ -1,0 +1,262 @@
+"""Thin ctypes binding of libdg.so (include/dg.h).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  torch tensors supply device memory and the current HIP stream.
+Functions keep the C names (dg_prefill_kv, dg_denoise_step, dg_sample_eb,
+dg_generate_block, ...) and raise DgError on a non-zero status.  If the
+library has not been built, loading fails loudly — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional
+
+import torch
+
+from .synth import ModelConfig, LAYER_KEYS
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dg.h")
+MAX_BATCH = 64
+
+STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE", -3: "DG_ERR_WORKSPACE",
+          -4: "DG_ERR_KV_CAPACITY", -5: "DG_ERR_HIP", -6: "DG_ERR_UNSUPPORTED"}
+
+
+class DgError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class Config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
+                                         "n_experts", "top_k", "expert_ffn", "shared_ffn", "vocab",
+                                         "canvas", "window", "global_every", "max_batch", "max_ctx")] + \
+              [("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(k, C.c_void_p) for k in LAYER_KEYS]
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights))]
+
+
+class KV(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("len", C.c_int64 * MAX_BATCH)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with discrete_diffusion_block_amd.build")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, f32, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+        sig = {
+            "dg_create": [C.POINTER(Config), C.POINTER(Weights), C.POINTER(vp)],
+            "dg_destroy": [vp],
+            "dg_workspace_size": [vp, i32, C.POINTER(sz)],
+            "dg_kv_size": [C.POINTER(Config), C.POINTER(sz)],
+            "dg_prefill_kv": [vp, C.POINTER(KV), vp, i32, i32, vp, sz, vp],
+            "dg_denoise_step": [vp, C.POINTER(KV), vp, i32, f32, vp, vp, sz, vp],
+            "dg_sample_workspace_size": [i32, i32, i32, C.POINTER(sz)],
+            "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
+            "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
+            "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
+            "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
+            "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = None if name == "dg_destroy" else C.c_int
+        L.dg_status_string.argtypes = [C.c_int]
+        L.dg_status_string.restype = C.c_char_p
+        L.dg_last_error.argtypes = []
+        L.dg_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of every function declared in include/dg.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dg_status|void|const char\*)\s+(dg_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int):
+    if status != 0:
+        raise DgError(status, lib().dg_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def make_config(cfg: ModelConfig, max_batch: int = 1, max_ctx: int = 2048) -> Config:
+    return Config(cfg.n_layers, cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                  cfg.n_experts, cfg.top_k, cfg.expert_ffn, cfg.shared_ffn, cfg.vocab, cfg.canvas,
+                  cfg.window, cfg.global_every, max_batch, max_ctx, cfg.rms_eps, cfg.rope_theta)
+
+
+# ------------------------------------------------------------------ raw C-named wrappers
+
+
+def dg_create(cfg: Config, weights: Weights):
+    ctx = C.c_void_p()
+    _check(lib().dg_create(C.byref(cfg), C.byref(weights), C.byref(ctx)))
+    return ctx
+
+
+def dg_destroy(ctx):
+    lib().dg_destroy(ctx)
+
+
+def dg_workspace_size(ctx, batch: int) -> int:
+    n = C.c_size_t()
+    _check(lib().dg_workspace_size(ctx, batch, C.byref(n)))
+    return n.value
+
+
+def dg_kv_size(cfg: Config) -> int:
+    n = C.c_size_t()
+    _check(lib().dg_kv_size(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def dg_prefill_kv(ctx, kv: KV, tokens: torch.Tensor, ws: torch.Tensor, stream=None):
+    b, n = tokens.shape
+    _check(lib().dg_prefill_kv(ctx, C.byref(kv), _p(tokens), b, n, _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_denoise_step(ctx, kv: KV, canvas: torch.Tensor, t: float, logits: torch.Tensor,
+                    ws: torch.Tensor, stream=None):
+    _check(lib().dg_denoise_step(ctx, C.byref(kv), _p(canvas), canvas.shape[0], float(t), _p(logits),
+                                 _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sample_workspace_size(batch: int, canvas: int, vocab: int) -> int:
+    n = C.c_size_t()
+    _check(lib().dg_sample_workspace_size(batch, canvas, vocab, C.byref(n)))
+    return n.value
+
+
+def dg_sample_eb(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all: bool,
+                 n_masked: torch.Tensor, ws: torch.Tensor, entropy: Optional[torch.Tensor] = None,
+                 argmax: Optional[torch.Tensor] = None, stream=None):
+    b, c, v = logits.shape
+    _check(lib().dg_sample_eb(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
+                              _p(entropy), _p(argmax), _p(n_masked), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_kv: bool,
+                      logits: torch.Tensor, n_masked: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().dg_generate_block(ctx, C.byref(kv), _p(canvas), canvas.shape[0], steps, float(gamma),
+                                   int(bool(append_kv)), _p(logits), _p(n_masked), _p(ws), ws.numel(),
+                                   _stream(stream)))
+
+
+def dg_test_router_topk(r: torch.Tensor, k: int, ids: torch.Tensor, w: torch.Tensor, stream=None):
+    M, E = r.shape
+    _check(lib().dg_test_router_topk(_p(r), M, E, k, _p(ids), _p(w), _stream(stream)))
+
+
+def dg_test_eb_select(entropy: torch.Tensor, argmax: torch.Tensor, canvas: torch.Tensor, vocab: int,
+                      gamma: float, commit_all: bool, n_masked: torch.Tensor, stream=None):
+    b, c = canvas.shape
+    _check(lib().dg_test_eb_select(_p(entropy), _p(argmax), _p(canvas), b, c, vocab, float(gamma),
+                                   int(bool(commit_all)), _p(n_masked), _stream(stream)))
+
+
+def dg_test_gemm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    _check(lib().dg_test_gemm(_p(x), _p(w), _p(y), M, N, K, _stream(stream)))
+
+
+# ------------------------------------------------------------------ convenience engine
+
+
+class Engine:
+    """Owns the ctx, the KV cache and the workspace for one model on one GPU.
+
+    `weights` is the dict produced by synth.make_weights on a CUDA device; the
+    engine keeps a reference so the borrowed device pointers stay valid.
+    """
+
+    def __init__(self, cfg: ModelConfig, weights: dict, max_batch: int = 1, max_ctx: int = 2048,
+                 device: str = "cuda"):
+        self.cfg = cfg
+        self.weights = weights
+        self.ccfg = make_config(cfg, max_batch, max_ctx)
+        n = cfg.n_layers
+        self._layers = (LayerWeights * n)()
+        for l in range(n):
+            lw = weights["layers"][l]
+            for key in LAYER_KEYS:
+                setattr(self._layers[l], key, lw[key].data_ptr())
+        self._w = Weights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
+                          C.cast(self._layers, C.POINTER(LayerWeights)))
+        self.ctx = dg_create(self.ccfg, self._w)
+        kv_bytes = dg_kv_size(self.ccfg)
+        self.k_cache = torch.zeros(kv_bytes // 2, dtype=torch.int16, device=device)
+        self.v_cache = torch.zeros(kv_bytes // 2, dtype=torch.int16, device=device)
+        self.kv = KV(self.k_cache.data_ptr(), self.v_cache.data_ptr())
+        self.max_batch = max_batch
+        self.ws = torch.empty(dg_workspace_size(self.ctx, max_batch), dtype=torch.uint8, device=device)
+
+    def close(self):
+        if self.ctx is not None:
+            dg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def lengths(self):
+        return [int(self.kv.len[b]) for b in range(self.max_batch)]
+
+    def reset(self):
+        for b in range(MAX_BATCH):
+            self.kv.len[b] = 0
+
+    def kv_view(self):
+        """(k, v) as bf16 tensors [L][B][Hkv][max_ctx][hd] and [L][B][Hkv][hd][max_ctx]."""
+        c = self.cfg
+        shp = (c.n_layers, self.max_batch, c.n_kv_heads, self.ccfg.max_ctx, c.head_dim)
+        k = self.k_cache.view(torch.bfloat16).view(shp)
+        v = self.v_cache.view(torch.bfloat16).view(c.n_layers, self.max_batch, c.n_kv_heads,
+                                                    c.head_dim, self.ccfg.max_ctx)
+        return k, v
+
+    def prefill_kv(self, tokens: torch.Tensor, stream=None):
+        dg_prefill_kv(self.ctx, self.kv, tokens, self.ws, stream)
+
+    def denoise_step(self, canvas: torch.Tensor, t: float, logits: torch.Tensor, stream=None):
+        dg_denoise_step(self.ctx, self.kv, canvas, t, logits, self.ws, stream)
+
+    def sample_eb(self, logits, canvas, gamma, commit_all, n_masked, entropy=None, argmax=None,
+                  stream=None):
+        dg_sample_eb(logits, canvas, gamma, commit_all, n_masked, self.ws, entropy, argmax, stream)
+
+    def generate_block(self, canvas, steps, gamma, append_kv, logits, n_masked, stream=None):
+        dg_generate_block(self.ctx, self.kv, canvas, steps, gamma, append_kv, logits, n_masked,
+                          self.ws, stream)

@@ -1,0 +1,181 @@
+/*
+ * dg.h — C ABI of the block-parallel diffusion denoising engine (MI355X / gfx950).
+ *
+ * The engine implements the inference hot path of block diffusion decoding as
+ * described in the DiffusionGemma Technical Report (§3.1 block-AR generation,
+ * §3.2 the denoising framework at inference time, §3.3 the entropy-bounded
+ * sampler) with the architecture listed in "DiffusionGemma 深度解析" (core
+ * architecture parameters: 30 layers, sliding window 1024, canvas 256, vocab
+ * 262K, 128 experts with top-8 routing plus one shared expert, absorbing [MASK]
+ * whose id equals the vocabulary size, timestep embedding on the decoder input).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named d_* are device memory owned by the caller.  bf16 tensors are
+ *    passed as uint16_t (raw bfloat16 bits), row-major, contiguous.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it: it never synchronises the host, never allocates and
+ *    never frees.  Device-side faults surface at the caller's next sync.
+ *  - Arguments and shapes are validated before anything is enqueued; on an
+ *    error nothing is written and the status says why (dg_last_error() gives a
+ *    thread-local detail string).
+ *  - Token ids are int32; [MASK] = vocab.  Canvas tokens that are not [MASK]
+ *    are committed and are never changed by any call.
+ *  - A dg_ctx is immutable after dg_create and may be shared by threads; calls
+ *    that run concurrently need distinct workspaces and KV caches.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_MAX_BATCH 64
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1,   /* NULL pointer, negative size, out-of-range value */
+  DG_ERR_SHAPE = -2,         /* a model dimension the kernels do not support */
+  DG_ERR_WORKSPACE = -3,     /* workspace smaller than dg_workspace_size() */
+  DG_ERR_KV_CAPACITY = -4,   /* the pass would write beyond max_ctx */
+  DG_ERR_HIP = -5,           /* a HIP launch failed (detail in dg_last_error) */
+  DG_ERR_UNSUPPORTED = -6
+} dg_status;
+
+/* Model shapes.  Supported: d_model % 64 == 0, head_dim in {32, 64, 128},
+ * n_q_heads % n_kv_heads == 0, expert_ffn % 64 == 0, shared_ffn % 64 == 0,
+ * n_experts <= 256, top_k <= min(n_experts, 16), canvas <= 1024,
+ * max_ctx % 64 == 0, 1 <= max_batch <= DG_MAX_BATCH. */
+typedef struct dg_config {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, expert_ffn, shared_ffn;
+  int32_t vocab;         /* V; the [MASK] token id is V (embedding has V+1 rows) */
+  int32_t canvas;        /* C, tokens denoised in parallel per sequence */
+  int32_t window;        /* sliding-window length W of non-global layers */
+  int32_t global_every;  /* 0: all layers slide; g > 0: layer l is global iff (l+1) % g == 0 */
+  int32_t max_batch, max_ctx;
+  float rms_eps, rope_theta;
+} dg_config;
+
+/* Weights of one layer (device pointers, borrowed for the ctx's lifetime).
+ * bf16 unless noted; all row-major. */
+typedef struct dg_layer_weights {
+  const float* attn_norm;      /* fp32 [d] RMSNorm gain before attention */
+  const uint16_t* w_qkv;       /* [(Hq + 2 Hkv) * hd][d]: q heads, then k heads, then v heads */
+  const uint16_t* w_o;         /* [d][Hq * hd] */
+  const float* ffn_norm;       /* fp32 [d] RMSNorm gain before the MoE block */
+  const uint16_t* w_router;    /* [E][d] */
+  const uint16_t* w_gate_up;   /* [E][2F][d]: per expert F gate rows, then F up rows */
+  const uint16_t* w_down;      /* [E][d][F] */
+  const uint16_t* ws_gate_up;  /* shared expert [2Fs][d] */
+  const uint16_t* ws_down;     /* shared expert [d][Fs] */
+} dg_layer_weights;
+
+typedef struct dg_weights {
+  const uint16_t* embed;              /* [V+1][d]; tied: logits use rows 0..V-1 */
+  const float* final_norm;            /* fp32 [d] */
+  const dg_layer_weights* layers;     /* HOST array of n_layers entries (copied by dg_create) */
+} dg_weights;
+
+/* KV cache (caller-owned device buffers, zero-filled before first use).
+ *   k: bf16 [n_layers][max_batch][n_kv_heads][max_ctx][head_dim]  (post-RoPE keys)
+ *   v: bf16 [n_layers][max_batch][n_kv_heads][head_dim][max_ctx]  (values, transposed)
+ * len[b] is the host-side count of committed positions of sequence b; the
+ * library advances it when it enqueues a prefill/append, so no device read-back
+ * is ever needed.  Slots len[b] .. len[b]+C-1 also serve as scratch for the
+ * canvas keys/values of a denoising step. */
+typedef struct dg_kv {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t len[DG_MAX_BATCH];
+} dg_kv;
+
+typedef struct dg_ctx dg_ctx;
+
+/* Create an engine for cfg with the given weights (pointers are borrowed; the
+ * dg_layer_weights array itself is copied).  Validates shapes.  Allocates only
+ * the ctx's host-side state. */
+dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out);
+void dg_destroy(dg_ctx* ctx);
+
+/* Bytes of device workspace needed by any call on `batch` sequences. */
+dg_status dg_workspace_size(const dg_ctx* ctx, int batch, size_t* bytes);
+/* Bytes of each of the k and v cache buffers for cfg. */
+dg_status dg_kv_size(const dg_config* cfg, size_t* bytes_each);
+
+const char* dg_status_string(dg_status s);
+const char* dg_last_error(void);
+
+/* Causal encoder pass (DiffusionGemma Technical Report §3.1, context encoding
+ * into the KV cache, eq. 3; and the append of a finished canvas, eq. 4).
+ * d_tokens: int32 [batch][n], ids in [0, V].  Token i of sequence b sits at
+ * position kv->len[b] + i; key j is visible to query i iff j <= i and (global
+ * layer or i - j < W).  Writes K/V of those positions in every layer and
+ * advances kv->len[b] by n.  Long inputs are processed in chunks (causal
+ * encoding splits exactly).  Errors: DG_ERR_KV_CAPACITY if len+n > max_ctx. */
+dg_status dg_prefill_kv(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batch, int n,
+                        void* d_ws, size_t ws_bytes, void* stream);
+
+/* One denoising forward pass of the bidirectional decoder (Technical Report
+ * §3.2 decoder forward pass; "DiffusionGemma 深度解析": timestep embedding).
+ * d_canvas: int32 [batch][C] (committed ids or [MASK]); t in [0, 1] is the
+ * diffusion time whose sinusoidal embedding is added to the canvas inputs.
+ * Canvas query c of sequence b sits at position len[b] + c and sees the last
+ * min(len[b], W) cached keys of a sliding layer (all len[b] of a global layer)
+ * plus all C canvas keys.  Output d_logits: bf16 [batch][C][V].
+ * Errors: DG_ERR_KV_CAPACITY if len[b] + C > max_ctx. */
+dg_status dg_denoise_step(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, int batch,
+                          float t, uint16_t* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Entropy-bounded unmasking (Technical Report §3.3).  For every [MASK] row of
+ * d_logits (bf16 [batch][canvas][vocab]): H = -sum p log p of softmax(row) and
+ * the argmax (lowest id among exact maxima).  Masked positions are ordered by
+ * (H asc, position asc); with S_k the running fp64 sum of H (fp32 values) in
+ * that order, the first k* = max(1, max{k : S_k <= gamma}) positions get their
+ * argmax committed (all of them when commit_all != 0).  Rows that are not
+ * [MASK] are neither read nor written.
+ * Outputs: d_canvas updated in place; d_entropy (fp32 [batch][canvas], NaN on
+ * rows that were not masked) and d_argmax (int32, -1 on such rows) may be NULL;
+ * d_n_masked (int32 [batch]) = masked rows left after the commit.
+ * Workspace: dg_sample_workspace_size().  Needs no ctx. */
+dg_status dg_sample_workspace_size(int batch, int canvas, int vocab, size_t* bytes);
+dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas,
+                       int vocab, float gamma, int commit_all, float* d_entropy,
+                       int32_t* d_argmax, int32_t* d_n_masked, void* d_ws, size_t ws_bytes,
+                       void* stream);
+
+/* Generate one block per sequence (Technical Report §3.1–§3.3): fill d_canvas
+ * (int32 [batch][C]) with [MASK]; for s = 0..steps-1 run dg_denoise_step at
+ * t_s = 1 - s/steps and dg_sample_eb (commit_all on the last step); then, if
+ * append_kv, run the causal append pass over the finished canvas (len += C).
+ * d_logits: bf16 [batch][C][V] scratch owned by the caller.  d_n_masked:
+ * int32 [batch], holds the masked count after the last step (0). */
+dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps,
+                            float gamma, int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
+                            void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---- kernel taps for tests (not part of the stable contract) ---- */
+
+/* Router selection alone: r fp32 [M][E] -> ids int32 [M][k] (by logit desc, id
+ * asc) and weights fp32 [M][k] (softmax over the k selected logits). */
+dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_ids,
+                              float* d_w, void* stream);
+
+/* Entropy-bounded selection alone on given fp32 entropies and argmax ids:
+ * same rule and outputs as dg_sample_eb, with d_entropy and d_argmax as inputs
+ * (read on [MASK] rows only). */
+dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int32_t* d_canvas,
+                            int batch, int canvas, int vocab, float gamma, int commit_all,
+                            int32_t* d_n_masked, void* stream);
+
+/* Plain bf16 GEMM y[M][N] = x[M][K] . w[N][K]^T, fp32 out (K % 64 == 0). */
+dg_status dg_test_gemm(const uint16_t* d_x, const uint16_t* d_w, float* d_y, int M, int N, int K,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,161 @@
+"""GPU parity of single kernels through the C ABI: GEMM, router top-k, entropy-bounded
+selection, and the full sampler on the 256 x 262144 sampler workload."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from discrete_diffusion_block_amd import dg, synth
+from oracle import dg_oracle as O
+from gpu_util import eb_decision_margin, eb_valid, require_gpu, to_np_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4, 64), (37, 100, 128), (256, 4096, 2816), (300, 132, 704),
+                                   (16, 2816, 2112), (1024, 512, 256)])
+def test_gemm_matches_fp64(M, N, K):
+    print(f"gemm M={M} N={N} K={K}", flush=True)
+    x, w = _bf16((M, K), 1), _bf16((N, K), 2, 0.05)
+    y = torch.full((M, N), float("nan"), device="cuda")
+    dg.dg_test_gemm(x.cuda(), w.cuda(), y)
+    torch.cuda.synchronize()
+    xd, wd = to_np_bf16(x), to_np_bf16(w)
+    ref = xd @ wd.T
+    bound = 1.01 * K * 2.0 ** -24 * (np.abs(xd) @ np.abs(wd).T) + 1e-30
+    err = np.abs(y.cpu().numpy() - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+@pytest.mark.parametrize("M,E,k", [(300, 128, 8), (64, 8, 2), (5, 256, 16), (33, 4, 4)])
+def test_router_topk_bit_exact(M, E, k):
+    print(f"topk M={M} E={E} k={k}", flush=True)
+    g = torch.Generator().manual_seed(M * 7 + E)
+    r = torch.randn(M, E, generator=g)
+    r[::3] = torch.round(r[::3] * 4) / 4            # exact ties in every third row
+    r[1] = 0.0                                       # a row of all-equal logits
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(M, k, device="cuda")
+    dg.dg_test_router_topk(r.cuda(), k, ids, w)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = O.router_topk(r.double().numpy(), k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+def _eb_case(batch, C, seed, quant=0.25, pmask=0.6):
+    g = torch.Generator().manual_seed(seed)
+    H = (torch.randint(0, 12, (batch, C), generator=g).float() * quant)
+    H += (torch.rand(batch, C, generator=g) < 0.3).float() * torch.rand(batch, C, generator=g)
+    amax = torch.randint(0, 1000, (batch, C), generator=g, dtype=torch.int32)
+    canvas = torch.randint(0, 1000, (batch, C), generator=g, dtype=torch.int32)
+    canvas[torch.rand(batch, C, generator=g) < pmask] = 1000
+    return H, amax, canvas
+
+
+@pytest.mark.parametrize("batch,C,gamma,commit_all,pmask", [
+    (3, 256, 2.0, False, 0.6), (1, 256, 0.0, False, 0.6), (2, 64, 1.5, False, 1.0),
+    (1, 1024, 7.25, False, 0.5), (1, 1, 0.5, False, 1.0), (2, 100, float("inf"), False, 0.7),
+    (2, 256, 0.5, True, 0.6), (1, 256, 3.0, False, 0.0)])
+def test_eb_select_bit_exact(batch, C, gamma, commit_all, pmask):
+    print(f"eb_select batch={batch} C={C} gamma={gamma} all={commit_all}", flush=True)
+    H, amax, canvas = _eb_case(batch, C, seed=C + batch, pmask=pmask)
+    d_canvas = canvas.cuda()
+    nm = torch.empty(batch, dtype=torch.int32, device="cuda")
+    dg.dg_test_eb_select(H.cuda(), amax.cuda(), d_canvas, 1000, gamma, commit_all, nm)
+    torch.cuda.synchronize()
+    out = d_canvas.cpu().numpy()
+    for b in range(batch):
+        masked = [i for i in range(C) if canvas[b, i] == 1000]
+        sel = O.eb_select(H[b].numpy(), masked, gamma, commit_all)
+        ref = canvas[b].numpy().copy()
+        ref[sel] = amax[b].numpy()[sel]
+        np.testing.assert_array_equal(out[b], ref)
+        assert nm[b].item() == len(masked) - len(sel)
+
+
+def test_eb_select_gamma_exactly_on_running_sum():
+    # entropies 0.5 each: S_4 == 2.0 exactly, so gamma = 2.0 commits 4 and 1.9999999 commits 3
+    C = 16
+    H = torch.full((1, C), 0.5)
+    amax = torch.arange(C, dtype=torch.int32).view(1, C) + 7
+    for gamma, want in ((2.0, 4), (1.9999999, 3), (0.49, 1)):
+        canvas = torch.full((1, C), 50, dtype=torch.int32).cuda()
+        nm = torch.empty(1, dtype=torch.int32, device="cuda")
+        dg.dg_test_eb_select(H.cuda(), amax.cuda(), canvas, 50, gamma, False, nm)
+        torch.cuda.synchronize()
+        c = canvas.cpu().numpy()[0]
+        assert list(c[:want]) == list(range(7, 7 + want)) and np.all(c[want:] == 50)
+        assert nm.item() == C - want
+
+
+def _sampler_inputs():
+    V, C = 262144, 256
+    logits = synth.make_sampler_logits(C, V)                     # N(0, 4^2) + 12 spike on 60% rows
+    canvas = synth.make_masked_canvas(C, V, 128)
+    # a second sequence exercising multi-commit, exact ties and near-zero entropies
+    l2 = synth.make_sampler_logits(C, V, seed=5)
+    l2f = l2.float()
+    g = torch.Generator().manual_seed(9)
+    sharp = torch.randperm(C, generator=g)[:40]
+    ids = torch.randint(0, V, (40,), generator=g)
+    l2f[sharp, ids] += 40.0                                       # H ~ 0
+    l2f[sharp[30:40]] = l2f[sharp[20:30]].clone()                 # 10 duplicated rows: exact ties
+    l2 = l2f.to(torch.bfloat16)
+    c2 = synth.make_masked_canvas(C, V, 200, seed=11)
+    c2[sharp] = V
+    return torch.stack([logits, l2]), torch.stack([canvas, c2])
+
+
+@pytest.mark.parametrize("gamma", [0.5, 2.0])
+def test_sampler_full_size_vs_oracle(gamma):
+    print(f"sampler 2x256x262144 gamma={gamma}", flush=True)
+    logits, canvas = _sampler_inputs()
+    B, C, V = logits.shape
+    d_canvas = canvas.cuda()
+    H = torch.empty(B, C, device="cuda")
+    am = torch.empty(B, C, dtype=torch.int32, device="cuda")
+    nm = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dg.dg_sample_workspace_size(B, C, V), dtype=torch.uint8, device="cuda")
+    dg.dg_sample_eb(logits.cuda(), d_canvas, gamma, False, nm, ws, H, am)
+    torch.cuda.synchronize()
+    ref_canvas, ref_H, ref_a, ref_nm, ref_sel = O.sample_eb(logits.double().numpy(), canvas.numpy(),
+                                                            gamma, False, V)
+    Hg = H.cpu().numpy()
+    ag = am.cpu().numpy()
+    out = d_canvas.cpu().numpy()
+    eps = 2e-5                       # fp32 entropy error bound (log V ~ 12.5, 262144 terms)
+    for b in range(B):
+        masked = [i for i in range(C) if canvas[b, i] == V]
+        # argmax: bit-exact (identical bf16 inputs; lowest id on ties)
+        np.testing.assert_array_equal(ag[b][masked], ref_a[b][masked])
+        assert np.all(ag[b][[i for i in range(C) if i not in masked]] == -1)
+        # entropy within the bound, and within [0, log V]
+        Hm = Hg[b][masked].astype(np.float64)
+        Ho, _ = O.entropy_argmax(logits[b, masked].double().numpy())
+        assert np.max(np.abs(Hm - Ho)) <= eps
+        assert np.all(Hm >= 0) and np.all(Hm <= math.log(V) + 1e-5)
+        # committed set: identical where the oracle's decision is certified, else valid
+        Hfull = np.full(C, np.nan)
+        Hfull[masked] = Ho
+        committed = [i for i in masked if out[b, i] != V]
+        if eb_decision_margin(Hfull, masked, gamma, False, eps):
+            np.testing.assert_array_equal(out[b], ref_canvas[b])
+            assert nm[b].item() == ref_nm[b]
+        else:
+            assert eb_valid(Hg[b], masked, committed, gamma, False)
+        # committed tokens never change
+        keep = canvas[b].numpy() != V
+        assert np.array_equal(out[b][keep], canvas[b].numpy()[keep])
+    assert len([i for i in range(C) if out[1, i] != V and canvas[1, i] == V]) >= 40
