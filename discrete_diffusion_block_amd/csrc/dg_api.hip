@@ -58,6 +58,8 @@ struct Ws {
   int32_t* offs;
   int32_t* perm;
   int32_t* inv;
+  int2* items;
+  int32_t* n_items;
   uint16_t* A;
   float* Y;
   uint16_t* As;
@@ -103,6 +105,8 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->offs = cv.take<int32_t>(c.n_experts + 1);
   ws->perm = cv.take<int32_t>(M * c.top_k);
   ws->inv = cv.take<int32_t>(M * c.top_k);
+  ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
+  ws->n_items = cv.take<int32_t>(1);
   ws->A = cv.take<uint16_t>(M * c.top_k * c.expert_ffn);
   ws->Y = cv.take<float>(M * c.top_k * c.d_model);
   ws->As = cv.take<uint16_t>(M * c.shared_ffn);
@@ -176,9 +180,12 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s);
     launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s);
     launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s);
-    launch_route(ws.ids, M, k, E, ws.cnt, ws.offs, ws.perm, ws.inv, s);
-    launch_moe_gate_up(ws.h, L.w_gate_up, ws.cnt, ws.offs, ws.perm, E, c.expert_ffn, d, ws.A, s);
-    launch_moe_down(ws.A, L.w_down, ws.cnt, ws.offs, E, c.expert_ffn, d, ws.Y, s);
+    launch_route(ws.ids, M, k, E, ws.cnt, ws.offs, ws.perm, ws.inv, ws.items, ws.n_items, s);
+    const int max_items = moe_max_items(M, k, E);
+    launch_moe_gate_up(ws.h, L.w_gate_up, ws.cnt, ws.offs, ws.perm, ws.items, ws.n_items, max_items,
+                       c.expert_ffn, d, ws.A, s);
+    launch_moe_down(ws.A, L.w_down, ws.cnt, ws.offs, ws.items, ws.n_items, max_items, c.expert_ffn, d,
+                    ws.Y, s);
     launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s);
     launch_gemm_f32(ws.As, L.ws_down, ws.x, M, d, c.shared_ffn, /*add=*/true, s);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);

@@ -40,6 +40,86 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
 
+// Two-stage software pipeline over n steps with no branch in the steady state:
+// load_a(i)/load_b(i) fill register set A/B with step i, mma_a()/mma_b() consume
+// them.  Keeping the loop body branch-free lets the compiler wait only for the
+// set it is about to use (vmcnt > 0) while the other set's loads stay in flight.
+template <class LA, class LB, class MA, class MB>
+__device__ __forceinline__ void pipeline2(int n, LA load_a, LB load_b, MA mma_a, MB mma_b) {
+  // sched_barrier(0) keeps the scheduler from sinking a prefetch below the MFMAs
+  // that wait on the other set, which would leave only one set in flight.
+  if (n <= 0) return;
+  load_a(0);
+  int s = 0;
+  for (; s + 2 < n; s += 2) {
+    load_b(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_a();
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_b();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (s + 1 < n) {
+    load_b(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_a();
+    mma_b();
+  } else {
+    mma_a();
+  }
+}
+
+// Three-stage variant: two register sets are in flight while the third is
+// consumed.  Steady state (no branches) covers steps s..s+2 per trip; the
+// tail handles the last 1..4 steps.
+template <class L0, class L1, class L2, class M0, class M1, class M2>
+__device__ __forceinline__ void pipeline3(int n, L0 l0, L1 l1, L2 l2, M0 m0, M1 m1, M2 m2) {
+  if (n <= 0) return;
+  l0(0);
+  if (n > 1) l1(1);
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s + 4 < n; s += 3) {
+    l2(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    m0();
+    __builtin_amdgcn_sched_barrier(0);
+    l0(s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    m1();
+    __builtin_amdgcn_sched_barrier(0);
+    l1(s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    m2();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int r = n - s;
+  if (r >= 3) l2(s + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  m0();
+  if (r == 4) l0(s + 3);
+  __builtin_amdgcn_sched_barrier(0);
+  if (r >= 2) m1();
+  if (r >= 3) m2();
+  if (r == 4) m0();
+}
+
+// 16-byte load that bypasses cache retention (weights are streamed exactly once).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Workgroups are dispatched round-robin over the XCDs (8 on MI355X), each with
+// its own L2.  xcd_swizzle(b, n) renumbers a 1-D grid of n blocks (n a multiple
+// of kXcd) so that consecutive logical indices run on the same XCD: blocks that
+// share data should be given consecutive logical indices.
+constexpr int kXcd = 8;
+__device__ __forceinline__ int xcd_swizzle(int b, int n) {
+  return (b % kXcd) * (n / kXcd) + b / kXcd;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -134,12 +134,12 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
   for (int i = 0; i < WN; ++i) {
     const int blk = min(blk0 + i, a.nblk - 1);
     const int row = min(row_of<EPI>(a, blk, r), a.N - 1);
-    wp[i] = a.w + (size_t)row * a.K + 16 * g;
+    wp[i] = a.w + (size_t)row * a.K + 8 * g;
   }
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const int m = min(m0 + 16 * j + r, a.M - 1);
-    xp[j] = a.x + (size_t)m * a.K + 16 * g;
+    xp[j] = a.x + (size_t)m * a.K + 8 * g;
   }
 
   f32x4 acc[WN][WM];
@@ -148,18 +148,18 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
+  u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2], A2[WN][2], B2[WM][2];
   auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
     const int k = it * 64;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       A[i][0] = ld16(wp[i] + k);
-      A[i][1] = ld16(wp[i] + k + 8);
+      A[i][1] = ld16(wp[i] + k + 32);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
       B[j][0] = ld16(xp[j] + k);
-      B[j][1] = ld16(xp[j] + k + 8);
+      B[j][1] = ld16(xp[j] + k + 32);
     }
   };
   auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
@@ -172,19 +172,12 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
       }
   };
 
+  // wave w takes the 64-wide k steps w, w+4, w+8, ...
   const int nk = a.K >> 6;
-  int it = w;
-  if (it < nk) load(A0, B0, it);
-  while (it < nk) {
-    const int it1 = it + 4;
-    if (it1 < nk) load(A1, B1, it1);
-    mma(A0, B0);
-    if (it1 >= nk) break;
-    const int it2 = it1 + 4;
-    if (it2 < nk) load(A0, B0, it2);
-    mma(A1, B1);
-    it = it2;
-  }
+  const int nw = w < nk ? (nk - w + 3) >> 2 : 0;
+  pipeline3(nw, [&](int s) { load(A0, B0, w + 4 * s); }, [&](int s) { load(A1, B1, w + 4 * s); },
+            [&](int s) { load(A2, B2, w + 4 * s); }, [&] { mma(A0, B0); }, [&] { mma(A1, B1); },
+            [&] { mma(A2, B2); });
 
 #pragma unroll
   for (int i = 0; i < WN; ++i)
@@ -258,57 +251,44 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
   const uint16_t* wp[WN];
   const uint16_t* xp[WM];
 #pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = w + (size_t)min(n_base + 16 * i + r, N - 1) * K + 16 * g;
+  for (int i = 0; i < WN; ++i) wp[i] = w + (size_t)min(n_base + 16 * i + r, N - 1) * K + 8 * g;
 #pragma unroll
-  for (int j = 0; j < WM; ++j) xp[j] = x + (size_t)min(m_base + 16 * j + r, M - 1) * K + 16 * g;
-  int jmax = 0;  // token blocks of this wave that hold at least one real row
-#pragma unroll
-  for (int j = 0; j < WM; ++j) jmax += (m_base + 16 * j < M) ? 1 : 0;
+  for (int j = 0; j < WM; ++j) xp[j] = x + (size_t)min(m_base + 16 * j + r, M - 1) * K + 8 * g;
 
   f32x4 acc[WN][WM];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (jmax == 0) return;
+  if (m_base >= M) return;
 
+  // all token blocks of a workgroup tile are loaded (rows past M are clamped duplicates)
+  // so the k loop stays branch-free
   u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
   auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
     const int k = it * 64;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      A[i][0] = ld16(wp[i] + k);
-      A[i][1] = ld16(wp[i] + k + 8);
+      A[i][0] = ld16_stream(wp[i] + k);
+      A[i][1] = ld16_stream(wp[i] + k + 32);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
-      if (j < jmax) {
-        B[j][0] = ld16(xp[j] + k);
-        B[j][1] = ld16(xp[j] + k + 8);
-      }
+      B[j][0] = ld16(xp[j] + k);
+      B[j][1] = ld16(xp[j] + k + 32);
     }
   };
   auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
 #pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      if (j < jmax) {
+    for (int j = 0; j < WM; ++j)
 #pragma unroll
-        for (int i = 0; i < WN; ++i) {
-          acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
-          acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
-        }
+      for (int i = 0; i < WN; ++i) {
+        acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
+        acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
       }
-    }
   };
-  const int nk = K >> 6;
-  load(A0, B0, 0);
-  for (int it = 0; it < nk; it += 2) {
-    if (it + 1 < nk) load(A1, B1, it + 1);
-    mma(A0, B0);
-    if (it + 1 >= nk) break;
-    if (it + 2 < nk) load(A0, B0, it + 2);
-    mma(A1, B1);
-  }
+  pipeline2(K >> 6, [&](int it) { load(A0, B0, it); }, [&](int it) { load(A1, B1, it); },
+            [&] { mma(A0, B0); }, [&] { mma(A1, B1); });
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const int m = m_base + 16 * j + r;

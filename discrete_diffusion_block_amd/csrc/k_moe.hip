@@ -84,7 +84,9 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int E, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ offs,
                                                      int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ inv) {
+                                                     int32_t* __restrict__ inv,
+                                                     int2* __restrict__ items,
+                                                     int32_t* __restrict__ n_items) {
   __shared__ int hist[256];
   __shared__ int base[256];
   __shared__ int wcnt[16][256];
@@ -94,14 +96,17 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
   for (int a = tid; a < A; a += blockDim.x) atomicAdd(&hist[ids[a]], 1);
   __syncthreads();
   if (tid == 0) {
-    int run = 0;
+    int run = 0, ni = 0;
     for (int e = 0; e < E; ++e) {
       base[e] = run;
       offs[e] = run;
       cnt[e] = hist[e];
       run += hist[e];
+      // work items of the grouped GEMMs: (expert, first slot) per kMoeGroup-token group
+      for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[ni++] = make_int2(e, t0);
     }
     offs[E] = run;
+    *n_items = ni;
   }
   __syncthreads();
   for (int start = 0; start < A; start += blockDim.x) {
@@ -137,183 +142,224 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
-                  int32_t* perm, int32_t* inv, hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, cnt, offs, perm, inv);
+                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, cnt, offs, perm, inv,
+                     items, n_items);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
+// Grouped expert GEMMs.  A workgroup owns one work item (expert e, group of up
+// to 32 of its tokens) and one tile of 16 output features; its 4 waves split
+// the K loop (interleaved 64-wide steps) and reduce through LDS.  Splitting K
+// keeps every wave's dependent chain short, so the kernel stays bandwidth-bound
+// both when tokens spread over all experts (~16 each) and when a uniform canvas
+// sends every token to the same few experts (many groups per expert, whose
+// workgroups then share the expert's weight tiles through L2).
+//
+// Lane group g reads bytes [64q + 16g, +16) of each 128-byte step q, so the 4
+// lanes of a row read 64 contiguous bytes per instruction.
+
+// gate/up: ag = x W_g^T, au = x W_u^T over this wave's k steps.
+template <int NT>
+__device__ __forceinline__ void gate_up_partial(const uint16_t* wg, const uint16_t* wu,
+                                                const uint16_t* const (&xp)[NT], int nk, int w,
+                                                f32x4 (&ag)[NT], f32x4 (&au)[NT]) {
+  u32x4 Ga[2], Ua[2], Xa[NT][2], Gb[2], Ub[2], Xb[NT][2], Gc[2], Uc[2], Xc[NT][2];
+  auto ld = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2], int step) {
+    const int k = (w + 4 * step) * 64;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      G[q] = ld16_stream(wg + k + 32 * q);
+      U[q] = ld16_stream(wu + k + 32 * q);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 32 * q);
+  };
+  auto mm = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        ag[j] = mfma16(G[q], X[j][q], ag[j]);
+        au[j] = mfma16(U[q], X[j][q], au[j]);
+      }
+  };
+  const int n = w < nk ? (nk - w + 3) >> 2 : 0;
+  pipeline3(n, [&](int t) { ld(Ga, Ua, Xa, t); }, [&](int t) { ld(Gb, Ub, Xb, t); },
+            [&](int t) { ld(Gc, Uc, Xc, t); }, [&] { mm(Ga, Ua, Xa); }, [&] { mm(Gb, Ub, Xb); },
+            [&] { mm(Gc, Uc, Xc); });
+}
+
+template <int NT>
+__device__ __forceinline__ void gate_up_item(const uint16_t* wg, const uint16_t* wu,
+                                             const uint16_t* h, const int32_t* perm, int off,
+                                             int t0, int ne, int F, int fb, int d, int lane,
+                                             int w, uint16_t* A, f32x4 (*red)[2][2][64]) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* xp[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) xp[j] = h + (size_t)perm[off + min(t0 + 16 * j + r, ne - 1)] * d + 8 * g;
+  f32x4 ag[NT], au[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gate_up_partial<NT>(wg, wu, xp, d >> 6, w, ag, au);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    red[w][0][j][lane] = ag[j];
+    red[w][1][j][lane] = au[j];
+  }
+  __syncthreads();
+  if (w < NT) {
+    const int j = w;
+    const f32x4 G = red[0][0][j][lane] + red[1][0][j][lane] + red[2][0][j][lane] + red[3][0][j][lane];
+    const f32x4 U = red[0][1][j][lane] + red[1][1][j][lane] + red[2][1][j][lane] + red[3][1][j][lane];
+    const int t = t0 + 16 * j + r;
+    if (t < ne) {
+      u32x2 o;
+      o.x = pack_bf2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
+      o.y = pack_bf2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
+      *reinterpret_cast<u32x2*>(A + (size_t)(off + t) * F + fb * 16 + 4 * g) = o;
+    }
+  }
+}
+
 // A[slot][f] = silu(x W_g[e][f]^T) * (x W_u[e][f]^T) for every slot of expert e,
-// x = h[perm[slot]].  Wave = (expert, 16 features); TT token tiles per pass.
-template <int TT>
+// x = h[perm[slot]].  Workgroup = (work item, 16 features); items vary fastest.
 __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ wgu,
                                                           const int32_t* __restrict__ cnt,
                                                           const int32_t* __restrict__ offs,
-                                                          const int32_t* __restrict__ perm, int E,
-                                                          int F, int d, uint16_t* __restrict__ A) {
-  const int lane = threadIdx.x & 63;
+                                                          const int32_t* __restrict__ perm,
+                                                          const int2* __restrict__ items,
+                                                          const int32_t* __restrict__ n_items,
+                                                          int max_items, int F, int d,
+                                                          uint16_t* __restrict__ A) {
+  __shared__ f32x4 red[4][2][2][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int nfb = F >> 4;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int e = wid / nfb, fb = wid - e * nfb;
-  if (e >= E) return;
-  const int ne = cnt[e];
-  if (ne == 0) return;
-  const int off = offs[e];
-  const uint16_t* wg = wgu + ((size_t)e * 2 * F + fb * 16 + r) * d + 16 * g;
+  // logical block = fb * max_items + item (items fastest), spread so that the
+  // groups of one expert -- which read the same weight tile -- share an XCD
+  const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int fb = lb / max_items, item = lb - fb * max_items;
+  if (fb >= (F >> 4) || item >= *n_items) return;    // uniform over the workgroup
+  const int2 it = items[item];
+  const int e = it.x, t0 = it.y;
+  const int ne = cnt[e], off = offs[e];
+  const uint16_t* wg = wgu + ((size_t)e * 2 * F + fb * 16 + r) * d + 8 * g;
   const uint16_t* wu = wg + (size_t)F * d;
-  const int nk = d >> 6;
-
-  for (int t0 = 0; t0 < ne; t0 += 16 * TT) {
-    const int nt = min(TT, (ne - t0 + 15) >> 4);
-    const uint16_t* xp[TT];
-#pragma unroll
-    for (int j = 0; j < TT; ++j) {
-      const int t = min(t0 + 16 * j + r, ne - 1);
-      xp[j] = h + (size_t)perm[off + t] * d + 16 * g;
-    }
-    f32x4 ag[TT], au[TT];
-#pragma unroll
-    for (int j = 0; j < TT; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 G0[2], U0[2], X0[TT][2], G1[2], U1[2], X1[TT][2];
-    auto load = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[TT][2], int it) {
-      const int k = it * 64;
-      G[0] = ld16(wg + k);
-      G[1] = ld16(wg + k + 8);
-      U[0] = ld16(wu + k);
-      U[1] = ld16(wu + k + 8);
-#pragma unroll
-      for (int j = 0; j < TT; ++j)
-        if (j < nt) {
-          X[j][0] = ld16(xp[j] + k);
-          X[j][1] = ld16(xp[j] + k + 8);
-        }
-    };
-    auto mma = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[TT][2]) {
-#pragma unroll
-      for (int j = 0; j < TT; ++j)
-        if (j < nt) {
-          ag[j] = mfma16(G[0], X[j][0], ag[j]);
-          ag[j] = mfma16(G[1], X[j][1], ag[j]);
-          au[j] = mfma16(U[0], X[j][0], au[j]);
-          au[j] = mfma16(U[1], X[j][1], au[j]);
-        }
-    };
-    load(G0, U0, X0, 0);
-    for (int it = 0; it < nk; it += 2) {
-      if (it + 1 < nk) load(G1, U1, X1, it + 1);
-      mma(G0, U0, X0);
-      if (it + 1 >= nk) break;
-      if (it + 2 < nk) load(G0, U0, X0, it + 2);
-      mma(G1, U1, X1);
-    }
-#pragma unroll
-    for (int j = 0; j < TT; ++j) {
-      const int t = t0 + 16 * j + r;
-      if (j < nt && t < ne) {
-        u32x2 o;
-        o.x = pack_bf2(silu_f(ag[j][0]) * au[j][0], silu_f(ag[j][1]) * au[j][1]);
-        o.y = pack_bf2(silu_f(ag[j][2]) * au[j][2], silu_f(ag[j][3]) * au[j][3]);
-        *reinterpret_cast<u32x2*>(A + (size_t)(off + t) * F + fb * 16 + 4 * g) = o;
-      }
-    }
-  }
+  if (ne - t0 <= 16)
+    gate_up_item<1>(wg, wu, h, perm, off, t0, ne, F, fb, d, lane, w, A, red);
+  else
+    gate_up_item<2>(wg, wu, h, perm, off, t0, ne, F, fb, d, lane, w, A, red);
 }
 
-// Y[slot][n] = A[slot] . W_d[e][n]^T.  Wave = (expert, 16*WN output rows).
-template <int TT, int WN>
-__global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restrict__ A,
-                                                       const uint16_t* __restrict__ wd,
-                                                       const int32_t* __restrict__ cnt,
-                                                       const int32_t* __restrict__ offs, int E,
-                                                       int F, int d, float* __restrict__ Y) {
-  const int lane = threadIdx.x & 63;
+// down: Y[slot][n] = A[slot] . W_d[e][n]^T for 16*WN output rows.
+template <int NT, int WN>
+__device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const uint16_t* A,
+                                          int off, int t0, int ne, int F, int d, int n0, int lane,
+                                          int w, float* Y, f32x4 (*red)[2][2][64]) {
   const int r = lane & 15, g = lane >> 4;
-  const int nnb = d / (16 * WN);
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int e = wid / nnb, nb = wid - e * nnb;
-  if (e >= E) return;
-  const int ne = cnt[e];
-  if (ne == 0) return;
-  const int off = offs[e];
-  const uint16_t* wp[WN];
+  const uint16_t* xp[NT];
 #pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = wd + ((size_t)e * d + nb * 16 * WN + 16 * i + r) * F + 16 * g;
-  const int nk = F >> 6;
-
-  for (int t0 = 0; t0 < ne; t0 += 16 * TT) {
-    const int nt = min(TT, (ne - t0 + 15) >> 4);
-    const uint16_t* xp[TT];
+  for (int j = 0; j < NT; ++j) xp[j] = A + (size_t)(off + min(t0 + 16 * j + r, ne - 1)) * F + 8 * g;
+  f32x4 acc[WN][NT];
 #pragma unroll
-    for (int j = 0; j < TT; ++j) xp[j] = A + (size_t)(off + min(t0 + 16 * j + r, ne - 1)) * F + 16 * g;
-    f32x4 acc[WN][TT];
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 Wa[WN][2], Xa[NT][2], Wb[WN][2], Xb[NT][2], Wc[WN][2], Xc[NT][2];
+  auto ld = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2], int step) {
+    const int k = (w + 4 * step) * 64;
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
-      for (int j = 0; j < TT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 W0[WN][2], X0[TT][2], W1[WN][2], X1[TT][2];
-    auto load = [&](u32x4 (&W)[WN][2], u32x4 (&X)[TT][2], int it) {
-      const int k = it * 64;
+      for (int q = 0; q < 2; ++q) W[i][q] = ld16_stream(wp[i] + k + 32 * q);
 #pragma unroll
-      for (int i = 0; i < WN; ++i) {
-        W[i][0] = ld16(wp[i] + k);
-        W[i][1] = ld16(wp[i] + k + 8);
-      }
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int j = 0; j < TT; ++j)
-        if (j < nt) {
-          X[j][0] = ld16(xp[j] + k);
-          X[j][1] = ld16(xp[j] + k + 8);
-        }
-    };
-    auto mma = [&](u32x4 (&W)[WN][2], u32x4 (&X)[TT][2]) {
+      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 32 * q);
+  };
+  auto mm = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2]) {
 #pragma unroll
-      for (int j = 0; j < TT; ++j)
-        if (j < nt) {
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-          for (int i = 0; i < WN; ++i) {
-            acc[i][j] = mfma16(W[i][0], X[j][0], acc[i][j]);
-            acc[i][j] = mfma16(W[i][1], X[j][1], acc[i][j]);
-          }
-        }
-    };
-    load(W0, X0, 0);
-    for (int it = 0; it < nk; it += 2) {
-      if (it + 1 < nk) load(W1, X1, it + 1);
-      mma(W0, X0);
-      if (it + 1 >= nk) break;
-      if (it + 2 < nk) load(W0, X0, it + 2);
-      mma(W1, X1);
-    }
+      for (int i = 0; i < WN; ++i)
 #pragma unroll
-    for (int j = 0; j < TT; ++j) {
-      const int t = t0 + 16 * j + r;
-      if (j < nt && t < ne) {
+        for (int q = 0; q < 2; ++q) acc[i][j] = mfma16(W[i][q], X[j][q], acc[i][j]);
+  };
+  const int nk = F >> 6;
+  const int n = w < nk ? (nk - w + 3) >> 2 : 0;
+  pipeline3(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
+            [&](int t) { ld(Wc, Xc, t); }, [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); },
+            [&] { mm(Wc, Xc); });
 #pragma unroll
-        for (int i = 0; i < WN; ++i)
-          *reinterpret_cast<f32x4*>(Y + (size_t)(off + t) * d + nb * 16 * WN + 16 * i + 4 * g) = acc[i][j];
-      }
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[w][i][j][lane] = acc[i][j];
+  __syncthreads();
+  // wave w finalises (row block i, token tile j) pairs w, w+4, ...
+  for (int p = w; p < WN * NT; p += 4) {
+    const int i = p / NT, j = p - i * NT;
+    const int t = t0 + 16 * j + r;
+    if (t < ne) {
+      const f32x4 v = red[0][i][j][lane] + red[1][i][j][lane] + red[2][i][j][lane] + red[3][i][j][lane];
+      *reinterpret_cast<f32x4*>(Y + (size_t)(off + t) * d + n0 + 16 * i + 4 * g) = v;
     }
   }
 }
 
+template <int WN>
+__global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restrict__ A,
+                                                       const uint16_t* __restrict__ wd,
+                                                       const int32_t* __restrict__ cnt,
+                                                       const int32_t* __restrict__ offs,
+                                                       const int2* __restrict__ items,
+                                                       const int32_t* __restrict__ n_items,
+                                                       int max_items, int F, int d,
+                                                       float* __restrict__ Y) {
+  static_assert(WN <= 2, "LDS tile holds at most 2 row blocks");
+  __shared__ f32x4 red[4][2][2][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int nb = lb / max_items, item = lb - nb * max_items;
+  if (nb >= d / (16 * WN) || item >= *n_items) return;
+  const int2 it = items[item];
+  const int e = it.x, t0 = it.y;
+  const int ne = cnt[e], off = offs[e];
+  const int n0 = nb * 16 * WN;
+  const uint16_t* wp[WN];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) wp[i] = wd + ((size_t)e * d + n0 + 16 * i + r) * F + 8 * g;
+  if (ne - t0 <= 16)
+    down_item<1, WN>(wp, A, off, t0, ne, F, d, n0, lane, w, Y, red);
+  else
+    down_item<2, WN>(wp, A, off, t0, ne, F, d, n0, lane, w, Y, red);
+}
+
+int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
+
 void launch_moe_gate_up(const uint16_t* h, const uint16_t* w_gate_up, const int32_t* cnt,
-                        const int32_t* offs, const int32_t* perm, int E, int F, int d,
-                        uint16_t* a, hipStream_t s) {
-  const int waves = E * (F / 16);
-  hipLaunchKernelGGL(moe_gate_up_kernel<2>, dim3((waves + 3) / 4), dim3(256), 0, s, h, w_gate_up, cnt,
-                     offs, perm, E, F, d, a);
+                        const int32_t* offs, const int32_t* perm, const int2* items,
+                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
+                        hipStream_t s) {
+  const int blocks = (max_items * (F / 16) + kXcd - 1) / kXcd * kXcd;
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, h, w_gate_up, cnt, offs, perm,
+                     items, n_items, max_items, F, d, a);
 }
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
-                     const int32_t* offs, int E, int F, int d, float* Y, hipStream_t s) {
+                     const int32_t* offs, const int2* items, const int32_t* n_items, int max_items,
+                     int F, int d, float* Y, hipStream_t s) {
   constexpr int WN = 2;
-  const int waves = E * (d / (16 * WN));
-  hipLaunchKernelGGL((moe_down_kernel<2, WN>), dim3((waves + 3) / 4), dim3(256), 0, s, a, w_down, cnt,
-                     offs, E, F, d, Y);
+  const int blocks = (max_items * (d / (16 * WN)) + kXcd - 1) / kXcd * kXcd;
+  hipLaunchKernelGGL((moe_down_kernel<WN>), dim3(blocks), dim3(256), 0, s, a, w_down, cnt, offs, items,
+                     n_items, max_items, F, d, Y);
 }
 
 }  // namespace dg

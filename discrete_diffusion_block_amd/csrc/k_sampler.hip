@@ -80,10 +80,13 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
   float s = 0.f, t = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    const float dlt = m - x[j];
-    const float e = (x[j] == -INFINITY) ? 0.f : __expf(-dlt);
-    s += e;
-    t += e * dlt;
+    // padding lanes (past the end of the vocabulary) hold -inf and contribute nothing
+    if (x[j] != -INFINITY) {
+      const float dlt = m - x[j];
+      const float e = __expf(-dlt);
+      s += e;
+      t += e * dlt;
+    }
   }
   s = block_sum(s, red);
   t = block_sum(t, red);

@@ -59,3 +59,20 @@ def eb_valid(H: np.ndarray, masked, committed, gamma: float, commit_all: bool) -
         else:
             break
     return sorted(committed) == sorted(order[:max(1, k)])
+
+
+# Router logits of the engine and of the oracle differ by fp32-vs-fp64 accumulation and by
+# rare one-ulp differences of the bf16-rounded normed input (~0.02 * 2^-8 per element);
+# 1e-3 bounds that generously.  A token whose k-th and (k+1)-th router logits are closer
+# than this is a routing near-tie: either expert set is correct under the precision contract.
+ROUTER_DELTA = 1e-3
+
+
+def routing_near_ties(trace_layers, k: int, delta: float = ROUTER_DELTA):
+    """Per layer, the set of token rows whose top-k router decision is a near-tie."""
+    out = []
+    for t in trace_layers:
+        r = -np.sort(-np.asarray(t["router"]), axis=1)
+        gap = r[:, k - 1] - r[:, k] if r.shape[1] > k else np.full(r.shape[0], np.inf)
+        out.append(set(np.nonzero(gap < delta)[0].tolist()))
+    return out
