@@ -1,0 +1,273 @@
+"""Benchmark: block-parallel diffusion decoding on one MI355X.
+
+One bench step = one call of dg_generate_block on the full 30-layer model
+(d 2816, 16q/8kv heads of 128, 128 experts top-8 + shared, vocab 262144,
+canvas 256): 12 denoising steps with entropy-bounded unmasking (gamma 2.0),
+then the causal append of the finished canvas to the KV cache.  The 1024-token
+random prompt is prefilled once before timing (the pages exclude prefill from
+latency).  Weights are random-init N(0, 0.02) bf16 and inputs are synthetic.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "discrete_diffusion_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(kind, cfg, M, counts_per_layer):
+    """(bound, unit, amount per launch) for a kernel kind at M canvas rows.
+
+    MoE kinds use the per-layer expert token counts of the latest denoising pass:
+    every expert with at least one token streams its weights once; every
+    assignment reads its activation row and writes its output row."""
+    d, F, Fs, E, V = cfg.d_model, cfg.expert_ffn, cfg.shared_ffn, cfg.n_experts, cfg.vocab
+    hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    if kind in ("moe_gate_up", "moe_down"):
+        per = []
+        for cnt in counts_per_layer:
+            used = sum(1 for c in cnt if c > 0)
+            A = sum(cnt)
+            if kind == "moe_gate_up":
+                per.append(used * 2 * F * d * 2 + A * d * 2 + A * F * 2)
+            else:
+                per.append(used * d * F * 2 + A * F * 2 + A * d * 4)
+        return "hbm", "GB/s", sum(per) / len(per)
+    if kind == "head":
+        return "hbm", "GB/s", V * d * 2 + M * d * 2 + M * V * 2
+    if kind == "qkv":
+        R = (hq + 2 * hkv) * hd
+        return "mfma", "TFLOP/s", 2.0 * M * R * d
+    if kind == "o_proj":
+        return "mfma", "TFLOP/s", 2.0 * M * d * hq * hd
+    if kind == "shared_gate_up":
+        return "mfma", "TFLOP/s", 2.0 * M * 2 * Fs * d
+    if kind == "shared_down":
+        return "mfma", "TFLOP/s", 2.0 * M * d * Fs
+    if kind == "attention":
+        keys = cfg.window + cfg.canvas
+        return "mfma", "TFLOP/s", 4.0 * M * hq * keys * hd
+    if kind == "sample_pass1":
+        return "hbm", "GB/s", M * V * 2
+    return None, None, None
+
+
+def cpu_baseline(budget_note: str):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Sample: one full-shape MoE layer (d 2816, 128 experts) plus the 262144-row
+    tied head, on a 256-token canvas over a 1024-token prefix.  Timed: one
+    denoising step of that 1-layer model (layer + head), the same step with the
+    head cut to 8 rows (layer alone), and one sampler call.  Extrapolated to the
+    benchmark unit (tokens/s of 256-token blocks, 12 steps + append, 30 layers):
+    block = 12 * (30 * t_layer + t_head + t_sample) + 30 * t_layer."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from discrete_diffusion_block_amd import synth
+    from oracle import dg_oracle as O
+
+    cfg = dataclasses.replace(synth.CONFIGS["full"], n_layers=1)
+    w = O.to_numpy_weights(synth.make_weights(cfg, device="cpu"))
+    prompt = synth.make_prompt(cfg, 1, 1024).numpy()
+    kv = O.KVCache(cfg, 1)
+    t0 = time.perf_counter()
+    O.prefill_kv(cfg, w, kv, prompt)
+    t_prefill = time.perf_counter() - t0
+    canvas = np.full((1, cfg.canvas), cfg.mask_id)
+    t0 = time.perf_counter()
+    logits = O.denoise_step(cfg, w, kv, canvas, 1.0)
+    t_a = time.perf_counter() - t0
+    cfg8 = dataclasses.replace(cfg, vocab=8)
+    w8 = dict(w)
+    w8["embed"] = np.concatenate([w["embed"][:8], w["embed"][cfg.vocab:cfg.vocab + 1]])
+    t0 = time.perf_counter()
+    O.denoise_step(cfg8, w8, kv, np.full((1, cfg.canvas), 8), 1.0)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.sample_eb(O.bf16(logits), canvas, 2.0, False, cfg.mask_id)
+    t_sample = time.perf_counter() - t0
+    t_head = max(t_a - t_layer, 0.0)
+    L = synth.CONFIGS["full"].n_layers
+    block = 12 * (L * t_layer + t_head + t_sample) + L * t_layer
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": 256.0 / block,
+        "unit": "tok/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"numpy float64 oracle: one full-shape MoE layer + 262144-row head denoising step "
+                   f"{t_a:.2f}s, layer alone {t_layer:.2f}s, sampler {t_sample:.2f}s (prefix prefill "
+                   f"{t_prefill:.1f}s untimed); extrapolated to 30 layers x (12 steps + append) per "
+                   f"256-token block; {budget_note}"),
+        "block_s_extrapolated": block,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10, help="timed blocks")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--denoise-steps", type=int, default=12)
+    ap.add_argument("--gamma", type=float, default=2.0)
+    ap.add_argument("--prompt", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the engine runs one process on one MI355X; see the design notes on sharding).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from discrete_diffusion_block_amd import dg, synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dg.lib()
+    cfg = synth.CONFIGS["full"]
+    C, V = cfg.canvas, cfg.vocab
+    n_blocks = args.warmup + args.steps + 3
+    max_ctx = int(math.ceil((args.prompt + C * n_blocks) / 64.0) * 64)
+    t0 = time.time()
+    w = synth.make_weights(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"weights {time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
+    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=max_ctx)
+    prompt = synth.make_prompt(cfg, 1, args.prompt, device="cuda")
+    eng.prefill_kv(prompt)
+    torch.cuda.synchronize()
+    logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    canvas = torch.empty(1, C, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole blocks
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    assert nm.item() == 0
+    ms_per_block = wall * 1000.0 / args.steps
+    value = C * args.steps / wall
+    log(f"{args.steps} blocks: {wall * 1e3:.1f} ms wall, {gpu_ms:.1f} ms GPU -> {value:.0f} tok/s")
+
+    # ---- one more block with per-launch HIP events (same stream, same work)
+    dg.dg_profile_begin(eng.ctx, 20000)
+    t0 = time.perf_counter()
+    eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    torch.cuda.synchronize()
+    prof_block_ms = (time.perf_counter() - t0) * 1e3
+    prof = dg.dg_profile_end(eng.ctx)
+    log("per-kind kernel ms in one block: " +
+        ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in sorted(prof.items(), key=lambda kv: -kv[1][0]) if v[1]))
+
+    # ---- denoise step alone (denoise + sampler), and the expert routing it produced
+    c2 = torch.full((1, C), V, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = 12
+    for s in range(reps):
+        eng.denoise_step(c2, 1.0 - s / reps, logits)
+        eng.sample_eb(logits, c2, args.gamma, s == reps - 1, nm)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    denoise_ms = e0.elapsed_time(e1) / reps
+    eng.denoise_step(torch.full((1, C), V, dtype=torch.int32, device="cuda"), 1.0, logits)
+    counts = eng.moe_counts().cpu().tolist()
+    used = [sum(1 for c in row if c > 0) for row in counts]
+
+    # ---- roofline of the dominant kernel kind
+    dom = max((k for k in prof if prof[k][1]), key=lambda k: prof[k][0])
+    bound, unit, amount = algorithmic_work(dom, cfg, C, counts)
+    avg_ms = prof[dom][0] / prof[dom][1]
+    roofline = None
+    if bound is not None:
+        if unit == "GB/s":
+            achieved, peak = amount / (avg_ms * 1e-3) / 1e9, HBM_PEAK_GBS
+        else:
+            achieved, peak = amount / (avg_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS
+        traffic = None
+        tfile = os.path.join(ROOT, "profiles", "traffic.json")
+        if os.path.exists(tfile):
+            t = json.load(open(tfile))
+            if t.get("kernel") == dom and t.get("source_digest") == kernel_source_digest():
+                traffic = t.get("bytes_per_launch")
+        roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                    "avg_launch_ms": round(avg_ms, 4), "launches": prof[dom][1],
+                    "algorithmic_per_launch": amount}
+
+    out = {
+        "metric": "output tok/s (256-tok canvas, 12 denoise steps + KV append per block)",
+        "value": round(value, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_block, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random-init N(0,0.02) bf16 weights, uniform-random 1024-token prompt)",
+        "config": {"workload": "full 256-token block generation: 30 MoE layers d2816, 16q/8kv x128, "
+                               "128 experts top-8 (F 704) + shared (F 2112), vocab 262144 tied, "
+                               "1024-token prompt, 12 steps, gamma 2.0, batch 1",
+                   "global_batch": 1, "seq_len": args.prompt, "canvas": C,
+                   "denoise_steps": args.denoise_steps, "parallelism": "single GPU"},
+        "denoise_step_ms": round(denoise_ms, 3),
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 3),
+        "tokens_per_forward": round(C / (args.denoise_steps + 1), 3),
+        "experts_used_per_layer_mean": round(sum(used) / len(used), 1),
+        "profiled_block_ms": round(prof_block_ms, 3),
+        "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)...")
+        try:
+            out["cpu_baseline"] = cpu_baseline("rank 0, N=1")
+        except Exception as exc:  # a host-side failure must not hide the GPU result
+            out["cpu_baseline"] = {"error": repr(exc)}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -14,11 +14,20 @@
 
 using namespace dg;
 
+// Optional per-launch event timing (dg_profile_begin/end).
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // two per record
+  std::vector<int> kind;
+  size_t used = 0;
+};
+
 struct dg_ctx {
   dg_config cfg;
   const uint16_t* embed;
   const float* final_norm;
   std::vector<dg_layer_weights> layers;
+  mutable Prof prof;
 };
 
 namespace {
@@ -41,6 +50,29 @@ dg_status check_launch(const char* what) {
   return DG_OK;
 }
 
+// Brackets one launch with profiling events when profiling is on.
+struct Timed {
+  const dg_ctx* c;
+  int kind;
+  hipStream_t s;
+  bool on;
+  Timed(const dg_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_) {
+    on = c && c->prof.on && c->prof.used < c->prof.kind.size();
+    if (on) (void)hipEventRecord(c->prof.ev[2 * c->prof.used], s);
+  }
+  ~Timed() {
+    if (on) {
+      (void)hipEventRecord(c->prof.ev[2 * c->prof.used + 1], s);
+      c->prof.kind[c->prof.used++] = kind;
+    }
+  }
+};
+#define DG_TIMED(ctx, kind, stmt) \
+  do {                            \
+    Timed _timed(ctx, kind, s);   \
+    stmt;                         \
+  } while (0)
+
 constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
 constexpr size_t kAlign = 256;
 
@@ -60,6 +92,7 @@ struct Ws {
   int32_t* inv;
   int2* items;
   int32_t* n_items;
+  int32_t* cnt_log;
   uint16_t* A;
   float* Y;
   uint16_t* As;
@@ -107,6 +140,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->inv = cv.take<int32_t>(M * c.top_k);
   ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
   ws->n_items = cv.take<int32_t>(1);
+  ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
   ws->A = cv.take<uint16_t>(M * c.top_k * c.expert_ffn);
   ws->Y = cv.take<float>(M * c.top_k * c.d_model);
   ws->As = cv.take<uint16_t>(M * c.shared_ffn);
@@ -165,33 +199,39 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
   const int d = c.d_model, hq = c.n_q_heads, hd = c.head_dim, E = c.n_experts, k = c.top_k;
   const float eps = c.rms_eps;
   const int nl = c.n_layers;
-  launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr, s);
-  launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, ctx->layers[0].attn_norm, eps,
-                    ws.x, ws.h, M, d, c.vocab, s);
+  DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr, s));
+  DG_TIMED(ctx, DG_K_EMBED,
+           launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, ctx->layers[0].attn_norm,
+                             eps, ws.x, ws.h, M, d, c.vocab, s));
   for (int l = 0; l < nl; ++l) {
     const dg_layer_weights& L = ctx->layers[l];
     const KvLayer kvl = kv_layer(ctx, kv, l);
-    launch_qkv_rope(ws.h, L.w_qkv, M, d, hq, kvl, g, ws.rope, ws.q, s);
+    DG_TIMED(ctx, DG_K_QKV, launch_qkv_rope(ws.h, L.w_qkv, M, d, hq, kvl, g, ws.rope, ws.q, s));
     // In the encoder only the keys/values are observable; the last layer's
     // attention output and FFN feed nothing, so they are not computed.
     if (!g.denoise && l == nl - 1) break;
-    launch_attention(ws.q, hq, kvl, g, ws.o, s);
-    launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s);
-    launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s);
-    launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s);
-    launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s);
-    launch_route(ws.ids, M, k, E, ws.cnt, ws.offs, ws.perm, ws.inv, ws.items, ws.n_items, s);
+    DG_TIMED(ctx, DG_K_ATTENTION, launch_attention(ws.q, hq, kvl, g, ws.o, s));
+    DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
+    DG_TIMED(ctx, DG_K_NORM, launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s));
+    DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
+    DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
+    DG_TIMED(ctx, DG_K_ROUTE,
+             launch_route(ws.ids, M, k, E, ws.cnt, ws.offs, ws.perm, ws.inv, ws.items, ws.n_items,
+                          ws.cnt_log + (size_t)l * E, s));
     const int max_items = moe_max_items(M, k, E);
-    launch_moe_gate_up(ws.h, L.w_gate_up, ws.cnt, ws.offs, ws.perm, ws.items, ws.n_items, max_items,
-                       c.expert_ffn, d, ws.A, s);
-    launch_moe_down(ws.A, L.w_down, ws.cnt, ws.offs, ws.items, ws.n_items, max_items, c.expert_ffn, d,
-                    ws.Y, s);
-    launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s);
-    launch_gemm_f32(ws.As, L.ws_down, ws.x, M, d, c.shared_ffn, /*add=*/true, s);
+    DG_TIMED(ctx, DG_K_MOE_GATE_UP,
+             launch_moe_gate_up(ws.h, L.w_gate_up, ws.cnt, ws.offs, ws.perm, ws.items, ws.n_items,
+                                max_items, c.expert_ffn, d, ws.A, s));
+    DG_TIMED(ctx, DG_K_MOE_DOWN,
+             launch_moe_down(ws.A, L.w_down, ws.cnt, ws.offs, ws.items, ws.n_items, max_items,
+                             c.expert_ffn, d, ws.Y, s));
+    DG_TIMED(ctx, DG_K_SHARED_GATE_UP, launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s));
+    DG_TIMED(ctx, DG_K_SHARED_DOWN,
+             launch_gemm_f32(ws.As, L.ws_down, ws.x, M, d, c.shared_ffn, /*add=*/true, s));
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
-    launch_combine(ws.x, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s);
+    DG_TIMED(ctx, DG_K_COMBINE, launch_combine(ws.x, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s));
   }
-  if (g.denoise) launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d, s);
+  if (g.denoise) DG_TIMED(ctx, DG_K_HEAD, launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d, s));
   return check_launch("transformer pass");
 }
 
@@ -271,10 +311,12 @@ dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batc
 
 dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
                       float gamma, int commit_all, float* d_entropy, int32_t* d_argmax,
-                      int32_t* d_n_masked, const Ws& ws, hipStream_t s) {
-  launch_sample_partials(d_logits, d_canvas, batch * canvas, vocab, ws.part, ws.part_arg, s);
-  launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
-                   canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, s);
+                      int32_t* d_n_masked, const Ws& ws, hipStream_t s, const dg_ctx* ctx = nullptr) {
+  DG_TIMED(ctx, DG_K_SAMPLE_PASS1,
+           launch_sample_partials(d_logits, d_canvas, batch * canvas, vocab, ws.part, ws.part_arg, s));
+  DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
+           launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
+                            canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, s));
   return check_launch("sampler");
 }
 
@@ -319,7 +361,11 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out) {
   return DG_OK;
 }
 
-void dg_destroy(dg_ctx* ctx) { delete ctx; }
+void dg_destroy(dg_ctx* ctx) {
+  if (!ctx) return;
+  for (hipEvent_t e : ctx->prof.ev) (void)hipEventDestroy(e);
+  delete ctx;
+}
 
 dg_status dg_workspace_size(const dg_ctx* ctx, int batch, size_t* bytes) {
   if (!ctx || !bytes) return fail(DG_ERR_INVALID_ARG, "NULL argument");
@@ -407,16 +453,60 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
   st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
   if (st != DG_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s);
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
   for (int step = 0; step < steps; ++step) {
     const float t = 1.0f - (float)step / (float)steps;
     st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s);
     if (st != DG_OK) return st;
     st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == steps - 1, nullptr,
-                     nullptr, d_n_masked, ws, s);
+                     nullptr, d_n_masked, ws, s, ctx);
     if (st != DG_OK) return st;
   }
   if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
+  return DG_OK;
+}
+
+dg_status dg_profile_begin(dg_ctx* ctx, int capacity) {
+  if (!ctx || capacity < 1) return fail(DG_ERR_INVALID_ARG, "bad profiling arguments");
+  Prof& p = ctx->prof;
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& e : p.ev)
+    if (hipEventCreate(&e) != hipSuccess) return fail(DG_ERR_HIP, "hipEventCreate failed");
+  p.kind.assign(capacity, -1);
+  p.used = 0;
+  p.on = true;
+  return DG_OK;
+}
+
+dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count) {
+  if (!ctx || !ms || !count) return fail(DG_ERR_INVALID_ARG, "NULL argument");
+  Prof& p = ctx->prof;
+  p.on = false;
+  for (int k = 0; k < DG_K_COUNT; ++k) {
+    ms[k] = 0.0;
+    count[k] = 0;
+  }
+  for (size_t i = 0; i < p.used; ++i) {
+    if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess) return fail(DG_ERR_HIP, "event sync failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess)
+      return fail(DG_ERR_HIP, "event timing failed");
+    ms[p.kind[i]] += t;
+    count[p.kind[i]] += 1;
+  }
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.kind.clear();
+  p.used = 0;
+  return DG_OK;
+}
+
+dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset) {
+  if (!ctx || !offset || batch < 1 || batch > ctx->cfg.max_batch) return fail(DG_ERR_INVALID_ARG, "bad arguments");
+  Ws ws;
+  carve(ctx->cfg, batch, reinterpret_cast<char*>(kAlign), &ws);   // offsets relative to an aligned base
+  *offset = reinterpret_cast<uintptr_t>(ws.cnt_log) - kAlign;
   return DG_OK;
 }
 

@@ -60,7 +60,8 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 constexpr int kMoeGroup = 32;        // tokens per grouped-GEMM work item
 int moe_max_items(int M, int k, int E);
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
-                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, hipStream_t s);
+                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
+                  hipStream_t s);
 void launch_moe_gate_up(const uint16_t* h, const uint16_t* w_gate_up, const int32_t* cnt,
                         const int32_t* offs, const int32_t* perm, const int2* items,
                         const int32_t* n_items, int max_items, int F, int d, uint16_t* a,

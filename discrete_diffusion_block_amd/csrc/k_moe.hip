@@ -86,7 +86,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv,
                                                      int2* __restrict__ items,
-                                                     int32_t* __restrict__ n_items) {
+                                                     int32_t* __restrict__ n_items,
+                                                     int32_t* __restrict__ cnt_log) {
   __shared__ int hist[256];
   __shared__ int base[256];
   __shared__ int wcnt[16][256];
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
       base[e] = run;
       offs[e] = run;
       cnt[e] = hist[e];
+      if (cnt_log) cnt_log[e] = hist[e];
       run += hist[e];
       // work items of the grouped GEMMs: (expert, first slot) per kMoeGroup-token group
       for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[ni++] = make_int2(e, t0);
@@ -142,9 +144,10 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
-                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, hipStream_t s) {
+                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
+                  hipStream_t s) {
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, cnt, offs, perm, inv,
-                     items, n_items);
+                     items, n_items, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs

@@ -21,6 +21,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dg.h")
 MAX_BATCH = 64
 
+KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
+                "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
+                "sample_pass1", "sample_select", "fill"]
+
 STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE", -3: "DG_ERR_WORKSPACE",
           -4: "DG_ERR_KV_CAPACITY", -5: "DG_ERR_HIP", -6: "DG_ERR_UNSUPPORTED"}
 
@@ -70,6 +74,9 @@ def lib():
             "dg_sample_workspace_size": [i32, i32, i32, C.POINTER(sz)],
             "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
+            "dg_profile_begin": [vp, i32],
+            "dg_profile_end": [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
+            "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
             "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
@@ -170,6 +177,25 @@ def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: floa
                                    _stream(stream)))
 
 
+def dg_profile_begin(ctx, capacity: int):
+    _check(lib().dg_profile_begin(ctx, capacity))
+
+
+def dg_profile_end(ctx):
+    """{kind: (total_ms, launches)} for the launches bracketed since dg_profile_begin."""
+    n = len(KERNEL_KINDS)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int32 * n)()
+    _check(lib().dg_profile_end(ctx, ms, cnt))
+    return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def dg_workspace_moe_counts(ctx, batch: int) -> int:
+    off = C.c_size_t()
+    _check(lib().dg_workspace_moe_counts(ctx, batch, C.byref(off)))
+    return off.value
+
+
 def dg_test_router_topk(r: torch.Tensor, k: int, ids: torch.Tensor, w: torch.Tensor, stream=None):
     M, E = r.shape
     _check(lib().dg_test_router_topk(_p(r), M, E, k, _p(ids), _p(w), _stream(stream)))
@@ -256,6 +282,12 @@ class Engine:
     def sample_eb(self, logits, canvas, gamma, commit_all, n_masked, entropy=None, argmax=None,
                   stream=None):
         dg_sample_eb(logits, canvas, gamma, commit_all, n_masked, self.ws, entropy, argmax, stream)
+
+    def moe_counts(self):
+        """Per-layer per-expert token counts of the latest pass (int32 [L][E], device)."""
+        off = dg_workspace_moe_counts(self.ctx, self.max_batch)
+        n = self.cfg.n_layers * self.cfg.n_experts
+        return self.ws[off:off + 4 * n].view(torch.int32).view(self.cfg.n_layers, self.cfg.n_experts)
 
     def generate_block(self, canvas, steps, gamma, append_kv, logits, n_masked, stream=None):
         dg_generate_block(self.ctx, self.kv, canvas, steps, gamma, append_kv, logits, n_masked,

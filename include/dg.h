@@ -157,6 +157,26 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
                             float gamma, int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
                             void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---- measurement helpers (diagnostics; not thread-safe) ---- */
+
+/* Kernel kinds the engine launches, for per-kind event timing. */
+typedef enum dg_kernel_kind {
+  DG_K_PREP = 0, DG_K_EMBED, DG_K_QKV, DG_K_ATTENTION, DG_K_O_PROJ, DG_K_NORM, DG_K_ROUTER,
+  DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
+  DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL, DG_K_COUNT
+} dg_kernel_kind;
+
+/* Start bracketing every kernel launch made through ctx (dg_prefill_kv,
+ * dg_denoise_step, dg_generate_block) with a pair of hipEvents recorded on the
+ * launch stream, for up to `capacity` launches (events are created here). */
+dg_status dg_profile_begin(dg_ctx* ctx, int capacity);
+/* Stop, wait for the recorded events, and return per kind the summed kernel
+ * milliseconds and launch counts (arrays of DG_K_COUNT entries). */
+dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count);
+/* Byte offset, inside a workspace sized for `batch`, of an int32 [n_layers][E]
+ * log of the per-expert token counts of the most recent pass through each layer. */
+dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset);
+
 /* ---- kernel taps for tests (not part of the stable contract) ---- */
 
 /* Router selection alone: r fp32 [M][E] -> ids int32 [M][k] (by logit desc, id
