@@ -158,7 +158,7 @@ def main():
     w = synth.make_weights(cfg, device="cuda")
     torch.cuda.synchronize()
     log(f"weights {time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
-    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=max_ctx)
+    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=max_ctx, free_source=True)
     prompt = synth.make_prompt(cfg, 1, args.prompt, device="cuda")
     eng.prefill_kv(prompt)
     torch.cuda.synchronize()

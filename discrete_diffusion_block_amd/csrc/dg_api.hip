@@ -77,25 +77,26 @@ constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
 constexpr size_t kAlign = 256;
 
 struct Ws {
-  float* x;
-  uint16_t* h;
-  uint16_t* q;
-  uint16_t* o;
+  float* x;        // residual stream, fp32 row-major [M][d]
+  uint16_t* h;     // normed activations, fragment-major [M_pad][d]
+  uint16_t* q;     // queries, fragment-major per (sequence, head) [n_pad][hd]
+  uint16_t* o;     // attention output, fragment-major [M_pad][Hq*hd]
   float2* rope;
   float* temb;
-  float* r;
+  float* r;        // router logits fp32 [M][E]
   int32_t* ids;
   float* wts;
   int32_t* cnt;
-  int32_t* offs;
-  int32_t* perm;
-  int32_t* inv;
+  int32_t* poff;   // padded (16-aligned) slot offsets [E+1]
+  int32_t* perm;   // token of each padded slot (-1 on padding)
+  int32_t* inv;    // padded slot of each assignment
   int2* items;
   int32_t* n_items;
   int32_t* cnt_log;
-  uint16_t* A;
-  float* Y;
-  uint16_t* As;
+  uint16_t* xg;    // expert-grouped token rows, fragment-major [P_pad][d]
+  uint16_t* A;     // expert SwiGLU outputs, fragment-major [P_pad][F]
+  float* Y;        // expert outputs fp32 [P][d]
+  uint16_t* As;    // shared-expert SwiGLU output, fragment-major [M_pad][Fs]
   float4* part;
   int* part_arg;
 };
@@ -121,29 +122,35 @@ size_t carve_sampler(Carver& cv, int batch, int canvas, int vocab, Ws* ws) {
   return cv.off;
 }
 
+size_t round16(size_t v) { return (v + 15) / 16 * 16; }
+
 size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
-  const size_t M = (size_t)batch * std::max(c.canvas, kPrefillChunk);
+  const size_t n = (size_t)std::max(c.canvas, kPrefillChunk);
+  const size_t M = (size_t)batch * n;
+  const size_t Mp = round16(M);
   const size_t qd = (size_t)c.n_q_heads * c.head_dim;
+  const size_t P = (size_t)moe_max_slots((int)M, c.top_k, c.n_experts);
   Carver cv{base};
   ws->x = cv.take<float>(M * c.d_model);
-  ws->h = cv.take<uint16_t>(M * c.d_model);
-  ws->q = cv.take<uint16_t>(M * qd);
-  ws->o = cv.take<uint16_t>(M * qd);
+  ws->h = cv.take<uint16_t>(Mp * c.d_model);
+  ws->q = cv.take<uint16_t>((size_t)batch * round16(n) * qd);
+  ws->o = cv.take<uint16_t>(Mp * qd);
   ws->rope = cv.take<float2>(M * (c.head_dim / 2));
   ws->temb = cv.take<float>(c.d_model);
   ws->r = cv.take<float>(M * c.n_experts);
   ws->ids = cv.take<int32_t>(M * c.top_k);
   ws->wts = cv.take<float>(M * c.top_k);
   ws->cnt = cv.take<int32_t>(c.n_experts);
-  ws->offs = cv.take<int32_t>(c.n_experts + 1);
-  ws->perm = cv.take<int32_t>(M * c.top_k);
+  ws->poff = cv.take<int32_t>(c.n_experts + 1);
+  ws->perm = cv.take<int32_t>(P);
   ws->inv = cv.take<int32_t>(M * c.top_k);
   ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
   ws->n_items = cv.take<int32_t>(1);
   ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
-  ws->A = cv.take<uint16_t>(M * c.top_k * c.expert_ffn);
-  ws->Y = cv.take<float>(M * c.top_k * c.d_model);
-  ws->As = cv.take<uint16_t>(M * c.shared_ffn);
+  ws->xg = cv.take<uint16_t>(round16(P) * c.d_model);
+  ws->A = cv.take<uint16_t>(round16(P) * c.expert_ffn);
+  ws->Y = cv.take<float>(P * c.d_model);
+  ws->As = cv.take<uint16_t>(Mp * c.shared_ffn);
   carve_sampler(cv, batch, c.canvas, c.vocab, ws);
   return cv.off + kAlign;
 }
@@ -216,14 +223,15 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
     DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
     DG_TIMED(ctx, DG_K_ROUTE,
-             launch_route(ws.ids, M, k, E, ws.cnt, ws.offs, ws.perm, ws.inv, ws.items, ws.n_items,
+             launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items,
                           ws.cnt_log + (size_t)l * E, s));
+    DG_TIMED(ctx, DG_K_GATHER, launch_gather(ws.h, ws.perm, ws.poff, M, k, E, d, ws.xg, s));
     const int max_items = moe_max_items(M, k, E);
     DG_TIMED(ctx, DG_K_MOE_GATE_UP,
-             launch_moe_gate_up(ws.h, L.w_gate_up, ws.cnt, ws.offs, ws.perm, ws.items, ws.n_items,
-                                max_items, c.expert_ffn, d, ws.A, s));
+             launch_moe_gate_up(ws.xg, L.w_gate_up, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
+                                c.expert_ffn, d, ws.A, s));
     DG_TIMED(ctx, DG_K_MOE_DOWN,
-             launch_moe_down(ws.A, L.w_down, ws.cnt, ws.offs, ws.items, ws.n_items, max_items,
+             launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
                              c.expert_ffn, d, ws.Y, s));
     DG_TIMED(ctx, DG_K_SHARED_GATE_UP, launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s));
     DG_TIMED(ctx, DG_K_SHARED_DOWN,
@@ -464,6 +472,29 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
   }
   if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
   return DG_OK;
+}
+
+dg_status dg_packed_elems(int rows, int cols, size_t* elems) {
+  if (!elems || rows < 1 || cols < 32 || cols % 32) return fail(DG_ERR_INVALID_ARG, "bad packing shape");
+  *elems = round16((size_t)rows) * (size_t)cols;
+  return DG_OK;
+}
+
+dg_status dg_pack_weight(int kind, const uint16_t* d_src, uint16_t* d_dst, int n_mats, int rows, int cols,
+                         int param, void* stream) {
+  if (!d_src || !d_dst || n_mats < 1 || rows < 1 || cols < 32 || cols % 32)
+    return fail(DG_ERR_INVALID_ARG, "bad packing arguments");
+  if (kind == DG_PACK_QKV) {
+    if ((param != 32 && param != 64 && param != 128) || rows % param)
+      return fail(DG_ERR_INVALID_ARG, "qkv packing needs rows = heads * head_dim");
+  } else if (kind == DG_PACK_GATE_UP) {
+    if (param < 16 || param % 16 || rows != 2 * param)
+      return fail(DG_ERR_INVALID_ARG, "gate/up packing needs rows = 2 * F, F % 16 == 0");
+  } else if (kind != DG_PACK_PLAIN) {
+    return fail(DG_ERR_INVALID_ARG, "unknown packing kind");
+  }
+  launch_pack(d_src, d_dst, n_mats, rows, cols, kind, param, (hipStream_t)stream);
+  return check_launch("pack");
 }
 
 dg_status dg_profile_begin(dg_ctx* ctx, int capacity) {

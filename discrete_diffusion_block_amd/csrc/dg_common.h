@@ -120,6 +120,42 @@ __device__ __forceinline__ int xcd_swizzle(int b, int n) {
   return (b % kXcd) * (n / kXcd) + b / kXcd;
 }
 
+// ---------------------------------------------------------------- layouts
+//
+// Fragment-major ("F-major") layout of a bf16 matrix X[R][K] (R padded to a
+// multiple of 16, K a multiple of 32): the matrix is cut into 16-row x 32-col
+// tiles of 512 elements (1 KiB), stored row-block-major with the k tiles of a
+// row block consecutive.  Inside a tile, lane l of a wave owns the 8 elements
+// (row l%16, cols 8*(l/16) .. +7) at element offset 8*l -- exactly the operand
+// fragment of v_mfma_f32_16x16x32_bf16.  Loading a fragment is therefore one
+// fully contiguous 1 KiB wave load, which the vector memory path serves about
+// four times faster than the 16-rows-by-64-bytes pattern of a row-major read.
+__host__ __device__ __forceinline__ size_t fm_index(size_t r, int c, int K) {
+  return (((r >> 4) * (size_t)(K >> 5) + (size_t)(c >> 5)) << 9) +
+         ((size_t)((((c & 31) >> 3) << 4) + (int)(r & 15)) << 3) + (c & 7);
+}
+// Start of the fragment tile (row block rb, k block kb) plus this lane's slot.
+__device__ __forceinline__ size_t fm_tile(size_t rb, int kb, int K, int lane) {
+  return ((rb * (size_t)(K >> 5) + (size_t)kb) << 9) + ((size_t)lane << 3);
+}
+
+// Key cache of one (layer, sequence, kv head): positions in chunks of 32, each
+// chunk two 16-key blocks (bb) whose row r holds key 8*(r/4) + 4*bb + r%4 of
+// the chunk, hd split in 32-wide k tiles.  With that key order, the scores a
+// lane receives from S^T = K Q^T are 8 consecutive keys of the chunk, which is
+// the lane's operand fragment for O^T += V^T P^T.
+__host__ __device__ __forceinline__ size_t k_index(int p, int c, int hd) {
+  const int pp = p & 31, bb = (pp >> 2) & 1, r = ((pp >> 3) << 2) | (pp & 3);
+  return (((size_t)((p >> 5) * 2 + bb) * (size_t)(hd >> 5) + (size_t)(c >> 5)) << 9) +
+         ((size_t)((((c & 31) >> 3) << 4) + r) << 3) + (c & 7);
+}
+// Value cache, stored transposed: for each 32-key chunk and 16-wide hd block, a
+// tile whose lane l holds V[keys 8*(l/16) .. +7 of the chunk][hd row l%16].
+__host__ __device__ __forceinline__ size_t v_index(int p, int c, int hd) {
+  return (((size_t)(p >> 5) * (size_t)(hd >> 4) + (size_t)(c >> 4)) << 9) +
+         ((size_t)((((p & 31) >> 3) << 4) + (c & 15)) << 3) + (p & 7);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

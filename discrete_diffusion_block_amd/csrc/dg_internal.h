@@ -59,16 +59,22 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
 constexpr int kMoeGroup = 32;        // tokens per grouped-GEMM work item
 int moe_max_items(int M, int k, int E);
-void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
+int moe_max_slots(int M, int k, int E);   // padded slot space: M*k + 15*E
+void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
                   hipStream_t s);
-void launch_moe_gate_up(const uint16_t* h, const uint16_t* w_gate_up, const int32_t* cnt,
-                        const int32_t* offs, const int32_t* perm, const int2* items,
-                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
-                        hipStream_t s);
+void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, int M, int k, int E,
+                   int d, uint16_t* xg, hipStream_t s);
+void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
+                        const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
+                        int F, int d, uint16_t* a, hipStream_t s);
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
-                     const int32_t* offs, const int2* items, const int32_t* n_items, int max_items,
+                     const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s);
+
+// ---- weight packing ----
+void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int kind, int param,
+                 hipStream_t s);
 
 // ---- sampler ----
 constexpr int kSampleChunk = 8192;   // logits per workgroup in the first sampler pass

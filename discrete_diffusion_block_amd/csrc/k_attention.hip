@@ -6,6 +6,8 @@
 //    sliding layers, [0, p] on global ones.
 // The projection kernel has already written this pass's keys/values into the
 // cache at positions len_b .., so every key lives in one contiguous range.
+// q, the key cache and the (transposed) value cache are stored in fragment
+// tiles, so each operand fragment below is one contiguous 1 KiB wave load.
 //
 // Work split: a workgroup owns 16 queries of one q head; its 4 waves take
 // interleaved 32-key chunks of the key range (split-KV) and merge their
@@ -15,8 +17,8 @@
 // rows of each 16-row MFMA block permuted so that a lane ends up holding the
 // scores of 8 consecutive keys (8g .. 8g+7 of the chunk) for its query.  Those
 // 8 probabilities are exactly the lane's B fragment for O^T += V^T . P^T, and
-// V is stored transposed in the cache ([hd][pos]), so the A fragment is one
-// 16-byte load.  Softmax state and output rescaling are lane-local (the lane's
+// V is stored transposed in tiles of 32 keys x 16 hd rows, so the A fragment
+// is one 16-byte slot of a contiguous 1 KiB tile.  Softmax state and output rescaling are lane-local (the lane's
 // output rows all belong to its query); only the chunk max needs two shuffles.
 #include <math.h>
 
@@ -42,12 +44,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   const int kvh = head / (hq / kv.hkv);
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
-  // query of this lane (clamped for the load; stores are guarded)
+  // query fragments: q is fragment-major per (sequence, head), [n_pad][HD]
   const int qi = min(i0 + r, n - 1);
-  const size_t qrow = ((size_t)b * n + qi) * hq + head;
+  const int npad = (n + 15) & ~15;
+  const uint16_t* qbase = q + ((size_t)b * hq + head) * (size_t)npad * HD;
   u32x4 qf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) qf[c] = ld16(q + qrow * HD + 32 * c + 8 * gq);
+  for (int c = 0; c < NC; ++c) qf[c] = ld16(qbase + fm_tile(i0 >> 4, c, HD, lane));
 
   // key range of this lane's query and of the whole 16-query tile
   int lo_q, hi_q, lo_t, hi_t;
@@ -81,11 +84,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
     f32x4 s[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const int key = kc + 8 * (r >> 2) + 4 * bb + (r & 3);
-      const uint16_t* kp = kbase + (size_t)key * HD + 8 * gq;
+      // tile (chunk, bb, c) of the key cache: one contiguous 1 KiB fragment
+      const uint16_t* kp = kbase + ((((size_t)(kc >> 5) * 2 + bb) * NC) << 9) + 8 * lane;
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) a = mfma16(ld16(kp + 32 * c), qf[c], a);
+      for (int c = 0; c < NC; ++c) a = mfma16(ld16(kp + 512 * c), qf[c], a);
       s[bb] = a;
     }
     // lane holds keys kc + 8*gq + e (e = 0..7) for query r
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
       acc[hb] *= alpha;
-      const u32x4 va = ld16(vbase + (size_t)(16 * hb + r) * kv.max_ctx + kc + 8 * gq);
+      const u32x4 va = ld16(vbase + (((size_t)(kc >> 5) * NB + hb) << 9) + 8 * lane);
       acc[hb] = mfma16(va, pb, acc[hb]);
     }
   }
@@ -153,7 +156,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   const float invL = L > 0.f ? 1.f / L : 0.f;
   const int iq = i0 + qq;
   if (iq < n) {
-    uint16_t* dst = o + (((size_t)b * n + iq) * hq + head) * HD + d0;
+    // o is fragment-major [M_pad][hq * HD] (the O projection's activation operand)
+    const size_t m = (size_t)b * n + iq;
+    const int K = hq * HD;
 #pragma unroll
     for (int e = 0; e < HD / 16; e += 2) {
       float v0 = 0.f, v1 = 0.f;
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
         v0 += sc[ww] * Ol[ww][qq][d0 + e];
         v1 += sc[ww] * Ol[ww][qq][d0 + e + 1];
       }
-      *reinterpret_cast<uint32_t*>(dst + e) = pack_bf2(v0 * invL, v1 * invL);
+      *reinterpret_cast<uint32_t*>(o + fm_index(m, head * HD + d0 + e, K)) = pack_bf2(v0 * invL, v1 * invL);
     }
   }
 }

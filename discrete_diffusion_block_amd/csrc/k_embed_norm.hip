@@ -1,7 +1,9 @@
 // Row-wise kernels: rotary/timestep tables, embedding gather (+ timestep
 // embedding) fused with the first RMSNorm, plain RMSNorm, and the MoE combine
-// fused with the residual add and the next RMSNorm.  All are HBM/latency bound
-// row sweeps: one 256-thread workgroup per token row, coalesced along d.
+// fused with the residual add and the next RMSNorm.  One 256-thread workgroup
+// per token row; each thread moves 8 consecutive features (16 B of bf16).
+// The residual stream x is fp32 row-major; the normed output h is written in
+// fragment-major layout for the GEMMs that consume it.
 #include "dg_common.h"
 #include "dg_internal.h"
 
@@ -40,11 +42,34 @@ void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d
   hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, s, g, hd, theta, rope_tab, d, t, temb);
 }
 
-__device__ __forceinline__ void norm_row(const float* xr, const float* gain, float eps, uint16_t* hr,
-                                         int d, float ss, float* red) {
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// h[m] (fragment-major, K = d) = x[m] / sqrt(mean(x^2) + eps) * gain, given ss = this
+// thread's share of sum(x^2).
+__device__ __forceinline__ void norm_row(const float* xr, const float* gain, float eps, uint16_t* h,
+                                         int m, int d, float ss, float* red) {
   const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) hr[c] = f2bf(xr[c] * inv * gain[c]);
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
+    float v[8], gg[8];
+    load8(xr + c, v);
+    load8(gain + c, gg);
+    u32x4 o;
+    o.x = pack_bf2(v[0] * inv * gg[0], v[1] * inv * gg[1]);
+    o.y = pack_bf2(v[2] * inv * gg[2], v[3] * inv * gg[3]);
+    o.z = pack_bf2(v[4] * inv * gg[4], v[5] * inv * gg[5]);
+    o.w = pack_bf2(v[6] * inv * gg[6], v[7] * inv * gg[7]);
+    *reinterpret_cast<u32x4*>(h + fm_index(m, c, d)) = o;
+  }
 }
 
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed,
@@ -55,16 +80,27 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, 
   const int m = blockIdx.x;
   // ids outside [0, V] (V = [MASK]) are clamped so a bad id can never read past the table
   const int tok = min(max(tokens[m], 0), vocab);
-  const uint16_t* er = embed + (size_t)tok * d;
   float* xr = x + (size_t)m * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float v = bf2f(er[c]);
-    if (temb) v += temb[c];
-    xr[c] = v;
-    ss += v * v;
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
+    const u32x4 e = ld16(embed + fm_index(tok, c, d));
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(e[j] << 16);
+      v[2 * j + 1] = __uint_as_float(e[j] & 0xffff0000u);
+    }
+    if (temb) {
+      float tt[8];
+      load8(temb + c, tt);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] += tt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+    store8(xr + c, v);
   }
-  norm_row(xr, gain, eps, h + (size_t)m * d, d, ss, red);
+  norm_row(xr, gain, eps, h, m, d, ss, red);
 }
 
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
@@ -80,8 +116,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const floa
   const int m = blockIdx.x;
   const float* xr = x + (size_t)m * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) ss += xr[c] * xr[c];
-  norm_row(xr, gain, eps, h + (size_t)m * d, d, ss, red);
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
+    float v[8];
+    load8(xr + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+  }
+  norm_row(xr, gain, eps, h, m, d, ss, red);
 }
 
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
@@ -105,14 +146,20 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* Y, 
   __syncthreads();
   float* xr = x + (size_t)m * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float y = 0.f;
-    for (int j = 0; j < k; ++j) y += wt[j] * Y[(size_t)slot[j] * d + c];
-    const float v = xr[c] + y;
-    xr[c] = v;
-    ss += v * v;
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
+    float v[8];
+    load8(xr + c, v);
+    for (int j = 0; j < k; ++j) {
+      float y[8];
+      load8(Y + (size_t)slot[j] * d + c, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += wt[j] * y[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    store8(xr + c, v);
   }
-  if (next_gain) norm_row(xr, next_gain, eps, h + (size_t)m * d, d, ss, red);
+  if (next_gain) norm_row(xr, next_gain, eps, h, m, d, ss, red);
 }
 
 void launch_combine(float* x, const float* Y, const float* wts, const int32_t* inv, int M, int k,

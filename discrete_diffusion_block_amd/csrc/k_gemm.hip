@@ -1,21 +1,20 @@
 // Dense bf16 GEMMs on MFMA (v_mfma_f32_16x16x32_bf16), fp32 accumulation.
 //
-// Every product here is y[m][n] = sum_k x[m][k] * w[n][k] with both operands
-// K-contiguous, so a lane's MFMA fragment (8 consecutive k of one row) is a
-// single 16-byte global load and no LDS staging is needed for the operands.
-// Weight rows go to the MFMA "A" side (16 rows per block), tokens to the "B"
-// side (16 tokens per block); a lane then holds 4 consecutive output features
-// of one token, which makes every epilogue a short vector store.
+// Every product is y[m][n] = sum_k x[m][k] * w[n][k].  Both operands live in
+// fragment-major layout (weights packed once, activations written that way by
+// the kernels that produce them), so every MFMA operand fragment is one
+// contiguous 1 KiB wave load straight into registers -- no LDS staging.
+// Weight rows sit on the MFMA A side (16 rows per block), tokens on the B side
+// (16 tokens per block); a lane then holds 4 consecutive output features of one
+// token, so each epilogue is a short vector store.
 //
 // dense_gemm: a workgroup of 4 waves owns one (WN x 16) feature x (WM x 16)
 // token tile and splits K between its waves (interleaved 64-wide k steps),
-// then reduces the four partial tiles through LDS in a fixed order.  That puts
-// 4x more loads in flight per tile, which is what batch-1 shapes (M = 256,
-// K = 2816, few tiles) need to hide HBM latency.
+// then reduces the four partial tiles through LDS in a fixed order.
 //
-// head_gemm: the tied LM head (N = 262144 rows of the embedding) — workgroup
-// tile 64 features x 256 tokens so the 256-token activation matrix is re-read
-// from L2 only once per 64 vocabulary rows.
+// head_gemm: the tied LM head (N = 262144 rows of the embedding) -- workgroup
+// tile 64 features x 256 tokens, so the activation tiles are re-read from L2
+// only once per 64 vocabulary rows.
 #include "dg_common.h"
 #include "dg_internal.h"
 
@@ -24,38 +23,19 @@ namespace dg {
 enum Epi { EPI_STORE_F32 = 0, EPI_ADD_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
 
 struct DenseArgs {
-  const uint16_t* x;
-  const uint16_t* w;
-  int M, N, K;      // N = weight rows addressable (loads clamp to N-1)
-  int nblk;         // 16-row blocks of the output feature space
+  const uint16_t* x;  // activations, fragment-major [M_pad][K]
+  const uint16_t* w;  // packed weights, fragment-major [N_pad][K]
+  int M, N, K;
+  int nblk;           // 16-row blocks of the packed weight
   float* yf;
   uint16_t* yb;
   int ldy;
-  int F;            // SwiGLU: gate rows [0,F), up rows [F,2F)
-  int hq, hd;       // QKV
+  int hq, hd;         // QKV
   KvLayer kv;
   PassGeom g;
   const float2* rope;
   uint16_t* q_out;
 };
-
-// Weight row feeding A-row r of 16-row block `blk`.
-template <int EPI>
-__device__ __forceinline__ int row_of(const DenseArgs& a, int blk, int r) {
-  if constexpr (EPI == EPI_SWIGLU) {
-    // block 2t = gate rows of features 16t.., block 2t+1 = the matching up rows
-    return (blk & 1) * a.F + (blk >> 1) * 16 + r;
-  } else if constexpr (EPI == EPI_QKV) {
-    // Within a head, block j covers rotary pairs 8j..8j+7 and their partners
-    // (i, i + hd/2), arranged so that lane group g ends up holding features
-    // {p, p+1, p+hd/2, p+1+hd/2} with p = 8j + 2g: RoPE is then lane-local.
-    const int per = a.hd >> 4;
-    const int head = blk / per, j = blk - head * per;
-    return head * a.hd + 8 * j + 2 * (r >> 2) + (r & 1) + ((r >> 1) & 1) * (a.hd >> 1);
-  } else {
-    return blk * 16 + r;
-  }
-}
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
@@ -78,43 +58,46 @@ __device__ __forceinline__ void epilogue(const DenseArgs& a, int blk0, int m, co
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
+    // packed block 2t = gate rows of features 16t.., block 2t+1 = the matching up rows
     const int f0 = (blk0 >> 1) * 16 + 4 * g;
     u32x2 o;
     o.x = pack_bf2(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1]);
     o.y = pack_bf2(silu(v[0][2]) * v[1][2], silu(v[0][3]) * v[1][3]);
-    *reinterpret_cast<u32x2*>(a.yb + (size_t)m * a.ldy + f0) = o;
-  } else {  // EPI_QKV
+    *reinterpret_cast<u32x2*>(a.yb + fm_index(m, f0, a.ldy)) = o;
+  } else {  // EPI_QKV: rows were packed so that lane group g holds features
+            // {p, p+1, p+hd/2, p+1+hd/2}, p = 8j + 2g, of head-local block j
     const int hd = a.hd, half = hd >> 1, per = hd >> 4;
     const int b = m / a.g.n, ii = m - b * a.g.n;
     const int pos = a.g.len[b] + ii;
+    const int npad = (a.g.n + 15) & ~15;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       const int blk = blk0 + i;
       if (blk >= a.nblk) continue;
       const int head = blk / per, j = blk - head * per;
       const int p = 8 * j + 2 * g;
-      float x0 = v[i][0], x1 = v[i][1], x2 = v[i][2], x3 = v[i][3];
+      const float x0 = v[i][0], x1 = v[i][1], x2 = v[i][2], x3 = v[i][3];
       if (head < a.hq + a.kv.hkv) {
         const float2 r0 = a.rope[(size_t)m * half + p], r1 = a.rope[(size_t)m * half + p + 1];
         const float y0 = x0 * r0.x - x2 * r0.y, y2 = x2 * r0.x + x0 * r0.y;
         const float y1 = x1 * r1.x - x3 * r1.y, y3 = x3 * r1.x + x1 * r1.y;
-        uint16_t* dst;
         if (head < a.hq) {
-          dst = a.q_out + ((size_t)m * a.hq + head) * hd;
+          uint16_t* base = a.q_out + ((size_t)b * a.hq + head) * (size_t)npad * hd;
+          *reinterpret_cast<uint32_t*>(base + fm_index(ii, p, hd)) = pack_bf2(y0, y1);
+          *reinterpret_cast<uint32_t*>(base + fm_index(ii, p + half, hd)) = pack_bf2(y2, y3);
         } else {
           const int kh = head - a.hq;
-          dst = a.kv.k + (((size_t)b * a.kv.hkv + kh) * a.kv.max_ctx + pos) * hd;
+          uint16_t* base = a.kv.k + ((size_t)b * a.kv.hkv + kh) * (size_t)a.kv.max_ctx * hd;
+          *reinterpret_cast<uint32_t*>(base + k_index(pos, p, hd)) = pack_bf2(y0, y1);
+          *reinterpret_cast<uint32_t*>(base + k_index(pos, p + half, hd)) = pack_bf2(y2, y3);
         }
-        *reinterpret_cast<uint32_t*>(dst + p) = pack_bf2(y0, y1);
-        *reinterpret_cast<uint32_t*>(dst + p + half) = pack_bf2(y2, y3);
       } else {
         const int vh = head - a.hq - a.kv.hkv;
-        uint16_t* base = a.kv.vt + ((size_t)b * a.kv.hkv + vh) * (size_t)hd * a.kv.max_ctx + pos;
-        const size_t ld = a.kv.max_ctx;
-        base[(size_t)p * ld] = f2bf(x0);
-        base[(size_t)(p + 1) * ld] = f2bf(x1);
-        base[(size_t)(p + half) * ld] = f2bf(x2);
-        base[(size_t)(p + half + 1) * ld] = f2bf(x3);
+        uint16_t* base = a.kv.vt + ((size_t)b * a.kv.hkv + vh) * (size_t)hd * a.kv.max_ctx;
+        base[v_index(pos, p, hd)] = f2bf(x0);
+        base[v_index(pos, p + 1, hd)] = f2bf(x1);
+        base[v_index(pos, p + half, hd)] = f2bf(x2);
+        base[v_index(pos, p + half + 1, hd)] = f2bf(x3);
       }
     }
   }
@@ -126,21 +109,16 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int blk0 = blockIdx.x * WN;
-  const int m0 = blockIdx.y * 16 * WM;
+  const int mb0 = blockIdx.y * WM;
 
+  // fragment tiles (rb, kb): rb clamped to the last real block (dropped in the epilogue)
   const uint16_t* wp[WN];
   const uint16_t* xp[WM];
+  const int mblocks = (a.M + 15) >> 4;
 #pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    const int blk = min(blk0 + i, a.nblk - 1);
-    const int row = min(row_of<EPI>(a, blk, r), a.N - 1);
-    wp[i] = a.w + (size_t)row * a.K + 8 * g;
-  }
+  for (int i = 0; i < WN; ++i) wp[i] = a.w + fm_tile(min(blk0 + i, a.nblk - 1), 0, a.K, lane);
 #pragma unroll
-  for (int j = 0; j < WM; ++j) {
-    const int m = min(m0 + 16 * j + r, a.M - 1);
-    xp[j] = a.x + (size_t)m * a.K + 8 * g;
-  }
+  for (int j = 0; j < WM; ++j) xp[j] = a.x + fm_tile(min(mb0 + j, mblocks - 1), 0, a.K, lane);
 
   f32x4 acc[WN][WM];
 #pragma unroll
@@ -150,16 +128,16 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
 
   u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2], A2[WN][2], B2[WM][2];
   auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
-    const int k = it * 64;
+    const int k = it * 1024;  // two 512-element k tiles per 64-wide step
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      A[i][0] = ld16(wp[i] + k);
-      A[i][1] = ld16(wp[i] + k + 32);
+      A[i][0] = ld16_stream(wp[i] + k);
+      A[i][1] = ld16_stream(wp[i] + k + 512);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
       B[j][0] = ld16(xp[j] + k);
-      B[j][1] = ld16(xp[j] + k + 32);
+      B[j][1] = ld16(xp[j] + k + 512);
     }
   };
   auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
@@ -194,7 +172,7 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
       s += red[((3 * WN + i) * WM + j) * 64 + lane];
       v[i] = s;
     }
-    epilogue<EPI, WN>(a, blk0, m0 + 16 * j + r, v, g);
+    epilogue<EPI, WN>(a, blk0, (mb0 + j) * 16 + r, v, g);
   }
 }
 
@@ -231,7 +209,7 @@ void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int
 void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,
                         uint16_t* a_out, hipStream_t s) {
   DenseArgs a{};
-  a.x = h; a.w = w_gate_up; a.M = M; a.K = K; a.N = 2 * F; a.F = F;
+  a.x = h; a.w = w_gate_up; a.M = M; a.K = K; a.N = 2 * F;
   a.nblk = 2 * (F / 16);
   a.yb = a_out; a.ldy = F;
   run_dense<2, 4, EPI_SWIGLU>(a, s);
@@ -246,36 +224,35 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int wn = wv & 1, wm = wv >> 1;
-  const int n_base = blockIdx.x * 32 * WN + wn * 16 * WN;
-  const int m_base = blockIdx.y * 32 * WM + wm * 16 * WM;
+  const int nb0 = blockIdx.x * 2 * WN + wn * WN;      // 16-row blocks of the head
+  const int mb0 = blockIdx.y * 2 * WM + wm * WM;      // 16-token blocks
+  const int nblocks = (N + 15) >> 4, mblocks = (M + 15) >> 4;
+  if (mb0 >= mblocks) return;
   const uint16_t* wp[WN];
   const uint16_t* xp[WM];
 #pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = w + (size_t)min(n_base + 16 * i + r, N - 1) * K + 8 * g;
+  for (int i = 0; i < WN; ++i) wp[i] = w + fm_tile(min(nb0 + i, nblocks - 1), 0, K, lane);
 #pragma unroll
-  for (int j = 0; j < WM; ++j) xp[j] = x + (size_t)min(m_base + 16 * j + r, M - 1) * K + 8 * g;
+  for (int j = 0; j < WM; ++j) xp[j] = x + fm_tile(min(mb0 + j, mblocks - 1), 0, K, lane);
 
   f32x4 acc[WN][WM];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (m_base >= M) return;
 
-  // all token blocks of a workgroup tile are loaded (rows past M are clamped duplicates)
-  // so the k loop stays branch-free
   u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
   auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
-    const int k = it * 64;
+    const int k = it * 1024;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       A[i][0] = ld16_stream(wp[i] + k);
-      A[i][1] = ld16_stream(wp[i] + k + 32);
+      A[i][1] = ld16_stream(wp[i] + k + 512);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
       B[j][0] = ld16(xp[j] + k);
-      B[j][1] = ld16(xp[j] + k + 32);
+      B[j][1] = ld16(xp[j] + k + 512);
     }
   };
   auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
@@ -291,11 +268,11 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
             [&] { mma(A0, B0); }, [&] { mma(A1, B1); });
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
-    const int m = m_base + 16 * j + r;
+    const int m = (mb0 + j) * 16 + r;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      const int n0 = n_base + 16 * i + 4 * g;
+      const int n0 = (nb0 + i) * 16 + 4 * g;
       uint16_t* dst = y + (size_t)m * N + n0;
       if (n0 + 3 < N) {
         u32x2 o;

@@ -78,11 +78,14 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 // ---------------------------------------------------------------- permutation
 
 // Stable counting sort of the M*k assignments (a = m*k + j) by expert, in one
-// 1024-thread workgroup: per-expert counts, exclusive offsets, then slots in
-// assignment order within each expert.  perm[slot] = token, inv[a] = slot.
+// 1024-thread workgroup.  Expert e owns the padded slot range
+// [poff[e], poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered
+// rows start on a fragment-tile boundary; slots keep assignment order within an
+// expert.  perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
+// (expert, first slot) of every 32-token group.
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
-                                                     int E, int32_t* __restrict__ cnt,
-                                                     int32_t* __restrict__ offs,
+                                                     int E, int P, int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ poff,
                                                      int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv,
                                                      int2* __restrict__ items,
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
   __shared__ int wcnt[16][256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int e = tid; e < E; e += blockDim.x) hist[e] = 0;
+  for (int i = tid; i < P; i += blockDim.x) perm[i] = -1;
   __syncthreads();
   for (int a = tid; a < A; a += blockDim.x) atomicAdd(&hist[ids[a]], 1);
   __syncthreads();
@@ -100,14 +104,13 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
     int run = 0, ni = 0;
     for (int e = 0; e < E; ++e) {
       base[e] = run;
-      offs[e] = run;
+      poff[e] = run;
       cnt[e] = hist[e];
       if (cnt_log) cnt_log[e] = hist[e];
-      run += hist[e];
-      // work items of the grouped GEMMs: (expert, first slot) per kMoeGroup-token group
       for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[ni++] = make_int2(e, t0);
+      run += (hist[e] + 15) & ~15;
     }
-    offs[E] = run;
+    poff[E] = run;
     *n_items = ni;
   }
   __syncthreads();
@@ -143,11 +146,33 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
   }
 }
 
-void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* offs,
+void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
                   hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, cnt, offs, perm, inv,
-                     items, n_items, cnt_log);
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, moe_max_slots(M, k, E),
+                     cnt, poff, perm, inv, items, n_items, cnt_log);
+}
+
+// Xg[slot] = h[perm[slot]] (zeros on padding), both fragment-major with K = d.
+// One wave per padded slot; a lane moves 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ h,
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ poff, int E, int P,
+                                                     int d, uint16_t* __restrict__ xg) {
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= P || slot >= poff[E]) return;
+  const int tok = perm[slot];
+  for (int c = 8 * lane; c < d; c += 8 * 64) {
+    const u32x4 v = tok >= 0 ? ld16(h + fm_index(tok, c, d)) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(xg + fm_index(slot, c, d)) = v;
+  }
+}
+
+void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, int M, int k, int E,
+                   int d, uint16_t* xg, hipStream_t s) {
+  const int P = moe_max_slots(M, k, E);
+  hipLaunchKernelGGL(gather_kernel, dim3((P + 3) / 4), dim3(256), 0, s, h, perm, poff, E, P, d, xg);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
@@ -165,23 +190,25 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)
 // Lane group g reads bytes [64q + 16g, +16) of each 128-byte step q, so the 4
 // lanes of a row read 64 contiguous bytes per instruction.
 
-// gate/up: ag = x W_g^T, au = x W_u^T over this wave's k steps.
+// gate/up: ag = x W_g^T, au = x W_u^T over this wave's k steps.  Every operand
+// pointer addresses a fragment tile (row block, k block 0) plus the lane slot;
+// a 64-wide k step covers two consecutive 1 KiB tiles.
 template <int NT>
 __device__ __forceinline__ void gate_up_partial(const uint16_t* wg, const uint16_t* wu,
                                                 const uint16_t* const (&xp)[NT], int nk, int w,
                                                 f32x4 (&ag)[NT], f32x4 (&au)[NT]) {
   u32x4 Ga[2], Ua[2], Xa[NT][2], Gb[2], Ub[2], Xb[NT][2], Gc[2], Uc[2], Xc[NT][2];
   auto ld = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2], int step) {
-    const int k = (w + 4 * step) * 64;
+    const int k = (w + 4 * step) * 1024;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      G[q] = ld16_stream(wg + k + 32 * q);
-      U[q] = ld16_stream(wu + k + 32 * q);
+      G[q] = ld16_stream(wg + k + 512 * q);
+      U[q] = ld16_stream(wu + k + 512 * q);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 32 * q);
+      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 512 * q);
   };
   auto mm = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2]) {
 #pragma unroll
@@ -200,13 +227,13 @@ __device__ __forceinline__ void gate_up_partial(const uint16_t* wg, const uint16
 
 template <int NT>
 __device__ __forceinline__ void gate_up_item(const uint16_t* wg, const uint16_t* wu,
-                                             const uint16_t* h, const int32_t* perm, int off,
-                                             int t0, int ne, int F, int fb, int d, int lane,
-                                             int w, uint16_t* A, f32x4 (*red)[2][2][64]) {
+                                             const uint16_t* xg, int slot0, int t0, int ne, int F,
+                                             int fb, int d, int lane, int w, uint16_t* A,
+                                             f32x4 (*red)[2][2][64]) {
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* xp[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = h + (size_t)perm[off + min(t0 + 16 * j + r, ne - 1)] * d + 8 * g;
+  for (int j = 0; j < NT; ++j) xp[j] = xg + fm_tile((slot0 >> 4) + j, 0, d, lane);
   f32x4 ag[NT], au[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -226,25 +253,25 @@ __device__ __forceinline__ void gate_up_item(const uint16_t* wg, const uint16_t*
       u32x2 o;
       o.x = pack_bf2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
       o.y = pack_bf2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
-      *reinterpret_cast<u32x2*>(A + (size_t)(off + t) * F + fb * 16 + 4 * g) = o;
+      *reinterpret_cast<u32x2*>(A + fm_index(slot0 + 16 * j + r, fb * 16 + 4 * g, F)) = o;
     }
   }
 }
 
 // A[slot][f] = silu(x W_g[e][f]^T) * (x W_u[e][f]^T) for every slot of expert e,
-// x = h[perm[slot]].  Workgroup = (work item, 16 features); items vary fastest.
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ h,
+// x = Xg[slot].  Workgroup = (work item, 16 features); items vary fastest.
+// The packed expert weight holds gate block f and up block f as row blocks
+// 2f and 2f + 1.
+__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ xg,
                                                           const uint16_t* __restrict__ wgu,
                                                           const int32_t* __restrict__ cnt,
-                                                          const int32_t* __restrict__ offs,
-                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ poff,
                                                           const int2* __restrict__ items,
                                                           const int32_t* __restrict__ n_items,
                                                           int max_items, int F, int d,
                                                           uint16_t* __restrict__ A) {
   __shared__ f32x4 red[4][2][2][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
   // logical block = fb * max_items + item (items fastest), spread so that the
   // groups of one expert -- which read the same weight tile -- share an XCD
   const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -252,24 +279,25 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
   if (fb >= (F >> 4) || item >= *n_items) return;    // uniform over the workgroup
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
-  const int ne = cnt[e], off = offs[e];
-  const uint16_t* wg = wgu + ((size_t)e * 2 * F + fb * 16 + r) * d + 8 * g;
-  const uint16_t* wu = wg + (size_t)F * d;
+  const int ne = cnt[e], slot0 = poff[e] + t0;
+  const size_t wmat = (size_t)e * 2 * F * d;
+  const uint16_t* wg = wgu + wmat + fm_tile(2 * fb, 0, d, lane);
+  const uint16_t* wu = wgu + wmat + fm_tile(2 * fb + 1, 0, d, lane);
   if (ne - t0 <= 16)
-    gate_up_item<1>(wg, wu, h, perm, off, t0, ne, F, fb, d, lane, w, A, red);
+    gate_up_item<1>(wg, wu, xg, slot0, t0, ne, F, fb, d, lane, w, A, red);
   else
-    gate_up_item<2>(wg, wu, h, perm, off, t0, ne, F, fb, d, lane, w, A, red);
+    gate_up_item<2>(wg, wu, xg, slot0, t0, ne, F, fb, d, lane, w, A, red);
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T for 16*WN output rows.
 template <int NT, int WN>
 __device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const uint16_t* A,
-                                          int off, int t0, int ne, int F, int d, int n0, int lane,
+                                          int slot0, int t0, int ne, int F, int d, int n0, int lane,
                                           int w, float* Y, f32x4 (*red)[2][2][64]) {
   const int r = lane & 15, g = lane >> 4;
   const uint16_t* xp[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = A + (size_t)(off + min(t0 + 16 * j + r, ne - 1)) * F + 8 * g;
+  for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
   f32x4 acc[WN][NT];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
@@ -277,15 +305,15 @@ __device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 Wa[WN][2], Xa[NT][2], Wb[WN][2], Xb[NT][2], Wc[WN][2], Xc[NT][2];
   auto ld = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2], int step) {
-    const int k = (w + 4 * step) * 64;
+    const int k = (w + 4 * step) * 1024;
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) W[i][q] = ld16_stream(wp[i] + k + 32 * q);
+      for (int q = 0; q < 2; ++q) W[i][q] = ld16_stream(wp[i] + k + 512 * q);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 32 * q);
+      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 512 * q);
   };
   auto mm = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2]) {
 #pragma unroll
@@ -311,7 +339,7 @@ __device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const
     const int t = t0 + 16 * j + r;
     if (t < ne) {
       const f32x4 v = red[0][i][j][lane] + red[1][i][j][lane] + red[2][i][j][lane] + red[3][i][j][lane];
-      *reinterpret_cast<f32x4*>(Y + (size_t)(off + t) * d + n0 + 16 * i + 4 * g) = v;
+      *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * i + 4 * g) = v;
     }
   }
 }
@@ -320,7 +348,7 @@ template <int WN>
 __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ wd,
                                                        const int32_t* __restrict__ cnt,
-                                                       const int32_t* __restrict__ offs,
+                                                       const int32_t* __restrict__ poff,
                                                        const int2* __restrict__ items,
                                                        const int32_t* __restrict__ n_items,
                                                        int max_items, int F, int d,
@@ -328,40 +356,39 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   static_assert(WN <= 2, "LDS tile holds at most 2 row blocks");
   __shared__ f32x4 red[4][2][2][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
   const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
   const int nb = lb / max_items, item = lb - nb * max_items;
   if (nb >= d / (16 * WN) || item >= *n_items) return;
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
-  const int ne = cnt[e], off = offs[e];
+  const int ne = cnt[e], slot0 = poff[e] + t0;
   const int n0 = nb * 16 * WN;
   const uint16_t* wp[WN];
 #pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = wd + ((size_t)e * d + n0 + 16 * i + r) * F + 8 * g;
+  for (int i = 0; i < WN; ++i) wp[i] = wd + (size_t)e * d * F + fm_tile((n0 >> 4) + i, 0, F, lane);
   if (ne - t0 <= 16)
-    down_item<1, WN>(wp, A, off, t0, ne, F, d, n0, lane, w, Y, red);
+    down_item<1, WN>(wp, A, slot0, t0, ne, F, d, n0, lane, w, Y, red);
   else
-    down_item<2, WN>(wp, A, off, t0, ne, F, d, n0, lane, w, Y, red);
+    down_item<2, WN>(wp, A, slot0, t0, ne, F, d, n0, lane, w, Y, red);
 }
 
 int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
+int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
 
-void launch_moe_gate_up(const uint16_t* h, const uint16_t* w_gate_up, const int32_t* cnt,
-                        const int32_t* offs, const int32_t* perm, const int2* items,
-                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
-                        hipStream_t s) {
+void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
+                        const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
+                        int F, int d, uint16_t* a, hipStream_t s) {
   const int blocks = (max_items * (F / 16) + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, h, w_gate_up, cnt, offs, perm,
-                     items, n_items, max_items, F, d, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, xg, w_gate_up, cnt, poff, items,
+                     n_items, max_items, F, d, a);
 }
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
-                     const int32_t* offs, const int2* items, const int32_t* n_items, int max_items,
+                     const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
   constexpr int WN = 2;
   const int blocks = (max_items * (d / (16 * WN)) + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL((moe_down_kernel<WN>), dim3(blocks), dim3(256), 0, s, a, w_down, cnt, offs, items,
+  hipLaunchKernelGGL((moe_down_kernel<WN>), dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
                      n_items, max_items, F, d, Y);
 }
 

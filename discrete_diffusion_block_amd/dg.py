@@ -23,7 +23,8 @@ MAX_BATCH = 64
 
 KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
-                "sample_pass1", "sample_select", "fill"]
+                "sample_pass1", "sample_select", "fill", "gather"]
+PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
 
 STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE", -3: "DG_ERR_WORKSPACE",
           -4: "DG_ERR_KV_CAPACITY", -5: "DG_ERR_HIP", -6: "DG_ERR_UNSUPPORTED"}
@@ -74,6 +75,8 @@ def lib():
             "dg_sample_workspace_size": [i32, i32, i32, C.POINTER(sz)],
             "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
+            "dg_packed_elems": [i32, i32, C.POINTER(sz)],
+            "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
             "dg_profile_begin": [vp, i32],
             "dg_profile_end": [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
             "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
@@ -177,6 +180,58 @@ def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: floa
                                    _stream(stream)))
 
 
+def dg_packed_elems(rows: int, cols: int) -> int:
+    n = C.c_size_t()
+    _check(lib().dg_packed_elems(rows, cols, C.byref(n)))
+    return n.value
+
+
+def dg_pack_weight(kind: int, src: torch.Tensor, dst: torch.Tensor, n_mats: int, rows: int, cols: int,
+                   param: int = 0, stream=None):
+    _check(lib().dg_pack_weight(kind, _p(src), _p(dst), n_mats, rows, cols, param, _stream(stream)))
+
+
+def pack(t: torch.Tensor, kind: int = PACK_PLAIN, param: int = 0) -> torch.Tensor:
+    """Fragment-major copy of the bf16 matrices in t (shape [..., rows, cols])."""
+    rows, cols = t.shape[-2], t.shape[-1]
+    n_mats = t.numel() // (rows * cols)
+    dst = torch.empty(n_mats * dg_packed_elems(rows, cols), dtype=torch.bfloat16, device=t.device)
+    dg_pack_weight(kind, t.contiguous(), dst, n_mats, rows, cols, param)
+    return dst
+
+
+def pack_weights(cfg: ModelConfig, w: dict, free_source: bool = False) -> dict:
+    """Engine-layout copy of synth.make_weights output (device tensors)."""
+    out = {"embed": pack(w["embed"]), "final_norm": w["final_norm"], "layers": []}
+    if free_source:
+        w["embed"] = None
+    for l, lw in enumerate(w["layers"]):
+        out["layers"].append({
+            "attn_norm": lw["attn_norm"], "ffn_norm": lw["ffn_norm"],
+            "w_qkv": pack(lw["w_qkv"], PACK_QKV, cfg.head_dim),
+            "w_o": pack(lw["w_o"]),
+            "w_router": pack(lw["w_router"]),
+            "w_gate_up": pack(lw["w_gate_up"], PACK_GATE_UP, cfg.expert_ffn),
+            "w_down": pack(lw["w_down"]),
+            "ws_gate_up": pack(lw["ws_gate_up"], PACK_GATE_UP, cfg.shared_ffn),
+            "ws_down": pack(lw["ws_down"]),
+        })
+        if free_source:
+            w["layers"][l] = None
+    return out
+
+
+def _k_index(p: torch.Tensor, c: torch.Tensor, hd: int) -> torch.Tensor:
+    pp = p & 31
+    bb = (pp >> 2) & 1
+    r = ((pp >> 3) << 2) | (pp & 3)
+    return ((((p >> 5) * 2 + bb) * (hd >> 5) + (c >> 5)) << 9) + (((((c & 31) >> 3) << 4) + r) << 3) + (c & 7)
+
+
+def _v_index(p: torch.Tensor, c: torch.Tensor, hd: int) -> torch.Tensor:
+    return ((((p >> 5) * (hd >> 4)) + (c >> 4)) << 9) + (((((p & 31) >> 3) << 4) + (c & 15)) << 3) + (p & 7)
+
+
 def dg_profile_begin(ctx, capacity: int):
     _check(lib().dg_profile_begin(ctx, capacity))
 
@@ -208,10 +263,9 @@ def dg_test_eb_select(entropy: torch.Tensor, argmax: torch.Tensor, canvas: torch
                                    int(bool(commit_all)), _p(n_masked), _stream(stream)))
 
 
-def dg_test_gemm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None):
-    M, K = x.shape
-    N = w.shape[0]
-    _check(lib().dg_test_gemm(_p(x), _p(w), _p(y), M, N, K, _stream(stream)))
+def dg_test_gemm(x_packed: torch.Tensor, w_packed: torch.Tensor, y: torch.Tensor, M: int, N: int,
+                 K: int, stream=None):
+    _check(lib().dg_test_gemm(_p(x_packed), _p(w_packed), _p(y), M, N, K, _stream(stream)))
 
 
 # ------------------------------------------------------------------ convenience engine
@@ -225,9 +279,10 @@ class Engine:
     """
 
     def __init__(self, cfg: ModelConfig, weights: dict, max_batch: int = 1, max_ctx: int = 2048,
-                 device: str = "cuda"):
+                 device: str = "cuda", packed: bool = False, free_source: bool = False):
         self.cfg = cfg
-        self.weights = weights
+        self.weights = weights if packed else pack_weights(cfg, weights, free_source)
+        weights = self.weights
         self.ccfg = make_config(cfg, max_batch, max_ctx)
         n = cfg.n_layers
         self._layers = (LayerWeights * n)()
@@ -265,13 +320,16 @@ class Engine:
             self.kv.len[b] = 0
 
     def kv_view(self):
-        """(k, v) as bf16 tensors [L][B][Hkv][max_ctx][hd] and [L][B][Hkv][hd][max_ctx]."""
+        """(k, v) decoded from the cache layout to bf16 [L][B][Hkv][max_ctx][hd] each."""
         c = self.cfg
-        shp = (c.n_layers, self.max_batch, c.n_kv_heads, self.ccfg.max_ctx, c.head_dim)
-        k = self.k_cache.view(torch.bfloat16).view(shp)
-        v = self.v_cache.view(torch.bfloat16).view(c.n_layers, self.max_batch, c.n_kv_heads,
-                                                    c.head_dim, self.ccfg.max_ctx)
-        return k, v
+        T, hd = self.ccfg.max_ctx, c.head_dim
+        p = torch.arange(T, device=self.k_cache.device).view(T, 1)
+        d = torch.arange(hd, device=self.k_cache.device).view(1, hd)
+        blocks = (c.n_layers, self.max_batch, c.n_kv_heads, T * hd)
+        k = self.k_cache.view(torch.bfloat16).view(blocks)[..., _k_index(p, d, hd).reshape(-1)]
+        v = self.v_cache.view(torch.bfloat16).view(blocks)[..., _v_index(p, d, hd).reshape(-1)]
+        shp = (c.n_layers, self.max_batch, c.n_kv_heads, T, hd)
+        return k.view(shp), v.view(shp)
 
     def prefill_kv(self, tokens: torch.Tensor, stream=None):
         dg_prefill_kv(self.ctx, self.kv, tokens, self.ws, stream)

@@ -60,29 +60,54 @@ typedef struct dg_config {
   float rms_eps, rope_theta;
 } dg_config;
 
+/* Weight packing.  The engine reads every bf16 weight matrix in a
+ * fragment-major layout: 16-row x 32-column tiles of 1 KiB, row-block-major,
+ * the 8 elements (row l%16, columns 8*(l/16)..+7) of a tile at element offset
+ * 8*l -- the operand fragment of one MFMA for lane l -- so each fragment is one
+ * contiguous wave load.  Rows are padded to a multiple of 16 (with zeros).
+ * dg_pack_weight converts n_mats consecutive row-major [rows][cols] matrices
+ * into that layout (dst holds n_mats * dg_packed_elems(rows, cols) elements):
+ *   DG_PACK_PLAIN    rows in order;
+ *   DG_PACK_QKV      param = head_dim: within each head the rows are ordered so
+ *                    that each lane receives the rotary pairs (i, i + hd/2);
+ *   DG_PACK_GATE_UP  param = F, rows = 2F: 16-row block 2t = gate rows 16t..,
+ *                    block 2t+1 = up rows F+16t..
+ * The source is not modified; the call only enqueues a kernel on `stream`. */
+typedef enum dg_pack_kind { DG_PACK_PLAIN = 0, DG_PACK_QKV = 1, DG_PACK_GATE_UP = 2 } dg_pack_kind;
+dg_status dg_packed_elems(int rows, int cols, size_t* elems);
+dg_status dg_pack_weight(int kind, const uint16_t* d_src, uint16_t* d_dst, int n_mats, int rows,
+                         int cols, int param, void* stream);
+
 /* Weights of one layer (device pointers, borrowed for the ctx's lifetime).
- * bf16 unless noted; all row-major. */
+ * Norm gains are fp32 [d]; every matrix is bf16, packed with dg_pack_weight
+ * from the row-major shape given here. */
 typedef struct dg_layer_weights {
   const float* attn_norm;      /* fp32 [d] RMSNorm gain before attention */
-  const uint16_t* w_qkv;       /* [(Hq + 2 Hkv) * hd][d]: q heads, then k heads, then v heads */
-  const uint16_t* w_o;         /* [d][Hq * hd] */
+  const uint16_t* w_qkv;       /* QKV-packed [(Hq + 2 Hkv) * hd][d]: q heads, k heads, v heads */
+  const uint16_t* w_o;         /* plain-packed [d][Hq * hd] */
   const float* ffn_norm;       /* fp32 [d] RMSNorm gain before the MoE block */
-  const uint16_t* w_router;    /* [E][d] */
-  const uint16_t* w_gate_up;   /* [E][2F][d]: per expert F gate rows, then F up rows */
-  const uint16_t* w_down;      /* [E][d][F] */
-  const uint16_t* ws_gate_up;  /* shared expert [2Fs][d] */
-  const uint16_t* ws_down;     /* shared expert [d][Fs] */
+  const uint16_t* w_router;    /* plain-packed [E][d] (rows padded to 16) */
+  const uint16_t* w_gate_up;   /* GATE_UP-packed, E matrices [2F][d] (F gate rows, F up rows) */
+  const uint16_t* w_down;      /* plain-packed, E matrices [d][F] */
+  const uint16_t* ws_gate_up;  /* shared expert, GATE_UP-packed [2Fs][d] */
+  const uint16_t* ws_down;     /* shared expert, plain-packed [d][Fs] */
 } dg_layer_weights;
 
 typedef struct dg_weights {
-  const uint16_t* embed;              /* [V+1][d]; tied: logits use rows 0..V-1 */
+  const uint16_t* embed;              /* plain-packed [V+1][d]; tied: logits use rows 0..V-1 */
   const float* final_norm;            /* fp32 [d] */
   const dg_layer_weights* layers;     /* HOST array of n_layers entries (copied by dg_create) */
 } dg_weights;
 
-/* KV cache (caller-owned device buffers, zero-filled before first use).
- *   k: bf16 [n_layers][max_batch][n_kv_heads][max_ctx][head_dim]  (post-RoPE keys)
- *   v: bf16 [n_layers][max_batch][n_kv_heads][head_dim][max_ctx]  (values, transposed)
+/* KV cache (caller-owned device buffers, zero-filled before first use), each
+ * n_layers * max_batch * n_kv_heads blocks of max_ctx * head_dim bf16, in the
+ * block order [layer][sequence][kv head].  Inside a block:
+ *   k (post-RoPE keys): 32-position chunks, each two 16-row tiles per 32-wide
+ *     hd slice; position p of a chunk is row 4*(p/8) + p%4 of tile (p/4)%2,
+ *     element (row r, dim c) of a tile at 8*(16*((c%32)/8) + r) + c%8;
+ *   v (values, transposed): per 32-position chunk and 16-wide hd slice a tile
+ *     with element (position p, dim c) at 8*(16*((p%32)/8) + c%16) + p%8.
+ * (Both are the MFMA operand fragments of the attention kernel.)
  * len[b] is the host-side count of committed positions of sequence b; the
  * library advances it when it enqueues a prefill/append, so no device read-back
  * is ever needed.  Slots len[b] .. len[b]+C-1 also serve as scratch for the
@@ -163,7 +188,8 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
 typedef enum dg_kernel_kind {
   DG_K_PREP = 0, DG_K_EMBED, DG_K_QKV, DG_K_ATTENTION, DG_K_O_PROJ, DG_K_NORM, DG_K_ROUTER,
   DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
-  DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL, DG_K_COUNT
+  DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL, DG_K_GATHER,
+  DG_K_COUNT
 } dg_kernel_kind;
 
 /* Start bracketing every kernel launch made through ctx (dg_prefill_kv,
@@ -191,7 +217,8 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
                             int batch, int canvas, int vocab, float gamma, int commit_all,
                             int32_t* d_n_masked, void* stream);
 
-/* Plain bf16 GEMM y[M][N] = x[M][K] . w[N][K]^T, fp32 out (K % 64 == 0). */
+/* bf16 GEMM y[M][N] = x[M][K] . w[N][K]^T, fp32 row-major out (K % 64 == 0);
+ * x and w both plain-packed (fragment-major, rows padded to 16). */
 dg_status dg_test_gemm(const uint16_t* d_x, const uint16_t* d_w, float* d_y, int M, int N, int K,
                        void* stream);
 

@@ -29,7 +29,7 @@ def test_gemm_matches_fp64(M, N, K):
     print(f"gemm M={M} N={N} K={K}", flush=True)
     x, w = _bf16((M, K), 1), _bf16((N, K), 2, 0.05)
     y = torch.full((M, N), float("nan"), device="cuda")
-    dg.dg_test_gemm(x.cuda(), w.cuda(), y)
+    dg.dg_test_gemm(dg.pack(x.cuda()), dg.pack(w.cuda()), y, M, N, K)
     torch.cuda.synchronize()
     xd, wd = to_np_bf16(x), to_np_bf16(w)
     ref = xd @ wd.T

@@ -42,7 +42,7 @@ def _kv_compare(eng, kv_ref, lo, hi, b=0, skip=None):
     k, v = eng.kv_view()
     for l in range(eng.cfg.n_layers):
         kg = k[l, b, :, lo:hi, :].float().cpu().numpy().transpose(1, 0, 2)   # [pos][h][hd]
-        vg = v[l, b, :, :, lo:hi].float().cpu().numpy().transpose(2, 0, 1)
+        vg = v[l, b, :, lo:hi, :].float().cpu().numpy().transpose(1, 0, 2)
         kr, vr = kv_ref.k[l][b][lo:hi], kv_ref.v[l][b][lo:hi]
         keep = np.ones(hi - lo, bool)
         if skip is not None:
@@ -178,7 +178,7 @@ def test_generate_block_equals_stepwise_and_appends(tiny):
     k1, v1 = eng.kv_view()
     k2, v2 = ref.kv_view()
     assert torch.equal(k1[:, :, :, :64 + C], k2[:, :, :, :64 + C])
-    assert torch.equal(v1[..., :64 + C], v2[..., :64 + C])
+    assert torch.equal(v1[:, :, :, :64 + C], v2[:, :, :, :64 + C])
     eng.close(); ref.close()
 
 
