@@ -213,7 +213,9 @@ def main():
     used = [sum(1 for c in row if c > 0) for row in counts]
 
     # ---- roofline of the dominant kernel kind
-    dom = max((k for k in prof if prof[k][1]), key=lambda k: prof[k][0])
+    # the dominant kernel among those bound by HBM or MFMA (the row kernels are latency-bound)
+    dom = max((k for k in prof if prof[k][1] and algorithmic_work(k, cfg, C, counts)[0]),
+              key=lambda k: prof[k][0])
     bound, unit, amount = algorithmic_work(dom, cfg, C, counts)
     avg_ms = prof[dom][0] / prof[dom][1]
     roofline = None

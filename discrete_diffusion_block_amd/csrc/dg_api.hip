@@ -549,6 +549,19 @@ dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_
   return check_launch("router top-k");
 }
 
+dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
+                        int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
+                        int32_t* d_items, int32_t* d_n_items, void* stream) {
+  if (!d_r || !d_ids || !d_w || !d_cnt || !d_poff || !d_perm || !d_inv || !d_items || !d_n_items ||
+      M < 1 || E < 4 || E > 256 || k < 1 || k > 16 || k > E)
+    return fail(DG_ERR_INVALID_ARG, "bad routing arguments");
+  hipStream_t s = (hipStream_t)stream;
+  launch_topk(d_r, M, E, k, d_ids, d_w, s);
+  launch_route(d_ids, M, k, E, d_cnt, d_poff, d_perm, d_inv, reinterpret_cast<int2*>(d_items), d_n_items,
+               nullptr, s);
+  return check_launch("route");
+}
+
 dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int32_t* d_canvas,
                             int batch, int canvas, int vocab, float gamma, int commit_all,
                             int32_t* d_n_masked, void* stream) {

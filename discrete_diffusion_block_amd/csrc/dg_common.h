@@ -156,6 +156,22 @@ __host__ __device__ __forceinline__ size_t v_index(int p, int c, int hd) {
          ((size_t)((((p & 31) >> 3) << 4) + (c & 15)) << 3) + (p & 7);
 }
 
+// Work-unit schedule for the grouped expert GEMMs: n_items work items x nfb
+// feature tiles.  XCD x (= blockIdx.x % kXcd) owns the contiguous item range
+// [x*n/kXcd, (x+1)*n/kXcd) and sweeps it feature-tile-major, so the token rows
+// of its items stay in its L2 across the sweep and consecutive workgroups
+// (same feature tile, neighbouring items of one expert) share weight tiles.
+// Returns false for blocks beyond this XCD's share.
+__device__ __forceinline__ bool xcd_item_schedule(int n_items, int nfb, int* item, int* fb) {
+  const int x = blockIdx.x % kXcd, rank = blockIdx.x / kXcd;
+  const int i0 = (int)((long)x * n_items / kXcd), i1 = (int)((long)(x + 1) * n_items / kXcd);
+  const int nx = i1 - i0;
+  if (nx <= 0 || rank >= nx * nfb) return false;
+  *fb = rank / nx;
+  *item = i0 + (rank - *fb * nx);
+  return true;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -78,17 +78,29 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
-  for (int ch = w; ch < nchunk; ch += 4) {
-    const int kc = kc0 + 32 * ch;
+  // One 32-key chunk: K fragments (2 blocks x NC k tiles) and V fragments (NB
+  // hd blocks), prefetched one chunk ahead through a two-stage pipeline.
+  u32x4 Ka[2][NC], Va[NB], Kb[2][NC], Vb[NB];
+  int kca = 0, kcb = 0;
+  auto load = [&](u32x4 (&K)[2][NC], u32x4 (&Vt)[NB], int& kcs, int step) {
+    kcs = kc0 + 32 * (w + 4 * step);
+    const uint16_t* kp = kbase + ((size_t)(kcs >> 5) * 2 * NC << 9) + 8 * lane;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) K[bb][c] = ld16(kp + ((bb * NC + c) << 9));
+    const uint16_t* vp = vbase + ((size_t)(kcs >> 5) * NB << 9) + 8 * lane;
+#pragma unroll
+    for (int hb = 0; hb < NB; ++hb) Vt[hb] = ld16(vp + (hb << 9));
+  };
+  auto process = [&](const u32x4 (&K)[2][NC], const u32x4 (&Vt)[NB], int kc) {
     // S^T blocks: block bb row rr <-> key kc + 8*(rr>>2) + 4*bb + (rr&3)
     f32x4 s[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      // tile (chunk, bb, c) of the key cache: one contiguous 1 KiB fragment
-      const uint16_t* kp = kbase + ((((size_t)(kc >> 5) * 2 + bb) * NC) << 9) + 8 * lane;
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) a = mfma16(ld16(kp + 512 * c), qf[c], a);
+      for (int c = 0; c < NC; ++c) a = mfma16(K[bb][c], qf[c], a);
       s[bb] = a;
     }
     // lane holds keys kc + 8*gq + e (e = 0..7) for query r
@@ -122,10 +134,12 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
       acc[hb] *= alpha;
-      const u32x4 va = ld16(vbase + (((size_t)(kc >> 5) * NB + hb) << 9) + 8 * lane);
-      acc[hb] = mfma16(va, pb, acc[hb]);
+      acc[hb] = mfma16(Vt[hb], pb, acc[hb]);
     }
-  }
+  };
+  const int nsteps = w < nchunk ? (nchunk - w + 3) >> 2 : 0;
+  pipeline2(nsteps, [&](int t) { load(Ka, Va, kca, t); }, [&](int t) { load(Kb, Vb, kcb, t); },
+            [&] { process(Ka, Va, kca); }, [&] { process(Kb, Vb, kcb); });
 
   float l_row = l_part + __shfl_xor(l_part, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);

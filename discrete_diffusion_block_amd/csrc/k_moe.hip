@@ -82,7 +82,8 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 // [poff[e], poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered
 // rows start on a fragment-tile boundary; slots keep assignment order within an
 // expert.  perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
-// (expert, first slot) of every 32-token group.
+// (expert, first slot) of every 32-token group.  Offsets come from one-wave
+// prefix scans; slot ranks from per-wave match counts.
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ poff,
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ cnt_log) {
   __shared__ int hist[256];
   __shared__ int base[256];
+  __shared__ int ibase[256];
   __shared__ int wcnt[16][256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int e = tid; e < E; e += blockDim.x) hist[e] = 0;
@@ -100,20 +102,50 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
   __syncthreads();
   for (int a = tid; a < A; a += blockDim.x) atomicAdd(&hist[ids[a]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int run = 0, ni = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = run;
-      poff[e] = run;
-      cnt[e] = hist[e];
-      if (cnt_log) cnt_log[e] = hist[e];
-      for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[ni++] = make_int2(e, t0);
-      run += (hist[e] + 15) & ~15;
+  if (wv == 0) {
+    // lane owns experts [lane*epl, lane*epl + epl)
+    const int epl = (E + 63) / 64;
+    int ps = 0, is = 0;
+    for (int i = 0; i < epl; ++i) {
+      const int e = lane * epl + i;
+      if (e < E) {
+        ps += (hist[e] + 15) & ~15;
+        is += (hist[e] + kMoeGroup - 1) / kMoeGroup;
+      }
     }
-    poff[E] = run;
-    *n_items = ni;
+    int incl_p = ps, incl_i = is;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tp = __shfl_up(incl_p, o, 64), ti = __shfl_up(incl_i, o, 64);
+      if (lane >= o) {
+        incl_p += tp;
+        incl_i += ti;
+      }
+    }
+    int run_p = incl_p - ps, run_i = incl_i - is;
+    for (int i = 0; i < epl; ++i) {
+      const int e = lane * epl + i;
+      if (e < E) {
+        const int c = hist[e];
+        base[e] = run_p;
+        poff[e] = run_p;
+        cnt[e] = c;
+        if (cnt_log) cnt_log[e] = c;
+        ibase[e] = run_i;
+        run_p += (c + 15) & ~15;
+        run_i += (c + kMoeGroup - 1) / kMoeGroup;
+      }
+    }
+    if (lane == 63) {
+      poff[E] = incl_p;
+      *n_items = incl_i;
+    }
   }
   __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int it = ibase[e];
+    for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
+  }
   for (int start = 0; start < A; start += blockDim.x) {
     for (int i = tid; i < 16 * E; i += blockDim.x) wcnt[i / E][i % E] = 0;
     __syncthreads();
@@ -138,9 +170,9 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
     }
     __syncthreads();
     for (int e2 = tid; e2 < E; e2 += blockDim.x) {
-      int s = 0;
-      for (int w2 = 0; w2 < 16; ++w2) s += wcnt[w2][e2];
-      base[e2] += s;
+      int s2 = 0;
+      for (int w2 = 0; w2 < 16; ++w2) s2 += wcnt[w2][e2];
+      base[e2] += s2;
     }
     __syncthreads();
   }
@@ -272,11 +304,8 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ A) {
   __shared__ f32x4 red[4][2][2][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // logical block = fb * max_items + item (items fastest), spread so that the
-  // groups of one expert -- which read the same weight tile -- share an XCD
-  const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int fb = lb / max_items, item = lb - fb * max_items;
-  if (fb >= (F >> 4) || item >= *n_items) return;    // uniform over the workgroup
+  int item, fb;
+  if (!xcd_item_schedule(*n_items, F >> 4, &item, &fb)) return;   // uniform over the workgroup
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
@@ -356,9 +385,8 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   static_assert(WN <= 2, "LDS tile holds at most 2 row blocks");
   __shared__ f32x4 red[4][2][2][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lb = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nb = lb / max_items, item = lb - nb * max_items;
-  if (nb >= d / (16 * WN) || item >= *n_items) return;
+  int item, nb;
+  if (!xcd_item_schedule(*n_items, d / (16 * WN), &item, &nb)) return;
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
@@ -378,7 +406,7 @@ int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
 void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
                         const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                         int F, int d, uint16_t* a, hipStream_t s) {
-  const int blocks = (max_items * (F / 16) + kXcd - 1) / kXcd * kXcd;
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / 16);
   hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, xg, w_gate_up, cnt, poff, items,
                      n_items, max_items, F, d, a);
 }
@@ -387,7 +415,7 @@ void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* c
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
   constexpr int WN = 2;
-  const int blocks = (max_items * (d / (16 * WN)) + kXcd - 1) / kXcd * kXcd;
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (d / (16 * WN));
   hipLaunchKernelGGL((moe_down_kernel<WN>), dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
                      n_items, max_items, F, d, Y);
 }

@@ -82,6 +82,7 @@ def lib():
             "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
             "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
+            "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
         }
         for name, args in sig.items():
@@ -254,6 +255,25 @@ def dg_workspace_moe_counts(ctx, batch: int) -> int:
 def dg_test_router_topk(r: torch.Tensor, k: int, ids: torch.Tensor, w: torch.Tensor, stream=None):
     M, E = r.shape
     _check(lib().dg_test_router_topk(_p(r), M, E, k, _p(ids), _p(w), _stream(stream)))
+
+
+def dg_test_route(r: torch.Tensor, k: int, stream=None) -> dict:
+    """Runs the routing kernels on router logits r [M][E]; returns their outputs."""
+    M, E = r.shape
+    A = M * k
+    dev = r.device
+    out = {"ids": torch.empty(M, k, dtype=torch.int32, device=dev),
+           "w": torch.empty(M, k, device=dev),
+           "cnt": torch.empty(E, dtype=torch.int32, device=dev),
+           "poff": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "perm": torch.empty(A + 15 * E, dtype=torch.int32, device=dev),
+           "inv": torch.empty(A, dtype=torch.int32, device=dev),
+           "items": torch.empty((A + 31) // 32 + E, 2, dtype=torch.int32, device=dev),
+           "n_items": torch.empty(1, dtype=torch.int32, device=dev)}
+    _check(lib().dg_test_route(_p(r), M, E, k, _p(out["ids"]), _p(out["w"]), _p(out["cnt"]),
+                               _p(out["poff"]), _p(out["perm"]), _p(out["inv"]), _p(out["items"]),
+                               _p(out["n_items"]), _stream(stream)))
+    return out
 
 
 def dg_test_eb_select(entropy: torch.Tensor, argmax: torch.Tensor, canvas: torch.Tensor, vocab: int,

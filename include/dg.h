@@ -210,6 +210,15 @@ dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset);
 dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_ids,
                               float* d_w, void* stream);
 
+/* Router top-k + the token->expert counting sort, as run in a layer.  Outputs:
+ * ids/w as dg_test_router_topk; cnt int32 [E]; poff int32 [E+1] (16-aligned
+ * padded slot offsets); perm int32 [M*k + 15E] (token of each padded slot, -1 on
+ * padding); inv int32 [M*k] (slot of assignment m*k+j); items int32x2
+ * [(M*k+31)/32 + E] and n_items int32 [1]. */
+dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
+                        int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
+                        int32_t* d_items, int32_t* d_n_items, void* stream);
+
 /* Entropy-bounded selection alone on given fp32 entropies and argmax ids:
  * same rule and outputs as dg_sample_eb, with d_entropy and d_argmax as inputs
  * (read on [MASK] rows only). */

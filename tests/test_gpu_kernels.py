@@ -159,3 +159,33 @@ def test_sampler_full_size_vs_oracle(gamma):
         keep = canvas[b].numpy() != V
         assert np.array_equal(out[b][keep], canvas[b].numpy()[keep])
     assert len([i for i in range(C) if out[1, i] != V and canvas[1, i] == V]) >= 40
+
+
+@pytest.mark.parametrize("M,E,k", [(256, 128, 8), (512, 128, 8), (33, 8, 2), (1000, 16, 3), (7, 4, 4),
+                                   (4096, 256, 16)])
+def test_routing_sort_bit_exact(M, E, k):
+    """Top-k ids bit-exact vs the oracle; the counting sort is a stable, padded grouping."""
+    print(f"route M={M} E={E} k={k}", flush=True)
+    g = torch.Generator().manual_seed(M + E)
+    r = torch.randn(M, E, generator=g)
+    r[::2] = torch.round(r[::2] * 2) / 2                    # exact ties
+    r[5:40] = r[5]                                           # identical rows: all route alike
+    out = {k2: v.cpu() for k2, v in dg.dg_test_route(r.cuda(), k).items()}
+    ref_ids, ref_w = O.router_topk(r.double().numpy(), k)
+    np.testing.assert_array_equal(out["ids"].numpy(), ref_ids)
+    np.testing.assert_allclose(out["w"].numpy(), ref_w, rtol=2e-6, atol=1e-7)
+    ids = ref_ids.reshape(-1)
+    cnt = np.bincount(ids, minlength=E)
+    np.testing.assert_array_equal(out["cnt"].numpy(), cnt)
+    poff = out["poff"].numpy()
+    assert poff[0] == 0 and np.all(poff % 16 == 0)
+    np.testing.assert_array_equal(np.diff(poff), (cnt + 15) // 16 * 16)
+    perm, inv = out["perm"].numpy(), out["inv"].numpy()
+    for e in range(E):
+        assign = np.nonzero(ids == e)[0]                    # assignment order within the expert
+        np.testing.assert_array_equal(inv[assign], poff[e] + np.arange(len(assign)))
+        np.testing.assert_array_equal(perm[poff[e]:poff[e] + len(assign)], assign // k)
+        assert np.all(perm[poff[e] + len(assign):poff[e + 1]] == -1)
+    items = out["items"].numpy()[:out["n_items"].item()]
+    want = [(e, t0) for e in range(E) for t0 in range(0, cnt[e], 32)]
+    assert [tuple(x) for x in items] == want
