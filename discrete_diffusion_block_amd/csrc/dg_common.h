@@ -72,13 +72,32 @@ __device__ __forceinline__ void pipeline2(int n, LA load_a, LB load_b, MA mma_a,
 }
 
 // Three-stage variant: two register sets are in flight while the third is
-// consumed.  Steady state (no branches) covers steps s..s+2 per trip; the
-// tail handles the last 1..4 steps.
+// consumed.  The steady-state loop is entered only after both prologue loads
+// were issued unconditionally: the compiler's wait-count analysis merges every
+// path into the loop header, and a path with fewer loads in flight would make
+// it wait for the whole pipeline at the top of each trip.
 template <class L0, class L1, class L2, class M0, class M1, class M2>
 __device__ __forceinline__ void pipeline3(int n, L0 l0, L1 l1, L2 l2, M0 m0, M1 m1, M2 m2) {
   if (n <= 0) return;
+  // last r = n - s steps (1..4) with steps s, s+1 (those < n) already loaded; s % 3 == 0
+  auto tail = [&](int s, int r) {
+    if (r >= 3) l2(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    m0();
+    if (r == 4) l0(s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r >= 2) m1();
+    if (r >= 3) m2();
+    if (r == 4) m0();
+  };
+  if (n < 5) {
+    l0(0);
+    if (n > 1) l1(1);
+    tail(0, n);
+    return;
+  }
   l0(0);
-  if (n > 1) l1(1);
+  l1(1);
   __builtin_amdgcn_sched_barrier(0);
   int s = 0;
   for (; s + 4 < n; s += 3) {
@@ -95,15 +114,70 @@ __device__ __forceinline__ void pipeline3(int n, L0 l0, L1 l1, L2 l2, M0 m0, M1 
     m2();
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int r = n - s;
-  if (r >= 3) l2(s + 2);
+  tail(s, n - s);
+}
+
+// Four-stage variant: three register sets are in flight while the fourth is
+// consumed; same structure as pipeline3.
+template <class L0, class L1, class L2, class L3, class M0, class M1, class M2, class M3>
+__device__ __forceinline__ void pipeline4(int n, L0 l0, L1 l1, L2 l2, L3 l3, M0 m0, M1 m1, M2 m2,
+                                          M3 m3) {
+  if (n <= 0) return;
+  // last r = n - s steps (1..7) with steps s .. s+2 (those < n) already loaded; s % 4 == 0
+  auto tail = [&](int s, int r) {
+    if (r > 3) l3(s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    m0();
+    if (r > 1) {
+      if (r > 4) l0(s + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      m1();
+    }
+    if (r > 2) {
+      if (r > 5) l1(s + 5);
+      __builtin_amdgcn_sched_barrier(0);
+      m2();
+    }
+    if (r > 3) {
+      if (r > 6) l2(s + 6);
+      __builtin_amdgcn_sched_barrier(0);
+      m3();
+    }
+    if (r > 4) m0();
+    if (r > 5) m1();
+    if (r > 6) m2();
+  };
+  if (n < 8) {
+    l0(0);
+    if (n > 1) l1(1);
+    if (n > 2) l2(2);
+    tail(0, n);
+    return;
+  }
+  l0(0);
+  l1(1);
+  l2(2);
   __builtin_amdgcn_sched_barrier(0);
-  m0();
-  if (r == 4) l0(s + 3);
-  __builtin_amdgcn_sched_barrier(0);
-  if (r >= 2) m1();
-  if (r >= 3) m2();
-  if (r == 4) m0();
+  int s = 0;
+  for (; s + 7 < n; s += 4) {
+    l3(s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    m0();
+    __builtin_amdgcn_sched_barrier(0);
+    l0(s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    m1();
+    __builtin_amdgcn_sched_barrier(0);
+    l1(s + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    m2();
+    __builtin_amdgcn_sched_barrier(0);
+    l2(s + 6);
+    __builtin_amdgcn_sched_barrier(0);
+    m3();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  tail(s, n - s);
 }
 
 // 16-byte load that bypasses cache retention (weights are streamed exactly once).

@@ -57,7 +57,7 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
 
 // ---- MoE ----
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
-constexpr int kMoeGroup = 32;        // tokens per grouped-GEMM work item
+constexpr int kMoeGroup = 64;        // tokens per grouped-GEMM work item
 int moe_max_items(int M, int k, int E);
 int moe_max_slots(int M, int k, int E);   // padded slot space: M*k + 15*E
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,

@@ -103,9 +103,9 @@ __device__ __forceinline__ void epilogue(const DenseArgs& a, int blk0, int m, co
   }
 }
 
-template <int WN, int WM, int EPI>
-__global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
-  extern __shared__ f32x4 red[];  // [4 waves][WN][WM][64 lanes]
+template <int WN, int WM, int EPI, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
+  extern __shared__ f32x4 red[];  // [NW waves][WN][WM][64 lanes]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int blk0 = blockIdx.x * WN;
@@ -150,11 +150,11 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
       }
   };
 
-  // wave w takes the 64-wide k steps w, w+4, w+8, ...
+  // wave w takes the 64-wide k steps w, w+NW, w+2NW, ...
   const int nk = a.K >> 6;
-  const int nw = w < nk ? (nk - w + 3) >> 2 : 0;
-  pipeline3(nw, [&](int s) { load(A0, B0, w + 4 * s); }, [&](int s) { load(A1, B1, w + 4 * s); },
-            [&](int s) { load(A2, B2, w + 4 * s); }, [&] { mma(A0, B0); }, [&] { mma(A1, B1); },
+  const int nw = w < nk ? (nk - w + NW - 1) / NW : 0;
+  pipeline3(nw, [&](int s) { load(A0, B0, w + NW * s); }, [&](int s) { load(A1, B1, w + NW * s); },
+            [&](int s) { load(A2, B2, w + NW * s); }, [&] { mma(A0, B0); }, [&] { mma(A1, B1); },
             [&] { mma(A2, B2); });
 
 #pragma unroll
@@ -162,25 +162,24 @@ __global__ __launch_bounds__(256) void dense_gemm(DenseArgs a) {
 #pragma unroll
     for (int j = 0; j < WM; ++j) red[((w * WN + i) * WM + j) * 64 + lane] = acc[i][j];
   __syncthreads();
-  for (int j = w; j < WM; j += 4) {
+  for (int j = w; j < WM; j += NW) {
     f32x4 v[WN];
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       f32x4 s = red[((0 * WN + i) * WM + j) * 64 + lane];
-      s += red[((1 * WN + i) * WM + j) * 64 + lane];
-      s += red[((2 * WN + i) * WM + j) * 64 + lane];
-      s += red[((3 * WN + i) * WM + j) * 64 + lane];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) s += red[((ww * WN + i) * WM + j) * 64 + lane];
       v[i] = s;
     }
     epilogue<EPI, WN>(a, blk0, (mb0 + j) * 16 + r, v, g);
   }
 }
 
-template <int WN, int WM, int EPI>
+template <int WN, int WM, int EPI, int NW = 4>
 static void run_dense(const DenseArgs& a, hipStream_t s) {
   dim3 grid((a.nblk + WN - 1) / WN, (a.M + 16 * WM - 1) / (16 * WM));
-  const size_t lds = sizeof(f32x4) * 4 * WN * WM * 64;
-  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI>), grid, dim3(256), lds, s, a);
+  const size_t lds = sizeof(f32x4) * NW * WN * WM * 64;
+  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), grid, dim3(64 * NW), lds, s, a);
 }
 
 void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,

@@ -82,7 +82,7 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 // [poff[e], poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered
 // rows start on a fragment-tile boundary; slots keep assignment order within an
 // expert.  perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
-// (expert, first slot) of every 32-token group.  Offsets come from one-wave
+// (expert, first token) of every kMoeGroup-token group.  Offsets come from one-wave
 // prefix scans; slot ranks from per-wave match counts.
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
@@ -211,132 +211,33 @@ void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, 
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
-// Grouped expert GEMMs.  A workgroup owns one work item (expert e, group of up
-// to 32 of its tokens) and one tile of 16 output features; its 4 waves split
-// the K loop (interleaved 64-wide steps) and reduce through LDS.  Splitting K
-// keeps every wave's dependent chain short, so the kernel stays bandwidth-bound
-// both when tokens spread over all experts (~16 each) and when a uniform canvas
-// sends every token to the same few experts (many groups per expert, whose
-// workgroups then share the expert's weight tiles through L2).
+// Grouped expert GEMMs.  A workgroup owns one work item (expert e, a group of up
+// to 64 of its tokens = NT blocks of 16) and a tile of output features; its 4
+// waves split the K loop (interleaved 64-wide steps) and reduce through LDS in
+// a fixed order.  Splitting K keeps every wave's dependent chain short and
+// reads every operand byte once per workgroup, so the kernel holds up both when
+// tokens spread over all experts (~16 each: a weight-streaming, HBM-bound
+// regime) and when a uniform canvas sends every token to a few experts (many
+// tokens per expert: the workgroup tile of 32 features x 64 tokens then reuses
+// each weight fragment across 4 token blocks and each token fragment across 4
+// weight blocks).
 //
-// Lane group g reads bytes [64q + 16g, +16) of each 128-byte step q, so the 4
-// lanes of a row read 64 contiguous bytes per instruction.
+// Every operand pointer addresses a fragment tile (row block, k block 0) plus
+// the lane's 16-byte slot; a 64-wide k step covers two consecutive 1 KiB tiles.
 
-// gate/up: ag = x W_g^T, au = x W_u^T over this wave's k steps.  Every operand
-// pointer addresses a fragment tile (row block, k block 0) plus the lane slot;
-// a 64-wide k step covers two consecutive 1 KiB tiles.
-template <int NT>
-__device__ __forceinline__ void gate_up_partial(const uint16_t* wg, const uint16_t* wu,
+constexpr int kGateUpFb = 2;   // 16-feature blocks per gate/up workgroup
+constexpr int kDownWn = 2;     // 16-row output blocks per down workgroup
+
+// acc[i][j] += W_i . X_j^T over this wave's k steps (steps w, w + 4, ...).
+template <int NW, int NT>
+__device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
                                                 const uint16_t* const (&xp)[NT], int nk, int w,
-                                                f32x4 (&ag)[NT], f32x4 (&au)[NT]) {
-  u32x4 Ga[2], Ua[2], Xa[NT][2], Gb[2], Ub[2], Xb[NT][2], Gc[2], Uc[2], Xc[NT][2];
-  auto ld = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2], int step) {
+                                                f32x4 (&acc)[NW][NT]) {
+  u32x4 Wa[NW][2], Xa[NT][2], Wb[NW][2], Xb[NT][2], Wc[NW][2], Xc[NT][2];
+  auto ld = [&](u32x4 (&W)[NW][2], u32x4 (&X)[NT][2], int step) {
     const int k = (w + 4 * step) * 1024;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      G[q] = ld16_stream(wg + k + 512 * q);
-      U[q] = ld16_stream(wu + k + 512 * q);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 512 * q);
-  };
-  auto mm = [&](u32x4 (&G)[2], u32x4 (&U)[2], u32x4 (&X)[NT][2]) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        ag[j] = mfma16(G[q], X[j][q], ag[j]);
-        au[j] = mfma16(U[q], X[j][q], au[j]);
-      }
-  };
-  const int n = w < nk ? (nk - w + 3) >> 2 : 0;
-  pipeline3(n, [&](int t) { ld(Ga, Ua, Xa, t); }, [&](int t) { ld(Gb, Ub, Xb, t); },
-            [&](int t) { ld(Gc, Uc, Xc, t); }, [&] { mm(Ga, Ua, Xa); }, [&] { mm(Gb, Ub, Xb); },
-            [&] { mm(Gc, Uc, Xc); });
-}
-
-template <int NT>
-__device__ __forceinline__ void gate_up_item(const uint16_t* wg, const uint16_t* wu,
-                                             const uint16_t* xg, int slot0, int t0, int ne, int F,
-                                             int fb, int d, int lane, int w, uint16_t* A,
-                                             f32x4 (*red)[2][2][64]) {
-  const int r = lane & 15, g = lane >> 4;
-  const uint16_t* xp[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = xg + fm_tile((slot0 >> 4) + j, 0, d, lane);
-  f32x4 ag[NT], au[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gate_up_partial<NT>(wg, wu, xp, d >> 6, w, ag, au);
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    red[w][0][j][lane] = ag[j];
-    red[w][1][j][lane] = au[j];
-  }
-  __syncthreads();
-  if (w < NT) {
-    const int j = w;
-    const f32x4 G = red[0][0][j][lane] + red[1][0][j][lane] + red[2][0][j][lane] + red[3][0][j][lane];
-    const f32x4 U = red[0][1][j][lane] + red[1][1][j][lane] + red[2][1][j][lane] + red[3][1][j][lane];
-    const int t = t0 + 16 * j + r;
-    if (t < ne) {
-      u32x2 o;
-      o.x = pack_bf2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
-      o.y = pack_bf2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
-      *reinterpret_cast<u32x2*>(A + fm_index(slot0 + 16 * j + r, fb * 16 + 4 * g, F)) = o;
-    }
-  }
-}
-
-// A[slot][f] = silu(x W_g[e][f]^T) * (x W_u[e][f]^T) for every slot of expert e,
-// x = Xg[slot].  Workgroup = (work item, 16 features); items vary fastest.
-// The packed expert weight holds gate block f and up block f as row blocks
-// 2f and 2f + 1.
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ xg,
-                                                          const uint16_t* __restrict__ wgu,
-                                                          const int32_t* __restrict__ cnt,
-                                                          const int32_t* __restrict__ poff,
-                                                          const int2* __restrict__ items,
-                                                          const int32_t* __restrict__ n_items,
-                                                          int max_items, int F, int d,
-                                                          uint16_t* __restrict__ A) {
-  __shared__ f32x4 red[4][2][2][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int item, fb;
-  if (!xcd_item_schedule(*n_items, F >> 4, &item, &fb)) return;   // uniform over the workgroup
-  const int2 it = items[item];
-  const int e = it.x, t0 = it.y;
-  const int ne = cnt[e], slot0 = poff[e] + t0;
-  const size_t wmat = (size_t)e * 2 * F * d;
-  const uint16_t* wg = wgu + wmat + fm_tile(2 * fb, 0, d, lane);
-  const uint16_t* wu = wgu + wmat + fm_tile(2 * fb + 1, 0, d, lane);
-  if (ne - t0 <= 16)
-    gate_up_item<1>(wg, wu, xg, slot0, t0, ne, F, fb, d, lane, w, A, red);
-  else
-    gate_up_item<2>(wg, wu, xg, slot0, t0, ne, F, fb, d, lane, w, A, red);
-}
-
-// down: Y[slot][n] = A[slot] . W_d[e][n]^T for 16*WN output rows.
-template <int NT, int WN>
-__device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const uint16_t* A,
-                                          int slot0, int t0, int ne, int F, int d, int n0, int lane,
-                                          int w, float* Y, f32x4 (*red)[2][2][64]) {
-  const int r = lane & 15, g = lane >> 4;
-  const uint16_t* xp[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
-  f32x4 acc[WN][NT];
-#pragma unroll
-  for (int i = 0; i < WN; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 Wa[WN][2], Xa[NT][2], Wb[WN][2], Xb[NT][2], Wc[WN][2], Xc[NT][2];
-  auto ld = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2], int step) {
-    const int k = (w + 4 * step) * 1024;
-#pragma unroll
-    for (int i = 0; i < WN; ++i)
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
       for (int q = 0; q < 2; ++q) W[i][q] = ld16_stream(wp[i] + k + 512 * q);
 #pragma unroll
@@ -344,60 +245,148 @@ __device__ __forceinline__ void down_item(const uint16_t* const (&wp)[WN], const
 #pragma unroll
       for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 512 * q);
   };
-  auto mm = [&](u32x4 (&W)[WN][2], u32x4 (&X)[NT][2]) {
+  auto mm = [&](u32x4 (&W)[NW][2], u32x4 (&X)[NT][2]) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < WN; ++i)
+      for (int i = 0; i < NW; ++i)
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[i][j] = mfma16(W[i][q], X[j][q], acc[i][j]);
   };
-  const int nk = F >> 6;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n = w < nk ? (nk - w + 3) >> 2 : 0;
   pipeline3(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
             [&](int t) { ld(Wc, Xc, t); }, [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); },
             [&] { mm(Wc, Xc); });
+}
+
+// Park this wave's partial tiles in LDS: red[((w * NW + i) * NT + j) * 64 + lane].
+template <int NW, int NT>
+__device__ __forceinline__ void park(const f32x4 (&acc)[NW][NT], f32x4* red, int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < WN; ++i)
+  for (int i = 0; i < NW; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) red[w][i][j][lane] = acc[i][j];
+    for (int j = 0; j < NT; ++j) red[((w * NW + i) * NT + j) * 64 + lane] = acc[i][j];
+}
+
+template <int NW, int NT>
+__device__ __forceinline__ f32x4 reduced(const f32x4* red, int i, int j, int lane) {
+  f32x4 v = red[(i * NT + j) * 64 + lane];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) v += red[((ww * NW + i) * NT + j) * 64 + lane];
+  return v;
+}
+
+// gate/up: for the FB feature blocks f0 + f, weight row blocks 2(f0 + f) (gate)
+// and 2(f0 + f) + 1 (up); A[slot][feature] = silu(gate) * up in bf16.
+template <int NT>
+__device__ __forceinline__ void gate_up_item(const uint16_t* wgu_e, const uint16_t* xg, int slot0,
+                                             int t0, int ne, int F, int f0, int d, int lane, int w,
+                                             uint16_t* A, f32x4* red) {
+  constexpr int FB = kGateUpFb, NW = 2 * kGateUpFb;
+  const uint16_t* wp[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) wp[i] = wgu_e + fm_tile(2 * f0 + i, 0, d, lane);
+  const uint16_t* xp[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) xp[j] = xg + fm_tile((slot0 >> 4) + j, 0, d, lane);
+  f32x4 acc[NW][NT];
+  grouped_partial<NW, NT>(wp, xp, d >> 6, w, acc);
+  park<NW, NT>(acc, red, w, lane);
   __syncthreads();
-  // wave w finalises (row block i, token tile j) pairs w, w+4, ...
-  for (int p = w; p < WN * NT; p += 4) {
-    const int i = p / NT, j = p - i * NT;
+  const int r = lane & 15, g = lane >> 4;
+  for (int p = w; p < FB * NT; p += 4) {
+    const int f = p / NT, j = p - f * NT;
     const int t = t0 + 16 * j + r;
     if (t < ne) {
-      const f32x4 v = red[0][i][j][lane] + red[1][i][j][lane] + red[2][i][j][lane] + red[3][i][j][lane];
-      *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * i + 4 * g) = v;
+      const f32x4 G = reduced<NW, NT>(red, 2 * f, j, lane);
+      const f32x4 U = reduced<NW, NT>(red, 2 * f + 1, j, lane);
+      u32x2 o;
+      o.x = pack_bf2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
+      o.y = pack_bf2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
+      *reinterpret_cast<u32x2*>(A + fm_index(slot0 + 16 * j + r, (f0 + f) * 16 + 4 * g, F)) = o;
     }
   }
 }
 
-template <int WN>
+// A[slot][f] = silu(x W_g[e][f]^T) * (x W_u[e][f]^T) for every slot of expert e,
+// x = Xg[slot].  Workgroup = (work item, kGateUpFb feature blocks).  The packed
+// expert weight holds gate block f and up block f as row blocks 2f and 2f + 1.
+__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ xg,
+                                                          const uint16_t* __restrict__ wgu,
+                                                          const int32_t* __restrict__ cnt,
+                                                          const int32_t* __restrict__ poff,
+                                                          const int2* __restrict__ items,
+                                                          const int32_t* __restrict__ n_items,
+                                                          int F, int d, uint16_t* __restrict__ A) {
+  __shared__ f32x4 red[4 * 2 * kGateUpFb * 4 * 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int item, fb;
+  if (!xcd_item_schedule(*n_items, F / (16 * kGateUpFb), &item, &fb)) return;   // uniform per workgroup
+  const int2 it = items[item];
+  const int e = it.x, t0 = it.y;
+  const int ne = cnt[e], slot0 = poff[e] + t0;
+  const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
+  const int f0 = fb * kGateUpFb;
+  switch (min(4, (ne - t0 + 15) >> 4)) {
+    case 1: gate_up_item<1>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+    case 2: gate_up_item<2>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+    case 3: gate_up_item<3>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+    default: gate_up_item<4>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+  }
+}
+
+// down: Y[slot][n] = A[slot] . W_d[e][n]^T for the kDownWn output row blocks n0/16 ..
+template <int NT>
+__device__ __forceinline__ void down_item(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
+                                          int ne, int F, int d, int n0, int lane, int w, float* Y,
+                                          f32x4* red) {
+  constexpr int NW = kDownWn;
+  const uint16_t* wp[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) wp[i] = wd_e + fm_tile((n0 >> 4) + i, 0, F, lane);
+  const uint16_t* xp[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
+  f32x4 acc[NW][NT];
+  grouped_partial<NW, NT>(wp, xp, F >> 6, w, acc);
+  park<NW, NT>(acc, red, w, lane);
+  __syncthreads();
+  const int r = lane & 15, g = lane >> 4;
+  for (int p = w; p < NW * NT; p += 4) {
+    const int i = p / NT, j = p - i * NT;
+    const int t = t0 + 16 * j + r;
+    if (t < ne)
+      *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * i + 4 * g) =
+          reduced<NW, NT>(red, i, j, lane);
+  }
+}
+
 __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ wd,
                                                        const int32_t* __restrict__ cnt,
                                                        const int32_t* __restrict__ poff,
                                                        const int2* __restrict__ items,
                                                        const int32_t* __restrict__ n_items,
-                                                       int max_items, int F, int d,
-                                                       float* __restrict__ Y) {
-  static_assert(WN <= 2, "LDS tile holds at most 2 row blocks");
-  __shared__ f32x4 red[4][2][2][64];
+                                                       int F, int d, float* __restrict__ Y) {
+  __shared__ f32x4 red[4 * kDownWn * 4 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int item, nb;
-  if (!xcd_item_schedule(*n_items, d / (16 * WN), &item, &nb)) return;
+  if (!xcd_item_schedule(*n_items, d / (16 * kDownWn), &item, &nb)) return;
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
-  const int n0 = nb * 16 * WN;
-  const uint16_t* wp[WN];
-#pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = wd + (size_t)e * d * F + fm_tile((n0 >> 4) + i, 0, F, lane);
-  if (ne - t0 <= 16)
-    down_item<1, WN>(wp, A, slot0, t0, ne, F, d, n0, lane, w, Y, red);
-  else
-    down_item<2, WN>(wp, A, slot0, t0, ne, F, d, n0, lane, w, Y, red);
+  const int n0 = nb * 16 * kDownWn;
+  const uint16_t* wd_e = wd + (size_t)e * d * F;
+  switch (min(4, (ne - t0 + 15) >> 4)) {
+    case 1: down_item<1>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+    case 2: down_item<2>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+    case 3: down_item<3>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+    default: down_item<4>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+  }
 }
 
 int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
@@ -406,18 +395,17 @@ int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
 void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
                         const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                         int F, int d, uint16_t* a, hipStream_t s) {
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / 16);
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGateUpFb));
   hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, xg, w_gate_up, cnt, poff, items,
-                     n_items, max_items, F, d, a);
+                     n_items, F, d, a);
 }
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
-  constexpr int WN = 2;
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (d / (16 * WN));
-  hipLaunchKernelGGL((moe_down_kernel<WN>), dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
-                     n_items, max_items, F, d, Y);
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (d / (16 * kDownWn));
+  hipLaunchKernelGGL(moe_down_kernel, dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
+                     n_items, F, d, Y);
 }
 
 }  // namespace dg

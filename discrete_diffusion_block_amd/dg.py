@@ -25,6 +25,7 @@ KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
                 "sample_pass1", "sample_select", "fill", "gather"]
 PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
+MOE_GROUP = 64   # tokens per grouped-GEMM work item in the routing tap's item list
 
 STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE", -3: "DG_ERR_WORKSPACE",
           -4: "DG_ERR_KV_CAPACITY", -5: "DG_ERR_HIP", -6: "DG_ERR_UNSUPPORTED"}

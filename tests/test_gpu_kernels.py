@@ -187,5 +187,5 @@ def test_routing_sort_bit_exact(M, E, k):
         np.testing.assert_array_equal(perm[poff[e]:poff[e] + len(assign)], assign // k)
         assert np.all(perm[poff[e] + len(assign):poff[e + 1]] == -1)
     items = out["items"].numpy()[:out["n_items"].item()]
-    want = [(e, t0) for e in range(E) for t0 in range(0, cnt[e], 32)]
+    want = [(e, t0) for e in range(E) for t0 in range(0, cnt[e], dg.MOE_GROUP)]
     assert [tuple(x) for x in items] == want
