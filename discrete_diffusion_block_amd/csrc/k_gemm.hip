@@ -129,10 +129,11 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
   u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2], A2[WN][2], B2[WM][2];
   auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
     const int k = it * 1024;  // two 512-element k tiles per 64-wide step
+    // every token tile re-reads these weight tiles, so they go through L2 as usual
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      A[i][0] = ld16_stream(wp[i] + k);
-      A[i][1] = ld16_stream(wp[i] + k + 512);
+      A[i][0] = ld16(wp[i] + k);
+      A[i][1] = ld16(wp[i] + k + 512);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
@@ -188,10 +189,19 @@ void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int 
   a.x = x; a.w = w; a.M = M; a.N = N; a.K = K;
   a.nblk = (N + 15) / 16;
   a.yf = y; a.ldy = N;
-  if (add)
-    run_dense<2, 4, EPI_ADD_F32>(a, s);
-  else
-    run_dense<2, 4, EPI_STORE_F32>(a, s);
+  // tile shapes measured at the 256-token canvas: narrow outputs (the router)
+  // want many small workgroups, wide ones 64 x 64 tiles
+  if (add) {
+    if (N <= 256)
+      run_dense<1, 1, EPI_ADD_F32>(a, s);
+    else
+      run_dense<4, 4, EPI_ADD_F32>(a, s);
+  } else {
+    if (N <= 256)
+      run_dense<1, 1, EPI_STORE_F32>(a, s);
+    else
+      run_dense<4, 4, EPI_STORE_F32>(a, s);
+  }
 }
 
 void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int hq,
@@ -202,7 +212,7 @@ void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int
   a.N = (hq + 2 * kv.hkv) * kv.hd;
   a.nblk = a.N / 16;
   a.hq = hq; a.hd = kv.hd; a.kv = kv; a.g = g; a.rope = rope_tab; a.q_out = q_out;
-  run_dense<2, 4, EPI_QKV>(a, s);
+  run_dense<4, 4, EPI_QKV>(a, s);
 }
 
 void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,

@@ -229,7 +229,10 @@ constexpr int kGateUpFb = 2;   // 16-feature blocks per gate/up workgroup
 constexpr int kDownWn = 2;     // 16-row output blocks per down workgroup
 
 // acc[i][j] += W_i . X_j^T over this wave's k steps (steps w, w + 4, ...).
-template <int NW, int NT>
+// STREAM: the weight tiles are read by this workgroup only (the expert has a
+// single work item), so they bypass cache retention; otherwise the expert's
+// other items re-read them from L2.
+template <int NW, int NT, bool STREAM>
 __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
                                                 const uint16_t* const (&xp)[NT], int nk, int w,
                                                 f32x4 (&acc)[NW][NT]) {
@@ -239,7 +242,8 @@ __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
 #pragma unroll
     for (int i = 0; i < NW; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) W[i][q] = ld16_stream(wp[i] + k + 512 * q);
+      for (int q = 0; q < 2; ++q)
+        W[i][q] = STREAM ? ld16_stream(wp[i] + k + 512 * q) : ld16(wp[i] + k + 512 * q);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -282,7 +286,7 @@ __device__ __forceinline__ f32x4 reduced(const f32x4* red, int i, int j, int lan
 
 // gate/up: for the FB feature blocks f0 + f, weight row blocks 2(f0 + f) (gate)
 // and 2(f0 + f) + 1 (up); A[slot][feature] = silu(gate) * up in bf16.
-template <int NT>
+template <int NT, bool STREAM>
 __device__ __forceinline__ void gate_up_item(const uint16_t* wgu_e, const uint16_t* xg, int slot0,
                                              int t0, int ne, int F, int f0, int d, int lane, int w,
                                              uint16_t* A, f32x4* red) {
@@ -294,7 +298,7 @@ __device__ __forceinline__ void gate_up_item(const uint16_t* wgu_e, const uint16
 #pragma unroll
   for (int j = 0; j < NT; ++j) xp[j] = xg + fm_tile((slot0 >> 4) + j, 0, d, lane);
   f32x4 acc[NW][NT];
-  grouped_partial<NW, NT>(wp, xp, d >> 6, w, acc);
+  grouped_partial<NW, NT, STREAM>(wp, xp, d >> 6, w, acc);
   park<NW, NT>(acc, red, w, lane);
   __syncthreads();
   const int r = lane & 15, g = lane >> 4;
@@ -331,16 +335,26 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
   const int f0 = fb * kGateUpFb;
-  switch (min(4, (ne - t0 + 15) >> 4)) {
-    case 1: gate_up_item<1>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-    case 2: gate_up_item<2>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-    case 3: gate_up_item<3>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-    default: gate_up_item<4>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+  const int nt = min(4, (ne - t0 + 15) >> 4);
+  if (ne <= kMoeGroup) {
+    switch (nt) {
+      case 1: gate_up_item<1, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      case 2: gate_up_item<2, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      case 3: gate_up_item<3, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      default: gate_up_item<4, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+    }
+  } else {
+    switch (nt) {
+      case 1: gate_up_item<1, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      case 2: gate_up_item<2, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      case 3: gate_up_item<3, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+      default: gate_up_item<4, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
+    }
   }
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T for the kDownWn output row blocks n0/16 ..
-template <int NT>
+template <int NT, bool STREAM>
 __device__ __forceinline__ void down_item(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
                                           int ne, int F, int d, int n0, int lane, int w, float* Y,
                                           f32x4* red) {
@@ -352,7 +366,7 @@ __device__ __forceinline__ void down_item(const uint16_t* wd_e, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
   f32x4 acc[NW][NT];
-  grouped_partial<NW, NT>(wp, xp, F >> 6, w, acc);
+  grouped_partial<NW, NT, STREAM>(wp, xp, F >> 6, w, acc);
   park<NW, NT>(acc, red, w, lane);
   __syncthreads();
   const int r = lane & 15, g = lane >> 4;
@@ -381,11 +395,21 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const int n0 = nb * 16 * kDownWn;
   const uint16_t* wd_e = wd + (size_t)e * d * F;
-  switch (min(4, (ne - t0 + 15) >> 4)) {
-    case 1: down_item<1>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-    case 2: down_item<2>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-    case 3: down_item<3>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-    default: down_item<4>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+  const int nt = min(4, (ne - t0 + 15) >> 4);
+  if (ne <= kMoeGroup) {
+    switch (nt) {
+      case 1: down_item<1, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 2: down_item<2, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 3: down_item<3, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      default: down_item<4, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+    }
+  } else {
+    switch (nt) {
+      case 1: down_item<1, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 2: down_item<2, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 3: down_item<3, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      default: down_item<4, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+    }
   }
 }
 
