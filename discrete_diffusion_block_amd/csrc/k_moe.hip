@@ -212,9 +212,11 @@ void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
 // Grouped expert GEMMs.  A workgroup owns one work item (expert e, a group of up
-// to 64 of its tokens = NT blocks of 16) and a tile of output features; its 4
-// waves split the K loop (interleaved 64-wide steps) and reduce through LDS in
-// a fixed order.  Splitting K keeps every wave's dependent chain short and
+// to 64 of its tokens = NT blocks of 16) and a tile of output features.  In the
+// gate/up GEMM (K = d_model) its 4 waves split the K loop (interleaved 64-wide
+// steps) and reduce through LDS in a fixed order; in the down GEMM (K = F, short)
+// each wave owns 32 output rows over the whole K loop and the token fragments
+// are shared through L1.  Splitting K keeps every wave's dependent chain short and
 // reads every operand byte once per workgroup, so the kernel holds up both when
 // tokens spread over all experts (~16 each: a weight-streaming, HBM-bound
 // regime) and when a uniform canvas sends every token to a few experts (many
@@ -226,19 +228,19 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)
 // the lane's 16-byte slot; a 64-wide k step covers two consecutive 1 KiB tiles.
 
 constexpr int kGateUpFb = 2;   // 16-feature blocks per gate/up workgroup
-constexpr int kDownWn = 2;     // 16-row output blocks per down workgroup
+constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 
-// acc[i][j] += W_i . X_j^T over this wave's k steps (steps w, w + 4, ...).
+// acc[i][j] += W_i . X_j^T over this wave's k steps (w, w + kstride, ...).
 // STREAM: the weight tiles are read by this workgroup only (the expert has a
 // single work item), so they bypass cache retention; otherwise the expert's
 // other items re-read them from L2.
 template <int NW, int NT, bool STREAM>
 __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
                                                 const uint16_t* const (&xp)[NT], int nk, int w,
-                                                f32x4 (&acc)[NW][NT]) {
+                                                f32x4 (&acc)[NW][NT], int kstride = 4) {
   u32x4 Wa[NW][2], Xa[NT][2], Wb[NW][2], Xb[NT][2], Wc[NW][2], Xc[NT][2];
   auto ld = [&](u32x4 (&W)[NW][2], u32x4 (&X)[NT][2], int step) {
-    const int k = (w + 4 * step) * 1024;
+    const int k = (w + kstride * step) * 1024;
 #pragma unroll
     for (int i = 0; i < NW; ++i)
 #pragma unroll
@@ -261,7 +263,7 @@ __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
   for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n = w < nk ? (nk - w + 3) >> 2 : 0;
+  const int n = w < nk ? (nk - w + kstride - 1) / kstride : 0;
   pipeline3(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
             [&](int t) { ld(Wc, Xc, t); }, [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); },
             [&] { mm(Wc, Xc); });
@@ -353,29 +355,32 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
   }
 }
 
-// down: Y[slot][n] = A[slot] . W_d[e][n]^T for the kDownWn output row blocks n0/16 ..
+// down: Y[slot][n] = A[slot] . W_d[e][n]^T; wave w owns output row blocks
+// n0/16 + 2w, +1 over the whole K loop (no split-K: K = F is short).
 template <int NT, bool STREAM>
 __device__ __forceinline__ void down_item(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
-                                          int ne, int F, int d, int n0, int lane, int w, float* Y,
-                                          f32x4* red) {
-  constexpr int NW = kDownWn;
+                                          int ne, int F, int d, int n0, int lane, int w, float* Y) {
+  constexpr int NW = 2;
+  const int nblk = d >> 4;
   const uint16_t* wp[NW];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) wp[i] = wd_e + fm_tile((n0 >> 4) + i, 0, F, lane);
+  for (int i = 0; i < NW; ++i) wp[i] = wd_e + fm_tile(min((n0 >> 4) + NW * w + i, nblk - 1), 0, F, lane);
   const uint16_t* xp[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
   f32x4 acc[NW][NT];
-  grouped_partial<NW, NT, STREAM>(wp, xp, F >> 6, w, acc);
-  park<NW, NT>(acc, red, w, lane);
-  __syncthreads();
+  grouped_partial<NW, NT, STREAM>(wp, xp, F >> 6, 0, acc, 1);
   const int r = lane & 15, g = lane >> 4;
-  for (int p = w; p < NW * NT; p += 4) {
-    const int i = p / NT, j = p - i * NT;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
     const int t = t0 + 16 * j + r;
-    if (t < ne)
-      *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * i + 4 * g) =
-          reduced<NW, NT>(red, i, j, lane);
+    if (t < ne) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        if ((n0 >> 4) + NW * w + i < nblk)
+          *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * (NW * w + i) + 4 * g) =
+              acc[i][j];
+    }
   }
 }
 
@@ -386,29 +391,28 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
                                                        const int2* __restrict__ items,
                                                        const int32_t* __restrict__ n_items,
                                                        int F, int d, float* __restrict__ Y) {
-  __shared__ f32x4 red[4 * kDownWn * 4 * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int item, nb;
-  if (!xcd_item_schedule(*n_items, d / (16 * kDownWn), &item, &nb)) return;
+  if (!xcd_item_schedule(*n_items, (d + kDownRows - 1) / kDownRows, &item, &nb)) return;
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
-  const int n0 = nb * 16 * kDownWn;
+  const int n0 = nb * kDownRows;
   const uint16_t* wd_e = wd + (size_t)e * d * F;
   const int nt = min(4, (ne - t0 + 15) >> 4);
   if (ne <= kMoeGroup) {
     switch (nt) {
-      case 1: down_item<1, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      case 2: down_item<2, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      case 3: down_item<3, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      default: down_item<4, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 1: down_item<1, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      case 2: down_item<2, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      case 3: down_item<3, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      default: down_item<4, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
     }
   } else {
     switch (nt) {
-      case 1: down_item<1, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      case 2: down_item<2, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      case 3: down_item<3, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
-      default: down_item<4, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y, red); break;
+      case 1: down_item<1, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      case 2: down_item<2, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      case 3: down_item<3, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
+      default: down_item<4, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
     }
   }
 }
@@ -427,7 +431,7 @@ void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (d / (16 * kDownWn));
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * ((d + kDownRows - 1) / kDownRows);
   hipLaunchKernelGGL(moe_down_kernel, dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
                      n_items, F, d, Y);
 }
