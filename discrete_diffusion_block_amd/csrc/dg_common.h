@@ -185,6 +185,23 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Direct global -> LDS copy of one 1 KiB fragment tile by one wave: lane l moves
+// the 16 bytes at src (its own slot of the tile) to lds_tile + 16 l, without
+// passing through registers.  NT marks the source as streamed once.  Completion
+// is tracked by the wave's vmcnt; the compiler does not order LDS reads after
+// these copies, so callers wait (vm_wait) and barrier explicitly.
+template <bool NT>
+__device__ __forceinline__ void tile_to_lds(const uint16_t* src, void* lds_tile) {
+  __builtin_amdgcn_global_load_lds(src, lds_tile, 16, 0, NT ? 2 : 0);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroups are dispatched round-robin over the XCDs (8 on MI355X), each with
 // its own L2.  xcd_swizzle(b, n) renumbers a 1-D grid of n blocks (n a multiple
 // of kXcd) so that consecutive logical indices run on the same XCD: blocks that

@@ -12,9 +12,9 @@
 // token tile and splits K between its waves (interleaved 64-wide k steps),
 // then reduces the four partial tiles through LDS in a fixed order.
 //
-// head_gemm: the tied LM head (N = 262144 rows of the embedding) -- workgroup
-// tile 64 features x 256 tokens, so the activation tiles are re-read from L2
-// only once per 64 vocabulary rows.
+// head_gemm: the tied LM head (N = 262144 rows of the embedding) -- 256 x 256
+// workgroup tiles with both operands staged through an LDS ring by direct
+// global->LDS copies.
 #include "dg_common.h"
 #include "dg_internal.h"
 
@@ -226,81 +226,106 @@ void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int
 
 // ---------------------------------------------------------------- LM head
 
-template <int WN, int WM>
+// Tied LM head, logits[m][v] = h[m] . E[v] in bf16.  Workgroup tile: 256 vocabulary
+// rows x 256 tokens; the 4 waves form a 2 x 2 grid of 128 x 128 sub-tiles (8 x 8
+// MFMA blocks each).  Operand tiles are staged through LDS: per 32-wide k step the
+// workgroup copies 16 weight and 16 token fragment tiles (32 KiB) straight from
+// global memory into a kHeadStages-deep LDS ring, so every weight byte is read
+// from HBM once, every token tile once per workgroup, and ~96 KiB of the weight
+// stream stays in flight per CU without occupying registers.
+constexpr int kHeadBlocks = 16;   // 16-row blocks per workgroup, on each side
+constexpr int kHeadStages = 4;
+constexpr int kHeadStageBytes = 2 * kHeadBlocks * 1024;
+
 __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ w,
-                                                 uint16_t* __restrict__ y, int M, int N, int K) {
+                                                 uint16_t* __restrict__ y, int M, int N, int K,
+                                                 int w_blocks) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int wn = wv & 1, wm = wv >> 1;
-  const int nb0 = blockIdx.x * 2 * WN + wn * WN;      // 16-row blocks of the head
-  const int mb0 = blockIdx.y * 2 * WM + wm * WM;      // 16-token blocks
-  const int nblocks = (N + 15) >> 4, mblocks = (M + 15) >> 4;
-  if (mb0 >= mblocks) return;
-  const uint16_t* wp[WN];
-  const uint16_t* xp[WM];
-#pragma unroll
-  for (int i = 0; i < WN; ++i) wp[i] = w + fm_tile(min(nb0 + i, nblocks - 1), 0, K, lane);
-#pragma unroll
-  for (int j = 0; j < WM; ++j) xp[j] = x + fm_tile(min(mb0 + j, mblocks - 1), 0, K, lane);
+  const int rb0 = blockIdx.x * kHeadBlocks, tb0 = blockIdx.y * kHeadBlocks;
+  const int t_blocks = (M + 15) >> 4;
+  const int nk = K >> 5;
 
-  f32x4 acc[WN][WM];
+  // copy duty: waves 0-1 stage the 16 weight tiles, waves 2-3 the 16 token tiles
+  const uint16_t* src[8];
 #pragma unroll
-  for (int i = 0; i < WN; ++i)
+  for (int u = 0; u < 8; ++u) {
+    const int q = wv * 8 + u;
+    src[u] = q < kHeadBlocks ? w + fm_tile(min(rb0 + q, w_blocks - 1), 0, K, lane)
+                             : x + fm_tile(min(tb0 + q - kHeadBlocks, t_blocks - 1), 0, K, lane);
+  }
+  auto issue = [&](int step, int slot) {
+    char* dst = ring + slot * kHeadStageBytes + wv * 8 * 1024;
+    if (wv < 2) {
 #pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 A0[WN][2], B0[WM][2], A1[WN][2], B1[WM][2];
-  auto load = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2], int it) {
-    const int k = it * 1024;
+      for (int u = 0; u < 8; ++u) tile_to_lds<true>(src[u] + step * 512, dst + u * 1024);
+    } else {
 #pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      A[i][0] = ld16_stream(wp[i] + k);
-      A[i][1] = ld16_stream(wp[i] + k + 512);
-    }
-#pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      B[j][0] = ld16(xp[j] + k);
-      B[j][1] = ld16(xp[j] + k + 512);
+      for (int u = 0; u < 8; ++u) tile_to_lds<false>(src[u] + step * 512, dst + u * 1024);
     }
   };
-  auto mma = [&](u32x4 (&A)[WN][2], u32x4 (&B)[WM][2]) {
+
+  const int wr = wv & 1, wt = wv >> 1;
+  f32x4 acc[8][8];
 #pragma unroll
-    for (int j = 0; j < WM; ++j)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int i = 0; i < WN; ++i) {
-        acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
-        acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
-      }
-  };
-  pipeline2(K >> 6, [&](int it) { load(A0, B0, it); }, [&](int it) { load(A1, B1, it); },
-            [&] { mma(A0, B0); }, [&] { mma(A1, B1); });
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-  for (int j = 0; j < WM; ++j) {
-    const int m = (mb0 + j) * 16 + r;
+  for (int st = 0; st < kHeadStages - 1; ++st)
+    if (st < nk) issue(st, st);
+  for (int s = 0; s < nk; ++s) {
+    // this wave's copies of step s have landed once at most the later steps' are in flight
+    const int later = min(kHeadStages - 2, nk - 1 - s);
+    if (later >= 2) vm_wait<16>();
+    else if (later == 1) vm_wait<8>();
+    else vm_wait<0>();
+    __syncthreads();   // every wave's copies of step s landed; slot (s - 1) is free
+    if (s + kHeadStages - 1 < nk) issue(s + kHeadStages - 1, (s + kHeadStages - 1) % kHeadStages);
+    const char* st = ring + (s % kHeadStages) * kHeadStageBytes + lane * 16;
+    u32x4 A[8], B[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = *reinterpret_cast<const u32x4*>(st + (wr * 8 + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      B[j] = *reinterpret_cast<const u32x4*>(st + (kHeadBlocks + wt * 8 + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
+  }
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = (tb0 + wt * 8 + j) * 16 + r;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const int n0 = (nb0 + i) * 16 + 4 * g;
-      uint16_t* dst = y + (size_t)m * N + n0;
-      if (n0 + 3 < N) {
-        u32x2 o;
-        o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
-        o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<u32x2*>(dst) = o;
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (n0 + e < N) dst[e] = f2bf(acc[i][j][e]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int n0 = (rb0 + wr * 8 + i) * 16 + 4 * g;
+      if (n0 >= N) continue;   // N is a multiple of 8, so n0 < N covers n0 .. n0 + 3
+      u32x2 o;
+      o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+      o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n0) = o;
     }
   }
 }
 
 void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
                       int K, hipStream_t s) {
-  constexpr int WN = 2, WM = 8;
-  dim3 grid((N + 32 * WN - 1) / (32 * WN), (M + 32 * WM - 1) / (32 * WM));
-  hipLaunchKernelGGL((head_gemm<WN, WM>), grid, dim3(256), 0, s, h, embed, logits, M, N, K);
+  constexpr size_t lds = (size_t)kHeadStages * kHeadStageBytes;
+  static bool raised = false;   // the 128 KiB ring exceeds the default dynamic-LDS limit
+  if (!raised) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&head_gemm),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    raised = true;
+  }
+  const int w_blocks = (N + 1 + 15) / 16;   // packed embedding rows: vocab + mask token, padded
+  dim3 grid((N + 16 * kHeadBlocks - 1) / (16 * kHeadBlocks), (M + 16 * kHeadBlocks - 1) / (16 * kHeadBlocks));
+  hipLaunchKernelGGL(head_gemm, grid, dim3(256), lds, s, h, embed, logits, M, N, K, w_blocks);
 }
 
 }  // namespace dg
