@@ -40,6 +40,18 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
 }
 
+// Two k tiles into one accumulator, issued back to back.  A dependent MFMA pair
+// forwards its accumulator and issues at the full rate (~16 clocks), while
+// consecutive MFMAs on different accumulators cost ~28 clocks each on this core
+// (measured), so every GEMM issues its MFMAs as such pairs; the scheduling
+// barrier stops the compiler from interleaving pairs back into that slow order.
+__device__ __forceinline__ f32x4 mfma16x2(u32x4 a0, u32x4 b0, u32x4 a1, u32x4 b1, f32x4 c) {
+  c = mfma16(a0, b0, c);
+  c = mfma16(a1, b1, c);
+  __builtin_amdgcn_sched_barrier(0);
+  return c;
+}
+
 // Two-stage software pipeline over n steps with no branch in the steady state:
 // load_a(i)/load_b(i) fill register set A/B with step i, mma_a()/mma_b() consume
 // them.  Keeping the loop body branch-free lets the compiler wait only for the
@@ -193,6 +205,19 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 template <bool NT>
 __device__ __forceinline__ void tile_to_lds(const uint16_t* src, void* lds_tile) {
   __builtin_amdgcn_global_load_lds(src, lds_tile, 16, 0, NT ? 2 : 0);
+}
+
+// LDS written only by direct copies looks never-stored to the optimizer, which may
+// then drop or hoist reads of it; reading through a laundered LDS-address-space
+// pointer keeps every read where it is written.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ lds_char* lds_launder(void* p) {
+  lds_char* q = (lds_char*)p;
+  asm volatile("" : "+v"(q));
+  return q;
+}
+__device__ __forceinline__ u32x4 ld16_lds(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
 }
 
 // s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave are in flight.

@@ -146,8 +146,7 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
     for (int i = 0; i < WN; ++i)
 #pragma unroll
       for (int j = 0; j < WM; ++j) {
-        acc[i][j] = mfma16(A[i][0], B[j][0], acc[i][j]);
-        acc[i][j] = mfma16(A[i][1], B[j][1], acc[i][j]);
+        acc[i][j] = mfma16x2(A[i][0], B[j][0], A[i][1], B[j][1], acc[i][j]);
       }
   };
 
@@ -226,85 +225,122 @@ void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int
 
 // ---------------------------------------------------------------- LM head
 
-// Tied LM head, logits[m][v] = h[m] . E[v] in bf16.  Workgroup tile: 256 vocabulary
-// rows x 256 tokens; the 4 waves form a 2 x 2 grid of 128 x 128 sub-tiles (8 x 8
-// MFMA blocks each).  Operand tiles are staged through LDS: per 32-wide k step the
-// workgroup copies 16 weight and 16 token fragment tiles (32 KiB) straight from
-// global memory into a kHeadStages-deep LDS ring, so every weight byte is read
-// from HBM once, every token tile once per workgroup, and ~96 KiB of the weight
-// stream stays in flight per CU without occupying registers.
-constexpr int kHeadBlocks = 16;   // 16-row blocks per workgroup, on each side
-constexpr int kHeadStages = 4;
-constexpr int kHeadStageBytes = 2 * kHeadBlocks * 1024;
+// Tied LM head, logits[m][v] = h[m] . E[v] in bf16.  Workgroup tile: 256
+// vocabulary rows x 256 tokens; the 4 waves form a 2 x 2 grid of 128 x 128
+// sub-tiles (8 x 8 MFMA blocks each, accumulators in AGPRs).  Operands are staged
+// through LDS by direct global->LDS copies in 64-wide k steps (two 1 KiB fragment
+// tiles per 16-row block).  The weight stream comes from HBM, so its ring is three
+// steps deep (copies go out two steps ahead); the token tiles are L2 hits and
+// ride a two-step ring one step ahead.  Weights are read from HBM exactly once and
+// every token tile once per workgroup.  Each accumulator takes its two k tiles
+// back to back (a dependent MFMA pair issues at the full rate).
+constexpr int kHeadRB = 16;       // 16-row weight blocks per workgroup
+constexpr int kHeadTB = 16;       // 16-token blocks per workgroup
+constexpr int kHeadKT = 2;        // 32-wide k tiles per step
+constexpr int kHeadWSlots = 3, kHeadXSlots = 2;
+constexpr int kHeadWBytes = kHeadRB * kHeadKT * 1024;   // one step of weights
+constexpr int kHeadXBytes = kHeadTB * kHeadKT * 1024;   // one step of token tiles
+constexpr int kHeadLds = kHeadWSlots * kHeadWBytes + kHeadXSlots * kHeadXBytes;
+constexpr int kHeadWCopies = kHeadRB * kHeadKT / 4;   // per wave per step
+constexpr int kHeadXCopies = kHeadTB * kHeadKT / 4;
 
 __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ w,
                                                  uint16_t* __restrict__ y, int M, int N, int K,
-                                                 int w_blocks) {
-  extern __shared__ __attribute__((aligned(1024))) char ring[];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+                                                 int w_blocks, int n_row_tiles, int n_tok_tiles) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];   // [W slots][X slots]
+  constexpr int WI = kHeadRB / 2, WJ = kHeadTB / 2;   // MFMA blocks per wave
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int rb0 = blockIdx.x * kHeadBlocks, tb0 = blockIdx.y * kHeadBlocks;
+  const int b = blockIdx.x, xcd = b % kXcd, rank = b / kXcd;
+  const int row_tile = (rank / n_tok_tiles) * kXcd + xcd, tok_tile = rank % n_tok_tiles;
+  if (row_tile >= n_row_tiles) return;
+  const int rb0 = row_tile * kHeadRB, tb0 = tok_tile * kHeadTB;
   const int t_blocks = (M + 15) >> 4;
-  const int nk = K >> 5;
+  const int nk = K / (32 * kHeadKT);
 
-  // copy duty: waves 0-1 stage the 16 weight tiles, waves 2-3 the 16 token tiles
-  const uint16_t* src[8];
+  // copy duty: wave wv copies weight blocks and token blocks wv * (RB / 4) + u;
+  // in a slot, block q's k tiles sit at (q * kHeadKT + t) KiB
+  constexpr int WB = kHeadRB / 4, XB = kHeadTB / 4;
+  const uint16_t* wsrc[WB];
+  const uint16_t* xsrc[XB];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int q = wv * 8 + u;
-    src[u] = q < kHeadBlocks ? w + fm_tile(min(rb0 + q, w_blocks - 1), 0, K, lane)
-                             : x + fm_tile(min(tb0 + q - kHeadBlocks, t_blocks - 1), 0, K, lane);
-  }
-  auto issue = [&](int step, int slot) {
-    char* dst = ring + slot * kHeadStageBytes + wv * 8 * 1024;
-    if (wv < 2) {
+  for (int u = 0; u < WB; ++u) wsrc[u] = w + fm_tile(min(rb0 + wv * WB + u, w_blocks - 1), 0, K, lane);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) tile_to_lds<true>(src[u] + step * 512, dst + u * 1024);
-    } else {
+  for (int u = 0; u < XB; ++u) xsrc[u] = x + fm_tile(min(tb0 + wv * XB + u, t_blocks - 1), 0, K, lane);
+  char* const wring = ring;
+  char* const xring = ring + kHeadWSlots * kHeadWBytes;
+  auto issue_w = [&](int step) {
+    char* dst = wring + (step % kHeadWSlots) * kHeadWBytes + wv * WB * kHeadKT * 1024;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) tile_to_lds<false>(src[u] + step * 512, dst + u * 1024);
-    }
+    for (int u = 0; u < WB; ++u)
+#pragma unroll
+      for (int t = 0; t < kHeadKT; ++t)
+        tile_to_lds<true>(wsrc[u] + (step * kHeadKT + t) * 512, dst + (u * kHeadKT + t) * 1024);
+  };
+  auto issue_x = [&](int step) {
+    char* dst = xring + (step % kHeadXSlots) * kHeadXBytes + wv * XB * kHeadKT * 1024;
+#pragma unroll
+    for (int u = 0; u < XB; ++u)
+#pragma unroll
+      for (int t = 0; t < kHeadKT; ++t)
+        tile_to_lds<false>(xsrc[u] + (step * kHeadKT + t) * 512, dst + (u * kHeadKT + t) * 1024);
   };
 
   const int wr = wv & 1, wt = wv >> 1;
-  f32x4 acc[8][8];
+  f32x4 acc[WI][WJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_char* const lw = lds_launder(wring);
+  lds_char* const lx = lds_launder(xring);
 
-#pragma unroll
-  for (int st = 0; st < kHeadStages - 1; ++st)
-    if (st < nk) issue(st, st);
+  // Copy order: W(0), X(0), W(1), then after step s's barrier X(s + 1), W(s + 2).
+  // At the top of step s the wave's copies of X(s) and W(s) have landed once at
+  // most the W(s + 1) batch that follows X(s) is in flight; the barrier then makes
+  // all waves' copies visible and retires every read of the slots refilled next
+  // (they held step s - 1).
+  issue_w(0);
+  issue_x(0);
+  if (nk > 1) issue_w(1);
+  u32x4 A[WI][kHeadKT], B[2][kHeadKT];
+  static_assert(kHeadKT == 2, "MFMA pairs");
   for (int s = 0; s < nk; ++s) {
-    // this wave's copies of step s have landed once at most the later steps' are in flight
-    const int later = min(kHeadStages - 2, nk - 1 - s);
-    if (later >= 2) vm_wait<16>();
-    else if (later == 1) vm_wait<8>();
+    if (s + 1 < nk) vm_wait<kHeadWCopies>();
     else vm_wait<0>();
-    __syncthreads();   // every wave's copies of step s landed; slot (s - 1) is free
-    if (s + kHeadStages - 1 < nk) issue(s + kHeadStages - 1, (s + kHeadStages - 1) % kHeadStages);
-    const char* st = ring + (s % kHeadStages) * kHeadStageBytes + lane * 16;
-    u32x4 A[8], B[8];
+    __builtin_amdgcn_s_barrier();
+    if (s + 1 < nk) issue_x(s + 1);
+    if (s + 2 < nk) issue_w(s + 2);
+    const lds_char* sw = lw + (s % kHeadWSlots) * kHeadWBytes + lane * 16;
+    const lds_char* sx = lx + (s % kHeadXSlots) * kHeadXBytes + lane * 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A[i] = *reinterpret_cast<const u32x4*>(st + (wr * 8 + i) * 1024);
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      B[j] = *reinterpret_cast<const u32x4*>(st + (kHeadBlocks + wt * 8 + j) * 1024);
+      for (int t = 0; t < kHeadKT; ++t) A[i][t] = ld16_lds(sw + ((wr * WI + i) * kHeadKT + t) * 1024);
+    auto readB = [&](int j) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+      for (int t = 0; t < kHeadKT; ++t) B[j & 1][t] = ld16_lds(sx + ((wt * WJ + j) * kHeadKT + t) * 1024);
+    };
+    readB(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
+    for (int j = 0; j < WJ; ++j) {
+      if (j + 1 < WJ) readB(j + 1);   // one token column ahead
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < WI; ++i)
+        acc[i][j] = mfma16x2(A[i][0], B[j & 1][0], A[i][1], B[j & 1][1], acc[i][j]);
+    }
   }
 
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = (tb0 + wt * 8 + j) * 16 + r;
+  for (int j = 0; j < WJ; ++j) {
+    const int m = (tb0 + wt * WJ + j) * 16 + r;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n0 = (rb0 + wr * 8 + i) * 16 + 4 * g;
+    for (int i = 0; i < WI; ++i) {
+      const int n0 = (rb0 + wr * WI + i) * 16 + 4 * g;
       if (n0 >= N) continue;   // N is a multiple of 8, so n0 < N covers n0 .. n0 + 3
       u32x2 o;
       o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
@@ -316,16 +352,19 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
 
 void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
                       int K, hipStream_t s) {
-  constexpr size_t lds = (size_t)kHeadStages * kHeadStageBytes;
-  static bool raised = false;   // the 128 KiB ring exceeds the default dynamic-LDS limit
+  constexpr size_t lds = (size_t)kHeadLds;
+  static bool raised = false;   // the ring exceeds the default dynamic-LDS limit
   if (!raised) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&head_gemm),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     raised = true;
   }
   const int w_blocks = (N + 1 + 15) / 16;   // packed embedding rows: vocab + mask token, padded
-  dim3 grid((N + 16 * kHeadBlocks - 1) / (16 * kHeadBlocks), (M + 16 * kHeadBlocks - 1) / (16 * kHeadBlocks));
-  hipLaunchKernelGGL(head_gemm, grid, dim3(256), lds, s, h, embed, logits, M, N, K, w_blocks);
+  const int n_row = (N + 16 * kHeadRB - 1) / (16 * kHeadRB);
+  const int n_tok = (M + 16 * kHeadTB - 1) / (16 * kHeadTB);
+  const int blocks = kXcd * ((n_row + kXcd - 1) / kXcd) * n_tok;
+  hipLaunchKernelGGL(head_gemm, dim3(blocks), dim3(256), lds, s, h, embed, logits, M, N, K, w_blocks,
+                     n_row, n_tok);
 }
 
 }  // namespace dg

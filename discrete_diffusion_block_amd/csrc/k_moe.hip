@@ -255,9 +255,7 @@ __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) acc[i][j] = mfma16(W[i][q], X[j][q], acc[i][j]);
+      for (int i = 0; i < NW; ++i) acc[i][j] = mfma16x2(W[i][0], X[j][0], W[i][1], X[j][1], acc[i][j]);
   };
 #pragma unroll
   for (int i = 0; i < NW; ++i)
