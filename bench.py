@@ -127,6 +127,55 @@ def cpu_baseline(budget_note: str):
     }
 
 
+def pmc_workload(n_steps: int = 2) -> None:
+    """Workload for hardware-counter passes (rocprofv3 --pmc): first the library's
+    plain 256 MiB copy kernel (a known byte count that calibrates the traffic
+    counters), then n_steps denoising steps of the full model over a 1024-token
+    prefix.  Nothing is timed."""
+    import torch
+    from discrete_diffusion_block_amd import dg, synth
+
+    cfg = synth.CONFIGS["full"]
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dg.dg_test_copy(src, dst, src.numel())      # dg::copy16_kernel: reads and writes 256 MiB
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.make_weights(cfg, device="cuda")
+    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=1024 + cfg.canvas, free_source=True)
+    eng.prefill_kv(synth.make_prompt(cfg, 1, 1024, device="cuda"))
+    logits = torch.empty(1, cfg.canvas, cfg.vocab, dtype=torch.bfloat16, device="cuda")
+    canvas = torch.full((1, cfg.canvas), cfg.vocab, dtype=torch.int32, device="cuda")
+    for s in range(n_steps):
+        eng.denoise_step(canvas, 1.0 - s / n_steps, logits)
+    torch.cuda.synchronize()
+    log(f"pmc workload done ({n_steps} denoising steps)")
+
+
+def summarize_pmc(root: str) -> str:
+    """Per-kernel mean of every counter in the rocprofv3 counter CSVs under root,
+    over the denoising passes of the counter workload only: dispatches from the
+    third embedding kernel on (the 1024-token prefill runs as two 512-token passes
+    before it)."""
+    import csv
+    import glob
+    import collections
+    rows = []
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    embeds = sorted({int(r["Dispatch_Id"]) for r in rows if "embed_norm_kernel" in r["Kernel_Name"]})
+    start = embeds[2] if len(embeds) > 2 else 0
+    agg = collections.defaultdict(list)
+    for r in rows:
+        if int(r["Dispatch_Id"]) >= start or "copy16_kernel" in r["Kernel_Name"]:
+            agg[(r["Kernel_Name"].split("(")[0][:60], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    lines = [f"{k:62s} {c:14s} dispatches {len(v):5d} mean {sum(v) / len(v):14.1f}"
+             for (k, c), v in sorted(agg.items())]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +185,14 @@ def main():
     ap.add_argument("--gamma", type=float, default=2.0)
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run the hardware-counter workload (copy calibration + 2 denoising steps) and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel counter means from rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the engine runs one process on one MI355X; see the design notes on sharding).",
@@ -150,6 +206,9 @@ def main():
         log("no GPU visible")
         sys.exit(1)
     dg.lib()
+    if args.pmc_workload:
+        pmc_workload()
+        return
     cfg = synth.CONFIGS["full"]
     C, V = cfg.canvas, cfg.vocab
     n_blocks = args.warmup + args.steps + 3

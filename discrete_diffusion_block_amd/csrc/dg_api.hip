@@ -28,6 +28,12 @@ struct dg_ctx {
   const float* final_norm;
   std::vector<dg_layer_weights> layers;
   mutable Prof prof;
+  // Side stream for the shared expert, which runs concurrently with the routed
+  // experts' routing chain; forked from and joined back into the caller's stream
+  // with events.  Created on first use, on the device current at that time.
+  mutable hipStream_t side = nullptr;
+  mutable hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  mutable int side_dev = -1;
 };
 
 namespace {
@@ -72,6 +78,33 @@ struct Timed {
     Timed _timed(ctx, kind, s);   \
     stmt;                         \
   } while (0)
+#define DG_TIMED_ON(ctx, kind, strm, stmt) \
+  do {                                     \
+    Timed _timed(ctx, kind, strm);         \
+    stmt;                                  \
+  } while (0)
+
+// The side stream for the current device, or nullptr (work then stays on the
+// caller's stream) if it cannot be set up or the context moved to another device.
+hipStream_t side_stream(const dg_ctx* ctx) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (ctx->side) return ctx->side_dev == dev ? ctx->side : nullptr;
+  hipStream_t st = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+    if (a) (void)hipEventDestroy(a);
+    (void)hipStreamDestroy(st);
+    return nullptr;
+  }
+  ctx->side = st;
+  ctx->ev_fork = a;
+  ctx->ev_join = b;
+  ctx->side_dev = dev;
+  return st;
+}
 
 constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
 constexpr size_t kAlign = 256;
@@ -97,6 +130,7 @@ struct Ws {
   uint16_t* A;     // expert SwiGLU outputs, fragment-major [P_pad][F]
   float* Y;        // expert outputs fp32 [P][d]
   uint16_t* As;    // shared-expert SwiGLU output, fragment-major [M_pad][Fs]
+  float* ys;       // shared-expert output fp32 row-major [M][d]
   float4* part;
   int* part_arg;
 };
@@ -151,6 +185,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->A = cv.take<uint16_t>(round16(P) * c.expert_ffn);
   ws->Y = cv.take<float>(P * c.d_model);
   ws->As = cv.take<uint16_t>(Mp * c.shared_ffn);
+  ws->ys = cv.take<float>(M * c.d_model);
   carve_sampler(cv, batch, c.canvas, c.vocab, ws);
   return cv.off + kAlign;
 }
@@ -220,6 +255,24 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_ATTENTION, launch_attention(ws.q, hq, kvl, g, ws.o, s));
     DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
     DG_TIMED(ctx, DG_K_NORM, launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s));
+    // The shared expert depends only on h: it runs on the side stream while the
+    // routed experts' routing chain (small, latency-bound kernels) runs here.  It
+    // reads h and writes As and ys, which nothing on this stream touches before
+    // the join; the combine kernel adds ys.
+    hipStream_t s2 = side_stream(ctx);
+    if (s2) {
+      (void)hipEventRecord(ctx->ev_fork, s);
+      (void)hipStreamWaitEvent(s2, ctx->ev_fork, 0);
+    } else {
+      s2 = s;
+    }
+    DG_TIMED_ON(ctx, DG_K_SHARED_GATE_UP, s2,
+                launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s2));
+    DG_TIMED_ON(ctx, DG_K_SHARED_DOWN, s2,
+                launch_gemm_f32(ws.As, L.ws_down, ws.ys, M, d, c.shared_ffn, /*add=*/false, s2));
+    if (s2 != s) {
+      (void)hipEventRecord(ctx->ev_join, s2);
+    }
     DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
     DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
     DG_TIMED(ctx, DG_K_ROUTE,
@@ -233,11 +286,10 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_MOE_DOWN,
              launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
                              c.expert_ffn, d, ws.Y, s));
-    DG_TIMED(ctx, DG_K_SHARED_GATE_UP, launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s));
-    DG_TIMED(ctx, DG_K_SHARED_DOWN,
-             launch_gemm_f32(ws.As, L.ws_down, ws.x, M, d, c.shared_ffn, /*add=*/true, s));
+    if (s2 != s) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
-    DG_TIMED(ctx, DG_K_COMBINE, launch_combine(ws.x, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s));
+    DG_TIMED(ctx, DG_K_COMBINE,
+             launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s));
   }
   if (g.denoise) DG_TIMED(ctx, DG_K_HEAD, launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d, s));
   return check_launch("transformer pass");
@@ -372,6 +424,12 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out) {
 void dg_destroy(dg_ctx* ctx) {
   if (!ctx) return;
   for (hipEvent_t e : ctx->prof.ev) (void)hipEventDestroy(e);
+  if (ctx->side) {
+    (void)hipStreamSynchronize(ctx->side);
+    (void)hipStreamDestroy(ctx->side);
+    (void)hipEventDestroy(ctx->ev_fork);
+    (void)hipEventDestroy(ctx->ev_join);
+  }
   delete ctx;
 }
 
@@ -579,6 +637,13 @@ dg_status dg_test_gemm(const uint16_t* d_x, const uint16_t* d_w, float* d_y, int
     return fail(DG_ERR_INVALID_ARG, "bad GEMM arguments");
   launch_gemm_f32(d_x, d_w, d_y, M, N, K, false, (hipStream_t)stream);
   return check_launch("gemm");
+}
+
+dg_status dg_test_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream) {
+  if (!d_src || !d_dst || n_bytes == 0 || n_bytes % 16)
+    return fail(DG_ERR_INVALID_ARG, "copy needs non-NULL buffers and a positive multiple of 16 bytes");
+  launch_copy16(d_src, d_dst, n_bytes, (hipStream_t)stream);
+  return check_launch("copy");
 }
 
 }  // extern "C"

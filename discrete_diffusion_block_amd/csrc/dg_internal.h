@@ -33,8 +33,8 @@ void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float
                        hipStream_t s);
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
                     hipStream_t s);
-void launch_combine(float* x, const float* Y, const float* wts, const int32_t* inv, int M, int k,
-                    int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
+void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
+                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
 
 // ---- dense GEMMs ----
 // y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).
@@ -84,6 +84,7 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, hipStream_t s);
+void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 }  // namespace dg

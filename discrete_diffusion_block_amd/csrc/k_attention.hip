@@ -38,10 +38,18 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
-  const int b = blockIdx.z, head = blockIdx.y;
-  const int i0 = blockIdx.x * 16;
+  // XCD-aware order: block bid runs on XCD bid % 8; every workgroup of one
+  // (sequence, kv head) pair -- its q heads x query tiles -- runs on the same XCD,
+  // so that pair's keys and values leave HBM once
+  const int grp = hq / kv.hkv, q_tiles = (g.n + 15) / 16, per_pair = grp * q_tiles;
+  const int rank = blockIdx.x / kXcd;
+  const int pair = (rank / per_pair) * kXcd + (int)(blockIdx.x % kXcd);
+  if (pair >= g.batch * kv.hkv) return;   // uniform per workgroup
+  const int b = pair / kv.hkv, kvh = pair - b * kv.hkv;
+  const int rem = rank % per_pair;
+  const int head = kvh * grp + rem / q_tiles;
+  const int i0 = (rem % q_tiles) * 16;
   const int n = g.n, len = g.len[b];
-  const int kvh = head / (hq / kv.hkv);
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
   // query fragments: q is fragment-major per (sequence, head), [n_pad][HD]
@@ -188,7 +196,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
 
 void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,
                       uint16_t* o, hipStream_t s) {
-  dim3 grid((g.n + 15) / 16, hq, g.batch);
+  const int pairs = g.batch * kv.hkv, per_pair = (hq / kv.hkv) * ((g.n + 15) / 16);
+  dim3 grid(kXcd * ((pairs + kXcd - 1) / kXcd) * per_pair);
   switch (kv.hd) {
     case 32: hipLaunchKernelGGL(attention_kernel<32>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
     case 64: hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;

@@ -130,8 +130,10 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, i
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, d);
 }
 
-// x[m] += sum_j w[m][j] * Y[inv[m*k + j]]  (j ascending), then h[m] = norm(x[m]) * next_gain.
-__global__ __launch_bounds__(256) void combine_kernel(float* x, const float* Y, const float* wts,
+// x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]
+// (j ascending), then h[m] = norm(x[m]) * next_gain.
+__global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys, const float* Y,
+                                                      const float* wts,
                                                       const int32_t* inv, int k, int d,
                                                       const float* next_gain, float eps,
                                                       uint16_t* h) {
@@ -147,8 +149,11 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* Y, 
   float* xr = x + (size_t)m * d;
   float ss = 0.f;
   for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
-    float v[8];
+    float v[8], u[8];
     load8(xr + c, v);
+    load8(ys + (size_t)m * d + c, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = u[e] + v[e];
     for (int j = 0; j < k; ++j) {
       float y[8];
       load8(Y + (size_t)slot[j] * d + c, y);
@@ -162,15 +167,28 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* Y, 
   if (next_gain) norm_row(xr, next_gain, eps, h, m, d, ss, red);
 }
 
-void launch_combine(float* x, const float* Y, const float* wts, const int32_t* inv, int M, int k,
-                    int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(M), dim3(256), 0, s, x, Y, wts, inv, k, d, next_gain, eps,
+void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
+                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(M), dim3(256), 0, s, x, ys, Y, wts, inv, k, d, next_gain, eps,
                      h);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void copy16_kernel(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
+  const size_t n = n_bytes / 16;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(copy16_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const u32x4*>(src),
+                     reinterpret_cast<u32x4*>(dst), n);
 }
 
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {

@@ -10,7 +10,8 @@
 //
 // dense_gemm: a workgroup of 4 waves owns one (WN x 16) feature x (WM x 16)
 // token tile and splits K between its waves (interleaved 64-wide k steps),
-// then reduces the four partial tiles through LDS in a fixed order.
+// then reduces the four partial tiles through LDS in a fixed order.  All token
+// tiles of a weight tile run on one XCD, so the weights leave HBM once.
 //
 // head_gemm: the tied LM head (N = 262144 rows of the embedding) -- 256 x 256
 // workgroup tiles with both operands staged through an LDS ring by direct
@@ -108,8 +109,14 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
   extern __shared__ f32x4 red[];  // [NW waves][WN][WM][64 lanes]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int blk0 = blockIdx.x * WN;
-  const int mb0 = blockIdx.y * WM;
+  // XCD-aware tile order: block b runs on XCD b % 8, and the token tiles of one
+  // weight tile take consecutive ranks on that XCD, so they share its L2 copy
+  const int n_tiles = (a.nblk + WN - 1) / WN, m_tiles = (a.M + 16 * WM - 1) / (16 * WM);
+  const int rank = blockIdx.x / kXcd;
+  const int n_tile = (rank / m_tiles) * kXcd + (int)(blockIdx.x % kXcd);
+  if (n_tile >= n_tiles) return;   // uniform per workgroup
+  const int blk0 = n_tile * WN;
+  const int mb0 = (rank % m_tiles) * WM;
 
   // fragment tiles (rb, kb): rb clamped to the last real block (dropped in the epilogue)
   const uint16_t* wp[WN];
@@ -177,9 +184,10 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
 
 template <int WN, int WM, int EPI, int NW = 4>
 static void run_dense(const DenseArgs& a, hipStream_t s) {
-  dim3 grid((a.nblk + WN - 1) / WN, (a.M + 16 * WM - 1) / (16 * WM));
+  const int n_tiles = (a.nblk + WN - 1) / WN, m_tiles = (a.M + 16 * WM - 1) / (16 * WM);
+  const int blocks = kXcd * ((n_tiles + kXcd - 1) / kXcd) * m_tiles;
   const size_t lds = sizeof(f32x4) * NW * WN * WM * 64;
-  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), grid, dim3(64 * NW), lds, s, a);
+  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), lds, s, a);
 }
 
 void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,

@@ -85,6 +85,7 @@ def lib():
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
             "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
+            "dg_test_copy": [vp, vp, C.c_size_t, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -282,6 +283,11 @@ def dg_test_eb_select(entropy: torch.Tensor, argmax: torch.Tensor, canvas: torch
     b, c = canvas.shape
     _check(lib().dg_test_eb_select(_p(entropy), _p(argmax), _p(canvas), b, c, vocab, float(gamma),
                                    int(bool(commit_all)), _p(n_masked), _stream(stream)))
+
+
+def dg_test_copy(src: torch.Tensor, dst: torch.Tensor, n_bytes: int, stream=None) -> None:
+    """Plain 16-byte-vector device copy (hardware byte-counter calibration)."""
+    _check(lib().dg_test_copy(_p(src), _p(dst), n_bytes, _stream(stream)))
 
 
 def dg_test_gemm(x_packed: torch.Tensor, w_packed: torch.Tensor, y: torch.Tensor, M: int, N: int,

@@ -214,7 +214,8 @@ dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_
  * ids/w as dg_test_router_topk; cnt int32 [E]; poff int32 [E+1] (16-aligned
  * padded slot offsets); perm int32 [M*k + 15E] (token of each padded slot, -1 on
  * padding); inv int32 [M*k] (slot of assignment m*k+j); items int32x2
- * [(M*k+31)/32 + E] and n_items int32 [1]. */
+ * [(M*k+63)/64 + E] -- (expert, first token) of every group of up to 64 of an
+ * expert's tokens, experts ascending -- and n_items int32 [1]. */
 dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
                         int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
                         int32_t* d_items, int32_t* d_n_items, void* stream);
@@ -230,6 +231,11 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
  * x and w both plain-packed (fragment-major, rows padded to 16). */
 dg_status dg_test_gemm(const uint16_t* d_x, const uint16_t* d_w, float* d_y, int M, int N, int K,
                        void* stream);
+
+/* Plain device copy of n_bytes (a positive multiple of 16) from d_src to d_dst
+ * with 16-byte loads and stores: a kernel of known traffic, for calibrating the
+ * hardware byte counters against which the other kernels are measured. */
+dg_status dg_test_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream);
 
 #ifdef __cplusplus
 }

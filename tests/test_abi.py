@@ -118,3 +118,9 @@ def test_sampler_validates(L):
     st = L.dg_sample_eb(C.c_void_p(0x1000), C.c_void_p(0x1000), 1, 256, 262144, float("nan"), 0, None,
                         None, C.c_void_p(0x1000), C.c_void_p(0x1000), need, None)
     assert st == -1
+
+
+def test_copy_tap_validates(L):
+    for n in (0, 24, 17):                                     # empty, not a multiple of 16
+        assert L.dg_test_copy(C.c_void_p(0x1000), C.c_void_p(0x2000), n, None) == -1
+    assert L.dg_test_copy(None, C.c_void_p(0x2000), 32, None) == -1

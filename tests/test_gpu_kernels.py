@@ -38,6 +38,18 @@ def test_gemm_matches_fp64(M, N, K):
     assert np.all(err <= bound), float((err / bound).max())
 
 
+@pytest.mark.parametrize("n_bytes", [16, 4096 + 48, 64 << 20])
+def test_copy_tap_bit_exact(n_bytes):
+    print(f"copy {n_bytes} bytes", flush=True)
+    g = torch.Generator().manual_seed(n_bytes % 1000)
+    src = torch.randint(0, 256, (n_bytes,), generator=g, dtype=torch.uint8).cuda()
+    dst = torch.zeros(n_bytes + 64, dtype=torch.uint8, device="cuda")
+    dg.dg_test_copy(src, dst, n_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n_bytes], src)
+    assert int(dst[n_bytes:].count_nonzero()) == 0            # nothing written past the end
+
+
 @pytest.mark.parametrize("M,E,k", [(300, 128, 8), (64, 8, 2), (5, 256, 16), (33, 4, 4)])
 def test_router_topk_bit_exact(M, E, k):
     print(f"topk M={M} E={E} k={k}", flush=True)
