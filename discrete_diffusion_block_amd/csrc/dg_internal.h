@@ -63,6 +63,7 @@ int moe_max_slots(int M, int k, int E);   // padded slot space: M*k + 15*E
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
                   hipStream_t s);
+
 void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, int M, int k, int E,
                    int d, uint16_t* xg, hipStream_t s);
 void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,

@@ -19,56 +19,72 @@ namespace dg {
 
 // ---------------------------------------------------------------- top-k
 
-// One wave per token.  Experts are ranked by (logit desc, id asc); NaN logits
-// rank below every number.  Weights: softmax over the k selected logits.
+// One wave ranks one token's E router logits by (logit desc, id asc); NaN logits
+// rank below every number.  ids/w get the k selected experts and the softmax of
+// their logits.  Selected logits stay in registers (k <= 16).
+__device__ __forceinline__ void topk_row(const float* __restrict__ rr, int E, int k, int lane,
+                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    float x = e < E ? rr[e] : -INFINITY;
+    if (x != x) x = -INFINITY;
+    v[i] = x;
+  }
+  unsigned taken = 0;
+  float sel[16];
+  int sid[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    sel[t] = -INFINITY;
+    sid[t] = 0;
+    if (t < k) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      sel[t] = bv;
+      sid[t] = bi;
+    }
+  }
+  float z = 0.f, ex[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    ex[t] = (t < k && sel[t] != -INFINITY) ? expf(sel[t] - sel[0]) : 0.f;
+    z += ex[t];
+  }
+  // lane t < k writes selection t
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    if (t < k && lane == t) {
+      ids[t] = sid[t];
+      w[t] = ex[t] / z;
+    }
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ r, int M, int E, int k,
                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    float x = e < E ? r[(size_t)m * E + e] : -INFINITY;
-    if (x != x) x = -INFINITY;
-    v[i] = e < E ? x : -INFINITY;
-  }
-  unsigned taken = 0;
-  float sel[16];
-  for (int t = 0; t < k; ++t) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    sel[t] = bv;
-    if (lane == 0) ids[(size_t)m * k + t] = bi;
-  }
-  if (lane == 0) {
-    float z = 0.f;
-    float ex[16];
-    for (int t = 0; t < k; ++t) {
-      ex[t] = (sel[t] == -INFINITY) ? 0.f : expf(sel[t] - sel[0]);
-      z += ex[t];
-    }
-    for (int t = 0; t < k; ++t) w[(size_t)m * k + t] = ex[t] / z;
-  }
+  topk_row(r + (size_t)m * E, E, k, lane, ids + (size_t)m * k, w + (size_t)m * k);
 }
 
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s) {
@@ -77,30 +93,34 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 
 // ---------------------------------------------------------------- permutation
 
-// Stable counting sort of the M*k assignments (a = m*k + j) by expert, in one
-// 1024-thread workgroup.  Expert e owns the padded slot range
-// [poff[e], poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered
-// rows start on a fragment-tile boundary; slots keep assignment order within an
-// expert.  perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
-// (expert, first token) of every kMoeGroup-token group.  Offsets come from one-wave
-// prefix scans; slot ranks from per-wave match counts.
-__global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
-                                                     int E, int P, int32_t* __restrict__ cnt,
-                                                     int32_t* __restrict__ poff,
-                                                     int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ inv,
-                                                     int2* __restrict__ items,
-                                                     int32_t* __restrict__ n_items,
-                                                     int32_t* __restrict__ cnt_log) {
-  __shared__ int hist[256];
-  __shared__ int base[256];
-  __shared__ int ibase[256];
-  __shared__ int wcnt[16][256];
+// Stable counting sort of the A = M*k assignments (a = m*k + j) by expert, by one
+// workgroup of NW waves.  Expert e owns the padded slot range [poff[e],
+// poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered rows start on
+// a fragment-tile boundary; slots keep assignment order within an expert.
+// perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
+// (expert, first token) of every kMoeGroup-token group.  Offsets come from
+// one-wave prefix scans; the rank of an assignment among equal experts of its
+// wave comes from ballots on the expert id's bits.
+template <int NW>
+struct RouteLds {
+  int hist[256];
+  int base[256];
+  int ibase[256];
+  int wcnt[NW][256];
+};
+
+template <int NW>
+__device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E, int P,
+                            int32_t* __restrict__ cnt, int32_t* __restrict__ poff,
+                            int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                            int2* __restrict__ items, int32_t* __restrict__ n_items,
+                            int32_t* __restrict__ cnt_log, RouteLds<NW>& L) {
+  constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += blockDim.x) hist[e] = 0;
-  for (int i = tid; i < P; i += blockDim.x) perm[i] = -1;
+  for (int e = tid; e < E; e += NT) L.hist[e] = 0;
+  for (int i = tid; i < P; i += NT) perm[i] = -1;
   __syncthreads();
-  for (int a = tid; a < A; a += blockDim.x) atomicAdd(&hist[ids[a]], 1);
+  for (int a = tid; a < A; a += NT) atomicAdd(&L.hist[ids[a]], 1);
   __syncthreads();
   if (wv == 0) {
     // lane owns experts [lane*epl, lane*epl + epl)
@@ -109,8 +129,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
-        ps += (hist[e] + 15) & ~15;
-        is += (hist[e] + kMoeGroup - 1) / kMoeGroup;
+        ps += (L.hist[e] + 15) & ~15;
+        is += (L.hist[e] + kMoeGroup - 1) / kMoeGroup;
       }
     }
     int incl_p = ps, incl_i = is;
@@ -126,12 +146,12 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
-        const int c = hist[e];
-        base[e] = run_p;
+        const int c = L.hist[e];
+        L.base[e] = run_p;
         poff[e] = run_p;
         cnt[e] = c;
         if (cnt_log) cnt_log[e] = c;
-        ibase[e] = run_i;
+        L.ibase[e] = run_i;
         run_p += (c + 15) & ~15;
         run_i += (c + kMoeGroup - 1) / kMoeGroup;
       }
@@ -142,40 +162,54 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    int it = ibase[e];
-    for (int t0 = 0; t0 < hist[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
+  for (int e = tid; e < E; e += NT) {
+    int it = L.ibase[e];
+    for (int t0 = 0; t0 < L.hist[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
   }
-  for (int start = 0; start < A; start += blockDim.x) {
-    for (int i = tid; i < 16 * E; i += blockDim.x) wcnt[i / E][i % E] = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int start = 0; start < A; start += NT) {
+    for (int i = tid; i < NW * E; i += NT) L.wcnt[i / E][i % E] = 0;
     __syncthreads();
     const int a = start + tid;
     const int e = a < A ? ids[a] : -1;
-    int rank = 0, tot = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j, 64);
-      if (ej == e) {
-        tot += 1;
-        if (j < lane) rank += 1;
-      }
+    // lanes holding the same expert: agree on validity and on each of 8 id bits
+    unsigned long long same = __ballot(e >= 0);
+    if (e < 0) same = ~same;
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const unsigned long long b1 = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? b1 : ~b1;
     }
-    if (e >= 0 && rank == tot - 1) wcnt[wv][e] = tot;
+    const int rank = __popcll(same & below), tot = __popcll(same);
+    if (e >= 0 && rank == tot - 1) L.wcnt[wv][e] = tot;
     __syncthreads();
     if (e >= 0) {
       int before = 0;
-      for (int w2 = 0; w2 < wv; ++w2) before += wcnt[w2][e];
-      const int slot = base[e] + before + rank;
+      for (int w2 = 0; w2 < wv; ++w2) before += L.wcnt[w2][e];
+      const int slot = L.base[e] + before + rank;
       perm[slot] = a / k;
       inv[a] = slot;
     }
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += blockDim.x) {
+    for (int e2 = tid; e2 < E; e2 += NT) {
       int s2 = 0;
-      for (int w2 = 0; w2 < 16; ++w2) s2 += wcnt[w2][e2];
-      base[e2] += s2;
+      for (int w2 = 0; w2 < NW; ++w2) s2 += L.wcnt[w2][e2];
+      L.base[e2] += s2;
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
+                                                     int E, int P, int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ poff,
+                                                     int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ inv,
+                                                     int2* __restrict__ items,
+                                                     int32_t* __restrict__ n_items,
+                                                     int32_t* __restrict__ cnt_log) {
+  __shared__ RouteLds<16> L;
+  route_block<16>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, cnt_log, L);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
