@@ -144,8 +144,11 @@ def router_topk(r: np.ndarray, k: int):
     """Top-k experts per row by (logit desc, id asc); weights = softmax over the k chosen logits.
 
     r: [n][E].  Returns ids int [n][k] (rank order) and weights float64 [n][k].
+    A NaN logit is read as -inf (it ranks with -inf, below every number; the
+    pages do not cover non-finite logits), and -0 ties with +0 as numbers do.
     """
     r = np.asarray(r, dtype=np.float64)
+    r = np.where(np.isnan(r), -np.inf, r)
     n, e = r.shape
     ids = np.zeros((n, k), dtype=np.int64)
     for i in range(n):

@@ -55,8 +55,12 @@ def test_router_topk_bit_exact(M, E, k):
     print(f"topk M={M} E={E} k={k}", flush=True)
     g = torch.Generator().manual_seed(M * 7 + E)
     r = torch.randn(M, E, generator=g)
-    r[::3] = torch.round(r[::3] * 4) / 4            # exact ties in every third row
+    r[::3] = torch.round(r[::3] * 4) / 4            # exact ties (and -0 vs +0) in every third row
     r[1] = 0.0                                       # a row of all-equal logits
+    r[2, ::2] = -0.0                                 # signed zeros tie with +0
+    r[4, :5] = float("nan")                          # NaN ranks as -inf
+    if M > 7:
+        r[7, 3:9] = float("-inf")
     ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
     w = torch.empty(M, k, device="cuda")
     dg.dg_test_router_topk(r.cuda(), k, ids, w)

@@ -331,3 +331,12 @@ def test_absorbing_forward_binomial_rate():
     keep = exp > 5
     chi2 = np.sum((counts[keep] - exp[keep]) ** 2 / exp[keep])
     assert chi2 < 40.0                                                   # dof ~ 10; p ~ 1e-5 cutoff
+
+
+def test_router_topk_non_finite_and_signed_zero():
+    # reading: NaN ranks as -inf (below every number, ties broken by id); -0 ties with +0
+    r = np.array([[np.nan, np.nan, np.nan, -np.inf, 0.0, -0.0, 1.0, 0.5]])
+    ids, w = O.router_topk(r, 5)
+    assert ids.tolist() == [[6, 7, 4, 5, 0]]
+    e = np.array([1.0, math.exp(-0.5), math.exp(-1.0), math.exp(-1.0), 0.0])
+    np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-15, atol=0)
