@@ -246,22 +246,19 @@ void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
 // Grouped expert GEMMs.  A workgroup owns one work item (expert e, a group of up
-// to 64 of its tokens = NT blocks of 16) and a tile of output features.  In the
-// gate/up GEMM (K = d_model) its 4 waves split the K loop (interleaved 64-wide
-// steps) and reduce through LDS in a fixed order; in the down GEMM (K = F, short)
-// each wave owns 32 output rows over the whole K loop and the token fragments
-// are shared through L1.  Splitting K keeps every wave's dependent chain short and
-// reads every operand byte once per workgroup, so the kernel holds up both when
-// tokens spread over all experts (~16 each: a weight-streaming, HBM-bound
-// regime) and when a uniform canvas sends every token to a few experts (many
-// tokens per expert: the workgroup tile of 32 features x 64 tokens then reuses
-// each weight fragment across 4 token blocks and each token fragment across 4
-// weight blocks).
+// to kMoeGroup = 64 of its tokens) and a tile of output features.  The gate/up
+// GEMM (K = d_model) stages weight and token fragment tiles through LDS rings by
+// direct global->LDS copies and computes a 128-row x 64-token tile; the down GEMM
+// (K = F, short) gives each wave 32 output rows over the whole K loop and shares
+// the token fragments through L1.  Either way every operand byte is read once per
+// workgroup, so the kernels hold up both when tokens spread over all experts (~16
+// each: a weight-streaming, HBM-bound regime) and when a uniform canvas sends
+// every token to a few experts (many work items per expert, whose workgroups
+// share the expert's weight tiles through L2).
 //
 // Every operand pointer addresses a fragment tile (row block, k block 0) plus
 // the lane's 16-byte slot; a 64-wide k step covers two consecutive 1 KiB tiles.
 
-constexpr int kGateUpFb = 2;   // 16-feature blocks per gate/up workgroup
 constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 
 // acc[i][j] += W_i . X_j^T over this wave's k steps (w, w + kstride, ...).
@@ -296,95 +293,156 @@ __device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n = w < nk ? (nk - w + kstride - 1) / kstride : 0;
-  pipeline3(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
-            [&](int t) { ld(Wc, Xc, t); }, [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); },
-            [&] { mm(Wc, Xc); });
+  pipeline2(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
+            [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); });
 }
 
-// Park this wave's partial tiles in LDS: red[((w * NW + i) * NT + j) * 64 + lane].
-template <int NW, int NT>
-__device__ __forceinline__ void park(const f32x4 (&acc)[NW][NT], f32x4* red, int w, int lane) {
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) red[((w * NW + i) * NT + j) * 64 + lane] = acc[i][j];
-}
+// Gate/up, operands staged through LDS.  Workgroup tile: 128 packed weight rows
+// (gate and up blocks of 4 feature blocks) x one work item (up to 64 tokens); the
+// 4 waves form a 2 x 2 grid of 64-row x 32-token sub-tiles.  Per 64-wide k
+// step the workgroup copies 8 weight and 4 token blocks (two 1 KiB fragment
+// tiles each) straight into LDS: weights into a three-step ring (two steps
+// ahead), token tiles -- L2 hits -- into a two-step ring (one step ahead).  The
+// 64 KiB of rings let two workgroups share a CU, which hides more latency than
+// deeper rings in one.  Every weight byte is read once per workgroup and shared
+// by all its token tiles.
+constexpr int kGuRB = 8, kGuTB = 4, kGuKT = 2;
+constexpr int kGuWSlots = 3, kGuXSlots = 2;
+constexpr int kGuWBytes = kGuRB * kGuKT * 1024, kGuXBytes = kGuTB * kGuKT * 1024;
+constexpr int kGuLds = kGuWSlots * kGuWBytes + kGuXSlots * kGuXBytes;
+constexpr int kGuCopies = kGuRB * kGuKT / 4;   // weight tile copies per wave per step
 
-template <int NW, int NT>
-__device__ __forceinline__ f32x4 reduced(const f32x4* red, int i, int j, int lane) {
-  f32x4 v = red[(i * NT + j) * 64 + lane];
+template <bool STREAM>
+__device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const uint16_t* xg, int slot0,
+                                                 int t0, int ne, int F, int f0, int d, int lane,
+                                                 int wv, uint16_t* A, char* ring) {
+  constexpr int WI = kGuRB / 2, WJ = kGuTB / 2;
+  const int ntb = min(kGuTB, (ne - t0 + 15) >> 4);   // token blocks of this item (>= 1)
+  const int nk = d / (32 * kGuKT);
+  constexpr int WB = kGuRB / 4, XB = kGuTB / 4;
+  const uint16_t* wsrc[WB];
+  const uint16_t* xsrc[XB];
 #pragma unroll
-  for (int ww = 1; ww < 4; ++ww) v += red[((ww * NW + i) * NT + j) * 64 + lane];
-  return v;
-}
-
-// gate/up: for the FB feature blocks f0 + f, weight row blocks 2(f0 + f) (gate)
-// and 2(f0 + f) + 1 (up); A[slot][feature] = silu(gate) * up in bf16.
-template <int NT, bool STREAM>
-__device__ __forceinline__ void gate_up_item(const uint16_t* wgu_e, const uint16_t* xg, int slot0,
-                                             int t0, int ne, int F, int f0, int d, int lane, int w,
-                                             uint16_t* A, f32x4* red) {
-  constexpr int FB = kGateUpFb, NW = 2 * kGateUpFb;
-  const uint16_t* wp[NW];
+  for (int u = 0; u < WB; ++u) wsrc[u] = wgu_e + fm_tile(2 * f0 + wv * WB + u, 0, d, lane);
+  // token blocks past the item's last one re-read that block (their outputs are dropped)
 #pragma unroll
-  for (int i = 0; i < NW; ++i) wp[i] = wgu_e + fm_tile(2 * f0 + i, 0, d, lane);
-  const uint16_t* xp[NT];
+  for (int u = 0; u < XB; ++u) xsrc[u] = xg + fm_tile((slot0 >> 4) + min(wv * XB + u, ntb - 1), 0, d, lane);
+  char* const wring = ring;
+  char* const xring = ring + kGuWSlots * kGuWBytes;
+  auto issue_w = [&](int step) {
+    char* dst = wring + (step % kGuWSlots) * kGuWBytes + wv * WB * kGuKT * 1024;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = xg + fm_tile((slot0 >> 4) + j, 0, d, lane);
-  f32x4 acc[NW][NT];
-  grouped_partial<NW, NT, STREAM>(wp, xp, d >> 6, w, acc);
-  park<NW, NT>(acc, red, w, lane);
-  __syncthreads();
+    for (int u = 0; u < WB; ++u)
+#pragma unroll
+      for (int t = 0; t < kGuKT; ++t)
+        tile_to_lds<STREAM>(wsrc[u] + (step * kGuKT + t) * 512, dst + (u * kGuKT + t) * 1024);
+  };
+  auto issue_x = [&](int step) {
+    char* dst = xring + (step % kGuXSlots) * kGuXBytes + wv * XB * kGuKT * 1024;
+#pragma unroll
+    for (int u = 0; u < XB; ++u)
+#pragma unroll
+      for (int t = 0; t < kGuKT; ++t)
+        tile_to_lds<false>(xsrc[u] + (step * kGuKT + t) * 512, dst + (u * kGuKT + t) * 1024);
+  };
+  const int wr = wv & 1, wt = wv >> 1;
+  f32x4 acc[WI][WJ];
+#pragma unroll
+  for (int i = 0; i < WI; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_char* const lw = lds_launder(wring);
+  lds_char* const lx = lds_launder(xring);
+  // After step j's barrier the wave copies X(j + XS - 1) then W(j + WS - 1); the
+  // prologue runs the same order for j = -(WS - 1) .. -1.  At the top of step s,
+  // X(s) and everything issued before it (W(s) included) have landed once at most
+  // the copies issued after X(s) are in flight.
+  constexpr int WS = kGuWSlots, XS = kGuXSlots;
+  static_assert(WS > XS && XS >= 2, "weights run further ahead than token tiles");
+  constexpr int kAfterX = kGuCopies + (XS - 2) * 2 * kGuCopies;
+  static_assert(kAfterX < 64, "vmcnt range");
+#pragma unroll
+  for (int j = -(WS - 1); j < 0; ++j) {
+    if (j + XS - 1 >= 0 && j + XS - 1 < nk) issue_x(j + XS - 1);
+    if (j + WS - 1 < nk) issue_w(j + WS - 1);
+  }
+  u32x4 Af[WI][kGuKT], Bf[WJ][kGuKT];
+  for (int s = 0; s < nk; ++s) {
+    if (s + WS - 2 < nk) vm_wait<kAfterX>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + XS - 1 < nk) issue_x(s + XS - 1);
+    if (s + WS - 1 < nk) issue_w(s + WS - 1);
+    const lds_char* sw = lw + (s % kGuWSlots) * kGuWBytes + lane * 16;
+    const lds_char* sx = lx + (s % kGuXSlots) * kGuXBytes + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int t = 0; t < kGuKT; ++t) Af[i][t] = ld16_lds(sw + ((wr * WI + i) * kGuKT + t) * 1024);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int t = 0; t < kGuKT; ++t) Bf[j][t] = ld16_lds(sx + ((wt * WJ + j) * kGuKT + t) * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int i = 0; i < WI; ++i) acc[i][j] = mfma16x2(Af[i][0], Bf[j][0], Af[i][1], Bf[j][1], acc[i][j]);
+  }
+  // wave rows: row blocks 2 f0 + wr * WI + i; pairs (i, i + 1) are gate / up of
+  // feature block f0 + wr * WI / 2 + i / 2
   const int r = lane & 15, g = lane >> 4;
-  for (int p = w; p < FB * NT; p += 4) {
-    const int f = p / NT, j = p - f * NT;
-    const int t = t0 + 16 * j + r;
-    if (t < ne) {
-      const f32x4 G = reduced<NW, NT>(red, 2 * f, j, lane);
-      const f32x4 U = reduced<NW, NT>(red, 2 * f + 1, j, lane);
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int tb = wt * WJ + j;
+    const int t = t0 + 16 * tb + r;
+    if (tb >= ntb || t >= ne) continue;
+#pragma unroll
+    for (int i = 0; i < WI; i += 2) {
+      const f32x4 G = acc[i][j], U = acc[i + 1][j];
       u32x2 o;
       o.x = pack_bf2(silu_f(G[0]) * U[0], silu_f(G[1]) * U[1]);
       o.y = pack_bf2(silu_f(G[2]) * U[2], silu_f(G[3]) * U[3]);
-      *reinterpret_cast<u32x2*>(A + fm_index(slot0 + 16 * j + r, (f0 + f) * 16 + 4 * g, F)) = o;
+      const int f = f0 + (wr * WI + i) / 2;
+      *reinterpret_cast<u32x2*>(A + fm_index(slot0 + 16 * tb + r, f * 16 + 4 * g, F)) = o;
     }
   }
 }
 
-// A[slot][f] = silu(x W_g[e][f]^T) * (x W_u[e][f]^T) for every slot of expert e,
-// x = Xg[slot].  Workgroup = (work item, kGateUpFb feature blocks).  The packed
-// expert weight holds gate block f and up block f as row blocks 2f and 2f + 1.
 __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ xg,
-                                                          const uint16_t* __restrict__ wgu,
-                                                          const int32_t* __restrict__ cnt,
-                                                          const int32_t* __restrict__ poff,
-                                                          const int2* __restrict__ items,
-                                                          const int32_t* __restrict__ n_items,
-                                                          int F, int d, uint16_t* __restrict__ A) {
-  __shared__ f32x4 red[4 * 2 * kGateUpFb * 4 * 64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+                                                              const uint16_t* __restrict__ wgu,
+                                                              const int32_t* __restrict__ cnt,
+                                                              const int32_t* __restrict__ poff,
+                                                              const int2* __restrict__ items,
+                                                              const int32_t* __restrict__ n_items,
+                                                              int F, int d, uint16_t* __restrict__ A) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int item, fb;
-  if (!xcd_item_schedule(*n_items, F / (16 * kGateUpFb), &item, &fb)) return;   // uniform per workgroup
+  if (!xcd_item_schedule(*n_items, F / (16 * kGuRB / 2), &item, &fb)) return;
   const int2 it = items[item];
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
-  const int f0 = fb * kGateUpFb;
-  const int nt = min(4, (ne - t0 + 15) >> 4);
-  if (ne <= kMoeGroup) {
-    switch (nt) {
-      case 1: gate_up_item<1, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      case 2: gate_up_item<2, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      case 3: gate_up_item<3, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      default: gate_up_item<4, true>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-    }
-  } else {
-    switch (nt) {
-      case 1: gate_up_item<1, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      case 2: gate_up_item<2, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      case 3: gate_up_item<3, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-      default: gate_up_item<4, false>(wgu_e, xg, slot0, t0, ne, F, f0, d, lane, w, A, red); break;
-    }
+  if (ne <= kMoeGroup)
+    gate_up_tile_lds<true>(wgu_e, xg, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+  else
+    gate_up_tile_lds<false>(wgu_e, xg, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+}
+
+void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
+                            const int32_t* poff, const int2* items, const int32_t* n_items,
+                            int max_items, int F, int d, uint16_t* a, hipStream_t s) {
+  static bool raised = false;
+  if (!raised) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kGuLds);
+    raised = true;
   }
+  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, xg, w_gate_up, cnt,
+                     poff, items, n_items, F, d, a);
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T; wave w owns output row blocks
@@ -451,14 +509,6 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
 
 int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
 int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
-
-void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
-                        const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
-                        int F, int d, uint16_t* a, hipStream_t s) {
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGateUpFb));
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), 0, s, xg, w_gate_up, cnt, poff, items,
-                     n_items, F, d, a);
-}
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
