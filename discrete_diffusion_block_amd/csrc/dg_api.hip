@@ -93,8 +93,10 @@ hipStream_t side_stream(const dg_ctx* ctx) {
   hipStream_t st = nullptr;
   hipEvent_t a = nullptr, b = nullptr;
   if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+  // both events only order work between two queues of this device: no system-scope
+  // (host-visibility) fence is needed when they are signalled
+  constexpr unsigned kFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (hipEventCreateWithFlags(&a, kFlags) != hipSuccess || hipEventCreateWithFlags(&b, kFlags) != hipSuccess) {
     if (a) (void)hipEventDestroy(a);
     (void)hipStreamDestroy(st);
     return nullptr;
@@ -254,25 +256,22 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     if (!g.denoise && l == nl - 1) break;
     DG_TIMED(ctx, DG_K_ATTENTION, launch_attention(ws.q, hq, kvl, g, ws.o, s));
     DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
-    DG_TIMED(ctx, DG_K_NORM, launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s));
     // The shared expert depends only on h: it runs on the side stream while the
     // routed experts' routing chain (small, latency-bound kernels) runs here.  It
     // reads h and writes As and ys, which nothing on this stream touches before
-    // the join; the combine kernel adds ys.
+    // the join; the combine kernel adds ys.  The fork and join events are
+    // signalled by the kernels' own completion (no marker packets on the queues).
     hipStream_t s2 = side_stream(ctx);
-    if (s2) {
-      (void)hipEventRecord(ctx->ev_fork, s);
-      (void)hipStreamWaitEvent(s2, ctx->ev_fork, 0);
-    } else {
-      s2 = s;
-    }
+    const bool fork = s2 != nullptr;
+    if (!fork) s2 = s;
+    DG_TIMED(ctx, DG_K_NORM,
+             launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s, fork ? ctx->ev_fork : nullptr));
+    if (fork) (void)hipStreamWaitEvent(s2, ctx->ev_fork, 0);
     DG_TIMED_ON(ctx, DG_K_SHARED_GATE_UP, s2,
                 launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s2));
     DG_TIMED_ON(ctx, DG_K_SHARED_DOWN, s2,
-                launch_gemm_f32(ws.As, L.ws_down, ws.ys, M, d, c.shared_ffn, /*add=*/false, s2));
-    if (s2 != s) {
-      (void)hipEventRecord(ctx->ev_join, s2);
-    }
+                launch_gemm_f32(ws.As, L.ws_down, ws.ys, M, d, c.shared_ffn, /*add=*/false, s2,
+                                fork ? ctx->ev_join : nullptr));
     DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
     DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
     DG_TIMED(ctx, DG_K_ROUTE,
@@ -286,7 +285,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_MOE_DOWN,
              launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
                              c.expert_ffn, d, ws.Y, s));
-    if (s2 != s) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
+    if (fork) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
     DG_TIMED(ctx, DG_K_COMBINE,
              launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s));

@@ -1,5 +1,6 @@
 // Internal launchers of the engine's kernels (not part of the C ABI).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -32,14 +33,16 @@ void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s);
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
-                    hipStream_t s);
+                    hipStream_t s,
+                    hipEvent_t done = nullptr);
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
 
 // ---- dense GEMMs ----
 // y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).
 void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,
-                     bool add, hipStream_t s);
+                     bool add, hipStream_t s,
+                     hipEvent_t done = nullptr);
 // q/k/v projection with RoPE; q -> q_out [M][Hq][hd], k/v -> cache at the pass positions.
 void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int hq,
                      const KvLayer& kv, const PassGeom& g, const float2* rope_tab,

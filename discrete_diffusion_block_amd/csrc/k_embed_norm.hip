@@ -126,8 +126,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const floa
 }
 
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
-                    hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, d);
+                    hipStream_t s, hipEvent_t done) {
+  // `done`, when given, is signalled by the kernel's own completion (no separate
+  // marker on the stream)
+  if (done)
+    hipExtLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, nullptr, done, 0, x, gain, eps, h, d);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, d);
 }
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]

@@ -183,15 +183,19 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
 }
 
 template <int WN, int WM, int EPI, int NW = 4>
-static void run_dense(const DenseArgs& a, hipStream_t s) {
+static void run_dense(const DenseArgs& a, hipStream_t s, hipEvent_t done = nullptr) {
   const int n_tiles = (a.nblk + WN - 1) / WN, m_tiles = (a.M + 16 * WM - 1) / (16 * WM);
   const int blocks = kXcd * ((n_tiles + kXcd - 1) / kXcd) * m_tiles;
   const size_t lds = sizeof(f32x4) * NW * WN * WM * 64;
-  hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), lds, s, a);
+  if (done)   // signalled by the kernel's own completion
+    hipExtLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), (uint32_t)lds, s,
+                          nullptr, done, 0, a);
+  else
+    hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), lds, s, a);
 }
 
 void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,
-                     bool add, hipStream_t s) {
+                     bool add, hipStream_t s, hipEvent_t done) {
   DenseArgs a{};
   a.x = x; a.w = w; a.M = M; a.N = N; a.K = K;
   a.nblk = (N + 15) / 16;
@@ -200,14 +204,14 @@ void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int 
   // want many small workgroups, wide ones 64 x 64 tiles
   if (add) {
     if (N <= 256)
-      run_dense<1, 1, EPI_ADD_F32>(a, s);
+      run_dense<1, 1, EPI_ADD_F32>(a, s, done);
     else
-      run_dense<4, 4, EPI_ADD_F32>(a, s);
+      run_dense<4, 4, EPI_ADD_F32>(a, s, done);
   } else {
     if (N <= 256)
-      run_dense<1, 1, EPI_STORE_F32>(a, s);
+      run_dense<1, 1, EPI_STORE_F32>(a, s, done);
     else
-      run_dense<4, 4, EPI_STORE_F32>(a, s);
+      run_dense<4, 4, EPI_STORE_F32>(a, s, done);
   }
 }
 
