@@ -114,6 +114,7 @@ constexpr size_t kAlign = 256;
 struct Ws {
   float* x;        // residual stream, fp32 row-major [M][d]
   uint16_t* h;     // normed activations, fragment-major [M_pad][d]
+  uint16_t* h_rm;  // the FFN-normed activations again, row-major [M][d] (expert row gathers)
   uint16_t* q;     // queries, fragment-major per (sequence, head) [n_pad][hd]
   uint16_t* o;     // attention output, fragment-major [M_pad][Hq*hd]
   float2* rope;
@@ -128,7 +129,6 @@ struct Ws {
   int2* items;
   int32_t* n_items;
   int32_t* cnt_log;
-  uint16_t* xg;    // expert-grouped token rows, fragment-major [P_pad][d]
   uint16_t* A;     // expert SwiGLU outputs, fragment-major [P_pad][F]
   float* Y;        // expert outputs fp32 [P][d]
   uint16_t* As;    // shared-expert SwiGLU output, fragment-major [M_pad][Fs]
@@ -169,6 +169,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   Carver cv{base};
   ws->x = cv.take<float>(M * c.d_model);
   ws->h = cv.take<uint16_t>(Mp * c.d_model);
+  ws->h_rm = cv.take<uint16_t>(M * c.d_model);
   ws->q = cv.take<uint16_t>((size_t)batch * round16(n) * qd);
   ws->o = cv.take<uint16_t>(Mp * qd);
   ws->rope = cv.take<float2>(M * (c.head_dim / 2));
@@ -183,7 +184,6 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
   ws->n_items = cv.take<int32_t>(1);
   ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
-  ws->xg = cv.take<uint16_t>(round16(P) * c.d_model);
   ws->A = cv.take<uint16_t>(round16(P) * c.expert_ffn);
   ws->Y = cv.take<float>(P * c.d_model);
   ws->As = cv.take<uint16_t>(Mp * c.shared_ffn);
@@ -265,7 +265,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     const bool fork = s2 != nullptr;
     if (!fork) s2 = s;
     DG_TIMED(ctx, DG_K_NORM,
-             launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, M, d, s, fork ? ctx->ev_fork : nullptr));
+             launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, ws.h_rm, M, d, s, fork ? ctx->ev_fork : nullptr));
     if (fork) (void)hipStreamWaitEvent(s2, ctx->ev_fork, 0);
     DG_TIMED_ON(ctx, DG_K_SHARED_GATE_UP, s2,
                 launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s2));
@@ -277,10 +277,9 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_ROUTE,
              launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items,
                           ws.cnt_log + (size_t)l * E, s));
-    DG_TIMED(ctx, DG_K_GATHER, launch_gather(ws.h, ws.perm, ws.poff, M, k, E, d, ws.xg, s));
     const int max_items = moe_max_items(M, k, E);
     DG_TIMED(ctx, DG_K_MOE_GATE_UP,
-             launch_moe_gate_up(ws.xg, L.w_gate_up, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
+             launch_moe_gate_up(ws.h_rm, ws.perm, L.w_gate_up, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
                                 c.expert_ffn, d, ws.A, s));
     DG_TIMED(ctx, DG_K_MOE_DOWN,
              launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,

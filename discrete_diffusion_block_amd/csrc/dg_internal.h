@@ -32,9 +32,9 @@ void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s);
-void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
-                    hipStream_t s,
-                    hipEvent_t done = nullptr);
+// h: fragment-major; h_rm (optional): the same values row-major [M][d]
+void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, uint16_t* h_rm, int M,
+                    int d, hipStream_t s, hipEvent_t done = nullptr);
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
 
@@ -67,11 +67,11 @@ void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
                   hipStream_t s);
 
-void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, int M, int k, int E,
-                   int d, uint16_t* xg, hipStream_t s);
-void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
-                        const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
-                        int F, int d, uint16_t* a, hipStream_t s);
+// x rows are gathered per slot from h_rm (row-major [M][d]) through perm
+void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_t* w_gate_up,
+                        const int32_t* cnt, const int32_t* poff, const int2* items,
+                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
+                        hipStream_t s);
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s);

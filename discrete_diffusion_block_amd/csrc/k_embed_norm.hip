@@ -54,9 +54,10 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
 }
 
 // h[m] (fragment-major, K = d) = x[m] / sqrt(mean(x^2) + eps) * gain, given ss = this
-// thread's share of sum(x^2).
+// thread's share of sum(x^2); also row-major into h_rm when given.
 __device__ __forceinline__ void norm_row(const float* xr, const float* gain, float eps, uint16_t* h,
-                                         int m, int d, float ss, float* red) {
+                                         int m, int d, float ss, float* red,
+                                         uint16_t* h_rm = nullptr) {
   const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
   for (int c = 8 * threadIdx.x; c < d; c += 8 * blockDim.x) {
@@ -69,6 +70,7 @@ __device__ __forceinline__ void norm_row(const float* xr, const float* gain, flo
     o.z = pack_bf2(v[4] * inv * gg[4], v[5] * inv * gg[5]);
     o.w = pack_bf2(v[6] * inv * gg[6], v[7] * inv * gg[7]);
     *reinterpret_cast<u32x4*>(h + fm_index(m, c, d)) = o;
+    if (h_rm) *reinterpret_cast<u32x4*>(h_rm + (size_t)m * d + c) = o;
   }
 }
 
@@ -111,7 +113,7 @@ void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float
 }
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const float* gain, float eps,
-                                                      uint16_t* h, int d) {
+                                                      uint16_t* h, uint16_t* h_rm, int d) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const float* xr = x + (size_t)m * d;
@@ -122,17 +124,17 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const floa
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
   }
-  norm_row(xr, gain, eps, h, m, d, ss, red);
+  norm_row(xr, gain, eps, h, m, d, ss, red, h_rm);
 }
 
-void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, int M, int d,
-                    hipStream_t s, hipEvent_t done) {
+void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, uint16_t* h_rm, int M,
+                    int d, hipStream_t s, hipEvent_t done) {
   // `done`, when given, is signalled by the kernel's own completion (no separate
   // marker on the stream)
   if (done)
-    hipExtLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, nullptr, done, 0, x, gain, eps, h, d);
+    hipExtLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, nullptr, done, 0, x, gain, eps, h, h_rm, d);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, d);
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, h_rm, d);
 }
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]

@@ -1,14 +1,14 @@
 // Mixture-of-experts block: router top-k, deterministic token->expert
 // permutation, and the two grouped expert GEMMs.
 //
-// At a 256-token canvas with 128 experts and top-8 routing, 2048 assignments
-// spread over (nearly) every expert, ~16 tokens each: the expert GEMMs stream
-// ~1.5 GB of weights per layer at an arithmetic intensity of ~16 flop/B, so
-// they are HBM-bound weight streamers.  Each wave owns 16 output features of
-// one expert and all of that expert's tokens: weight rows go to the MFMA A
-// side and are read from HBM exactly once; the expert's gathered token rows
-// (B side, a few KB) come from L2.  No token ever moves: rows are gathered
-// through the permutation at load time.
+// With a trained router, a 256-token canvas spreads its 2048 assignments over
+// most of the 128 experts (~16-24 tokens each): the expert GEMMs then stream
+// ~1 GB of weights per layer at a low arithmetic intensity and are HBM-bound.
+// When a uniform canvas sends every token to a few experts, the same kernels
+// run many work items per expert and the weight tiles are shared through L2.
+// Weight rows sit on the MFMA A side and are read from HBM once per work item;
+// token rows never move: the gate/up GEMM gathers them through the permutation
+// while copying its operand tiles into LDS.
 #include <limits.h>
 #include <math.h>
 
@@ -219,28 +219,6 @@ void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t
                      cnt, poff, perm, inv, items, n_items, cnt_log);
 }
 
-// Xg[slot] = h[perm[slot]] (zeros on padding), both fragment-major with K = d.
-// One wave per padded slot; a lane moves 16-byte chunks.
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ h,
-                                                     const int32_t* __restrict__ perm,
-                                                     const int32_t* __restrict__ poff, int E, int P,
-                                                     int d, uint16_t* __restrict__ xg) {
-  const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (slot >= P || slot >= poff[E]) return;
-  const int tok = perm[slot];
-  for (int c = 8 * lane; c < d; c += 8 * 64) {
-    const u32x4 v = tok >= 0 ? ld16(h + fm_index(tok, c, d)) : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(xg + fm_index(slot, c, d)) = v;
-  }
-}
-
-void launch_gather(const uint16_t* h, const int32_t* perm, const int32_t* poff, int M, int k, int E,
-                   int d, uint16_t* xg, hipStream_t s) {
-  const int P = moe_max_slots(M, k, E);
-  hipLaunchKernelGGL(gather_kernel, dim3((P + 3) / 4), dim3(256), 0, s, h, perm, poff, E, P, d, xg);
-}
-
 // ---------------------------------------------------------------- grouped GEMMs
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
@@ -313,9 +291,10 @@ constexpr int kGuLds = kGuWSlots * kGuWBytes + kGuXSlots * kGuXBytes;
 constexpr int kGuCopies = kGuRB * kGuKT / 4;   // weight tile copies per wave per step
 
 template <bool STREAM>
-__device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const uint16_t* xg, int slot0,
-                                                 int t0, int ne, int F, int f0, int d, int lane,
-                                                 int wv, uint16_t* A, char* ring) {
+__device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const uint16_t* h_rm,
+                                                 const int32_t* perm, int slot0, int t0, int ne, int F,
+                                                 int f0, int d, int lane, int wv, uint16_t* A,
+                                                 char* ring) {
   constexpr int WI = kGuRB / 2, WJ = kGuTB / 2;
   const int ntb = min(kGuTB, (ne - t0 + 15) >> 4);   // token blocks of this item (>= 1)
   const int nk = d / (32 * kGuKT);
@@ -324,9 +303,15 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   const uint16_t* xsrc[XB];
 #pragma unroll
   for (int u = 0; u < WB; ++u) wsrc[u] = wgu_e + fm_tile(2 * f0 + wv * WB + u, 0, d, lane);
-  // token blocks past the item's last one re-read that block (their outputs are dropped)
+  // The token tiles are gathered on the fly: lane (r, g) of a fragment tile copies
+  // the 16 bytes of its slot's token row (row-major h) at k columns 8g .. 8g + 7 of
+  // the tile.  Token blocks past the item's last one re-read that block, and
+  // padding slots read row 0: their outputs are dropped.
 #pragma unroll
-  for (int u = 0; u < XB; ++u) xsrc[u] = xg + fm_tile((slot0 >> 4) + min(wv * XB + u, ntb - 1), 0, d, lane);
+  for (int u = 0; u < XB; ++u) {
+    const int tok = perm[slot0 + 16 * min(wv * XB + u, ntb - 1) + (lane & 15)];
+    xsrc[u] = h_rm + (size_t)max(tok, 0) * d + 8 * (lane >> 4);
+  }
   char* const wring = ring;
   char* const xring = ring + kGuWSlots * kGuWBytes;
   auto issue_w = [&](int step) {
@@ -343,7 +328,7 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
     for (int u = 0; u < XB; ++u)
 #pragma unroll
       for (int t = 0; t < kGuKT; ++t)
-        tile_to_lds<false>(xsrc[u] + (step * kGuKT + t) * 512, dst + (u * kGuKT + t) * 1024);
+        tile_to_lds<false>(xsrc[u] + (step * kGuKT + t) * 32, dst + (u * kGuKT + t) * 1024);
   };
   const int wr = wv & 1, wt = wv >> 1;
   f32x4 acc[WI][WJ];
@@ -409,8 +394,9 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   }
 }
 
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ xg,
-                                                              const uint16_t* __restrict__ wgu,
+__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ h_rm,
+                                                          const int32_t* __restrict__ perm,
+                                                          const uint16_t* __restrict__ wgu,
                                                               const int32_t* __restrict__ cnt,
                                                               const int32_t* __restrict__ poff,
                                                               const int2* __restrict__ items,
@@ -426,14 +412,15 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
   if (ne <= kMoeGroup)
-    gate_up_tile_lds<true>(wgu_e, xg, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+    gate_up_tile_lds<true>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
   else
-    gate_up_tile_lds<false>(wgu_e, xg, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+    gate_up_tile_lds<false>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
 }
 
-void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int32_t* cnt,
-                            const int32_t* poff, const int2* items, const int32_t* n_items,
-                            int max_items, int F, int d, uint16_t* a, hipStream_t s) {
+void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_t* w_gate_up,
+                        const int32_t* cnt, const int32_t* poff, const int2* items,
+                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
+                        hipStream_t s) {
   static bool raised = false;
   if (!raised) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel),
@@ -441,8 +428,8 @@ void launch_moe_gate_up(const uint16_t* xg, const uint16_t* w_gate_up, const int
     raised = true;
   }
   const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, xg, w_gate_up, cnt,
-                     poff, items, n_items, F, d, a);
+  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, h_rm, perm, w_gate_up,
+                     cnt, poff, items, n_items, F, d, a);
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T; wave w owns output row blocks

@@ -23,7 +23,7 @@ MAX_BATCH = 64
 
 KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
-                "sample_pass1", "sample_select", "fill", "gather"]
+                "sample_pass1", "sample_select", "fill"]
 PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
 MOE_GROUP = 64   # tokens per grouped-GEMM work item in the routing tap's item list
 

@@ -188,7 +188,7 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
 typedef enum dg_kernel_kind {
   DG_K_PREP = 0, DG_K_EMBED, DG_K_QKV, DG_K_ATTENTION, DG_K_O_PROJ, DG_K_NORM, DG_K_ROUTER,
   DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
-  DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL, DG_K_GATHER,
+  DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL,
   DG_K_COUNT
 } dg_kernel_kind;
 
