@@ -9,9 +9,9 @@
 // q, the key cache and the (transposed) value cache are stored in fragment
 // tiles, so each operand fragment below is one contiguous 1 KiB wave load.
 //
-// Work split: a workgroup owns 16 queries of one q head; its 4 waves take
-// interleaved 32-key chunks of the key range (split-KV) and merge their
-// (max, sum, output) partials through LDS in a fixed order.
+// Work split: a workgroup owns 16 queries of one q head; its NW waves (8; 4 at
+// hd 32) take interleaved 32-key chunks of the key range (split-KV) and merge
+// their (max, sum, output) partials through LDS in a fixed order.
 //
 // Layout trick: scores are computed transposed, S^T = K . Q^T, with the key
 // rows of each 16-row MFMA block permuted so that a lane ends up holding the
@@ -27,14 +27,15 @@
 
 namespace dg {
 
-template <int HD>
-__global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restrict__ q, int hq,
-                                                        KvLayer kv, PassGeom g,
-                                                        uint16_t* __restrict__ o) {
+
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(const uint16_t* __restrict__ q, int hq,
+                                                            KvLayer kv, PassGeom g,
+                                                            uint16_t* __restrict__ o) {
   constexpr int NC = HD / 32;   // k-steps of the score MFMA
   constexpr int NB = HD / 16;   // output blocks of 16 hd rows
-  __shared__ float Ol[4][16][HD + 4];
-  __shared__ float ml[4][16][2];
+  __shared__ float Ol[NW][16][HD + 4];
+  __shared__ float ml[NW][16][2];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   u32x4 Ka[2][NC], Va[NB], Kb[2][NC], Vb[NB];
   int kca = 0, kcb = 0;
   auto load = [&](u32x4 (&K)[2][NC], u32x4 (&Vt)[NB], int& kcs, int step) {
-    kcs = kc0 + 32 * (w + 4 * step);
+    kcs = kc0 + 32 * (w + NW * step);
     const uint16_t* kp = kbase + ((size_t)(kcs >> 5) * 2 * NC << 9) + 8 * lane;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
       acc[hb] = mfma16(Vt[hb], pb, acc[hb]);
     }
   };
-  const int nsteps = w < nchunk ? (nchunk - w + 3) >> 2 : 0;
+  const int nsteps = w < nchunk ? (nchunk - w + NW - 1) / NW : 0;
   pipeline2(nsteps, [&](int t) { load(Ka, Va, kca, t); }, [&](int t) { load(Kb, Vb, kcb, t); },
             [&] { process(Ka, Va, kca); }, [&] { process(Kb, Vb, kcb); });
 
@@ -161,16 +162,19 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
   }
   __syncthreads();
 
-  // merge the 4 waves: thread t -> query t/16, hd slice (t%16) * HD/16
-  const int qq = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * (HD / 16);
+  // merge the NW waves: thread t -> query t / TPQ, hd slice (t % TPQ) * HD / TPQ
+  constexpr int TPQ = 4 * NW;                 // threads per query (64 * NW / 16)
+  constexpr int CPT = HD / TPQ;               // hd columns per thread
+  static_assert(CPT >= 2 && CPT % 2 == 0, "bf16 pairs per thread");
+  const int qq = threadIdx.x / TPQ;
+  const int d0 = (threadIdx.x % TPQ) * CPT;
   float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, ml[ww][qq][0]);
-  float sc[4];
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[ww][qq][0]);
+  float sc[NW];
   float L = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
+  for (int ww = 0; ww < NW; ++ww) {
     const float mw = ml[ww][qq][0];
     sc[ww] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
     L += sc[ww] * ml[ww][qq][1];
@@ -182,10 +186,10 @@ __global__ __launch_bounds__(256) void attention_kernel(const uint16_t* __restri
     const size_t m = (size_t)b * n + iq;
     const int K = hq * HD;
 #pragma unroll
-    for (int e = 0; e < HD / 16; e += 2) {
+    for (int e = 0; e < CPT; e += 2) {
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         v0 += sc[ww] * Ol[ww][qq][d0 + e];
         v1 += sc[ww] * Ol[ww][qq][d0 + e + 1];
       }
@@ -198,10 +202,11 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
                       uint16_t* o, hipStream_t s) {
   const int pairs = g.batch * kv.hkv, per_pair = (hq / kv.hkv) * ((g.n + 15) / 16);
   dim3 grid(kXcd * ((pairs + kXcd - 1) / kXcd) * per_pair);
+  // 8 waves split the key range (4 for hd 32, where the merge runs out of columns)
   switch (kv.hd) {
-    case 32: hipLaunchKernelGGL(attention_kernel<32>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
-    case 64: hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
-    default: hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(256), 0, s, q, hq, kv, g, o); break;
+    case 32: hipLaunchKernelGGL((attention_kernel<32, 4>), grid, dim3(256), 0, s, q, hq, kv, g, o); break;
+    case 64: hipLaunchKernelGGL((attention_kernel<64, 8>), grid, dim3(512), 0, s, q, hq, kv, g, o); break;
+    default: hipLaunchKernelGGL((attention_kernel<128, 8>), grid, dim3(512), 0, s, q, hq, kv, g, o); break;
   }
 }
 
