@@ -47,6 +47,8 @@ def algorithmic_work(kind, cfg, M, counts_per_layer):
     d, F, Fs, E, V = cfg.d_model, cfg.expert_ffn, cfg.shared_ffn, cfg.n_experts, cfg.vocab
     hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     if kind in ("moe_gate_up", "moe_down"):
+        if counts_per_layer is None:
+            return "hbm", "GB/s", None
         per = []
         for cnt in counts_per_layer:
             used = sum(1 for c in cnt if c > 0)
@@ -176,6 +178,71 @@ def summarize_pmc(root: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prompt: int) -> str:
+    """Per-kernel launch statistics from the rocprofv3 kernel-trace CSV under root of a
+    `bench.py --steps S --warmup W` run: the denoising passes of the S timed blocks.
+    Passes start at the engine's prep kernel; the prompt prefill takes the first
+    ceil(prompt / 512) passes, then each block runs denoise_steps denoising passes (the
+    ones that end in the vocabulary head) and one append pass."""
+    import csv
+    import glob
+    import collections
+    rows = []
+    for f in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(r for r in csv.DictReader(fh) if r["Kernel_Name"].startswith(("dg::", "void dg::")))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "prep_kernel" in r["Kernel_Name"]] + [len(rows)]
+    passes = [rows[a:b] for a, b in zip(starts[:-1], starts[1:])]
+    per_block = denoise_steps + 1
+    first = -(-prompt // 512) + warmup * per_block
+    timed = passes[first:first + steps * per_block]
+    denoise = [p for p in timed if any("head_gemm" in r["Kernel_Name"] for r in p)]
+    agg = collections.defaultdict(list)
+    for p in denoise:
+        for r in p:
+            name = r["Kernel_Name"].replace("void ", "").split("(")[0]
+            agg[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    span = sum((int(p[-1]["End_Timestamp"]) - int(p[0]["Start_Timestamp"])) / 1e3 for p in denoise)
+    total = sum(sum(v) for v in agg.values())
+    lines = [f"denoising passes of the timed blocks: {len(denoise)} (of {len(timed)} passes in "
+             f"{steps} blocks); mean pass span {span / max(1, len(denoise)) / 1e3:.3f} ms",
+             f"{'kernel':58s} {'calls':>6s} {'total ms':>9s} {'avg us':>8s} {'min us':>8s} "
+             f"{'max us':>8s} {'share':>6s}"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k[:58]:58s} {len(v):6d} {sum(v) / 1e3:9.2f} {sum(v) / len(v):8.2f} "
+                     f"{min(v):8.2f} {max(v):8.2f} {100 * sum(v) / total:5.1f}%")
+    return "\n".join(lines)
+
+
+def write_traffic(fetch_txt: str, write_txt: str, kind: str) -> dict:
+    """Calibrated HBM bytes per launch of one kernel kind from the two counter summaries
+    (FETCH_SIZE and WRITE_SIZE passes of --pmc-workload, printed by --summarize-pmc).
+    Each counter is scaled by the ratio of the copy kernel's true byte count (256 MiB
+    read, 256 MiB written) to what the same counter reads for it."""
+    def means(path):
+        out = {}
+        for line in open(path):
+            parts = line.split()
+            if len(parts) >= 6:
+                out[parts[0]] = float(parts[-1])
+        return out
+    fe, wr = means(fetch_txt), means(write_txt)
+    copy_kib = float(256 << 10)
+    fs, ws = copy_kib / fe["dg::copy16_kernel"], copy_kib / wr["dg::copy16_kernel"]
+    name = f"dg::{kind}_kernel"
+    t = {"kernel": kind, "source_digest": kernel_source_digest(),
+         "bytes_per_launch": int(round((fe[name] * fs + wr[name] * ws) * 1024)),
+         "fetch_kib_per_launch_raw": fe[name], "write_kib_per_launch_raw": wr[name],
+         "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+         "calibration": f"dg::copy16_kernel copying 256 MiB reads FETCH_SIZE {fe['dg::copy16_kernel']:.1f} KiB "
+                        f"and WRITE_SIZE {wr['dg::copy16_kernel']:.1f} KiB",
+         "workload": "python3 bench.py --pmc-workload (denoising passes only: 2 steps, 30 layers)"}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(t, fh, indent=1)
+    return t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,9 +256,20 @@ def main():
                     help="run the hardware-counter workload (copy calibration + 2 denoising steps) and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel counter means from rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel launch statistics from rocprofv3 kernel-trace CSVs under DIR and exit")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_TXT", "WRITE_TXT", "KIND"),
+                    help="write profiles/traffic.json for KIND from two --summarize-pmc outputs and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.warmup, args.steps, args.denoise_steps,
+                              args.prompt))
+        return
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic)))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -256,27 +334,42 @@ def main():
     log("per-kind kernel ms in one block: " +
         ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in sorted(prof.items(), key=lambda kv: -kv[1][0]) if v[1]))
 
-    # ---- denoise step alone (denoise + sampler), and the expert routing it produced
+    # ---- denoise step alone (denoise + sampler)
     c2 = torch.full((1, C), V, dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    reps = 12
+    reps = args.denoise_steps
     for s in range(reps):
         eng.denoise_step(c2, 1.0 - s / reps, logits)
         eng.sample_eb(logits, c2, args.gamma, s == reps - 1, nm)
     e1.record(stream)
     torch.cuda.synchronize()
     denoise_ms = e0.elapsed_time(e1) / reps
-    eng.denoise_step(torch.full((1, C), V, dtype=torch.int32, device="cuda"), 1.0, logits)
-    counts = eng.moe_counts().cpu().tolist()
-    used = [sum(1 for c in row if c > 0) for row in counts]
 
-    # ---- roofline of the dominant kernel kind
-    # the dominant kernel among those bound by HBM or MFMA (the row kernels are latency-bound)
-    dom = max((k for k in prof if prof[k][1] and algorithmic_work(k, cfg, C, counts)[0]),
+    # ---- roofline of the dominant kernel kind: among the kinds bound by HBM or MFMA
+    # (the row kernels are latency-bound), the one with the most time in the profiled
+    # block.  Its launches are timed alone (HIP events on the engine's stream around
+    # that kind only) over the denoising passes of one block's worth of steps; the
+    # algorithmic amount of each pass uses that pass's own per-layer expert counts.
+    dom = max((k for k in prof if prof[k][1] and algorithmic_work(k, cfg, C, None)[0]),
               key=lambda k: prof[k][0])
-    bound, unit, amount = algorithmic_work(dom, cfg, C, counts)
-    avg_ms = prof[dom][0] / prof[dom][1]
+    c2.fill_(V)
+    dom_ms, dom_launches, amount_sum, used = 0.0, 0, 0.0, []
+    for s in range(reps):
+        dg.dg_profile_begin(eng.ctx, 4 * cfg.n_layers, kinds=[dom])
+        eng.denoise_step(c2, 1.0 - s / reps, logits)
+        p1 = dg.dg_profile_end(eng.ctx)[dom]
+        counts = eng.moe_counts().cpu().tolist()
+        eng.sample_eb(logits, c2, args.gamma, s == reps - 1, nm)
+        bound, unit, amount = algorithmic_work(dom, cfg, C, counts)
+        dom_ms += p1[0]
+        dom_launches += p1[1]
+        amount_sum += amount * p1[1]
+        used += [sum(1 for c in row if c > 0) for row in counts]
+    torch.cuda.synchronize()
+    avg_ms = dom_ms / dom_launches
+    amount = amount_sum / dom_launches
+    log(f"{dom}: {dom_launches} launches, {avg_ms * 1e3:.2f} us average")
     roofline = None
     if bound is not None:
         if unit == "GB/s":
@@ -291,8 +384,8 @@ def main():
                 traffic = t.get("bytes_per_launch")
         roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                     "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                    "avg_launch_ms": round(avg_ms, 4), "launches": prof[dom][1],
-                    "algorithmic_per_launch": amount}
+                    "avg_launch_ms": round(avg_ms, 4), "launches": dom_launches,
+                    "algorithmic_per_launch": round(amount)}
 
     out = {
         "metric": "output tok/s (256-tok canvas, 12 denoise steps + KV append per block)",

@@ -17,6 +17,7 @@ using namespace dg;
 // Optional per-launch event timing (dg_profile_begin/end).
 struct Prof {
   bool on = false;
+  uint32_t mask = 0;            // kinds timed (bit per dg_kernel_kind)
   std::vector<hipEvent_t> ev;   // two per record
   std::vector<int> kind;
   size_t used = 0;
@@ -63,7 +64,7 @@ struct Timed {
   hipStream_t s;
   bool on;
   Timed(const dg_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_) {
-    on = c && c->prof.on && c->prof.used < c->prof.kind.size();
+    on = c && c->prof.on && (c->prof.mask >> k & 1u) && c->prof.used < c->prof.kind.size();
     if (on) (void)hipEventRecord(c->prof.ev[2 * c->prof.used], s);
   }
   ~Timed() {
@@ -553,9 +554,11 @@ dg_status dg_pack_weight(int kind, const uint16_t* d_src, uint16_t* d_dst, int n
   return check_launch("pack");
 }
 
-dg_status dg_profile_begin(dg_ctx* ctx, int capacity) {
+dg_status dg_profile_begin(dg_ctx* ctx, int capacity, uint32_t kind_mask) {
   if (!ctx || capacity < 1) return fail(DG_ERR_INVALID_ARG, "bad profiling arguments");
+  if (kind_mask >> DG_K_COUNT) return fail(DG_ERR_INVALID_ARG, "kind_mask names an unknown kernel kind");
   Prof& p = ctx->prof;
+  p.mask = kind_mask ? kind_mask : (1u << DG_K_COUNT) - 1u;
   for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
   p.ev.assign(2 * (size_t)capacity, nullptr);
   for (auto& e : p.ev)

@@ -78,7 +78,7 @@ def lib():
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
             "dg_packed_elems": [i32, i32, C.POINTER(sz)],
             "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
-            "dg_profile_begin": [vp, i32],
+            "dg_profile_begin": [vp, i32, C.c_uint32],
             "dg_profile_end": [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
             "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
             "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
@@ -235,8 +235,10 @@ def _v_index(p: torch.Tensor, c: torch.Tensor, hd: int) -> torch.Tensor:
     return ((((p >> 5) * (hd >> 4)) + (c >> 4)) << 9) + (((((p & 31) >> 3) << 4) + (c & 15)) << 3) + (p & 7)
 
 
-def dg_profile_begin(ctx, capacity: int):
-    _check(lib().dg_profile_begin(ctx, capacity))
+def dg_profile_begin(ctx, capacity: int, kinds=None):
+    """kinds: iterable of names from KERNEL_KINDS to time (None: every kind)."""
+    mask = 0 if kinds is None else sum(1 << KERNEL_KINDS.index(k) for k in kinds)
+    _check(lib().dg_profile_begin(ctx, capacity, mask))
 
 
 def dg_profile_end(ctx):

@@ -192,10 +192,14 @@ typedef enum dg_kernel_kind {
   DG_K_COUNT
 } dg_kernel_kind;
 
-/* Start bracketing every kernel launch made through ctx (dg_prefill_kv,
+/* Start bracketing the kernel launches made through ctx (dg_prefill_kv,
  * dg_denoise_step, dg_generate_block) with a pair of hipEvents recorded on the
- * launch stream, for up to `capacity` launches (events are created here). */
-dg_status dg_profile_begin(dg_ctx* ctx, int capacity);
+ * launch stream, for up to `capacity` launches (events are created here).
+ * kind_mask selects the kinds timed (bit DG_K_x); 0 times every kind.  Each
+ * bracket adds two event markers to its stream, so timing fewer kinds leaves the
+ * rest of the schedule (and the overlap with the side stream) closer to an
+ * untimed run. */
+dg_status dg_profile_begin(dg_ctx* ctx, int capacity, uint32_t kind_mask);
 /* Stop, wait for the recorded events, and return per kind the summed kernel
  * milliseconds and launch counts (arrays of DG_K_COUNT entries). */
 dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count);
