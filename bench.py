@@ -387,6 +387,24 @@ def main():
                     "avg_launch_ms": round(avg_ms, 4), "launches": dom_launches,
                     "algorithmic_per_launch": round(amount)}
 
+    # the whole sampler call (entropy/argmax pass over all 256 rows' logits + selection) on a
+    # fully masked canvas, 10 calls back to back; the canvas reset between calls (a fill
+    # kernel) is inside the timed span, so the rate is slightly understated
+    n_s = 10
+    es0, es1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    es0.record(stream)
+    for _ in range(n_s):
+        c2.fill_(V)
+        eng.sample_eb(logits, c2, args.gamma, False, nm)
+    es1.record(stream)
+    torch.cuda.synchronize()
+    samp_ms = es0.elapsed_time(es1) / n_s
+    samp_bytes = C * V * 2
+    sampler = {"bound": "hbm", "achieved": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1),
+               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(samp_bytes / (samp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "kernel": "dg_sample_eb call (entropy/argmax pass + selection)",
+               "avg_call_ms": round(samp_ms, 4), "bytes_per_call": samp_bytes}
     out = {
         "metric": "output tok/s (256-tok canvas, 12 denoise steps + KV append per block)",
         "value": round(value, 1),
@@ -412,6 +430,7 @@ def main():
         "profiled_block_ms": round(prof_block_ms, 3),
         "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]},
         "roofline": roofline,
+        "sampler_roofline": sampler,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -81,7 +81,7 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int
                  hipStream_t s);
 
 // ---- sampler ----
-constexpr int kSampleChunk = 8192;   // logits per workgroup in the first sampler pass
+constexpr int kSampleChunk = 16384;  // logits per workgroup in the first sampler pass (multiple of 2048)
 void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
                             float4* part, int* part_arg, hipStream_t s);
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,

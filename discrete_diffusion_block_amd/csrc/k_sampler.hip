@@ -4,7 +4,7 @@
 // stays within the budget gamma (at least one per step).
 //
 // Pass 1 streams the bf16 logits once (HBM-bound: 512 KiB per 262144-wide
-// row): one 256-thread workgroup per (row, 8192-logit chunk) computes the
+// row): one 256-thread workgroup per (row, kSampleChunk-logit chunk) computes the
 // chunk max m_c, its lowest argmax, s_c = sum exp(x - m_c) and
 // t_c = sum exp(x - m_c) (m_c - x).  Rows that are not [MASK] are skipped.
 // Pass 2 (one workgroup per sequence) merges the chunks of each row in index
@@ -17,82 +17,134 @@
 
 namespace dg {
 
+// Merge two (max, argmax, s, t) partials of disjoint logit sets, each with
+// s = sum exp(x - m) and t = sum exp(x - m) (m - x): rescale both to the larger max.
+// An empty partial has m = -inf, s = t = 0.  Equal maxima keep the lower index.
+__device__ __forceinline__ void merge_part(float& m, int& a, float& s, float& t, float m2, int a2,
+                                           float s2, float t2) {
+  const float M = fmaxf(m, m2);
+  float s1 = 0.f, t1 = 0.f;
+  if (m != -INFINITY) {
+    const float f = __expf(m - M);
+    s1 = s * f;
+    t1 = (t + (M - m) * s) * f;
+  }
+  if (m2 != -INFINITY) {
+    const float f = __expf(m2 - M);
+    s1 += s2 * f;
+    t1 += (t2 + (M - m2) * s2) * f;
+  }
+  if (m2 > m || (m2 == m && a2 < a)) a = a2;
+  m = M;
+  s = s1;
+  t = t1;
+}
+
+// One workgroup per (masked row, kSampleChunk logits).  Each thread loads its
+// kSampleChunk / 2048 16-byte pieces up front (all in flight at once, streamed past
+// the caches) and reduces them to a thread-local (max, s, t) in two register passes;
+// the workgroup merges the 256 partials, and only the lanes holding the chunk maximum
+// search their own elements for its lowest index.  The pass is VALU-bound at about
+// ten operations per logit, so every per-element step is kept to one instruction:
+//  * the max of the high bf16 halves is taken on the raw 32-bit words (the low half
+//    only perturbs mantissa bits below the bf16 ulp) and masked once at the end;
+//  * exp(x - m) = 2^-(m - x) log2 e with d' = (m - x) log2 e formed by one fma, so
+//    t = sum e (m - x) accumulates e d' and is divided by log2 e once.
 __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __restrict__ logits,
                                                               const int32_t* __restrict__ canvas,
                                                               int vocab, int nchunks,
                                                               float4* __restrict__ part,
                                                               int* __restrict__ part_arg) {
-  __shared__ float rv[4];
-  __shared__ int ri[4];
-  __shared__ float red[16];
+  __shared__ float4 wp[4];
+  __shared__ int wa[4];
+  __shared__ float chunk_max;
   const int row = blockIdx.y, ch = blockIdx.x;
   if (canvas[row] != vocab) return;
   const int tid = threadIdx.x;
   const int c0 = ch * kSampleChunk;
+  const int c1 = min(vocab, c0 + kSampleChunk);
   const uint16_t* lp = logits + (size_t)row * vocab;
-
-  float x[32];
-  float bv = -INFINITY;
-  int bi = INT_MAX;
+  constexpr int NL = kSampleChunk / (256 * 8);
+  // pieces past the end of the vocabulary hold bf16 -1.0e30 (0xf14a): it never wins
+  // the max, its exp underflows to exactly 0 and (m - x) log2 e stays finite, so it
+  // adds nothing to s or t (logits are finite and far inside the fp32 range)
+  constexpr uint32_t kPad = 0xf14af14au;
+  u32x4 v[NL];
+  if (c1 - c0 == kSampleChunk) {               // every chunk but a ragged last one
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e0 = c0 + (i * 256 + tid) * 8;
-    if (e0 < vocab && e0 < c0 + kSampleChunk) {
-      const u32x4 v = ld16(lp + e0);
+    for (int i = 0; i < NL; ++i) v[i] = ld16_stream(lp + c0 + (i * 256 + tid) * 8);
+  } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[8 * i + 2 * j] = __uint_as_float(v[j] << 16);
-        x[8 * i + 2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (x[8 * i + j] > bv) {
-          bv = x[8 * i + j];
-          bi = e0 + j;
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[8 * i + j] = -INFINITY;
+    for (int i = 0; i < NL; ++i) {
+      const int e0 = c0 + (i * 256 + tid) * 8;   // vocab % 8 == 0: a piece is wholly in or out
+      v[i] = e0 < c1 ? ld16_stream(lp + e0) : u32x4{kPad, kPad, kPad, kPad};
     }
   }
-  // (max, lowest index) over the workgroup
+  float mh = -INFINITY, ml = -INFINITY;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > bv || (ov == bv && oi < bi)) {
-      bv = ov;
-      bi = oi;
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mh = fmaxf(mh, __uint_as_float(v[i][j]));
+      ml = fmaxf(ml, __uint_as_float(v[i][j] << 16));
     }
-  }
-  if ((tid & 63) == 0) {
-    rv[tid >> 6] = bv;
-    ri[tid >> 6] = bi;
-  }
-  __syncthreads();
-  float m = rv[0];
-  int am = ri[0];
-  for (int w = 1; w < 4; ++w)
-    if (rv[w] > m || (rv[w] == m && ri[w] < am)) {
-      m = rv[w];
-      am = ri[w];
-    }
+  const float m = fmaxf(__uint_as_float(__float_as_uint(mh) & 0xffff0000u), ml);
+  constexpr float kLog2e = 1.44269504088896341f;
+  const float mL = m * kLog2e;
   float s = 0.f, t = 0.f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    // padding lanes (past the end of the vocabulary) hold -inf and contribute nothing
-    if (x[j] != -INFINITY) {
-      const float dlt = m - x[j];
-      const float e = __expf(-dlt);
-      s += e;
-      t += e * dlt;
+  for (int i = 0; i < NL; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xl = __uint_as_float(v[i][j] << 16), xh = __uint_as_float(v[i][j] & 0xffff0000u);
+      const float dl = __builtin_fmaf(xl, -kLog2e, mL), dh = __builtin_fmaf(xh, -kLog2e, mL);
+      const float el = __builtin_amdgcn_exp2f(-dl), eh = __builtin_amdgcn_exp2f(-dh);
+      s += el;
+      t = __builtin_fmaf(el, dl, t);
+      s += eh;
+      t = __builtin_fmaf(eh, dh, t);
     }
+  t *= 1.0f / kLog2e;
+  // (max, s, t) over the workgroup: xor butterfly within each wave, then the waves;
+  // the thread keeps its own maximum m for the argmax search below
+  float mm = m, ss = s, tt = t;
+  int a = INT_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(mm, o, 64), s2 = __shfl_xor(ss, o, 64), t2 = __shfl_xor(tt, o, 64);
+    merge_part(mm, a, ss, tt, m2, INT_MAX, s2, t2);
   }
-  s = block_sum(s, red);
-  t = block_sum(t, red);
+  if ((tid & 63) == 0) wp[tid >> 6] = make_float4(mm, ss, tt, 0.f);
+  __syncthreads();
   if (tid == 0) {
-    part[(size_t)row * nchunks + ch] = make_float4(m, s, t, 0.f);
-    part_arg[(size_t)row * nchunks + ch] = am;
+    float M = wp[0].x, S = wp[0].y, T = wp[0].z;
+    int A = INT_MAX;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge_part(M, A, S, T, wp[w].x, INT_MAX, wp[w].y, wp[w].z);
+    chunk_max = M;
+    wp[0] = make_float4(M, S, T, 0.f);
+  }
+  __syncthreads();
+  // lowest index holding the chunk maximum: only lanes whose own maximum equals it look
+  const float M = chunk_max;
+  if (m == M) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w = v[i][j >> 1];
+        const float x = __uint_as_float(j & 1 ? (w & 0xffff0000u) : (w << 16));
+        if (x == M && a == INT_MAX) a = c0 + (i * 256 + tid) * 8 + j;
+      }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = min(a, __shfl_xor(a, o, 64));
+  if ((tid & 63) == 0) wa[tid >> 6] = a;
+  __syncthreads();
+  if (tid == 0) {
+    const int A = min(min(wa[0], wa[1]), min(wa[2], wa[3]));
+    part[(size_t)row * nchunks + ch] = wp[0];
+    part_arg[(size_t)row * nchunks + ch] = A;
   }
 }
 
@@ -112,9 +164,8 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
                                                          float* __restrict__ H_out,
                                                          int32_t* __restrict__ amax_out,
                                                          int32_t* __restrict__ n_masked) {
-  __shared__ float Hs[1024];
-  __shared__ int msk[1024];
-  __shared__ int order[1024];
+  __shared__ __attribute__((aligned(16))) float Hs[1024];
+  __shared__ __attribute__((aligned(16))) float sortedH[1024];
   __shared__ int nm_s, kstar_s;
   const int b = blockIdx.x, c = threadIdx.x;
   const size_t idx = (size_t)b * C + c;
@@ -125,18 +176,27 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     if (part) {
       const float4* pr = part + idx * nchunks;
       const int* pa = part_arg + idx * nchunks;
-      float M = -INFINITY;
-      for (int k = 0; k < nchunks; ++k) M = fmaxf(M, pr[k].x);
+      // chunks merged in index order with the same rule as inside a chunk
+      float M = -INFINITY, S = 0.f, T = 0.f;
       a = INT_MAX;
-      float S = 0.f, T = 0.f;
-      for (int k = 0; k < nchunks; ++k) {
-        const float4 p = pr[k];
-        if (p.x == M && a == INT_MAX) a = pa[k];
-        const float sc = expf(p.x - M);
-        S += p.y * sc;
-        T += sc * (p.z + (M - p.x) * p.y);
+      int k = 0;
+      for (; k + 4 <= nchunks; k += 4) {
+        float4 p[4];
+        int q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = pr[k + u];
+          q[u] = pa[k + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) merge_part(M, a, S, T, p[u].x, q[u], p[u].y, p[u].z);
       }
-      H = logf(S) + T / S;
+      for (; k < nchunks; ++k) {
+        const float4 p = pr[k];
+        merge_part(M, a, S, T, p.x, pa[k], p.y, p.z);
+      }
+      // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
+      H = fmaxf(logf(S) + T / S, 0.f);
     } else {
       H = H_in[idx];
       a = amax_in[idx];
@@ -144,26 +204,27 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     if (a < 0 || a >= vocab) a = min(max(a, 0), vocab - 1);
   }
   const float key = (masked && !(H != H)) ? H : INFINITY;
-  if (c < C) {
-    Hs[c] = key;
-    msk[c] = masked ? 1 : 0;
-  }
-  __syncthreads();
-  int rank = 0, nm = 0;
+  // unmasked positions hold NaN, which no comparison below counts
+  if (c < C) Hs[c] = masked ? key : __int_as_float(0x7fc00000);
+  const int nm_all = __syncthreads_count(masked);
+  int rank = 0;
   if (masked) {
-    for (int j = 0; j < C; ++j) {
-      if (!msk[j]) continue;
-      nm += 1;
-      const float hj = Hs[j];
-      if (hj < key || (hj == key && j < c)) rank += 1;
+    // rank = #{j : (H_j, j) < (H_c, c)}, four broadcast LDS reads at a time
+    const float4* H4 = reinterpret_cast<const float4*>(Hs);
+    const int C4 = C >> 2;
+    for (int q = 0; q < C4; ++q) {
+      const float4 h = H4[q];
+      const int j = 4 * q;
+      rank += (h.x < key || (h.x == key && j < c)) + (h.y < key || (h.y == key && j + 1 < c)) +
+              (h.z < key || (h.z == key && j + 2 < c)) + (h.w < key || (h.w == key && j + 3 < c));
     }
-    order[rank] = c;
+    for (int j = 4 * C4; j < C; ++j) {
+      const float hj = Hs[j];
+      rank += (hj < key || (hj == key && j < c));
+    }
+    sortedH[rank] = key;
   }
-  if (c == 0) {
-    int cntm = 0;
-    for (int j = 0; j < C; ++j) cntm += msk[j];
-    nm_s = cntm;
-  }
+  if (c == 0) nm_s = nm_all;
   __syncthreads();
   if (c == 0) {
     const int n = nm_s;
@@ -171,14 +232,23 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     if (commit_all || n == 0) {
       ks = n;
     } else {
+      // running fp64 sum in rank order; entries are read four at a time
       double S = 0.0;
       int k = 0;
-      for (int j = 0; j < n; ++j) {
-        S += (double)Hs[order[j]];
-        if (S <= (double)gamma)
-          k = j + 1;
-        else
-          break;
+      bool over = false;
+      const float4* s4 = reinterpret_cast<const float4*>(sortedH);
+      for (int j = 0; j < n && !over; j += 4) {
+        const float4 h = s4[j >> 2];
+        const float hv[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (over || j + u >= n) break;
+          S += (double)hv[u];
+          if (S <= (double)gamma)
+            k = j + u + 1;
+          else
+            over = true;
+        }
       }
       ks = k < 1 ? 1 : k;
     }
@@ -191,7 +261,6 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     if (amax_out) amax_out[idx] = masked ? a : -1;
     if (masked && rank < kstar_s) canvas[idx] = a;
   }
-  (void)nm;
 }
 
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
