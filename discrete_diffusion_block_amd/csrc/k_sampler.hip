@@ -155,6 +155,7 @@ void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int r
                      vocab, nchunks, part, part_arg);
 }
 
+template <int TPR>   // threads per canvas row in the chunk merge
 __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restrict__ part,
                                                          const int* __restrict__ part_arg,
                                                          int nchunks, const float* __restrict__ H_in,
@@ -166,43 +167,66 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
                                                          int32_t* __restrict__ n_masked) {
   __shared__ __attribute__((aligned(16))) float Hs[1024];
   __shared__ __attribute__((aligned(16))) float sortedH[1024];
+  __shared__ float Hrow[1024];
+  __shared__ int arow[1024];
   __shared__ int nm_s, kstar_s;
-  const int b = blockIdx.x, c = threadIdx.x;
-  const size_t idx = (size_t)b * C + c;
-  const bool masked = c < C && canvas[idx] == vocab;
-  float H = INFINITY;
-  int a = 0;
-  if (masked) {
+  const int b = blockIdx.x;
+  // phase 1: entropy and argmax of each row; the row's TPR threads (adjacent lanes)
+  // merge interleaved subsets of its chunks, then combine through shuffles
+  {
+    const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+    const size_t ridx = (size_t)b * C + r;
+    const bool rmasked = r < C && canvas[ridx] == vocab;
+    float H = INFINITY;
+    int a = 0;
     if (part) {
-      const float4* pr = part + idx * nchunks;
-      const int* pa = part_arg + idx * nchunks;
-      // chunks merged in index order with the same rule as inside a chunk
       float M = -INFINITY, S = 0.f, T = 0.f;
       a = INT_MAX;
-      int k = 0;
-      for (; k + 4 <= nchunks; k += 4) {
-        float4 p[4];
-        int q[4];
+      if (rmasked) {
+        const float4* pr = part + ridx * nchunks;
+        const int* pa = part_arg + ridx * nchunks;
+        int k = sub;
+        for (; k + 3 * TPR < nchunks; k += 4 * TPR) {
+          float4 p[4];
+          int q[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          p[u] = pr[k + u];
-          q[u] = pa[k + u];
+          for (int u = 0; u < 4; ++u) {
+            p[u] = pr[k + u * TPR];
+            q[u] = pa[k + u * TPR];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) merge_part(M, a, S, T, p[u].x, q[u], p[u].y, p[u].z);
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) merge_part(M, a, S, T, p[u].x, q[u], p[u].y, p[u].z);
+        for (; k < nchunks; k += TPR) {
+          const float4 p = pr[k];
+          merge_part(M, a, S, T, p.x, pa[k], p.y, p.z);
+        }
       }
-      for (; k < nchunks; ++k) {
-        const float4 p = pr[k];
-        merge_part(M, a, S, T, p.x, pa[k], p.y, p.z);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64), t2 = __shfl_xor(T, o, 64);
+        const int a2 = __shfl_xor(a, o, 64);
+        merge_part(M, a, S, T, m2, a2, s2, t2);
       }
       // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
-      H = fmaxf(logf(S) + T / S, 0.f);
-    } else {
-      H = H_in[idx];
-      a = amax_in[idx];
+      if (rmasked) H = fmaxf(logf(S) + T / S, 0.f);
+    } else if (rmasked) {
+      H = H_in[ridx];
+      a = amax_in[ridx];
     }
-    if (a < 0 || a >= vocab) a = min(max(a, 0), vocab - 1);
+    if (rmasked && (a < 0 || a >= vocab)) a = min(max(a, 0), vocab - 1);
+    if (sub == 0 && r < C) {
+      Hrow[r] = rmasked ? H : __int_as_float(0x7fc00000);
+      arow[r] = rmasked ? a : -1;
+    }
   }
+  __syncthreads();
+  // phase 2: one thread per row
+  const int c = threadIdx.x;
+  const size_t idx = (size_t)b * C + c;
+  const bool masked = c < C && arow[c] >= 0;
+  const float H = c < C ? Hrow[c] : 0.f;
+  const int a = c < C ? arow[c] : -1;
   const float key = (masked && !(H != H)) ? H : INFINITY;
   // unmasked positions hold NaN, which no comparison below counts
   if (c < C) Hs[c] = masked ? key : __int_as_float(0x7fc00000);
@@ -257,8 +281,8 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
   }
   __syncthreads();
   if (c < C) {
-    if (H_out) H_out[idx] = masked ? H : __int_as_float(0x7fc00000);
-    if (amax_out) amax_out[idx] = masked ? a : -1;
+    if (H_out) H_out[idx] = H;          // NaN on unmasked rows
+    if (amax_out) amax_out[idx] = a;    // -1 on unmasked rows
     if (masked && rank < kstar_s) canvas[idx] = a;
   }
 }
@@ -267,9 +291,13 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, hipStream_t s) {
-  const int threads = ((C + 63) / 64) * 64;
-  hipLaunchKernelGGL(eb_select_kernel, dim3(batch), dim3(threads), 0, s, part, part_arg, nchunks,
-                     H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+  const int rows64 = ((C + 63) / 64) * 64;
+  if (4 * rows64 <= 1024)
+    hipLaunchKernelGGL(eb_select_kernel<4>, dim3(batch), dim3(4 * rows64), 0, s, part, part_arg, nchunks,
+                       H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+  else
+    hipLaunchKernelGGL(eb_select_kernel<1>, dim3(batch), dim3(rows64), 0, s, part, part_arg, nchunks,
+                       H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
 }
 
 }  // namespace dg
