@@ -177,6 +177,47 @@ def test_sampler_full_size_vs_oracle(gamma):
     assert len([i for i in range(C) if out[1, i] != V and canvas[1, i] == V]) >= 40
 
 
+def test_sampler_ragged_vocab_and_cross_chunk_ties():
+    """A vocabulary that is not a whole number of the first pass's chunks (40008 logits:
+    two full chunks and a ragged third), with the maximum planted at chunk edges, twice
+    across chunks (the lower index must win) and twice inside one chunk."""
+    V, C = 40008, 64
+    print(f"sampler 1x{C}x{V} ragged", flush=True)
+    g = torch.Generator().manual_seed(21)
+    lf = torch.randn(C, V, generator=g) * 4.0
+    big = 30.0
+    lf[0, V - 1] = big                       # last logit of the ragged chunk
+    lf[1, 0] = big                           # first logit
+    lf[2, 16383] = big                       # last of chunk 0 ...
+    lf[2, 16384] = big                       # ... and first of chunk 1: 16383 wins
+    lf[3, 5] = big
+    lf[3, 39000] = big                       # tie across the first and the ragged chunk
+    lf[4, 100] = big
+    lf[4, 101] = big                         # adjacent tie inside a chunk
+    lf[5, 20000] = big
+    lf[5, 20000 + 2048] = big                # tie inside chunk 1, different threads
+    lf[6] = 0.0                              # uniform row: every index ties, H = log V
+    logits = lf.to(torch.bfloat16).view(1, C, V)
+    canvas = torch.full((1, C), V, dtype=torch.int32)
+    d_canvas = canvas.cuda()
+    H = torch.empty(1, C, device="cuda")
+    am = torch.empty(1, C, dtype=torch.int32, device="cuda")
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dg.dg_sample_workspace_size(1, C, V), dtype=torch.uint8, device="cuda")
+    dg.dg_sample_eb(logits.cuda(), d_canvas, 1.0, False, nm, ws, H, am)
+    torch.cuda.synchronize()
+    Ho, ao = O.entropy_argmax(logits[0].double().numpy())
+    ag = am.cpu().numpy()[0]
+    np.testing.assert_array_equal(ag, ao)
+    assert list(ag[:7]) == [V - 1, 0, 16383, 5, 100, 20000, 0]
+    Hg = H.cpu().numpy()[0].astype(np.float64)
+    assert np.max(np.abs(Hg - Ho)) <= 2e-5
+    assert abs(Hg[6] - math.log(V)) <= 2e-5
+    out = d_canvas.cpu().numpy()[0]
+    committed = [i for i in range(C) if out[i] != V]
+    assert eb_valid(Hg, list(range(C)), committed, 1.0, False)
+
+
 @pytest.mark.parametrize("M,E,k", [(256, 128, 8), (512, 128, 8), (33, 8, 2), (1000, 16, 3), (7, 4, 4),
                                    (4096, 256, 16)])
 def test_routing_sort_bit_exact(M, E, k):
