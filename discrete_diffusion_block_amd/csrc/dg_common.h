@@ -207,6 +207,17 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* src, void* lds_tile)
   __builtin_amdgcn_global_load_lds(src, lds_tile, 16, 0, NT ? 2 : 0);
 }
 
+// The same copy issued from inline asm.  The compiler's wait-count bookkeeping then
+// never sees it, which keeps its waits for the caller's ordinary loads precise (with
+// LDS copies in its model it falls back to waiting for every outstanding load); the
+// caller waits for the copy itself with vm_wait.  The asm writes no register, so no
+// register the compiler allocates depends on the copy's completion.
+__device__ __forceinline__ void tile_to_lds_untracked(const uint16_t* src, void* lds_tile) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_tile);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
+               : "memory", "m0");
+}
+
 // LDS written only by direct copies looks never-stored to the optimizer, which may
 // then drop or hoist reads of it; reading through a laundered LDS-address-space
 // pointer keeps every read where it is written.

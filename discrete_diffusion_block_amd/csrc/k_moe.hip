@@ -227,9 +227,10 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)
 // to kMoeGroup = 64 of its tokens) and a tile of output features.  The gate/up
 // GEMM (K = d_model) stages weight and token fragment tiles through LDS rings by
 // direct global->LDS copies and computes a 128-row x 64-token tile; the down GEMM
-// (K = F, short) gives each wave 32 output rows over the whole K loop and shares
-// the token fragments through L1.  Either way every operand byte is read once per
-// workgroup, so the kernels hold up both when tokens spread over all experts (~16
+// (K = F, short) gives each wave 32 output rows over the whole K loop, with its
+// weights in registers and the item's activation tiles shared through an LDS ring.
+// Either way every operand byte is read once per workgroup, so the kernels hold up
+// both when tokens spread over all experts (~16
 // each: a weight-streaming, HBM-bound regime) and when a uniform canvas sends
 // every token to a few experts (many work items per expert, whose workgroups
 // share the expert's weight tiles through L2).
@@ -239,42 +240,10 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)
 
 constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 
-// acc[i][j] += W_i . X_j^T over this wave's k steps (w, w + kstride, ...).
-// STREAM: the weight tiles are read by this workgroup only (the expert has a
-// single work item), so they bypass cache retention; otherwise the expert's
+// STREAM (both GEMMs): the weight tiles are read by this workgroup only (the expert
+// has a single work item), so they bypass cache retention; otherwise the expert's
 // other items re-read them from L2.
-template <int NW, int NT, bool STREAM>
-__device__ __forceinline__ void grouped_partial(const uint16_t* const (&wp)[NW],
-                                                const uint16_t* const (&xp)[NT], int nk, int w,
-                                                f32x4 (&acc)[NW][NT], int kstride = 4) {
-  u32x4 Wa[NW][2], Xa[NT][2], Wb[NW][2], Xb[NT][2], Wc[NW][2], Xc[NT][2];
-  auto ld = [&](u32x4 (&W)[NW][2], u32x4 (&X)[NT][2], int step) {
-    const int k = (w + kstride * step) * 1024;
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        W[i][q] = STREAM ? ld16_stream(wp[i] + k + 512 * q) : ld16(wp[i] + k + 512 * q);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) X[j][q] = ld16(xp[j] + k + 512 * q);
-  };
-  auto mm = [&](u32x4 (&W)[NW][2], u32x4 (&X)[NT][2]) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int i = 0; i < NW; ++i) acc[i][j] = mfma16x2(W[i][0], X[j][0], W[i][1], X[j][1], acc[i][j]);
-  };
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n = w < nk ? (nk - w + kstride - 1) / kstride : 0;
-  pipeline2(n, [&](int t) { ld(Wa, Xa, t); }, [&](int t) { ld(Wb, Xb, t); },
-            [&] { mm(Wa, Xa); }, [&] { mm(Wb, Xb); });
-}
-
+//
 // Gate/up, operands staged through LDS.  Workgroup tile: 128 packed weight rows
 // (gate and up blocks of 4 feature blocks) x one work item (up to 64 tokens); the
 // 4 waves form a 2 x 2 grid of 64-row x 32-token sub-tiles.  Per 64-wide k
@@ -432,32 +401,89 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
                      cnt, poff, items, n_items, F, d, a);
 }
 
-// down: Y[slot][n] = A[slot] . W_d[e][n]^T; wave w owns output row blocks
-// n0/16 + 2w, +1 over the whole K loop (no split-K: K = F is short).
-template <int NT, bool STREAM>
-__device__ __forceinline__ void down_item(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
-                                          int ne, int F, int d, int n0, int lane, int w, float* Y) {
-  constexpr int NW = 2;
+// down: Y[slot][n] = A[slot] . W_d[e][n]^T over K = F.  Workgroup tile: 128 output
+// rows x one work item.  Wave wv owns row blocks 2wv, 2wv + 1 and loads their weight
+// fragments straight into registers two steps ahead (each weight byte is used by that
+// wave alone); the item's activation tiles, shared by the four waves, are copied once
+// per workgroup into a three-step LDS ring.
+constexpr int kDnXS = 3;
+constexpr int kDnXBytes = 4 * kGuKT * 1024;      // 64 tokens x 64 k
+constexpr int kDnLds = kDnXS * kDnXBytes;
+
+template <bool STREAM, int NT>
+__device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
+                                          int ne, int F, int d, int n0, int lane, int wv, float* Y,
+                                          char* ring) {
   const int nblk = d >> 4;
-  const uint16_t* wp[NW];
+  const int nk = F / (32 * kGuKT);                // >= 1 (F % 64 == 0)
+  const int rb0 = (n0 >> 4) + 2 * wv;
+  const uint16_t* w0 = wd_e + fm_tile(min(rb0, nblk - 1), 0, F, lane);
+  const uint16_t* w1 = wd_e + fm_tile(min(rb0 + 1, nblk - 1), 0, F, lane);
+  // wave wv copies token block wv (the item's last block again past its end; unread)
+  const uint16_t* xsrc = A + fm_tile((slot0 >> 4) + min(wv, NT - 1), 0, F, lane);
+  lds_char* const lx = lds_launder(ring);
+  typedef u32x4 WSet[4];                           // rows rb0 k0, k1; rows rb0+1 k0, k1
+  auto issue = [&](int step, WSet& w) {
+    char* dst = ring + (step % kDnXS) * kDnXBytes + wv * kGuKT * 1024;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) wp[i] = wd_e + fm_tile(min((n0 >> 4) + NW * w + i, nblk - 1), 0, F, lane);
-  const uint16_t* xp[NT];
+    for (int t = 0; t < kGuKT; ++t) tile_to_lds_untracked(xsrc + (step * kGuKT + t) * 512, dst + t * 1024);
+    const int o = step * kGuKT * 512;
+    if (STREAM) {
+      w[0] = ld16_stream(w0 + o); w[1] = ld16_stream(w0 + o + 512);
+      w[2] = ld16_stream(w1 + o); w[3] = ld16_stream(w1 + o + 512);
+    } else {
+      w[0] = ld16(w0 + o); w[1] = ld16(w0 + o + 512);
+      w[2] = ld16(w1 + o); w[3] = ld16(w1 + o + 512);
+    }
+  };
+  f32x4 acc[2][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) xp[j] = A + fm_tile((slot0 >> 4) + j, 0, F, lane);
-  f32x4 acc[NW][NT];
-  grouped_partial<NW, NT, STREAM>(wp, xp, F >> 6, 0, acc, 1);
-  const int r = lane & 15, g = lane >> 4;
+  for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // step s: its copies and loads were issued two iterations earlier; the previous
+  // iteration's (kGuKT copies + 4 loads) may still be in flight unless it issued none.
+  // Refilling ring slot (s + 2) % 3 is safe after the barrier: every wave consumed
+  // that slot's step s - 1 before arriving.
+  auto body = [&](int s, WSet& wc, WSet& wn, bool more, bool last) {
+    if (!last) vm_wait<kGuKT + 4>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (more) issue(s + 2, wn);
+    const lds_char* sx = lx + (s % kDnXS) * kDnXBytes + lane * 16;
+    u32x4 X[NT][kGuKT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int t = 0; t < kGuKT; ++t) X[j][t] = ld16_lds(sx + (j * kGuKT + t) * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc[0][j] = mfma16x2(wc[0], X[j][0], wc[1], X[j][1], acc[0][j]);
+      acc[1][j] = mfma16x2(wc[2], X[j][0], wc[3], X[j][1], acc[1][j]);
+    }
+  };
+  WSet ws0, ws1, ws2;
+  issue(0, ws0);
+  if (nk > 1) issue(1, ws1);
+  int s = 0;
+  for (; s + 5 <= nk; s += 3) {     // steady state: every iteration issues step s + 2
+    body(s, ws0, ws2, true, false);
+    body(s + 1, ws1, ws0, true, false);
+    body(s + 2, ws2, ws1, true, false);
+  }
+  const int r = nk - s;             // 1 .. 4 steps left
+  if (r > 0) body(s, ws0, ws2, r > 2, r == 1);
+  if (r > 1) body(s + 1, ws1, ws0, r > 3, r == 2);
+  if (r > 2) body(s + 2, ws2, ws1, false, r == 3);
+  if (r > 3) body(s + 3, ws0, ws2, false, true);
+  const int rr = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int t = t0 + 16 * j + r;
-    if (t < ne) {
+    const int t = t0 + 16 * j + rr;
+    if (t >= ne) continue;
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-        if ((n0 >> 4) + NW * w + i < nblk)
-          *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + r) * d + n0 + 16 * (NW * w + i) + 4 * g) =
-              acc[i][j];
-    }
+    for (int i = 0; i < 2; ++i)
+      if (rb0 + i < nblk)
+        *reinterpret_cast<f32x4*>(Y + (size_t)(slot0 + 16 * j + rr) * d + (rb0 + i) * 16 + 4 * g) = acc[i][j];
   }
 }
 
@@ -468,7 +494,9 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
                                                        const int2* __restrict__ items,
                                                        const int32_t* __restrict__ n_items,
                                                        int F, int d, float* __restrict__ Y) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int item, nb;
   if (!xcd_item_schedule(*n_items, (d + kDownRows - 1) / kDownRows, &item, &nb)) return;
   const int2 it = items[item];
@@ -477,21 +505,17 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   const int n0 = nb * kDownRows;
   const uint16_t* wd_e = wd + (size_t)e * d * F;
   const int nt = min(4, (ne - t0 + 15) >> 4);
-  if (ne <= kMoeGroup) {
-    switch (nt) {
-      case 1: down_item<1, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      case 2: down_item<2, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      case 3: down_item<3, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      default: down_item<4, true>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-    }
-  } else {
-    switch (nt) {
-      case 1: down_item<1, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      case 2: down_item<2, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      case 3: down_item<3, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-      default: down_item<4, false>(wd_e, A, slot0, t0, ne, F, d, n0, lane, w, Y); break;
-    }
+  // an expert with a single work item streams its weights (read by no other item)
+#define DOWN_TILE(NT)                                                                            \
+  (ne <= kMoeGroup ? down_tile<true, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring)   \
+                   : down_tile<false, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring))
+  switch (nt) {
+    case 1: DOWN_TILE(1); break;
+    case 2: DOWN_TILE(2); break;
+    case 3: DOWN_TILE(3); break;
+    default: DOWN_TILE(4); break;
   }
+#undef DOWN_TILE
 }
 
 int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
@@ -501,7 +525,7 @@ void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* c
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
   const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * ((d + kDownRows - 1) / kDownRows);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(blocks), dim3(256), 0, s, a, w_down, cnt, poff, items,
+  hipLaunchKernelGGL(moe_down_kernel, dim3(blocks), dim3(256), kDnLds, s, a, w_down, cnt, poff, items,
                      n_items, F, d, Y);
 }
 
