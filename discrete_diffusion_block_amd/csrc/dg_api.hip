@@ -602,7 +602,7 @@ dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset) 
 
 dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
                               void* stream) {
-  if (!d_r || !d_ids || !d_w || M < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E)
+  if (!d_r || !d_ids || !d_w || M < 1 || E < 4 || E > 256 || E % 4 || k < 1 || k > 16 || k > E)
     return fail(DG_ERR_INVALID_ARG, "bad router arguments");
   launch_topk(d_r, M, E, k, d_ids, d_w, (hipStream_t)stream);
   return check_launch("router top-k");
@@ -612,7 +612,7 @@ dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, f
                         int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
                         int32_t* d_items, int32_t* d_n_items, void* stream) {
   if (!d_r || !d_ids || !d_w || !d_cnt || !d_poff || !d_perm || !d_inv || !d_items || !d_n_items ||
-      M < 1 || E < 4 || E > 256 || k < 1 || k > 16 || k > E)
+      M < 1 || E < 4 || E > 256 || E % 4 || k < 1 || k > 16 || k > E)
     return fail(DG_ERR_INVALID_ARG, "bad routing arguments");
   hipStream_t s = (hipStream_t)stream;
   launch_topk(d_r, M, E, k, d_ids, d_w, s);

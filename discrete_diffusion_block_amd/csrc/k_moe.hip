@@ -19,49 +19,65 @@ namespace dg {
 
 // ---------------------------------------------------------------- top-k
 
-// One wave ranks one token's E router logits by (logit desc, id asc); NaN logits
-// rank below every number.  ids/w get the k selected experts and the softmax of
-// their logits.  Selected logits stay in registers (k <= 16).
-__device__ __forceinline__ void topk_row(const float* __restrict__ rr, int E, int k, int lane,
-                                         int32_t* __restrict__ ids, float* __restrict__ w) {
-  float v[4];
+// Selection key of logit x of expert e: larger key = larger logit, then lower id;
+// NaN ranks as -inf and -0 as +0.  Keys are unique and nonzero.
+__device__ __forceinline__ uint64_t sel_key(float x, int e) {
+  if (x != x) x = -INFINITY;
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t)o << 32 | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+// rotation by N lanes within each 16-lane DPP row
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xf, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ uint64_t row_max64(uint64_t v) {
+  const uint64_t o = (uint64_t)row_ror<N>((uint32_t)(v >> 32)) << 32 | row_ror<N>((uint32_t)v);
+  return o > v ? o : v;
+}
+
+constexpr int kTopkRows = 16;                // token rows per workgroup (16 lanes each)
+constexpr int kTopkStride = 256 + 16;        // LDS row stride (floats): rows 16 banks apart
+
+// The k largest of one token row's E logits, 16 lanes per row, lane l holding
+// experts l + 16 i (i < EPL).  Round t takes on every lane the largest key below
+// the previous round's winner, then the row maximum by DPP rotations within the
+// 16 lanes; the winners come out in rank order.  The weights are the softmax of
+// the k selected logits.
+template <int EPL>
+__device__ __forceinline__ void select_row(const float* rl, int row, int m, int M, int E, int k,
+                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int sl = threadIdx.x & 15;
+  uint64_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    float x = e < E ? rr[e] : -INFINITY;
-    if (x != x) x = -INFINITY;
-    v[i] = x;
+  for (int i = 0; i < EPL; ++i) {
+    const int e = sl + 16 * i;
+    key[i] = e < E ? sel_key(rl[row * kTopkStride + e], e) : 0ull;
   }
-  unsigned taken = 0;
   float sel[16];
   int sid[16];
+  uint64_t prev = ~0ull;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     sel[t] = -INFINITY;
     sid[t] = 0;
     if (t < k) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
+      uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      sel[t] = bv;
-      sid[t] = bi;
+      for (int i = 0; i < EPL; ++i) best = (key[i] < prev && key[i] > best) ? key[i] : best;
+      best = row_max64<8>(best);
+      best = row_max64<4>(best);
+      best = row_max64<2>(best);
+      best = row_max64<1>(best);
+      prev = best;
+      sel[t] = key_logit(best);
+      sid[t] = (int)(0xffffffffu - (uint32_t)best);
     }
   }
   float z = 0.f, ex[16];
@@ -70,25 +86,50 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ rr, int E, in
     ex[t] = (t < k && sel[t] != -INFINITY) ? expf(sel[t] - sel[0]) : 0.f;
     z += ex[t];
   }
-  // lane t < k writes selection t
+  if (m < M)
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
-    if (t < k && lane == t) {
-      ids[t] = sid[t];
-      w[t] = ex[t] / z;
-    }
+    for (int t = 0; t < 16; ++t)
+      if (t < k && sl == t) {
+        ids[(size_t)m * k + t] = sid[t];
+        w[(size_t)m * k + t] = ex[t] / z;
+      }
 }
 
+// Workgroup = 16 token rows: the rows' logits are staged in LDS, then each wave
+// selects for 4 rows at once.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ r, int M, int E, int k,
                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  topk_row(r + (size_t)m * E, E, k, lane, ids + (size_t)m * k, w + (size_t)m * k);
+  __shared__ float rl[kTopkRows * kTopkStride];
+  const int tid = threadIdx.x, m0 = blockIdx.x * kTopkRows;
+  // 16 rows x E logits as 16-byte pieces (E % 4 == 0), at most 4 per thread, all in flight
+  const int q = E >> 2;
+  f32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + 256 * u, row = i / q;
+    if (i < kTopkRows * q && m0 + row < M)
+      v[u] = *reinterpret_cast<const f32x4*>(r + (size_t)(m0 + row) * E + 4 * (i - row * q));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + 256 * u, row = i / q;
+    if (i < kTopkRows * q && m0 + row < M)
+      *reinterpret_cast<f32x4*>(&rl[row * kTopkStride + 4 * (i - row * q)]) = v[u];
+  }
+  __syncthreads();
+  const int row = tid >> 4, m = m0 + row;
+  switch ((E + 15) >> 4) {
+    case 1: select_row<1>(rl, row, m, M, E, k, ids, w); break;
+    case 2: select_row<2>(rl, row, m, M, E, k, ids, w); break;
+    case 3: case 4: select_row<4>(rl, row, m, M, E, k, ids, w); break;
+    case 5: case 6: case 7: case 8: select_row<8>(rl, row, m, M, E, k, ids, w); break;
+    default: select_row<16>(rl, row, m, M, E, k, ids, w); break;
+  }
 }
 
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((M + 3) / 4), dim3(256), 0, s, r, M, E, k, ids, w);
+  hipLaunchKernelGGL(topk_kernel, dim3((M + kTopkRows - 1) / kTopkRows), dim3(256), 0, s, r, M, E, k,
+                     ids, w);
 }
 
 // ---------------------------------------------------------------- permutation
@@ -98,29 +139,70 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
 // poff[e] + cnt[e]) with poff 16-aligned, so each expert's gathered rows start on
 // a fragment-tile boundary; slots keep assignment order within an expert.
 // perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
-// (expert, first token) of every kMoeGroup-token group.  Offsets come from
-// one-wave prefix scans; the rank of an assignment among equal experts of its
-// wave comes from ballots on the expert id's bits.
-template <int NW>
+// (expert, first token) of every kMoeGroup-token group.
+//
+// Wave w owns the contiguous assignment range [w*per, (w+1)*per) and walks it 64 at
+// a time; the lanes holding one expert find each other by ballots on the id's bits,
+// which gives each assignment its rank among them.  A first walk counts every
+// expert per wave (no workgroup barrier inside the walk: each count is updated by
+// one lane of its wave), a one-wave prefix scan turns the totals into offsets, and
+// a second walk writes slot = offset of (wave, expert) + running rank.  The ids are
+// staged in LDS when they fit.
+template <int NW, int CAP>
 struct RouteLds {
-  int hist[256];
   int base[256];
   int ibase[256];
+  int tot[256];
   int wcnt[NW][256];
+  int ids[CAP];
 };
 
-template <int NW>
+// Lanes of this wave holding the same expert id e (8 bits; e < 0: no assignment):
+// the rank of this lane among them and their number.
+__device__ __forceinline__ void same_expert(int e, int lane, int& rank, int& tot) {
+  unsigned long long same = __ballot(e >= 0);
+  if (e < 0) same = ~same;
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const unsigned long long b1 = __ballot(e >= 0 && ((e >> bit) & 1));
+    same &= ((e >> bit) & 1) ? b1 : ~b1;
+  }
+  rank = __popcll(same & ((1ull << lane) - 1ull));
+  tot = __popcll(same);
+}
+
+template <int NW, int CAP>
 __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E, int P,
                             int32_t* __restrict__ cnt, int32_t* __restrict__ poff,
                             int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                             int2* __restrict__ items, int32_t* __restrict__ n_items,
-                            int32_t* __restrict__ cnt_log, RouteLds<NW>& L) {
+                            int32_t* __restrict__ cnt_log, RouteLds<NW, CAP>& L) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += NT) L.hist[e] = 0;
+  for (int i = tid; i < NW * E; i += NT) L.wcnt[i / E][i % E] = 0;
   for (int i = tid; i < P; i += NT) perm[i] = -1;
+  const bool staged = A <= CAP;
+  if (staged) {
+    constexpr int U = (CAP + NT - 1) / NT;   // every load in flight at once
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (tid + u * NT < A) v[u] = ids[tid + u * NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (tid + u * NT < A) L.ids[tid + u * NT] = v[u];
+  }
   __syncthreads();
-  for (int a = tid; a < A; a += NT) atomicAdd(&L.hist[ids[a]], 1);
+  const int per = ((A + NW - 1) / NW + 63) & ~63;
+  const int w0 = min(A, wv * per), w1 = min(A, w0 + per);
+  auto id_at = [&](int a) { return a < w1 ? (staged ? L.ids[a] : ids[a]) : -1; };
+  int* wc = L.wcnt[wv];
+  for (int c = w0; c < w1; c += 64) {
+    const int e = id_at(c + lane);
+    int rank, tot;
+    same_expert(e, lane, rank, tot);
+    if (e >= 0 && rank == tot - 1) wc[e] += tot;
+  }
   __syncthreads();
   if (wv == 0) {
     // lane owns experts [lane*epl, lane*epl + epl)
@@ -129,8 +211,11 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
-        ps += (L.hist[e] + 15) & ~15;
-        is += (L.hist[e] + kMoeGroup - 1) / kMoeGroup;
+        int c = 0;
+        for (int w2 = 0; w2 < NW; ++w2) c += L.wcnt[w2][e];
+        L.tot[e] = c;
+        ps += (c + 15) & ~15;
+        is += (c + kMoeGroup - 1) / kMoeGroup;
       }
     }
     int incl_p = ps, incl_i = is;
@@ -146,7 +231,7 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
-        const int c = L.hist[e];
+        const int c = L.tot[e];
         L.base[e] = run_p;
         poff[e] = run_p;
         cnt[e] = c;
@@ -164,41 +249,30 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   __syncthreads();
   for (int e = tid; e < E; e += NT) {
     int it = L.ibase[e];
-    for (int t0 = 0; t0 < L.hist[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
-  }
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int start = 0; start < A; start += NT) {
-    for (int i = tid; i < NW * E; i += NT) L.wcnt[i / E][i % E] = 0;
-    __syncthreads();
-    const int a = start + tid;
-    const int e = a < A ? ids[a] : -1;
-    // lanes holding the same expert: agree on validity and on each of 8 id bits
-    unsigned long long same = __ballot(e >= 0);
-    if (e < 0) same = ~same;
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const unsigned long long b1 = __ballot(e >= 0 && ((e >> bit) & 1));
-      same &= ((e >> bit) & 1) ? b1 : ~b1;
+    for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
+    // per-wave running slot of expert e: its offset plus the earlier waves' counts
+    int run = L.base[e];
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int c = L.wcnt[w2][e];
+      L.wcnt[w2][e] = run;
+      run += c;
     }
-    const int rank = __popcll(same & below), tot = __popcll(same);
-    if (e >= 0 && rank == tot - 1) L.wcnt[wv][e] = tot;
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int c = w0; c < w1; c += 64) {
+    const int a = c + lane, e = id_at(a);
+    int rank, tot;
+    same_expert(e, lane, rank, tot);
     if (e >= 0) {
-      int before = 0;
-      for (int w2 = 0; w2 < wv; ++w2) before += L.wcnt[w2][e];
-      const int slot = L.base[e] + before + rank;
+      const int slot = wc[e] + rank;
       perm[slot] = a / k;
       inv[a] = slot;
     }
-    __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += NT) {
-      int s2 = 0;
-      for (int w2 = 0; w2 < NW; ++w2) s2 += L.wcnt[w2][e2];
-      L.base[e2] += s2;
-    }
-    __syncthreads();
+    if (e >= 0 && rank == tot - 1) wc[e] += tot;
   }
 }
+
+constexpr int kRouteIds = 4096;   // ids staged in LDS (16 KiB)
 
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
@@ -208,8 +282,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int2* __restrict__ items,
                                                      int32_t* __restrict__ n_items,
                                                      int32_t* __restrict__ cnt_log) {
-  __shared__ RouteLds<16> L;
-  route_block<16>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, cnt_log, L);
+  __shared__ RouteLds<16, kRouteIds> L;
+  route_block<16, kRouteIds>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, cnt_log, L);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,

@@ -209,8 +209,9 @@ dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset);
 
 /* ---- kernel taps for tests (not part of the stable contract) ---- */
 
-/* Router selection alone: r fp32 [M][E] -> ids int32 [M][k] (by logit desc, id
- * asc) and weights fp32 [M][k] (softmax over the k selected logits). */
+/* Router selection alone: r fp32 [M][E] (E a multiple of 4 in [4, 256], rows
+ * 16-byte aligned) -> ids int32 [M][k] (by logit desc, id asc) and weights fp32
+ * [M][k] (softmax over the k selected logits). */
 dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_ids,
                               float* d_w, void* stream);
 
