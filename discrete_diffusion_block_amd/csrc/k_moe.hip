@@ -321,15 +321,26 @@ constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 // Gate/up, operands staged through LDS.  Workgroup tile: 128 packed weight rows
 // (gate and up blocks of 4 feature blocks) x one work item (up to 64 tokens); the
 // 4 waves form a 2 x 2 grid of 64-row x 32-token sub-tiles.  Per 64-wide k
-// step the workgroup copies 8 weight and 4 token blocks (two 1 KiB fragment
-// tiles each) straight into LDS: weights into a three-step ring (two steps
-// ahead), token tiles -- L2 hits -- into a two-step ring (one step ahead).  The
-// 64 KiB of rings let two workgroups share a CU, which hides more latency than
+// step the workgroup copies 8 weight blocks (two 1 KiB fragment tiles each) and
+// 4 token blocks straight into LDS: weights into a three-step ring (two steps
+// ahead), token rows -- L2 hits -- into a two-step ring (one step ahead).  The
+// ~66 KiB of rings let two workgroups share a CU, which hides more latency than
 // deeper rings in one.  Every weight byte is read once per workgroup and shared
 // by all its token tiles.
+//
+// A token block's 64-wide k step is 16 rows x 128 bytes of row-major h, gathered
+// through the permutation.  It is copied as two 8-row halves in which every lane
+// moves one 16-byte piece, so each row's 128 bytes come in as one whole cache
+// line (a fragment-shaped copy would touch each line twice, 64 bytes at a time,
+// and the per-CU rate of line requests is what bounds this kernel).  In LDS a
+// half is 8 rows of 128 bytes with the pieces of row r stored XOR-swizzled by r,
+// and the second half starts 1152 bytes after the first: the MFMA operand reads
+// (16 rows, one piece column each) then hit 16 distinct bank groups.
 constexpr int kGuRB = 8, kGuTB = 4, kGuKT = 2;
 constexpr int kGuWSlots = 3, kGuXSlots = 2;
-constexpr int kGuWBytes = kGuRB * kGuKT * 1024, kGuXBytes = kGuTB * kGuKT * 1024;
+constexpr int kGuXHalf = 1024 + 128;           // bytes from one 8-row half to the next
+constexpr int kGuXBlock = 2 * kGuXHalf;        // one token block of a k step
+constexpr int kGuWBytes = kGuRB * kGuKT * 1024, kGuXBytes = kGuTB * kGuXBlock;
 constexpr int kGuLds = kGuWSlots * kGuWBytes + kGuXSlots * kGuXBytes;
 constexpr int kGuCopies = kGuRB * kGuKT / 4;   // weight tile copies per wave per step
 
@@ -343,17 +354,19 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   const int nk = d / (32 * kGuKT);
   constexpr int WB = kGuRB / 4, XB = kGuTB / 4;
   const uint16_t* wsrc[WB];
-  const uint16_t* xsrc[XB];
 #pragma unroll
   for (int u = 0; u < WB; ++u) wsrc[u] = wgu_e + fm_tile(2 * f0 + wv * WB + u, 0, d, lane);
-  // The token tiles are gathered on the fly: lane (r, g) of a fragment tile copies
-  // the 16 bytes of its slot's token row (row-major h) at k columns 8g .. 8g + 7 of
-  // the tile.  Token blocks past the item's last one re-read that block, and
-  // padding slots read row 0: their outputs are dropped.
+  // The token rows are gathered on the fly: in half h of a token block, lane i
+  // copies piece (i % 8) ^ (i / 8) of the step's 128 bytes of row 8h + i / 8.
+  // Token blocks past the item's last one re-read that block, and padding slots
+  // read row 0: their outputs are dropped.
+  static_assert(XB == 1, "one token block per wave");
+  const uint16_t* xsrc[2];
 #pragma unroll
-  for (int u = 0; u < XB; ++u) {
-    const int tok = perm[slot0 + 16 * min(wv * XB + u, ntb - 1) + (lane & 15)];
-    xsrc[u] = h_rm + (size_t)max(tok, 0) * d + 8 * (lane >> 4);
+  for (int h = 0; h < 2; ++h) {
+    const int rr = lane >> 3;
+    const int tok = perm[slot0 + 16 * min(wv, ntb - 1) + 8 * h + rr];
+    xsrc[h] = h_rm + (size_t)max(tok, 0) * d + 8 * ((lane & 7) ^ rr);
   }
   char* const wring = ring;
   char* const xring = ring + kGuWSlots * kGuWBytes;
@@ -366,12 +379,9 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
         tile_to_lds<STREAM>(wsrc[u] + (step * kGuKT + t) * 512, dst + (u * kGuKT + t) * 1024);
   };
   auto issue_x = [&](int step) {
-    char* dst = xring + (step % kGuXSlots) * kGuXBytes + wv * XB * kGuKT * 1024;
+    char* dst = xring + (step % kGuXSlots) * kGuXBytes + wv * kGuXBlock;
 #pragma unroll
-    for (int u = 0; u < XB; ++u)
-#pragma unroll
-      for (int t = 0; t < kGuKT; ++t)
-        tile_to_lds<false>(xsrc[u] + (step * kGuKT + t) * 32, dst + (u * kGuKT + t) * 1024);
+    for (int h = 0; h < 2; ++h) tile_to_lds<false>(xsrc[h] + step * 64, dst + h * kGuXHalf);
   };
   const int wr = wv & 1, wt = wv >> 1;
   f32x4 acc[WI][WJ];
@@ -394,6 +404,13 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
     if (j + XS - 1 >= 0 && j + XS - 1 < nk) issue_x(j + XS - 1);
     if (j + WS - 1 < nk) issue_w(j + WS - 1);
   }
+  // this lane's operand (token row r, k group g) of k tile t within a token block
+  int xoff[kGuKT];
+  {
+    const int r = lane & 15, g = lane >> 4, rr = r & 7;
+#pragma unroll
+    for (int t = 0; t < kGuKT; ++t) xoff[t] = (r >> 3) * kGuXHalf + rr * 128 + (((4 * t + g) ^ rr) << 4);
+  }
   u32x4 Af[WI][kGuKT], Bf[WJ][kGuKT];
   for (int s = 0; s < nk; ++s) {
     if (s + WS - 2 < nk) vm_wait<kAfterX>();
@@ -402,7 +419,7 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
     if (s + XS - 1 < nk) issue_x(s + XS - 1);
     if (s + WS - 1 < nk) issue_w(s + WS - 1);
     const lds_char* sw = lw + (s % kGuWSlots) * kGuWBytes + lane * 16;
-    const lds_char* sx = lx + (s % kGuXSlots) * kGuXBytes + lane * 16;
+    const lds_char* sx = lx + (s % kGuXSlots) * kGuXBytes;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -410,7 +427,7 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
 #pragma unroll
-      for (int t = 0; t < kGuKT; ++t) Bf[j][t] = ld16_lds(sx + ((wt * WJ + j) * kGuKT + t) * 1024);
+      for (int t = 0; t < kGuKT; ++t) Bf[j][t] = ld16_lds(sx + (wt * WJ + j) * kGuXBlock + xoff[t]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
