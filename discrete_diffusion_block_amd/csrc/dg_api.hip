@@ -63,14 +63,18 @@ struct Timed {
   int kind;
   hipStream_t s;
   bool on;
+  // The events ride on the launch itself (next_launch_events): they time the kernel
+  // from its start to its completion without adding packets to the stream.
   Timed(const dg_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_) {
     on = c && c->prof.on && (c->prof.mask >> k & 1u) && c->prof.used < c->prof.kind.size();
-    if (on) (void)hipEventRecord(c->prof.ev[2 * c->prof.used], s);
+    if (on) next_launch_events() = LaunchEvents{c->prof.ev[2 * c->prof.used], c->prof.ev[2 * c->prof.used + 1]};
   }
   ~Timed() {
     if (on) {
-      (void)hipEventRecord(c->prof.ev[2 * c->prof.used + 1], s);
-      c->prof.kind[c->prof.used++] = kind;
+      // a statement that launched nothing leaves its events unused: not counted
+      const bool used = next_launch_events().start == nullptr;
+      next_launch_events() = LaunchEvents{};
+      c->prof.kind[c->prof.used++] = used ? kind : -1;
     }
   }
 };
@@ -578,6 +582,7 @@ dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count) {
     count[k] = 0;
   }
   for (size_t i = 0; i < p.used; ++i) {
+    if (p.kind[i] < 0) continue;
     if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess) return fail(DG_ERR_HIP, "event sync failed");
     float t = 0.f;
     if (hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess)

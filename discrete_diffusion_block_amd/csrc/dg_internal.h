@@ -26,6 +26,35 @@ struct KvLayer {
   int window;                // 0 = global layer
 };
 
+// Every kernel launch goes through launch_kernel.  The engine's profiler may park a
+// pair of timing events in next_launch_events(); the next launch then attaches them
+// to its own dispatch (signalled as the kernel starts and when it completes, so no
+// marker packets change the schedule being measured) and clears them.  `done`
+// (optional) is signalled by the kernel's completion, for another stream to wait on.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& next_launch_events() {
+  static thread_local LaunchEvents e;
+  return e;
+}
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                          hipEvent_t done, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  LaunchEvents& ev = next_launch_events();
+  if (ev.start) {
+    const LaunchEvents t = ev;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, t.start, t.stop, 0u, static_cast<KArgs>(args)...);
+    if (done) (void)hipEventRecord(done, s);
+  } else if (done) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, nullptr, done, 0u, static_cast<KArgs>(args)...);
+  } else {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, nullptr, nullptr, 0u, static_cast<KArgs>(args)...);
+  }
+}
+
 // ---- embed / norm / prep ----
 void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
                  float* temb, hipStream_t s);

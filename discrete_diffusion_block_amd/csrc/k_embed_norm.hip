@@ -39,7 +39,7 @@ void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d
                  float* temb, hipStream_t s) {
   const long total = (long)g.batch * g.n * (hd / 2) + (temb ? d : 0);
   const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
-  hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(256), 0, s, g, hd, theta, rope_tab, d, t, temb);
+  launch_kernel(prep_kernel, dim3(blocks), dim3(256), 0, s, nullptr, g, hd, theta, rope_tab, d, t, temb);
 }
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, 
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s) {
-  hipLaunchKernelGGL(embed_norm_kernel, dim3(M), dim3(256), 0, s, tokens, embed, temb, gain, eps, x,
-                     h, d, vocab);
+  launch_kernel(embed_norm_kernel, dim3(M), dim3(256), 0, s, nullptr, tokens, embed, temb, gain, eps, x, h, d,
+                vocab);
 }
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const float* gain, float eps,
@@ -131,10 +131,7 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
                     int d, hipStream_t s, hipEvent_t done) {
   // `done`, when given, is signalled by the kernel's own completion (no separate
   // marker on the stream)
-  if (done)
-    hipExtLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, nullptr, done, 0, x, gain, eps, h, h_rm, d);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gain, eps, h, h_rm, d);
+  launch_kernel(rmsnorm_kernel, dim3(M), dim3(256), 0, s, done, x, gain, eps, h, h_rm, d);
 }
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]
@@ -176,8 +173,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys,
 
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(M), dim3(256), 0, s, x, ys, Y, wts, inv, k, d, next_gain, eps,
-                     h);
+  launch_kernel(combine_kernel, dim3(M), dim3(256), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
@@ -194,13 +190,13 @@ __global__ __launch_bounds__(256) void copy16_kernel(const u32x4* __restrict__ s
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
   const size_t n = n_bytes / 16;
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 8192);
-  hipLaunchKernelGGL(copy16_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const u32x4*>(src),
-                     reinterpret_cast<u32x4*>(dst), n);
+  launch_kernel(copy16_kernel, dim3(blocks), dim3(256), 0, s, nullptr, reinterpret_cast<const u32x4*>(src),
+                reinterpret_cast<u32x4*>(dst), n);
 }
 
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+  launch_kernel(fill_i32_kernel, dim3(blocks), dim3(256), 0, s, nullptr, p, v, n);
 }
 
 }  // namespace dg

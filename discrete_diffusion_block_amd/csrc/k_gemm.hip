@@ -187,11 +187,8 @@ static void run_dense(const DenseArgs& a, hipStream_t s, hipEvent_t done = nullp
   const int n_tiles = (a.nblk + WN - 1) / WN, m_tiles = (a.M + 16 * WM - 1) / (16 * WM);
   const int blocks = kXcd * ((n_tiles + kXcd - 1) / kXcd) * m_tiles;
   const size_t lds = sizeof(f32x4) * NW * WN * WM * 64;
-  if (done)   // signalled by the kernel's own completion
-    hipExtLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), (uint32_t)lds, s,
-                          nullptr, done, 0, a);
-  else
-    hipLaunchKernelGGL((dense_gemm<WN, WM, EPI, NW>), dim3(blocks), dim3(64 * NW), lds, s, a);
+  // `done` (optional) is signalled by the kernel's own completion
+  launch_kernel(dense_gemm<WN, WM, EPI, NW>, dim3(blocks), dim3(64 * NW), lds, s, done, a);
 }
 
 void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int N, int K,
@@ -375,8 +372,8 @@ void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits
   const int n_row = (N + 16 * kHeadRB - 1) / (16 * kHeadRB);
   const int n_tok = (M + 16 * kHeadTB - 1) / (16 * kHeadTB);
   const int blocks = kXcd * ((n_row + kXcd - 1) / kXcd) * n_tok;
-  hipLaunchKernelGGL(head_gemm, dim3(blocks), dim3(256), lds, s, h, embed, logits, M, N, K, w_blocks,
-                     n_row, n_tok);
+  launch_kernel(head_gemm, dim3(blocks), dim3(256), lds, s, nullptr, h, embed, logits, M, N, K, w_blocks,
+                n_row, n_tok);
 }
 
 }  // namespace dg

@@ -128,8 +128,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ r, 
 }
 
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((M + kTopkRows - 1) / kTopkRows), dim3(256), 0, s, r, M, E, k,
-                     ids, w);
+  launch_kernel(topk_kernel, dim3((M + kTopkRows - 1) / kTopkRows), dim3(256), 0, s, nullptr, r, M, E, k,
+                ids, w);
 }
 
 // ---------------------------------------------------------------- permutation
@@ -289,8 +289,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
                   hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(1024), 0, s, ids, M * k, k, E, moe_max_slots(M, k, E),
-                     cnt, poff, perm, inv, items, n_items, cnt_log);
+  launch_kernel(route_kernel, dim3(1), dim3(1024), 0, s, nullptr, ids, M * k, k, E, moe_max_slots(M, k, E),
+                cnt, poff, perm, inv, items, n_items, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
@@ -488,8 +488,8 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
     raised = true;
   }
   const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
-  hipLaunchKernelGGL(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, h_rm, perm, w_gate_up,
-                     cnt, poff, items, n_items, F, d, a);
+  launch_kernel(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, nullptr, h_rm, perm, w_gate_up,
+                cnt, poff, items, n_items, F, d, a);
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T over K = F.  Workgroup tile: 128 output
@@ -616,8 +616,8 @@ void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* c
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
                      int F, int d, float* Y, hipStream_t s) {
   const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * ((d + kDownRows - 1) / kDownRows);
-  hipLaunchKernelGGL(moe_down_kernel, dim3(blocks), dim3(256), kDnLds, s, a, w_down, cnt, poff, items,
-                     n_items, F, d, Y);
+  launch_kernel(moe_down_kernel, dim3(blocks), dim3(256), kDnLds, s, nullptr, a, w_down, cnt, poff, items,
+                n_items, F, d, Y);
 }
 
 }  // namespace dg

@@ -49,7 +49,7 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int
   const int Rpad = (R + 15) / 16 * 16;
   const size_t total = (size_t)nmat * Rpad * (K / 8);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, src, dst, nmat, R, K, Rpad, kind, param);
+  launch_kernel(pack_kernel, dim3(blocks), dim3(256), 0, s, nullptr, src, dst, nmat, R, K, Rpad, kind, param);
 }
 
 // Row-major bf16 activations -> fragment-major (test tap support).

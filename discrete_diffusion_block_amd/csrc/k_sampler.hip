@@ -151,8 +151,8 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
 void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
                             float4* part, int* part_arg, hipStream_t s) {
   const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
-  hipLaunchKernelGGL(sample_partials_kernel, dim3(nchunks, rows), dim3(256), 0, s, logits, canvas,
-                     vocab, nchunks, part, part_arg);
+  launch_kernel(sample_partials_kernel, dim3(nchunks, rows), dim3(256), 0, s, nullptr, logits, canvas,
+                vocab, nchunks, part, part_arg);
 }
 
 template <int TPR>   // threads per canvas row in the chunk merge
@@ -293,11 +293,11 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       int32_t* n_masked, hipStream_t s) {
   const int rows64 = ((C + 63) / 64) * 64;
   if (4 * rows64 <= 1024)
-    hipLaunchKernelGGL(eb_select_kernel<4>, dim3(batch), dim3(4 * rows64), 0, s, part, part_arg, nchunks,
-                       H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+    launch_kernel(eb_select_kernel<4>, dim3(batch), dim3(4 * rows64), 0, s, nullptr, part, part_arg, nchunks,
+                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
   else
-    hipLaunchKernelGGL(eb_select_kernel<1>, dim3(batch), dim3(rows64), 0, s, part, part_arg, nchunks,
-                       H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+    launch_kernel(eb_select_kernel<1>, dim3(batch), dim3(rows64), 0, s, nullptr, part, part_arg, nchunks,
+                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
 }
 
 }  // namespace dg
