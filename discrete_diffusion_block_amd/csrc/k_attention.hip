@@ -205,10 +205,9 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
   // 8 waves split the key range (4 for hd 32, where the merge runs out of columns)
   switch (kv.hd) {
     case 32: launch_kernel(attention_kernel<32, 4>, grid, dim3(256), 0, s, nullptr, q, hq, kv, g, o); break;
-                           case 64: launch_kernel(attention_kernel<64, 8>, grid, dim3(512), 0, s, nullptr, q, hq, kv, g, o); break;
+    case 64: launch_kernel(attention_kernel<64, 8>, grid, dim3(512), 0, s, nullptr, q, hq, kv, g, o); break;
     default: launch_kernel(attention_kernel<128, 8>, grid, dim3(512), 0, s, nullptr, q, hq, kv, g, o); break;
-                           }
-                           }
-                           
-                           }  // namespace dg
-                           
+  }
+}
+
+}  // namespace dg
