@@ -337,7 +337,7 @@ constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 // and the second half starts 1152 bytes after the first: the MFMA operand reads
 // (16 rows, one piece column each) then hit 16 distinct bank groups.
 constexpr int kGuRB = 8, kGuTB = 4, kGuKT = 2;
-constexpr int kGuWSlots = 3, kGuXSlots = 2;
+constexpr int kGuWSlots = 3, kGuXSlots = 3;
 constexpr int kGuXHalf = 1024 + 128;           // bytes from one 8-row half to the next
 constexpr int kGuXBlock = 2 * kGuXHalf;        // one token block of a k step
 constexpr int kGuWBytes = kGuRB * kGuKT * 1024, kGuXBytes = kGuTB * kGuXBlock;
@@ -392,12 +392,15 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   lds_char* const lw = lds_launder(wring);
   lds_char* const lx = lds_launder(xring);
   // After step j's barrier the wave copies X(j + XS - 1) then W(j + WS - 1); the
-  // prologue runs the same order for j = -(WS - 1) .. -1.  At the top of step s,
-  // X(s) and everything issued before it (W(s) included) have landed once at most
-  // the copies issued after X(s) are in flight.
+  // prologue runs the same order for j = -(WS - 1) .. -1.  At the top of step s
+  // the copies issued after X(s) are W(s + WS - XS) and, for each of the XS - 2
+  // steps since, one X and one W step.  When WS > XS, W(s) was issued before X(s)
+  // and waiting until only those later copies are in flight covers both; when
+  // WS == XS, W(s) is the one right after X(s) and must land too.
   constexpr int WS = kGuWSlots, XS = kGuXSlots;
-  static_assert(WS > XS && XS >= 2, "weights run further ahead than token tiles");
-  constexpr int kAfterX = kGuCopies + (XS - 2) * 2 * kGuCopies;
+  static_assert(WS >= XS && XS >= 2, "weights run at least as far ahead as token rows");
+  constexpr int kXCopies = 2, kStepCopies = kXCopies + kGuCopies;
+  constexpr int kAfterX = (WS > XS ? kGuCopies : 0) + (XS - 2) * kStepCopies;
   static_assert(kAfterX < 64, "vmcnt range");
 #pragma unroll
   for (int j = -(WS - 1); j < 0; ++j) {
@@ -413,7 +416,7 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   }
   u32x4 Af[WI][kGuKT], Bf[WJ][kGuKT];
   for (int s = 0; s < nk; ++s) {
-    if (s + WS - 2 < nk) vm_wait<kAfterX>();
+    if (s + WS - 2 < nk) vm_wait<kAfterX>();   // every copy counted above exists
     else vm_wait<0>();
     __builtin_amdgcn_s_barrier();
     if (s + XS - 1 < nk) issue_x(s + XS - 1);
