@@ -212,6 +212,19 @@ def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prom
     for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{k[:58]:58s} {len(v):6d} {sum(v) / 1e3:9.2f} {sum(v) / len(v):8.2f} "
                      f"{min(v):8.2f} {max(v):8.2f} {100 * sum(v) / total:5.1f}%")
+    # the run's last denoise_steps denoising passes are the ones in which bench.py times
+    # the dominant kind with HIP events (the roofline figure of its JSON line)
+    roof = [p for p in passes if any("head_gemm" in r["Kernel_Name"] for r in p)][-denoise_steps:]
+    ragg = collections.defaultdict(list)
+    for p in roof:
+        for r in p:
+            name = r["Kernel_Name"].replace("void ", "").split("(")[0]
+            ragg[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines.append("")
+    lines.append(f"roofline passes (the run's last {len(roof)} denoising passes, in which bench.py times "
+                 f"the dominant kind with HIP events on its launches):")
+    for k, v in sorted(ragg.items(), key=lambda kv: -sum(kv[1]))[:6]:
+        lines.append(f"{k[:58]:58s} {len(v):6d} launches, avg {sum(v) / len(v):8.2f} us")
     return "\n".join(lines)
 
 

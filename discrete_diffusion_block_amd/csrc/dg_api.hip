@@ -63,16 +63,20 @@ struct Timed {
   int kind;
   hipStream_t s;
   bool on;
-  // The events ride on the launch itself (next_launch_events): they time the kernel
-  // from its start to its completion without adding packets to the stream.
+  // The start event is a marker ahead of the launch (it fires once the stream's
+  // previous work is done, i.e. as the kernel can begin); the stop event rides on the
+  // launch itself (next_launch_events) and fires at the kernel's completion.
   Timed(const dg_ctx* c_, int k, hipStream_t s_) : c(c_), kind(k), s(s_) {
     on = c && c->prof.on && (c->prof.mask >> k & 1u) && c->prof.used < c->prof.kind.size();
-    if (on) next_launch_events() = LaunchEvents{c->prof.ev[2 * c->prof.used], c->prof.ev[2 * c->prof.used + 1]};
+    if (on) {
+      (void)hipEventRecord(c->prof.ev[2 * c->prof.used], s);
+      next_launch_events() = LaunchEvents{c->prof.ev[2 * c->prof.used + 1]};
+    }
   }
   ~Timed() {
     if (on) {
-      // a statement that launched nothing leaves its events unused: not counted
-      const bool used = next_launch_events().start == nullptr;
+      // a statement that launched nothing leaves its stop event unused: not counted
+      const bool used = next_launch_events().stop == nullptr;
       next_launch_events() = LaunchEvents{};
       c->prof.kind[c->prof.used++] = used ? kind : -1;
     }

@@ -27,12 +27,12 @@ struct KvLayer {
 };
 
 // Every kernel launch goes through launch_kernel.  The engine's profiler may park a
-// pair of timing events in next_launch_events(); the next launch then attaches them
-// to its own dispatch (signalled as the kernel starts and when it completes, so no
-// marker packets change the schedule being measured) and clears them.  `done`
-// (optional) is signalled by the kernel's completion, for another stream to wait on.
+// timing event in next_launch_events(); the next launch then has it signalled by
+// its own completion (no marker packet after the kernel) and clears it.  `done`
+// (optional) is likewise signalled by the kernel's completion, for another stream
+// to wait on.
 struct LaunchEvents {
-  hipEvent_t start = nullptr, stop = nullptr;
+  hipEvent_t stop = nullptr;
 };
 inline LaunchEvents& next_launch_events() {
   static thread_local LaunchEvents e;
@@ -43,16 +43,13 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_
                           hipEvent_t done, Args... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
   LaunchEvents& ev = next_launch_events();
-  if (ev.start) {
-    const LaunchEvents t = ev;
+  hipEvent_t stop = done;
+  if (ev.stop) {
+    stop = ev.stop;
     ev = LaunchEvents{};
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, t.start, t.stop, 0u, static_cast<KArgs>(args)...);
-    if (done) (void)hipEventRecord(done, s);
-  } else if (done) {
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, nullptr, done, 0u, static_cast<KArgs>(args)...);
-  } else {
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, nullptr, nullptr, 0u, static_cast<KArgs>(args)...);
   }
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, nullptr, stop, 0u, static_cast<KArgs>(args)...);
+  if (done && stop != done) (void)hipEventRecord(done, s);
 }
 
 // ---- embed / norm / prep ----

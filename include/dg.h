@@ -194,10 +194,10 @@ typedef enum dg_kernel_kind {
 
 /* Start timing the kernel launches made through ctx (dg_prefill_kv,
  * dg_denoise_step, dg_generate_block), up to `capacity` launches (events are
- * created here).  Each timed launch carries a pair of hipEvents on its own
- * dispatch, signalled as the kernel starts and when it completes, so the
- * measured schedule has no extra packets.  kind_mask selects the kinds timed
- * (bit DG_K_x); 0 times every kind.  Not thread-safe. */
+ * created here).  Each timed launch gets a start event recorded on its stream
+ * just ahead of it (it fires as the stream's previous work completes) and a stop
+ * event signalled by the kernel's own completion.  kind_mask selects the kinds
+ * timed (bit DG_K_x); 0 times every kind.  Not thread-safe. */
 dg_status dg_profile_begin(dg_ctx* ctx, int capacity, uint32_t kind_mask);
 /* Stop, wait for the recorded events, and return per kind the summed kernel
  * milliseconds and launch counts (arrays of DG_K_COUNT entries). */
