@@ -118,6 +118,7 @@ hipStream_t side_stream(const dg_ctx* ctx) {
 }
 
 constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
+constexpr int kPassCounters = 16;    // device counters cleared at the start of every pass
 constexpr size_t kAlign = 256;
 
 struct Ws {
@@ -138,6 +139,8 @@ struct Ws {
   int2* items;
   int32_t* n_items;
   int32_t* cnt_log;
+  int32_t* rows;   // logits row of each compacted [MASK] row (head restricted to masked rows)
+  int32_t* counters;   // [0]: compacted [MASK] rows; cleared at the start of every pass
   uint16_t* A;     // expert SwiGLU outputs, fragment-major [P_pad][F]
   float* Y;        // expert outputs fp32 [P][d]
   uint16_t* As;    // shared-expert SwiGLU output, fragment-major [M_pad][Fs]
@@ -193,6 +196,8 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
   ws->n_items = cv.take<int32_t>(1);
   ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
+  ws->rows = cv.take<int32_t>(M);
+  ws->counters = cv.take<int32_t>(kPassCounters);
   ws->A = cv.take<uint16_t>(round16(P) * c.expert_ffn);
   ws->Y = cv.take<float>(P * c.d_model);
   ws->As = cv.take<uint16_t>(Mp * c.shared_ffn);
@@ -245,14 +250,18 @@ KvLayer kv_layer(const dg_ctx* ctx, const dg_kv* kv, int l) {
 }
 
 // One transformer pass over batch x n tokens (denoise: + final norm + tied head).
+// masked_head (denoise passes): the head computes only the rows whose canvas token is
+// [MASK] -- the only rows the sampler reads -- and leaves the other logits rows as
+// they were.
 dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const int32_t* tokens,
-                   float t, uint16_t* logits, const Ws& ws, hipStream_t s) {
+                   float t, uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false) {
   const dg_config& c = ctx->cfg;
   const int M = g.batch * g.n;
   const int d = c.d_model, hq = c.n_q_heads, hd = c.head_dim, E = c.n_experts, k = c.top_k;
   const float eps = c.rms_eps;
   const int nl = c.n_layers;
-  DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr, s));
+  DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr,
+                                       ws.counters, kPassCounters, s));
   DG_TIMED(ctx, DG_K_EMBED,
            launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, ctx->layers[0].attn_norm,
                              eps, ws.x, ws.h, M, d, c.vocab, s));
@@ -295,10 +304,15 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
                              c.expert_ffn, d, ws.Y, s));
     if (fork) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
+    const bool compact = masked_head && g.denoise && l == nl - 1;
     DG_TIMED(ctx, DG_K_COMBINE,
-             launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h, s));
+             launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h,
+                            compact ? tokens : nullptr, c.vocab, compact ? ws.rows : nullptr, ws.counters, s));
   }
-  if (g.denoise) DG_TIMED(ctx, DG_K_HEAD, launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d, s));
+  const bool compact = masked_head && g.denoise;
+  if (g.denoise)
+    DG_TIMED(ctx, DG_K_HEAD, launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d,
+                                              compact ? ws.counters : nullptr, compact ? ws.rows : nullptr, s));
   return check_launch("transformer pass");
 }
 
@@ -320,7 +334,7 @@ dg_status get_ws(const dg_ctx* ctx, int batch, void* d_ws, size_t ws_bytes, Ws* 
 }
 
 dg_status denoise_impl(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, int batch, float t,
-                       uint16_t* d_logits, const Ws& ws, hipStream_t s) {
+                       uint16_t* d_logits, const Ws& ws, hipStream_t s, bool masked_head = false) {
   PassGeom g{};
   g.batch = batch;
   g.n = ctx->cfg.canvas;
@@ -331,7 +345,7 @@ dg_status denoise_impl(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, in
                   (long long)kv->len[b], ctx->cfg.canvas, ctx->cfg.max_ctx);
     g.len[b] = (int)kv->len[b];
   }
-  return run_pass(ctx, kv, g, d_canvas, t, d_logits, ws, s);
+  return run_pass(ctx, kv, g, d_canvas, t, d_logits, ws, s, masked_head);
 }
 
 dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batch, int n,
@@ -529,7 +543,7 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
   DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
   for (int step = 0; step < steps; ++step) {
     const float t = 1.0f - (float)step / (float)steps;
-    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s);
+    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/true);
     if (st != DG_OK) return st;
     st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == steps - 1, nullptr,
                      nullptr, d_n_masked, ws, s, ctx);

@@ -53,16 +53,21 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_
 }
 
 // ---- embed / norm / prep ----
+// also clears zero[0 .. nzero)
 void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
-                 float* temb, hipStream_t s);
+                 float* temb, int32_t* zero, int nzero, hipStream_t s);
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s);
 // h: fragment-major; h_rm (optional): the same values row-major [M][d]
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, uint16_t* h_rm, int M,
                     int d, hipStream_t s, hipEvent_t done = nullptr);
+// rows_out given: only the [MASK] rows of canvas (mask id mask_id) are normed,
+// compacted into h (the order of arrival); rows_out lists their row indices and
+// *count (zero on entry) their number
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
-                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s);
+                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
+                    const int32_t* canvas, int mask_id, int32_t* rows_out, int32_t* count, hipStream_t s);
 
 // ---- dense GEMMs ----
 // y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).
@@ -77,8 +82,9 @@ void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int
 void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,
                         uint16_t* a, hipStream_t s);
 // tied LM head: logits bf16 [M][N] = h . E[0:N]^T
+// count given: h holds *count rows compacted, rows[i] the logits row of row i
 void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
-                      int K, hipStream_t s);
+                      int K, const int32_t* count, const int32_t* rows, hipStream_t s);
 
 // ---- attention ----
 void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,

@@ -12,8 +12,11 @@ namespace dg {
 // rope_tab[m][i] = (cos, sin)(pos(m) * theta^(-2i/hd)), computed in fp64 so that
 // positions in the tens of thousands keep full fp32 accuracy.
 // temb[j] = sin(1000 t f_j) (j < d/2), cos(1000 t f_{j-d/2}) (j >= d/2), f_j = 10000^(-j/(d/2)).
+// Workgroup 0 also clears the pass's counters zero[0 .. nzero).
 __global__ void prep_kernel(PassGeom g, int hd, float theta, float2* rope_tab, int d, float t,
-                            float* temb) {
+                            float* temb, int32_t* zero, int nzero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   const int half = hd / 2;
   const int M = g.batch * g.n;
   const long total = (long)M * half + (temb ? d : 0);
@@ -36,10 +39,11 @@ __global__ void prep_kernel(PassGeom g, int hd, float theta, float2* rope_tab, i
 }
 
 void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
-                 float* temb, hipStream_t s) {
+                 float* temb, int32_t* zero, int nzero, hipStream_t s) {
   const long total = (long)g.batch * g.n * (hd / 2) + (temb ? d : 0);
   const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
-  launch_kernel(prep_kernel, dim3(blocks), dim3(256), 0, s, nullptr, g, hd, theta, rope_tab, d, t, temb);
+  launch_kernel(prep_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, nullptr, g, hd, theta, rope_tab, d, t,
+                temb, zero, nzero);
 }
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
@@ -135,13 +139,20 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
 }
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]
-// (j ascending), then h[m] = norm(x[m]) * next_gain.
+// (j ascending), then h[m] = norm(x[m]) * next_gain.  With rows_out given (the
+// last layer of a pass whose head only needs the [MASK] rows of canvas), only
+// those rows are normed, each into the next free h row i taken from *count
+// (zero on entry; it ends as the number of [MASK] rows), with rows_out[i] = m.
+// The order of the compacted rows varies from run to run; every logits row the
+// head computes from them does not depend on it.
 __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys, const float* Y,
                                                       const float* wts,
                                                       const int32_t* inv, int k, int d,
                                                       const float* next_gain, float eps,
-                                                      uint16_t* h) {
+                                                      uint16_t* h, const int32_t* canvas, int mask_id,
+                                                      int32_t* rows_out, int32_t* count) {
   __shared__ float red[16];
+  __shared__ int out_row;
   __shared__ int slot[16];
   __shared__ float wt[16];
   const int m = blockIdx.x;
@@ -168,12 +179,26 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys,
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     store8(xr + c, v);
   }
-  if (next_gain) norm_row(xr, next_gain, eps, h, m, d, ss, red);
+  if (!next_gain) return;
+  if (rows_out) {
+    if (canvas[m] != mask_id) return;   // uniform per workgroup
+    if (threadIdx.x == 0) {
+      const int i = atomicAdd(count, 1);
+      rows_out[i] = m;
+      out_row = i;
+    }
+    __syncthreads();
+    norm_row(xr, next_gain, eps, h, out_row, d, ss, red);
+  } else {
+    norm_row(xr, next_gain, eps, h, m, d, ss, red);
+  }
 }
 
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
-                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h, hipStream_t s) {
-  launch_kernel(combine_kernel, dim3(M), dim3(256), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h);
+                    int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
+                    const int32_t* canvas, int mask_id, int32_t* rows_out, int32_t* count, hipStream_t s) {
+  launch_kernel(combine_kernel, dim3(M), dim3(256), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h,
+                canvas, mask_id, rows_out, count);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {

@@ -16,6 +16,8 @@
 // head_gemm: the tied LM head (N = 262144 rows of the embedding) -- 256 x 256
 // workgroup tiles with both operands staged through an LDS ring by direct
 // global->LDS copies.
+#include <type_traits>
+
 #include "dg_common.h"
 #include "dg_internal.h"
 
@@ -235,13 +237,18 @@ void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int
 // ---------------------------------------------------------------- LM head
 
 // Tied LM head, logits[m][v] = h[m] . E[v] in bf16.  Workgroup tile: 256
-// vocabulary rows x 256 tokens; the 4 waves form a 2 x 2 grid of 128 x 128
-// sub-tiles (8 x 8 MFMA blocks each, accumulators in AGPRs).  Operands are staged
-// through LDS by direct global->LDS copies in 64-wide k steps (two 1 KiB fragment
-// tiles per 16-row block).  The weight stream comes from HBM, so its ring is three
-// steps deep (copies go out two steps ahead); the token tiles are L2 hits and
-// ride a two-step ring one step ahead.  Weights are read from HBM exactly once and
-// every token tile once per workgroup.  Each accumulator takes its two k tiles
+// vocabulary rows x up to 256 tokens.  A full tile splits over the 4 waves as a
+// 2 x 2 grid of 128 x 128 sub-tiles (8 x 8 MFMA blocks each, accumulators in
+// AGPRs); a tile with fewer token rows to produce gives wave w vocabulary rows
+// 64w .. 64w + 63 against its active token blocks (4 x 4, 8 or 12 MFMA blocks), so
+// the MFMA work shrinks with the rows.  When the pass only needs the [MASK] rows
+// (count given), h holds those *count rows compacted, and rows[] maps each
+// compacted row to its logits row.  Operands are staged through LDS by direct
+// global->LDS copies in 64-wide k steps (two 1 KiB fragment tiles per 16-row
+// block).  The weight stream comes from HBM, so its ring
+// is three steps deep (copies go out two steps ahead); the token tiles are L2 hits
+// and ride a two-step ring one step ahead.  Weights are read from HBM exactly once
+// and every token tile once per workgroup.  Each accumulator takes its two k tiles
 // back to back (a dependent MFMA pair issues at the full rate).
 constexpr int kHeadRB = 16;       // 16-row weight blocks per workgroup
 constexpr int kHeadTB = 16;       // 16-token blocks per workgroup
@@ -256,17 +263,22 @@ constexpr int kHeadXCopies = kHeadTB * kHeadKT / 4;
 __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
                                                  const uint16_t* __restrict__ w,
                                                  uint16_t* __restrict__ y, int M, int N, int K,
-                                                 int w_blocks, int n_row_tiles, int n_tok_tiles) {
+                                                 int w_blocks, int n_row_tiles, int n_tok_tiles,
+                                                 const int32_t* __restrict__ count,
+                                                 const int32_t* __restrict__ rows) {
   extern __shared__ __attribute__((aligned(1024))) char ring[];   // [W slots][X slots]
-  constexpr int WI = kHeadRB / 2, WJ = kHeadTB / 2;   // MFMA blocks per wave
+  constexpr int WI = kHeadRB / 4, WJ = kHeadTB;   // MFMA blocks per wave (rows x tokens)
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int b = blockIdx.x, xcd = b % kXcd, rank = b / kXcd;
   const int row_tile = (rank / n_tok_tiles) * kXcd + xcd, tok_tile = rank % n_tok_tiles;
   if (row_tile >= n_row_tiles) return;
+  // rows to produce: all M, or the *count [MASK] rows compacted in h
+  const int Mc = count ? __builtin_amdgcn_readfirstlane(*count) : M;
   const int rb0 = row_tile * kHeadRB, tb0 = tok_tile * kHeadTB;
-  const int t_blocks = (M + 15) >> 4;
+  if (tb0 * 16 >= Mc) return;                        // uniform per workgroup
+  const int nb = min(kHeadTB, (Mc - tb0 * 16 + 15) >> 4);   // active token blocks of the tile
   const int nk = K / (32 * kHeadKT);
 
   // copy duty: wave wv copies weight blocks and token blocks wv * (RB / 4) + u;
@@ -276,8 +288,9 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
   const uint16_t* xsrc[XB];
 #pragma unroll
   for (int u = 0; u < WB; ++u) wsrc[u] = w + fm_tile(min(rb0 + wv * WB + u, w_blocks - 1), 0, K, lane);
+  // token blocks past the active ones re-read the last active block (their rows are never used)
 #pragma unroll
-  for (int u = 0; u < XB; ++u) xsrc[u] = x + fm_tile(min(tb0 + wv * XB + u, t_blocks - 1), 0, K, lane);
+  for (int u = 0; u < XB; ++u) xsrc[u] = x + fm_tile(tb0 + min(wv * XB + u, nb - 1), 0, K, lane);
   char* const wring = ring;
   char* const xring = ring + kHeadWSlots * kHeadWBytes;
   auto issue_w = [&](int step) {
@@ -297,70 +310,147 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
         tile_to_lds<false>(xsrc[u] + (step * kHeadKT + t) * 512, dst + (u * kHeadKT + t) * 1024);
   };
 
-  const int wr = wv & 1, wt = wv >> 1;
-  f32x4 acc[WI][WJ];
-#pragma unroll
-  for (int i = 0; i < WI; ++i)
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   lds_char* const lw = lds_launder(wring);
   lds_char* const lx = lds_launder(xring);
-
-  // Copy order: W(0), X(0), W(1), then after step s's barrier X(s + 1), W(s + 2).
-  // At the top of step s the wave's copies of X(s) and W(s) have landed once at
-  // most the W(s + 1) batch that follows X(s) is in flight; the barrier then makes
-  // all waves' copies visible and retires every read of the slots refilled next
-  // (they held step s - 1).
-  issue_w(0);
-  issue_x(0);
-  if (nk > 1) issue_w(1);
-  u32x4 A[WI][kHeadKT], B[2][kHeadKT];
-  static_assert(kHeadKT == 2, "MFMA pairs");
-  for (int s = 0; s < nk; ++s) {
-    if (s + 1 < nk) vm_wait<kHeadWCopies>();
-    else vm_wait<0>();
-    __builtin_amdgcn_s_barrier();
-    if (s + 1 < nk) issue_x(s + 1);
-    if (s + 2 < nk) issue_w(s + 2);
-    const lds_char* sw = lw + (s % kHeadWSlots) * kHeadWBytes + lane * 16;
-    const lds_char* sx = lx + (s % kHeadXSlots) * kHeadXBytes + lane * 16;
+  // the tile's token-block count, rounded up to a multiple of 4, is a compile-time
+  // loop bound: blocks past nb repeat the last active block and are dropped
+  auto run = [&](auto nbt) {
+    constexpr int NB = decltype(nbt)::value;
+    int orow[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int mc = (tb0 + j) * 16 + r;
+      orow[j] = (j < nb && mc < Mc) ? (rows ? rows[mc] : mc) : -1;
+    }
+    f32x4 acc[WI][NB];
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int t = 0; t < kHeadKT; ++t) A[i][t] = ld16_lds(sw + ((wr * WI + i) * kHeadKT + t) * 1024);
-    auto readB = [&](int j) {
-#pragma unroll
-      for (int t = 0; t < kHeadKT; ++t) B[j & 1][t] = ld16_lds(sx + ((wt * WJ + j) * kHeadKT + t) * 1024);
-    };
-    readB(0);
-#pragma unroll
-    for (int j = 0; j < WJ; ++j) {
-      if (j + 1 < WJ) readB(j + 1);   // one token column ahead
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Copy order: W(0), X(0), W(1), then after step s's barrier X(s + 1), W(s + 2).
+    // At the top of step s the wave's copies of X(s) and W(s) have landed once at
+    // most the W(s + 1) batch that follows X(s) is in flight; the barrier then makes
+    // all waves' copies visible and retires every read of the slots refilled next
+    // (they held step s - 1).
+    issue_w(0);
+    issue_x(0);
+    if (nk > 1) issue_w(1);
+    u32x4 A[WI][kHeadKT], B[2][kHeadKT];
+    static_assert(kHeadKT == 2, "MFMA pairs");
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) vm_wait<kHeadWCopies>();
+      else vm_wait<0>();
+      __builtin_amdgcn_s_barrier();
+      if (s + 1 < nk) issue_x(s + 1);
+      if (s + 2 < nk) issue_w(s + 2);
+      const lds_char* sw = lw + (s % kHeadWSlots) * kHeadWBytes + lane * 16;
+      const lds_char* sx = lx + (s % kHeadXSlots) * kHeadXBytes + lane * 16;
 #pragma unroll
       for (int i = 0; i < WI; ++i)
-        acc[i][j] = mfma16x2(A[i][0], B[j & 1][0], A[i][1], B[j & 1][1], acc[i][j]);
+#pragma unroll
+        for (int t = 0; t < kHeadKT; ++t) A[i][t] = ld16_lds(sw + ((wv * WI + i) * kHeadKT + t) * 1024);
+      auto readB = [&](int j) {
+#pragma unroll
+        for (int t = 0; t < kHeadKT; ++t) B[j & 1][t] = ld16_lds(sx + (j * kHeadKT + t) * 1024);
+      };
+      readB(0);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j + 1 < NB) readB(j + 1);   // one token column ahead
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+          acc[i][j] = mfma16x2(A[i][0], B[j & 1][0], A[i][1], B[j & 1][1], acc[i][j]);
+      }
     }
-  }
 
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const int m = (tb0 + wt * WJ + j) * 16 + r;
-    if (m >= M) continue;
+    for (int j = 0; j < NB; ++j) {
+      if (orow[j] < 0) continue;
+      const size_t m = (size_t)orow[j];
 #pragma unroll
-    for (int i = 0; i < WI; ++i) {
-      const int n0 = (rb0 + wr * WI + i) * 16 + 4 * g;
-      if (n0 >= N) continue;   // N is a multiple of 8, so n0 < N covers n0 .. n0 + 3
-      u32x2 o;
-      o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
-      o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<u32x2*>(y + (size_t)m * N + n0) = o;
+      for (int i = 0; i < WI; ++i) {
+        const int n0 = (rb0 + wv * WI + i) * 16 + 4 * g;
+        if (n0 >= N) continue;   // N is a multiple of 8, so n0 < N covers n0 .. n0 + 3
+        u32x2 o;
+        o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+        o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(y + m * N + n0) = o;
+      }
     }
-  }
+  };
+  // A full tile (16 token blocks) takes the 2 x 2 grid of 128 x 128 wave tiles
+  // instead: each fragment read from LDS then feeds 8 MFMA blocks, not 4 or 16.
+  auto run_full = [&]() {
+    constexpr int FI = kHeadRB / 2, FJ = kHeadTB / 2;
+    const int wr = wv & 1, wt = wv >> 1;
+    // logits rows of this lane's tokens, loaded before the k loop hides their latency
+    int orow[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int mc = (tb0 + wt * FJ + j) * 16 + r;
+      orow[j] = mc < Mc ? (rows ? rows[mc] : mc) : -1;
+    }
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue_w(0);
+    issue_x(0);
+    if (nk > 1) issue_w(1);
+    u32x4 A[FI][kHeadKT], B[2][kHeadKT];
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) vm_wait<kHeadWCopies>();
+      else vm_wait<0>();
+      __builtin_amdgcn_s_barrier();
+      if (s + 1 < nk) issue_x(s + 1);
+      if (s + 2 < nk) issue_w(s + 2);
+      const lds_char* sw = lw + (s % kHeadWSlots) * kHeadWBytes + lane * 16;
+      const lds_char* sx = lx + (s % kHeadXSlots) * kHeadXBytes + lane * 16;
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int t = 0; t < kHeadKT; ++t) A[i][t] = ld16_lds(sw + ((wr * FI + i) * kHeadKT + t) * 1024);
+      auto readB = [&](int j) {
+#pragma unroll
+        for (int t = 0; t < kHeadKT; ++t) B[j & 1][t] = ld16_lds(sx + ((wt * FJ + j) * kHeadKT + t) * 1024);
+      };
+      readB(0);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        if (j + 1 < FJ) readB(j + 1);   // one token column ahead
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = mfma16x2(A[i][0], B[j & 1][0], A[i][1], B[j & 1][1], acc[i][j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      if (orow[j] < 0) continue;
+      const size_t m = (size_t)orow[j];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int n0 = (rb0 + wr * FI + i) * 16 + 4 * g;
+        if (n0 >= N) continue;
+        u32x2 o;
+        o.x = pack_bf2(acc[i][j][0], acc[i][j][1]);
+        o.y = pack_bf2(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2*>(y + m * N + n0) = o;
+      }
+    }
+  };
+  static_assert(WJ == 16, "token-block classes");
+  if (nb <= 4) run(std::integral_constant<int, 4>{});
+  else if (nb <= 8) run(std::integral_constant<int, 8>{});
+  else if (nb <= 12) run(std::integral_constant<int, 12>{});
+  else run_full();
 }
 
 void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
-                      int K, hipStream_t s) {
+                      int K, const int32_t* count, const int32_t* rows, hipStream_t s) {
   constexpr size_t lds = (size_t)kHeadLds;
   static bool raised = false;   // the ring exceeds the default dynamic-LDS limit
   if (!raised) {
@@ -373,7 +463,7 @@ void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits
   const int n_tok = (M + 16 * kHeadTB - 1) / (16 * kHeadTB);
   const int blocks = kXcd * ((n_row + kXcd - 1) / kXcd) * n_tok;
   launch_kernel(head_gemm, dim3(blocks), dim3(256), lds, s, nullptr, h, embed, logits, M, N, K, w_blocks,
-                n_row, n_tok);
+                n_row, n_tok, count, rows);
 }
 
 }  // namespace dg

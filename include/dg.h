@@ -173,11 +173,15 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
                        void* stream);
 
 /* Generate one block per sequence (Technical Report §3.1–§3.3): fill d_canvas
- * (int32 [batch][C]) with [MASK]; for s = 0..steps-1 run dg_denoise_step at
+ * (int32 [batch][C]) with [MASK]; for s = 0..steps-1 run the denoising pass at
  * t_s = 1 - s/steps and dg_sample_eb (commit_all on the last step); then, if
  * append_kv, run the causal append pass over the finished canvas (len += C).
- * d_logits: bf16 [batch][C][V] scratch owned by the caller.  d_n_masked:
- * int32 [batch], holds the masked count after the last step (0). */
+ * The denoising passes here compute the head only for the rows that are still
+ * [MASK] (the only rows the sampler reads; committed tokens are never revised),
+ * so the head's work shrinks as the block fills in.
+ * d_logits: bf16 [batch][C][V] scratch owned by the caller; row c holds the
+ * logits of the last step in which position c was [MASK].  d_n_masked: int32
+ * [batch], holds the masked count after the last step (0). */
 dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps,
                             float gamma, int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
                             void* d_ws, size_t ws_bytes, void* stream);

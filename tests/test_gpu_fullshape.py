@@ -160,3 +160,43 @@ def test_fullshape_batch_two_ragged(full):
         near = _near_rows(tr[b], cfg.top_k)
         assert len(near) <= 0.75 * C, len(near)
         _logit_check(lg[b], ref[b], [i for i in range(C) if i not in near])
+
+
+def test_fullshape_generate_block_masked_head(full):
+    """dg_generate_block computes the head only for the rows still [MASK]; with gamma set
+    to commit ~100 rows per step the head sees 256, ~156 and ~56 rows (16, 10 and 4 token
+    blocks of its tile).  Its canvas must equal the same steps driven through
+    dg_denoise_step (whole head) and dg_sample_eb, bit for bit, for two sequences."""
+    cfg, w_np, w_gpu, prompt, kv, trace, eng = full
+    V, C = cfg.vocab, cfg.canvas
+    steps, gamma = 3, 100 * float(np.log(V))
+    p2 = synth.make_prompt(cfg, 1, 600, seed=17)
+    print("full-shape generate_block with the masked-row head (2 sequences)", flush=True)
+    logits = torch.empty(2, C, V, dtype=torch.bfloat16, device="cuda")
+    nm = torch.empty(2, dtype=torch.int32, device="cuda")
+
+    def fresh():
+        eng.reset()
+        eng.prefill_kv(torch.cat([prompt[:, :600], p2]).contiguous().cuda())
+        eng.kv.len[1] = 600
+
+    fresh()
+    blk = torch.empty(2, C, dtype=torch.int32, device="cuda")
+    eng.generate_block(blk, steps, gamma, False, logits, nm)
+    torch.cuda.synchronize()
+    assert nm.tolist() == [0, 0]
+
+    fresh()
+    canvas = torch.full((2, C), cfg.mask_id, dtype=torch.int32, device="cuda")
+    left = []
+    for s in range(steps):
+        # t exactly as dg_generate_block forms it, in fp32 (the EB ranking of the
+        # near-uniform random-init rows turns a 1-ulp change of t into other commits)
+        t = float(np.float32(1.0) - np.float32(s) / np.float32(steps))
+        eng.denoise_step(canvas, t, logits)
+        eng.sample_eb(logits, canvas, gamma, s == steps - 1, nm)
+        torch.cuda.synchronize()
+        left.append(nm.tolist())
+    print(f"  masked rows left after each step: {left}", flush=True)
+    assert 100 <= C - left[0][0] <= 110 and left[1][0] < left[0][0]   # the head saw shrinking row sets
+    assert torch.equal(blk, canvas)

@@ -50,7 +50,8 @@ def test_copy_tap_bit_exact(n_bytes):
     assert int(dst[n_bytes:].count_nonzero()) == 0            # nothing written past the end
 
 
-@pytest.mark.parametrize("M,E,k", [(300, 128, 8), (64, 8, 2), (5, 256, 16), (33, 4, 4)])
+@pytest.mark.parametrize("M,E,k", [(300, 128, 8), (64, 8, 2), (5, 256, 16), (33, 4, 4), (70, 100, 5),
+                                   (40, 48, 6), (17, 32, 16)])
 def test_router_topk_bit_exact(M, E, k):
     print(f"topk M={M} E={E} k={k}", flush=True)
     g = torch.Generator().manual_seed(M * 7 + E)
@@ -219,7 +220,7 @@ def test_sampler_ragged_vocab_and_cross_chunk_ties():
 
 
 @pytest.mark.parametrize("M,E,k", [(256, 128, 8), (512, 128, 8), (33, 8, 2), (1000, 16, 3), (7, 4, 4),
-                                   (4096, 256, 16)])
+                                   (4096, 256, 16), (300, 100, 5), (257, 128, 16)])
 def test_routing_sort_bit_exact(M, E, k):
     """Top-k ids bit-exact vs the oracle; the counting sort is a stable, padded grouping."""
     print(f"route M={M} E={E} k={k}", flush=True)
