@@ -226,3 +226,34 @@ def test_batch_two_sequences_with_different_lengths(tiny):
     err = np.abs(to_np_bf16(logits) - ref).max()
     assert err <= LOGIT_TOL, err
     eng.close()
+
+
+@pytest.mark.parametrize("global_every", [0, 2])
+def test_short_window_and_global_layers(tiny, global_every):
+    """A 24-token sliding window on a 64-token prompt (every layer, or layer 0 only with
+    layer 1 global): the encoder's causal window during prefill and, in the denoising
+    pass, a truncated prefix on sliding layers and the whole prefix on the global one.
+    K/V after prefill and the logits of one denoising step against the oracle."""
+    import dataclasses
+    cfg0, w_np, w_gpu, prompt = tiny
+    cfg = dataclasses.replace(cfg0, window=24, global_every=global_every)
+    V, C = cfg.vocab, cfg.canvas
+    print(f"tiny window 24, global_every {global_every}", flush=True)
+    kv = O.KVCache(cfg, 1)
+    tr = [[]]
+    O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
+    eng = dg.Engine(cfg, w_gpu, max_batch=1, max_ctx=128)
+    eng.prefill_kv(prompt.cuda())
+    near = routing_near_ties(tr[0][:-1], cfg.top_k)
+    _kv_compare(eng, kv, 0, 64, skip=_contaminated(near, cfg.n_layers))
+    canvas = synth.make_masked_canvas(C, V, 20, seed=3).reshape(1, C)
+    tr = [[]]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), 0.7, trace=tr)
+    logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
+    eng.denoise_step(canvas.cuda(), 0.7, logits)
+    torch.cuda.synchronize()
+    rows = [i for i in range(C) if i not in set().union(*routing_near_ties(tr[0], cfg.top_k))]
+    assert len(rows) >= C // 2
+    err = np.abs(to_np_bf16(logits)[0][rows] - ref[0][rows]).max()
+    assert err <= LOGIT_TOL, err
+    eng.close()
