@@ -42,31 +42,31 @@ __device__ __forceinline__ void merge_part(float& m, int& a, float& s, float& t,
 
 // One workgroup per (masked row, kSampleChunk logits).  Each thread loads its
 // kSampleChunk / 2048 16-byte pieces up front (all in flight at once, streamed past
-// the caches) and reduces them to a thread-local (max, s, t) in two register passes;
-// the workgroup merges the 256 partials, and only the lanes holding the chunk maximum
-// search their own elements for its lowest index.  The pass is VALU-bound at about
-// ten operations per logit, so every per-element step is kept to one instruction:
+// the caches); the workgroup first agrees on the chunk maximum M (one barrier), then
+// every thread sums exp(x - M) and exp(x - M) (M - x) over its own pieces against that
+// common M, so the partials combine by plain sums (no per-level rescaling), and only
+// the lanes holding M search their own elements for its lowest index.  Per element
+// the work is kept to one instruction per step:
 //  * the max of the high bf16 halves is taken on the raw 32-bit words (the low half
 //    only perturbs mantissa bits below the bf16 ulp) and masked once at the end;
-//  * exp(x - m) = 2^-(m - x) log2 e with d' = (m - x) log2 e formed by one fma, so
-//    t = sum e (m - x) accumulates e d' and is divided by log2 e once.
+//  * exp(x - M) = 2^-(M - x) log2 e with d' = (M - x) log2 e formed by one fma, so
+//    t = sum e (M - x) accumulates e d' and is divided by log2 e once.
 __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __restrict__ logits,
                                                               const int32_t* __restrict__ canvas,
                                                               int vocab, int nchunks,
                                                               float4* __restrict__ part,
                                                               int* __restrict__ part_arg) {
-  __shared__ float4 wp[4];
-  __shared__ int wa[4];
-  __shared__ float chunk_max;
+  __shared__ float wmax[4];
+  __shared__ float4 wsum[4];
   const int row = blockIdx.y, ch = blockIdx.x;
   if (canvas[row] != vocab) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c0 = ch * kSampleChunk;
   const int c1 = min(vocab, c0 + kSampleChunk);
   const uint16_t* lp = logits + (size_t)row * vocab;
   constexpr int NL = kSampleChunk / (256 * 8);
   // pieces past the end of the vocabulary hold bf16 -1.0e30 (0xf14a): it never wins
-  // the max, its exp underflows to exactly 0 and (m - x) log2 e stays finite, so it
+  // the max, its exp underflows to exactly 0 and (M - x) log2 e stays finite, so it
   // adds nothing to s or t (logits are finite and far inside the fp32 range)
   constexpr uint32_t kPad = 0xf14af14au;
   u32x4 v[NL];
@@ -89,8 +89,32 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
       ml = fmaxf(ml, __uint_as_float(v[i][j] << 16));
     }
   const float m = fmaxf(__uint_as_float(__float_as_uint(mh) & 0xffff0000u), ml);
+  // each pass below unpacks the halves again rather than keeping them from the pass
+  // before (the empty asm hides that they are the same words): keeping them would
+  // cost 32 more registers and a third of the resident workgroups
+#pragma unroll
+  for (int i = 0; i < NL; ++i) asm volatile("" : "+v"(v[i]));
+  const float wm = wave_max(m);
+  if (lane == 0) wmax[w] = wm;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // lowest index holding M: only lanes whose own maximum equals it look, scanning
+  // their elements from the highest index down so the last hit is the lowest
+  int a = INT_MAX;
+  if (m == M) {
+#pragma unroll
+    for (int i = NL - 1; i >= 0; --i)
+#pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        const uint32_t u = v[i][j >> 1];
+        const float x = __uint_as_float(j & 1 ? (u & 0xffff0000u) : (u << 16));
+        if (x == M) a = c0 + (i * 256 + tid) * 8 + j;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) asm volatile("" : "+v"(v[i]));
   constexpr float kLog2e = 1.44269504088896341f;
-  const float mL = m * kLog2e;
+  const float mL = M * kLog2e;
   float s = 0.f, t = 0.f;
 #pragma unroll
   for (int i = 0; i < NL; ++i)
@@ -105,46 +129,17 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
       t = __builtin_fmaf(eh, dh, t);
     }
   t *= 1.0f / kLog2e;
-  // (max, s, t) over the workgroup: xor butterfly within each wave, then the waves;
-  // the thread keeps its own maximum m for the argmax search below
-  float mm = m, ss = s, tt = t;
-  int a = INT_MAX;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(mm, o, 64), s2 = __shfl_xor(ss, o, 64), t2 = __shfl_xor(tt, o, 64);
-    merge_part(mm, a, ss, tt, m2, INT_MAX, s2, t2);
-  }
-  if ((tid & 63) == 0) wp[tid >> 6] = make_float4(mm, ss, tt, 0.f);
-  __syncthreads();
-  if (tid == 0) {
-    float M = wp[0].x, S = wp[0].y, T = wp[0].z;
-    int A = INT_MAX;
-#pragma unroll
-    for (int w = 1; w < 4; ++w) merge_part(M, A, S, T, wp[w].x, INT_MAX, wp[w].y, wp[w].z);
-    chunk_max = M;
-    wp[0] = make_float4(M, S, T, 0.f);
-  }
-  __syncthreads();
-  // lowest index holding the chunk maximum: only lanes whose own maximum equals it look
-  const float M = chunk_max;
-  if (m == M) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w = v[i][j >> 1];
-        const float x = __uint_as_float(j & 1 ? (w & 0xffff0000u) : (w << 16));
-        if (x == M && a == INT_MAX) a = c0 + (i * 256 + tid) * 8 + j;
-      }
-  }
+  s = wave_sum(s);
+  t = wave_sum(t);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) a = min(a, __shfl_xor(a, o, 64));
-  if ((tid & 63) == 0) wa[tid >> 6] = a;
+  if (lane == 0) wsum[w] = make_float4(s, t, __int_as_float(a), 0.f);
   __syncthreads();
   if (tid == 0) {
-    const int A = min(min(wa[0], wa[1]), min(wa[2], wa[3]));
-    part[(size_t)row * nchunks + ch] = wp[0];
-    part_arg[(size_t)row * nchunks + ch] = A;
+    const float4 p0 = wsum[0], p1 = wsum[1], p2 = wsum[2], p3 = wsum[3];
+    part[(size_t)row * nchunks + ch] = make_float4(M, (p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y), 0.f);
+    part_arg[(size_t)row * nchunks + ch] =
+        min(min(__float_as_int(p0.z), __float_as_int(p1.z)), min(__float_as_int(p2.z), __float_as_int(p3.z)));
   }
 }
 
@@ -155,7 +150,17 @@ void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int r
                 vocab, nchunks, part, part_arg);
 }
 
-template <int TPR>   // threads per canvas row in the chunk merge
+// Order key of a masked row: (H, row) as one unsigned 64-bit integer that compares
+// like the pair -- the fp32 bits of H mapped to an order-preserving unsigned form
+// (-0 taken as +0, NaN as +inf) above the row index.
+__device__ __forceinline__ uint64_t eb_key(float H, int row) {
+  if (H != H) H = INFINITY;
+  const uint32_t u = __float_as_uint(H + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t)o << 32 | (uint32_t)row;
+}
+
+template <int TPR>   // threads per canvas row (chunk merge and rank count)
 __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restrict__ part,
                                                          const int* __restrict__ part_arg,
                                                          int nchunks, const float* __restrict__ H_in,
@@ -165,92 +170,83 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
                                                          float* __restrict__ H_out,
                                                          int32_t* __restrict__ amax_out,
                                                          int32_t* __restrict__ n_masked) {
-  __shared__ __attribute__((aligned(16))) float Hs[1024];
+  __shared__ __attribute__((aligned(16))) uint64_t keys[1024];
   __shared__ __attribute__((aligned(16))) float sortedH[1024];
-  __shared__ float Hrow[1024];
-  __shared__ int arow[1024];
+  __shared__ int rank_s[1024];
   __shared__ int nm_s, kstar_s;
   const int b = blockIdx.x;
-  // phase 1: entropy and argmax of each row; the row's TPR threads (adjacent lanes)
-  // merge interleaved subsets of its chunks, then combine through shuffles
-  {
-    const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
-    const size_t ridx = (size_t)b * C + r;
-    const bool rmasked = r < C && canvas[ridx] == vocab;
-    float H = INFINITY;
-    int a = 0;
-    if (part) {
-      float M = -INFINITY, S = 0.f, T = 0.f;
-      a = INT_MAX;
-      if (rmasked) {
-        const float4* pr = part + ridx * nchunks;
-        const int* pa = part_arg + ridx * nchunks;
-        int k = sub;
-        for (; k + 3 * TPR < nchunks; k += 4 * TPR) {
-          float4 p[4];
-          int q[4];
+  // the row's TPR threads are adjacent lanes
+  const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+  const size_t ridx = (size_t)b * C + r;
+  const bool masked = r < C && canvas[ridx] == vocab;
+  // phase 1: entropy and argmax of each masked row; the row's threads merge
+  // interleaved subsets of its chunks, then combine through shuffles
+  float H = INFINITY;
+  int a = 0;
+  if (part) {
+    float M = -INFINITY, S = 0.f, T = 0.f;
+    a = INT_MAX;
+    if (masked) {
+      const float4* pr = part + ridx * nchunks;
+      const int* pa = part_arg + ridx * nchunks;
+      int k = sub;
+      for (; k + 3 * TPR < nchunks; k += 4 * TPR) {
+        float4 p[4];
+        int q[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            p[u] = pr[k + u * TPR];
-            q[u] = pa[k + u * TPR];
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) merge_part(M, a, S, T, p[u].x, q[u], p[u].y, p[u].z);
+        for (int u = 0; u < 4; ++u) {
+          p[u] = pr[k + u * TPR];
+          q[u] = pa[k + u * TPR];
         }
-        for (; k < nchunks; k += TPR) {
-          const float4 p = pr[k];
-          merge_part(M, a, S, T, p.x, pa[k], p.y, p.z);
-        }
-      }
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) {
-        const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64), t2 = __shfl_xor(T, o, 64);
-        const int a2 = __shfl_xor(a, o, 64);
-        merge_part(M, a, S, T, m2, a2, s2, t2);
+        for (int u = 0; u < 4; ++u) merge_part(M, a, S, T, p[u].x, q[u], p[u].y, p[u].z);
       }
-      // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
-      if (rmasked) H = fmaxf(logf(S) + T / S, 0.f);
-    } else if (rmasked) {
-      H = H_in[ridx];
-      a = amax_in[ridx];
+      for (; k < nchunks; k += TPR) {
+        const float4 p = pr[k];
+        merge_part(M, a, S, T, p.x, pa[k], p.y, p.z);
+      }
     }
-    if (rmasked && (a < 0 || a >= vocab)) a = min(max(a, 0), vocab - 1);
-    if (sub == 0 && r < C) {
-      Hrow[r] = rmasked ? H : __int_as_float(0x7fc00000);
-      arow[r] = rmasked ? a : -1;
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+      const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64), t2 = __shfl_xor(T, o, 64);
+      const int a2 = __shfl_xor(a, o, 64);
+      merge_part(M, a, S, T, m2, a2, s2, t2);
     }
+    // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
+    if (masked) H = fmaxf(logf(S) + T / S, 0.f);
+  } else if (masked) {
+    H = H_in[ridx];
+    a = amax_in[ridx];
   }
-  __syncthreads();
-  // phase 2: one thread per row
-  const int c = threadIdx.x;
-  const size_t idx = (size_t)b * C + c;
-  const bool masked = c < C && arow[c] >= 0;
-  const float H = c < C ? Hrow[c] : 0.f;
-  const int a = c < C ? arow[c] : -1;
-  const float key = (masked && !(H != H)) ? H : INFINITY;
-  // unmasked positions hold NaN, which no comparison below counts
-  if (c < C) Hs[c] = masked ? key : __int_as_float(0x7fc00000);
-  const int nm_all = __syncthreads_count(masked);
-  int rank = 0;
+  if (masked && (a < 0 || a >= vocab)) a = min(max(a, 0), vocab - 1);
+  // unmasked rows (and the padding up to a multiple of 8) take the largest key,
+  // which no masked row's key exceeds, so they are never counted below one
+  const int Cp = (C + 7) & ~7;
+  const uint64_t key = masked ? eb_key(H, r) : ~0ull;
+  if (sub == 0 && r < Cp) keys[r] = key;
+  const int nm_all = __syncthreads_count(masked && sub == 0);
+  // phase 2: rank of each masked row = #{masked j : key_j < key_r}; the row's TPR
+  // threads count interleaved pairs of keys (one 16-byte LDS read per pair)
   if (masked) {
-    // rank = #{j : (H_j, j) < (H_c, c)}, four broadcast LDS reads at a time
-    const float4* H4 = reinterpret_cast<const float4*>(Hs);
-    const int C4 = C >> 2;
-    for (int q = 0; q < C4; ++q) {
-      const float4 h = H4[q];
-      const int j = 4 * q;
-      rank += (h.x < key || (h.x == key && j < c)) + (h.y < key || (h.y == key && j + 1 < c)) +
-              (h.z < key || (h.z == key && j + 2 < c)) + (h.w < key || (h.w == key && j + 3 < c));
+    // the row's threads can hold H differing in the last bit (their shuffle merges
+    // round in different orders), so all of them rank the key thread 0 stored
+    const uint64_t key = keys[r];
+    const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
+    int rank = 0;
+    for (int q = sub; q < Cp / 2; q += TPR) {
+      const ulonglong2 kk = k2[q];
+      rank += (kk.x < key) + (kk.y < key);
     }
-    for (int j = 4 * C4; j < C; ++j) {
-      const float hj = Hs[j];
-      rank += (hj < key || (hj == key && j < c));
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    if (sub == 0) {
+      sortedH[rank] = (H != H) ? INFINITY : H;
+      rank_s[r] = rank;
     }
-    sortedH[rank] = key;
   }
-  if (c == 0) nm_s = nm_all;
+  if (threadIdx.x == 0) nm_s = nm_all;
   __syncthreads();
-  if (c == 0) {
+  if (threadIdx.x == 0) {
     const int n = nm_s;
     int ks;
     if (commit_all || n == 0) {
@@ -280,10 +276,10 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     n_masked[b] = n - ks;
   }
   __syncthreads();
-  if (c < C) {
-    if (H_out) H_out[idx] = H;          // NaN on unmasked rows
-    if (amax_out) amax_out[idx] = a;    // -1 on unmasked rows
-    if (masked && rank < kstar_s) canvas[idx] = a;
+  if (sub == 0 && r < C) {
+    if (H_out) H_out[ridx] = masked ? H : __int_as_float(0x7fc00000);   // NaN on unmasked rows
+    if (amax_out) amax_out[ridx] = masked ? a : -1;                       // -1 on unmasked rows
+    if (masked && rank_s[r] < kstar_s) canvas[ridx] = a;
   }
 }
 
