@@ -138,6 +138,8 @@ struct Ws {
   int32_t* inv;    // padded slot of each assignment
   int2* items;
   int32_t* n_items;
+  int2* items2;
+  int32_t* n_items2;
   int32_t* cnt_log;
   int32_t* rows;   // logits row of each compacted [MASK] row (head restricted to masked rows)
   int32_t* counters;   // [0]: compacted [MASK] rows; cleared at the start of every pass
@@ -195,6 +197,8 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->inv = cv.take<int32_t>(M * c.top_k);
   ws->items = cv.take<int2>(moe_max_items((int)M, c.top_k, c.n_experts));
   ws->n_items = cv.take<int32_t>(1);
+  ws->items2 = cv.take<int2>(moe_max_items2((int)M, c.top_k, c.n_experts));
+  ws->n_items2 = cv.take<int32_t>(1);
   ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
   ws->rows = cv.take<int32_t>(M);
   ws->counters = cv.take<int32_t>(kPassCounters);
@@ -293,11 +297,13 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
     DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
     DG_TIMED(ctx, DG_K_ROUTE,
-             launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items,
+             launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items, ws.items2,
+                          ws.n_items2,
                           ws.cnt_log + (size_t)l * E, s));
     const int max_items = moe_max_items(M, k, E);
     DG_TIMED(ctx, DG_K_MOE_GATE_UP,
-             launch_moe_gate_up(ws.h_rm, ws.perm, L.w_gate_up, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
+             launch_moe_gate_up(ws.h_rm, ws.perm, L.w_gate_up, ws.cnt, ws.poff, ws.items2, ws.n_items2,
+                                moe_max_items2(M, k, E),
                                 c.expert_ffn, d, ws.A, s));
     DG_TIMED(ctx, DG_K_MOE_DOWN,
              launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
@@ -640,7 +646,7 @@ dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, f
   hipStream_t s = (hipStream_t)stream;
   launch_topk(d_r, M, E, k, d_ids, d_w, s);
   launch_route(d_ids, M, k, E, d_cnt, d_poff, d_perm, d_inv, reinterpret_cast<int2*>(d_items), d_n_items,
-               nullptr, s);
+               nullptr, nullptr, nullptr, s);
   return check_launch("route");
 }
 

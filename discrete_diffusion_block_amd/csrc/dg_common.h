@@ -284,18 +284,21 @@ __host__ __device__ __forceinline__ size_t v_index(int p, int c, int hd) {
 }
 
 // Work-unit schedule for the grouped expert GEMMs: n_items work items x nfb
-// feature tiles.  XCD x (= blockIdx.x % kXcd) owns the contiguous item range
-// [x*n/kXcd, (x+1)*n/kXcd) and sweeps it feature-tile-major, so the token rows
-// of its items stay in its L2 across the sweep and consecutive workgroups
-// (same feature tile, neighbouring items of one expert) share weight tiles.
-// Returns false for blocks beyond this XCD's share.
+// feature tiles, numbered item-major (u = item * nfb + fb).  XCD x (= blockIdx.x %
+// kXcd) owns the contiguous range [x*T/kXcd, (x+1)*T/kXcd) of the T = n_items * nfb
+// units, so every XCD gets the same number of workgroups to within one, the feature
+// tiles of an item run back to back on one XCD (its token rows stay in that L2), and
+// the neighbouring items of one expert -- consecutive in the list -- share weight
+// tiles there.  Returns false for blocks beyond this XCD's share; the grid needs
+// kXcd * ceil(T / kXcd) blocks.
 __device__ __forceinline__ bool xcd_item_schedule(int n_items, int nfb, int* item, int* fb) {
   const int x = blockIdx.x % kXcd, rank = blockIdx.x / kXcd;
-  const int i0 = (int)((long)x * n_items / kXcd), i1 = (int)((long)(x + 1) * n_items / kXcd);
-  const int nx = i1 - i0;
-  if (nx <= 0 || rank >= nx * nfb) return false;
-  *fb = rank / nx;
-  *item = i0 + (rank - *fb * nx);
+  const long T = (long)n_items * nfb;
+  const long u0 = (long)x * T / kXcd, u1 = (long)(x + 1) * T / kXcd;
+  if (rank >= u1 - u0) return false;
+  const int u = (int)(u0 + rank);
+  *item = u / nfb;
+  *fb = u - *item * nfb;
   return true;
 }
 

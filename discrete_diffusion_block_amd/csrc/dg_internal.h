@@ -92,17 +92,22 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
 
 // ---- MoE ----
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
-constexpr int kMoeGroup = 64;        // tokens per grouped-GEMM work item
+constexpr int kMoeGroup = 64;        // tokens per expert down work item
+constexpr int kMoeGroup2 = 128;      // tokens per expert gate/up work item
 int moe_max_items(int M, int k, int E);
+int moe_max_items2(int M, int k, int E);
 int moe_max_slots(int M, int k, int E);   // padded slot space: M*k + 15*E
+// items: (expert, first token) of every kMoeGroup-token group; items2 (optional)
+// the same for kMoeGroup2-token groups
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
-                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
-                  hipStream_t s);
+                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int2* items2,
+                  int32_t* n_items2, int32_t* cnt_log, hipStream_t s);
 
-// x rows are gathered per slot from h_rm (row-major [M][d]) through perm
+// x rows are gathered per slot from h_rm (row-major [M][d]) through perm; work
+// items of kMoeGroup2 tokens
 void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_t* w_gate_up,
-                        const int32_t* cnt, const int32_t* poff, const int2* items,
-                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
+                        const int32_t* cnt, const int32_t* poff, const int2* items2,
+                        const int32_t* n_items2, int max_items2, int F, int d, uint16_t* a,
                         hipStream_t s);
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
                      const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,

@@ -152,6 +152,7 @@ template <int NW, int CAP>
 struct RouteLds {
   int base[256];
   int ibase[256];
+  int ibase2[256];
   int tot[256];
   int wcnt[NW][256];
   int ids[CAP];
@@ -176,6 +177,7 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
                             int32_t* __restrict__ cnt, int32_t* __restrict__ poff,
                             int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                             int2* __restrict__ items, int32_t* __restrict__ n_items,
+                            int2* __restrict__ items2, int32_t* __restrict__ n_items2,
                             int32_t* __restrict__ cnt_log, RouteLds<NW, CAP>& L) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -207,7 +209,7 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   if (wv == 0) {
     // lane owns experts [lane*epl, lane*epl + epl)
     const int epl = (E + 63) / 64;
-    int ps = 0, is = 0;
+    int ps = 0, is = 0, is2 = 0;
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
@@ -216,18 +218,20 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
         L.tot[e] = c;
         ps += (c + 15) & ~15;
         is += (c + kMoeGroup - 1) / kMoeGroup;
+        is2 += (c + kMoeGroup2 - 1) / kMoeGroup2;
       }
     }
-    int incl_p = ps, incl_i = is;
+    int incl_p = ps, incl_i = is, incl_i2 = is2;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int tp = __shfl_up(incl_p, o, 64), ti = __shfl_up(incl_i, o, 64);
+      const int tp = __shfl_up(incl_p, o, 64), ti = __shfl_up(incl_i, o, 64), ti2 = __shfl_up(incl_i2, o, 64);
       if (lane >= o) {
         incl_p += tp;
         incl_i += ti;
+        incl_i2 += ti2;
       }
     }
-    int run_p = incl_p - ps, run_i = incl_i - is;
+    int run_p = incl_p - ps, run_i = incl_i - is, run_i2 = incl_i2 - is2;
     for (int i = 0; i < epl; ++i) {
       const int e = lane * epl + i;
       if (e < E) {
@@ -237,19 +241,26 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
         cnt[e] = c;
         if (cnt_log) cnt_log[e] = c;
         L.ibase[e] = run_i;
+        L.ibase2[e] = run_i2;
         run_p += (c + 15) & ~15;
         run_i += (c + kMoeGroup - 1) / kMoeGroup;
+        run_i2 += (c + kMoeGroup2 - 1) / kMoeGroup2;
       }
     }
     if (lane == 63) {
       poff[E] = incl_p;
       *n_items = incl_i;
+      if (n_items2) *n_items2 = incl_i2;
     }
   }
   __syncthreads();
   for (int e = tid; e < E; e += NT) {
     int it = L.ibase[e];
     for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
+    if (items2) {
+      int it2 = L.ibase2[e];
+      for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup2) items2[it2++] = make_int2(e, t0);
+    }
     // per-wave running slot of expert e: its offset plus the earlier waves' counts
     int run = L.base[e];
     for (int w2 = 0; w2 < NW; ++w2) {
@@ -281,26 +292,30 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ inv,
                                                      int2* __restrict__ items,
                                                      int32_t* __restrict__ n_items,
+                                                     int2* __restrict__ items2,
+                                                     int32_t* __restrict__ n_items2,
                                                      int32_t* __restrict__ cnt_log) {
   __shared__ RouteLds<16, kRouteIds> L;
-  route_block<16, kRouteIds>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, cnt_log, L);
+  route_block<16, kRouteIds>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log,
+                             L);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
-                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int32_t* cnt_log,
-                  hipStream_t s) {
+                  int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int2* items2,
+                  int32_t* n_items2, int32_t* cnt_log, hipStream_t s) {
   launch_kernel(route_kernel, dim3(1), dim3(1024), 0, s, nullptr, ids, M * k, k, E, moe_max_slots(M, k, E),
-                cnt, poff, perm, inv, items, n_items, cnt_log);
+                cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
-// Grouped expert GEMMs.  A workgroup owns one work item (expert e, a group of up
-// to kMoeGroup = 64 of its tokens) and a tile of output features.  The gate/up
-// GEMM (K = d_model) stages weight and token fragment tiles through LDS rings by
-// direct global->LDS copies and computes a 128-row x 64-token tile; the down GEMM
+// Grouped expert GEMMs.  A workgroup owns one work item (expert e and a group of
+// its tokens: up to kMoeGroup2 = 128 for the gate/up GEMM, kMoeGroup = 64 for the
+// down GEMM) and a tile of output features.  The gate/up GEMM (K = d_model) stages
+// weight and token fragment tiles through LDS rings by direct global->LDS copies
+// and computes a 128-row x 128-token tile; the down GEMM
 // (K = F, short) gives each wave 32 output rows over the whole K loop, with its
 // weights in registers and the item's activation tiles shared through an LDS ring.
 // Either way every operand byte is read once per workgroup, so the kernels hold up
@@ -319,71 +334,71 @@ constexpr int kDownRows = 128; // output rows per down workgroup (32 per wave)
 // other items re-read them from L2.
 //
 // Gate/up, operands staged through LDS.  Workgroup tile: 128 packed weight rows
-// (gate and up blocks of 4 feature blocks) x one work item (up to 64 tokens); the
-// 4 waves form a 2 x 2 grid of 64-row x 32-token sub-tiles.  Per 64-wide k
-// step the workgroup copies 8 weight blocks (two 1 KiB fragment tiles each) and
-// 4 token blocks straight into LDS: weights into a three-step ring (two steps
-// ahead), token rows -- L2 hits -- into a two-step ring (one step ahead).  The
-// ~66 KiB of rings let two workgroups share a CU, which hides more latency than
-// deeper rings in one.  Every weight byte is read once per workgroup and shared
-// by all its token tiles.
+// (gate and up blocks of 4 feature blocks) x one gate/up work item of up to 128
+// tokens; the 8 waves form a 2 x 4 grid of 64-row x 32-token sub-tiles.  Per
+// 64-wide k step the workgroup copies 8 weight blocks (two 1 KiB fragment tiles
+// each) and up to 8 token blocks straight into LDS: weights into a three-step
+// ring (two steps ahead), token rows -- L2 hits -- into a two-step ring (one step
+// ahead).  Wave w copies weight block w and token block w; a wave whose token
+// block lies past the item's tokens copies none.  The 80 KiB of rings let two
+// workgroups share a CU.  Every weight byte is read once per workgroup and shared
+// by up to 128 tokens, every token byte once per workgroup and shared by 128
+// weight rows: per multiply-add this moves a third less than a 64-token tile.
 //
 // A token block's 64-wide k step is 16 rows x 128 bytes of row-major h, gathered
 // through the permutation.  It is copied as two 8-row halves in which every lane
 // moves one 16-byte piece, so each row's 128 bytes come in as one whole cache
 // line (a fragment-shaped copy would touch each line twice, 64 bytes at a time,
-// and the per-CU rate of line requests is what bounds this kernel).  In LDS a
-// half is 8 rows of 128 bytes with the pieces of row r stored XOR-swizzled by r,
-// and the second half starts 1152 bytes after the first: the MFMA operand reads
-// (16 rows, one piece column each) then hit 16 distinct bank groups.
-constexpr int kGuRB = 8, kGuTB = 4, kGuKT = 2;
-constexpr int kGuWSlots = 3, kGuXSlots = 3;
-constexpr int kGuXHalf = 1024 + 128;           // bytes from one 8-row half to the next
+// and the per-CU rate of line requests is what bounds this kernel).  In LDS half
+// h holds rows 8h .. 8h + 7, 128 bytes each, with piece c of row 8h + q stored in
+// slot c ^ q ^ h: the MFMA operand read of one piece column (16 rows) then hits
+// 16 distinct 16-byte bank groups of the 256-byte bank row (the even and odd rows
+// of a half fill opposite 128-byte halves; the two halves differ in the slot's
+// lowest bit).
+constexpr int kGuRB = 8, kGuTB = 8, kGuKT = 2, kGuWaves = 8;
+constexpr int kGuWSlots = 3, kGuXSlots = 2;
+constexpr int kGuXHalf = 1024;                  // bytes from one 8-row half to the next
 constexpr int kGuXBlock = 2 * kGuXHalf;        // one token block of a k step
 constexpr int kGuWBytes = kGuRB * kGuKT * 1024, kGuXBytes = kGuTB * kGuXBlock;
 constexpr int kGuLds = kGuWSlots * kGuWBytes + kGuXSlots * kGuXBytes;
-constexpr int kGuCopies = kGuRB * kGuKT / 4;   // weight tile copies per wave per step
+constexpr int kGuCopies = kGuRB * kGuKT / kGuWaves;   // weight tile copies per wave per step
+static_assert(kMoeGroup2 == 16 * kGuTB, "one token block per wave");
 
 template <bool STREAM>
 __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const uint16_t* h_rm,
                                                  const int32_t* perm, int slot0, int t0, int ne, int F,
                                                  int f0, int d, int lane, int wv, uint16_t* A,
                                                  char* ring) {
-  constexpr int WI = kGuRB / 2, WJ = kGuTB / 2;
+  constexpr int WI = 4, WJ = 2;                      // MFMA blocks per wave (rows x tokens)
   const int ntb = min(kGuTB, (ne - t0 + 15) >> 4);   // token blocks of this item (>= 1)
   const int nk = d / (32 * kGuKT);
-  constexpr int WB = kGuRB / 4, XB = kGuTB / 4;
-  const uint16_t* wsrc[WB];
-#pragma unroll
-  for (int u = 0; u < WB; ++u) wsrc[u] = wgu_e + fm_tile(2 * f0 + wv * WB + u, 0, d, lane);
-  // The token rows are gathered on the fly: in half h of a token block, lane i
-  // copies piece (i % 8) ^ (i / 8) of the step's 128 bytes of row 8h + i / 8.
-  // Token blocks past the item's last one re-read that block, and padding slots
-  // read row 0: their outputs are dropped.
-  static_assert(XB == 1, "one token block per wave");
+  const bool has_x = wv < ntb;                       // this wave copies a token block
+  const uint16_t* wsrc = wgu_e + fm_tile(2 * f0 + wv, 0, d, lane);
+  // The token rows are gathered on the fly: in half h of token block wv, lane i
+  // copies piece (i % 8) ^ (i / 8) ^ h of the step's 128 bytes of row 8h + i / 8.
+  // Padding slots read row 0: their outputs are dropped.
   const uint16_t* xsrc[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int rr = lane >> 3;
-    const int tok = perm[slot0 + 16 * min(wv, ntb - 1) + 8 * h + rr];
-    xsrc[h] = h_rm + (size_t)max(tok, 0) * d + 8 * ((lane & 7) ^ rr);
+    const int tok = has_x ? perm[slot0 + 16 * wv + 8 * h + rr] : 0;
+    xsrc[h] = h_rm + (size_t)max(tok, 0) * d + 8 * ((lane & 7) ^ rr ^ h);
   }
   char* const wring = ring;
   char* const xring = ring + kGuWSlots * kGuWBytes;
   auto issue_w = [&](int step) {
-    char* dst = wring + (step % kGuWSlots) * kGuWBytes + wv * WB * kGuKT * 1024;
+    char* dst = wring + (step % kGuWSlots) * kGuWBytes + wv * kGuKT * 1024;
 #pragma unroll
-    for (int u = 0; u < WB; ++u)
-#pragma unroll
-      for (int t = 0; t < kGuKT; ++t)
-        tile_to_lds<STREAM>(wsrc[u] + (step * kGuKT + t) * 512, dst + (u * kGuKT + t) * 1024);
+    for (int t = 0; t < kGuKT; ++t) tile_to_lds<STREAM>(wsrc + (step * kGuKT + t) * 512, dst + t * 1024);
   };
   auto issue_x = [&](int step) {
+    if (!has_x) return;
     char* dst = xring + (step % kGuXSlots) * kGuXBytes + wv * kGuXBlock;
 #pragma unroll
     for (int h = 0; h < 2; ++h) tile_to_lds<false>(xsrc[h] + step * 64, dst + h * kGuXHalf);
   };
   const int wr = wv & 1, wt = wv >> 1;
+  const bool has_mma = 2 * wt < ntb;                 // some token block of this wave is real
   f32x4 acc[WI][WJ];
 #pragma unroll
   for (int i = 0; i < WI; ++i)
@@ -396,11 +411,15 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   // the copies issued after X(s) are W(s + WS - XS) and, for each of the XS - 2
   // steps since, one X and one W step.  When WS > XS, W(s) was issued before X(s)
   // and waiting until only those later copies are in flight covers both; when
-  // WS == XS, W(s) is the one right after X(s) and must land too.
+  // WS == XS, W(s) is the one right after X(s) and must land too.  A wave without
+  // token copies has only W(s + 1) .. W(s + WS - 2) after W(s).  The barrier then
+  // makes every wave's copies visible and retires all reads of the slots refilled
+  // next.
   constexpr int WS = kGuWSlots, XS = kGuXSlots;
   static_assert(WS >= XS && XS >= 2, "weights run at least as far ahead as token rows");
-  constexpr int kXCopies = 2, kStepCopies = kXCopies + kGuCopies;
+  constexpr int kStepCopies = 2 + kGuCopies;
   constexpr int kAfterX = (WS > XS ? kGuCopies : 0) + (XS - 2) * kStepCopies;
+  constexpr int kAfterW = (WS - 2) * kGuCopies;
   static_assert(kAfterX < 64, "vmcnt range");
 #pragma unroll
   for (int j = -(WS - 1); j < 0; ++j) {
@@ -410,17 +429,22 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   // this lane's operand (token row r, k group g) of k tile t within a token block
   int xoff[kGuKT];
   {
-    const int r = lane & 15, g = lane >> 4, rr = r & 7;
+    const int r = lane & 15, g = lane >> 4, rr = r & 7, h = r >> 3;
 #pragma unroll
-    for (int t = 0; t < kGuKT; ++t) xoff[t] = (r >> 3) * kGuXHalf + rr * 128 + (((4 * t + g) ^ rr) << 4);
+    for (int t = 0; t < kGuKT; ++t) xoff[t] = h * kGuXHalf + rr * 128 + (((4 * t + g) ^ rr ^ h) << 4);
   }
   u32x4 Af[WI][kGuKT], Bf[WJ][kGuKT];
   for (int s = 0; s < nk; ++s) {
-    if (s + WS - 2 < nk) vm_wait<kAfterX>();   // every copy counted above exists
-    else vm_wait<0>();
+    if (s + WS - 2 < nk) {                   // every copy counted above exists
+      if (has_x) vm_wait<kAfterX>();
+      else vm_wait<kAfterW>();
+    } else {
+      vm_wait<0>();
+    }
     __builtin_amdgcn_s_barrier();
     if (s + XS - 1 < nk) issue_x(s + XS - 1);
     if (s + WS - 1 < nk) issue_w(s + WS - 1);
+    if (!has_mma) continue;
     const lds_char* sw = lw + (s % kGuWSlots) * kGuWBytes + lane * 16;
     const lds_char* sx = lx + (s % kGuXSlots) * kGuXBytes;
 #pragma unroll
@@ -457,14 +481,14 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   }
 }
 
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __restrict__ h_rm,
-                                                          const int32_t* __restrict__ perm,
-                                                          const uint16_t* __restrict__ wgu,
-                                                              const int32_t* __restrict__ cnt,
-                                                              const int32_t* __restrict__ poff,
-                                                              const int2* __restrict__ items,
-                                                              const int32_t* __restrict__ n_items,
-                                                              int F, int d, uint16_t* __restrict__ A) {
+__global__ __launch_bounds__(64 * kGuWaves) void moe_gate_up_kernel(const uint16_t* __restrict__ h_rm,
+                                                                    const int32_t* __restrict__ perm,
+                                                                    const uint16_t* __restrict__ wgu,
+                                                                    const int32_t* __restrict__ cnt,
+                                                                    const int32_t* __restrict__ poff,
+                                                                    const int2* __restrict__ items,
+                                                                    const int32_t* __restrict__ n_items,
+                                                                    int F, int d, uint16_t* __restrict__ A) {
   extern __shared__ __attribute__((aligned(1024))) char ring[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -474,15 +498,16 @@ __global__ __launch_bounds__(256) void moe_gate_up_kernel(const uint16_t* __rest
   const int e = it.x, t0 = it.y;
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
-  if (ne <= kMoeGroup)
+  // an expert with a single work item streams its weights (read by no other item)
+  if (ne <= kMoeGroup2)
     gate_up_tile_lds<true>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
   else
     gate_up_tile_lds<false>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
 }
 
 void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_t* w_gate_up,
-                        const int32_t* cnt, const int32_t* poff, const int2* items,
-                        const int32_t* n_items, int max_items, int F, int d, uint16_t* a,
+                        const int32_t* cnt, const int32_t* poff, const int2* items2,
+                        const int32_t* n_items2, int max_items2, int F, int d, uint16_t* a,
                         hipStream_t s) {
   static bool raised = false;
   if (!raised) {
@@ -490,9 +515,9 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
                         hipFuncAttributeMaxDynamicSharedMemorySize, kGuLds);
     raised = true;
   }
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
-  launch_kernel(moe_gate_up_kernel, dim3(blocks), dim3(256), kGuLds, s, nullptr, h_rm, perm, w_gate_up,
-                cnt, poff, items, n_items, F, d, a);
+  const int blocks = kXcd * ((max_items2 + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
+  launch_kernel(moe_gate_up_kernel, dim3(blocks), dim3(64 * kGuWaves), kGuLds, s, nullptr, h_rm, perm,
+                w_gate_up, cnt, poff, items2, n_items2, F, d, a);
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T over K = F.  Workgroup tile: 128 output
@@ -613,6 +638,7 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
 }
 
 int moe_max_items(int M, int k, int E) { return (M * k + kMoeGroup - 1) / kMoeGroup + E; }
+int moe_max_items2(int M, int k, int E) { return (M * k + kMoeGroup2 - 1) / kMoeGroup2 + E; }
 int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
