@@ -300,13 +300,12 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
              launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items, ws.items2,
                           ws.n_items2,
                           ws.cnt_log + (size_t)l * E, s));
-    const int max_items = moe_max_items(M, k, E);
     DG_TIMED(ctx, DG_K_MOE_GATE_UP,
              launch_moe_gate_up(ws.h_rm, ws.perm, L.w_gate_up, ws.cnt, ws.poff, ws.items2, ws.n_items2,
                                 moe_max_items2(M, k, E),
                                 c.expert_ffn, d, ws.A, s));
     DG_TIMED(ctx, DG_K_MOE_DOWN,
-             launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items, ws.n_items, max_items,
+             launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items2, ws.n_items2, moe_max_items2(M, k, E),
                              c.expert_ffn, d, ws.Y, s));
     if (fork) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);

@@ -92,8 +92,8 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
 
 // ---- MoE ----
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
-constexpr int kMoeGroup = 64;        // tokens per expert down work item
-constexpr int kMoeGroup2 = 128;      // tokens per expert gate/up work item
+constexpr int kMoeGroup = 64;        // tokens per work item of the routing test tap's list
+constexpr int kMoeGroup2 = 128;      // tokens per expert GEMM work item
 int moe_max_items(int M, int k, int E);
 int moe_max_items2(int M, int k, int E);
 int moe_max_slots(int M, int k, int E);   // padded slot space: M*k + 15*E
@@ -109,8 +109,9 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
                         const int32_t* cnt, const int32_t* poff, const int2* items2,
                         const int32_t* n_items2, int max_items2, int F, int d, uint16_t* a,
                         hipStream_t s);
+// work items of kMoeGroup2 tokens
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
-                     const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
+                     const int32_t* poff, const int2* items2, const int32_t* n_items2, int max_items2,
                      int F, int d, float* Y, hipStream_t s);
 
 // ---- weight packing ----

@@ -521,13 +521,15 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
 }
 
 // down: Y[slot][n] = A[slot] . W_d[e][n]^T over K = F.  Workgroup tile: 128 output
-// rows x one work item.  Wave wv owns row blocks 2wv, 2wv + 1 and loads their weight
-// fragments straight into registers two steps ahead (each weight byte is used by that
-// wave alone); the item's activation tiles, shared by the four waves, are copied once
-// per workgroup into a three-step LDS ring.
+// rows x one work item of up to 128 tokens (NT token blocks).  Wave wv owns row
+// blocks 2wv, 2wv + 1 and loads their weight fragments straight into registers two
+// steps ahead (each weight byte is used by that wave alone); the item's activation
+// tiles, shared by the four waves, are copied once per workgroup into a three-step
+// LDS ring, wave wv copying token blocks 2wv and 2wv + 1 where they exist.
 constexpr int kDnXS = 3;
-constexpr int kDnXBytes = 4 * kGuKT * 1024;      // 64 tokens x 64 k
+constexpr int kDnXBytes = 8 * kGuKT * 1024;      // 128 tokens x 64 k
 constexpr int kDnLds = kDnXS * kDnXBytes;
+static_assert(kMoeGroup2 == 128, "eight token blocks per down work item");
 
 template <bool STREAM, int NT>
 __device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
@@ -538,14 +540,18 @@ __device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* 
   const int rb0 = (n0 >> 4) + 2 * wv;
   const uint16_t* w0 = wd_e + fm_tile(min(rb0, nblk - 1), 0, F, lane);
   const uint16_t* w1 = wd_e + fm_tile(min(rb0 + 1, nblk - 1), 0, F, lane);
-  // wave wv copies token block wv (the item's last block again past its end; unread)
-  const uint16_t* xsrc = A + fm_tile((slot0 >> 4) + min(wv, NT - 1), 0, F, lane);
+  // wave wv copies token blocks 2wv (when 2wv < NT) and 2wv + 1 (when 2wv + 1 < NT)
+  const int ncopy = max(0, min(2, NT - 2 * wv));
+  const uint16_t* xsrc = A + fm_tile((slot0 >> 4) + min(2 * wv, NT - 1), 0, F, lane);
   lds_char* const lx = lds_launder(ring);
   typedef u32x4 WSet[4];                           // rows rb0 k0, k1; rows rb0+1 k0, k1
   auto issue = [&](int step, WSet& w) {
-    char* dst = ring + (step % kDnXS) * kDnXBytes + wv * kGuKT * 1024;
+    char* dst = ring + (step % kDnXS) * kDnXBytes + 2 * wv * kGuKT * 1024;
+    for (int b = 0; b < ncopy; ++b)
 #pragma unroll
-    for (int t = 0; t < kGuKT; ++t) tile_to_lds_untracked(xsrc + (step * kGuKT + t) * 512, dst + t * 1024);
+      for (int t = 0; t < kGuKT; ++t)
+        tile_to_lds_untracked(xsrc + ((size_t)b * (F >> 5) + step * kGuKT + t) * 512,
+                              dst + (b * kGuKT + t) * 1024);
     const int o = step * kGuKT * 512;
     if (STREAM) {
       w[0] = ld16_stream(w0 + o); w[1] = ld16_stream(w0 + o + 512);
@@ -559,12 +565,15 @@ __device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // step s: its copies and loads were issued two iterations earlier; the previous
-  // iteration's (kGuKT copies + 4 loads) may still be in flight unless it issued none.
+  // iteration's (ncopy * kGuKT copies + 4 loads) may still be in flight unless it
+  // issued none.
   // Refilling ring slot (s + 2) % 3 is safe after the barrier: every wave consumed
   // that slot's step s - 1 before arriving.
   auto body = [&](int s, WSet& wc, WSet& wn, bool more, bool last) {
-    if (!last) vm_wait<kGuKT + 4>();
-    else vm_wait<0>();
+    if (last) vm_wait<0>();
+    else if (ncopy == 2) vm_wait<2 * kGuKT + 4>();
+    else if (ncopy == 1) vm_wait<kGuKT + 4>();
+    else vm_wait<4>();
     __builtin_amdgcn_s_barrier();
     if (more) issue(s + 2, wn);
     const lds_char* sx = lx + (s % kDnXS) * kDnXBytes + lane * 16;
@@ -623,16 +632,20 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   const int ne = cnt[e], slot0 = poff[e] + t0;
   const int n0 = nb * kDownRows;
   const uint16_t* wd_e = wd + (size_t)e * d * F;
-  const int nt = min(4, (ne - t0 + 15) >> 4);
+  const int nt = min(8, (ne - t0 + 15) >> 4);
   // an expert with a single work item streams its weights (read by no other item)
 #define DOWN_TILE(NT)                                                                            \
-  (ne <= kMoeGroup ? down_tile<true, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring)   \
-                   : down_tile<false, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring))
+  (ne <= kMoeGroup2 ? down_tile<true, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring)  \
+                    : down_tile<false, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring))
   switch (nt) {
     case 1: DOWN_TILE(1); break;
     case 2: DOWN_TILE(2); break;
     case 3: DOWN_TILE(3); break;
-    default: DOWN_TILE(4); break;
+    case 4: DOWN_TILE(4); break;
+    case 5: DOWN_TILE(5); break;
+    case 6: DOWN_TILE(6); break;
+    case 7: DOWN_TILE(7); break;
+    default: DOWN_TILE(8); break;
   }
 #undef DOWN_TILE
 }
@@ -642,11 +655,11 @@ int moe_max_items2(int M, int k, int E) { return (M * k + kMoeGroup2 - 1) / kMoe
 int moe_max_slots(int M, int k, int E) { return M * k + 15 * E; }
 
 void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* cnt,
-                     const int32_t* poff, const int2* items, const int32_t* n_items, int max_items,
+                     const int32_t* poff, const int2* items2, const int32_t* n_items2, int max_items2,
                      int F, int d, float* Y, hipStream_t s) {
-  const int blocks = kXcd * ((max_items + kXcd - 1) / kXcd) * ((d + kDownRows - 1) / kDownRows);
-  launch_kernel(moe_down_kernel, dim3(blocks), dim3(256), kDnLds, s, nullptr, a, w_down, cnt, poff, items,
-                n_items, F, d, Y);
+  const int blocks = kXcd * ((max_items2 + kXcd - 1) / kXcd) * ((d + kDownRows - 1) / kDownRows);
+  launch_kernel(moe_down_kernel, dim3(blocks), dim3(256), kDnLds, s, nullptr, a, w_down, cnt, poff, items2,
+                n_items2, F, d, Y);
 }
 
 }  // namespace dg
