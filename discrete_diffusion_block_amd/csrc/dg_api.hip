@@ -140,6 +140,7 @@ struct Ws {
   int32_t* n_items;
   int2* items2;
   int32_t* n_items2;
+  int32_t* prev_amax;  // [batch][C]: the previous step's argmax (adaptive stop)
   int32_t* cnt_log;
   int32_t* rows;   // logits row of each compacted [MASK] row (head restricted to masked rows)
   int32_t* counters;   // [0]: compacted [MASK] rows; cleared at the start of every pass
@@ -206,6 +207,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->Y = cv.take<float>(P * c.d_model);
   ws->As = cv.take<uint16_t>(Mp * c.shared_ffn);
   ws->ys = cv.take<float>(M * c.d_model);
+  ws->prev_amax = cv.take<int32_t>((size_t)batch * c.canvas);
   carve_sampler(cv, batch, c.canvas, c.vocab, ws);
   return cv.off + kAlign;
 }
@@ -395,14 +397,27 @@ dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batc
   return DG_OK;
 }
 
+// Sampler extras of the Technical Report (§3.3): temperature, and the adaptive stop
+// state (prev_amax NULL: off).
+struct SampleOpts {
+  float temperature = 1.0f;
+  float e_stop = -1.0f;
+  int32_t* prev_amax = nullptr;
+  int step = 0;
+  int32_t* done_step = nullptr;
+};
+
 dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
                       float gamma, int commit_all, float* d_entropy, int32_t* d_argmax,
-                      int32_t* d_n_masked, const Ws& ws, hipStream_t s, const dg_ctx* ctx = nullptr) {
+                      int32_t* d_n_masked, const Ws& ws, hipStream_t s, const dg_ctx* ctx = nullptr,
+                      const SampleOpts& o = SampleOpts{}) {
   DG_TIMED(ctx, DG_K_SAMPLE_PASS1,
-           launch_sample_partials(d_logits, d_canvas, batch * canvas, vocab, ws.part, ws.part_arg, s));
+           launch_sample_partials(d_logits, d_canvas, batch * canvas, vocab, 1.0f / o.temperature, ws.part,
+                                  ws.part_arg, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
            launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
-                            canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, s));
+                            canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax,
+                            o.e_stop, o.step, o.done_step, s));
   return check_launch("sampler");
 }
 
@@ -510,6 +525,33 @@ dg_status dg_sample_workspace_size(int batch, int canvas, int vocab, size_t* byt
   return DG_OK;
 }
 
+dg_status dg_sample_eb_ex(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                          float gamma, int commit_all, float temperature, float e_stop,
+                          int32_t* d_prev_argmax, int step, int32_t* d_done_step, float* d_entropy,
+                          int32_t* d_argmax, int32_t* d_n_masked, void* d_ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
+  if (st != DG_OK) return st;
+  if (!d_logits || !d_canvas || !d_n_masked || !d_ws) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  if (!(temperature > 0.0f) || temperature > 3.0e38f) return fail(DG_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (e_stop != e_stop) return fail(DG_ERR_INVALID_ARG, "e_stop is NaN");
+  if (step < 0) return fail(DG_ERR_INVALID_ARG, "step must be >= 0");
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
+  Carver cv{base};
+  Ws ws;
+  carve_sampler(cv, batch, canvas, vocab, &ws);
+  SampleOpts o;
+  o.temperature = temperature;
+  o.e_stop = e_stop;
+  o.prev_amax = d_prev_argmax;
+  o.step = step;
+  o.done_step = d_done_step;
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
+                     d_n_masked, ws, (hipStream_t)stream, nullptr, o);
+}
+
 dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
                        float gamma, int commit_all, float* d_entropy, int32_t* d_argmax,
                        int32_t* d_n_masked, void* d_ws, size_t ws_bytes, void* stream) {
@@ -552,6 +594,49 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     if (st != DG_OK) return st;
     st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == steps - 1, nullptr,
                      nullptr, d_n_masked, ws, s, ctx);
+    if (st != DG_OK) return st;
+  }
+  if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
+  return DG_OK;
+}
+
+dg_status dg_generate_block_ex(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
+                               float gamma, float tau_max, float tau_min, float e_stop, int append_kv,
+                               uint16_t* d_logits, int32_t* d_n_masked, int32_t* d_done_step, void* d_ws,
+                               size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_canvas || !d_logits || !d_n_masked || !d_done_step) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (max_steps < 1) return fail(DG_ERR_INVALID_ARG, "max_steps must be >= 1");
+  if (gamma != gamma || e_stop != e_stop) return fail(DG_ERR_INVALID_ARG, "gamma or e_stop is NaN");
+  if (!(tau_max > 0.0f) || !(tau_min > 0.0f) || tau_max > 3.0e38f || tau_min > 3.0e38f)
+    return fail(DG_ERR_INVALID_ARG, "temperatures must be finite and > 0");
+  const dg_config& c = ctx->cfg;
+  for (int b = 0; b < batch; ++b)
+    if (kv->len[b] + c.canvas > c.max_ctx)
+      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + canvas %d exceeds max_ctx %d", b,
+                  (long long)kv->len[b], c.canvas, c.max_ctx);
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(ws.prev_amax, -1, (size_t)batch * c.canvas, s));
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_done_step, 0, (size_t)batch, s));
+  for (int step = 0; step < max_steps; ++step) {
+    const float t = 1.0f - (float)step / (float)max_steps;
+    SampleOpts o;
+    o.temperature = tau_min + (tau_max - tau_min) * t;
+    if (!(o.temperature > 0.0f)) return fail(DG_ERR_INVALID_ARG, "annealed temperature must stay > 0");
+    o.e_stop = e_stop;
+    o.prev_amax = ws.prev_amax;
+    o.step = step;
+    o.done_step = d_done_step;
+    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/true);
+    if (st != DG_OK) return st;
+    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == max_steps - 1, nullptr,
+                     nullptr, d_n_masked, ws, s, ctx, o);
     if (st != DG_OK) return st;
   }
   if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
@@ -656,7 +741,7 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
       vocab < 1 || gamma != gamma)
     return fail(DG_ERR_INVALID_ARG, "bad selection arguments");
   launch_eb_select(nullptr, nullptr, 0, d_entropy, d_argmax, d_canvas, batch, canvas, vocab, gamma,
-                   commit_all, nullptr, nullptr, d_n_masked, (hipStream_t)stream);
+                   commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, (hipStream_t)stream);
   return check_launch("eb select");
 }
 

@@ -120,12 +120,17 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int
 
 // ---- sampler ----
 constexpr int kSampleChunk = 16384;  // logits per workgroup in the first sampler pass (multiple of 2048)
+// inv_tau = 1 / sampling temperature (1 = the plain distribution)
 void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
-                            float4* part, int* part_arg, hipStream_t s);
+                            float inv_tau, float4* part, int* part_arg, hipStream_t s);
+// prev_amax (optional, [batch][C] in/out): the previous step's argmax, for the
+// adaptive stop at e_stop; done_step (optional, [batch]): set to step + 1 where it is
+// 0 and the call leaves no [MASK] row
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
-                      int32_t* n_masked, hipStream_t s);
+                      int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
+                      hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

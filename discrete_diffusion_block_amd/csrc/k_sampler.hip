@@ -5,8 +5,10 @@
 //
 // Pass 1 streams the bf16 logits once (HBM-bound: 512 KiB per 262144-wide
 // row): one 256-thread workgroup per (row, kSampleChunk-logit chunk) computes the
-// chunk max m_c, its lowest argmax, s_c = sum exp(x - m_c) and
-// t_c = sum exp(x - m_c) (m_c - x).  Rows that are not [MASK] are skipped.
+// chunk's lowest argmax and, for the logits y = x / tau at the sampling
+// temperature tau (1 unless annealed, §3.3), the chunk max m_c of y,
+// s_c = sum exp(y - m_c) and t_c = sum exp(y - m_c) (m_c - y).  Rows that are not
+// [MASK] are skipped.
 // Pass 2 (one workgroup per sequence) merges the chunks of each row in index
 // order, H = log S + T / S, ranks the masked rows by (H, position), takes the
 // running fp64 sum in rank order, and commits the argmax of the first k* rows.
@@ -53,7 +55,7 @@ __device__ __forceinline__ void merge_part(float& m, int& a, float& s, float& t,
 //    t = sum e (M - x) accumulates e d' and is divided by log2 e once.
 __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __restrict__ logits,
                                                               const int32_t* __restrict__ canvas,
-                                                              int vocab, int nchunks,
+                                                              int vocab, int nchunks, float inv_tau,
                                                               float4* __restrict__ part,
                                                               int* __restrict__ part_arg) {
   __shared__ float wmax[4];
@@ -114,14 +116,15 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
 #pragma unroll
   for (int i = 0; i < NL; ++i) asm volatile("" : "+v"(v[i]));
   constexpr float kLog2e = 1.44269504088896341f;
-  const float mL = M * kLog2e;
+  const float kL = kLog2e * inv_tau;            // exactly log2 e at tau = 1
+  const float mL = M * kL;
   float s = 0.f, t = 0.f;
 #pragma unroll
   for (int i = 0; i < NL; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float xl = __uint_as_float(v[i][j] << 16), xh = __uint_as_float(v[i][j] & 0xffff0000u);
-      const float dl = __builtin_fmaf(xl, -kLog2e, mL), dh = __builtin_fmaf(xh, -kLog2e, mL);
+      const float dl = __builtin_fmaf(xl, -kL, mL), dh = __builtin_fmaf(xh, -kL, mL);
       const float el = __builtin_amdgcn_exp2f(-dl), eh = __builtin_amdgcn_exp2f(-dh);
       s += el;
       t = __builtin_fmaf(el, dl, t);
@@ -137,17 +140,18 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
   __syncthreads();
   if (tid == 0) {
     const float4 p0 = wsum[0], p1 = wsum[1], p2 = wsum[2], p3 = wsum[3];
-    part[(size_t)row * nchunks + ch] = make_float4(M, (p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y), 0.f);
+    part[(size_t)row * nchunks + ch] =
+        make_float4(M * inv_tau, (p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y), 0.f);
     part_arg[(size_t)row * nchunks + ch] =
         min(min(__float_as_int(p0.z), __float_as_int(p1.z)), min(__float_as_int(p2.z), __float_as_int(p3.z)));
   }
 }
 
 void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
-                            float4* part, int* part_arg, hipStream_t s) {
+                            float inv_tau, float4* part, int* part_arg, hipStream_t s) {
   const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
   launch_kernel(sample_partials_kernel, dim3(nchunks, rows), dim3(256), 0, s, nullptr, logits, canvas,
-                vocab, nchunks, part, part_arg);
+                vocab, nchunks, inv_tau, part, part_arg);
 }
 
 // Order key of a masked row: (H, row) as one unsigned 64-bit integer that compares
@@ -169,8 +173,11 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
                                                          int vocab, float gamma, int commit_all,
                                                          float* __restrict__ H_out,
                                                          int32_t* __restrict__ amax_out,
-                                                         int32_t* __restrict__ n_masked) {
+                                                         int32_t* __restrict__ n_masked,
+                                                         int32_t* __restrict__ prev_amax, float e_stop,
+                                                         int step, int32_t* __restrict__ done_step) {
   __shared__ __attribute__((aligned(16))) uint64_t keys[1024];
+  __shared__ double hsum[16];
   __shared__ __attribute__((aligned(16))) float sortedH[1024];
   __shared__ int rank_s[1024];
   __shared__ int nm_s, kstar_s;
@@ -224,7 +231,17 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
   const int Cp = (C + 7) & ~7;
   const uint64_t key = masked ? eb_key(H, r) : ~0ull;
   if (sub == 0 && r < Cp) keys[r] = key;
+  // adaptive stop (prev_amax given; §3.3): the masked rows' entropies summed in fp64
+  // (per wave, then the waves in order) and the rows whose argmax moved since the
+  // previous step counted
+  bool moved = false;
+  if (prev_amax) {
+    const double hv = wave_sum_d((masked && sub == 0) ? (double)H : 0.0);
+    if ((threadIdx.x & 63) == 0) hsum[threadIdx.x >> 6] = hv;
+    moved = masked && sub == 0 && a != prev_amax[ridx];
+  }
   const int nm_all = __syncthreads_count(masked && sub == 0);
+  const int n_moved = prev_amax ? __syncthreads_count(moved) : 1;
   // phase 2: rank of each masked row = #{masked j : key_j < key_r}; the row's TPR
   // threads count interleaved pairs of keys (one 16-byte LDS read per pair)
   if (masked) {
@@ -248,8 +265,14 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
   __syncthreads();
   if (threadIdx.x == 0) {
     const int n = nm_s;
+    bool stop = false;
+    if (n_moved == 0 && n > 0) {
+      double hs = 0.0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) hs += hsum[w];
+      stop = hs / n < (double)e_stop;
+    }
     int ks;
-    if (commit_all || n == 0) {
+    if (commit_all || stop || n == 0) {
       ks = n;
     } else {
       // running fp64 sum in rank order; entries are read four at a time
@@ -274,11 +297,13 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     }
     kstar_s = ks;
     n_masked[b] = n - ks;
+    if (done_step && n - ks == 0 && done_step[b] == 0) done_step[b] = step + 1;
   }
   __syncthreads();
   if (sub == 0 && r < C) {
     if (H_out) H_out[ridx] = masked ? H : __int_as_float(0x7fc00000);   // NaN on unmasked rows
     if (amax_out) amax_out[ridx] = masked ? a : -1;                       // -1 on unmasked rows
+    if (prev_amax) prev_amax[ridx] = masked ? a : -1;
     if (masked && rank_s[r] < kstar_s) canvas[ridx] = a;
   }
 }
@@ -286,14 +311,17 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
-                      int32_t* n_masked, hipStream_t s) {
+                      int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
+                      hipStream_t s) {
   const int rows64 = ((C + 63) / 64) * 64;
   if (4 * rows64 <= 1024)
     launch_kernel(eb_select_kernel<4>, dim3(batch), dim3(4 * rows64), 0, s, nullptr, part, part_arg, nchunks,
-                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked, prev_amax,
+                  e_stop, step, done_step);
   else
     launch_kernel(eb_select_kernel<1>, dim3(batch), dim3(rows64), 0, s, nullptr, part, part_arg, nchunks,
-                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked);
+                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked, prev_amax,
+                  e_stop, step, done_step);
 }
 
 }  // namespace dg

@@ -76,6 +76,10 @@ def lib():
             "dg_sample_workspace_size": [i32, i32, i32, C.POINTER(sz)],
             "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
+            "dg_sample_eb_ex": [vp, vp, i32, i32, i32, f32, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, sz,
+                                vp],
+            "dg_generate_block_ex": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, i32, vp, vp, vp,
+                                     vp, sz, vp],
             "dg_packed_elems": [i32, i32, C.POINTER(sz)],
             "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
             "dg_profile_begin": [vp, i32, C.c_uint32],
@@ -174,6 +178,27 @@ def dg_sample_eb(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commi
     b, c, v = logits.shape
     _check(lib().dg_sample_eb(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
                               _p(entropy), _p(argmax), _p(n_masked), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sample_eb_ex(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all: bool,
+                    temperature: float, e_stop: float, prev_argmax: Optional[torch.Tensor], step: int,
+                    done_step: Optional[torch.Tensor], n_masked: torch.Tensor, ws: torch.Tensor,
+                    entropy: Optional[torch.Tensor] = None, argmax: Optional[torch.Tensor] = None,
+                    stream=None):
+    b, c, v = logits.shape
+    _check(lib().dg_sample_eb_ex(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
+                                 float(temperature), float(e_stop), _p(prev_argmax), int(step),
+                                 _p(done_step), _p(entropy), _p(argmax), _p(n_masked), _p(ws), ws.numel(),
+                                 _stream(stream)))
+
+
+def dg_generate_block_ex(ctx, kv: KV, canvas: torch.Tensor, max_steps: int, gamma: float, tau_max: float,
+                         tau_min: float, e_stop: float, append_kv: bool, logits: torch.Tensor,
+                         n_masked: torch.Tensor, done_step: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().dg_generate_block_ex(ctx, C.byref(kv), _p(canvas), canvas.shape[0], max_steps, float(gamma),
+                                      float(tau_max), float(tau_min), float(e_stop), int(bool(append_kv)),
+                                      _p(logits), _p(n_masked), _p(done_step), _p(ws), ws.numel(),
+                                      _stream(stream)))
 
 
 def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_kv: bool,
@@ -370,6 +395,11 @@ class Engine:
                   stream=None):
         dg_sample_eb(logits, canvas, gamma, commit_all, n_masked, self.ws, entropy, argmax, stream)
 
+    def sample_eb_ex(self, logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step,
+                     done_step, n_masked, entropy=None, argmax=None, stream=None):
+        dg_sample_eb_ex(logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step, done_step,
+                        n_masked, self.ws, entropy, argmax, stream)
+
     def moe_counts(self):
         """Per-layer per-expert token counts of the latest pass (int32 [L][E], device)."""
         off = dg_workspace_moe_counts(self.ctx, self.max_batch)
@@ -379,3 +409,8 @@ class Engine:
     def generate_block(self, canvas, steps, gamma, append_kv, logits, n_masked, stream=None):
         dg_generate_block(self.ctx, self.kv, canvas, steps, gamma, append_kv, logits, n_masked,
                           self.ws, stream)
+
+    def generate_block_ex(self, canvas, max_steps, gamma, tau_max, tau_min, e_stop, append_kv, logits,
+                          n_masked, done_step, stream=None):
+        dg_generate_block_ex(self.ctx, self.kv, canvas, max_steps, gamma, tau_max, tau_min, e_stop,
+                             append_kv, logits, n_masked, done_step, self.ws, stream)

@@ -172,6 +172,26 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
                        int32_t* d_argmax, int32_t* d_n_masked, void* d_ws, size_t ws_bytes,
                        void* stream);
 
+/* dg_sample_eb with the two extras of the Technical Report's default sampler (§3.3):
+ *  - temperature annealing: H is the entropy of softmax(row / temperature)
+ *    (temperature finite and > 0; 1 gives dg_sample_eb; the argmax does not depend
+ *    on it);
+ *  - adaptive stopping, when d_prev_argmax (int32 [batch][canvas], in/out) is not
+ *    NULL: it holds the previous step's argmax of every row (-1 where there was
+ *    none: fill it with -1 before a block's first step) and is overwritten with
+ *    this step's (-1 on rows that were not [MASK]).  A sequence whose [MASK] rows
+ *    have a mean H (fp64) below e_stop and every argmax equal to the previous
+ *    step's commits all of them in this call.
+ * d_done_step (int32 [batch], may be NULL): an entry that is 0 is set to step + 1
+ * when this call leaves its sequence with no [MASK] row.  Other arguments, outputs
+ * and the workspace as for dg_sample_eb.  Errors: DG_ERR_INVALID_ARG for a
+ * temperature that is not finite and > 0, a NaN gamma or e_stop, or step < 0. */
+dg_status dg_sample_eb_ex(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas,
+                          int vocab, float gamma, int commit_all, float temperature, float e_stop,
+                          int32_t* d_prev_argmax, int step, int32_t* d_done_step,
+                          float* d_entropy, int32_t* d_argmax, int32_t* d_n_masked, void* d_ws,
+                          size_t ws_bytes, void* stream);
+
 /* Generate one block per sequence (Technical Report §3.1–§3.3): fill d_canvas
  * (int32 [batch][C]) with [MASK]; for s = 0..steps-1 run the denoising pass at
  * t_s = 1 - s/steps and dg_sample_eb (commit_all on the last step); then, if
@@ -185,6 +205,21 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
 dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps,
                             float gamma, int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
                             void* d_ws, size_t ws_bytes, void* stream);
+
+/* dg_generate_block with the Technical Report's default sampler (§3.3) on the
+ * absorbing canvas: up to max_steps steps at t_s = 1 - s/max_steps, entropies at
+ * the temperature tau_min + (tau_max - tau_min) t_s (annealed linearly from tau_max
+ * to tau_min; both finite and > 0), and the adaptive stop with threshold e_stop
+ * (< 0: off; see dg_sample_eb_ex), which commits a sequence's remaining positions
+ * at once; the last step commits whatever is left.  d_done_step (int32 [batch],
+ * out): the number of steps after which each canvas was complete.  The previous
+ * argmax lives in the workspace.  Once a canvas is complete its later steps change
+ * nothing, but their denoising passes still run: nothing is skipped on the device
+ * and the host never waits. */
+dg_status dg_generate_block_ex(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
+                               float gamma, float tau_max, float tau_min, float e_stop,
+                               int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
+                               int32_t* d_done_step, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---- measurement helpers (diagnostics; not thread-safe) ---- */
 

@@ -33,7 +33,7 @@ in the design notes of the repository):
     C canvas keys.  Encoder (prefill/append): key j visible to query i iff
     j <= i and (global layer or i - j < W).
   * Sampler: per masked row, argmax (lowest id on ties) and entropy
-    H = -sum p log p of softmax(logits).  Selection: masked positions ordered
+    H = -sum p log p of softmax(logits / tau) (tau = 1 unless annealed).  Selection: masked positions ordered
     by (H asc, position asc); S_k = running fp64 sum of H in that order;
     commit the first k* = max(1, max{k : S_k <= gamma}) positions, or all
     when commit_all (the last step of a block).
@@ -306,14 +306,17 @@ def denoise_step(cfg, weights: dict, kv: KVCache, canvas: np.ndarray, t: float,
 # --------------------------------------------------------------------------------------
 
 
-def entropy_argmax(rows: np.ndarray):
-    """Per row of logits: (H, argmax).  H = -sum p log p with p = softmax(row), in float64.
+def entropy_argmax(rows: np.ndarray, tau: float = 1.0):
+    """Per row of logits: (H, argmax).  H = -sum p log p with p = softmax(row / tau), in
+    float64 (tau > 0 is the sampling temperature of DiffusionGemma Technical Report §3.3,
+    "temperature annealing"; tau = 1 is the plain distribution).
 
-    argmax is the lowest index among exact maxima.
+    argmax is the lowest index among exact maxima of the row (the same for every tau).
     """
-    x = np.asarray(rows, dtype=np.float64)
+    raw = np.asarray(rows, dtype=np.float64)
+    a = np.argmax(raw, axis=-1)
+    x = raw / float(tau)
     m = np.max(x, axis=-1, keepdims=True)
-    a = np.argmax(x, axis=-1)
     e = np.exp(x - m)
     p = e / np.sum(e, axis=-1, keepdims=True)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -343,13 +346,36 @@ def eb_select(H32: np.ndarray, masked: List[int], gamma: float, commit_all: bool
     return order[:max(1, k)]
 
 
+def temperature(t: float, tau_max: float, tau_min: float) -> float:
+    """Technical Report §3.3, temperature annealing: the temperature moves linearly along
+    the denoising time t in [0, 1], from tau_max at t = 1 (the start of a block) to
+    tau_min at t = 0."""
+    return tau_min + (tau_max - tau_min) * t
+
+
+def adaptive_stop(H32: np.ndarray, amax: np.ndarray, prev_amax: np.ndarray, masked: List[int],
+                  e_stop: float) -> bool:
+    """Technical Report §3.3, adaptive stopping, on the masked rows of one canvas (the only
+    rows the absorbing sampler predicts): true when their mean entropy is below e_stop and
+    every one of them has the same most likely token as at the previous step.  The mean
+    is the exactly rounded float64 sum of the float32 entropies divided by their number."""
+    if not masked:
+        return False
+    mean = math.fsum(float(np.float32(H32[i])) for i in masked) / len(masked)
+    return mean < e_stop and all(int(amax[i]) == int(prev_amax[i]) for i in masked)
+
+
 def sample_eb(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: bool,
-              mask_id: int):
+              mask_id: int, tau: float = 1.0, e_stop: Optional[float] = None,
+              prev_amax: Optional[np.ndarray] = None):
     """One sampler call on logits [B][C][V] (values as the engine stores them: bf16).
 
     Returns (new_canvas, H32 [B][C] (NaN on unmasked rows), argmax [B][C] (-1 on
     unmasked rows), n_masked [B] after the commit, committed list per batch).
     Committed tokens are never revised: only [MASK] rows are read or written.
+    Entropies are taken at temperature tau.  With e_stop given, a sequence whose masked
+    rows pass adaptive_stop against prev_amax [B][C] (the previous step's argmax, -1
+    where there was none) commits all of them.
     """
     canvas = np.array(canvas, dtype=np.int64, copy=True)
     B, C = canvas.shape
@@ -360,10 +386,11 @@ def sample_eb(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: 
     for b in range(B):
         masked = [i for i in range(C) if canvas[b, i] == mask_id]
         if masked:
-            H, a = entropy_argmax(logits[b, masked])
+            H, a = entropy_argmax(logits[b, masked], tau)
             H32[b, masked] = H.astype(np.float32)
             amax[b, masked] = a
-        sel = eb_select(H32[b], masked, gamma, commit_all)
+        stop = e_stop is not None and adaptive_stop(H32[b], amax[b], prev_amax[b], masked, e_stop)
+        sel = eb_select(H32[b], masked, gamma, commit_all or stop)
         for i in sel:
             canvas[b, i] = amax[b, i]
         committed.append(sel)
@@ -393,6 +420,38 @@ def generate_block(cfg, weights: dict, kv: KVCache, batch: int, steps: int, gamm
     if append:
         prefill_kv(cfg, weights, kv, canvas, rnd)
     return canvas
+
+
+def generate_block_annealed(cfg, weights: dict, kv: KVCache, batch: int, max_steps: int, gamma: float,
+                            tau_max: float, tau_min: float, e_stop: float, append: bool = True,
+                            rnd: bool = True, record: Optional[list] = None):
+    """The Technical Report's sampler (§3.3) on the absorbing canvas: up to max_steps steps
+    with t_s = 1 - s/max_steps, entropies at the annealed temperature
+    temperature(t_s, tau_max, tau_min), and the adaptive stop, which commits every masked
+    position of a sequence at once; the last step commits the rest.  Steps after a
+    sequence is complete change nothing for it.  Returns (canvas [B][C], steps [B]): the
+    step count after which each canvas was complete."""
+    canvas = np.full((batch, cfg.canvas), cfg.mask_id, dtype=np.int64)
+    prev = np.full((batch, cfg.canvas), -1, dtype=np.int64)
+    done_at = np.zeros(batch, dtype=np.int64)
+    for s in range(max_steps):
+        t = 1.0 - s / max_steps
+        tau = temperature(t, tau_max, tau_min)
+        logits = denoise_step(cfg, weights, kv, canvas, t, rnd)
+        stored = bf16(logits) if rnd else logits
+        new, H32, amax, n_masked, committed = sample_eb(stored, canvas, gamma, s == max_steps - 1,
+                                                        cfg.mask_id, tau, e_stop, prev)
+        if record is not None:
+            record.append({"t": t, "tau": tau, "canvas_in": canvas.copy(), "H": H32, "argmax": amax,
+                           "n_masked": n_masked, "committed": committed})
+        for b in range(batch):
+            if done_at[b] == 0 and n_masked[b] == 0:
+                done_at[b] = s + 1
+        prev = amax
+        canvas = new
+    if append:
+        prefill_kv(cfg, weights, kv, canvas, rnd)
+    return canvas, done_at
 
 
 # --------------------------------------------------------------------------------------

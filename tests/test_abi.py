@@ -124,3 +124,44 @@ def test_copy_tap_validates(L):
     for n in (0, 24, 17):                                     # empty, not a multiple of 16
         assert L.dg_test_copy(C.c_void_p(0x1000), C.c_void_p(0x2000), n, None) == -1
     assert L.dg_test_copy(None, C.c_void_p(0x2000), 32, None) == -1
+
+
+def test_sampler_ex_validates(L):
+    need = dg.dg_sample_workspace_size(1, 256, 262144)
+    p = C.c_void_p(0x1000)
+    ok = dict(temperature=0.6, e_stop=0.005, step=0)
+    def call(temperature, e_stop, step, ws_bytes=need):
+        return L.dg_sample_eb_ex(p, p, 1, 256, 262144, 1.0, 0, temperature, e_stop, None, step, None, None,
+                                 None, p, p, ws_bytes, None)
+    assert call(0.0, 0.005, 0) == -1                      # temperature must be > 0
+    assert call(-1.0, 0.005, 0) == -1
+    assert call(float("inf"), 0.005, 0) == -1
+    assert call(float("nan"), 0.005, 0) == -1
+    assert call(0.6, float("nan"), 0) == -1
+    assert call(0.6, 0.005, -1) == -1
+    assert call(**ok, ws_bytes=need - 1) == -3
+
+
+def test_generate_ex_validates_before_launching(L):
+    cfg = synth.CONFIGS["tiny"]
+    w, keep = _fake_weights(cfg)
+    ctx = dg.dg_create(dg.make_config(cfg, 1, 128), w)
+    try:
+        kv = dg.KV(0x1000, 0x1000)
+        need = dg.dg_workspace_size(ctx, 1)
+        p = C.c_void_p(0x1000)
+        for max_steps, tau_max, tau_min, e_stop in ((0, 0.8, 0.4, 0.005), (4, 0.0, 0.4, 0.005),
+                                                    (4, 0.8, -0.4, 0.005), (4, 0.8, 0.4, float("nan")),
+                                                    (4, float("inf"), 0.4, 0.005)):
+            st = L.dg_generate_block_ex(ctx, C.byref(kv), p, 1, max_steps, 1.0, tau_max, tau_min, e_stop, 1,
+                                        p, p, p, p, need, None)
+            assert st == -1
+        st = L.dg_generate_block_ex(ctx, C.byref(kv), p, 1, 4, 1.0, 0.8, 0.4, 0.005, 1, p, p, None, p,
+                                    need, None)
+        assert st == -1                                   # d_done_step is required
+        st = L.dg_generate_block_ex(ctx, C.byref(kv), p, 1, 4, 1.0, 0.8, 0.4, 0.005, 1, p, p, p, p,
+                                    need - 1, None)
+        assert st == -3
+        assert kv.len[0] == 0
+    finally:
+        dg.dg_destroy(ctx)

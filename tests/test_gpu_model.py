@@ -257,3 +257,45 @@ def test_short_window_and_global_layers(tiny, global_every):
     err = np.abs(to_np_bf16(logits)[0][rows] - ref[0][rows]).max()
     assert err <= LOGIT_TOL, err
     eng.close()
+
+
+@pytest.mark.parametrize("e_stop", [0.005, 1e30])
+def test_generate_block_ex_equals_stepwise(tiny, e_stop):
+    """dg_generate_block_ex == dg_denoise_step + dg_sample_eb_ex driven step by step (bitwise), with
+    the temperature annealed 0.8 -> 0.4 and the adaptive stop (with e_stop 1e30 it fires at the
+    first step whose masked argmaxes all repeat)."""
+    cfg, w_np, w_gpu, prompt = tiny
+    V, C = cfg.vocab, cfg.canvas
+    steps, gamma, tmax, tmin = 5, 1.0, 0.8, 0.4
+    print(f"generate_block_ex e_stop={e_stop}", flush=True)
+    logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    done = torch.empty(1, dtype=torch.int32, device="cuda")
+    eng = dg.Engine(cfg, w_gpu, max_batch=1, max_ctx=128)
+    eng.prefill_kv(prompt.cuda())
+    blk = torch.empty(1, C, dtype=torch.int32, device="cuda")
+    eng.generate_block_ex(blk, steps, gamma, tmax, tmin, e_stop, True, logits, nm, done)
+    torch.cuda.synchronize()
+    assert nm.item() == 0 and eng.lengths[0] == 64 + C
+
+    ref = dg.Engine(cfg, w_gpu, max_batch=1, max_ctx=128)
+    ref.prefill_kv(prompt.cuda())
+    canvas = torch.full((1, C), cfg.mask_id, dtype=torch.int32, device="cuda")
+    prev = torch.full((1, C), -1, dtype=torch.int32, device="cuda")
+    done_ref = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s in range(steps):
+        t = np.float32(1) - np.float32(s) / np.float32(steps)
+        tau = np.float32(tmin) + (np.float32(tmax) - np.float32(tmin)) * t
+        ref.denoise_step(canvas, float(t), logits)
+        ref.sample_eb_ex(logits, canvas, gamma, s == steps - 1, float(tau), e_stop, prev, s, done_ref, nm)
+    ref.prefill_kv(canvas)
+    torch.cuda.synchronize()
+    assert torch.equal(blk, canvas)
+    assert done.item() == done_ref.item()
+    if e_stop == 0.005:
+        assert done.item() == steps                 # random-init logits: H ~ log V, no early stop
+    assert 1 <= done.item() <= steps
+    k1, v1 = eng.kv_view()
+    k2, v2 = ref.kv_view()
+    assert torch.equal(k1[:, :, :, :64 + C], k2[:, :, :, :64 + C])
+    eng.close(); ref.close()

@@ -340,3 +340,83 @@ def test_router_topk_non_finite_and_signed_zero():
     assert ids.tolist() == [[6, 7, 4, 5, 0]]
     e = np.array([1.0, math.exp(-0.5), math.exp(-1.0), math.exp(-1.0), 0.0])
     np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ temperature, adaptive stop
+
+
+def test_tempered_entropy_two_point_closed_form():
+    # two logits a, b at temperature tau: p = 1 / (1 + exp((b - a) / tau)), H = binary entropy
+    for a, b, tau in [(1.0, 2.0, 0.5), (0.0, 3.0, 0.8), (-2.0, 1.5, 0.4), (4.0, 4.0, 0.6), (0.0, 1.0, 1.0)]:
+        p = 1.0 / (1.0 + math.exp((b - a) / tau))
+        want = -sum(q * math.log(q) for q in (p, 1.0 - p) if q > 0)
+        H, am = O.entropy_argmax(np.array([[a, b]]), tau)
+        assert abs(H[0] - want) < 1e-12
+        assert am[0] == (0 if a >= b else 1)
+
+
+def test_tempered_entropy_matches_torch_categorical_and_orders_by_tau():
+    x = rng(5).normal(0.0, 4.0, size=(6, 5000))
+    x[0, 17] += 40.0                              # a near-certain row
+    prev = None
+    for tau in (0.4, 0.6, 0.8, 1.0, 1.7):
+        H, a = O.entropy_argmax(x, tau)
+        ref = torch.distributions.Categorical(logits=torch.tensor(x) / tau).entropy().numpy()
+        np.testing.assert_allclose(H, ref, rtol=0, atol=1e-9)
+        np.testing.assert_array_equal(a, np.argmax(x, axis=1))   # the mode does not move with tau
+        if prev is not None:
+            assert np.all(H > prev)                # a hotter softmax is more uncertain
+        prev = H
+    # uniform rows stay uniform at any temperature
+    Hu, _ = O.entropy_argmax(np.zeros((2, 1000)), 0.4)
+    np.testing.assert_allclose(Hu, math.log(1000), atol=1e-12)
+
+
+def test_temperature_schedule_endpoints():
+    assert O.temperature(1.0, 0.8, 0.4) == 0.8
+    assert O.temperature(0.0, 0.8, 0.4) == 0.4
+    assert abs(O.temperature(0.25, 0.8, 0.4) - 0.5) < 1e-15
+    taus = [O.temperature(1.0 - s / 12, 0.8, 0.4) for s in range(12)]
+    assert all(x > y for x, y in zip(taus, taus[1:]))
+
+
+def test_adaptive_stop_brute_force():
+    H = np.array([0.001, 0.002, np.nan, 0.004], dtype=np.float32)
+    a = np.array([5, 6, -1, 7])
+    masked = [0, 1, 3]
+    assert O.adaptive_stop(H, a, np.array([5, 6, -1, 7]), masked, 0.005)
+    assert not O.adaptive_stop(H, a, np.array([5, 9, -1, 7]), masked, 0.005)   # a mode moved
+    assert not O.adaptive_stop(H, a, np.array([5, 6, -1, 7]), masked, 0.002)   # mean 0.00233
+    assert not O.adaptive_stop(H, a, a, [], 0.005)                             # nothing left
+    assert not O.adaptive_stop(H, a, np.full(4, -1), masked, 1e9)              # first step
+
+
+def test_sample_eb_adaptive_stop_commits_everything():
+    V, C = 300, 24
+    g = rng(8)
+    x = g.normal(0.0, 1.0, size=(1, C, V))
+    sharp = g.integers(0, V, size=C)
+    x[0, np.arange(C), sharp] += 60.0              # every row near-certain: H ~ 1e-23
+    canvas = np.full((1, C), V)
+    canvas[0, :4] = [1, 2, 3, 4]                   # committed positions stay
+    prev = np.full((1, C), -1)
+    prev[0, 4:] = sharp[4:]
+    new, H32, amax, nm, sel = O.sample_eb(x, canvas, 0.5, False, V, 1.0, 0.005, prev)
+    assert nm[0] == 0 and sorted(sel[0]) == list(range(4, C))
+    assert np.array_equal(new[0, 4:], sharp[4:]) and np.array_equal(new[0, :4], [1, 2, 3, 4])
+    prev[0, 9] = (sharp[9] + 1) % V                # one mode differs from the last step: no stop
+    new2, _, _, nm2, sel2 = O.sample_eb(x, canvas, 0.5, False, V, 1.0, 0.005, prev)
+    plain = O.sample_eb(x, canvas, 0.5, False, V)
+    assert sel2 == plain[4] and nm2[0] == C - 4 - len(sel2[0])
+
+
+def test_annealed_generate_reduces_to_plain_generate():
+    cfg = synth.CONFIGS["tiny"]
+    w = O.to_numpy_weights(synth.make_weights(cfg))
+    prompt = synth.make_prompt(cfg, 1, 16).numpy()
+    kv1, kv2 = O.KVCache(cfg, 1), O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, kv1, prompt)
+    O.prefill_kv(cfg, w, kv2, prompt)
+    plain = O.generate_block(cfg, w, kv1, 1, 3, 1.0, append=False)
+    ann, steps = O.generate_block_annealed(cfg, w, kv2, 1, 3, 1.0, 1.0, 1.0, -1.0, append=False)
+    assert np.array_equal(plain, ann) and steps[0] == 3
