@@ -259,15 +259,16 @@ def test_short_window_and_global_layers(tiny, global_every):
     eng.close()
 
 
-@pytest.mark.parametrize("e_stop", [0.005, 1e30])
-def test_generate_block_ex_equals_stepwise(tiny, e_stop):
+@pytest.mark.parametrize("e_stop,gamma", [(0.005, 1.0), (1e30, 1.0), (0.005, math.inf)])
+def test_generate_block_ex_equals_stepwise(tiny, e_stop, gamma):
     """dg_generate_block_ex == dg_denoise_step + dg_sample_eb_ex driven step by step (bitwise), with
     the temperature annealed 0.8 -> 0.4 and the adaptive stop (with e_stop 1e30 it fires at the
-    first step whose masked argmaxes all repeat)."""
+    first step whose masked argmaxes all repeat).  With gamma = inf the first step commits the
+    whole canvas and the four later steps must change nothing."""
     cfg, w_np, w_gpu, prompt = tiny
     V, C = cfg.vocab, cfg.canvas
-    steps, gamma, tmax, tmin = 5, 1.0, 0.8, 0.4
-    print(f"generate_block_ex e_stop={e_stop}", flush=True)
+    steps, tmax, tmin = 5, 0.8, 0.4
+    print(f"generate_block_ex e_stop={e_stop} gamma={gamma}", flush=True)
     logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
     nm = torch.empty(1, dtype=torch.int32, device="cuda")
     done = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -292,8 +293,10 @@ def test_generate_block_ex_equals_stepwise(tiny, e_stop):
     torch.cuda.synchronize()
     assert torch.equal(blk, canvas)
     assert done.item() == done_ref.item()
-    if e_stop == 0.005:
+    if e_stop == 0.005 and gamma == 1.0:
         assert done.item() == steps                 # random-init logits: H ~ log V, no early stop
+    if gamma == math.inf:
+        assert done.item() == 1
     assert 1 <= done.item() <= steps
     k1, v1 = eng.kv_view()
     k2, v2 = ref.kv_view()
