@@ -61,12 +61,19 @@ __device__ __forceinline__ void epilogue(const DenseArgs& a, int blk0, int m, co
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // packed block 2t = gate rows of features 16t.., block 2t+1 = the matching up rows
-    const int f0 = (blk0 >> 1) * 16 + 4 * g;
-    u32x2 o;
-    o.x = pack_bf2(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1]);
-    o.y = pack_bf2(silu(v[0][2]) * v[1][2], silu(v[0][3]) * v[1][3]);
-    *reinterpret_cast<u32x2*>(a.yb + fm_index(m, f0, a.ldy)) = o;
+    // packed block 2t = gate rows of features 16t.., block 2t+1 = the matching up rows;
+    // the tile's blocks (blk0 even) form WN / 2 such pairs, the last ones possibly past
+    // the matrix (their loads were clamped; nothing is written for them)
+    static_assert(WN % 2 == 0, "gate/up block pairs");
+#pragma unroll
+    for (int i = 0; i < WN; i += 2) {
+      if (blk0 + i + 1 >= a.nblk) break;
+      const int f0 = ((blk0 + i) >> 1) * 16 + 4 * g;
+      u32x2 o;
+      o.x = pack_bf2(silu(v[i][0]) * v[i + 1][0], silu(v[i][1]) * v[i + 1][1]);
+      o.y = pack_bf2(silu(v[i][2]) * v[i + 1][2], silu(v[i][3]) * v[i + 1][3]);
+      *reinterpret_cast<u32x2*>(a.yb + fm_index(m, f0, a.ldy)) = o;
+    }
   } else {  // EPI_QKV: rows were packed so that lane group g holds features
             // {p, p+1, p+hd/2, p+1+hd/2}, p = 8j + 2g, of head-local block j
     const int hd = a.hd, half = hd >> 1, per = hd >> 4;
@@ -231,7 +238,11 @@ void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int
   a.x = h; a.w = w_gate_up; a.M = M; a.K = K; a.N = 2 * F;
   a.nblk = 2 * (F / 16);
   a.yb = a_out; a.ldy = F;
-  run_dense<2, 4, EPI_SWIGLU>(a, s);
+  // 64-row weight tiles (two gate/up block pairs): one workgroup per CU at 348
+  // registers per lane, which leaves room on every CU for the routing kernels and
+  // the expert GEMMs that run beside this one (the 32-row tile at 232 registers put
+  // two workgroups on each CU and took the registers those kernels need)
+  run_dense<4, 4, EPI_SWIGLU>(a, s);
 }
 
 // ---------------------------------------------------------------- LM head
