@@ -1,7 +1,8 @@
 // Row-wise kernels: rotary/timestep tables, embedding gather (+ timestep
 // embedding) fused with the first RMSNorm, plain RMSNorm, and the MoE combine
-// fused with the residual add and the next RMSNorm.  One 256-thread workgroup
-// per token row; each thread moves 8 consecutive features (16 B of bf16).
+// fused with the residual add and the next RMSNorm.  One workgroup per token row
+// with one thread per 8 consecutive features (16 B of bf16), rounded up to whole
+// waves (row_threads), so each thread makes a single pass over its features.
 // The residual stream x is fp32 row-major; the normed output h is written in
 // fragment-major layout for the GEMMs that consume it.
 #include "dg_common.h"
@@ -78,7 +79,7 @@ __device__ __forceinline__ void norm_row(const float* xr, const float* gain, flo
   }
 }
 
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed,
+__global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed,
                                                          const float* temb, const float* gain,
                                                          float eps, float* x, uint16_t* h, int d,
                                                          int vocab) {
@@ -109,14 +110,17 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tokens, 
   norm_row(xr, gain, eps, h, m, d, ss, red);
 }
 
+// threads of a row workgroup: one per 8 features, whole waves, at most 1024
+static int row_threads(int d) { return std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64)); }
+
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s) {
-  launch_kernel(embed_norm_kernel, dim3(M), dim3(256), 0, s, nullptr, tokens, embed, temb, gain, eps, x, h, d,
+  launch_kernel(embed_norm_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, tokens, embed, temb, gain, eps, x, h, d,
                 vocab);
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const float* gain, float eps,
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* x, const float* gain, float eps,
                                                       uint16_t* h, uint16_t* h_rm, int d) {
   __shared__ float red[16];
   const int m = blockIdx.x;
@@ -135,7 +139,7 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
                     int d, hipStream_t s, hipEvent_t done) {
   // `done`, when given, is signalled by the kernel's own completion (no separate
   // marker on the stream)
-  launch_kernel(rmsnorm_kernel, dim3(M), dim3(256), 0, s, done, x, gain, eps, h, h_rm, d);
+  launch_kernel(rmsnorm_kernel, dim3(M), dim3(row_threads(d)), 0, s, done, x, gain, eps, h, h_rm, d);
 }
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]
@@ -145,7 +149,7 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
 // (zero on entry; it ends as the number of [MASK] rows), with rows_out[i] = m.
 // The order of the compacted rows varies from run to run; every logits row the
 // head computes from them does not depend on it.
-__global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys, const float* Y,
+__global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys, const float* Y,
                                                       const float* wts,
                                                       const int32_t* inv, int k, int d,
                                                       const float* next_gain, float eps,
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* x, const float* ys,
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
                     const int32_t* canvas, int mask_id, int32_t* rows_out, int32_t* count, hipStream_t s) {
-  launch_kernel(combine_kernel, dim3(M), dim3(256), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h,
+  launch_kernel(combine_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h,
                 canvas, mask_id, rows_out, count);
 }
 
