@@ -4,8 +4,10 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "dg.h"
@@ -31,10 +33,23 @@ struct dg_ctx {
   mutable Prof prof;
   // Side stream for the shared expert, which runs concurrently with the routed
   // experts' routing chain; forked from and joined back into the caller's stream
-  // with events.  Created on first use, on the device current at that time.
-  mutable hipStream_t side = nullptr;
-  mutable hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  mutable int side_dev = -1;
+  // with events.  Created by dg_create on the device current then (side_dev);
+  // calls made on another device keep all work on the caller's stream.  Calls
+  // from several threads may enqueue on it at once: each call forks and joins
+  // with an event pair of its own, and every item a call puts on the side stream
+  // waits only for work its own call enqueued earlier, so the calls serialise
+  // there without ever waiting on each other in a cycle.
+  hipStream_t side = nullptr;
+  int side_dev = -1;
+  // Fork/join event pairs, one per call in flight (taken at the start of a call,
+  // given back at its end; a pair given back may still be pending on the device,
+  // which is fine: a wait refers to the record that preceded it).
+  mutable std::mutex ev_mu;
+  mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_free;
+  mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_all;
+  // Forced routing (test tap, not thread-safe): when set, layer l of every pass
+  // takes its expert ids from force_ids + l * M * k instead of the router's top-k.
+  const int32_t* force_ids = nullptr;
 };
 
 namespace {
@@ -93,29 +108,43 @@ struct Timed {
     stmt;                                  \
   } while (0)
 
-// The side stream for the current device, or nullptr (work then stays on the
-// caller's stream) if it cannot be set up or the context moved to another device.
-hipStream_t side_stream(const dg_ctx* ctx) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  if (ctx->side) return ctx->side_dev == dev ? ctx->side : nullptr;
-  hipStream_t st = nullptr;
-  hipEvent_t a = nullptr, b = nullptr;
-  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  // both events only order work between two queues of this device: no system-scope
-  // (host-visibility) fence is needed when they are signalled
-  constexpr unsigned kFlags = hipEventDisableTiming | hipEventDisableSystemFence;
-  if (hipEventCreateWithFlags(&a, kFlags) != hipSuccess || hipEventCreateWithFlags(&b, kFlags) != hipSuccess) {
-    if (a) (void)hipEventDestroy(a);
-    (void)hipStreamDestroy(st);
-    return nullptr;
+// Fork/join events of one call: the side stream and an event pair for the current
+// device, or a null side stream (all work then stays on the caller's stream) when
+// the call runs on another device than the ctx's or the events cannot be made.
+struct SideFork {
+  const dg_ctx* ctx = nullptr;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  explicit SideFork(const dg_ctx* c) : ctx(c) {
+    int dev = -1;
+    if (!c->side || hipGetDevice(&dev) != hipSuccess || dev != c->side_dev) return;
+    std::lock_guard<std::mutex> lk(c->ev_mu);
+    if (c->ev_free.empty()) {
+      // both events only order work between two queues of this device: no
+      // system-scope (host-visibility) fence is needed when they are signalled
+      constexpr unsigned kFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreateWithFlags(&a, kFlags) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&b, kFlags) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
+      c->ev_all.emplace_back(a, b);
+      c->ev_free.emplace_back(a, b);
+    }
+    fork = c->ev_free.back().first;
+    join = c->ev_free.back().second;
+    c->ev_free.pop_back();
+    side = c->side;
   }
-  ctx->side = st;
-  ctx->ev_fork = a;
-  ctx->ev_join = b;
-  ctx->side_dev = dev;
-  return st;
-}
+  ~SideFork() {
+    if (!side) return;
+    std::lock_guard<std::mutex> lk(ctx->ev_mu);
+    ctx->ev_free.emplace_back(fork, join);
+  }
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+};
 
 constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
 constexpr int kPassCounters = 16;    // device counters cleared at the start of every pass
@@ -182,6 +211,8 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   const size_t qd = (size_t)c.n_q_heads * c.head_dim;
   const size_t P = (size_t)moe_max_slots((int)M, c.top_k, c.n_experts);
   Carver cv{base};
+  // first, so that its offset is the same for every batch (dg_workspace_moe_counts)
+  ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
   ws->x = cv.take<float>(M * c.d_model);
   ws->h = cv.take<uint16_t>(Mp * c.d_model);
   ws->h_rm = cv.take<uint16_t>(M * c.d_model);
@@ -200,7 +231,6 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->n_items = cv.take<int32_t>(1);
   ws->items2 = cv.take<int2>(moe_max_items2((int)M, c.top_k, c.n_experts));
   ws->n_items2 = cv.take<int32_t>(1);
-  ws->cnt_log = cv.take<int32_t>((size_t)c.n_layers * c.n_experts);
   ws->rows = cv.take<int32_t>(M);
   ws->counters = cv.take<int32_t>(kPassCounters);
   ws->A = cv.take<uint16_t>(round16(P) * c.expert_ffn);
@@ -266,6 +296,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
   const int d = c.d_model, hq = c.n_q_heads, hd = c.head_dim, E = c.n_experts, k = c.top_k;
   const float eps = c.rms_eps;
   const int nl = c.n_layers;
+  SideFork sf(ctx);
   DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr,
                                        ws.counters, kPassCounters, s));
   DG_TIMED(ctx, DG_K_EMBED,
@@ -285,19 +316,23 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     // reads h and writes As and ys, which nothing on this stream touches before
     // the join; the combine kernel adds ys.  The fork and join events are
     // signalled by the kernels' own completion (no marker packets on the queues).
-    hipStream_t s2 = side_stream(ctx);
+    hipStream_t s2 = sf.side;
     const bool fork = s2 != nullptr;
     if (!fork) s2 = s;
     DG_TIMED(ctx, DG_K_NORM,
-             launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, ws.h_rm, M, d, s, fork ? ctx->ev_fork : nullptr));
-    if (fork) (void)hipStreamWaitEvent(s2, ctx->ev_fork, 0);
+             launch_rmsnorm(ws.x, L.ffn_norm, eps, ws.h, ws.h_rm, M, d, s, fork ? sf.fork : nullptr));
+    if (fork) (void)hipStreamWaitEvent(s2, sf.fork, 0);
     DG_TIMED_ON(ctx, DG_K_SHARED_GATE_UP, s2,
                 launch_gemm_swiglu(ws.h, L.ws_gate_up, M, c.shared_ffn, d, ws.As, s2));
     DG_TIMED_ON(ctx, DG_K_SHARED_DOWN, s2,
                 launch_gemm_f32(ws.As, L.ws_down, ws.ys, M, d, c.shared_ffn, /*add=*/false, s2,
-                                fork ? ctx->ev_join : nullptr));
+                                fork ? sf.join : nullptr));
     DG_TIMED(ctx, DG_K_ROUTER, launch_gemm_f32(ws.h, L.w_router, ws.r, M, E, d, /*add=*/false, s));
-    DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
+    if (ctx->force_ids)
+      DG_TIMED(ctx, DG_K_TOPK,
+               launch_forced_route(ws.r, M, E, k, ctx->force_ids + (size_t)l * M * k, ws.ids, ws.wts, s));
+    else
+      DG_TIMED(ctx, DG_K_TOPK, launch_topk(ws.r, M, E, k, ws.ids, ws.wts, s));
     DG_TIMED(ctx, DG_K_ROUTE,
              launch_route(ws.ids, M, k, E, ws.cnt, ws.poff, ws.perm, ws.inv, ws.items, ws.n_items, ws.items2,
                           ws.n_items2,
@@ -309,7 +344,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_MOE_DOWN,
              launch_moe_down(ws.A, L.w_down, ws.cnt, ws.poff, ws.items2, ws.n_items2, moe_max_items2(M, k, E),
                              c.expert_ffn, d, ws.Y, s));
-    if (fork) (void)hipStreamWaitEvent(s, ctx->ev_join, 0);
+    if (fork) (void)hipStreamWaitEvent(s, sf.join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
     const bool compact = masked_head && g.denoise && l == nl - 1;
     DG_TIMED(ctx, DG_K_COMBINE,
@@ -440,6 +475,11 @@ const char* dg_status_string(dg_status s) {
 
 const char* dg_last_error(void) { return g_err.c_str(); }
 
+#ifndef DG_SOURCE_DIGEST
+#define DG_SOURCE_DIGEST "unstamped"
+#endif
+const char* dg_source_digest(void) { return DG_SOURCE_DIGEST; }
+
 dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out) {
   if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -458,6 +498,13 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out) {
   c->embed = w->embed;
   c->final_norm = w->final_norm;
   c->layers.assign(w->layers, w->layers + cfg->n_layers);
+  int dev = -1;
+  hipStream_t side = nullptr;
+  if (hipGetDevice(&dev) == hipSuccess && hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess) {
+    c->side = side;
+    c->side_dev = dev;
+  }
+  (void)hipGetLastError();   // no device (or no side stream) is not an error: work stays on one stream
   *out = c;
   return DG_OK;
 }
@@ -468,8 +515,10 @@ void dg_destroy(dg_ctx* ctx) {
   if (ctx->side) {
     (void)hipStreamSynchronize(ctx->side);
     (void)hipStreamDestroy(ctx->side);
-    (void)hipEventDestroy(ctx->ev_fork);
-    (void)hipEventDestroy(ctx->ev_join);
+  }
+  for (auto& e : ctx->ev_all) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
   }
   delete ctx;
 }
@@ -710,6 +759,12 @@ dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset) 
   Ws ws;
   carve(ctx->cfg, batch, reinterpret_cast<char*>(kAlign), &ws);   // offsets relative to an aligned base
   *offset = reinterpret_cast<uintptr_t>(ws.cnt_log) - kAlign;
+  return DG_OK;
+}
+
+dg_status dg_test_force_routing(dg_ctx* ctx, const int32_t* d_ids) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  ctx->force_ids = d_ids;
   return DG_OK;
 }
 

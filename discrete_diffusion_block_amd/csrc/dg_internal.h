@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dg.h"
 
 namespace dg {
@@ -52,6 +54,21 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_
   if (done && stop != done) (void)hipEventRecord(done, s);
 }
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per
+// device (the attribute is per device; each device gets its own bit).  Safe to call
+// from several threads: a second concurrent setter repeats an idempotent call.
+struct LdsLimit {
+  std::atomic<uint64_t> devices{0};
+};
+inline void raise_lds_limit(LdsLimit& st, const void* fn, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (st.devices.load(std::memory_order_acquire) & bit) return;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess)
+    st.devices.fetch_or(bit, std::memory_order_release);
+}
+
 // ---- embed / norm / prep ----
 // also clears zero[0 .. nzero)
 void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
@@ -92,6 +109,9 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
 
 // ---- MoE ----
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);
+// the given expert ids (forced [M][k]) in place of the top-k; weights from r
+void launch_forced_route(const float* r, int M, int E, int k, const int32_t* forced, int32_t* ids, float* w,
+                         hipStream_t s);
 constexpr int kMoeGroup = 64;        // tokens per work item of the routing test tap's list
 constexpr int kMoeGroup2 = 128;      // tokens per expert GEMM work item
 int moe_max_items(int M, int k, int E);

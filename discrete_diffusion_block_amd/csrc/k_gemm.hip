@@ -463,12 +463,8 @@ __global__ __launch_bounds__(256) void head_gemm(const uint16_t* __restrict__ x,
 void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits, int M, int N,
                       int K, const int32_t* count, const int32_t* rows, hipStream_t s) {
   constexpr size_t lds = (size_t)kHeadLds;
-  static bool raised = false;   // the ring exceeds the default dynamic-LDS limit
-  if (!raised) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&head_gemm),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    raised = true;
-  }
+  static LdsLimit limit;   // the ring exceeds the default dynamic-LDS limit
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&head_gemm), (int)lds);
   const int w_blocks = (N + 1 + 15) / 16;   // packed embedding rows: vocab + mask token, padded
   const int n_row = (N + 16 * kHeadRB - 1) / (16 * kHeadRB);
   const int n_tok = (M + 16 * kHeadTB - 1) / (16 * kHeadTB);

@@ -132,6 +132,38 @@ void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hi
                 ids, w);
 }
 
+// Routing with the experts given (a test tap): row m takes the k expert ids
+// forced[m][0..k) in that order; its weights are the softmax of the router logits
+// r[m][id] at those ids (taken against their largest, as in the top-k kernel).
+// One thread per row.
+__global__ __launch_bounds__(256) void forced_route_kernel(const float* __restrict__ r, int M, int E,
+                                                           int k, const int32_t* __restrict__ forced,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ w) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  float x[16];
+  float mx = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    const int e = min(max(forced[(size_t)m * k + j], 0), E - 1);
+    ids[(size_t)m * k + j] = e;
+    x[j] = r[(size_t)m * E + e];
+    mx = fmaxf(mx, x[j]);
+  }
+  float z = 0.f;
+  for (int j = 0; j < k; ++j) {
+    x[j] = expf(x[j] - mx);
+    z += x[j];
+  }
+  for (int j = 0; j < k; ++j) w[(size_t)m * k + j] = x[j] / z;
+}
+
+void launch_forced_route(const float* r, int M, int E, int k, const int32_t* forced, int32_t* ids, float* w,
+                         hipStream_t s) {
+  launch_kernel(forced_route_kernel, dim3((M + 255) / 256), dim3(256), 0, s, nullptr, r, M, E, k, forced, ids,
+                w);
+}
+
 // ---------------------------------------------------------------- permutation
 
 // Stable counting sort of the A = M*k assignments (a = m*k + j) by expert, by one
@@ -509,12 +541,8 @@ void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_
                         const int32_t* cnt, const int32_t* poff, const int2* items2,
                         const int32_t* n_items2, int max_items2, int F, int d, uint16_t* a,
                         hipStream_t s) {
-  static bool raised = false;
-  if (!raised) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kGuLds);
-    raised = true;
-  }
+  static LdsLimit limit;
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&moe_gate_up_kernel), kGuLds);
   const int blocks = kXcd * ((max_items2 + kXcd - 1) / kXcd) * (F / (16 * kGuRB / 2));
   launch_kernel(moe_gate_up_kernel, dim3(blocks), dim3(64 * kGuWaves), kGuLds, s, nullptr, h_rm, perm,
                 w_gate_up, cnt, poff, items2, n_items2, F, d, a);

@@ -15,6 +15,7 @@ from typing import Optional
 
 import torch
 
+from .build import source_digest
 from .synth import ModelConfig, LAYER_KEYS
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
@@ -86,6 +87,7 @@ def lib():
             "dg_profile_end": [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
             "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
             "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
+            "dg_test_force_routing": [vp, vp],
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
             "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
@@ -99,6 +101,12 @@ def lib():
         L.dg_status_string.restype = C.c_char_p
         L.dg_last_error.argtypes = []
         L.dg_last_error.restype = C.c_char_p
+        L.dg_source_digest.argtypes = []
+        L.dg_source_digest.restype = C.c_char_p
+        built, here = L.dg_source_digest().decode(), source_digest()
+        if built != here:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (digest {built}, tree {here}): "
+                               "rebuild it with discrete_diffusion_block_amd.build")
         _lib = L
     return _lib
 
@@ -279,6 +287,12 @@ def dg_workspace_moe_counts(ctx, batch: int) -> int:
     off = C.c_size_t()
     _check(lib().dg_workspace_moe_counts(ctx, batch, C.byref(off)))
     return off.value
+
+
+def dg_test_force_routing(ctx, ids: Optional[torch.Tensor]):
+    """ids: int32 device tensor [n_layers][M][top_k] (the expert ids each layer of the
+    following passes uses), or None to restore the router."""
+    _check(lib().dg_test_force_routing(ctx, _p(ids)))
 
 
 def dg_test_router_topk(r: torch.Tensor, k: int, ids: torch.Tensor, w: torch.Tensor, stream=None):

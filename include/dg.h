@@ -20,8 +20,15 @@
  *    thread-local detail string).
  *  - Token ids are int32; [MASK] = vocab.  Canvas tokens that are not [MASK]
  *    are committed and are never changed by any call.
- *  - A dg_ctx is immutable after dg_create and may be shared by threads; calls
- *    that run concurrently need distinct workspaces and KV caches.
+ *  - Threads: a dg_ctx may be shared by threads once dg_create has returned.
+ *    Calls that run concurrently need distinct workspaces and KV caches (and
+ *    their own logits/canvas buffers); each call forks the shared expert onto the
+ *    ctx's side stream with a fork/join event pair of its own (taken from a
+ *    mutex-guarded pool), so concurrent calls serialise on that stream but never
+ *    share an event.  The measurement helpers (dg_profile_*) and the test taps
+ *    that change a ctx (dg_test_force_routing) are not thread-safe.
+ *  - Device: a ctx belongs to the device current at dg_create (its weights live
+ *    there); call it with that device current.
  */
 #ifndef DG_H
 #define DG_H
@@ -121,8 +128,10 @@ typedef struct dg_kv {
 typedef struct dg_ctx dg_ctx;
 
 /* Create an engine for cfg with the given weights (pointers are borrowed; the
- * dg_layer_weights array itself is copied).  Validates shapes.  Allocates only
- * the ctx's host-side state. */
+ * dg_layer_weights array itself is copied).  Validates shapes.  Allocates the
+ * ctx's host-side state and creates its side stream on the current device (no
+ * device memory); without a usable device it still succeeds and every call then
+ * keeps all work on the caller's stream. */
 dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out);
 void dg_destroy(dg_ctx* ctx);
 
@@ -133,6 +142,10 @@ dg_status dg_kv_size(const dg_config* cfg, size_t* bytes_each);
 
 const char* dg_status_string(dg_status s);
 const char* dg_last_error(void);
+/* Digest of the sources this library was built from (16 hex digits; "unstamped"
+ * when the build did not define it).  The Python binding compares it with the
+ * sources next to it and refuses a library built from others. */
+const char* dg_source_digest(void);
 
 /* Causal encoder pass (DiffusionGemma Technical Report §3.1, context encoding
  * into the KV cache, eq. 3; and the append of a finished canvas, eq. 4).
@@ -246,6 +259,16 @@ dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count);
 dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset);
 
 /* ---- kernel taps for tests (not part of the stable contract) ---- */
+
+/* Teacher-forced routing: while d_ids is not NULL, layer l of every pass through
+ * ctx takes the expert ids d_ids[l][m][0..top_k) (int32 [n_layers][M][top_k],
+ * M = batch * tokens of each following pass -- the caller gives one array per
+ * pass, so a prefill must fit one pass: at most max(canvas, 512) tokens) in that
+ * order instead of the router's top-k; the weights are still the softmax of the
+ * engine's own router logits at those ids.  Ids are clamped to [0, E).  NULL
+ * restores the router.  For parity tests that must not depend on near-tied
+ * routing decisions; not thread-safe. */
+dg_status dg_test_force_routing(dg_ctx* ctx, const int32_t* d_ids);
 
 /* Router selection alone: r fp32 [M][E] (E a multiple of 4 in [4, 256], rows
  * 16-byte aligned) -> ids int32 [M][k] (by logit desc, id asc) and weights fp32
