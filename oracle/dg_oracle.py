@@ -324,6 +324,122 @@ def entropy_argmax(rows: np.ndarray, tau: float = 1.0):
     return -np.sum(plogp, axis=-1), a
 
 
+# --------------------------------------------------------------------------------------
+# Canonical decision entropy
+# --------------------------------------------------------------------------------------
+#
+# The entropy-bounded sampler (DiffusionGemma Technical Report §3.3) turns entropies
+# into an integer decision: the order of the masked positions and the point where the
+# running entropy sum passes the budget.  Two correct float implementations of
+# -sum p log p (different exp/log code, different summation order) differ in the last
+# bits, so the decision is taken on one canonical value: Ĥ, a fixed function of the
+# row's bf16 logits built only from IEEE float64 add, subtract, multiply, divide,
+# round-to-nearest-even, exact power-of-two scaling and integer addition, each in a
+# fixed order, so that any implementation that follows it gets the same bits.
+#   1. m = max of the row; u_v = (m - x_v) * (1 / tau)   (float64; tau as float32)
+#   2. e_v = exp(-u_v), evaluated as: k = rint(u / ln2);
+#      r = (u - k ln2_hi) - k ln2_lo (Cody and Waite's two-part reduction, ln2_hi with
+#      enough trailing zero bits that k ln2_hi is exact); e^-r by the Taylor series
+#      sum_{i<=12} (-r)^i / i! in Horner form (one rounding per multiply and per add);
+#      e = that * 2^-k.  Terms with u >= 30 are 0.
+#   3. s_v = rint(e_v 2^40), t_v = rint((e_v u_v) 2^40), summed exactly as integers
+#      (order-independent): S = sum s_v, T = sum t_v.  The dropped fraction is at most
+#      V 2^-41 <= 1.2e-7 of the leading term.
+#   4. Ĥ = float32(max(0, (log(S) - 40 ln2) + T / S)), with S and T converted to
+#      float64 as hi * 2^32 + lo (one rounding), and log(a) = j ln2 + 2 atanh(s) for
+#      a = f 2^j, f in [sqrt(1/2), sqrt(2)), s = (f - 1) / (f + 1), atanh by its series
+#      s (1 + z/3 + z^2/5 + ... + z^12/25), z = s^2, in Horner form.
+# |Ĥ - H| stays below ~3e-6 for V <= 2^23 (quantisation 1.2e-7 relative in S and T,
+# the u >= 30 tail V e^-30 (1 + 30) <= 8e-7, the float32 rounding of the result
+# <= 8e-7); the pins check it against -sum p log p.
+
+def _from_decimal(x) -> float:
+    return float(x)          # Decimal -> float is correctly rounded
+
+
+def _canon_constants():
+    from decimal import Context, Decimal
+    from fractions import Fraction
+    ctx = Context(prec=80)
+    ln2 = Decimal(2).ln(ctx)
+    ln2_d = _from_decimal(ln2)
+    # ln2_hi: ln 2 truncated to 32 significant bits (21 trailing zero bits of the
+    # 53-bit significand), so k * ln2_hi is exact for every k < 2^21
+    mant, exp = math.frexp(ln2_d)
+    hi = math.ldexp(math.floor(math.ldexp(mant, 32)), exp - 32)
+    lo = _from_decimal(ctx.subtract(ln2, Decimal(hi)))
+    inv_ln2 = _from_decimal(ctx.divide(Decimal(1), ln2))
+    sqrt_half = _from_decimal(Decimal("0.5").sqrt(ctx))
+    exp_c = [float(Fraction(1, math.factorial(i))) for i in range(13)]
+    log_c = [float(Fraction(1, 2 * i + 1)) for i in range(13)]
+    return ln2_d, hi, lo, inv_ln2, sqrt_half, exp_c, log_c
+
+
+_LN2, _LN2_HI, _LN2_LO, _INV_LN2, _SQRT_HALF, _EXP_C, _LOG_C = _canon_constants()
+_CANON_UMAX = 30.0
+_CANON_Q = 2.0 ** 40
+
+
+def canon_exp_neg(u: np.ndarray) -> np.ndarray:
+    """e^-u for float64 u >= 0 by the fixed sequence of step 2 above (0 for u >= 30)."""
+    u = np.asarray(u, dtype=np.float64)
+    k = np.rint(u * _INV_LN2)
+    r = (u - k * _LN2_HI) - k * _LN2_LO
+    y = -r
+    p = np.full_like(y, _EXP_C[12])
+    for c in reversed(_EXP_C[:12]):
+        p = p * y
+        p = p + c
+    e = np.ldexp(p, -np.clip(k, 0, 2000).astype(np.int64))
+    return np.where(u < _CANON_UMAX, e, 0.0)
+
+
+def canon_log(a: np.ndarray) -> np.ndarray:
+    """Natural log of float64 a >= 1 by the fixed sequence of step 4 above."""
+    a = np.asarray(a, dtype=np.float64)
+    f, j = np.frexp(a)
+    low = f < _SQRT_HALF
+    f = np.where(low, f * 2.0, f)
+    j = np.where(low, j - 1, j).astype(np.float64)
+    s = (f - 1.0) / (f + 1.0)
+    z = s * s
+    p = np.full_like(z, _LOG_C[12])
+    for c in reversed(_LOG_C[:12]):
+        p = p * z
+        p = p + c
+    return j * _LN2 + (2.0 * s) * p
+
+
+def _u64_to_f64(v: np.ndarray) -> np.ndarray:
+    v = np.asarray(v, dtype=np.uint64)
+    hi = (v >> np.uint64(32)).astype(np.float64)
+    lo = (v & np.uint64(0xFFFFFFFF)).astype(np.float64)
+    return hi * 4294967296.0 + lo
+
+
+def entropy_canonical_sums(rows: np.ndarray, tau: float = 1.0):
+    """Steps 1-3 above: the exact integer sums (S, T) per row (uint64)."""
+    x = np.asarray(rows, dtype=np.float64)
+    m = np.max(x, axis=-1, keepdims=True)
+    inv = 1.0 / float(np.float32(tau))
+    u = (m - x) * inv
+    e = canon_exp_neg(u)
+    qs = np.rint(e * _CANON_Q).astype(np.uint64)
+    qt = np.rint((e * u) * _CANON_Q).astype(np.uint64)
+    return qs.sum(axis=-1, dtype=np.uint64), qt.sum(axis=-1, dtype=np.uint64)
+
+
+def entropy_canonical(rows: np.ndarray, tau: float = 1.0) -> np.ndarray:
+    """The canonical decision entropy Ĥ (float32) of each row of bf16 logits at
+    temperature tau; see the steps above.  V must stay below 2^23."""
+    rows = np.asarray(rows, dtype=np.float64)
+    assert rows.shape[-1] < (1 << 23)
+    S, T = entropy_canonical_sums(rows, tau)
+    Sf, Tf = _u64_to_f64(S), _u64_to_f64(T)
+    h = (canon_log(Sf) - 40.0 * _LN2) + Tf / Sf
+    return np.maximum(h, 0.0).astype(np.float32)
+
+
 def eb_select(H32: np.ndarray, masked: List[int], gamma: float, commit_all: bool) -> List[int]:
     """Entropy-bounded selection (DiffusionGemma Technical Report §3.3).
 
@@ -358,11 +474,15 @@ def adaptive_stop(H32: np.ndarray, amax: np.ndarray, prev_amax: np.ndarray, mask
     """Technical Report §3.3, adaptive stopping, on the masked rows of one canvas (the only
     rows the absorbing sampler predicts): true when their mean entropy is below e_stop and
     every one of them has the same most likely token as at the previous step.  The mean
-    is the exactly rounded float64 sum of the float32 entropies divided by their number."""
+    is the float64 running sum of the float32 entropies in position order, divided by
+    their number (a fixed order, so that the decision is reproducible bit for bit)."""
     if not masked:
         return False
-    mean = math.fsum(float(np.float32(H32[i])) for i in masked) / len(masked)
-    return mean < e_stop and all(int(amax[i]) == int(prev_amax[i]) for i in masked)
+    acc = 0.0
+    for i in sorted(masked):
+        acc += float(np.float32(H32[i]))
+    mean = acc / len(masked)
+    return mean < float(np.float32(e_stop)) and all(int(amax[i]) == int(prev_amax[i]) for i in masked)
 
 
 def sample_eb(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: bool,
@@ -373,9 +493,10 @@ def sample_eb(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: 
     Returns (new_canvas, H32 [B][C] (NaN on unmasked rows), argmax [B][C] (-1 on
     unmasked rows), n_masked [B] after the commit, committed list per batch).
     Committed tokens are never revised: only [MASK] rows are read or written.
-    Entropies are taken at temperature tau.  With e_stop given, a sequence whose masked
-    rows pass adaptive_stop against prev_amax [B][C] (the previous step's argmax, -1
-    where there was none) commits all of them.
+    Entropies are taken at temperature tau; the decisions (order, budget, stop) use the
+    canonical entropy Ĥ (entropy_canonical), which H32 holds.  With e_stop given, a
+    sequence whose masked rows pass adaptive_stop against prev_amax [B][C] (the previous
+    step's argmax, -1 where there was none) commits all of them.
     """
     canvas = np.array(canvas, dtype=np.int64, copy=True)
     B, C = canvas.shape
@@ -386,9 +507,9 @@ def sample_eb(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: 
     for b in range(B):
         masked = [i for i in range(C) if canvas[b, i] == mask_id]
         if masked:
-            H, a = entropy_argmax(logits[b, masked], tau)
-            H32[b, masked] = H.astype(np.float32)
-            amax[b, masked] = a
+            rows = np.asarray(logits[b, masked], dtype=np.float64)
+            H32[b, masked] = entropy_canonical(rows, tau)
+            amax[b, masked] = np.argmax(rows, axis=-1)
         stop = e_stop is not None and adaptive_stop(H32[b], amax[b], prev_amax[b], masked, e_stop)
         sel = eb_select(H32[b], masked, gamma, commit_all or stop)
         for i in sel:

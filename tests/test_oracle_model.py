@@ -47,14 +47,23 @@ def _rope_complex(x, pos, theta):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def _dense_block(x, pos, lw, cfg, prefix_kv, causal):
+def _bf(t):
+    """torch's own float -> bfloat16 cast (round to nearest even), back to float64."""
+    return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def _dense_block(x, pos, lw, cfg, prefix_kv, causal, rnd=False):
+    """One pre-norm block from torch routines.  rnd: values the engine stores in bf16
+    (normed state, post-RoPE q and k, v, attention output, the SwiGLU activations) go
+    through torch's bf16 cast at those points."""
+    R = _bf if rnd else (lambda t: t)
     d, hq, hkv, hd = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     n = x.shape[0]
-    h = F.rms_norm(x, (d,), _t(lw["attn_norm"]), eps=cfg.rms_eps)
+    h = R(F.rms_norm(x, (d,), _t(lw["attn_norm"]), eps=cfg.rms_eps))
     qkv = h @ _t(lw["w_qkv"]).T
-    q = _rope_complex(qkv[:, :hq * hd].reshape(n, hq, hd), pos, cfg.rope_theta)
-    k = _rope_complex(qkv[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), pos, cfg.rope_theta)
-    v = qkv[:, (hq + hkv) * hd:].reshape(n, hkv, hd)
+    q = R(_rope_complex(qkv[:, :hq * hd].reshape(n, hq, hd), pos, cfg.rope_theta))
+    k = R(_rope_complex(qkv[:, hq * hd:(hq + hkv) * hd].reshape(n, hkv, hd), pos, cfg.rope_theta))
+    v = R(qkv[:, (hq + hkv) * hd:].reshape(n, hkv, hd))
     K = torch.cat([prefix_kv[0], k]) if prefix_kv is not None else k
     V = torch.cat([prefix_kv[1], v]) if prefix_kv is not None else v
     if causal:
@@ -64,40 +73,47 @@ def _dense_block(x, pos, lw, cfg, prefix_kv, causal):
         mask = None
     o = F.scaled_dot_product_attention(q.permute(1, 0, 2)[None], K.permute(1, 0, 2)[None],
                                        V.permute(1, 0, 2)[None], attn_mask=mask, enable_gqa=True)
-    x = x + o[0].permute(1, 0, 2).reshape(n, -1) @ _t(lw["w_o"]).T
-    h2 = F.rms_norm(x, (d,), _t(lw["ffn_norm"]), eps=cfg.rms_eps)
+    x = x + R(o[0].permute(1, 0, 2).reshape(n, -1)) @ _t(lw["w_o"]).T
+    h2 = R(F.rms_norm(x, (d,), _t(lw["ffn_norm"]), eps=cfg.rms_eps))
     f, fs = cfg.expert_ffn, cfg.shared_ffn
     wgu, wd = _t(lw["w_gate_up"][0]), _t(lw["w_down"][0])
-    y = (F.silu(h2 @ wgu[:f].T) * (h2 @ wgu[f:].T)) @ wd.T
+    y = R(F.silu(h2 @ wgu[:f].T) * (h2 @ wgu[f:].T)) @ wd.T
     sgu, sd = _t(lw["ws_gate_up"]), _t(lw["ws_down"])
-    y = y + (F.silu(h2 @ sgu[:fs].T) * (h2 @ sgu[fs:].T)) @ sd.T
+    y = y + R(F.silu(h2 @ sgu[:fs].T) * (h2 @ sgu[fs:].T)) @ sd.T
     return x + y, k, v
 
 
-def test_single_expert_model_matches_dense_torch_reference():
+@pytest.mark.parametrize("rnd", [False, True])
+def test_single_expert_model_matches_dense_torch_reference(rnd):
+    """rnd=True pins where the oracle rounds to bf16: the same torch reference with
+    torch's bf16 cast at the engine's storage points.  Moving a rounding point (for
+    example rounding q and k before RoPE instead of after) changes the logits by
+    ~1e-3, far outside the 1e-9 bound."""
     cfg = cfg_small(n_experts=1, top_k=1, window=64)
     w = weights(cfg)
     prompt = np.array([[3, 17, 60, 1, 9]])
     canvas = np.array([[64, 64, 5, 64, 2, 64]])
     t = 0.625
     kv = O.KVCache(cfg, 1)
-    O.prefill_kv(cfg, w, kv, prompt, rnd=False)
-    logits = O.denoise_step(cfg, w, kv, canvas, t, rnd=False)
+    O.prefill_kv(cfg, w, kv, prompt, rnd=rnd)
+    logits = O.denoise_step(cfg, w, kv, canvas, t, rnd=rnd)
 
     # reference: causal pass over the prompt, then the canvas with temb at positions P..P+C-1
     P, C = 5, 6
     x = _t(w["embed"][prompt[0]])
     cache = []
     for l in range(cfg.n_layers):
-        x, k, v = _dense_block(x, list(range(P)), w["layers"][l], cfg, None, causal=True)
+        x, k, v = _dense_block(x, list(range(P)), w["layers"][l], cfg, None, causal=True, rnd=rnd)
         cache.append((k, v))
     half = cfg.d_model // 2
     f = 10000.0 ** (-torch.arange(half, dtype=torch.float64) / half)
     temb = torch.cat([torch.sin(1000 * t * f), torch.cos(1000 * t * f)])
     x = _t(w["embed"][canvas[0]]) + temb
     for l in range(cfg.n_layers):
-        x, _, _ = _dense_block(x, list(range(P, P + C)), w["layers"][l], cfg, cache[l], causal=False)
+        x, _, _ = _dense_block(x, list(range(P, P + C)), w["layers"][l], cfg, cache[l], causal=False, rnd=rnd)
     hf = F.rms_norm(x, (cfg.d_model,), _t(w["final_norm"]), eps=cfg.rms_eps)
+    if rnd:
+        hf = _bf(hf)
     ref = hf @ _t(w["embed"][:cfg.vocab]).T
     np.testing.assert_allclose(logits[0], ref.numpy(), rtol=1e-9, atol=1e-11)
     for l in range(cfg.n_layers):

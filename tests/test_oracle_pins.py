@@ -420,3 +420,74 @@ def test_annealed_generate_reduces_to_plain_generate():
     plain = O.generate_block(cfg, w, kv1, 1, 3, 1.0, append=False)
     ann, steps = O.generate_block_annealed(cfg, w, kv2, 1, 3, 1.0, 1.0, 1.0, -1.0, append=False)
     assert np.array_equal(plain, ann) and steps[0] == 3
+
+
+def _annealed_loop(cfg, w, kv, steps, gamma, tau_max, tau_min, e_stop):
+    """The Technical Report's sampler (§3.3) on the absorbing canvas, written out step by
+    step from its parts: t_s = 1 - s/N, tau_s linear in t_s from tau_max (t = 1) to
+    tau_min (t = 0), decisions on the canonical entropy, the stop (mean entropy of the
+    masked rows below e_stop and every argmax as at the previous step) committing all,
+    the last step committing all."""
+    V, C = cfg.vocab, cfg.canvas
+    canvas = np.full(C, V)
+    prev = np.full(C, -1)
+    done, taus = 0, []
+    for s in range(steps):
+        t = 1.0 - s / steps
+        tau = tau_min + (tau_max - tau_min) * t
+        taus.append(tau)
+        logits = O.bf16(O.denoise_step(cfg, w, kv, canvas[None], t))[0]
+        masked = [i for i in range(C) if canvas[i] == V]
+        H = np.full(C, np.nan, np.float32)
+        a = np.full(C, -1)
+        if masked:
+            H[masked] = O.entropy_canonical(logits[masked], tau)
+            a[masked] = np.argmax(logits[masked], axis=1)
+        acc = 0.0
+        for i in masked:
+            acc += float(H[i])
+        stop = bool(masked) and acc / len(masked) < float(np.float32(e_stop)) and \
+            all(a[i] == prev[i] for i in masked)
+        order = sorted(masked, key=lambda i: (float(H[i]), i))
+        if s == steps - 1 or stop:
+            chosen = order
+        else:
+            run, chosen = 0.0, []
+            for i in order:
+                run += float(H[i])
+                if run > float(np.float32(gamma)):
+                    break
+                chosen.append(i)
+            chosen = chosen or order[:1]
+        for i in chosen:
+            canvas[i] = a[i]
+        if not done and not np.any(canvas == V):
+            done = s + 1
+        prev = a
+    return canvas, done, taus
+
+
+@pytest.mark.parametrize("e_stop,gamma,steps", [(1e30, 1.0, 48), (-1.0, 3.0 * 8.27, 6)])
+def test_annealed_generator_vs_independent_loop(e_stop, gamma, steps):
+    """tau annealed 0.8 -> 0.4 (not 1) with the stop on (e_stop 1e30: it fires at the first
+    step whose masked argmaxes all repeat; with the pages' budget of 48 steps consecutive
+    steps move t little enough for that to happen) or off with a budget of ~3 rows per
+    step."""
+    cfg = synth.CONFIGS["tiny"]
+    w = O.to_numpy_weights(synth.make_weights(cfg))
+    prompt = synth.make_prompt(cfg, 1, 16).numpy()
+    kv1, kv2 = O.KVCache(cfg, 1), O.KVCache(cfg, 1)
+    O.prefill_kv(cfg, w, kv1, prompt)
+    O.prefill_kv(cfg, w, kv2, prompt)
+    rec = []
+    got, done = O.generate_block_annealed(cfg, w, kv1, 1, steps, gamma, 0.8, 0.4, e_stop, append=False,
+                                          record=rec)
+    want, want_done, taus = _annealed_loop(cfg, w, kv2, steps, gamma, 0.8, 0.4, e_stop)
+    np.testing.assert_array_equal(got[0], want)
+    assert done[0] == want_done
+    np.testing.assert_allclose([r["tau"] for r in rec], taus, rtol=0, atol=1e-15)
+    assert taus[0] == pytest.approx(0.8) and taus[-1] == pytest.approx(0.4 + 0.4 / steps)
+    if e_stop > 1.0:
+        assert 1 < want_done < steps          # the stop fired, before the last step
+    else:
+        assert want_done == steps and len(rec[0]["committed"][0]) >= 2
