@@ -179,6 +179,10 @@ struct Ws {
   float* ys;       // shared-expert output fp32 row-major [M][d]
   float4* part;
   int* part_arg;
+  ulonglong2* cpart;   // canonical-entropy integer chunk sums
+  int32_t* sflag;      // [batch]: sequence deferred to the canonical entropy
+  int32_t* smoved;     // [batch]
+  int32_t* samax;      // [batch][C]
 };
 
 struct Carver {
@@ -199,6 +203,10 @@ size_t carve_sampler(Carver& cv, int batch, int canvas, int vocab, Ws* ws) {
   const size_t rows = (size_t)batch * canvas;
   ws->part = cv.take<float4>(rows * sample_chunks(vocab));
   ws->part_arg = cv.take<int>(rows * sample_chunks(vocab));
+  ws->cpart = cv.take<ulonglong2>(rows * sample_chunks(vocab));
+  ws->sflag = cv.take<int32_t>(batch);
+  ws->smoved = cv.take<int32_t>(batch);
+  ws->samax = cv.take<int32_t>(rows);
   return cv.off;
 }
 
@@ -452,7 +460,16 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
            launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
                             canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax,
-                            o.e_stop, o.step, o.done_step, s));
+                            o.e_stop, o.step, o.done_step, ws.sflag, ws.smoved, ws.samax, s));
+  // sequences whose decision the fast entropies could not certify: canonical entropy
+  // (every workgroup of a decided sequence returns at once)
+  DG_TIMED(ctx, DG_K_SAMPLE_CANON,
+           launch_canon_partials(d_logits, d_canvas, batch, canvas, vocab, o.temperature, ws.part, ws.sflag,
+                                 ws.cpart, s));
+  DG_TIMED(ctx, DG_K_SAMPLE_SELECT_CANON,
+           launch_eb_select_canon(ws.cpart, sample_chunks(vocab), d_canvas, batch, canvas, vocab, gamma,
+                                  commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax, o.e_stop, o.step,
+                                  o.done_step, ws.sflag, ws.smoved, ws.samax, s));
   return check_launch("sampler");
 }
 
@@ -796,7 +813,8 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
       vocab < 1 || gamma != gamma)
     return fail(DG_ERR_INVALID_ARG, "bad selection arguments");
   launch_eb_select(nullptr, nullptr, 0, d_entropy, d_argmax, d_canvas, batch, canvas, vocab, gamma,
-                   commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, (hipStream_t)stream);
+                   commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, nullptr, nullptr,
+                   nullptr, (hipStream_t)stream);
   return check_launch("eb select");
 }
 

@@ -143,14 +143,29 @@ constexpr int kSampleChunk = 16384;  // logits per workgroup in the first sample
 // inv_tau = 1 / sampling temperature (1 = the plain distribution)
 void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
                             float inv_tau, float4* part, int* part_arg, hipStream_t s);
-// prev_amax (optional, [batch][C] in/out): the previous step's argmax, for the
-// adaptive stop at e_stop; done_step (optional, [batch]): set to step + 1 where it is
-// 0 and the call leaves no [MASK] row
+// Pass 2: merge the chunk partials (part given) or take the given entropies and
+// argmaxes (H_in / amax_in), rank, and commit.  prev_amax (optional, [batch][C]
+// in/out): the previous step's argmax, for the adaptive stop at e_stop; done_step
+// (optional, [batch]): set to step + 1 where it is 0 and the call leaves no [MASK]
+// row.  With part given and flag non-NULL, a sequence whose decision is not
+// certified under the fast entropies' error bound is left undecided: flag[b] = 1,
+// moved[b] = its count of moved argmaxes, amax_ws = its argmaxes (for the canonical
+// passes below); decided sequences get flag[b] = 0.
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                      hipStream_t s);
+                      int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s);
+// Pass 3: exact integer sums of the canonical entropy for the masked rows of the
+// flagged sequences (tau: the temperature; part: pass 1's partials, for the row max).
+void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
+                           float tau, const float4* part, const int32_t* flag, ulonglong2* cpart,
+                           hipStream_t s);
+// Pass 4: the decision of the flagged sequences on the canonical entropy.
+void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
+                            float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
+                            int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
+                            int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

@@ -135,15 +135,28 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(const uint16_t* __re
     }
     l_part = l_part * alpha + ps;
     m_run = m_new;
-    u32x4 pb;
-    pb.x = pack_bf2(p[0], p[1]);
-    pb.y = pack_bf2(p[2], p[3]);
-    pb.z = pack_bf2(p[4], p[5]);
-    pb.w = pack_bf2(p[6], p[7]);
+    // P enters the bf16 PV product as a pair: hi = bf16(P), lo = bf16(P - hi), so the
+    // product carries P to ~2^-17 relative (a single bf16 P would add a 2^-9 error to every
+    // probability, which near-uniform attention does not average away)
+    u32x4 pb, pl;
+    {
+      float lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo[e] = p[e] - bf2f(f2bf(p[e]));
+      pb.x = pack_bf2(p[0], p[1]);
+      pb.y = pack_bf2(p[2], p[3]);
+      pb.z = pack_bf2(p[4], p[5]);
+      pb.w = pack_bf2(p[6], p[7]);
+      pl.x = pack_bf2(lo[0], lo[1]);
+      pl.y = pack_bf2(lo[2], lo[3]);
+      pl.z = pack_bf2(lo[4], lo[5]);
+      pl.w = pack_bf2(lo[6], lo[7]);
+    }
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
       acc[hb] *= alpha;
       acc[hb] = mfma16(Vt[hb], pb, acc[hb]);
+      acc[hb] = mfma16(Vt[hb], pl, acc[hb]);
     }
   };
   const int nsteps = w < nchunk ? (nchunk - w + NW - 1) / NW : 0;

@@ -11,7 +11,14 @@
 // [MASK] are skipped.
 // Pass 2 (one workgroup per sequence) merges the chunks of each row in index
 // order, H = log S + T / S, ranks the masked rows by (H, position), takes the
-// running fp64 sum in rank order, and commits the argmax of the first k* rows.
+// running fp64 sum in rank order, and commits the argmax of the first k* rows --
+// when that decision is certified: no entropy gap or running sum that decides it
+// lies within the fast pass's error bound of the boundary.  Otherwise the sequence
+// is deferred to the canonical entropy Ĥ (a fixed sequence of IEEE float64
+// operations and exact integer sums, reproducible bit for bit by any implementation
+// that follows it): pass 3 computes its integer sums for the deferred sequences'
+// masked rows only, and pass 4 takes their decision on Ĥ.  Either way the committed
+// set is the one the rule gives on Ĥ.
 #include <math.h>
 
 #include "dg_common.h"
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
   if (tid == 0) {
     const float4 p0 = wsum[0], p1 = wsum[1], p2 = wsum[2], p3 = wsum[3];
     part[(size_t)row * nchunks + ch] =
-        make_float4(M * inv_tau, (p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y), 0.f);
+        make_float4(M * inv_tau, (p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y), M);
     part_arg[(size_t)row * nchunks + ch] =
         min(min(__float_as_int(p0.z), __float_as_int(p1.z)), min(__float_as_int(p2.z), __float_as_int(p3.z)));
   }
@@ -164,38 +171,213 @@ __device__ __forceinline__ uint64_t eb_key(float H, int row) {
   return (uint64_t)o << 32 | (uint32_t)row;
 }
 
-template <int TPR>   // threads per canvas row (chunk merge and rank count)
-__global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restrict__ part,
-                                                         const int* __restrict__ part_arg,
-                                                         int nchunks, const float* __restrict__ H_in,
-                                                         const int32_t* __restrict__ amax_in,
-                                                         int32_t* __restrict__ canvas, int C,
-                                                         int vocab, float gamma, int commit_all,
-                                                         float* __restrict__ H_out,
-                                                         int32_t* __restrict__ amax_out,
-                                                         int32_t* __restrict__ n_masked,
-                                                         int32_t* __restrict__ prev_amax, float e_stop,
-                                                         int step, int32_t* __restrict__ done_step) {
+// ---------------------------------------------------------------- canonical entropy
+//
+// Ĥ of a row of bf16 logits x at temperature tau:
+//   u = (m - x) * (1 / tau) in float64 (m = the row maximum, tau the float32 value);
+//   e^-u by k = rint(u / ln2), r = (u - k ln2_hi) - k ln2_lo (Cody and Waite's
+//   two-part reduction; ln2_hi holds ln 2 to 32 significant bits, so k ln2_hi is
+//   exact), e^-r = sum_{i<=12} (-r)^i / i! in Horner form, times 2^-k; 0 for u >= 30;
+//   S = sum rint(e 2^40), T = sum rint((e u) 2^40) as exact 64-bit integers;
+//   Ĥ = float32(max(0, (log S' - 40 ln2) + T' / S')) with S', T' the float64 values
+//   hi * 2^32 + lo of S, T, and log a = j ln2 + 2 s (1 + z/3 + ... + z^12/25) for
+//   a = f 2^j, f in [sqrt(1/2), sqrt(2)), s = (f - 1) / (f + 1), z = s^2.
+// Every operation is one IEEE float64 add, subtract, multiply or divide rounded to
+// nearest even (the pragma keeps the compiler from fusing a multiply and an add),
+// rint, an exact scaling by a power of two, or an integer add, so the result does
+// not depend on the machine or the summation order.  |Ĥ - H| <= 3e-6.
+constexpr double kLn2 = 0x1.62e42fefa39efp-1;        // nearest double to ln 2
+constexpr double kLn2Hi = 0x1.62e42fee00000p-1;      // ln 2 to 32 significant bits
+constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;     // nearest double to ln 2 - kLn2Hi
+constexpr double kInvLn2 = 0x1.71547652b82fep+0;     // nearest double to 1 / ln 2
+constexpr double kSqrtHalf = 0x1.6a09e667f3bcdp-1;   // nearest double to sqrt(1/2)
+constexpr double kCanonQ = 1099511627776.0;          // 2^40
+constexpr double kCanonUMax = 30.0;
+
+__device__ __forceinline__ double canon_exp_neg(double u) {
+#pragma clang fp contract(off)
+  if (!(u < kCanonUMax)) return 0.0;
+  const double k = rint(u * kInvLn2);
+  const double r = (u - k * kLn2Hi) - k * kLn2Lo;
+  const double y = -r;
+  // 1 / i! for i = 12 .. 0, each the correctly rounded quotient
+  double p = 1.0 / 479001600.0;
+  p = p * y + 1.0 / 39916800.0;
+  p = p * y + 1.0 / 3628800.0;
+  p = p * y + 1.0 / 362880.0;
+  p = p * y + 1.0 / 40320.0;
+  p = p * y + 1.0 / 5040.0;
+  p = p * y + 1.0 / 720.0;
+  p = p * y + 1.0 / 120.0;
+  p = p * y + 1.0 / 24.0;
+  p = p * y + 1.0 / 6.0;
+  p = p * y + 0.5;
+  p = p * y + 1.0;
+  p = p * y + 1.0;
+  return ldexp(p, -(int)k);
+}
+
+__device__ __forceinline__ double canon_log(double a) {
+#pragma clang fp contract(off)
+  int j = 0;
+  double f = frexp(a, &j);
+  if (f < kSqrtHalf) {
+    f = f * 2.0;
+    j -= 1;
+  }
+  const double s = (f - 1.0) / (f + 1.0);
+  const double z = s * s;
+  // 1 / (2i + 1) for i = 12 .. 0
+  double p = 1.0 / 25.0;
+  p = p * z + 1.0 / 23.0;
+  p = p * z + 1.0 / 21.0;
+  p = p * z + 1.0 / 19.0;
+  p = p * z + 1.0 / 17.0;
+  p = p * z + 1.0 / 15.0;
+  p = p * z + 1.0 / 13.0;
+  p = p * z + 1.0 / 11.0;
+  p = p * z + 1.0 / 9.0;
+  p = p * z + 1.0 / 7.0;
+  p = p * z + 1.0 / 5.0;
+  p = p * z + 1.0 / 3.0;
+  p = p * z + 1.0;
+  return (double)j * kLn2 + (2.0 * s) * p;
+}
+
+__device__ __forceinline__ double u64_to_f64(uint64_t v) {
+#pragma clang fp contract(off)
+  return (double)(uint32_t)(v >> 32) * 4294967296.0 + (double)(uint32_t)v;
+}
+
+__device__ __forceinline__ float canon_entropy(uint64_t S, uint64_t T) {
+#pragma clang fp contract(off)
+  const double Sf = u64_to_f64(S), Tf = u64_to_f64(T);
+  constexpr double kC40 = 40.0 * kLn2;
+  const double h = (canon_log(Sf) - kC40) + Tf / Sf;
+  return (float)(h > 0.0 ? h : 0.0);
+}
+
+// Pass 3: exact integer sums (S, T) of one (row, kSampleChunk-logit chunk) for the
+// canonical entropy, for the masked rows of the sequences pass 2 deferred (flag set);
+// every other workgroup returns at once.  The row maximum is the largest raw chunk
+// maximum pass 1 recorded.
+__global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __restrict__ logits,
+                                                             const int32_t* __restrict__ canvas, int C,
+                                                             int vocab, int nchunks, float tau,
+                                                             const float4* __restrict__ part,
+                                                             const int32_t* __restrict__ flag,
+                                                             ulonglong2* __restrict__ cpart) {
+  __shared__ uint64_t red[2][4];
+  const int row = blockIdx.y, ch = blockIdx.x;
+  if (flag[row / C] == 0 || canvas[row] != vocab) return;   // uniform per workgroup
+  float m = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) m = fmaxf(m, part[(size_t)row * nchunks + c].w);
+  const double md = (double)m, inv = 1.0 / (double)tau;
+  const int c0 = ch * kSampleChunk, c1 = min(vocab, c0 + kSampleChunk);
+  const uint16_t* lp = logits + (size_t)row * vocab;
+  uint64_t S = 0, T = 0;
+  for (int i = c0 + 8 * threadIdx.x; i < c1; i += 8 * 256) {   // vocab % 8 == 0
+    const u32x4 v = ld16(lp + i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = v[j >> 1];
+      const double x = (double)__uint_as_float(j & 1 ? (w & 0xffff0000u) : (w << 16));
+      double u, e;
+      {
+#pragma clang fp contract(off)
+        u = (md - x) * inv;
+        e = canon_exp_neg(u);
+        S += (uint64_t)rint(e * kCanonQ);
+        T += (uint64_t)rint((e * u) * kCanonQ);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    S += __shfl_xor(S, o, 64);
+    T += __shfl_xor(T, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = S;
+    red[1][w] = T;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    cpart[(size_t)row * nchunks + ch] =
+        make_ulonglong2(red[0][0] + red[0][1] + red[0][2] + red[0][3], red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+}
+
+void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
+                           float tau, const float4* part, const int32_t* flag, ulonglong2* cpart,
+                           hipStream_t s) {
+  const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
+  launch_kernel(canon_partials_kernel, dim3(nchunks, batch * C), dim3(256), 0, s, nullptr, logits, canvas, C,
+                vocab, nchunks, tau, part, flag, cpart);
+}
+
+// ---------------------------------------------------------------- selection
+
+// Bound on |H_fast - Ĥ| used to certify a fast decision.  The fast pass sums exp
+// terms in fp32 along chains of at most ~80 roundings (64 per thread, 6 + 2 in the
+// workgroup, <= 8 in the chunk merge), so S and T carry a relative error below
+// ~1e-5 each; with T / S <= log V ~ 12.5 that bounds |H_fast - H| by ~2.6e-4, and
+// |Ĥ - H| <= 3e-6.  The float64 running sums over <= 1024 entropies below 16 add at
+// most ~2e-9 of rounding, bounded by kSumSlack.
+constexpr double kCertEps = 5e-4;
+constexpr double kSumSlack = 1e-8;
+
+enum SelMode { SEL_FAST = 0, SEL_CANON = 1, SEL_GIVEN = 2 };
+
+struct SelArgs {
+  const float4* part;        // SEL_FAST: fp32 chunk partials (tempered max, s, t, raw max)
+  const int* part_arg;       //           and chunk argmaxes
+  int nchunks;
+  const ulonglong2* cpart;   // SEL_CANON: exact integer chunk sums (S, T)
+  const float* H_in;         // SEL_GIVEN: entropies and argmaxes given
+  const int32_t* amax_in;
+  int32_t* canvas;
+  int C, vocab;
+  float gamma;
+  int commit_all;
+  float* H_out;
+  int32_t* amax_out;
+  int32_t* n_masked;
+  int32_t* prev_amax;        // adaptive stop (NULL: off)
+  float e_stop;
+  int step;
+  int32_t* done_step;
+  int32_t* flag;             // [batch]: SEL_FAST sets 1 where it defers the decision, else 0
+  int32_t* moved;            // [batch]: SEL_FAST's count of moved argmaxes, for SEL_CANON
+  int32_t* amax_ws;          // [batch][C]: every masked row's argmax, for SEL_CANON
+};
+
+template <int TPR, int MODE>   // threads per canvas row (chunk merge and rank count)
+__global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
   __shared__ __attribute__((aligned(16))) uint64_t keys[1024];
-  __shared__ double hsum[16];
   __shared__ __attribute__((aligned(16))) float sortedH[1024];
+  __shared__ float Hpos[1024];
   __shared__ int rank_s[1024];
   __shared__ int nm_s, kstar_s;
   const int b = blockIdx.x;
+  if (MODE == SEL_CANON && A.flag[b] == 0) return;   // decided by the fast pass
+  const int C = A.C;
   // the row's TPR threads are adjacent lanes
   const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
   const size_t ridx = (size_t)b * C + r;
-  const bool masked = r < C && canvas[ridx] == vocab;
-  // phase 1: entropy and argmax of each masked row; the row's threads merge
-  // interleaved subsets of its chunks, then combine through shuffles
+  const bool masked = r < C && A.canvas[ridx] == A.vocab;
+  // phase 1: entropy and argmax of each masked row
   float H = INFINITY;
   int a = 0;
-  if (part) {
+  if (MODE == SEL_FAST) {
+    // the row's threads merge interleaved subsets of its chunks, then combine
+    // through shuffles
+    const int nchunks = A.nchunks;
     float M = -INFINITY, S = 0.f, T = 0.f;
     a = INT_MAX;
     if (masked) {
-      const float4* pr = part + ridx * nchunks;
-      const int* pa = part_arg + ridx * nchunks;
+      const float4* pr = A.part + ridx * nchunks;
+      const int* pa = A.part_arg + ridx * nchunks;
       int k = sub;
       for (; k + 3 * TPR < nchunks; k += 4 * TPR) {
         float4 p[4];
@@ -221,27 +403,45 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
     }
     // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
     if (masked) H = fmaxf(logf(S) + T / S, 0.f);
+  } else if (MODE == SEL_CANON) {
+    uint64_t S = 0, T = 0;
+    if (masked)
+      for (int k = sub; k < A.nchunks; k += TPR) {
+        const ulonglong2 p = A.cpart[ridx * A.nchunks + k];
+        S += p.x;
+        T += p.y;
+      }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+      S += __shfl_xor(S, o, 64);
+      T += __shfl_xor(T, o, 64);
+    }
+    if (masked) {
+      H = canon_entropy(S, T);
+      a = A.amax_ws[ridx];
+    }
   } else if (masked) {
-    H = H_in[ridx];
-    a = amax_in[ridx];
+    H = A.H_in[ridx];
+    a = A.amax_in[ridx];
   }
-  if (masked && (a < 0 || a >= vocab)) a = min(max(a, 0), vocab - 1);
+  if (masked && (a < 0 || a >= A.vocab)) a = min(max(a, 0), A.vocab - 1);
   // unmasked rows (and the padding up to a multiple of 8) take the largest key,
   // which no masked row's key exceeds, so they are never counted below one
   const int Cp = (C + 7) & ~7;
   const uint64_t key = masked ? eb_key(H, r) : ~0ull;
   if (sub == 0 && r < Cp) keys[r] = key;
-  // adaptive stop (prev_amax given; §3.3): the masked rows' entropies summed in fp64
-  // (per wave, then the waves in order) and the rows whose argmax moved since the
-  // previous step counted
-  bool moved = false;
-  if (prev_amax) {
-    const double hv = wave_sum_d((masked && sub == 0) ? (double)H : 0.0);
-    if ((threadIdx.x & 63) == 0) hsum[threadIdx.x >> 6] = hv;
-    moved = masked && sub == 0 && a != prev_amax[ridx];
+  if (sub == 0 && r < C) Hpos[r] = H;
+  // adaptive stop (prev_amax given; §3.3): the rows whose argmax moved since the
+  // previous step (SEL_CANON takes the fast pass's count: prev_amax holds this
+  // step's argmaxes by then)
+  int n_moved = 1;
+  if (A.prev_amax) {
+    if (MODE == SEL_CANON)
+      n_moved = A.moved[b];
+    else
+      n_moved = __syncthreads_count(masked && sub == 0 && a != A.prev_amax[ridx]);
   }
   const int nm_all = __syncthreads_count(masked && sub == 0);
-  const int n_moved = prev_amax ? __syncthreads_count(moved) : 1;
   // phase 2: rank of each masked row = #{masked j : key_j < key_r}; the row's TPR
   // threads count interleaved pairs of keys (one 16-byte LDS read per pair)
   if (masked) {
@@ -265,21 +465,28 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
   __syncthreads();
   if (threadIdx.x == 0) {
     const int n = nm_s;
+    const double g = (double)A.gamma;
+    bool cert = true;
     bool stop = false;
-    if (n_moved == 0 && n > 0) {
+    if (A.prev_amax && n_moved == 0 && n > 0) {
+      // mean entropy of the masked rows: float64 running sum in position order
       double hs = 0.0;
-      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) hs += hsum[w];
-      stop = hs / n < (double)e_stop;
+      for (int i = 0; i < C; ++i)
+        if (A.canvas[(size_t)b * C + i] == A.vocab) hs += (double)Hpos[i];
+      const double mean = hs / n;
+      stop = mean < (double)A.e_stop;
+      if (MODE == SEL_FAST && fabs(mean - (double)A.e_stop) <= kCertEps + kSumSlack) cert = false;
     }
     int ks;
-    if (commit_all || stop || n == 0) {
+    if (A.commit_all || stop || n == 0) {
       ks = n;
     } else {
-      // running fp64 sum in rank order; entries are read four at a time
-      double S = 0.0;
+      // running fp64 sum in rank order (S_k of the first k rows); k_nat = the number
+      // of leading running sums within gamma (the sums never decrease)
+      double S = 0.0, S_at = 0.0;
       int k = 0;
-      bool over = false;
       const float4* s4 = reinterpret_cast<const float4*>(sortedH);
+      bool over = false;
       for (int j = 0; j < n && !over; j += 4) {
         const float4 h = s4[j >> 2];
         const float hv[4] = {h.x, h.y, h.z, h.w};
@@ -287,41 +494,90 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(const float4* __restric
         for (int u = 0; u < 4; ++u) {
           if (over || j + u >= n) break;
           S += (double)hv[u];
-          if (S <= (double)gamma)
+          if (S <= g) {
             k = j + u + 1;
-          else
+            S_at = S;
+          } else {
             over = true;
+          }
         }
       }
       ks = k < 1 ? 1 : k;
+      if (MODE == SEL_FAST) {
+        // certified when no Ĥ within kCertEps of each fast H changes the set:
+        // the ks-th and (ks+1)-th entropies are more than 2 eps apart, and the
+        // running sums at ks (when within gamma) and at ks + 1 stay on their side
+        // of gamma by more than eps per term
+        const double S_ks = k >= 1 ? S_at : (double)sortedH[0];
+        if (ks < n) {
+          const double next = S_ks + (double)sortedH[ks];
+          if ((double)sortedH[ks] - (double)sortedH[ks - 1] <= 2.0 * kCertEps) cert = false;
+          if (next - g <= (ks + 1) * kCertEps + kSumSlack) cert = false;
+        }
+        if (k >= 1 && g - S_at <= k * kCertEps + kSumSlack) cert = false;
+      }
+    }
+    if (MODE == SEL_FAST && A.flag) {
+      A.flag[b] = cert ? 0 : 1;
+      if (!cert) {
+        A.moved[b] = n_moved;
+        ks = 0;                               // the canonical pass decides
+      }
     }
     kstar_s = ks;
-    n_masked[b] = n - ks;
-    if (done_step && n - ks == 0 && done_step[b] == 0) done_step[b] = step + 1;
+    if (cert || MODE != SEL_FAST || !A.flag) {
+      A.n_masked[b] = n - ks;
+      if (A.done_step && n - ks == 0 && A.done_step[b] == 0) A.done_step[b] = A.step + 1;
+    }
   }
   __syncthreads();
   if (sub == 0 && r < C) {
-    if (H_out) H_out[ridx] = masked ? H : __int_as_float(0x7fc00000);   // NaN on unmasked rows
-    if (amax_out) amax_out[ridx] = masked ? a : -1;                       // -1 on unmasked rows
-    if (prev_amax) prev_amax[ridx] = masked ? a : -1;
-    if (masked && rank_s[r] < kstar_s) canvas[ridx] = a;
+    if (A.H_out) A.H_out[ridx] = masked ? H : __int_as_float(0x7fc00000);   // NaN on unmasked rows
+    if (MODE != SEL_CANON) {
+      if (A.amax_out) A.amax_out[ridx] = masked ? a : -1;                   // -1 on unmasked rows
+      if (A.prev_amax) A.prev_amax[ridx] = masked ? a : -1;
+      if (A.amax_ws && masked) A.amax_ws[ridx] = a;
+    }
+    if (masked && rank_s[r] < kstar_s) A.canvas[ridx] = a;
   }
+}
+
+template <int MODE>
+static void run_select(const SelArgs& a, int batch, hipStream_t s) {
+  const int rows64 = ((a.C + 63) / 64) * 64;
+  if (4 * rows64 <= 1024)
+    launch_kernel(eb_select_kernel<4, MODE>, dim3(batch), dim3(4 * rows64), 0, s, nullptr, a);
+  else
+    launch_kernel(eb_select_kernel<1, MODE>, dim3(batch), dim3(rows64), 0, s, nullptr, a);
 }
 
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                      hipStream_t s) {
-  const int rows64 = ((C + 63) / 64) * 64;
-  if (4 * rows64 <= 1024)
-    launch_kernel(eb_select_kernel<4>, dim3(batch), dim3(4 * rows64), 0, s, nullptr, part, part_arg, nchunks,
-                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked, prev_amax,
-                  e_stop, step, done_step);
-  else
-    launch_kernel(eb_select_kernel<1>, dim3(batch), dim3(rows64), 0, s, nullptr, part, part_arg, nchunks,
-                  H_in, amax_in, canvas, C, vocab, gamma, commit_all, H_out, amax_out, n_masked, prev_amax,
-                  e_stop, step, done_step);
+                      int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s) {
+  SelArgs a{};
+  a.part = part; a.part_arg = part_arg; a.nchunks = nchunks;
+  a.H_in = H_in; a.amax_in = amax_in;
+  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
+  a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
+  a.prev_amax = prev_amax; a.e_stop = e_stop; a.step = step; a.done_step = done_step;
+  a.flag = flag; a.moved = moved; a.amax_ws = amax_ws;
+  if (part) run_select<SEL_FAST>(a, batch, s);
+  else run_select<SEL_GIVEN>(a, batch, s);
+}
+
+void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
+                            float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
+                            int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
+                            int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s) {
+  SelArgs a{};
+  a.cpart = cpart; a.nchunks = nchunks;
+  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
+  a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
+  a.prev_amax = prev_amax; a.e_stop = e_stop; a.step = step; a.done_step = done_step;
+  a.flag = flag; a.moved = moved; a.amax_ws = amax_ws;
+  run_select<SEL_CANON>(a, batch, s);
 }
 
 }  // namespace dg

@@ -24,7 +24,7 @@ MAX_BATCH = 64
 
 KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
-                "sample_pass1", "sample_select", "fill"]
+                "sample_pass1", "sample_select", "fill", "sample_canon", "sample_select_canon"]
 PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
 MOE_GROUP = 64   # tokens per grouped-GEMM work item in the routing tap's item list
 
@@ -236,22 +236,27 @@ def pack(t: torch.Tensor, kind: int = PACK_PLAIN, param: int = 0) -> torch.Tenso
     return dst
 
 
+def pack_layer(cfg: ModelConfig, lw: dict) -> dict:
+    """Engine-layout copy of one layer of synth.make_weights output (device tensors)."""
+    return {
+        "attn_norm": lw["attn_norm"], "ffn_norm": lw["ffn_norm"],
+        "w_qkv": pack(lw["w_qkv"], PACK_QKV, cfg.head_dim),
+        "w_o": pack(lw["w_o"]),
+        "w_router": pack(lw["w_router"]),
+        "w_gate_up": pack(lw["w_gate_up"], PACK_GATE_UP, cfg.expert_ffn),
+        "w_down": pack(lw["w_down"]),
+        "ws_gate_up": pack(lw["ws_gate_up"], PACK_GATE_UP, cfg.shared_ffn),
+        "ws_down": pack(lw["ws_down"]),
+    }
+
+
 def pack_weights(cfg: ModelConfig, w: dict, free_source: bool = False) -> dict:
     """Engine-layout copy of synth.make_weights output (device tensors)."""
     out = {"embed": pack(w["embed"]), "final_norm": w["final_norm"], "layers": []}
     if free_source:
         w["embed"] = None
     for l, lw in enumerate(w["layers"]):
-        out["layers"].append({
-            "attn_norm": lw["attn_norm"], "ffn_norm": lw["ffn_norm"],
-            "w_qkv": pack(lw["w_qkv"], PACK_QKV, cfg.head_dim),
-            "w_o": pack(lw["w_o"]),
-            "w_router": pack(lw["w_router"]),
-            "w_gate_up": pack(lw["w_gate_up"], PACK_GATE_UP, cfg.expert_ffn),
-            "w_down": pack(lw["w_down"]),
-            "ws_gate_up": pack(lw["ws_gate_up"], PACK_GATE_UP, cfg.shared_ffn),
-            "ws_down": pack(lw["ws_down"]),
-        })
+        out["layers"].append(pack_layer(cfg, lw))
         if free_source:
             w["layers"][l] = None
     return out

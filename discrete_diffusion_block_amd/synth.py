@@ -118,18 +118,21 @@ def _gain(n, gen, device) -> torch.Tensor:
 
 
 def make_weights(cfg: ModelConfig, seed: int = SEED_WEIGHTS, device: str = "cpu",
-                 std: float = 0.02, layers: Optional[List[int]] = None) -> dict:
+                 std: float = 0.02, layers: Optional[List[int]] = None, with_embed: bool = True) -> dict:
     """Random-init weights.  Returns {"embed", "final_norm", "layers": [dict per layer]}.
 
     Each tensor has its own generator seeded from (seed, tensor index), so a
     layer's weights do not depend on which other layers were drawn.
     embed is [V+1][d] bf16; row V is the [MASK] embedding (the head uses rows 0..V-1).
     Norm gains are fp32, every matrix is bf16 and row-major as listed in layer_shapes().
+    with_embed=False leaves out embed and final_norm (None), for drawing layers one at a
+    time.
     """
     shapes = layer_shapes(cfg)
     w = {
-        "embed": _normal_bf16((cfg.vocab + 1, cfg.d_model), std, _gen(seed * 1000003 + 1, device), device),
-        "final_norm": _gain(cfg.d_model, _gen(seed * 1000003 + 2, device), device),
+        "embed": _normal_bf16((cfg.vocab + 1, cfg.d_model), std, _gen(seed * 1000003 + 1, device), device)
+        if with_embed else None,
+        "final_norm": _gain(cfg.d_model, _gen(seed * 1000003 + 2, device), device) if with_embed else None,
         "layers": [],
     }
     todo = range(cfg.n_layers) if layers is None else layers

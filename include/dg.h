@@ -241,6 +241,7 @@ typedef enum dg_kernel_kind {
   DG_K_PREP = 0, DG_K_EMBED, DG_K_QKV, DG_K_ATTENTION, DG_K_O_PROJ, DG_K_NORM, DG_K_ROUTER,
   DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
   DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL,
+  DG_K_SAMPLE_CANON, DG_K_SAMPLE_SELECT_CANON,
   DG_K_COUNT
 } dg_kernel_kind;
 

@@ -15,34 +15,6 @@ def to_np_bf16(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def eb_decision_margin(H: np.ndarray, masked, gamma: float, commit_all: bool, eps: float) -> bool:
-    """True when the entropy-bounded selection on H (float64) cannot change under any
-    perturbation of each entropy by at most eps (the decision is certified)."""
-    if commit_all or len(masked) == 0:
-        return True
-    order = sorted(masked, key=lambda i: (H[i], i))
-    hs = [H[i] for i in order]
-    s, k = 0.0, 0
-    sums = []
-    for j, h in enumerate(hs):
-        s += h
-        sums.append(s)
-    for j, sj in enumerate(sums):
-        if sj <= gamma:
-            k = j + 1
-        else:
-            break
-    k = max(1, k)
-    # the k-th and (k+1)-th ranked rows must be separated, and the running sums at the
-    # decision boundary must be farther from gamma than the accumulated uncertainty
-    if k < len(hs) and hs[k] - hs[k - 1] <= 2 * eps:
-        return False
-    for j in (k - 1, k):
-        if 0 <= j < len(sums) and abs(sums[j] - gamma) <= (j + 1) * eps:
-            return False
-    return True
-
-
 def eb_valid(H: np.ndarray, masked, committed, gamma: float, commit_all: bool) -> bool:
     """Property check: `committed` is the selection the rule makes on its own float32
     entropies H (running float64 sum in (H, position) order, at least one)."""
@@ -76,3 +48,58 @@ def routing_near_ties(trace_layers, k: int, delta: float = ROUTER_DELTA):
         gap = r[:, k - 1] - r[:, k] if r.shape[1] > k else np.full(r.shape[0], np.inf)
         out.append(set(np.nonzero(gap < delta)[0].tolist()))
     return out
+
+
+def forced_ids(traces, n_layers, lo=0, hi=None):
+    """int32 [n_layers][B * (hi - lo)][k]: the oracle's expert ids of tokens lo..hi-1 of
+    every sequence (traces[b][l]["ids"], sequences in batch order), the layout the
+    engine's forced-routing tap reads for one pass."""
+    out = []
+    for l in range(n_layers):
+        rows = [np.asarray(tr[l]["ids"])[lo:hi] for tr in traces]
+        out.append(np.concatenate(rows, axis=0))
+    return np.ascontiguousarray(np.stack(out).astype(np.int32))
+
+
+class forced_routing:
+    """Within the block, every pass through eng uses the given expert ids (one pass)."""
+
+    def __init__(self, eng, ids):
+        self.eng = eng
+        self.ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+
+    def __enter__(self):
+        from discrete_diffusion_block_amd import dg
+        dg.dg_test_force_routing(self.eng.ctx, self.ids)
+        return self
+
+    def __exit__(self, *exc):
+        from discrete_diffusion_block_amd import dg
+        torch.cuda.synchronize()          # the ids stay alive until the pass has read them
+        dg.dg_test_force_routing(self.eng.ctx, None)
+        return False
+
+
+def argmax_agreement(gpu_logits, ref_logits, margin):
+    """(raw agreement, agreement on rows whose reference top-2 gap exceeds margin, number
+    of such rows) of the row argmaxes."""
+    a_g = np.argmax(gpu_logits, axis=1)
+    a_r = np.argmax(ref_logits, axis=1)
+    top2 = -np.sort(-ref_logits, axis=1)[:, :2]
+    clear = (top2[:, 0] - top2[:, 1]) > margin
+    raw = float(np.mean(a_g == a_r))
+    cl = float(np.mean((a_g == a_r)[clear])) if clear.any() else 1.0
+    return raw, cl, int(clear.sum())
+
+
+def logit_error_split(lg, ref):
+    """Where the max |engine - oracle| of stored bf16 logits comes from: the engine stores
+    bf16, whose rounding alone moves a logit by up to half an ulp (1/64 in [4, 8)).  Returns
+    a short text with the max difference, the max difference beyond the rounding of the
+    oracle's own value to bf16 (|lg - ref| - |bf16(ref) - ref|, the computation's share),
+    and the 99.99th percentile."""
+    from oracle import dg_oracle as O
+    d = np.abs(lg - ref)
+    own = np.abs(O.bf16(ref) - ref)
+    return (f"compute share {float((d - own).max()):.3e}, p99.99 {float(np.quantile(d, 0.9999)):.3e}, "
+            f"largest |ref| {float(np.abs(ref).max()):.2f}")

@@ -2,21 +2,19 @@
 16 query / 8 KV heads of 128, 128 experts of 704 top-8 + a 2112-wide shared expert,
 vocab 262144 + [MASK], canvas 256, sliding window 1024.  These shapes take the kernel
 variants the tiny model never reaches (head-dim-128 attention, the LDS-staged expert
-gate/up and vocabulary head, multi-tile GEMMs) on a prefix longer than the window.
+gate/up and vocabulary head, multi-tile GEMMs) on a prefix longer than the window, and
+a global layer over a 4096-token prefix (the long-context workload's layer type).
 
-The oracle finishes each pass in a few seconds at these sizes, so whole outputs are
-compared: prefill K/V of both layers, and the logits of denoise steps for one and for
-two sequences of different committed lengths.
+Routing is teacher-forced (dg_test_force_routing): every pass takes the oracle's expert
+ids, so near-tied router logits (the engine's fp32 sums against the oracle's float64
+ones move them by up to ~7e-3 at this width) cannot send a row to another expert, and
+every row of every output is compared.
 
-Tolerances.  Every bf16 re-rounding stage (normed state, attention probabilities, the
-SwiGLU activation) turns the engine's fp32-vs-fp64 differences into whole-ulp flips of
-some elements, so after one layer at width 2816 the residual stream differs from the
-oracle's by ~0.6% relative (measured: layer-1 K/V per-head relative error <= 0.8%,
-logits <= 0.5% per row, <= 0.03 absolute with logit std ~1.07).  The same differences
-move router logits by up to ~7e-3, so a token whose 8th and 9th router logits are closer
-than ROUTER_DELTA is a routing near-tie: either expert set is correct, and such rows
-(and, for K/V, rows whose earlier layer had one) are left out.  A wrong index, a
-dropped tile or a wrong expert moves a row by >= 2% and a logit by >= 0.1."""
+Tolerances.  Logits: max |delta| <= 3e-2 on every row (the bf16-compute bound; logit std
+~1.07).  K/V: each head vector within 1.5% relative (bf16 re-rounding of the normed state,
+the attention probabilities and the SwiGLU activations turns fp32-vs-fp64 differences
+into whole-ulp flips).  Argmax: raw agreement is reported; rows whose oracle top-two
+logits are more than 2 x 3e-2 apart must agree (closer ones are decided by bf16 noise)."""
 import dataclasses
 
 import numpy as np
@@ -25,17 +23,15 @@ import torch
 
 from discrete_diffusion_block_amd import dg, synth
 from oracle import dg_oracle as O
-from gpu_util import require_gpu, routing_near_ties, to_np_bf16
+from gpu_util import argmax_agreement, forced_ids, forced_routing, logit_error_split, require_gpu, to_np_bf16
 
 pytestmark = pytest.mark.gpu
 
-ROUTER_DELTA = 1.5e-2     # 2x the largest router-logit difference measured at this width
 KV_REL = 1.5e-2           # per-head relative error of K/V vectors
 KV_ABS = 6e-2
-LOGIT_REL = 1e-2          # per-row relative error of the logits
-LOGIT_ABS = 6e-2
+LOGIT_ABS = 3e-2          # max |delta| of the logits, every row
 PROMPT = 1100             # > window: the canvas and the last prefill rows see a truncated prefix
-SPLIT = 700               # prefill in two calls, the second crossing the window edge
+CALLS = [(0, 512), (512, 700), (700, 1100)]   # prefill calls (one pass each); the last crosses the window edge
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -43,123 +39,125 @@ def _gpu():
     require_gpu()
 
 
-@pytest.fixture(scope="module")
-def full():
-    cfg = dataclasses.replace(synth.CONFIGS["layer"], n_layers=2)
-    print("full-shape weights (2 layers, vocab 262144)", flush=True)
+def _load(cfg):
     w_cpu = synth.make_weights(cfg)
     w_np = O.to_numpy_weights(w_cpu)
     w_gpu = {"embed": w_cpu["embed"].cuda(), "final_norm": w_cpu["final_norm"].cuda(),
              "layers": [{k: v.cuda() for k, v in lw.items()} for lw in w_cpu["layers"]]}
-    del w_cpu
+    return w_np, w_gpu
+
+
+@pytest.fixture(scope="module")
+def full():
+    cfg = dataclasses.replace(synth.CONFIGS["layer"], n_layers=2)
+    print("full-shape weights (2 layers, vocab 262144)", flush=True)
+    w_np, w_gpu = _load(cfg)
     prompt = synth.make_prompt(cfg, 1, PROMPT)
     kv = O.KVCache(cfg, 1)
     tr = [[]]
     O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
     eng = dg.Engine(cfg, w_gpu, max_batch=2, max_ctx=2048)
-    yield cfg, w_np, w_gpu, prompt, kv, tr[0], eng
+    yield cfg, w_np, w_gpu, prompt, kv, tr, eng
     eng.close()
 
 
-def _rel_check(got, ref, keep):
-    d = (got - ref)[keep]
-    rel = np.linalg.norm(d, axis=-1) / np.maximum(np.linalg.norm(ref[keep], axis=-1), 1e-6)
+def _prefill(eng, cfg, prompt, tr, calls):
+    eng.reset()
+    for lo, hi in calls:
+        with forced_routing(eng, forced_ids(tr, cfg.n_layers, lo, hi)):
+            eng.prefill_kv(prompt[:, lo:hi].contiguous().cuda())
+
+
+def _rel_check(got, ref):
+    d = got - ref
+    rel = np.linalg.norm(d, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-6)
     assert rel.max() <= KV_REL, float(rel.max())
     assert np.abs(d).max() <= KV_ABS, float(np.abs(d).max())
+    return float(rel.max())
 
 
-def _logit_check(lg, ref, rows):
-    """Per-row relative and absolute error on the kept rows; the argmax must agree on
-    every row whose top-two oracle logits are further apart than twice the absolute bound."""
-    d = lg[rows] - ref[rows]
-    rel = np.linalg.norm(d, axis=1) / np.linalg.norm(ref[rows], axis=1)
-    err = np.abs(d).max()
-    print(f"  kept rows {len(rows)}, row rel max {rel.max():.3e}, max |delta| {err:.3e}", flush=True)
-    assert rel.max() <= LOGIT_REL, float(rel.max())
-    assert err <= LOGIT_ABS, float(err)
-    top2 = -np.sort(-ref[rows], axis=1)[:, :2]
-    clear = (top2[:, 0] - top2[:, 1]) > 2 * LOGIT_ABS
-    assert clear.sum() >= len(rows) // 4
-    assert np.array_equal(np.argmax(lg[rows], 1)[clear], np.argmax(ref[rows], 1)[clear])
+def _logit_check(lg, ref, label):
+    """Every row within LOGIT_ABS; argmax agreement reported, and required on clear rows."""
+    err = float(np.abs(lg - ref).max())
+    raw, clear, n_clear = argmax_agreement(lg, ref, 2 * LOGIT_ABS)
+    print(f"  {label}: max |delta| {err:.3e} over {lg.shape[0]} rows ({logit_error_split(lg, ref)}); "
+          f"argmax agreement raw {raw:.4f}, {clear:.4f} on the {n_clear} rows with a top-2 margin > "
+          f"{2 * LOGIT_ABS}", flush=True)
+    assert err <= LOGIT_ABS, err
+    assert clear == 1.0
+    return err, raw
 
 
 def test_fullshape_prefill_kv(full):
-    cfg, w_np, w_gpu, prompt, kv, trace, eng = full
-    print(f"full-shape prefill {SPLIT}+{PROMPT - SPLIT}", flush=True)
-    eng.reset()
-    eng.prefill_kv(prompt[:, :SPLIT].contiguous().cuda())
-    eng.prefill_kv(prompt[:, SPLIT:].contiguous().cuda())
+    cfg, w_np, w_gpu, prompt, kv, tr, eng = full
+    print(f"full-shape prefill in calls {CALLS}", flush=True)
+    _prefill(eng, cfg, prompt, tr, CALLS)
     torch.cuda.synchronize()
     assert eng.lengths[0] == PROMPT
-    # layer 1's K/V are computed from the state after layer 0's attention (window-limited
-    # causal, head dim 128) and MoE; rows whose layer-0 routing is a near-tie are excluded
-    near = routing_near_ties(trace[:1], cfg.top_k, ROUTER_DELTA)[0]
-    assert len(near) <= 0.3 * PROMPT, len(near)
     k, v = eng.kv_view()
     for l in range(cfg.n_layers):
-        keep = np.ones(PROMPT, bool)
-        if l > 0:
-            keep[sorted(near)] = False
         kg = k[l, 0, :, :PROMPT, :].float().cpu().numpy().transpose(1, 0, 2)
         vg = v[l, 0, :, :PROMPT, :].float().cpu().numpy().transpose(1, 0, 2)
-        _rel_check(kg, kv.k[l][0], keep)
-        _rel_check(vg, kv.v[l][0], keep)
-
-
-def _near_rows(trace_b, k):
-    """Canvas rows with a routing near-tie at any layer (a row's own state; its effect on
-    other rows through attention is one key among > 1000 and stays far inside LOGIT_ABS)."""
-    return set().union(*routing_near_ties(trace_b, k, ROUTER_DELTA))
+        rk, rv = _rel_check(kg, kv.k[l][0]), _rel_check(vg, kv.v[l][0])
+        print(f"  layer {l}: K rel {rk:.2e}, V rel {rv:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("masked,t", [(256, 1.0), (128, 0.5)])
 def test_fullshape_denoise_logits(full, masked, t):
-    cfg, w_np, w_gpu, prompt, kv, trace, eng = full
+    cfg, w_np, w_gpu, prompt, kv, tr, eng = full
     V, C = cfg.vocab, cfg.canvas
     print(f"full-shape denoise masked={masked} t={t}", flush=True)
-    eng.reset()
-    eng.prefill_kv(prompt.cuda())
+    _prefill(eng, cfg, prompt, tr, CALLS)
     canvas = synth.make_masked_canvas(C, V, masked).view(1, C)
+    trd = [[]]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), t, trace=trd)[0]
     logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
-    eng.denoise_step(canvas.cuda(), t, logits)
-    torch.cuda.synchronize()
-    tr = [[]]
-    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), t, trace=tr)[0]
-    near = _near_rows(tr[0], cfg.top_k)
-    assert len(near) <= 0.75 * C, len(near)
-    _logit_check(to_np_bf16(logits)[0], ref, [i for i in range(C) if i not in near])
+    with forced_routing(eng, forced_ids(trd, cfg.n_layers)):
+        eng.denoise_step(canvas.cuda(), t, logits)
+    _logit_check(to_np_bf16(logits)[0], ref, f"masked {masked}")
 
 
 def test_fullshape_batch_two_ragged(full):
     """Two sequences (1100 and 300 committed tokens) denoised in one pass: M = 512 rows
     through every kernel, one prefix longer than the window and one shorter."""
-    cfg, w_np, w_gpu, prompt, kv, trace, eng = full
+    cfg, w_np, w_gpu, prompt, kv, tr, eng = full
     V, C = cfg.vocab, cfg.canvas
     p2 = synth.make_prompt(cfg, 1, PROMPT, seed=91)
     print("full-shape batch-2 denoise (1100 + 300)", flush=True)
+    kv2 = O.KVCache(cfg, 1)
+    tr2 = [[]]
+    O.prefill_kv(cfg, w_np, kv2, p2[:, :300].numpy(), trace=tr2)
+    # batch-2 prefill passes of n <= 256 tokens per sequence (M = 2n <= 512: one pass each);
+    # sequence 1 only needs its first 300 tokens (causal: later ones do not change them)
+    both = torch.cat([prompt, p2]).contiguous()
     eng.reset()
-    eng.prefill_kv(torch.cat([prompt, p2]).contiguous().cuda())
-    # causal encoding: the first 300 positions of sequence 1 do not depend on the rest
+    for lo in range(0, PROMPT, 256):
+        hi = min(PROMPT, lo + 256)
+        ids0 = forced_ids(tr, cfg.n_layers, lo, hi)
+        # sequence 1's tokens from 300 on are past its compared range: any valid routing
+        ids1 = np.zeros_like(ids0)
+        if lo < 300:
+            part = forced_ids(tr2, cfg.n_layers, lo, min(hi, 300))
+            ids1[:, :part.shape[1]] = part
+        ids = np.ascontiguousarray(np.concatenate([ids0, ids1], axis=1))
+        with forced_routing(eng, ids):
+            eng.prefill_kv(both[:, lo:hi].contiguous().cuda())
     eng.kv.len[1] = 300
     canvas = torch.stack([synth.make_masked_canvas(C, V, 200, seed=5),
                           synth.make_masked_canvas(C, V, 256, seed=6)]).contiguous()
-    logits = torch.empty(2, C, V, dtype=torch.bfloat16, device="cuda")
-    eng.denoise_step(canvas.cuda(), 0.8, logits)
-    torch.cuda.synchronize()
-    kv2 = O.KVCache(cfg, 1)
-    O.prefill_kv(cfg, w_np, kv2, p2[:, :300].numpy())
-    both = O.KVCache(cfg, 2)
+    bothkv = O.KVCache(cfg, 2)
     for l in range(cfg.n_layers):
-        both.k[l] = [kv.k[l][0], kv2.k[l][0]]
-        both.v[l] = [kv.v[l][0], kv2.v[l][0]]
-    both.len = [PROMPT, 300]
-    tr = [[], []]
-    ref = O.denoise_step(cfg, w_np, both, canvas.numpy(), 0.8, trace=tr)
+        bothkv.k[l] = [kv.k[l][0], kv2.k[l][0]]
+        bothkv.v[l] = [kv.v[l][0], kv2.v[l][0]]
+    bothkv.len = [PROMPT, 300]
+    trd = [[], []]
+    ref = O.denoise_step(cfg, w_np, bothkv, canvas.numpy(), 0.8, trace=trd)
+    logits = torch.empty(2, C, V, dtype=torch.bfloat16, device="cuda")
+    with forced_routing(eng, forced_ids(trd, cfg.n_layers)):
+        eng.denoise_step(canvas.cuda(), 0.8, logits)
     lg = to_np_bf16(logits)
     for b in range(2):
-        near = _near_rows(tr[b], cfg.top_k)
-        assert len(near) <= 0.75 * C, len(near)
-        _logit_check(lg[b], ref[b], [i for i in range(C) if i not in near])
+        _logit_check(lg[b], ref[b], f"sequence {b}")
 
 
 def test_fullshape_generate_block_masked_head(full):
@@ -167,7 +165,7 @@ def test_fullshape_generate_block_masked_head(full):
     to commit ~100 rows per step the head sees 256, ~156 and ~56 rows (16, 10 and 4 token
     blocks of its tile).  Its canvas must equal the same steps driven through
     dg_denoise_step (whole head) and dg_sample_eb, bit for bit, for two sequences."""
-    cfg, w_np, w_gpu, prompt, kv, trace, eng = full
+    cfg, w_np, w_gpu, prompt, kv, tr, eng = full
     V, C = cfg.vocab, cfg.canvas
     steps, gamma = 3, 100 * float(np.log(V))
     p2 = synth.make_prompt(cfg, 1, 600, seed=17)
@@ -200,3 +198,36 @@ def test_fullshape_generate_block_masked_head(full):
     print(f"  masked rows left after each step: {left}", flush=True)
     assert 100 <= C - left[0][0] <= 110 and left[1][0] < left[0][0]   # the head saw shrinking row sets
     assert torch.equal(blk, canvas)
+
+
+def test_fullshape_global_layer_long_prefix():
+    """Layer 1 global (the long-context workload's every-6th-layer type, here global_every
+    2) over a 4096-token prefix, layer 0 sliding (window 1024): the prefill's causal mask
+    over thousands of keys in the global layer, and a denoising step whose canvas attends
+    to all 4096 cached keys there and to the last 1024 in layer 0."""
+    cfg = dataclasses.replace(synth.CONFIGS["layer"], n_layers=2, global_every=2)
+    P = 4096
+    print(f"full-shape global layer, {P}-token prefix", flush=True)
+    w_np, w_gpu = _load(cfg)
+    prompt = synth.make_prompt(cfg, 1, P, seed=23)
+    kv = O.KVCache(cfg, 1)
+    tr = [[]]
+    O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
+    eng = dg.Engine(cfg, w_gpu, max_batch=1, max_ctx=P + cfg.canvas)
+    _prefill(eng, cfg, prompt, tr, [(lo, lo + 512) for lo in range(0, P, 512)])
+    torch.cuda.synchronize()
+    k, v = eng.kv_view()
+    for l in range(cfg.n_layers):
+        rk = _rel_check(k[l, 0, :, :P, :].float().cpu().numpy().transpose(1, 0, 2), kv.k[l][0])
+        rv = _rel_check(v[l, 0, :, :P, :].float().cpu().numpy().transpose(1, 0, 2), kv.v[l][0])
+        print(f"  layer {l} ({'global' if cfg.is_global(l) else 'sliding'}): K rel {rk:.2e}, V rel {rv:.2e}",
+              flush=True)
+    C, V = cfg.canvas, cfg.vocab
+    canvas = synth.make_masked_canvas(C, V, 192, seed=8).view(1, C)
+    trd = [[]]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), 0.9, trace=trd)[0]
+    logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
+    with forced_routing(eng, forced_ids(trd, cfg.n_layers)):
+        eng.denoise_step(canvas.cuda(), 0.9, logits)
+    _logit_check(to_np_bf16(logits)[0], ref, "global layer over 4096 keys")
+    eng.close()
