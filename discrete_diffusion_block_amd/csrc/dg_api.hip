@@ -473,6 +473,35 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
   return check_launch("sampler");
 }
 
+// ---- static scratch for the sampler variant that allocates nothing ----
+//
+// dg_sample_eb_noalloc keeps the sampler's workspace in this file-scope device array
+// (each device holds its own copy from module load until the process ends).  Host code
+// never names the array when it needs its memory: the name is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device, kept below.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call per device).
+dg_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -633,6 +662,28 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
   carve_sampler(cv, batch, canvas, vocab, &ws);
   return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
                      d_n_masked, ws, (hipStream_t)stream);
+}
+
+dg_status dg_sample_eb_noalloc(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                               float gamma, int commit_all, float* d_entropy, int32_t* d_argmax,
+                               int32_t* d_n_masked, void* stream) {
+  size_t need = 0;
+  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
+  if (st != DG_OK) return st;
+  if (need > kScratchBytes)
+    return fail(DG_ERR_WORKSPACE,
+                "%d x %d rows of %d logits need %zu bytes of sampler scratch, beyond the library's static %zu "
+                "bytes: call dg_sample_eb with a workspace",
+                batch, canvas, vocab, need, kScratchBytes);
+  if (!d_logits || !d_canvas || !d_n_masked) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != DG_OK) return st;
+  // the same kernels as dg_sample_eb; every scratch word they read this call was
+  // written earlier in this call, so nothing needs clearing first
+  return dg_sample_eb(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked,
+                      ws, kScratchBytes, stream);
 }
 
 dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps,

@@ -76,6 +76,7 @@ def lib():
             "dg_denoise_step": [vp, C.POINTER(KV), vp, i32, f32, vp, vp, sz, vp],
             "dg_sample_workspace_size": [i32, i32, i32, C.POINTER(sz)],
             "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
+            "dg_sample_eb_noalloc": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp],
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
             "dg_sample_eb_ex": [vp, vp, i32, i32, i32, f32, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, sz,
                                 vp],
@@ -186,6 +187,15 @@ def dg_sample_eb(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commi
     b, c, v = logits.shape
     _check(lib().dg_sample_eb(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
                               _p(entropy), _p(argmax), _p(n_masked), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_sample_eb_noalloc(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all: bool,
+                         n_masked: torch.Tensor, entropy: Optional[torch.Tensor] = None,
+                         argmax: Optional[torch.Tensor] = None, stream=None):
+    """dg_sample_eb with the library's static scratch in place of a workspace."""
+    b, c, v = logits.shape
+    _check(lib().dg_sample_eb_noalloc(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
+                                      _p(entropy), _p(argmax), _p(n_masked), _stream(stream)))
 
 
 def dg_sample_eb_ex(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all: bool,

@@ -185,6 +185,19 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
                        int32_t* d_argmax, int32_t* d_n_masked, void* d_ws, size_t ws_bytes,
                        void* stream);
 
+/* dg_sample_eb for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same rule,
+ * kernels, arguments and outputs, but no workspace argument -- the sampler's scratch
+ * is a static 4 MiB array inside the library (one per device, held until the process
+ * ends; enough for about 7000 canvas rows of 262144 logits).  Calls whose
+ * dg_sample_workspace_size exceeds 4 MiB fail with DG_ERR_WORKSPACE before anything
+ * is enqueued.  The call allocates and frees nothing.  Every call on a device shares
+ * that device's scratch: calls that overlap in time on one device (other streams,
+ * other threads) race and must be serialised by the caller. */
+dg_status dg_sample_eb_noalloc(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas,
+                               int vocab, float gamma, int commit_all, float* d_entropy,
+                               int32_t* d_argmax, int32_t* d_n_masked, void* stream);
+
 /* dg_sample_eb with the two extras of the Technical Report's default sampler (§3.3):
  *  - temperature annealing: H is the entropy of softmax(row / temperature)
  *    (temperature finite and > 0; 1 gives dg_sample_eb; the argmax does not depend
