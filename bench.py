@@ -72,6 +72,8 @@ def algorithmic_work(kind, cfg, M, counts_per_layer):
     if kind == "attention":
         keys = cfg.window + cfg.canvas
         return "mfma", "TFLOP/s", 4.0 * M * hq * keys * hd
+    if kind == "attention_global":
+        return "mfma", "TFLOP/s", None     # depends on the prefix length: computed by the caller
     if kind == "sample_pass1":
         return "hbm", "GB/s", M * V * 2
     return None, None, None
@@ -116,6 +118,22 @@ def cpu_baseline(budget_note: str):
     L = synth.CONFIGS["full"].n_layers
     block = 12 * (L * t_layer + t_head + t_sample) + L * t_layer
     cores = len(os.sched_getaffinity(0))
+    # the same sample on one core (BLAS and OpenMP pools limited to one thread)
+    one_core = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.denoise_step(cfg8, w8, kv, np.full((1, cfg.canvas), 8), 1.0)
+            t_layer1 = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            O.denoise_step(cfg, w, kv, canvas, 1.0)
+            t_a1 = time.perf_counter() - t0
+        block1 = 12 * (L * t_layer1 + max(t_a1 - t_layer1, 0.0) + t_sample) + L * t_layer1
+        one_core = {"value": 256.0 / block1, "cores": 1,
+                    "sample": f"layer alone {t_layer1:.2f}s, layer + head {t_a1:.2f}s on one core, same extrapolation"}
+    except Exception as exc:  # threadpoolctl missing or a pool it cannot limit
+        one_core = {"error": repr(exc)}
     return {
         "value": 256.0 / block,
         "unit": "tok/s",
@@ -126,14 +144,23 @@ def cpu_baseline(budget_note: str):
                    f"{t_prefill:.1f}s untimed); extrapolated to 30 layers x (12 steps + append) per "
                    f"256-token block; {budget_note}"),
         "block_s_extrapolated": block,
+        "one_core": one_core,
     }
 
 
-def pmc_workload(n_steps: int = 2) -> None:
+def moe_bytes(kind, cfg, counts):
+    """Algorithmic bytes of one launch of an expert GEMM kind, from one layer's expert
+    token counts (see algorithmic_work)."""
+    return algorithmic_work(kind, cfg, cfg.canvas, [counts])[2]
+
+
+def pmc_workload(n_steps: int = 2, counts_out: str = None) -> None:
     """Workload for hardware-counter passes (rocprofv3 --pmc): first the library's
     plain 256 MiB copy kernel (a known byte count that calibrates the traffic
     counters), then n_steps denoising steps of the full model over a 1024-token
-    prefix.  Nothing is timed."""
+    prefix.  Nothing is timed.  counts_out: a JSON file that receives this run's own
+    per-layer expert token counts of every denoising pass and the gate/up and down
+    GEMMs' algorithmic bytes per launch they imply."""
     import torch
     from discrete_diffusion_block_amd import dg, synth
 
@@ -148,10 +175,21 @@ def pmc_workload(n_steps: int = 2) -> None:
     eng.prefill_kv(synth.make_prompt(cfg, 1, 1024, device="cuda"))
     logits = torch.empty(1, cfg.canvas, cfg.vocab, dtype=torch.bfloat16, device="cuda")
     canvas = torch.full((1, cfg.canvas), cfg.vocab, dtype=torch.int32, device="cuda")
+    passes = []
     for s in range(n_steps):
         eng.denoise_step(canvas, 1.0 - s / n_steps, logits)
+        passes.append(eng.moe_counts().cpu().tolist())
     torch.cuda.synchronize()
-    log(f"pmc workload done ({n_steps} denoising steps)")
+    flat = [c for p in passes for c in p]
+    rec = {"workload": "python3 bench.py --pmc-workload: 2 denoising steps of the 30-layer model, 1024-token prefix",
+           "experts_used_per_layer_mean": sum(sum(1 for x in c if x) for c in flat) / len(flat),
+           "moe_gate_up_bytes_per_launch": sum(moe_bytes("moe_gate_up", cfg, c) for c in flat) / len(flat),
+           "moe_down_bytes_per_launch": sum(moe_bytes("moe_down", cfg, c) for c in flat) / len(flat),
+           "counts": passes}
+    if counts_out:
+        with open(counts_out, "w") as fh:
+            json.dump(rec, fh)
+    log(f"pmc workload done ({n_steps} denoising steps, {rec['experts_used_per_layer_mean']:.1f} experts/layer)")
 
 
 def summarize_pmc(root: str) -> str:
@@ -178,12 +216,16 @@ def summarize_pmc(root: str) -> str:
     return "\n".join(lines)
 
 
-def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prompt: int) -> str:
+def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prompt: int,
+                    bench_json: str = None) -> str:
     """Per-kernel launch statistics from the rocprofv3 kernel-trace CSV under root of a
     `bench.py --steps S --warmup W` run: the denoising passes of the S timed blocks.
     Passes start at the engine's prep kernel; the prompt prefill takes the first
     ceil(prompt / 512) passes, then each block runs denoise_steps denoising passes (the
-    ones that end in the vocabulary head) and one append pass."""
+    ones that end in the vocabulary head) and one append pass.  bench_json: that same
+    run's JSON line, whose roofline figure (the dominant kind's algorithmic bytes per
+    launch over the run's last denoise_steps passes, from their own expert counts) is
+    divided by the trace's average duration of the same launches."""
     import csv
     import glob
     import collections
@@ -212,27 +254,43 @@ def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prom
     for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{k[:58]:58s} {len(v):6d} {sum(v) / 1e3:9.2f} {sum(v) / len(v):8.2f} "
                      f"{min(v):8.2f} {max(v):8.2f} {100 * sum(v) / total:5.1f}%")
-    # the run's last denoise_steps denoising passes are the ones in which bench.py times
-    # the dominant kind with HIP events (the roofline figure of its JSON line)
-    roof = [p for p in passes if any("head_gemm" in r["Kernel_Name"] for r in p)][-denoise_steps:]
+    # the run's last denoise_steps denoising passes of the 30-layer model are the ones in
+    # which bench.py times the dominant kind with HIP events (the roofline figure of its
+    # JSON line); they precede the sampler and the secondary workloads' passes
+    heads = [p for p in passes if sum("head_gemm" in r["Kernel_Name"] for r in p) == 1 and len(p) > 300]
+    roof = heads[steps * denoise_steps + warmup * denoise_steps + denoise_steps:][:denoise_steps]
     ragg = collections.defaultdict(list)
     for p in roof:
         for r in p:
             name = r["Kernel_Name"].replace("void ", "").split("(")[0]
             ragg[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines.append("")
-    lines.append(f"roofline passes (the run's last {len(roof)} denoising passes, in which bench.py times "
-                 f"the dominant kind with HIP events on its launches):")
-    for k, v in sorted(ragg.items(), key=lambda kv: -sum(kv[1]))[:6]:
+    lines.append(f"roofline passes ({len(roof)} denoising passes after the profiled block, in which bench.py "
+                 f"times the dominant kind with HIP events on its launches):")
+    for k, v in sorted(ragg.items(), key=lambda kv: -sum(kv[1]))[:8]:
         lines.append(f"{k[:58]:58s} {len(v):6d} launches, avg {sum(v) / len(v):8.2f} us")
+    if bench_json:
+        js = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        rf = js["roofline"]
+        name = f"dg::{rf['kernel']}_kernel"
+        v = ragg.get(name)
+        if v:
+            avg = sum(v) / len(v)
+            ach = rf["algorithmic_per_launch"] / (avg * 1e-6) / 1e9
+            lines.append(f"{name}: this run's algorithmic {rf['algorithmic_per_launch'] / 1e6:.1f} MB per launch "
+                         f"(its own expert counts, {js.get('experts_used_per_layer_mean')} experts/layer) / trace "
+                         f"average {avg:.2f} us = {ach:.0f} GB/s = {ach / HBM_PEAK_GBS:.3f} of HBM peak; the "
+                         f"HIP-event average of the same launches {rf['avg_launch_ms'] * 1e3:.2f} us -> frac "
+                         f"{rf['frac']}")
     return "\n".join(lines)
 
 
-def write_traffic(fetch_txt: str, write_txt: str, kind: str) -> dict:
+def write_traffic(fetch_txt: str, write_txt: str, kind: str, counts_json: str) -> dict:
     """Calibrated HBM bytes per launch of one kernel kind from the two counter summaries
-    (FETCH_SIZE and WRITE_SIZE passes of --pmc-workload, printed by --summarize-pmc).
-    Each counter is scaled by the ratio of the copy kernel's true byte count (256 MiB
-    read, 256 MiB written) to what the same counter reads for it."""
+    (FETCH_SIZE and WRITE_SIZE passes of --pmc-workload, printed by --summarize-pmc), set
+    against that workload's own algorithmic bytes (its counts file).  Each counter is
+    scaled by the ratio of the copy kernel's true byte count (256 MiB read, 256 MiB
+    written) to what the same counter reads for it."""
     def means(path):
         out = {}
         for line in open(path):
@@ -241,19 +299,232 @@ def write_traffic(fetch_txt: str, write_txt: str, kind: str) -> dict:
                 out[parts[0]] = float(parts[-1])
         return out
     fe, wr = means(fetch_txt), means(write_txt)
+    cj = json.load(open(counts_json))
     copy_kib = float(256 << 10)
     fs, ws = copy_kib / fe["dg::copy16_kernel"], copy_kib / wr["dg::copy16_kernel"]
     name = f"dg::{kind}_kernel"
+    hw = int(round((fe[name] * fs + wr[name] * ws) * 1024))
+    alg = cj.get(f"{kind}_bytes_per_launch")
     t = {"kernel": kind, "source_digest": kernel_source_digest(),
-         "bytes_per_launch": int(round((fe[name] * fs + wr[name] * ws) * 1024)),
+         "bytes_per_launch": hw,
+         "algorithmic_bytes_per_launch": alg,
+         "traffic_over_algorithmic": round(hw / alg, 3) if alg else None,
+         "experts_used_per_layer_mean": cj.get("experts_used_per_layer_mean"),
          "fetch_kib_per_launch_raw": fe[name], "write_kib_per_launch_raw": wr[name],
          "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
          "calibration": f"dg::copy16_kernel copying 256 MiB reads FETCH_SIZE {fe['dg::copy16_kernel']:.1f} KiB "
                         f"and WRITE_SIZE {wr['dg::copy16_kernel']:.1f} KiB",
-         "workload": "python3 bench.py --pmc-workload (denoising passes only: 2 steps, 30 layers)"}
+         "workload": cj.get("workload")}
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
         json.dump(t, fh, indent=1)
     return t
+
+
+def spread_canvas(cfg, n_distinct: int, seed: int = 4):
+    """int32 [1][C]: committed tokens drawn from n_distinct seeded random ids."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randint(0, cfg.vocab, (n_distinct,), generator=g, dtype=torch.int32)
+    return ids[torch.randint(0, n_distinct, (1, cfg.canvas), generator=g)].contiguous()
+
+
+def kind_roofline(eng, cfg, kind, run_pass, reps, counts_fn=None, flops_fn=None):
+    """HIP-event timing of one kind's launches over `reps` passes (run_pass(s) enqueues
+    pass s); the algorithmic amount of every pass from its own expert counts
+    (counts_fn) or flops_fn(s).  Returns (avg launch ms, amount per launch, launches,
+    per-pass extras)."""
+    from discrete_diffusion_block_amd import dg
+    import torch
+    tot_ms, launches, amount_sum, used = 0.0, 0, 0.0, []
+    for s in range(reps):
+        dg.dg_profile_begin(eng.ctx, 8 * cfg.n_layers, kinds=[kind])
+        run_pass(s)
+        p1 = dg.dg_profile_end(eng.ctx)[kind]
+        if counts_fn is not None:
+            counts = counts_fn()
+            amount = algorithmic_work(kind, cfg, cfg.canvas, counts)[2]
+            used += [sum(1 for c in row if c > 0) for row in counts]
+        else:
+            amount = flops_fn(s)
+        tot_ms += p1[0]
+        launches += p1[1]
+        amount_sum += amount * p1[1]
+    torch.cuda.synchronize()
+    return tot_ms / launches, amount_sum / launches, launches, used
+
+
+def roofline_obj(bound, unit, avg_ms, amount, launches, kind, traffic=None, **extra):
+    if unit == "GB/s":
+        achieved, peak = amount / (avg_ms * 1e-3) / 1e9, HBM_PEAK_GBS
+    else:
+        achieved, peak = amount / (avg_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS
+    out = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kind,
+           "avg_launch_ms": round(avg_ms, 4), "launches": launches, "algorithmic_per_launch": round(amount)}
+    out.update(extra)
+    return out
+
+
+def sampler_roofline(eng, cfg, gamma):
+    """The sampler on four distinct 128 MiB logits buffers in rotation (512 MiB: more than
+    the 256 MB Infinity Cache, so every call reads its logits from HBM), each a fully
+    masked 256 x 262144 canvas of the sampler workload (N(0, 4^2) + a +12 spike on 60% of
+    rows).  The whole call is timed with HIP events on the stream; the pass alone with
+    the profiler's events on its launches (dg_test_sample_eb_profiled)."""
+    import torch
+    from discrete_diffusion_block_amd import dg, synth
+    C, V = cfg.canvas, cfg.vocab
+    bufs = [synth.make_sampler_logits(C, V, seed=70 + i, device="cuda").view(1, C, V) for i in range(4)]
+    canv = [torch.full((1, C), V, dtype=torch.int32, device="cuda") for _ in range(4)]
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dg.dg_sample_workspace_size(1, C, V), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    n = 24
+    for c in canv:
+        c.fill_(V)
+    for i in range(4):                                     # warm-up
+        dg.dg_sample_eb(bufs[i], canv[i], gamma, False, nm, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fill_ms = 0.0
+    for c in canv:
+        c.fill_(V)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        dg.dg_sample_eb(bufs[i % 4], canv[i % 4], gamma, False, nm, ws)
+        if i % 4 == 3:
+            for c in canv:
+                c.fill_(V)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / n
+    # the pass alone (and the selection kernels), timed on their own launches
+    for c in canv:
+        c.fill_(V)
+    dg.dg_profile_begin(eng.ctx, 16 * n)
+    for i in range(n):
+        dg.dg_test_sample_eb_profiled(eng.ctx, bufs[i % 4], canv[i % 4], gamma, False, nm, ws)
+        if i % 4 == 3:
+            for c in canv:
+                c.fill_(V)
+    prof = dg.dg_profile_end(eng.ctx)
+    pass_ms = prof["sample_pass1"][0] / prof["sample_pass1"][1]
+    nbytes = C * V * 2
+    return {"bound": "hbm", "achieved": round(nbytes / (pass_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(nbytes / (pass_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "sample_partials (entropy/argmax pass) on 4 rotating 128 MiB buffers",
+            "avg_launch_ms": round(pass_ms, 4), "bytes_per_launch": nbytes,
+            "call": {"avg_call_ms": round(call_ms, 4),
+                     "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+                     "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "note": "whole dg_sample_eb call: pass, selection, the canonical-entropy passes "
+                             "(they return at once for certified decisions), launch gaps; the canvas "
+                             "refill every 4 calls is inside the span"},
+            "select_ms": round(prof["sample_select"][0] / max(1, prof["sample_select"][1]), 4),
+            "canonical_passes_ms": round((prof["sample_canon"][0] + prof["sample_select_canon"][0]) /
+                                         max(1, prof["sample_canon"][1]), 4)}
+
+
+def spread_line(eng, cfg, n_distinct, reps):
+    """The expert GEMMs at a routing spread like the Technical Report's (~84 unique experts
+    per layer on a real 256-token canvas, §6 GPU time breakdown, MoE).  With random-init
+    weights a denoising pass cannot show it: the timestep embedding (norm ~37 against ~1 for
+    a token embedding) makes every canvas row alike, and the whole canvas goes to ~15
+    experts.  The causal encoder pass that appends a finished canvas adds no timestep
+    embedding, and its causal contexts differ from row to row: its 2048 assignments reach
+    93-99 of the 128 experts per layer (measured: 92.8 over a canvas of 6 distinct token
+    ids, 99 over 256 random ones), about 21 tokens each -- the regime of a trained model.
+    Timed: that append pass over a canvas of n_distinct ids, repeated over the same cache
+    slots, with HIP events on the expert GEMMs' launches (layers 0-28: the encoder's last
+    layer feeds no K/V and has no FFN)."""
+    import torch
+    canvas = spread_canvas(cfg, n_distinct).cuda()
+    L0 = eng.lengths[0]
+    L = cfg.n_layers
+
+    def append(s):
+        eng.kv.len[0] = L0
+        eng.prefill_kv(canvas)
+
+    append(0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(reps):
+        append(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pass_ms = e0.elapsed_time(e1) / reps
+    out = {}
+    for kind in ("moe_gate_up", "moe_down"):
+        avg, amount, launches, used = kind_roofline(
+            eng, cfg, kind, append, reps, counts_fn=lambda: eng.moe_counts()[:L - 1].cpu().tolist())
+        out[kind] = roofline_obj("hbm", "GB/s", avg, amount, launches, kind,
+                                 experts_used_per_layer_mean=round(sum(used) / len(used), 1),
+                                 tokens_per_used_expert=round(2048 * (L - 1) / sum(used), 1))
+    eng.kv.len[0] = L0
+    return {"workload": f"causal append pass of the 30-layer model over a 256-token canvas of {n_distinct} "
+                        f"distinct token ids: the random-init router spreads its 2048 assignments to "
+                        f"{out['moe_gate_up']['experts_used_per_layer_mean']} of 128 experts per layer (the "
+                        f"Technical Report's ~84 on a real canvas)",
+            "append_pass_ms": round(pass_ms, 3), "roofline": out["moe_gate_up"], "moe_down": out["moe_down"]}
+
+
+def long_context_line(packed, args):
+    """The long-context batched workload: the same 30-layer model with every 6th layer
+    attending globally (layers 5, 11, ..., 29; the rest a 1024-token window), 8 sequences
+    with 32768-token random prompts prefilled once, then whole blocks (12 steps + append)
+    for all 8 canvases at once."""
+    import torch
+    from discrete_diffusion_block_amd import dg, synth
+    cfg = synth.CONFIGS["long"]
+    B, P, C, V = args.lc_batch, args.lc_prompt, cfg.canvas, cfg.vocab
+    blocks = args.lc_warmup + args.lc_steps + 1
+    max_ctx = int(math.ceil((P + C * (blocks + 1)) / 64.0) * 64)
+    eng = dg.Engine(cfg, packed, max_batch=B, max_ctx=max_ctx, packed=True)
+    prompt = synth.make_prompt(cfg, B, P, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eng.prefill_kv(prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    log(f"long context: prefill {B} x {P} tokens {prefill_s:.1f}s")
+    logits = torch.empty(B, C, V, dtype=torch.bfloat16, device="cuda")
+    nm = torch.empty(B, dtype=torch.int32, device="cuda")
+    canvas = torch.empty(B, C, dtype=torch.int32, device="cuda")
+    for _ in range(args.lc_warmup):
+        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.lc_steps):
+        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = B * C * args.lc_steps / wall
+    # global-layer attention: HIP events on its launches over one block's denoising passes
+    hq, hd = cfg.n_q_heads, cfg.head_dim
+    c2 = torch.full((B, C), V, dtype=torch.int32, device="cuda")
+    lens = [int(x) for x in eng.lengths[:B]]
+    flops = sum(4.0 * C * hq * (L + C) * hd for L in lens)
+    reps = args.denoise_steps
+    avg, amount, launches, _ = kind_roofline(
+        eng, cfg, "attention_global", lambda s: eng.denoise_step(c2, 1.0 - s / reps, logits), reps,
+        flops_fn=lambda s: flops)
+    dg.dg_profile_begin(eng.ctx, 20000)
+    eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    torch.cuda.synchronize()
+    prof = dg.dg_profile_end(eng.ctx)
+    eng.close()
+    return {"metric": "output tok/s (8 canvases of 256 tokens, 12 denoise steps + KV append per block)",
+            "value": round(value, 1), "unit": "tok/s", "ms_per_block": round(wall * 1e3 / args.lc_steps, 2),
+            "workload": f"long-context batched block generation: 30 MoE layers (every 6th global, the rest "
+                        f"window 1024), batch {B}, {P}-token random prompts prefilled once ({prefill_s:.1f}s), "
+                        f"12 steps, gamma {args.gamma}",
+            "blocks": args.lc_steps, "warmup": args.lc_warmup,
+            "roofline": roofline_obj("mfma", "TFLOP/s", avg, amount, launches, "attention_global",
+                                     keys_per_query=[L + C for L in lens]),
+            "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]}}
 
 
 def main():
@@ -265,13 +536,23 @@ def main():
     ap.add_argument("--gamma", type=float, default=2.0)
     ap.add_argument("--prompt", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline only: skip the sampler, spread-routing and long-context lines")
+    ap.add_argument("--spread-distinct", type=int, default=6,
+                    help="distinct token ids of the spread-routing canvas")
+    ap.add_argument("--lc-batch", type=int, default=8)
+    ap.add_argument("--lc-prompt", type=int, default=32768)
+    ap.add_argument("--lc-steps", type=int, default=2, help="timed blocks of the long-context line")
+    ap.add_argument("--lc-warmup", type=int, default=1)
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run the hardware-counter workload (copy calibration + 2 denoising steps) and exit")
+    ap.add_argument("--counts-out", metavar="JSON", help="with --pmc-workload: where its expert counts go")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel counter means from rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print per-kernel launch statistics from rocprofv3 kernel-trace CSVs under DIR and exit")
-    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_TXT", "WRITE_TXT", "KIND"),
+    ap.add_argument("--bench-json", metavar="FILE", help="with --summarize-trace: the profiled run's JSON line")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_TXT", "WRITE_TXT", "KIND", "COUNTS_JSON"),
                     help="write profiles/traffic.json for KIND from two --summarize-pmc outputs and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -279,7 +560,7 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.warmup, args.steps, args.denoise_steps,
-                              args.prompt))
+                              args.prompt, args.bench_json))
         return
     if args.write_traffic:
         print(json.dumps(write_traffic(*args.write_traffic)))
@@ -298,11 +579,11 @@ def main():
         sys.exit(1)
     dg.lib()
     if args.pmc_workload:
-        pmc_workload()
+        pmc_workload(counts_out=args.counts_out)
         return
     cfg = synth.CONFIGS["full"]
     C, V = cfg.canvas, cfg.vocab
-    n_blocks = args.warmup + args.steps + 3
+    n_blocks = args.warmup + args.steps + 4
     max_ctx = int(math.ceil((args.prompt + C * n_blocks) / 64.0) * 64)
     t0 = time.time()
     w = synth.make_weights(cfg, device="cuda")
@@ -347,11 +628,40 @@ def main():
     log("per-kind kernel ms in one block: " +
         ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in sorted(prof.items(), key=lambda kv: -kv[1][0]) if v[1]))
 
-    # ---- denoise step alone (denoise + sampler)
+    # ---- roofline of the dominant kernel kind: among the kinds bound by HBM or MFMA
+    # (the row kernels are latency-bound), the one with the most time in the profiled
+    # block.  Its launches are timed alone (HIP events on the engine's stream around
+    # that kind only) over the denoising passes of one block's worth of steps on a fresh
+    # all-[MASK] canvas; the algorithmic amount of each pass uses that pass's own
+    # per-layer expert counts.
+    dom = max((k for k in prof if prof[k][1] and algorithmic_work(k, cfg, C, None)[0] and k != "attention_global"),
+              key=lambda k: prof[k][0])
     c2 = torch.full((1, C), V, dtype=torch.int32, device="cuda")
+    reps = args.denoise_steps
+
+    def dom_pass(s):
+        eng.denoise_step(c2, 1.0 - s / reps, logits)
+
+    bound, unit, _ = algorithmic_work(dom, cfg, C, None)
+    counts_fn = (lambda: eng.moe_counts().cpu().tolist()) if dom.startswith("moe") else None
+    flops_fn = None if counts_fn else (lambda s: algorithmic_work(dom, cfg, C, None)[2])
+    avg_ms, amount, dom_launches, used = kind_roofline(eng, cfg, dom, dom_pass, reps, counts_fn, flops_fn)
+    log(f"{dom}: {dom_launches} launches, {avg_ms * 1e3:.2f} us average")
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("kernel") == dom and t.get("source_digest") == kernel_source_digest():
+            traffic = t.get("bytes_per_launch")
+    roofline = roofline_obj(bound, unit, avg_ms, amount, dom_launches, dom, traffic)
+    if not used:
+        used = [sum(1 for c in row if c > 0) for row in eng.moe_counts().cpu().tolist()]
+    experts = round(sum(used) / len(used), 1)
+
+    # ---- denoise step alone (denoise + sampler)
+    c2.fill_(V)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    reps = args.denoise_steps
     for s in range(reps):
         eng.denoise_step(c2, 1.0 - s / reps, logits)
         eng.sample_eb(logits, c2, args.gamma, s == reps - 1, nm)
@@ -359,65 +669,6 @@ def main():
     torch.cuda.synchronize()
     denoise_ms = e0.elapsed_time(e1) / reps
 
-    # ---- roofline of the dominant kernel kind: among the kinds bound by HBM or MFMA
-    # (the row kernels are latency-bound), the one with the most time in the profiled
-    # block.  Its launches are timed alone (HIP events on the engine's stream around
-    # that kind only) over the denoising passes of one block's worth of steps; the
-    # algorithmic amount of each pass uses that pass's own per-layer expert counts.
-    dom = max((k for k in prof if prof[k][1] and algorithmic_work(k, cfg, C, None)[0]),
-              key=lambda k: prof[k][0])
-    c2.fill_(V)
-    dom_ms, dom_launches, amount_sum, used = 0.0, 0, 0.0, []
-    for s in range(reps):
-        dg.dg_profile_begin(eng.ctx, 4 * cfg.n_layers, kinds=[dom])
-        eng.denoise_step(c2, 1.0 - s / reps, logits)
-        p1 = dg.dg_profile_end(eng.ctx)[dom]
-        counts = eng.moe_counts().cpu().tolist()
-        eng.sample_eb(logits, c2, args.gamma, s == reps - 1, nm)
-        bound, unit, amount = algorithmic_work(dom, cfg, C, counts)
-        dom_ms += p1[0]
-        dom_launches += p1[1]
-        amount_sum += amount * p1[1]
-        used += [sum(1 for c in row if c > 0) for row in counts]
-    torch.cuda.synchronize()
-    avg_ms = dom_ms / dom_launches
-    amount = amount_sum / dom_launches
-    log(f"{dom}: {dom_launches} launches, {avg_ms * 1e3:.2f} us average")
-    roofline = None
-    if bound is not None:
-        if unit == "GB/s":
-            achieved, peak = amount / (avg_ms * 1e-3) / 1e9, HBM_PEAK_GBS
-        else:
-            achieved, peak = amount / (avg_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS
-        traffic = None
-        tfile = os.path.join(ROOT, "profiles", "traffic.json")
-        if os.path.exists(tfile):
-            t = json.load(open(tfile))
-            if t.get("kernel") == dom and t.get("source_digest") == kernel_source_digest():
-                traffic = t.get("bytes_per_launch")
-        roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                    "avg_launch_ms": round(avg_ms, 4), "launches": dom_launches,
-                    "algorithmic_per_launch": round(amount)}
-
-    # the whole sampler call (entropy/argmax pass over all 256 rows' logits + selection) on a
-    # fully masked canvas, 10 calls back to back; the canvas reset between calls (a fill
-    # kernel) is inside the timed span, so the rate is slightly understated
-    n_s = 10
-    es0, es1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    es0.record(stream)
-    for _ in range(n_s):
-        c2.fill_(V)
-        eng.sample_eb(logits, c2, args.gamma, False, nm)
-    es1.record(stream)
-    torch.cuda.synchronize()
-    samp_ms = es0.elapsed_time(es1) / n_s
-    samp_bytes = C * V * 2
-    sampler = {"bound": "hbm", "achieved": round(samp_bytes / (samp_ms * 1e-3) / 1e9, 1),
-               "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "frac": round(samp_bytes / (samp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-               "kernel": "dg_sample_eb call (entropy/argmax pass + selection)",
-               "avg_call_ms": round(samp_ms, 4), "bytes_per_call": samp_bytes}
     out = {
         "metric": "output tok/s (256-tok canvas, 12 denoise steps + KV append per block)",
         "value": round(value, 1),
@@ -433,19 +684,38 @@ def main():
         "data": "synthetic (random-init N(0,0.02) bf16 weights, uniform-random 1024-token prompt)",
         "config": {"workload": "full 256-token block generation: 30 MoE layers d2816, 16q/8kv x128, "
                                "128 experts top-8 (F 704) + shared (F 2112), vocab 262144 tied, "
-                               "1024-token prompt, 12 steps, gamma 2.0, batch 1",
+                               "1024-token prompt, 12 steps, gamma 2.0, batch 1; the random-init router sends "
+                               f"the all-[MASK] canvas to ~{experts} of the 128 experts per layer, so the MoE "
+                               "streams that many experts' weights (a trained model spreads to ~84: see "
+                               "spread_routing)",
                    "global_batch": 1, "seq_len": args.prompt, "canvas": C,
                    "denoise_steps": args.denoise_steps, "parallelism": "single GPU"},
         "denoise_step_ms": round(denoise_ms, 3),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 3),
         "tokens_per_forward": round(C / (args.denoise_steps + 1), 3),
-        "experts_used_per_layer_mean": round(sum(used) / len(used), 1),
+        "experts_used_per_layer_mean": experts,
         "profiled_block_ms": round(prof_block_ms, 3),
         "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]},
         "roofline": roofline,
-        "sampler_roofline": sampler,
+        "sampler_roofline": None,
+        "spread_routing": None,
+        "long_context_batch8": None,
         "cpu_baseline": None,
     }
+    if not args.no_extras:
+        log("sampler on rotating buffers...")
+        out["sampler_roofline"] = sampler_roofline(eng, cfg, args.gamma)
+        log("spread routing...")
+        out["spread_routing"] = spread_line(eng, cfg, args.spread_distinct, reps)
+        packed = eng.weights
+        eng.close()
+        del logits
+        torch.cuda.empty_cache()
+        log("long-context batched workload...")
+        try:
+            out["long_context_batch8"] = long_context_line(packed, args)
+        except Exception as exc:  # report, but never lose the headline
+            out["long_context_batch8"] = {"error": repr(exc)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)...")
         try:

@@ -183,6 +183,9 @@ struct Ws {
   int32_t* sflag;      // [batch]: sequence deferred to the canonical entropy
   int32_t* smoved;     // [batch]
   int32_t* samax;      // [batch][C]
+  float* shf;          // [batch][C]: fast entropies
+  float2* swin;        // [batch]: boundary windows
+  int32_t* skstar;     // [batch]
 };
 
 struct Carver {
@@ -207,6 +210,9 @@ size_t carve_sampler(Carver& cv, int batch, int canvas, int vocab, Ws* ws) {
   ws->sflag = cv.take<int32_t>(batch);
   ws->smoved = cv.take<int32_t>(batch);
   ws->samax = cv.take<int32_t>(rows);
+  ws->shf = cv.take<float>(rows);
+  ws->swin = cv.take<float2>(batch);
+  ws->skstar = cv.take<int32_t>(batch);
   return cv.off;
 }
 
@@ -317,7 +323,8 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     // In the encoder only the keys/values are observable; the last layer's
     // attention output and FFN feed nothing, so they are not computed.
     if (!g.denoise && l == nl - 1) break;
-    DG_TIMED(ctx, DG_K_ATTENTION, launch_attention(ws.q, hq, kvl, g, ws.o, s));
+    DG_TIMED(ctx, kvl.window == 0 ? DG_K_ATTENTION_GLOBAL : DG_K_ATTENTION,
+             launch_attention(ws.q, hq, kvl, g, ws.o, s));
     DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
     // The shared expert depends only on h: it runs on the side stream while the
     // routed experts' routing chain (small, latency-bound kernels) runs here.  It
@@ -460,16 +467,17 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
            launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
                             canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax,
-                            o.e_stop, o.step, o.done_step, ws.sflag, ws.smoved, ws.samax, s));
+                            o.e_stop, o.step, o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin,
+                            ws.skstar, s));
   // sequences whose decision the fast entropies could not certify: canonical entropy
   // (every workgroup of a decided sequence returns at once)
   DG_TIMED(ctx, DG_K_SAMPLE_CANON,
            launch_canon_partials(d_logits, d_canvas, batch, canvas, vocab, o.temperature, ws.part, ws.sflag,
-                                 ws.cpart, s));
+                                 ws.shf, ws.swin, ws.cpart, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT_CANON,
            launch_eb_select_canon(ws.cpart, sample_chunks(vocab), d_canvas, batch, canvas, vocab, gamma,
                                   commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax, o.e_stop, o.step,
-                                  o.done_step, ws.sflag, ws.smoved, ws.samax, s));
+                                  o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin, ws.skstar, s));
   return check_launch("sampler");
 }
 
@@ -822,6 +830,24 @@ dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count) {
   return DG_OK;
 }
 
+dg_status dg_test_sample_eb_profiled(dg_ctx* ctx, const uint16_t* d_logits, int32_t* d_canvas, int batch,
+                                     int canvas, int vocab, float gamma, int commit_all, int32_t* d_n_masked,
+                                     void* d_ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  size_t need = 0;
+  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
+  if (st != DG_OK) return st;
+  if (!d_logits || !d_canvas || !d_n_masked || !d_ws) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
+  Carver cv{base};
+  Ws ws;
+  carve_sampler(cv, batch, canvas, vocab, &ws);
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, nullptr, nullptr, d_n_masked, ws,
+                     (hipStream_t)stream, ctx);
+}
+
 dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset) {
   if (!ctx || !offset || batch < 1 || batch > ctx->cfg.max_batch) return fail(DG_ERR_INVALID_ARG, "bad arguments");
   Ws ws;
@@ -865,7 +891,7 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
     return fail(DG_ERR_INVALID_ARG, "bad selection arguments");
   launch_eb_select(nullptr, nullptr, 0, d_entropy, d_argmax, d_canvas, batch, canvas, vocab, gamma,
                    commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, nullptr, nullptr,
-                   nullptr, (hipStream_t)stream);
+                   nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
   return check_launch("eb select");
 }
 

@@ -155,17 +155,21 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                      int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s);
+                      int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
+                      int32_t* kstar_ws, hipStream_t s);
 // Pass 3: exact integer sums of the canonical entropy for the masked rows of the
-// flagged sequences (tau: the temperature; part: pass 1's partials, for the row max).
+// flagged sequences -- all of them (flag 1) or those whose fast entropy Hf lies in the
+// sequence's window win (flag 2) (tau: the temperature; part: pass 1's partials, for
+// the row max).
 void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
-                           float tau, const float4* part, const int32_t* flag, ulonglong2* cpart,
-                           hipStream_t s);
+                           float tau, const float4* part, const int32_t* flag, const float* Hf, const float2* win,
+                           ulonglong2* cpart, hipStream_t s);
 // Pass 4: the decision of the flagged sequences on the canonical entropy.
 void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
                             float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                            int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s);
+                            int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
+                            int32_t* kstar_ws, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

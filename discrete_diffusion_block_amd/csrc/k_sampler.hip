@@ -266,10 +266,18 @@ __global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __r
                                                              int vocab, int nchunks, float tau,
                                                              const float4* __restrict__ part,
                                                              const int32_t* __restrict__ flag,
+                                                             const float* __restrict__ Hf,
+                                                             const float2* __restrict__ win,
                                                              ulonglong2* __restrict__ cpart) {
   __shared__ uint64_t red[2][4];
-  const int row = blockIdx.y, ch = blockIdx.x;
-  if (flag[row / C] == 0 || canvas[row] != vocab) return;   // uniform per workgroup
+  const int row = blockIdx.y, ch = blockIdx.x, b = row / C;
+  const int f = flag[b];
+  if (f == 0 || canvas[row] != vocab) return;   // uniform per workgroup
+  if (f == 2) {                                 // only the rows of the boundary window
+    const float h = Hf[row];
+    const float2 w = win[b];
+    if (!(h >= w.x && h <= w.y)) return;
+  }
   float m = -INFINITY;
   for (int c = 0; c < nchunks; ++c) m = fmaxf(m, part[(size_t)row * nchunks + c].w);
   const double md = (double)m, inv = 1.0 / (double)tau;
@@ -309,11 +317,11 @@ __global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __r
 }
 
 void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
-                           float tau, const float4* part, const int32_t* flag, ulonglong2* cpart,
-                           hipStream_t s) {
+                           float tau, const float4* part, const int32_t* flag, const float* Hf, const float2* win,
+                           ulonglong2* cpart, hipStream_t s) {
   const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
   launch_kernel(canon_partials_kernel, dim3(nchunks, batch * C), dim3(256), 0, s, nullptr, logits, canvas, C,
-                vocab, nchunks, tau, part, flag, cpart);
+                vocab, nchunks, tau, part, flag, Hf, win, cpart);
 }
 
 // ---------------------------------------------------------------- selection
@@ -347,9 +355,14 @@ struct SelArgs {
   float e_stop;
   int step;
   int32_t* done_step;
-  int32_t* flag;             // [batch]: SEL_FAST sets 1 where it defers the decision, else 0
+  int32_t* flag;             // [batch]: SEL_FAST sets 0 (decided), 1 (deferred: every masked row's Ĥ is
+                             // needed) or 2 (deferred: only the order of the rows in a window at the
+                             // budget boundary is open; k* is already certain)
   int32_t* moved;            // [batch]: SEL_FAST's count of moved argmaxes, for SEL_CANON
   int32_t* amax_ws;          // [batch][C]: every masked row's argmax, for SEL_CANON
+  float* Hf_ws;              // [batch][C]: every masked row's fast entropy
+  float2* win;               // [batch]: the window [lo, hi] of fast entropies whose Ĥ decides (flag 2)
+  int32_t* kstar_ws;         // [batch]: the certain k* (flag 2)
 };
 
 template <int TPR, int MODE>   // threads per canvas row (chunk merge and rank count)
@@ -369,6 +382,8 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
   // phase 1: entropy and argmax of each masked row
   float H = INFINITY;
   int a = 0;
+  float hf = 0.f;         // SEL_CANON, flag 2: the row's fast entropy
+  bool in_win = true;     // SEL_CANON, flag 2: the row lies in the boundary window
   if (MODE == SEL_FAST) {
     // the row's threads merge interleaved subsets of its chunks, then combine
     // through shuffles
@@ -404,8 +419,14 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
     // H >= 0 exactly; the fp32 partials can leave a rounding residue of ~1e-7 below
     if (masked) H = fmaxf(logf(S) + T / S, 0.f);
   } else if (MODE == SEL_CANON) {
+    // flag 1: every masked row's Ĥ; flag 2: Ĥ of the window rows only (their sums are the
+    // only ones pass 3 computed), the fast entropy elsewhere
+    if (masked && A.flag[b] == 2) {
+      hf = A.Hf_ws[ridx];
+      in_win = hf >= A.win[b].x && hf <= A.win[b].y;
+    }
     uint64_t S = 0, T = 0;
-    if (masked)
+    if (masked && in_win)
       for (int k = sub; k < A.nchunks; k += TPR) {
         const ulonglong2 p = A.cpart[ridx * A.nchunks + k];
         S += p.x;
@@ -417,7 +438,7 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
       T += __shfl_xor(T, o, 64);
     }
     if (masked) {
-      H = canon_entropy(S, T);
+      H = in_win ? canon_entropy(S, T) : hf;
       a = A.amax_ws[ridx];
     }
   } else if (masked) {
@@ -428,7 +449,10 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
   // unmasked rows (and the padding up to a multiple of 8) take the largest key,
   // which no masked row's key exceeds, so they are never counted below one
   const int Cp = (C + 7) & ~7;
-  const uint64_t key = masked ? eb_key(H, r) : ~0ull;
+  uint64_t key = masked ? eb_key(H, r) : ~0ull;
+  // flag 2: rows below the window precede every window row (in position order), rows
+  // above it follow every masked row; only the window rows are ranked by (Ĥ, position)
+  if (MODE == SEL_CANON && masked && !in_win) key = hf < A.win[b].x ? (uint64_t)r : ~0ull;
   if (sub == 0 && r < Cp) keys[r] = key;
   if (sub == 0 && r < C) Hpos[r] = H;
   // adaptive stop (prev_amax given; §3.3): the rows whose argmax moved since the
@@ -466,8 +490,10 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
   if (threadIdx.x == 0) {
     const int n = nm_s;
     const double g = (double)A.gamma;
-    bool cert = true;
+    bool cert = true;       // SEL_FAST: the fast entropies decide
+    bool order_only = true; // SEL_FAST, not cert: only the order at the boundary is open
     bool stop = false;
+    float2 window = make_float2(0.f, 0.f);
     if (A.prev_amax && n_moved == 0 && n > 0) {
       // mean entropy of the masked rows: float64 running sum in position order
       double hs = 0.0;
@@ -475,10 +501,12 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
         if (A.canvas[(size_t)b * C + i] == A.vocab) hs += (double)Hpos[i];
       const double mean = hs / n;
       stop = mean < (double)A.e_stop;
-      if (MODE == SEL_FAST && fabs(mean - (double)A.e_stop) <= kCertEps + kSumSlack) cert = false;
+      if (MODE == SEL_FAST && fabs(mean - (double)A.e_stop) <= kCertEps + kSumSlack) cert = order_only = false;
     }
     int ks;
-    if (A.commit_all || stop || n == 0) {
+    if (MODE == SEL_CANON && A.flag[b] == 2) {
+      ks = A.kstar_ws[b];                     // certain; the ranking above settled the order
+    } else if (A.commit_all || stop || n == 0) {
       ks = n;
     } else {
       // running fp64 sum in rank order (S_k of the first k rows); k_nat = the number
@@ -511,16 +539,28 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
         const double S_ks = k >= 1 ? S_at : (double)sortedH[0];
         if (ks < n) {
           const double next = S_ks + (double)sortedH[ks];
-          if ((double)sortedH[ks] - (double)sortedH[ks - 1] <= 2.0 * kCertEps) cert = false;
-          if (next - g <= (ks + 1) * kCertEps + kSumSlack) cert = false;
+          if ((double)sortedH[ks] - (double)sortedH[ks - 1] <= 2.0 * kCertEps) {
+            cert = false;
+            // rows with a fast entropy below h_ks - 2 eps are in whatever the Ĥ, rows above
+            // h_(ks+1) + 2 eps out: only the rows between need Ĥ
+            window = make_float2((float)((double)sortedH[ks - 1] - 2.0 * kCertEps),
+                                 (float)((double)sortedH[ks] + 2.0 * kCertEps));
+          }
+          if (next - g <= (ks + 1) * kCertEps + kSumSlack) cert = order_only = false;
         }
-        if (k >= 1 && g - S_at <= k * kCertEps + kSumSlack) cert = false;
+        if (k >= 1 && g - S_at <= k * kCertEps + kSumSlack) cert = order_only = false;
       }
     }
     if (MODE == SEL_FAST && A.flag) {
-      A.flag[b] = cert ? 0 : 1;
+      A.flag[b] = cert ? 0 : (order_only ? 2 : 1);
       if (!cert) {
         A.moved[b] = n_moved;
+        if (order_only) {
+          // widen by a float32 ulp on each side so that the rounding of the bounds to
+          // float can only add rows to the window
+          A.win[b] = make_float2(nextafterf(window.x, -INFINITY), nextafterf(window.y, INFINITY));
+          A.kstar_ws[b] = ks;
+        }
         ks = 0;                               // the canonical pass decides
       }
     }
@@ -537,6 +577,7 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
       if (A.amax_out) A.amax_out[ridx] = masked ? a : -1;                   // -1 on unmasked rows
       if (A.prev_amax) A.prev_amax[ridx] = masked ? a : -1;
       if (A.amax_ws && masked) A.amax_ws[ridx] = a;
+      if (A.Hf_ws && masked) A.Hf_ws[ridx] = H;
     }
     if (masked && rank_s[r] < kstar_s) A.canvas[ridx] = a;
   }
@@ -555,9 +596,11 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                      int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s) {
+                      int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
+                      int32_t* kstar_ws, hipStream_t s) {
   SelArgs a{};
   a.part = part; a.part_arg = part_arg; a.nchunks = nchunks;
+  a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
   a.H_in = H_in; a.amax_in = amax_in;
   a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
   a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
@@ -570,9 +613,11 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
 void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
                             float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
-                            int32_t* flag, int32_t* moved, int32_t* amax_ws, hipStream_t s) {
+                            int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
+                            int32_t* kstar_ws, hipStream_t s) {
   SelArgs a{};
   a.cpart = cpart; a.nchunks = nchunks;
+  a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
   a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
   a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
   a.prev_amax = prev_amax; a.e_stop = e_stop; a.step = step; a.done_step = done_step;

@@ -24,7 +24,8 @@ MAX_BATCH = 64
 
 KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
-                "sample_pass1", "sample_select", "fill", "sample_canon", "sample_select_canon"]
+                "sample_pass1", "sample_select", "fill", "sample_canon", "sample_select_canon",
+                "attention_global"]
 PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
 MOE_GROUP = 64   # tokens per grouped-GEMM work item in the routing tap's item list
 
@@ -89,6 +90,7 @@ def lib():
             "dg_workspace_moe_counts": [vp, i32, C.POINTER(sz)],
             "dg_test_router_topk": [vp, i32, i32, i32, vp, vp, vp],
             "dg_test_force_routing": [vp, vp],
+            "dg_test_sample_eb_profiled": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, sz, vp],
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
             "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
@@ -308,6 +310,15 @@ def dg_test_force_routing(ctx, ids: Optional[torch.Tensor]):
     """ids: int32 device tensor [n_layers][M][top_k] (the expert ids each layer of the
     following passes uses), or None to restore the router."""
     _check(lib().dg_test_force_routing(ctx, _p(ids)))
+
+
+def dg_test_sample_eb_profiled(ctx, logits: torch.Tensor, canvas: torch.Tensor, gamma: float,
+                               commit_all: bool, n_masked: torch.Tensor, ws: torch.Tensor, stream=None):
+    """dg_sample_eb with its launches timed by ctx's profiler."""
+    b, c, v = logits.shape
+    _check(lib().dg_test_sample_eb_profiled(ctx, _p(logits), _p(canvas), b, c, v, float(gamma),
+                                            int(bool(commit_all)), _p(n_masked), _p(ws), ws.numel(),
+                                            _stream(stream)))
 
 
 def dg_test_router_topk(r: torch.Tensor, k: int, ids: torch.Tensor, w: torch.Tensor, stream=None):

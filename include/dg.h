@@ -254,7 +254,7 @@ typedef enum dg_kernel_kind {
   DG_K_PREP = 0, DG_K_EMBED, DG_K_QKV, DG_K_ATTENTION, DG_K_O_PROJ, DG_K_NORM, DG_K_ROUTER,
   DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
   DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL,
-  DG_K_SAMPLE_CANON, DG_K_SAMPLE_SELECT_CANON,
+  DG_K_SAMPLE_CANON, DG_K_SAMPLE_SELECT_CANON, DG_K_ATTENTION_GLOBAL,
   DG_K_COUNT
 } dg_kernel_kind;
 
@@ -268,6 +268,13 @@ dg_status dg_profile_begin(dg_ctx* ctx, int capacity, uint32_t kind_mask);
 /* Stop, wait for the recorded events, and return per kind the summed kernel
  * milliseconds and launch counts (arrays of DG_K_COUNT entries). */
 dg_status dg_profile_end(dg_ctx* ctx, double* ms, int32_t* count);
+/* Attention launches of global layers are timed as DG_K_ATTENTION_GLOBAL, those of
+ * sliding-window layers as DG_K_ATTENTION. */
+/* dg_sample_eb with its launches timed by ctx's profiler (a measurement tap: the
+ * sampler itself needs no ctx). */
+dg_status dg_test_sample_eb_profiled(dg_ctx* ctx, const uint16_t* d_logits, int32_t* d_canvas, int batch,
+                                     int canvas, int vocab, float gamma, int commit_all, int32_t* d_n_masked,
+                                     void* d_ws, size_t ws_bytes, void* stream);
 /* Byte offset, inside a workspace sized for `batch`, of an int32 [n_layers][E]
  * log of the per-expert token counts of the most recent pass through each layer. */
 dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset);
