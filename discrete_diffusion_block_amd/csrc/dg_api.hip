@@ -156,6 +156,8 @@ struct Ws {
   uint16_t* h_rm;  // the FFN-normed activations again, row-major [M][d] (expert row gathers)
   uint16_t* q;     // queries, fragment-major per (sequence, head) [n_pad][hd]
   uint16_t* o;     // attention output, fragment-major [M_pad][Hq*hd]
+  float* att_po;   // attention split-KV partial outputs [kAttnMaxSplitRows * Hq][hd]
+  float2* att_pml; // and their (max, sum) [kAttnMaxSplitRows * Hq]
   float2* rope;
   float* temb;
   float* r;        // router logits fp32 [M][E]
@@ -232,6 +234,8 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->h_rm = cv.take<uint16_t>(M * c.d_model);
   ws->q = cv.take<uint16_t>((size_t)batch * round16(n) * qd);
   ws->o = cv.take<uint16_t>(Mp * qd);
+  ws->att_po = cv.take<float>((size_t)kAttnMaxSplitRows * qd);
+  ws->att_pml = cv.take<float2>((size_t)kAttnMaxSplitRows * c.n_q_heads);
   ws->rope = cv.take<float2>(M * (c.head_dim / 2));
   ws->temb = cv.take<float>(c.d_model);
   ws->r = cv.take<float>(M * c.n_experts);
@@ -324,7 +328,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     // attention output and FFN feed nothing, so they are not computed.
     if (!g.denoise && l == nl - 1) break;
     DG_TIMED(ctx, kvl.window == 0 ? DG_K_ATTENTION_GLOBAL : DG_K_ATTENTION,
-             launch_attention(ws.q, hq, kvl, g, ws.o, s));
+             launch_attention(ws.q, hq, kvl, g, ws.o, ws.att_po, ws.att_pml, s));
     DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
     // The shared expert depends only on h: it runs on the side stream while the
     // routed experts' routing chain (small, latency-bound kernels) runs here.  It

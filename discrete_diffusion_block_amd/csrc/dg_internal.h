@@ -104,8 +104,12 @@ void launch_gemm_head(const uint16_t* h, const uint16_t* embed, uint16_t* logits
                       int K, const int32_t* count, const int32_t* rows, hipStream_t s);
 
 // ---- attention ----
-void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,
-                      uint16_t* o, hipStream_t s);
+// split-KV partials: nsplit * batch * (queries rounded up to 32) stays within this many
+// rows per q head (part_o holds kAttnMaxSplitRows * hq * hd floats, part_ml as many
+// float2 / hd); part_o NULL: no split
+constexpr int kAttnMaxSplitRows = 4096;
+void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
+                      float* part_o, float2* part_ml, hipStream_t s);
 
 // ---- MoE ----
 void launch_topk(const float* r, int M, int E, int k, int32_t* ids, float* w, hipStream_t s);

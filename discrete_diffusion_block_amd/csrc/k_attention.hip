@@ -6,20 +6,26 @@
 //    sliding layers, [0, p] on global ones.
 // The projection kernel has already written this pass's keys/values into the
 // cache at positions len_b .., so every key lives in one contiguous range.
-// q, the key cache and the (transposed) value cache are stored in fragment
-// tiles, so each operand fragment below is one contiguous 1 KiB wave load.
 //
-// Work split: a workgroup owns 16 queries of one q head; its NW waves (8; 4 at
-// hd 32) take interleaved 32-key chunks of the key range (split-KV) and merge
-// their (max, sum, output) partials through LDS in a fixed order.
+// Work split.  A workgroup serves one (sequence, kv head) pair: NWV waves, each
+// owning 32 query rows (two 16-row MFMA blocks) of one q head of the pair's GQA
+// group, so the workgroup covers both q heads of a group and 64 queries of each.
+// Keys stream through LDS in 64-key stages (K and transposed V, copied straight
+// from the cache's fragment tiles into a two-stage ring by direct global->LDS
+// loads, one copy per workgroup) and every wave reads each stage: one K/V byte
+// from L2 feeds 128 query rows.  When the pairs alone give too few workgroups to
+// fill the chip, the key range of each pair is split over several workgroups
+// (split-KV); each writes its unnormalised partial (max, sum, output) and a merge
+// kernel combines the splits in a fixed order.
 //
-// Layout trick: scores are computed transposed, S^T = K . Q^T, with the key
-// rows of each 16-row MFMA block permuted so that a lane ends up holding the
-// scores of 8 consecutive keys (8g .. 8g+7 of the chunk) for its query.  Those
-// 8 probabilities are exactly the lane's B fragment for O^T += V^T . P^T, and
-// V is stored transposed in tiles of 32 keys x 16 hd rows, so the A fragment
-// is one 16-byte slot of a contiguous 1 KiB tile.  Softmax state and output rescaling are lane-local (the lane's
-// output rows all belong to its query); only the chunk max needs two shuffles.
+// Layout trick (kept from the cache format): scores are computed transposed,
+// S^T = K . Q^T, with the key rows of each 16-row block permuted so that a lane
+// holds the scores of 8 consecutive keys for its query -- exactly the lane's B
+// fragment for O^T += V^T . P^T, with V stored transposed in 32-key x 16-hd tiles.
+// Softmax state and output rescaling are lane-local; the stage max needs two
+// shuffles.  P enters the bf16 PV product as a pair hi = bf16(P), lo = bf16(P - hi)
+// (~2^-17 relative), because near-uniform attention does not average a single
+// bf16 rounding of P away.
 #include <math.h>
 
 #include "dg_common.h"
@@ -27,199 +33,351 @@
 
 namespace dg {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int HD, int NW>
-__global__ __launch_bounds__(64 * NW) void attention_kernel(const uint16_t* __restrict__ q, int hq,
-                                                            KvLayer kv, PassGeom g,
-                                                            uint16_t* __restrict__ o) {
-  constexpr int NC = HD / 32;   // k-steps of the score MFMA
-  constexpr int NB = HD / 16;   // output blocks of 16 hd rows
-  __shared__ float Ol[NW][16][HD + 4];
-  __shared__ float ml[NW][16][2];
+// Two fp32 -> bf16 (round to nearest even) in one instruction, packed low first.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+struct AttnArgs {
+  const uint16_t* q;      // fragment-major per (sequence, q head): [npad16][HD]
+  uint16_t* o;            // fragment-major [M_pad][hq * HD] (written when nsplit == 1)
+  float* part_o;          // [nsplit][batch][hq][npad32][HD] unnormalised partial outputs
+  float2* part_ml;        // [nsplit][batch][hq][npad32] (max in log2 units, sum)
+  KvLayer kv;
+  PassGeom g;
+  int hq;
+  int grp;                // q heads per kv head
+  int qt32;               // 32-query tiles per head: ceil(n / 32)
+  int wg_per_pair;        // ceil(grp * qt32 / NWV)
+  int nsplit;
+};
+
+constexpr int kAttnStageKeys = 64;
+
+template <int HD, int NWV>
+__global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
+  constexpr int NC = HD / 32;                 // k-steps of the score MFMA
+  constexpr int NB = HD / 16;                 // 16-row output blocks of hd
+  constexpr int KCH = 2 * NC * 1024;          // bytes of one 32-key K chunk (2 key blocks x NC tiles)
+  constexpr int VCH = NB * 1024;              // bytes of one 32-key transposed-V chunk
+  constexpr int STAGE = 2 * (KCH + VCH);      // one 64-key stage: K chunk 0, K chunk 1, V chunk 0, V chunk 1
+  constexpr int COPIES = STAGE / 1024 / NWV;  // 1 KiB copies per wave per stage
+  static_assert(STAGE % (1024 * NWV) == 0, "whole copies per wave");
+  extern __shared__ __attribute__((aligned(1024))) char ring[];   // [2][STAGE]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, gq = lane >> 4;
-  // XCD-aware order: block bid runs on XCD bid % 8; every workgroup of one
-  // (sequence, kv head) pair -- its q heads x query tiles -- runs on the same XCD,
-  // so that pair's keys and values leave HBM once
-  const int grp = hq / kv.hkv, q_tiles = (g.n + 15) / 16, per_pair = grp * q_tiles;
-  const int rank = blockIdx.x / kXcd;
-  const int pair = (rank / per_pair) * kXcd + (int)(blockIdx.x % kXcd);
-  if (pair >= g.batch * kv.hkv) return;   // uniform per workgroup
-  const int b = pair / kv.hkv, kvh = pair - b * kv.hkv;
-  const int rem = rank % per_pair;
-  const int head = kvh * grp + rem / q_tiles;
-  const int i0 = (rem % q_tiles) * 16;
-  const int n = g.n, len = g.len[b];
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  const PassGeom& g = a.g;
+  const KvLayer& kv = a.kv;
 
-  // query fragments: q is fragment-major per (sequence, head), [n_pad][HD]
-  const int qi = min(i0 + r, n - 1);
-  const int npad = (n + 15) & ~15;
-  const uint16_t* qbase = q + ((size_t)b * hq + head) * (size_t)npad * HD;
-  u32x4 qf[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) qf[c] = ld16(qbase + fm_tile(i0 >> 4, c, HD, lane));
-
-  // key range of this lane's query and of the whole 16-query tile
-  int lo_q, hi_q, lo_t, hi_t;
-  if (g.denoise) {
-    lo_q = kv.window > 0 ? max(0, len - kv.window) : 0;
-    hi_q = len + n;
-    lo_t = lo_q;
-    hi_t = hi_q;
-  } else {
-    const int p = len + qi;
-    lo_q = kv.window > 0 ? max(0, p - kv.window + 1) : 0;
-    hi_q = p + 1;
-    const int pf = len + i0, pl = len + min(i0 + 15, n - 1);
-    lo_t = kv.window > 0 ? max(0, pf - kv.window + 1) : 0;
-    hi_t = pl + 1;
+  // unit -> (pair, workgroup of the pair, split); XCD x owns a contiguous range of the
+  // units, so all workgroups of one pair share an XCD's L2 copy of its keys and values
+  int unit;
+  {
+    const int x = blockIdx.x % kXcd, rank = blockIdx.x / kXcd;
+    const long T = (long)g.batch * kv.hkv * a.wg_per_pair * a.nsplit;
+    const long u0 = (long)x * T / kXcd, u1 = (long)(x + 1) * T / kXcd;
+    if (rank >= u1 - u0) return;              // uniform per workgroup
+    unit = (int)(u0 + rank);
   }
-  const int kc0 = lo_t & ~31;
-  const int nchunk = (hi_t - kc0 + 31) >> 5;
+  const int split = unit % a.nsplit;
+  const int wgp = (unit / a.nsplit) % a.wg_per_pair;
+  const int pair = unit / (a.nsplit * a.wg_per_pair);
+  const int b = pair / kv.hkv, kvh = pair - b * kv.hkv;
+  const int n = g.n, len = g.len[b];
+  const int ngroups = a.grp * a.qt32;
+  const int rg0 = wgp * NWV;
+  const int rg = rg0 + w;
+  const bool active = rg < ngroups;
+  const int head = kvh * a.grp + (active ? rg / a.qt32 : 0);
+  const int q0 = active ? (rg % a.qt32) * 32 : 0;
+
+  // key range of the workgroup (the union over its waves' queries), in 64-key stages
+  int lo_t, hi_t;
+  if (g.denoise) {
+    lo_t = kv.window > 0 ? max(0, len - kv.window) : 0;
+    hi_t = len + n;
+  } else {
+    int qmin = n, qmax = -1;
+    for (int j = 0; j < NWV && rg0 + j < ngroups; ++j) {
+      const int qq = ((rg0 + j) % a.qt32) * 32;
+      qmin = min(qmin, qq);
+      qmax = max(qmax, min(qq + 31, n - 1));
+    }
+    lo_t = kv.window > 0 ? max(0, len + qmin - kv.window + 1) : 0;
+    hi_t = len + qmax + 1;
+  }
+  const int st0 = lo_t / kAttnStageKeys;
+  const int nst = (hi_t - st0 * kAttnStageKeys + kAttnStageKeys - 1) / kAttnStageKeys;
+  const int s_begin = st0 + (int)((long)nst * split / a.nsplit);
+  const int s_end = st0 + (int)((long)nst * (split + 1) / a.nsplit);
+
+  // this lane's two queries (blocks qb = 0, 1: queries q0 + 16 qb + r) and their fragments
+  const int npad16 = (n + 15) & ~15;
+  const uint16_t* qbase = a.q + ((size_t)b * a.hq + head) * (size_t)npad16 * HD;
+  u32x4 qf[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int blk = min((q0 >> 4) + qb, (n - 1) >> 4);     // padded rows read the last block
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[qb][c] = ld16(qbase + fm_tile(blk, c, HD, lane));
+  }
+  int lo_q[2], hi_q[2];                       // visible key range of each of the lane's queries
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (g.denoise) {
+      lo_q[qb] = lo_t;
+      hi_q[qb] = hi_t;
+    } else {
+      const int p = len + q0 + 16 * qb + r;
+      lo_q[qb] = kv.window > 0 ? max(0, p - kv.window + 1) : 0;
+      hi_q[qb] = p + 1;
+    }
+  }
+  // the wave's whole 32-query range, for deciding which stages need no mask at all
+  const int p_first = len + q0, p_last = len + min(q0 + 31, n - 1);
 
   const uint16_t* kbase = kv.k + ((size_t)b * kv.hkv + kvh) * (size_t)kv.max_ctx * HD;
   const uint16_t* vbase = kv.vt + ((size_t)b * kv.hkv + kvh) * (size_t)HD * kv.max_ctx;
-
-  f32x4 acc[NB];
+  // stage st: K chunks 2 st, 2 st + 1 (contiguous), then V chunks 2 st, 2 st + 1
+  auto issue = [&](int st, int slot) {
+    char* dst = ring + slot * STAGE;
+    const uint16_t* ks = kbase + (size_t)(2 * st) * (KCH / 2);
+    const uint16_t* vs = vbase + (size_t)(2 * st) * (VCH / 2);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-
-  // One 32-key chunk: K fragments (2 blocks x NC k tiles) and V fragments (NB
-  // hd blocks), prefetched one chunk ahead through a two-stage pipeline.
-  u32x4 Ka[2][NC], Va[NB], Kb[2][NC], Vb[NB];
-  int kca = 0, kcb = 0;
-  auto load = [&](u32x4 (&K)[2][NC], u32x4 (&Vt)[NB], int& kcs, int step) {
-    kcs = kc0 + 32 * (w + NW * step);
-    const uint16_t* kp = kbase + ((size_t)(kcs >> 5) * 2 * NC << 9) + 8 * lane;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) K[bb][c] = ld16(kp + ((bb * NC + c) << 9));
-    const uint16_t* vp = vbase + ((size_t)(kcs >> 5) * NB << 9) + 8 * lane;
-#pragma unroll
-    for (int hb = 0; hb < NB; ++hb) Vt[hb] = ld16(vp + (hb << 9));
+    for (int c = 0; c < COPIES; ++c) {
+      const int t = w * COPIES + c;           // 1 KiB tile index within the stage
+      const uint16_t* src = t < 2 * KCH / 1024 ? ks + t * 512 : vs + (t - 2 * KCH / 1024) * 512;
+      tile_to_lds<false>(src + 8 * lane, dst + t * 1024);
+    }
   };
-  auto process = [&](const u32x4 (&K)[2][NC], const u32x4 (&Vt)[NB], int kc) {
-    // S^T blocks: block bb row rr <-> key kc + 8*(rr>>2) + 4*bb + (rr&3)
-    f32x4 s[2];
+
+  f32x4 acc[2][NB];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) a = mfma16(K[bb][c], qf[c], a);
-      s[bb] = a;
+    for (int i = 0; i < NB; ++i) acc[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);   // softmax in log2 units
+  lds_char* const lr = lds_launder(ring);
+
+  if (s_begin < s_end) issue(s_begin, 0);
+  for (int st = s_begin; st < s_end; ++st) {
+    const int slot = (st - s_begin) & 1;
+    vm_wait<0>();
+    __builtin_amdgcn_s_barrier();             // stage st visible; stage st - 1's slot free
+    if (st + 1 < s_end) issue(st + 1, slot ^ 1);
+    if (!active) continue;
+    const lds_char* sk = lr + slot * STAGE + lane * 16;
+    const lds_char* sv = sk + 2 * KCH;
+    const int kc0 = st * kAttnStageKeys;
+    // scores of both 32-key chunks for both query blocks: s[qb][chunk][bb]
+    f32x4 s[2][2][2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        u32x4 kf[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kf[c] = ld16_lds(sk + ch * KCH + ((bb * NC + c) << 10));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NC; ++c) t = mfma16(kf[c], qf[qb][c], t);
+          s[qb][ch][bb] = t;
+        }
+      }
+    // lane holds keys kc0 + 32 ch + 8 gq + e (e = 0..7: bb = e / 4, row e % 4) for query r
+    const bool nomask = g.denoise ? (kc0 >= lo_t && kc0 + kAttnStageKeys <= hi_t)
+                                  : (kc0 + kAttnStageKeys - 1 <= p_first &&
+                                     (kv.window == 0 || p_last - kc0 < kv.window));
+    u32x4 ph[2][2], pl[2][2];
+    float alpha[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float sv16[16];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = s[qb][ch][e >> 2][e & 3] * scale;
+          const int key = kc0 + 32 * ch + 8 * gq + e;
+          const float x = (nomask || (key >= lo_q[qb] && key < hi_q[qb])) ? v : -INFINITY;
+          sv16[8 * ch + e] = x;
+          cmax = fmaxf(cmax, x);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run[qb], cmax);
+      alpha[qb] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[qb] - m_new);
+      float p[16];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = (sv16[e] == -INFINITY) ? 0.f : exp2f(sv16[e] - m_new);
+        ps += p[e];
+      }
+      l_part[qb] = l_part[qb] * alpha[qb] + ps;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = p[8 * ch + 2 * j], x1 = p[8 * ch + 2 * j + 1];
+          hi[j] = cvt_pk_bf16(x0, x1);
+          lo[j] = cvt_pk_bf16(x0 - __uint_as_float(hi[j] << 16), x1 - __uint_as_float(hi[j] & 0xffff0000u));
+        }
+        ph[qb][ch] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        pl[qb][ch] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
     }
-    // lane holds keys kc + 8*gq + e (e = 0..7) for query r
-    float sv[8];
-    float cmax = -INFINITY;
+    // rescale the outputs only when some lane's running max moved
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = kc + 8 * gq + e;
-      const float v = s[e >> 2][e & 3] * scale;
-      sv[e] = (key >= lo_q && key < hi_q) ? v : -INFINITY;
-      cmax = fmaxf(cmax, sv[e]);
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    float p[8];
-    float ps = 0.f;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - m_new);
-      ps += p[e];
-    }
-    l_part = l_part * alpha + ps;
-    m_run = m_new;
-    // P enters the bf16 PV product as a pair: hi = bf16(P), lo = bf16(P - hi), so the
-    // product carries P to ~2^-17 relative (a single bf16 P would add a 2^-9 error to every
-    // probability, which near-uniform attention does not average away)
-    u32x4 pb, pl;
-    {
-      float lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lo[e] = p[e] - bf2f(f2bf(p[e]));
-      pb.x = pack_bf2(p[0], p[1]);
-      pb.y = pack_bf2(p[2], p[3]);
-      pb.z = pack_bf2(p[4], p[5]);
-      pb.w = pack_bf2(p[6], p[7]);
-      pl.x = pack_bf2(lo[0], lo[1]);
-      pl.y = pack_bf2(lo[2], lo[3]);
-      pl.z = pack_bf2(lo[4], lo[5]);
-      pl.w = pack_bf2(lo[6], lo[7]);
+        for (int hb = 0; hb < NB; ++hb) acc[qb][hb] *= alpha[qb];
     }
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
-      acc[hb] *= alpha;
-      acc[hb] = mfma16(Vt[hb], pb, acc[hb]);
-      acc[hb] = mfma16(Vt[hb], pl, acc[hb]);
-    }
-  };
-  const int nsteps = w < nchunk ? (nchunk - w + NW - 1) / NW : 0;
-  pipeline2(nsteps, [&](int t) { load(Ka, Va, kca, t); }, [&](int t) { load(Kb, Vb, kcb, t); },
-            [&] { process(Ka, Va, kca); }, [&] { process(Kb, Vb, kcb); });
-
-  float l_row = l_part + __shfl_xor(l_part, 16, 64);
-  l_row += __shfl_xor(l_row, 32, 64);
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb)
+      for (int ch = 0; ch < 2; ++ch) {
+        const u32x4 vf = ld16_lds(sv + ch * VCH + (hb << 10));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Ol[w][r][16 * hb + 4 * gq + e] = acc[hb][e];
-  if (gq == 0) {
-    ml[w][r][0] = m_run;
-    ml[w][r][1] = l_row;
-  }
-  __syncthreads();
-
-  // merge the NW waves: thread t -> query t / TPQ, hd slice (t % TPQ) * HD / TPQ
-  constexpr int TPQ = 4 * NW;                 // threads per query (64 * NW / 16)
-  constexpr int CPT = HD / TPQ;               // hd columns per thread
-  static_assert(CPT >= 2 && CPT % 2 == 0, "bf16 pairs per thread");
-  const int qq = threadIdx.x / TPQ;
-  const int d0 = (threadIdx.x % TPQ) * CPT;
-  float M = -INFINITY;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml[ww][qq][0]);
-  float sc[NW];
-  float L = 0.f;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    const float mw = ml[ww][qq][0];
-    sc[ww] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-    L += sc[ww] * ml[ww][qq][1];
-  }
-  const float invL = L > 0.f ? 1.f / L : 0.f;
-  const int iq = i0 + qq;
-  if (iq < n) {
-    // o is fragment-major [M_pad][hq * HD] (the O projection's activation operand)
-    const size_t m = (size_t)b * n + iq;
-    const int K = hq * HD;
-#pragma unroll
-    for (int e = 0; e < CPT; e += 2) {
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        v0 += sc[ww] * Ol[ww][qq][d0 + e];
-        v1 += sc[ww] * Ol[ww][qq][d0 + e + 1];
+        for (int qb = 0; qb < 2; ++qb) {
+          acc[qb][hb] = mfma16(vf, ph[qb][ch], acc[qb][hb]);
+          acc[qb][hb] = mfma16(vf, pl[qb][ch], acc[qb][hb]);
+        }
       }
-      *reinterpret_cast<uint32_t*>(o + fm_index(m, head * HD + d0 + e, K)) = pack_bf2(v0 * invL, v1 * invL);
+    }
+  }
+  if (!active) return;
+
+  // each lane's query: the four lanes of a query (gq = 0..3) hold disjoint keys' sums
+  const int npad32 = a.qt32 * 32;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l_row = l_part[qb] + __shfl_xor(l_part[qb], 16, 64);
+    l_row += __shfl_xor(l_row, 32, 64);
+    const int iq = q0 + 16 * qb + r;
+    if (a.nsplit == 1) {
+      if (iq >= n) continue;
+      const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+      const size_t m = (size_t)b * n + iq;
+      const int K = a.hq * HD;
+#pragma unroll
+      for (int hb = 0; hb < NB; ++hb) {
+        const int c = head * HD + 16 * hb + 4 * gq;
+        u32x2 o2;
+        o2.x = cvt_pk_bf16(acc[qb][hb][0] * inv, acc[qb][hb][1] * inv);
+        o2.y = cvt_pk_bf16(acc[qb][hb][2] * inv, acc[qb][hb][3] * inv);
+        *reinterpret_cast<u32x2*>(a.o + fm_index(m, c, K)) = o2;
+      }
+    } else {
+      const size_t row = (((size_t)split * g.batch + b) * a.hq + head) * npad32 + iq;
+      if (gq == 0) a.part_ml[row] = make_float2(m_run[qb], l_row);
+#pragma unroll
+      for (int hb = 0; hb < NB; ++hb)
+        *reinterpret_cast<f32x4*>(a.part_o + row * HD + 16 * hb + 4 * gq) = acc[qb][hb];
     }
   }
 }
 
-void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g,
-                      uint16_t* o, hipStream_t s) {
-  const int pairs = g.batch * kv.hkv, per_pair = (hq / kv.hkv) * ((g.n + 15) / 16);
-  dim3 grid(kXcd * ((pairs + kXcd - 1) / kXcd) * per_pair);
-  // 8 waves split the key range (4 for hd 32, where the merge runs out of columns)
+// Merge of the split-KV partials: one thread per 8 output features of one (sequence,
+// head, query); the splits are combined in split order.
+template <int HD>
+__global__ __launch_bounds__(256) void attention_merge_kernel(const float* __restrict__ part_o,
+                                                              const float2* __restrict__ part_ml, int nsplit,
+                                                              int batch, int hq, int n, int npad32,
+                                                              uint16_t* __restrict__ o) {
+  constexpr int TPR = HD / 8;
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long rows = (long)batch * hq * n;
+  if (t >= rows * TPR) return;
+  const int c8 = (int)(t % TPR) * 8;
+  long rr = t / TPR;
+  const int iq = (int)(rr % n);
+  rr /= n;
+  const int head = (int)(rr % hq), b = (int)(rr / hq);
+  const size_t base = ((size_t)b * hq + head) * npad32 + iq;
+  const size_t stride = (size_t)batch * hq * npad32;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[s * stride + base].x);
+  float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = part_ml[s * stride + base];
+    if (ml.x == -INFINITY) continue;
+    const float f = exp2f(ml.x - M);
+    L += ml.y * f;
+    const float* po = part_o + (s * stride + base) * HD + c8;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(po), v1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += v0[e] * f;
+      acc[4 + e] += v1[e] * f;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const size_t m = (size_t)b * n + iq;
+  u32x4 out;
+  out.x = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+  out.y = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
+  out.z = cvt_pk_bf16(acc[4] * inv, acc[5] * inv);
+  out.w = cvt_pk_bf16(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<u32x4*>(o + fm_index(m, head * HD + c8, hq * HD)) = out;
+}
+
+template <int HD, int NWV>
+static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
+                          float* part_o, float2* part_ml, hipStream_t s) {
+  constexpr int STAGE = 2 * (2 * (HD / 32) * 1024 + (HD / 16) * 1024);
+  static LdsLimit limit;
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&attention_kernel<HD, NWV>), 2 * STAGE);
+  AttnArgs a{};
+  a.q = q; a.o = o; a.part_o = part_o; a.part_ml = part_ml;
+  a.kv = kv; a.g = g; a.hq = hq;
+  a.grp = hq / kv.hkv;
+  a.qt32 = (g.n + 31) / 32;
+  a.wg_per_pair = (a.grp * a.qt32 + NWV - 1) / NWV;
+  const int pairs = g.batch * kv.hkv;
+  const int base_wgs = pairs * a.wg_per_pair;
+  // split the key range when the pairs alone leave CUs idle: aim at ~2 workgroups per
+  // CU, keep at least two 64-key stages per split, and stay within the partial buffer
+  int max_keys = 0;
+  for (int bb = 0; bb < g.batch; ++bb) {
+    const int keys = g.denoise ? (kv.window > 0 ? min(g.len[bb], kv.window) : g.len[bb]) + g.n
+                               : (kv.window > 0 ? min(g.len[bb] + g.n, kv.window + 63) : g.len[bb] + g.n);
+    max_keys = max(max_keys, keys);
+  }
+  const int stages = (max_keys + kAttnStageKeys - 1) / kAttnStageKeys + 1;
+  int nsplit = (512 + base_wgs - 1) / base_wgs;
+  nsplit = min(nsplit, max(1, stages / 2));
+  nsplit = min(nsplit, max(1, kAttnMaxSplitRows / (g.batch * a.qt32 * 32)));
+  if (!part_o) nsplit = 1;
+  a.nsplit = max(1, nsplit);
+  const long units = (long)base_wgs * a.nsplit;
+  const int blocks = (int)(kXcd * ((units + kXcd - 1) / kXcd));
+  launch_kernel(attention_kernel<HD, NWV>, dim3(blocks), dim3(64 * NWV), 2 * STAGE, s, nullptr, a);
+  if (a.nsplit > 1) {
+    const long threads = (long)g.batch * hq * g.n * (HD / 8);
+    launch_kernel(attention_merge_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, nullptr,
+                  part_o, part_ml, a.nsplit, g.batch, hq, g.n, a.qt32 * 32, o);
+  }
+}
+
+void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
+                      float* part_o, float2* part_ml, hipStream_t s) {
   switch (kv.hd) {
-    case 32: launch_kernel(attention_kernel<32, 4>, grid, dim3(256), 0, s, nullptr, q, hq, kv, g, o); break;
-    case 64: launch_kernel(attention_kernel<64, 8>, grid, dim3(512), 0, s, nullptr, q, hq, kv, g, o); break;
-    default: launch_kernel(attention_kernel<128, 8>, grid, dim3(512), 0, s, nullptr, q, hq, kv, g, o); break;
+    case 32: run_attention<32, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
+    case 64: run_attention<64, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
+    default: run_attention<128, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
   }
 }
 

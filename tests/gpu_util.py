@@ -103,3 +103,29 @@ def logit_error_split(lg, ref):
     own = np.abs(O.bf16(ref) - ref)
     return (f"compute share {float((d - own).max()):.3e}, p99.99 {float(np.quantile(d, 0.9999)):.3e}, "
             f"largest |ref| {float(np.abs(ref).max()):.2f}")
+
+
+def oracle_nudged_logits(cfg, w_np, prompt, canvas, t, prefill_ids, denoise_ids, eps=1e-7):
+    """The oracle again with every normed state multiplied by (1 + eps N(0, 1)) -- a
+    perturbation below an fp32 ulp for eps 1e-7 -- and the routing replayed from the given
+    per-layer expert ids (prefill, then denoise), so no routing decision can differ:
+    logits [C][V] of one denoising step after prefilling prompt [1][P].  Their distance
+    from the plain oracle's logits is the model's own spread under sub-ulp rounding
+    differences, the floor under any bf16-compute implementation's tolerance."""
+    from oracle import dg_oracle as O
+    replay = iter([np.asarray(x) for x in prefill_ids] + [np.asarray(x) for x in denoise_ids])
+    orig_norm, orig_topk = O.rms_norm, O.router_topk
+    O.rms_norm = lambda x, g, e: orig_norm(x, g, e) * (1 + eps * np.random.default_rng(0).standard_normal(np.shape(x)))
+
+    def topk_replay(r, k):
+        ids = next(replay)
+        sel = np.take_along_axis(np.asarray(r, np.float64), ids, axis=1)
+        wts = np.exp(sel - sel.max(axis=1, keepdims=True))
+        return ids, wts / wts.sum(axis=1, keepdims=True)
+    O.router_topk = topk_replay
+    try:
+        kv = O.KVCache(cfg, 1)
+        O.prefill_kv(cfg, w_np, kv, np.asarray(prompt))
+        return O.denoise_step(cfg, w_np, kv, np.asarray(canvas), t)[0]
+    finally:
+        O.rms_norm, O.router_topk = orig_norm, orig_topk

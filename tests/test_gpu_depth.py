@@ -26,7 +26,8 @@ import torch
 
 from discrete_diffusion_block_amd import dg, synth
 from oracle import dg_oracle as O
-from gpu_util import argmax_agreement, forced_ids, forced_routing, logit_error_split, require_gpu, to_np_bf16
+from gpu_util import (argmax_agreement, forced_ids, forced_routing, logit_error_split, oracle_nudged_logits,
+                      require_gpu, to_np_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -128,23 +129,8 @@ def test_thirty_layer_teacher_forced_steps():
     # the floor: the oracle against itself, every normed state nudged by a relative 1e-7
     # (below an fp32 ulp), routed exactly as before (the recorded expert ids are replayed)
     print("oracle again, normed states nudged by 1e-7 (routing replayed)", flush=True)
-    pre = [np.asarray(x["ids"]) for x in tr_prefill]
-    replay = iter(pre + routes[0])
-    orig_norm, orig_topk = O.rms_norm, O.router_topk
-    O.rms_norm = lambda x, g, e: orig_norm(x, g, e) * (1 + 1e-7 * np.random.default_rng(0).standard_normal(np.shape(x)))
-
-    def topk_replay(r, k):
-        ids = next(replay)
-        sel = np.take_along_axis(np.asarray(r, np.float64), ids, axis=1)
-        wts = np.exp(sel - sel.max(axis=1, keepdims=True))
-        return ids, wts / wts.sum(axis=1, keepdims=True)
-    O.router_topk = topk_replay
-    try:
-        kv2 = O.KVCache(cfg, 1)
-        O.prefill_kv(cfg, w_np, kv2, prompt.numpy())
-        nudged = O.denoise_step(cfg, w_np, kv2, canvases[0][0], 1.0)[0]
-    finally:
-        O.rms_norm, O.router_topk = orig_norm, orig_topk
+    nudged = oracle_nudged_logits(cfg, w_np, prompt.numpy(), canvases[0][0], 1.0,
+                                  [x["ids"] for x in tr_prefill], routes[0])
     floor = float(np.abs(nudged - refs[0]).max())
     print(f"  oracle's own spread after 30 layers at t=1: max {floor:.3e}, p99.99 "
           f"{float(np.quantile(np.abs(nudged - refs[0]), 0.9999)):.3e}; engine max {results[0][0]:.3e} "
