@@ -425,7 +425,7 @@ def sampler_roofline(eng, cfg, gamma):
                                          max(1, prof["sample_canon"][1]), 4)}
 
 
-def spread_line(eng, cfg, n_distinct, reps):
+def spread_line(eng, cfg, n_distinct, reps, prompt_len):
     """The expert GEMMs at a routing spread like the Technical Report's (~84 unique experts
     per layer on a real 256-token canvas, §6 GPU time breakdown, MoE).  With random-init
     weights a denoising pass cannot show it: the timestep embedding (norm ~37 against ~1 for
@@ -439,7 +439,10 @@ def spread_line(eng, cfg, n_distinct, reps):
     layer feeds no K/V and has no FFN)."""
     import torch
     canvas = spread_canvas(cfg, n_distinct).cuda()
-    L0 = eng.lengths[0]
+    # the pass runs right after the prompt (its window: the 1024 random prompt tokens),
+    # as the append of the first block does
+    L_saved = eng.lengths[0]
+    L0 = prompt_len
     L = cfg.n_layers
 
     def append(s):
@@ -463,7 +466,7 @@ def spread_line(eng, cfg, n_distinct, reps):
         out[kind] = roofline_obj("hbm", "GB/s", avg, amount, launches, kind,
                                  experts_used_per_layer_mean=round(sum(used) / len(used), 1),
                                  tokens_per_used_expert=round(2048 * (L - 1) / sum(used), 1))
-    eng.kv.len[0] = L0
+    eng.kv.len[0] = L_saved
     return {"workload": f"causal append pass of the 30-layer model over a 256-token canvas of {n_distinct} "
                         f"distinct token ids: the random-init router spreads its 2048 assignments to "
                         f"{out['moe_gate_up']['experts_used_per_layer_mean']} of 128 experts per layer (the "
@@ -706,7 +709,7 @@ def main():
         log("sampler on rotating buffers...")
         out["sampler_roofline"] = sampler_roofline(eng, cfg, args.gamma)
         log("spread routing...")
-        out["spread_routing"] = spread_line(eng, cfg, args.spread_distinct, reps)
+        out["spread_routing"] = spread_line(eng, cfg, args.spread_distinct, reps, args.prompt)
         packed = eng.weights
         eng.close()
         del logits
