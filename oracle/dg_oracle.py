@@ -37,6 +37,9 @@ in the design notes of the repository):
     by (H asc, position asc); S_k = running fp64 sum of H in that order;
     commit the first k* = max(1, max{k : S_k <= gamma}) positions, or all
     when commit_all (the last step of a block).
+  * Uniform ("multinomial") variant: the canvas starts as uniformly random tokens;
+    every position is a candidate at every step; accepted positions take their
+    argmax and the rest are re-noised uniformly (Philox4x64-10 tokens).
   * Precision contract ("bf16 compute, fp32 accumulate"): with rnd=True the
     oracle rounds to bfloat16 (RNE, via fp32) exactly the values the engine
     stores as bf16 — normed activations, q/k/v, attention output, SwiGLU
@@ -471,11 +474,12 @@ def temperature(t: float, tau_max: float, tau_min: float) -> float:
 
 def adaptive_stop(H32: np.ndarray, amax: np.ndarray, prev_amax: np.ndarray, masked: List[int],
                   e_stop: float) -> bool:
-    """Technical Report §3.3, adaptive stopping, on the masked rows of one canvas (the only
-    rows the absorbing sampler predicts): true when their mean entropy is below e_stop and
-    every one of them has the same most likely token as at the previous step.  The mean
-    is the float64 running sum of the float32 entropies in position order, divided by
-    their number (a fixed order, so that the decision is reproducible bit for bit)."""
+    """Technical Report §3.3, adaptive stopping, on the candidate rows of one canvas (the
+    masked rows for the absorbing sampler, every row for the uniform variant): true when
+    their mean entropy is below e_stop and every one of them has the same most likely
+    token as at the previous step.  The mean is the float64 running sum of the float32
+    entropies in position order, divided by their number (a fixed order, so that the
+    decision is reproducible bit for bit)."""
     if not masked:
         return False
     acc = 0.0
@@ -567,6 +571,131 @@ def generate_block_annealed(cfg, weights: dict, kv: KVCache, batch: int, max_ste
                            "n_masked": n_masked, "committed": committed})
         for b in range(batch):
             if done_at[b] == 0 and n_masked[b] == 0:
+                done_at[b] = s + 1
+        prev = amax
+        canvas = new
+    if append:
+        prefill_kv(cfg, weights, kv, canvas, rnd)
+    return canvas, done_at
+
+
+# --------------------------------------------------------------------------------------
+# Uniform ("multinomial") variant
+# --------------------------------------------------------------------------------------
+#
+# DiffusionGemma Technical Report §2.1 (the corruption path ends in the uniform prior
+# over the vocabulary), §3.2 ("canvas initialisation": the canvas starts as uniformly
+# random tokens; "multinomial diffusion": tokens accepted at an earlier step of the
+# current canvas can still change) and §3.3 (tokens are accepted in order of increasing
+# entropy under the bound; every other position is re-noised uniformly at random).
+# Readings: every position of the canvas is a candidate at every step; an accepted
+# position takes its most likely token (lowest id on ties), as in the absorbing sampler;
+# the last step accepts every position; a canvas is complete when the adaptive stop fires
+# or after the last step, and is not touched afterwards.
+#
+# Random tokens: Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+# as easy as 1, 2, 3", SC 2011) with counter (position, sequence, draw, 0) and key
+# (seed, 0); draw 0 fills the initial canvas, draw s + 1 re-noises after step s.  The
+# first output word x gives the token floor(x V / 2^64).
+
+_U64 = (1 << 64) - 1
+_PHILOX_MUL = (0xD2E7470EE14C6C93, 0xCA5A826395121157)   # the two round multipliers
+_PHILOX_BUMP = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)  # the Weyl key increments
+
+
+def philox4x64(counter, key, rounds: int = 10):
+    """One Philox4x64 block: four 64-bit output words for a 4-word counter and 2-word key.
+    Each round multiplies words 0 and 2 by the two constants (full 128-bit products),
+    swaps the halves across the pairs and XORs in the other words and the key; the key
+    advances by the Weyl increments between rounds."""
+    x0, x1, x2, x3 = (int(v) & _U64 for v in counter)
+    k0, k1 = (int(v) & _U64 for v in key)
+    for _ in range(rounds):
+        p0 = _PHILOX_MUL[0] * x0
+        p1 = _PHILOX_MUL[1] * x2
+        x0, x1, x2, x3 = (p1 >> 64) ^ x1 ^ k0, p1 & _U64, (p0 >> 64) ^ x3 ^ k1, p0 & _U64
+        k0 = (k0 + _PHILOX_BUMP[0]) & _U64
+        k1 = (k1 + _PHILOX_BUMP[1]) & _U64
+    return x0, x1, x2, x3
+
+
+def uniform_token(seed: int, draw: int, seq: int, pos: int, vocab: int) -> int:
+    """The uniformly random token of (seed, draw, sequence, position) in [0, vocab)."""
+    x = philox4x64((pos, seq, draw, 0), (seed, 0))[0]
+    return (x * int(vocab)) >> 64
+
+
+def uniform_canvas(seed: int, draw: int, batch: int, C: int, vocab: int) -> np.ndarray:
+    """A canvas [B][C] of uniformly random tokens (draw 0: the initial canvas)."""
+    return np.array([[uniform_token(seed, draw, b, i, vocab) for i in range(C)] for b in range(batch)],
+                    dtype=np.int64)
+
+
+def sample_eb_uniform(logits: np.ndarray, canvas: np.ndarray, gamma: float, commit_all: bool,
+                      seed: int, draw: int, tau: float = 1.0, e_stop: Optional[float] = None,
+                      prev_amax: Optional[np.ndarray] = None, frozen: Optional[np.ndarray] = None):
+    """One sampler call of the uniform variant on logits [B][C][V] (bf16 values).
+
+    Every position is a candidate: Ĥ and argmax of every row at temperature tau; the
+    accepted positions are eb_select's over all of them (all when commit_all, or when
+    the adaptive stop fires against prev_amax); each accepted position takes its argmax
+    and every other one uniform_token(seed, draw, b, position).  A frozen sequence
+    (complete before this call) is neither read nor written.  Returns (new_canvas,
+    H32 [B][C] (NaN where frozen), argmax [B][C] (-1 where frozen), n_open [B] = the
+    number of re-noised positions, accepted list per batch, complete [B])."""
+    canvas = np.array(canvas, dtype=np.int64, copy=True)
+    B, C = canvas.shape
+    V = logits.shape[-1]
+    H32 = np.full((B, C), np.nan, dtype=np.float32)
+    amax = np.full((B, C), -1, dtype=np.int64)
+    n_open = np.zeros(B, dtype=np.int64)
+    complete = np.zeros(B, dtype=bool)
+    accepted = []
+    for b in range(B):
+        if frozen is not None and frozen[b]:
+            accepted.append([])
+            continue
+        rows = np.asarray(logits[b], dtype=np.float64)
+        H32[b] = entropy_canonical(rows, tau)
+        amax[b] = np.argmax(rows, axis=-1)
+        cand = list(range(C))
+        stop = e_stop is not None and adaptive_stop(H32[b], amax[b], prev_amax[b], cand, e_stop)
+        sel = eb_select(H32[b], cand, gamma, commit_all or stop)
+        keep = set(sel)
+        for i in range(C):
+            canvas[b, i] = amax[b, i] if i in keep else uniform_token(seed, draw, b, i, V)
+        accepted.append(sel)
+        n_open[b] = C - len(sel)
+        complete[b] = bool(commit_all or stop)
+    return canvas, H32, amax, n_open, accepted, complete
+
+
+def generate_block_uniform(cfg, weights: dict, kv: KVCache, batch: int, max_steps: int, gamma: float,
+                           seed: int, tau_max: float = 1.0, tau_min: float = 1.0,
+                           e_stop: Optional[float] = None, append: bool = True, rnd: bool = True,
+                           record: Optional[list] = None):
+    """One canvas per sequence by the uniform variant: the canvas starts as
+    uniform_canvas(seed, 0, ...); step s (t_s = 1 - s/max_steps, temperature
+    temperature(t_s, tau_max, tau_min)) runs the decoder over the whole canvas and
+    sample_eb_uniform with draw s + 1; the last step accepts every position.  Returns
+    (canvas [B][C], steps [B]): the step count after which each canvas was complete."""
+    C, V = cfg.canvas, cfg.vocab
+    canvas = uniform_canvas(seed, 0, batch, C, V)
+    prev = np.full((batch, C), -1, dtype=np.int64)
+    done_at = np.zeros(batch, dtype=np.int64)
+    for s in range(max_steps):
+        t = 1.0 - s / max_steps
+        tau = temperature(t, tau_max, tau_min)
+        frozen = done_at > 0
+        logits = denoise_step(cfg, weights, kv, canvas, t, rnd)
+        stored = bf16(logits) if rnd else logits
+        new, H32, amax, n_open, accepted, complete = sample_eb_uniform(
+            stored, canvas, gamma, s == max_steps - 1, seed, s + 1, tau, e_stop, prev, frozen)
+        if record is not None:
+            record.append({"t": t, "tau": tau, "canvas_in": canvas.copy(), "H": H32, "argmax": amax,
+                           "n_open": n_open, "accepted": accepted, "complete": complete})
+        for b in range(batch):
+            if not frozen[b] and complete[b]:
                 done_at[b] = s + 1
         prev = amax
         canvas = new
