@@ -459,6 +459,11 @@ struct SampleOpts {
   int32_t* prev_amax = nullptr;
   int step = 0;
   int32_t* done_step = nullptr;
+  // uniform variant (Technical Report §3.2, multinomial diffusion): every position a
+  // candidate, the others re-noised with the tokens of (seed, draw)
+  int uniform = 0;
+  uint64_t seed = 0;
+  int draw = 0;
 };
 
 dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
@@ -466,22 +471,23 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
                       int32_t* d_n_masked, const Ws& ws, hipStream_t s, const dg_ctx* ctx = nullptr,
                       const SampleOpts& o = SampleOpts{}) {
   DG_TIMED(ctx, DG_K_SAMPLE_PASS1,
-           launch_sample_partials(d_logits, d_canvas, batch * canvas, vocab, 1.0f / o.temperature, ws.part,
-                                  ws.part_arg, s));
+           launch_sample_partials(d_logits, d_canvas, batch, canvas, vocab, 1.0f / o.temperature, o.uniform,
+                                  o.uniform ? o.done_step : nullptr, ws.part, ws.part_arg, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
            launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
                             canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax,
                             o.e_stop, o.step, o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin,
-                            ws.skstar, s));
+                            ws.skstar, o.uniform, o.seed, o.draw, s));
   // sequences whose decision the fast entropies could not certify: canonical entropy
   // (every workgroup of a decided sequence returns at once)
   DG_TIMED(ctx, DG_K_SAMPLE_CANON,
-           launch_canon_partials(d_logits, d_canvas, batch, canvas, vocab, o.temperature, ws.part, ws.sflag,
-                                 ws.shf, ws.swin, ws.cpart, s));
+           launch_canon_partials(d_logits, d_canvas, batch, canvas, vocab, o.temperature, o.uniform, ws.part,
+                                 ws.sflag, ws.shf, ws.swin, ws.cpart, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT_CANON,
            launch_eb_select_canon(ws.cpart, sample_chunks(vocab), d_canvas, batch, canvas, vocab, gamma,
                                   commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax, o.e_stop, o.step,
-                                  o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin, ws.skstar, s));
+                                  o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin, ws.skstar,
+                                  o.uniform, o.seed, o.draw, s));
   return check_launch("sampler");
 }
 
@@ -511,6 +517,81 @@ dg_status scratch_ptr(void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
+// Validation and workspace carving shared by the sampler entry points.
+dg_status sample_checked(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                         float gamma, int commit_all, float* d_entropy, int32_t* d_argmax, int32_t* d_n,
+                         void* d_ws, size_t ws_bytes, void* stream, const SampleOpts& o) {
+  size_t need = 0;
+  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
+  if (st != DG_OK) return st;
+  if (!d_logits || !d_canvas || !d_n || !d_ws) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  if (!(o.temperature > 0.0f) || o.temperature > 3.0e38f)
+    return fail(DG_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (o.e_stop != o.e_stop) return fail(DG_ERR_INVALID_ARG, "e_stop is NaN");
+  if (o.step < 0) return fail(DG_ERR_INVALID_ARG, "step must be >= 0");
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
+  Carver cv{base};
+  Ws ws;
+  carve_sampler(cv, batch, canvas, vocab, &ws);
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n, ws,
+                     (hipStream_t)stream, nullptr, o);
+}
+
+// The annealed, adaptively stopped block generation of the Technical Report (§3.3) on the
+// absorbing canvas (uniform 0: all [MASK] at the start, masked rows only in the head) or
+// the uniform variant (§3.2: uniformly random tokens at the start, draw s + 1 re-noises
+// after step s, every row in the head).
+dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
+                            float tau_max, float tau_min, float e_stop, int uniform, uint64_t seed, int append_kv,
+                            uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step, void* d_ws, size_t ws_bytes,
+                            void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_canvas || !d_logits || !d_n || !d_done_step) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (max_steps < 1) return fail(DG_ERR_INVALID_ARG, "max_steps must be >= 1");
+  if (gamma != gamma || e_stop != e_stop) return fail(DG_ERR_INVALID_ARG, "gamma or e_stop is NaN");
+  if (!(tau_max > 0.0f) || !(tau_min > 0.0f) || tau_max > 3.0e38f || tau_min > 3.0e38f)
+    return fail(DG_ERR_INVALID_ARG, "temperatures must be finite and > 0");
+  const dg_config& c = ctx->cfg;
+  for (int b = 0; b < batch; ++b)
+    if (kv->len[b] + c.canvas > c.max_ctx)
+      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + canvas %d exceeds max_ctx %d", b,
+                  (long long)kv->len[b], c.canvas, c.max_ctx);
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (uniform)
+    DG_TIMED(ctx, DG_K_FILL, launch_uniform_canvas(d_canvas, batch, c.canvas, c.vocab, seed, 0, s));
+  else
+    DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(ws.prev_amax, -1, (size_t)batch * c.canvas, s));
+  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_done_step, 0, (size_t)batch, s));
+  for (int step = 0; step < max_steps; ++step) {
+    const float t = 1.0f - (float)step / (float)max_steps;
+    SampleOpts o;
+    o.temperature = tau_min + (tau_max - tau_min) * t;
+    if (!(o.temperature > 0.0f)) return fail(DG_ERR_INVALID_ARG, "annealed temperature must stay > 0");
+    o.e_stop = e_stop;
+    o.prev_amax = ws.prev_amax;
+    o.step = step;
+    o.done_step = d_done_step;
+    o.uniform = uniform;
+    o.seed = seed;
+    o.draw = step + 1;
+    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/!uniform);
+    if (st != DG_OK) return st;
+    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == max_steps - 1, nullptr,
+                     nullptr, d_n, ws, s, ctx, o);
+    if (st != DG_OK) return st;
+  }
+  if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
   return DG_OK;
 }
 
@@ -636,27 +717,42 @@ dg_status dg_sample_eb_ex(const uint16_t* d_logits, int32_t* d_canvas, int batch
                           float gamma, int commit_all, float temperature, float e_stop,
                           int32_t* d_prev_argmax, int step, int32_t* d_done_step, float* d_entropy,
                           int32_t* d_argmax, int32_t* d_n_masked, void* d_ws, size_t ws_bytes, void* stream) {
-  size_t need = 0;
-  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
-  if (st != DG_OK) return st;
-  if (!d_logits || !d_canvas || !d_n_masked || !d_ws) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
-  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
-  if (!(temperature > 0.0f) || temperature > 3.0e38f) return fail(DG_ERR_INVALID_ARG, "temperature must be finite and > 0");
-  if (e_stop != e_stop) return fail(DG_ERR_INVALID_ARG, "e_stop is NaN");
-  if (step < 0) return fail(DG_ERR_INVALID_ARG, "step must be >= 0");
-  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
-  Carver cv{base};
-  Ws ws;
-  carve_sampler(cv, batch, canvas, vocab, &ws);
   SampleOpts o;
   o.temperature = temperature;
   o.e_stop = e_stop;
   o.prev_amax = d_prev_argmax;
   o.step = step;
   o.done_step = d_done_step;
-  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
-                     d_n_masked, ws, (hipStream_t)stream, nullptr, o);
+  return sample_checked(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
+                        d_n_masked, d_ws, ws_bytes, stream, o);
+}
+
+dg_status dg_sample_eb_uniform(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                               float gamma, int commit_all, float temperature, float e_stop,
+                               int32_t* d_prev_argmax, int step, int32_t* d_done_step, uint64_t seed, int draw,
+                               float* d_entropy, int32_t* d_argmax, int32_t* d_n_open, void* d_ws,
+                               size_t ws_bytes, void* stream) {
+  if (draw < 0) return fail(DG_ERR_INVALID_ARG, "draw must be >= 0");
+  SampleOpts o;
+  o.temperature = temperature;
+  o.e_stop = e_stop;
+  o.prev_amax = d_prev_argmax;
+  o.step = step;
+  o.done_step = d_done_step;
+  o.uniform = 1;
+  o.seed = seed;
+  o.draw = draw;
+  return sample_checked(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
+                        d_n_open, d_ws, ws_bytes, stream, o);
+}
+
+dg_status dg_uniform_canvas(int32_t* d_canvas, int batch, int canvas, int vocab, uint64_t seed, int draw,
+                            void* stream) {
+  if (!d_canvas) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (batch < 1 || canvas < 1 || vocab < 1 || draw < 0 || (int64_t)batch * canvas > (int64_t)1 << 30)
+    return fail(DG_ERR_INVALID_ARG, "bad canvas sizes or draw");
+  launch_uniform_canvas(d_canvas, batch, canvas, vocab, seed, draw, (hipStream_t)stream);
+  return check_launch("uniform canvas");
 }
 
 dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
@@ -733,43 +829,16 @@ dg_status dg_generate_block_ex(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int ba
                                float gamma, float tau_max, float tau_min, float e_stop, int append_kv,
                                uint16_t* d_logits, int32_t* d_n_masked, int32_t* d_done_step, void* d_ws,
                                size_t ws_bytes, void* stream) {
-  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
-  dg_status st = check_kv(ctx, kv, batch);
-  if (st != DG_OK) return st;
-  if (!d_canvas || !d_logits || !d_n_masked || !d_done_step) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
-  if (max_steps < 1) return fail(DG_ERR_INVALID_ARG, "max_steps must be >= 1");
-  if (gamma != gamma || e_stop != e_stop) return fail(DG_ERR_INVALID_ARG, "gamma or e_stop is NaN");
-  if (!(tau_max > 0.0f) || !(tau_min > 0.0f) || tau_max > 3.0e38f || tau_min > 3.0e38f)
-    return fail(DG_ERR_INVALID_ARG, "temperatures must be finite and > 0");
-  const dg_config& c = ctx->cfg;
-  for (int b = 0; b < batch; ++b)
-    if (kv->len[b] + c.canvas > c.max_ctx)
-      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + canvas %d exceeds max_ctx %d", b,
-                  (long long)kv->len[b], c.canvas, c.max_ctx);
-  Ws ws;
-  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
-  if (st != DG_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
-  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(ws.prev_amax, -1, (size_t)batch * c.canvas, s));
-  DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_done_step, 0, (size_t)batch, s));
-  for (int step = 0; step < max_steps; ++step) {
-    const float t = 1.0f - (float)step / (float)max_steps;
-    SampleOpts o;
-    o.temperature = tau_min + (tau_max - tau_min) * t;
-    if (!(o.temperature > 0.0f)) return fail(DG_ERR_INVALID_ARG, "annealed temperature must stay > 0");
-    o.e_stop = e_stop;
-    o.prev_amax = ws.prev_amax;
-    o.step = step;
-    o.done_step = d_done_step;
-    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/true);
-    if (st != DG_OK) return st;
-    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == max_steps - 1, nullptr,
-                     nullptr, d_n_masked, ws, s, ctx, o);
-    if (st != DG_OK) return st;
-  }
-  if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
-  return DG_OK;
+  return generate_annealed(ctx, kv, d_canvas, batch, max_steps, gamma, tau_max, tau_min, e_stop, 0, 0, append_kv,
+                           d_logits, d_n_masked, d_done_step, d_ws, ws_bytes, stream);
+}
+
+dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
+                                    float gamma, float tau_max, float tau_min, float e_stop, uint64_t seed,
+                                    int append_kv, uint16_t* d_logits, int32_t* d_n_open, int32_t* d_done_step,
+                                    void* d_ws, size_t ws_bytes, void* stream) {
+  return generate_annealed(ctx, kv, d_canvas, batch, max_steps, gamma, tau_max, tau_min, e_stop, 1, seed,
+                           append_kv, d_logits, d_n_open, d_done_step, d_ws, ws_bytes, stream);
 }
 
 dg_status dg_packed_elems(int rows, int cols, size_t* elems) {
@@ -895,7 +964,7 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
     return fail(DG_ERR_INVALID_ARG, "bad selection arguments");
   launch_eb_select(nullptr, nullptr, 0, d_entropy, d_argmax, d_canvas, batch, canvas, vocab, gamma,
                    commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, nullptr, nullptr,
-                   nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream);
+                   nullptr, nullptr, nullptr, nullptr, 0, 0, 0, (hipStream_t)stream);
   return check_launch("eb select");
 }
 

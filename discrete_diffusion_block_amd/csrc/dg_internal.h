@@ -144,9 +144,14 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int
 
 // ---- sampler ----
 constexpr int kSampleChunk = 16384;  // logits per workgroup in the first sampler pass (multiple of 2048)
-// inv_tau = 1 / sampling temperature (1 = the plain distribution)
-void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
-                            float inv_tau, float4* part, int* part_arg, hipStream_t s);
+// inv_tau = 1 / sampling temperature (1 = the plain distribution).  all_rows: every
+// row is a candidate (uniform variant), except those of sequences with frozen[b] != 0
+// (frozen optional); otherwise the [MASK] rows.
+void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
+                            float inv_tau, int all_rows, const int32_t* frozen, float4* part, int* part_arg,
+                            hipStream_t s);
+// A canvas [batch][C] of the uniformly random tokens of (seed, draw).
+void launch_uniform_canvas(int32_t* canvas, int batch, int C, int vocab, uint64_t seed, int draw, hipStream_t s);
 // Pass 2: merge the chunk partials (part given) or take the given entropies and
 // argmaxes (H_in / amax_in), rank, and commit.  prev_amax (optional, [batch][C]
 // in/out): the previous step's argmax, for the adaptive stop at e_stop; done_step
@@ -154,26 +159,29 @@ void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int r
 // row.  With part given and flag non-NULL, a sequence whose decision is not
 // certified under the fast entropies' error bound is left undecided: flag[b] = 1,
 // moved[b] = its count of moved argmaxes, amax_ws = its argmaxes (for the canonical
-// passes below); decided sequences get flag[b] = 0.
+// passes below); decided sequences get flag[b] = 0.  uniform: every row of a sequence
+// whose done_step is 0 is a candidate, and the decided sequences' rows outside the
+// accepted set take the uniformly random tokens of (seed, draw); done_step is set when
+// the stop fires or commit_all.
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                       int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
-                      int32_t* kstar_ws, hipStream_t s);
+                      int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s);
 // Pass 3: exact integer sums of the canonical entropy for the masked rows of the
 // flagged sequences -- all of them (flag 1) or those whose fast entropy Hf lies in the
 // sequence's window win (flag 2) (tau: the temperature; part: pass 1's partials, for
 // the row max).
 void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
-                           float tau, const float4* part, const int32_t* flag, const float* Hf, const float2* win,
-                           ulonglong2* cpart, hipStream_t s);
+                           float tau, int all_rows, const float4* part, const int32_t* flag, const float* Hf,
+                           const float2* win, ulonglong2* cpart, hipStream_t s);
 // Pass 4: the decision of the flagged sequences on the canonical entropy.
 void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
                             float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                             int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
-                            int32_t* kstar_ws, hipStream_t s);
+                            int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

@@ -19,6 +19,11 @@
 // that follows it): pass 3 computes its integer sums for the deferred sequences'
 // masked rows only, and pass 4 takes their decision on Ĥ.  Either way the committed
 // set is the one the rule gives on Ĥ.
+//
+// The uniform ("multinomial") variant (Technical Report §3.2, multinomial diffusion;
+// §3.3): every position of a canvas is a candidate (accepted tokens stay revisable),
+// and every position outside the accepted set is re-noised to a uniformly random token.
+// A sequence whose canvas was complete before the call (done step set) is left alone.
 #include <math.h>
 
 #include "dg_common.h"
@@ -63,12 +68,14 @@ __device__ __forceinline__ void merge_part(float& m, int& a, float& s, float& t,
 __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __restrict__ logits,
                                                               const int32_t* __restrict__ canvas,
                                                               int vocab, int nchunks, float inv_tau,
+                                                              int C, int all_rows,
+                                                              const int32_t* __restrict__ frozen,
                                                               float4* __restrict__ part,
                                                               int* __restrict__ part_arg) {
   __shared__ float wmax[4];
   __shared__ float4 wsum[4];
   const int row = blockIdx.y, ch = blockIdx.x;
-  if (canvas[row] != vocab) return;
+  if (all_rows ? (frozen && frozen[row / C] != 0) : canvas[row] != vocab) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c0 = ch * kSampleChunk;
   const int c1 = min(vocab, c0 + kSampleChunk);
@@ -154,11 +161,54 @@ __global__ __launch_bounds__(256) void sample_partials_kernel(const uint16_t* __
   }
 }
 
-void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int rows, int vocab,
-                            float inv_tau, float4* part, int* part_arg, hipStream_t s) {
+void launch_sample_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
+                            float inv_tau, int all_rows, const int32_t* frozen, float4* part, int* part_arg,
+                            hipStream_t s) {
   const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
-  launch_kernel(sample_partials_kernel, dim3(nchunks, rows), dim3(256), 0, s, nullptr, logits, canvas,
-                vocab, nchunks, inv_tau, part, part_arg);
+  launch_kernel(sample_partials_kernel, dim3(nchunks, batch * C), dim3(256), 0, s, nullptr, logits, canvas,
+                vocab, nchunks, inv_tau, C, all_rows, frozen, part, part_arg);
+}
+
+// ---------------------------------------------------------------- uniform tokens
+//
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC 2011): ten rounds, each taking the full 128-bit products of words 0 and 2
+// with the two round multipliers, crossing the halves over the pairs and XOR-ing in the
+// other words and the key, which advances by the two Weyl increments between rounds.
+// The token of (seed, draw, sequence, position) is floor(x V / 2^64) for x the first
+// output word of the block at counter (position, sequence, draw, 0) under key (seed, 0).
+__device__ __forceinline__ uint64_t philox_first_word(uint64_t x0, uint64_t x1, uint64_t x2, uint64_t k0) {
+  constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull, kMul1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kBump0 = 0x9E3779B97F4A7C15ull, kBump1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x3 = 0, k1 = 0;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint64_t hi0 = __umul64hi(kMul0, x0), lo0 = kMul0 * x0;
+    const uint64_t hi1 = __umul64hi(kMul1, x2), lo1 = kMul1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += kBump0;
+    k1 += kBump1;
+  }
+  return x0;
+}
+
+__device__ __forceinline__ int uniform_token(uint64_t seed, int draw, int seq, int pos, int vocab) {
+  return (int)__umul64hi(philox_first_word((uint64_t)pos, (uint64_t)seq, (uint64_t)draw, seed), (uint64_t)vocab);
+}
+
+__global__ __launch_bounds__(256) void uniform_canvas_kernel(int32_t* __restrict__ canvas, int batch, int C,
+                                                             int vocab, uint64_t seed, int draw) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= batch * C) return;
+  canvas[i] = uniform_token(seed, draw, i / C, i % C, vocab);
+}
+
+void launch_uniform_canvas(int32_t* canvas, int batch, int C, int vocab, uint64_t seed, int draw, hipStream_t s) {
+  launch_kernel(uniform_canvas_kernel, dim3((batch * C + 255) / 256), dim3(256), 0, s, nullptr, canvas, batch, C,
+                vocab, seed, draw);
 }
 
 // Order key of a masked row: (H, row) as one unsigned 64-bit integer that compares
@@ -263,7 +313,7 @@ __device__ __forceinline__ float canon_entropy(uint64_t S, uint64_t T) {
 // maximum pass 1 recorded.
 __global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __restrict__ logits,
                                                              const int32_t* __restrict__ canvas, int C,
-                                                             int vocab, int nchunks, float tau,
+                                                             int vocab, int nchunks, float tau, int all_rows,
                                                              const float4* __restrict__ part,
                                                              const int32_t* __restrict__ flag,
                                                              const float* __restrict__ Hf,
@@ -272,7 +322,7 @@ __global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __r
   __shared__ uint64_t red[2][4];
   const int row = blockIdx.y, ch = blockIdx.x, b = row / C;
   const int f = flag[b];
-  if (f == 0 || canvas[row] != vocab) return;   // uniform per workgroup
+  if (f == 0 || (!all_rows && canvas[row] != vocab)) return;   // uniform per workgroup
   if (f == 2) {                                 // only the rows of the boundary window
     const float h = Hf[row];
     const float2 w = win[b];
@@ -317,11 +367,11 @@ __global__ __launch_bounds__(256) void canon_partials_kernel(const uint16_t* __r
 }
 
 void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int batch, int C, int vocab,
-                           float tau, const float4* part, const int32_t* flag, const float* Hf, const float2* win,
-                           ulonglong2* cpart, hipStream_t s) {
+                           float tau, int all_rows, const float4* part, const int32_t* flag, const float* Hf,
+                           const float2* win, ulonglong2* cpart, hipStream_t s) {
   const int nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
   launch_kernel(canon_partials_kernel, dim3(nchunks, batch * C), dim3(256), 0, s, nullptr, logits, canvas, C,
-                vocab, nchunks, tau, part, flag, Hf, win, cpart);
+                vocab, nchunks, tau, all_rows, part, flag, Hf, win, cpart);
 }
 
 // ---------------------------------------------------------------- selection
@@ -363,6 +413,9 @@ struct SelArgs {
   float* Hf_ws;              // [batch][C]: every masked row's fast entropy
   float2* win;               // [batch]: the window [lo, hi] of fast entropies whose Ĥ decides (flag 2)
   int32_t* kstar_ws;         // [batch]: the certain k* (flag 2)
+  int uniform;               // uniform variant: every row a candidate, the rest re-noised
+  uint64_t seed;             //   with the tokens of (seed, draw)
+  int draw;
 };
 
 template <int TPR, int MODE>   // threads per canvas row (chunk merge and rank count)
@@ -372,13 +425,17 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
   __shared__ float Hpos[1024];
   __shared__ int rank_s[1024];
   __shared__ int nm_s, kstar_s;
+  __shared__ int decided_s;
   const int b = blockIdx.x;
   if (MODE == SEL_CANON && A.flag[b] == 0) return;   // decided by the fast pass
   const int C = A.C;
   // the row's TPR threads are adjacent lanes
   const int r = threadIdx.x / TPR, sub = threadIdx.x % TPR;
   const size_t ridx = (size_t)b * C + r;
-  const bool masked = r < C && A.canvas[ridx] == A.vocab;
+  // candidate rows ("masked" below): the [MASK] rows, or in the uniform variant every row
+  // of a sequence not yet complete (its done step is read before any thread writes it)
+  const bool frozen = A.uniform && A.done_step && A.done_step[b] != 0;
+  const bool masked = r < C && !frozen && (A.uniform || A.canvas[ridx] == A.vocab);
   // phase 1: entropy and argmax of each masked row
   float H = INFINITY;
   int a = 0;
@@ -498,7 +555,7 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
       // mean entropy of the masked rows: float64 running sum in position order
       double hs = 0.0;
       for (int i = 0; i < C; ++i)
-        if (A.canvas[(size_t)b * C + i] == A.vocab) hs += (double)Hpos[i];
+        if (A.uniform || A.canvas[(size_t)b * C + i] == A.vocab) hs += (double)Hpos[i];
       const double mean = hs / n;
       stop = mean < (double)A.e_stop;
       if (MODE == SEL_FAST && fabs(mean - (double)A.e_stop) <= kCertEps + kSumSlack) cert = order_only = false;
@@ -565,9 +622,13 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
       }
     }
     kstar_s = ks;
-    if (cert || MODE != SEL_FAST || !A.flag) {
+    const bool decided = cert || MODE != SEL_FAST || !A.flag;
+    decided_s = decided;
+    if (decided) {
       A.n_masked[b] = n - ks;
-      if (A.done_step && n - ks == 0 && A.done_step[b] == 0) A.done_step[b] = A.step + 1;
+      // complete: no [MASK] left; in the uniform variant, the stop fired or the last step
+      const bool complete = A.uniform ? (n > 0 && (A.commit_all || stop)) : n - ks == 0;
+      if (A.done_step && complete && A.done_step[b] == 0) A.done_step[b] = A.step + 1;
     }
   }
   __syncthreads();
@@ -579,7 +640,10 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
       if (A.amax_ws && masked) A.amax_ws[ridx] = a;
       if (A.Hf_ws && masked) A.Hf_ws[ridx] = H;
     }
-    if (masked && rank_s[r] < kstar_s) A.canvas[ridx] = a;
+    if (masked && rank_s[r] < kstar_s)
+      A.canvas[ridx] = a;
+    else if (A.uniform && masked && decided_s)
+      A.canvas[ridx] = uniform_token(A.seed, A.draw, b, r, A.vocab);
   }
 }
 
@@ -597,8 +661,9 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
                       float gamma, int commit_all, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                       int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
-                      int32_t* kstar_ws, hipStream_t s) {
+                      int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s) {
   SelArgs a{};
+  a.uniform = uniform; a.seed = seed; a.draw = draw;
   a.part = part; a.part_arg = part_arg; a.nchunks = nchunks;
   a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
   a.H_in = H_in; a.amax_in = amax_in;
@@ -614,8 +679,9 @@ void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canva
                             float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                             int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
-                            int32_t* kstar_ws, hipStream_t s) {
+                            int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s) {
   SelArgs a{};
+  a.uniform = uniform; a.seed = seed; a.draw = draw;
   a.cpart = cpart; a.nchunks = nchunks;
   a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
   a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;

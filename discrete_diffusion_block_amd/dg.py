@@ -67,7 +67,7 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with discrete_diffusion_block_amd.build")
         L = C.CDLL(LIB_PATH)
-        vp, i32, f32, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+        vp, i32, f32, sz, u64 = C.c_void_p, C.c_int, C.c_float, C.c_size_t, C.c_uint64
         sig = {
             "dg_create": [C.POINTER(Config), C.POINTER(Weights), C.POINTER(vp)],
             "dg_destroy": [vp],
@@ -83,6 +83,11 @@ def lib():
                                 vp],
             "dg_generate_block_ex": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, i32, vp, vp, vp,
                                      vp, sz, vp],
+            "dg_uniform_canvas": [vp, i32, i32, i32, u64, i32, vp],
+            "dg_sample_eb_uniform": [vp, vp, i32, i32, i32, f32, i32, f32, f32, vp, i32, vp, u64, i32, vp, vp,
+                                     vp, vp, sz, vp],
+            "dg_generate_block_uniform": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, u64, i32, vp, vp,
+                                          vp, vp, sz, vp],
             "dg_packed_elems": [i32, i32, C.POINTER(sz)],
             "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
             "dg_profile_begin": [vp, i32, C.c_uint32],
@@ -219,6 +224,33 @@ def dg_generate_block_ex(ctx, kv: KV, canvas: torch.Tensor, max_steps: int, gamm
                                       float(tau_max), float(tau_min), float(e_stop), int(bool(append_kv)),
                                       _p(logits), _p(n_masked), _p(done_step), _p(ws), ws.numel(),
                                       _stream(stream)))
+
+
+def dg_uniform_canvas(canvas: torch.Tensor, vocab: int, seed: int, draw: int, stream=None):
+    b, c = canvas.shape
+    _check(lib().dg_uniform_canvas(_p(canvas), b, c, int(vocab), int(seed) & (2 ** 64 - 1), int(draw),
+                                   _stream(stream)))
+
+
+def dg_sample_eb_uniform(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all: bool,
+                         temperature: float, e_stop: float, prev_argmax: Optional[torch.Tensor], step: int,
+                         done_step: Optional[torch.Tensor], seed: int, draw: int, n_open: torch.Tensor,
+                         ws: torch.Tensor, entropy: Optional[torch.Tensor] = None,
+                         argmax: Optional[torch.Tensor] = None, stream=None):
+    b, c, v = logits.shape
+    _check(lib().dg_sample_eb_uniform(_p(logits), _p(canvas), b, c, v, float(gamma), int(bool(commit_all)),
+                                      float(temperature), float(e_stop), _p(prev_argmax), int(step),
+                                      _p(done_step), int(seed) & (2 ** 64 - 1), int(draw), _p(entropy),
+                                      _p(argmax), _p(n_open), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_generate_block_uniform(ctx, kv: KV, canvas: torch.Tensor, max_steps: int, gamma: float, tau_max: float,
+                              tau_min: float, e_stop: float, seed: int, append_kv: bool, logits: torch.Tensor,
+                              n_open: torch.Tensor, done_step: torch.Tensor, ws: torch.Tensor, stream=None):
+    _check(lib().dg_generate_block_uniform(ctx, C.byref(kv), _p(canvas), canvas.shape[0], max_steps,
+                                           float(gamma), float(tau_max), float(tau_min), float(e_stop),
+                                           int(seed) & (2 ** 64 - 1), int(bool(append_kv)), _p(logits),
+                                           _p(n_open), _p(done_step), _p(ws), ws.numel(), _stream(stream)))
 
 
 def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_kv: bool,
@@ -454,3 +486,13 @@ class Engine:
                           n_masked, done_step, stream=None):
         dg_generate_block_ex(self.ctx, self.kv, canvas, max_steps, gamma, tau_max, tau_min, e_stop,
                              append_kv, logits, n_masked, done_step, self.ws, stream)
+
+    def sample_eb_uniform(self, logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step,
+                          done_step, seed, draw, n_open, entropy=None, argmax=None, stream=None):
+        dg_sample_eb_uniform(logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step, done_step,
+                             seed, draw, n_open, self.ws, entropy, argmax, stream)
+
+    def generate_block_uniform(self, canvas, max_steps, gamma, tau_max, tau_min, e_stop, seed, append_kv,
+                               logits, n_open, done_step, stream=None):
+        dg_generate_block_uniform(self.ctx, self.kv, canvas, max_steps, gamma, tau_max, tau_min, e_stop, seed,
+                                  append_kv, logits, n_open, done_step, self.ws, stream)

@@ -247,6 +247,53 @@ dg_status dg_generate_block_ex(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int ba
                                int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
                                int32_t* d_done_step, void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---- uniform ("multinomial") variant (Technical Report §2.1; §3.2, canvas
+ * initialisation and multinomial diffusion; §3.3) ----
+ * The canvas starts as uniformly random tokens; at every step every position is a
+ * candidate, so tokens accepted at an earlier step of the same canvas can change;
+ * the accepted positions take their argmax and all others are re-noised uniformly.
+ * Random tokens: Philox4x64-10 (Salmon, Moraes, Dror and Shaw, SC 2011), counter
+ * (position, sequence, draw, 0), key (seed, 0); token = floor(x * vocab / 2^64) for x
+ * the block's first output word.  Draw 0 is the initial canvas; the generator below
+ * re-noises after step s with draw s + 1. */
+
+/* Fill d_canvas (int32 [batch][canvas], device) with the tokens of (seed, draw).
+ * Errors: DG_ERR_INVALID_ARG for a NULL pointer, sizes < 1, more than 2^30 positions
+ * or draw < 0. */
+dg_status dg_uniform_canvas(int32_t* d_canvas, int batch, int canvas, int vocab, uint64_t seed, int draw,
+                            void* stream);
+
+/* dg_sample_eb_ex for the uniform variant.  Every row of a sequence is a candidate
+ * (d_canvas may hold any token ids; [MASK] plays no part): the accepted rows are the
+ * first k* of all rows in (Ĥ, position) order, by the same rule, and take their
+ * argmax; every other row takes the token of (seed, draw, its sequence, its
+ * position).  d_done_step (int32 [batch], may be NULL): a sequence whose entry is not
+ * 0 is complete and is neither read nor written (its entropy/argmax outputs hold NaN
+ * and -1 and its d_n_open 0); an entry that is 0 is set to step + 1 when the
+ * adaptive stop fires or commit_all (the sequence is then complete).  d_n_open (int32
+ * [batch], out): the number of re-noised rows.  d_prev_argmax, temperature, e_stop,
+ * d_entropy, d_argmax and the workspace as for dg_sample_eb_ex (the stop's mean runs
+ * over every row).  Errors as for dg_sample_eb_ex, and DG_ERR_INVALID_ARG for
+ * draw < 0. */
+dg_status dg_sample_eb_uniform(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas,
+                               int vocab, float gamma, int commit_all, float temperature, float e_stop,
+                               int32_t* d_prev_argmax, int step, int32_t* d_done_step, uint64_t seed,
+                               int draw, float* d_entropy, int32_t* d_argmax, int32_t* d_n_open,
+                               void* d_ws, size_t ws_bytes, void* stream);
+
+/* dg_generate_block_ex for the uniform variant: d_canvas starts as the tokens of
+ * (seed, draw 0); step s (t_s = 1 - s/max_steps, temperature annealed as in
+ * dg_generate_block_ex) runs the denoising pass with the head over every row and
+ * dg_sample_eb_uniform with draw s + 1 (commit_all on the last step); a canvas is
+ * complete when the stop fires or after the last step and is not changed afterwards.
+ * Then the append pass if append_kv.  d_n_open: int32 [batch] (0 at the end);
+ * d_done_step: int32 [batch], the number of steps after which each canvas was
+ * complete.  Errors as for dg_generate_block_ex. */
+dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
+                                    float gamma, float tau_max, float tau_min, float e_stop, uint64_t seed,
+                                    int append_kv, uint16_t* d_logits, int32_t* d_n_open,
+                                    int32_t* d_done_step, void* d_ws, size_t ws_bytes, void* stream);
+
 /* ---- measurement helpers (diagnostics; not thread-safe) ---- */
 
 /* Kernel kinds the engine launches, for per-kind event timing. */
