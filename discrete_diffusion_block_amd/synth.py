@@ -148,6 +148,16 @@ def make_weights(cfg: ModelConfig, seed: int = SEED_WEIGHTS, device: str = "cpu"
     return w
 
 
+def make_selfcond_weights(cfg: ModelConfig, seed: int = SEED_WEIGHTS, device: str = "cpu",
+                          std: float = 0.02) -> dict:
+    """Random-init weights of the self-conditioning feed-forward network (a SwiGLU network
+    d -> shared_ffn -> d): {"sc_gate_up": [2 Fs][d] (Fs gate rows, then Fs up rows),
+    "sc_down": [d][Fs]}, bf16, each from its own seeded generator."""
+    d, Fs = cfg.d_model, cfg.shared_ffn
+    return {"sc_gate_up": _normal_bf16((2 * Fs, d), std, _gen(seed * 1000003 + 3, device), device),
+            "sc_down": _normal_bf16((d, Fs), std, _gen(seed * 1000003 + 4, device), device)}
+
+
 def make_prompt(cfg: ModelConfig, batch: int, length: int, seed: int = SEED_PROMPT,
                 device: str = "cpu") -> torch.Tensor:
     """Uniform-random token ids in [0, V): int32 [batch][length]."""
@@ -195,7 +205,7 @@ def expected_unique_experts(n_experts: int, assignments: int) -> float:
     return n_experts * (1.0 - (1.0 - 1.0 / n_experts) ** assignments)
 
 
-__all__ = ["ModelConfig", "CONFIGS", "make_weights", "make_prompt", "make_canvas",
+__all__ = ["ModelConfig", "CONFIGS", "make_weights", "make_selfcond_weights", "make_prompt", "make_canvas",
            "make_sampler_logits", "make_masked_canvas", "make_uniforms", "layer_shapes",
            "LAYER_KEYS", "SEED_WEIGHTS", "SEED_PROMPT", "SEED_LOGITS", "SEED_MASKED",
            "expected_unique_experts"]

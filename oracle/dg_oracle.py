@@ -37,6 +37,8 @@ in the design notes of the repository):
     by (H asc, position asc); S_k = running fp64 sum of H in that order;
     commit the first k* = max(1, max{k : S_k <= gamma}) positions, or all
     when commit_all (the last step of a block).
+  * Self-conditioning: z = SwiGLU(softmax(L) E) from a step's logits, added to the
+    canvas rows' input at the next step (0 at the first).
   * Uniform ("multinomial") variant: the canvas starts as uniformly random tokens;
     every position is a candidate at every step; accepted positions take their
     argmax and the rest are re-noised uniformly (Philox4x64-10 tokens).
@@ -271,12 +273,15 @@ def prefill_kv(cfg, weights: dict, kv: KVCache, tokens: np.ndarray, rnd: bool = 
 
 
 def denoise_step(cfg, weights: dict, kv: KVCache, canvas: np.ndarray, t: float,
-                 rnd: bool = True, trace: Optional[list] = None) -> np.ndarray:
+                 rnd: bool = True, trace: Optional[list] = None,
+                 z: Optional[np.ndarray] = None) -> np.ndarray:
     """Bidirectional decoder pass over the canvas [B][C]; returns logits float64 [B][C][V].
 
     DiffusionGemma Technical Report §3.1–3.2: the canvas attends to the cached
     context and bidirectionally within itself; "DiffusionGemma 深度解析": a
     timestep embedding conditions the denoiser.  Canvas K/V are not cached.
+    z [B][C][d] (optional): the self-conditioning signal, added to the canvas rows'
+    input with the timestep embedding (see self_condition).
     """
     R = bf16 if rnd else _ident
     canvas = np.asarray(canvas)
@@ -289,6 +294,8 @@ def denoise_step(cfg, weights: dict, kv: KVCache, canvas: np.ndarray, t: float,
         P = kv.len[b]
         pos = np.arange(P, P + C)
         x = _embed_rows(weights, canvas[b]) + temb[None, :]
+        if z is not None:
+            x = x + np.asarray(z[b], np.float64)
         for l in range(cfg.n_layers):
             lo = 0 if cfg.is_global(l) else max(0, P - cfg.window)
 
@@ -302,6 +309,40 @@ def denoise_step(cfg, weights: dict, kv: KVCache, canvas: np.ndarray, t: float,
         hf = R(rms_norm(x, weights["final_norm"], cfg.rms_eps))
         logits[b] = hf @ E.T
     return logits
+
+
+# --------------------------------------------------------------------------------------
+# Self-conditioning
+# --------------------------------------------------------------------------------------
+#
+# DiffusionGemma Technical Report §3.2 (decoder forward pass; denoising iteration, eq. 5-6)
+# and §6 (GPU time breakdown, sampling): the decoder has a third input z_t in R^{C x d}
+# that feeds its previous prediction back.  After each step the clean-token probabilities
+# p̂₀ = softmax(L_t) over the vocabulary give z_{t - dt} = FFW(p̂₀ E), E the token embedding
+# matrix [V][d], FFW a feed-forward network; the embedding product and the softmax run in
+# full precision.  Readings: z enters the decoder added to the canvas rows' input
+# embedding (beside the timestep embedding); z = 0 at a canvas's first step (training
+# conditions half its data on z = 0); p̂₀ is the plain softmax (temperature 1: the
+# temperature only shapes the transition); FFW is a SwiGLU network d -> Fs -> d (Fs =
+# the shared expert's width) with its own weights, computed like the model's other
+# feed-forward networks (its input p̂₀E and its activation stored in bf16); with
+# self-conditioning every canvas row's logits are computed at every step.
+
+def self_condition(logits: np.ndarray, embed: np.ndarray, sc: dict, rnd: bool = True):
+    """z [n][d] (and u = p̂₀ E, float64 [n][d]) from rows of logits [n][V] (the values the
+    decoder stored).  p̂₀ = softmax of each row in float64; u = p̂₀ · E[0:V]; z = SwiGLU
+    with sc["sc_gate_up"] ([2 Fs][d]: Fs gate rows, then Fs up rows) and sc["sc_down"]
+    ([d][Fs]) on u rounded to bf16."""
+    R = bf16 if rnd else _ident
+    L = np.asarray(logits, np.float64)
+    V = L.shape[-1]
+    e = np.exp(L - L.max(axis=-1, keepdims=True))
+    p = e / e.sum(axis=-1, keepdims=True)
+    u = p @ np.asarray(embed[:V], np.float64)
+    wgu = np.asarray(sc["sc_gate_up"], np.float64)
+    Fs = wgu.shape[0] // 2
+    z = swiglu_ffn(R(u), wgu[:Fs], wgu[Fs:], sc["sc_down"], R)
+    return z, u
 
 
 # --------------------------------------------------------------------------------------
@@ -549,26 +590,33 @@ def generate_block(cfg, weights: dict, kv: KVCache, batch: int, steps: int, gamm
 
 def generate_block_annealed(cfg, weights: dict, kv: KVCache, batch: int, max_steps: int, gamma: float,
                             tau_max: float, tau_min: float, e_stop: float, append: bool = True,
-                            rnd: bool = True, record: Optional[list] = None):
+                            rnd: bool = True, record: Optional[list] = None,
+                            self_cond: Optional[dict] = None):
     """The Technical Report's sampler (§3.3) on the absorbing canvas: up to max_steps steps
     with t_s = 1 - s/max_steps, entropies at the annealed temperature
     temperature(t_s, tau_max, tau_min), and the adaptive stop, which commits every masked
     position of a sequence at once; the last step commits the rest.  Steps after a
-    sequence is complete change nothing for it.  Returns (canvas [B][C], steps [B]): the
-    step count after which each canvas was complete."""
+    sequence is complete change nothing for it.  With self_cond (self-conditioning weights,
+    see self_condition) each step's decoder takes z from the previous step's logits (z = 0
+    at the first step).  Returns (canvas [B][C], steps [B]): the step count after which
+    each canvas was complete."""
     canvas = np.full((batch, cfg.canvas), cfg.mask_id, dtype=np.int64)
     prev = np.full((batch, cfg.canvas), -1, dtype=np.int64)
     done_at = np.zeros(batch, dtype=np.int64)
+    z = np.zeros((batch, cfg.canvas, cfg.d_model)) if self_cond is not None else None
     for s in range(max_steps):
         t = 1.0 - s / max_steps
         tau = temperature(t, tau_max, tau_min)
-        logits = denoise_step(cfg, weights, kv, canvas, t, rnd)
+        logits = denoise_step(cfg, weights, kv, canvas, t, rnd, z=z)
         stored = bf16(logits) if rnd else logits
+        z_in = z
+        if self_cond is not None:
+            z = np.stack([self_condition(stored[b], weights["embed"], self_cond, rnd)[0] for b in range(batch)])
         new, H32, amax, n_masked, committed = sample_eb(stored, canvas, gamma, s == max_steps - 1,
                                                         cfg.mask_id, tau, e_stop, prev)
         if record is not None:
             record.append({"t": t, "tau": tau, "canvas_in": canvas.copy(), "H": H32, "argmax": amax,
-                           "n_masked": n_masked, "committed": committed})
+                           "n_masked": n_masked, "committed": committed, "z_in": z_in})
         for b in range(batch):
             if done_at[b] == 0 and n_masked[b] == 0:
                 done_at[b] = s + 1
@@ -673,27 +721,32 @@ def sample_eb_uniform(logits: np.ndarray, canvas: np.ndarray, gamma: float, comm
 def generate_block_uniform(cfg, weights: dict, kv: KVCache, batch: int, max_steps: int, gamma: float,
                            seed: int, tau_max: float = 1.0, tau_min: float = 1.0,
                            e_stop: Optional[float] = None, append: bool = True, rnd: bool = True,
-                           record: Optional[list] = None):
+                           record: Optional[list] = None, self_cond: Optional[dict] = None):
     """One canvas per sequence by the uniform variant: the canvas starts as
     uniform_canvas(seed, 0, ...); step s (t_s = 1 - s/max_steps, temperature
     temperature(t_s, tau_max, tau_min)) runs the decoder over the whole canvas and
-    sample_eb_uniform with draw s + 1; the last step accepts every position.  Returns
-    (canvas [B][C], steps [B]): the step count after which each canvas was complete."""
+    sample_eb_uniform with draw s + 1; the last step accepts every position.  With
+    self_cond, z as in generate_block_annealed.  Returns (canvas [B][C], steps [B]): the
+    step count after which each canvas was complete."""
     C, V = cfg.canvas, cfg.vocab
     canvas = uniform_canvas(seed, 0, batch, C, V)
     prev = np.full((batch, C), -1, dtype=np.int64)
     done_at = np.zeros(batch, dtype=np.int64)
+    z = np.zeros((batch, C, cfg.d_model)) if self_cond is not None else None
     for s in range(max_steps):
         t = 1.0 - s / max_steps
         tau = temperature(t, tau_max, tau_min)
         frozen = done_at > 0
-        logits = denoise_step(cfg, weights, kv, canvas, t, rnd)
+        logits = denoise_step(cfg, weights, kv, canvas, t, rnd, z=z)
         stored = bf16(logits) if rnd else logits
+        z_in = z
+        if self_cond is not None:
+            z = np.stack([self_condition(stored[b], weights["embed"], self_cond, rnd)[0] for b in range(batch)])
         new, H32, amax, n_open, accepted, complete = sample_eb_uniform(
             stored, canvas, gamma, s == max_steps - 1, seed, s + 1, tau, e_stop, prev, frozen)
         if record is not None:
             record.append({"t": t, "tau": tau, "canvas_in": canvas.copy(), "H": H32, "argmax": amax,
-                           "n_open": n_open, "accepted": accepted, "complete": complete})
+                           "n_open": n_open, "accepted": accepted, "complete": complete, "z_in": z_in})
         for b in range(batch):
             if not frozen[b] and complete[b]:
                 done_at[b] = s + 1
