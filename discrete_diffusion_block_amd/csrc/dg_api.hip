@@ -30,6 +30,10 @@ struct dg_ctx {
   const uint16_t* embed;
   const float* final_norm;
   std::vector<dg_layer_weights> layers;
+  // self-conditioning weights (all NULL: none)
+  const uint16_t* embed_t = nullptr;
+  const uint16_t* sc_gate_up = nullptr;
+  const uint16_t* sc_down = nullptr;
   mutable Prof prof;
   // Side stream for the shared expert, which runs concurrently with the routed
   // experts' routing chain; forked from and joined back into the caller's stream
@@ -188,6 +192,12 @@ struct Ws {
   float* shf;          // [batch][C]: fast entropies
   float2* swin;        // [batch]: boundary windows
   int32_t* skstar;     // [batch]
+  // self-conditioning (carved only when the ctx has its weights): rows = batch * C
+  float2* sc_stats;    // [rows]: (max log2e, 1 / S)
+  float* sc_part;      // [splits][rows][d]: partial sums of p̂₀ E
+  uint16_t* sc_u;      // p̂₀ E in bf16, fragment-major [rows_pad][d]
+  uint16_t* sc_act;    // FFW activation, fragment-major [rows_pad][Fs]
+  float* sc_z;         // the signal, fp32 row-major [rows][d]
 };
 
 struct Carver {
@@ -220,7 +230,7 @@ size_t carve_sampler(Carver& cv, int batch, int canvas, int vocab, Ws* ws) {
 
 size_t round16(size_t v) { return (v + 15) / 16 * 16; }
 
-size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
+size_t carve(const dg_config& c, int batch, char* base, Ws* ws, bool self_cond) {
   const size_t n = (size_t)std::max(c.canvas, kPrefillChunk);
   const size_t M = (size_t)batch * n;
   const size_t Mp = round16(M);
@@ -257,6 +267,17 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws) {
   ws->ys = cv.take<float>(M * c.d_model);
   ws->prev_amax = cv.take<int32_t>((size_t)batch * c.canvas);
   carve_sampler(cv, batch, c.canvas, c.vocab, ws);
+  ws->sc_stats = nullptr;
+  ws->sc_part = ws->sc_z = nullptr;
+  ws->sc_u = ws->sc_act = nullptr;
+  if (self_cond) {
+    const size_t rows = (size_t)batch * c.canvas;
+    ws->sc_stats = cv.take<float2>(rows);
+    ws->sc_part = cv.take<float>((size_t)sc_splits((int)rows, c.d_model, c.vocab) * rows * c.d_model);
+    ws->sc_u = cv.take<uint16_t>(round16(rows) * c.d_model);
+    ws->sc_act = cv.take<uint16_t>(round16(rows) * c.shared_ffn);
+    ws->sc_z = cv.take<float>(rows * c.d_model);
+  }
   return cv.off + kAlign;
 }
 
@@ -308,7 +329,8 @@ KvLayer kv_layer(const dg_ctx* ctx, const dg_kv* kv, int l) {
 // [MASK] -- the only rows the sampler reads -- and leaves the other logits rows as
 // they were.
 dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const int32_t* tokens,
-                   float t, uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false) {
+                   float t, uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false,
+                   const float* z = nullptr) {
   const dg_config& c = ctx->cfg;
   const int M = g.batch * g.n;
   const int d = c.d_model, hq = c.n_q_heads, hd = c.head_dim, E = c.n_experts, k = c.top_k;
@@ -318,8 +340,8 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
   DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr,
                                        ws.counters, kPassCounters, s));
   DG_TIMED(ctx, DG_K_EMBED,
-           launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, ctx->layers[0].attn_norm,
-                             eps, ws.x, ws.h, M, d, c.vocab, s));
+           launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, g.denoise ? z : nullptr,
+                             ctx->layers[0].attn_norm, eps, ws.x, ws.h, M, d, c.vocab, s));
   for (int l = 0; l < nl; ++l) {
     const dg_layer_weights& L = ctx->layers[l];
     const KvLayer kvl = kv_layer(ctx, kv, l);
@@ -386,16 +408,17 @@ dg_status check_kv(const dg_ctx* ctx, const dg_kv* kv, int batch) {
 }
 
 dg_status get_ws(const dg_ctx* ctx, int batch, void* d_ws, size_t ws_bytes, Ws* ws) {
-  const size_t need = carve(ctx->cfg, batch, nullptr, ws);
+  const size_t need = carve(ctx->cfg, batch, nullptr, ws, ctx->embed_t != nullptr);
   if (!d_ws) return fail(DG_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
-  carve(ctx->cfg, batch, base, ws);
+  carve(ctx->cfg, batch, base, ws, ctx->embed_t != nullptr);
   return DG_OK;
 }
 
 dg_status denoise_impl(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, int batch, float t,
-                       uint16_t* d_logits, const Ws& ws, hipStream_t s, bool masked_head = false) {
+                       uint16_t* d_logits, const Ws& ws, hipStream_t s, bool masked_head = false,
+                       const float* z = nullptr) {
   PassGeom g{};
   g.batch = batch;
   g.n = ctx->cfg.canvas;
@@ -406,7 +429,22 @@ dg_status denoise_impl(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, in
                   (long long)kv->len[b], ctx->cfg.canvas, ctx->cfg.max_ctx);
     g.len[b] = (int)kv->len[b];
   }
-  return run_pass(ctx, kv, g, d_canvas, t, d_logits, ws, s, masked_head);
+  return run_pass(ctx, kv, g, d_canvas, t, d_logits, ws, s, masked_head, z);
+}
+
+// Self-conditioning signal z (and u = p̂₀ E in fp32 when u_out is given) of the
+// batch * C logits rows (Technical Report §3.2, eq. 5-6).
+dg_status self_cond_impl(const dg_ctx* ctx, const uint16_t* logits, int batch, float* z, float* u_out,
+                         const Ws& ws, hipStream_t s) {
+  const dg_config& c = ctx->cfg;
+  const int M = batch * c.canvas, d = c.d_model, V = c.vocab;
+  DG_TIMED(ctx, DG_K_SC_STATS, launch_sc_rowstats(logits, M, V, ws.sc_stats, s));
+  DG_TIMED(ctx, DG_K_SC_EMBED, launch_sc_embed(logits, ws.sc_stats, ctx->embed_t, M, d, V, ws.sc_part, s));
+  DG_TIMED(ctx, DG_K_SC_REDUCE,
+           launch_sc_reduce(ws.sc_part, sc_splits(M, d, V), ws.sc_stats, M, d, ws.sc_u, u_out, s));
+  DG_TIMED(ctx, DG_K_SC_FFW, launch_gemm_swiglu(ws.sc_u, ctx->sc_gate_up, M, c.shared_ffn, d, ws.sc_act, s));
+  DG_TIMED(ctx, DG_K_SC_FFW, launch_gemm_f32(ws.sc_act, ctx->sc_down, z, M, d, c.shared_ffn, /*add=*/false, s));
+  return check_launch("self-conditioning");
 }
 
 dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batch, int n,
@@ -549,8 +587,10 @@ dg_status sample_checked(const uint16_t* d_logits, int32_t* d_canvas, int batch,
 dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
                             float tau_max, float tau_min, float e_stop, int uniform, uint64_t seed, int append_kv,
                             uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step, void* d_ws, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, bool self_cond = false) {
   if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (self_cond && !ctx->embed_t)
+    return fail(DG_ERR_UNSUPPORTED, "the ctx was created without self-conditioning weights");
   dg_status st = check_kv(ctx, kv, batch);
   if (st != DG_OK) return st;
   if (!d_canvas || !d_logits || !d_n || !d_done_step) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
@@ -585,8 +625,15 @@ dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     o.uniform = uniform;
     o.seed = seed;
     o.draw = step + 1;
-    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/!uniform);
+    // with self-conditioning every row's logits feed z; otherwise the absorbing canvas
+    // needs only its [MASK] rows
+    st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/!uniform && !self_cond,
+                      self_cond && step > 0 ? ws.sc_z : nullptr);
     if (st != DG_OK) return st;
+    if (self_cond && step + 1 < max_steps) {
+      st = self_cond_impl(ctx, d_logits, batch, ws.sc_z, nullptr, ws, s);
+      if (st != DG_OK) return st;
+    }
     st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == max_steps - 1, nullptr,
                      nullptr, d_n, ws, s, ctx, o);
     if (st != DG_OK) return st;
@@ -631,12 +678,18 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, dg_ctx** out) {
         !L.ws_gate_up || !L.ws_down)
       return fail(DG_ERR_INVALID_ARG, "layer %d has a NULL weight", l);
   }
+  const int n_sc = (w->embed_t != nullptr) + (w->sc_gate_up != nullptr) + (w->sc_down != nullptr);
+  if (n_sc != 0 && n_sc != 3) return fail(DG_ERR_INVALID_ARG, "self-conditioning weights: set all three or none");
+  if (n_sc == 3 && cfg->vocab % 32) return fail(DG_ERR_SHAPE, "self-conditioning needs vocab % 32 == 0");
   dg_ctx* c = new (std::nothrow) dg_ctx;
   if (!c) return fail(DG_ERR_INVALID_ARG, "out of host memory");
   c->cfg = *cfg;
   c->embed = w->embed;
   c->final_norm = w->final_norm;
   c->layers.assign(w->layers, w->layers + cfg->n_layers);
+  c->embed_t = w->embed_t;
+  c->sc_gate_up = w->sc_gate_up;
+  c->sc_down = w->sc_down;
   int dev = -1;
   hipStream_t side = nullptr;
   if (hipGetDevice(&dev) == hipSuccess && hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess) {
@@ -666,7 +719,7 @@ dg_status dg_workspace_size(const dg_ctx* ctx, int batch, size_t* bytes) {
   if (!ctx || !bytes) return fail(DG_ERR_INVALID_ARG, "NULL argument");
   if (batch < 1 || batch > ctx->cfg.max_batch) return fail(DG_ERR_INVALID_ARG, "batch out of range");
   Ws ws;
-  *bytes = carve(ctx->cfg, batch, nullptr, &ws);
+  *bytes = carve(ctx->cfg, batch, nullptr, &ws, ctx->embed_t != nullptr);
   return DG_OK;
 }
 
@@ -841,6 +894,39 @@ dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, i
                            append_kv, d_logits, d_n_open, d_done_step, d_ws, ws_bytes, stream);
 }
 
+dg_status dg_generate_block_sc(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
+                               float tau_max, float tau_min, float e_stop, int uniform, uint64_t seed,
+                               int append_kv, uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step,
+                               void* d_ws, size_t ws_bytes, void* stream) {
+  return generate_annealed(ctx, kv, d_canvas, batch, max_steps, gamma, tau_max, tau_min, e_stop, uniform ? 1 : 0,
+                           seed, append_kv, d_logits, d_n, d_done_step, d_ws, ws_bytes, stream, /*self_cond=*/true);
+}
+
+dg_status dg_self_cond(dg_ctx* ctx, const uint16_t* d_logits, int batch, float* d_z, float* d_u, void* d_ws,
+                       size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (!ctx->embed_t) return fail(DG_ERR_UNSUPPORTED, "the ctx was created without self-conditioning weights");
+  if (!d_logits || !d_z) return fail(DG_ERR_INVALID_ARG, "logits or z is NULL");
+  if (batch < 1 || batch > ctx->cfg.max_batch) return fail(DG_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
+  Ws ws;
+  dg_status st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  return self_cond_impl(ctx, d_logits, batch, d_z, d_u, ws, (hipStream_t)stream);
+}
+
+dg_status dg_denoise_step_sc(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, int batch, float t,
+                             const float* d_z, uint16_t* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_canvas || !d_logits) return fail(DG_ERR_INVALID_ARG, "canvas or logits is NULL");
+  if (!(t >= 0.f && t <= 1.f)) return fail(DG_ERR_INVALID_ARG, "t must be in [0, 1]");
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  return denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, (hipStream_t)stream, false, d_z);
+}
+
 dg_status dg_packed_elems(int rows, int cols, size_t* elems) {
   if (!elems || rows < 1 || cols < 32 || cols % 32) return fail(DG_ERR_INVALID_ARG, "bad packing shape");
   *elems = round16((size_t)rows) * (size_t)cols;
@@ -857,6 +943,10 @@ dg_status dg_pack_weight(int kind, const uint16_t* d_src, uint16_t* d_dst, int n
   } else if (kind == DG_PACK_GATE_UP) {
     if (param < 16 || param % 16 || rows != 2 * param)
       return fail(DG_ERR_INVALID_ARG, "gate/up packing needs rows = 2 * F, F % 16 == 0");
+  } else if (kind == DG_PACK_TRANSPOSE) {
+    if (n_mats != 1 || rows % 32) return fail(DG_ERR_INVALID_ARG, "transpose packing needs n_mats = 1, rows % 32 == 0");
+    launch_pack_transpose(d_src, d_dst, rows, cols, (hipStream_t)stream);
+    return check_launch("pack");
   } else if (kind != DG_PACK_PLAIN) {
     return fail(DG_ERR_INVALID_ARG, "unknown packing kind");
   }
@@ -924,7 +1014,7 @@ dg_status dg_test_sample_eb_profiled(dg_ctx* ctx, const uint16_t* d_logits, int3
 dg_status dg_workspace_moe_counts(const dg_ctx* ctx, int batch, size_t* offset) {
   if (!ctx || !offset || batch < 1 || batch > ctx->cfg.max_batch) return fail(DG_ERR_INVALID_ARG, "bad arguments");
   Ws ws;
-  carve(ctx->cfg, batch, reinterpret_cast<char*>(kAlign), &ws);   // offsets relative to an aligned base
+  carve(ctx->cfg, batch, reinterpret_cast<char*>(kAlign), &ws, ctx->embed_t != nullptr);   // offsets relative to an aligned base
   *offset = reinterpret_cast<uintptr_t>(ws.cnt_log) - kAlign;
   return DG_OK;
 }

@@ -73,7 +73,8 @@ inline void raise_lds_limit(LdsLimit& st, const void* fn, int bytes) {
 // also clears zero[0 .. nzero)
 void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
                  float* temb, int32_t* zero, int nzero, hipStream_t s);
-void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
+// z (optional): the self-conditioning signal, fp32 row-major [M][d], added with temb
+void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb, const float* z,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s);
 // h: fragment-major; h_rm (optional): the same values row-major [M][d]
@@ -141,6 +142,8 @@ void launch_moe_down(const uint16_t* a, const uint16_t* w_down, const int32_t* c
 // ---- weight packing ----
 void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int kind, int param,
                  hipStream_t s);
+// Fragment-major copy of the transpose of row-major src [rows][cols]: packed [cols][rows].
+void launch_pack_transpose(const uint16_t* src, uint16_t* dst, int rows, int cols, hipStream_t s);
 
 // ---- sampler ----
 constexpr int kSampleChunk = 16384;  // logits per workgroup in the first sampler pass (multiple of 2048)
@@ -182,6 +185,20 @@ void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canva
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                             int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
                             int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s);
+// ---- self-conditioning (p̂₀ = softmax of each logits row, u = p̂₀ E, z = FFW(u)) ----
+// k slices of the p̂₀ E product for M rows, N = d features, K = V (the partial buffer
+// holds sc_splits * M * N floats).
+int sc_splits(int M, int N, int K);
+// stats[m] = (m log2e, 1 / S): the row maximum and the softmax denominator, fp32.
+void launch_sc_rowstats(const uint16_t* logits, int M, int V, float2* stats, hipStream_t s);
+// part[split][m][n] = sum over the split's k of exp(x_mk - max_m) E^T[n][k]; et: E^T
+// packed fragment-major ([N][K]).
+void launch_sc_embed(const uint16_t* logits, const float2* stats, const uint16_t* et, int M, int N, int K,
+                     float* part, hipStream_t s);
+// u = (sum of the partials) / S: bf16 fragment-major into u_fm, fp32 row-major into
+// u_out when given.
+void launch_sc_reduce(const float* part, int nsplit, const float2* stats, int M, int N, uint16_t* u_fm,
+                      float* u_out, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

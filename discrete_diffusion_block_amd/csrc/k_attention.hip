@@ -33,14 +33,6 @@
 
 namespace dg {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> bf16 (round to nearest even) in one instruction, packed low first.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
 struct AttnArgs {
   const uint16_t* q;      // fragment-major per (sequence, q head): [npad16][HD]
   uint16_t* o;            // fragment-major [M_pad][hq * HD] (written when nsplit == 1)

@@ -79,8 +79,9 @@ __device__ __forceinline__ void norm_row(const float* xr, const float* gain, flo
   }
 }
 
+// x[m] = E[token] (+ temb) (+ z[m], the self-conditioning signal), then the first RMSNorm.
 __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed,
-                                                         const float* temb, const float* gain,
+                                                         const float* temb, const float* z, const float* gain,
                                                          float eps, float* x, uint16_t* h, int d,
                                                          int vocab) {
   __shared__ float red[16];
@@ -103,6 +104,12 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens,
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] += tt[j];
     }
+    if (z) {
+      float zz[8];
+      load8(z + (size_t)m * d + c, zz);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] += zz[j];
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
     store8(xr + c, v);
@@ -113,11 +120,11 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens,
 // threads of a row workgroup: one per 8 features, whole waves, at most 1024
 static int row_threads(int d) { return std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64)); }
 
-void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb,
+void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb, const float* z,
                        const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
                        hipStream_t s) {
-  launch_kernel(embed_norm_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, tokens, embed, temb, gain, eps, x, h, d,
-                vocab);
+  launch_kernel(embed_norm_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, tokens, embed, temb, z, gain, eps, x,
+                h, d, vocab);
 }
 
 __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* x, const float* gain, float eps,

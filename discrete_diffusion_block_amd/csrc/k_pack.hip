@@ -6,6 +6,8 @@
 //             four output rows are the rotary pairs (i, i+hd/2), (i+1, i+1+hd/2).
 //  * gate_up: packed block 2t = gate rows 16t.., block 2t+1 = up rows F+16t..,
 //             so one 32-row wave tile carries matching gate and up features.
+//  * transpose: the packed matrix is the source's transpose (the embedding as the
+//             k-major operand of the self-conditioning product).
 #include "dg_common.h"
 #include "dg_internal.h"
 
@@ -50,6 +52,33 @@ void launch_pack(const uint16_t* src, uint16_t* dst, int nmat, int R, int K, int
   const size_t total = (size_t)nmat * Rpad * (K / 8);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
   launch_kernel(pack_kernel, dim3(blocks), dim3(256), 0, s, nullptr, src, dst, nmat, R, K, Rpad, kind, param);
+}
+
+// One thread per 8 consecutive packed columns (source rows c .. c + 7) of one packed
+// row p (source column p); one-time work, so the strided gather is acceptable.
+__global__ void pack_transpose_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int rows,
+                                      int cols, int Rpad) {
+  const size_t total = (size_t)Rpad * (rows >> 3);
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % (size_t)(rows >> 3)) * 8;
+    const int p = (int)(i / (size_t)(rows >> 3));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p < cols) {
+      uint16_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = src[(size_t)(c + j) * cols + p];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (uint32_t)e[2 * j] | ((uint32_t)e[2 * j + 1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + fm_index(p, c, rows)) = v;
+  }
+}
+
+void launch_pack_transpose(const uint16_t* src, uint16_t* dst, int rows, int cols, hipStream_t s) {
+  const int Rpad = (cols + 15) / 16 * 16;
+  const size_t total = (size_t)Rpad * (rows / 8);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  launch_kernel(pack_transpose_kernel, dim3(blocks), dim3(256), 0, s, nullptr, src, dst, rows, cols, Rpad);
 }
 
 // Row-major bf16 activations -> fragment-major (test tap support).

@@ -25,8 +25,8 @@ MAX_BATCH = 64
 KERNEL_KINDS = ["prep", "embed", "qkv", "attention", "o_proj", "norm", "router", "topk", "route",
                 "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "combine", "head",
                 "sample_pass1", "sample_select", "fill", "sample_canon", "sample_select_canon",
-                "attention_global"]
-PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
+                "attention_global", "sc_stats", "sc_embed", "sc_reduce", "sc_ffw"]
+PACK_PLAIN, PACK_QKV, PACK_GATE_UP, PACK_TRANSPOSE = 0, 1, 2, 3
 MOE_GROUP = 64   # tokens per grouped-GEMM work item in the routing tap's item list
 
 STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE", -3: "DG_ERR_WORKSPACE",
@@ -51,7 +51,8 @@ class LayerWeights(C.Structure):
 
 
 class Weights(C.Structure):
-    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights))]
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights)),
+                ("embed_t", C.c_void_p), ("sc_gate_up", C.c_void_p), ("sc_down", C.c_void_p)]
 
 
 class KV(C.Structure):
@@ -88,6 +89,10 @@ def lib():
                                      vp, vp, sz, vp],
             "dg_generate_block_uniform": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, u64, i32, vp, vp,
                                           vp, vp, sz, vp],
+            "dg_self_cond": [vp, vp, i32, vp, vp, vp, sz, vp],
+            "dg_denoise_step_sc": [vp, C.POINTER(KV), vp, i32, f32, vp, vp, vp, sz, vp],
+            "dg_generate_block_sc": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, i32, u64, i32, vp, vp,
+                                     vp, vp, sz, vp],
             "dg_packed_elems": [i32, i32, C.POINTER(sz)],
             "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
             "dg_profile_begin": [vp, i32, C.c_uint32],
@@ -253,6 +258,27 @@ def dg_generate_block_uniform(ctx, kv: KV, canvas: torch.Tensor, max_steps: int,
                                            _p(n_open), _p(done_step), _p(ws), ws.numel(), _stream(stream)))
 
 
+def dg_self_cond(ctx, logits: torch.Tensor, z: torch.Tensor, ws: torch.Tensor, u: Optional[torch.Tensor] = None,
+                 stream=None):
+    _check(lib().dg_self_cond(ctx, _p(logits), logits.shape[0], _p(z), _p(u), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_denoise_step_sc(ctx, kv: KV, canvas: torch.Tensor, t: float, z: Optional[torch.Tensor], logits: torch.Tensor,
+                       ws: torch.Tensor, stream=None):
+    _check(lib().dg_denoise_step_sc(ctx, C.byref(kv), _p(canvas), canvas.shape[0], float(t), _p(z), _p(logits),
+                                    _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_generate_block_sc(ctx, kv: KV, canvas: torch.Tensor, max_steps: int, gamma: float, tau_max: float,
+                         tau_min: float, e_stop: float, uniform: bool, seed: int, append_kv: bool,
+                         logits: torch.Tensor, n: torch.Tensor, done_step: torch.Tensor, ws: torch.Tensor,
+                         stream=None):
+    _check(lib().dg_generate_block_sc(ctx, C.byref(kv), _p(canvas), canvas.shape[0], max_steps, float(gamma),
+                                      float(tau_max), float(tau_min), float(e_stop), int(bool(uniform)),
+                                      int(seed) & (2 ** 64 - 1), int(bool(append_kv)), _p(logits), _p(n),
+                                      _p(done_step), _p(ws), ws.numel(), _stream(stream)))
+
+
 def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_kv: bool,
                       logits: torch.Tensor, n_masked: torch.Tensor, ws: torch.Tensor, stream=None):
     _check(lib().dg_generate_block(ctx, C.byref(kv), _p(canvas), canvas.shape[0], steps, float(gamma),
@@ -272,10 +298,12 @@ def dg_pack_weight(kind: int, src: torch.Tensor, dst: torch.Tensor, n_mats: int,
 
 
 def pack(t: torch.Tensor, kind: int = PACK_PLAIN, param: int = 0) -> torch.Tensor:
-    """Fragment-major copy of the bf16 matrices in t (shape [..., rows, cols])."""
+    """Fragment-major copy of the bf16 matrices in t (shape [..., rows, cols]); with
+    PACK_TRANSPOSE, of the transpose of the single matrix t."""
     rows, cols = t.shape[-2], t.shape[-1]
     n_mats = t.numel() // (rows * cols)
-    dst = torch.empty(n_mats * dg_packed_elems(rows, cols), dtype=torch.bfloat16, device=t.device)
+    elems = dg_packed_elems(cols, rows) if kind == PACK_TRANSPOSE else n_mats * dg_packed_elems(rows, cols)
+    dst = torch.empty(elems, dtype=torch.bfloat16, device=t.device)
     dg_pack_weight(kind, t.contiguous(), dst, n_mats, rows, cols, param)
     return dst
 
@@ -294,9 +322,20 @@ def pack_layer(cfg: ModelConfig, lw: dict) -> dict:
     }
 
 
-def pack_weights(cfg: ModelConfig, w: dict, free_source: bool = False) -> dict:
-    """Engine-layout copy of synth.make_weights output (device tensors)."""
+def pack_selfcond(cfg: ModelConfig, embed: torch.Tensor, sc: dict) -> dict:
+    """Engine-layout self-conditioning weights: the transposed embedding rows 0..V-1 and
+    the FFW of synth.make_selfcond_weights (device tensors)."""
+    return {"embed_t": pack(embed[:cfg.vocab], PACK_TRANSPOSE),
+            "sc_gate_up": pack(sc["sc_gate_up"], PACK_GATE_UP, cfg.shared_ffn),
+            "sc_down": pack(sc["sc_down"])}
+
+
+def pack_weights(cfg: ModelConfig, w: dict, free_source: bool = False, selfcond: Optional[dict] = None) -> dict:
+    """Engine-layout copy of synth.make_weights output (device tensors); with selfcond
+    (synth.make_selfcond_weights output), also the self-conditioning weights."""
     out = {"embed": pack(w["embed"]), "final_norm": w["final_norm"], "layers": []}
+    if selfcond is not None:
+        out["selfcond"] = pack_selfcond(cfg, w["embed"], selfcond)
     if free_source:
         w["embed"] = None
     for l, lw in enumerate(w["layers"]):
@@ -405,9 +444,12 @@ class Engine:
     """
 
     def __init__(self, cfg: ModelConfig, weights: dict, max_batch: int = 1, max_ctx: int = 2048,
-                 device: str = "cuda", packed: bool = False, free_source: bool = False):
+                 device: str = "cuda", packed: bool = False, free_source: bool = False,
+                 selfcond: Optional[dict] = None):
+        """selfcond: self-conditioning weights (synth.make_selfcond_weights) for unpacked
+        `weights`; packed weights carry them packed under "selfcond" (pack_weights)."""
         self.cfg = cfg
-        self.weights = weights if packed else pack_weights(cfg, weights, free_source)
+        self.weights = weights if packed else pack_weights(cfg, weights, free_source, selfcond)
         weights = self.weights
         self.ccfg = make_config(cfg, max_batch, max_ctx)
         n = cfg.n_layers
@@ -416,8 +458,11 @@ class Engine:
             lw = weights["layers"][l]
             for key in LAYER_KEYS:
                 setattr(self._layers[l], key, lw[key].data_ptr())
+        sc = weights.get("selfcond")
         self._w = Weights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
-                          C.cast(self._layers, C.POINTER(LayerWeights)))
+                          C.cast(self._layers, C.POINTER(LayerWeights)),
+                          sc["embed_t"].data_ptr() if sc else None, sc["sc_gate_up"].data_ptr() if sc else None,
+                          sc["sc_down"].data_ptr() if sc else None)
         self.ctx = dg_create(self.ccfg, self._w)
         kv_bytes = dg_kv_size(self.ccfg)
         self.k_cache = torch.zeros(kv_bytes // 2, dtype=torch.int16, device=device)
@@ -491,6 +536,17 @@ class Engine:
                           done_step, seed, draw, n_open, entropy=None, argmax=None, stream=None):
         dg_sample_eb_uniform(logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step, done_step,
                              seed, draw, n_open, self.ws, entropy, argmax, stream)
+
+    def self_cond(self, logits, z, u=None, stream=None):
+        dg_self_cond(self.ctx, logits, z, self.ws, u, stream)
+
+    def denoise_step_sc(self, canvas, t, z, logits, stream=None):
+        dg_denoise_step_sc(self.ctx, self.kv, canvas, t, z, logits, self.ws, stream)
+
+    def generate_block_sc(self, canvas, max_steps, gamma, tau_max, tau_min, e_stop, uniform, seed, append_kv, logits,
+                          n, done_step, stream=None):
+        dg_generate_block_sc(self.ctx, self.kv, canvas, max_steps, gamma, tau_max, tau_min, e_stop, uniform, seed,
+                             append_kv, logits, n, done_step, self.ws, stream)
 
     def generate_block_uniform(self, canvas, max_steps, gamma, tau_max, tau_min, e_stop, seed, append_kv,
                                logits, n_open, done_step, stream=None):

@@ -79,8 +79,13 @@ typedef struct dg_config {
  *                    that each lane receives the rotary pairs (i, i + hd/2);
  *   DG_PACK_GATE_UP  param = F, rows = 2F: 16-row block 2t = gate rows 16t..,
  *                    block 2t+1 = up rows F+16t..
+ *   DG_PACK_TRANSPOSE the packed matrix is the transpose [cols][rows] of the
+ *                    source (n_mats = 1, rows % 32 == 0; dst holds
+ *                    dg_packed_elems(cols, rows) elements) -- the embedding rows
+ *                    0..V-1 as the self-conditioning product's operand.
  * The source is not modified; the call only enqueues a kernel on `stream`. */
-typedef enum dg_pack_kind { DG_PACK_PLAIN = 0, DG_PACK_QKV = 1, DG_PACK_GATE_UP = 2 } dg_pack_kind;
+typedef enum dg_pack_kind { DG_PACK_PLAIN = 0, DG_PACK_QKV = 1, DG_PACK_GATE_UP = 2,
+                            DG_PACK_TRANSPOSE = 3 } dg_pack_kind;
 dg_status dg_packed_elems(int rows, int cols, size_t* elems);
 dg_status dg_pack_weight(int kind, const uint16_t* d_src, uint16_t* d_dst, int n_mats, int rows,
                          int cols, int param, void* stream);
@@ -104,6 +109,11 @@ typedef struct dg_weights {
   const uint16_t* embed;              /* plain-packed [V+1][d]; tied: logits use rows 0..V-1 */
   const float* final_norm;            /* fp32 [d] */
   const dg_layer_weights* layers;     /* HOST array of n_layers entries (copied by dg_create) */
+  /* Self-conditioning (Technical Report §3.2, eq. 5-6): all three NULL (no
+   * self-conditioning) or all set; needs vocab % 32 == 0. */
+  const uint16_t* embed_t;            /* TRANSPOSE-packed embedding rows 0..V-1: [d][V] */
+  const uint16_t* sc_gate_up;         /* GATE_UP-packed [2Fs][d], Fs = shared_ffn */
+  const uint16_t* sc_down;            /* plain-packed [d][Fs] */
 } dg_weights;
 
 /* KV cache (caller-owned device buffers, zero-filled before first use), each
@@ -294,6 +304,38 @@ dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, i
                                     int append_kv, uint16_t* d_logits, int32_t* d_n_open,
                                     int32_t* d_done_step, void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---- self-conditioning (Technical Report §3.2, decoder forward pass and denoising
+ * iteration, eq. 5-6; §6, sampling) ----
+ * The decoder's third input z [C][d] feeds its previous prediction back: from a
+ * step's logits L, p̂₀ = softmax(L) per row and z = FFW(p̂₀ E), E the embedding rows
+ * 0..V-1, FFW = W_down (silu(W_gate u) * (W_up u)) a SwiGLU network of width
+ * shared_ffn; z is added to the canvas rows' input (token embedding + timestep
+ * embedding) of the next step, and is 0 at a canvas's first step.  The softmax and
+ * the product p̂₀ E run at fp32 precision (p̂₀ carried to 2^-18 relative, fp32
+ * accumulation); u = p̂₀ E enters the FFW rounded to bf16 like every GEMM input.
+ * The ctx needs the self-conditioning weights (dg_weights.embed_t, sc_gate_up,
+ * sc_down); otherwise these calls return DG_ERR_UNSUPPORTED. */
+
+/* z (fp32 [batch][C][d], out) from d_logits (bf16 [batch][C][V], every row read);
+ * d_u (fp32 [batch][C][d], may be NULL): p̂₀ E before its bf16 rounding.  Workspace:
+ * dg_workspace_size of the ctx. */
+dg_status dg_self_cond(dg_ctx* ctx, const uint16_t* d_logits, int batch, float* d_z, float* d_u, void* d_ws,
+                       size_t ws_bytes, void* stream);
+
+/* dg_denoise_step with the self-conditioning signal d_z (fp32 [batch][C][d], NULL: z = 0,
+ * the plain pass) added to the canvas rows' input. */
+dg_status dg_denoise_step_sc(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, int batch, float t,
+                             const float* d_z, uint16_t* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+
+/* dg_generate_block_ex (uniform = 0) or dg_generate_block_uniform (uniform = 1, with
+ * seed) with self-conditioning: step 0 runs with z = 0, and after every step but the
+ * last z is recomputed from that step's logits for the next one; the head computes
+ * every canvas row at every step.  z lives in the workspace. */
+dg_status dg_generate_block_sc(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
+                               float tau_max, float tau_min, float e_stop, int uniform, uint64_t seed,
+                               int append_kv, uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step,
+                               void* d_ws, size_t ws_bytes, void* stream);
+
 /* ---- measurement helpers (diagnostics; not thread-safe) ---- */
 
 /* Kernel kinds the engine launches, for per-kind event timing. */
@@ -302,6 +344,7 @@ typedef enum dg_kernel_kind {
   DG_K_TOPK, DG_K_ROUTE, DG_K_MOE_GATE_UP, DG_K_MOE_DOWN, DG_K_SHARED_GATE_UP, DG_K_SHARED_DOWN,
   DG_K_COMBINE, DG_K_HEAD, DG_K_SAMPLE_PASS1, DG_K_SAMPLE_SELECT, DG_K_FILL,
   DG_K_SAMPLE_CANON, DG_K_SAMPLE_SELECT_CANON, DG_K_ATTENTION_GLOBAL,
+  DG_K_SC_STATS, DG_K_SC_EMBED, DG_K_SC_REDUCE, DG_K_SC_FFW,
   DG_K_COUNT
 } dg_kernel_kind;
 
