@@ -474,6 +474,104 @@ def spread_line(eng, cfg, n_distinct, reps, prompt_len):
             "append_pass_ms": round(pass_ms, 3), "roofline": out["moe_gate_up"], "moe_down": out["moe_down"]}
 
 
+UNIFORM_BLOCKS, UNIFORM_WARMUP = 3, 1
+
+
+def uniform_line(eng, cfg, args, logits):
+    """The uniform ("multinomial") variant of the Technical Report (§3.2, multinomial
+    diffusion; §3.3): the same model, context and sampler settings as the headline, but the
+    canvas starts as uniformly random tokens, every position stays a candidate at every
+    step (so the head computes all 256 rows of every step, where the absorbing canvas
+    needs only its [MASK] rows) and the rest are re-noised from the counter-based
+    generator.  Whole blocks with the KV append, timed on the host clock."""
+    import torch
+    C = cfg.canvas
+    canvas = torch.empty(1, C, dtype=torch.int32, device="cuda")
+    n_open = torch.empty(1, dtype=torch.int32, device="cuda")
+    done = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def block(i):
+        eng.generate_block_uniform(canvas, args.denoise_steps, args.gamma, 1.0, 1.0, -1.0, 1000 + i, True, logits,
+                                   n_open, done)
+    for i in range(UNIFORM_WARMUP):
+        block(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(UNIFORM_BLOCKS):
+        block(UNIFORM_WARMUP + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert n_open.item() == 0 and done.item() == args.denoise_steps
+    return {"workload": f"uniform-noise variant of the headline workload: a canvas of uniformly random tokens, "
+                        f"{args.denoise_steps} steps, gamma {args.gamma}, tau 1, every position revisable and "
+                        f"re-noised unless accepted, head over all {C} rows each step, KV append, batch 1",
+            "value": round(C * UNIFORM_BLOCKS / wall, 1), "unit": "tok/s",
+            "ms_per_block": round(wall * 1e3 / UNIFORM_BLOCKS, 2), "blocks": UNIFORM_BLOCKS,
+            "warmup": UNIFORM_WARMUP}
+
+
+SC_REPS, SC_BLOCKS, SC_WARMUP = 10, 3, 1
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def selfcond_line(eng, cfg, args, logits):
+    """Self-conditioning (Technical Report §3.2, eq. 5-6; §6, sampling): the signal
+    z = FFW(softmax(L) E) of a 256-row step, its kernels timed alone with HIP events over
+    SC_REPS calls on the logits of a denoising pass, and whole blocks of the absorbing
+    sampler with self-conditioning on (the head then computes every row at every step).
+    The embedding product is 2 * 256 * 2816 * 262144 = 378 GFLOP at the pages' full
+    precision; the engine runs it as two bf16 MFMA products (p in two bf16 parts), so
+    its rate is reported against the fp32 MFMA peak (the product's own precision) and,
+    for the MFMA work it issues, against the bf16 peak."""
+    import torch
+    from discrete_diffusion_block_amd import dg
+    C, V, d = cfg.canvas, cfg.vocab, cfg.d_model
+    c2 = torch.full((1, C), V, dtype=torch.int32, device="cuda")
+    eng.denoise_step(c2, 1.0, logits)
+    z = torch.empty(1, C, d, device="cuda")
+    eng.self_cond(logits, z)
+    torch.cuda.synchronize()
+    kinds = ["sc_stats", "sc_embed", "sc_reduce", "sc_ffw"]
+    dg.dg_profile_begin(eng.ctx, 8 * SC_REPS, kinds=kinds)
+    for _ in range(SC_REPS):
+        eng.self_cond(logits, z)
+    prof = dg.dg_profile_end(eng.ctx)
+    per = {k: prof[k][0] / SC_REPS for k in kinds}
+    emb_ms = prof["sc_embed"][0] / prof["sc_embed"][1]
+    flops = 2.0 * C * d * V
+    achieved = flops / (emb_ms * 1e-3) / 1e12
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    done = torch.empty(1, dtype=torch.int32, device="cuda")
+    canvas = torch.empty(1, C, dtype=torch.int32, device="cuda")
+
+    def block():
+        eng.generate_block_sc(canvas, args.denoise_steps, args.gamma, 1.0, 1.0, -1.0, False, 0, True, logits, n,
+                              done)
+    for _ in range(SC_WARMUP):
+        block()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(SC_BLOCKS):
+        block()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert n.item() == 0
+    return {"workload": f"self-conditioning signal of a {C}-row step (V {V}, d {d}, FFW width {cfg.shared_ffn}); "
+                        f"blocks: the headline workload with self-conditioning on ({args.denoise_steps} steps, gamma "
+                        f"{args.gamma}, z from each step's logits into the next, head over all rows)",
+            "ms_per_step": round(sum(per.values()), 4),
+            "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+            "embed_product": {"bound": "mfma", "algorithmic_gflop": round(flops / 1e9, 1),
+                              "achieved": round(achieved, 1), "unit": "TFLOP/s",
+                              "peak_fp32": FP32_MFMA_PEAK_TFLOPS,
+                              "frac_of_fp32_peak": round(achieved / FP32_MFMA_PEAK_TFLOPS, 3),
+                              "bf16_mfma_issued_tflops": round(2 * achieved, 1),
+                              "frac_of_bf16_peak": round(2 * achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "avg_launch_ms": round(emb_ms, 4)},
+            "blocks_tok_s": round(C * SC_BLOCKS / wall, 1), "ms_per_block": round(wall * 1e3 / SC_BLOCKS, 2),
+            "blocks": SC_BLOCKS, "warmup": SC_WARMUP}
+
+
 def long_context_line(packed, args):
     """The long-context batched workload: the same 30-layer model with every 6th layer
     attending globally (layers 5, 11, ..., 29; the rest a 1024-token window), 8 sequences
@@ -586,13 +684,14 @@ def main():
         return
     cfg = synth.CONFIGS["full"]
     C, V = cfg.canvas, cfg.vocab
-    n_blocks = args.warmup + args.steps + 4
+    n_blocks = args.warmup + args.steps + 4 + UNIFORM_BLOCKS + UNIFORM_WARMUP + SC_BLOCKS + SC_WARMUP
     max_ctx = int(math.ceil((args.prompt + C * n_blocks) / 64.0) * 64)
     t0 = time.time()
     w = synth.make_weights(cfg, device="cuda")
     torch.cuda.synchronize()
     log(f"weights {time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
-    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=max_ctx, free_source=True)
+    eng = dg.Engine(cfg, w, max_batch=1, max_ctx=max_ctx, free_source=True,
+                    selfcond=synth.make_selfcond_weights(cfg, device="cuda"))
     prompt = synth.make_prompt(cfg, 1, args.prompt, device="cuda")
     eng.prefill_kv(prompt)
     torch.cuda.synchronize()
@@ -703,6 +802,8 @@ def main():
         "sampler_roofline": None,
         "spread_routing": None,
         "long_context_batch8": None,
+        "uniform_variant": None,
+        "self_conditioning": None,
         "cpu_baseline": None,
     }
     if not args.no_extras:
@@ -710,6 +811,10 @@ def main():
         out["sampler_roofline"] = sampler_roofline(eng, cfg, args.gamma)
         log("spread routing...")
         out["spread_routing"] = spread_line(eng, cfg, args.spread_distinct, reps, args.prompt)
+        log("uniform-noise variant...")
+        out["uniform_variant"] = uniform_line(eng, cfg, args, logits)
+        log("self-conditioning...")
+        out["self_conditioning"] = selfcond_line(eng, cfg, args, logits)
         packed = eng.weights
         eng.close()
         del logits

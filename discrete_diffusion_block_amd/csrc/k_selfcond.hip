@@ -11,11 +11,11 @@
 //    to 2^-18 relative, and accumulates in fp32 -- the same precision as an fp32 GEMM
 //    over this length, at the bf16 rate.  E enters transposed (E^T [d][V] packed once,
 //    fragment-major), so each MFMA operand is one contiguous 1 KiB wave load.
-//    Workgroup tile: 256 features x 256 canvas rows x one k slice; the four waves share
+//    Workgroup tile: 256 features x 256 canvas rows x one k slice; the waves share
 //    the E^T tiles (global->LDS copies, three-step ring) and the p tiles (each wave
-//    copies a quarter of the logits chunks into LDS, turns them into p tiles and stores
-//    those in a two-step ring); each wave owns a 128 x 128 quarter of the outputs (8 x 8
-//    MFMA blocks).  Every global read is a direct global->LDS copy waited for
+//    copies a quarter of the logits chunks into LDS, three-step ring, turns them into p
+//    tiles and stores those in a two-step ring); both copy streams run two k steps ahead;
+//    each of the four waves owns a 128 x 128 quarter of the outputs (8 x 8 MFMA blocks).  Every global read is a direct global->LDS copy waited for
 //    explicitly, so no copy in flight ever holds up the one being waited for.  The row tiles of one (row block, k
 //    slice) run consecutively on one XCD, so its logits slice is fetched into that L2
 //    once.  Partial sums go to part[split][m][n].
@@ -84,13 +84,14 @@ __global__ __launch_bounds__(256) void sc_rowstats_kernel(const uint16_t* __rest
 
 constexpr int kScRB = 16;   // 16-feature blocks of E^T per workgroup
 constexpr int kScTB = 16;   // 16-row blocks of canvas rows per workgroup
-constexpr int kScASlots = 3, kScPSlots = 2, kScLSlots = 2;
+constexpr int kScASlots = 3, kScPSlots = 2, kScLSlots = 3;
 constexpr int kScABytes = kScRB * 1024;         // one 32-wide k step of E^T tiles
 constexpr int kScPBytes = kScTB * 2 * 1024;     // one k step of p tiles, hi and lo
 constexpr int kScLBytes = kScTB * 1024;         // one k step of logits chunks (16 rows x 64 B each)
 constexpr int kScLds = kScASlots * kScABytes + kScPSlots * kScPBytes + kScLSlots * kScLBytes;
-constexpr int kScACopies = kScRB / 4;           // E^T tiles each wave copies per step
-constexpr int kScPBlocks = kScTB / 4;           // p row blocks each wave computes per step
+constexpr int kScWaves = 4;
+constexpr int kScACopies = kScRB / kScWaves;    // E^T tiles each wave copies per step
+constexpr int kScPBlocks = kScTB / kScWaves;    // p row blocks each wave computes per step
 
 struct ScArgs {
   const uint16_t* logits;   // bf16 [M][K] row-major
@@ -104,7 +105,7 @@ struct ScArgs {
 
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
+__global__ __launch_bounds__(64 * kScWaves) void sc_embed_gemm(ScArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char ring[];   // [A slots][P slots][L slots]
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
   char* const aring = ring;
   char* const pring = ring + kScASlots * kScABytes;
   char* const lring = pring + kScPSlots * kScPBytes;
-  // E^T copy duty: blocks wv * 4 .. + 3 of the step (past the matrix: the last block,
-  // whose outputs are dropped)
+  // E^T copy duty: kScACopies blocks from wv * kScACopies of the step (past the matrix:
+  // the last block, whose outputs are dropped)
   const uint16_t* asrc[kScACopies];
 #pragma unroll
   for (int u = 0; u < kScACopies; ++u)
@@ -135,9 +136,10 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
 #pragma unroll
     for (int u = 0; u < kScACopies; ++u) tile_to_lds_untracked(asrc[u] + step * 512, dst + u * 1024);
   };
-  // p duty: row blocks wv * 4 .. + 3 of the tile, lane row r, k 8g .. 8g + 7 of each
-  // step (rows past M read the last row; their outputs are dropped).  The lane copies
-  // its 16 logits bytes of each block into the L slot and reads back the same bytes.
+  // p duty: kScPBlocks row blocks from wv * kScPBlocks of the tile, lane row r, k 8g ..
+  // 8g + 7 of each step (rows past M read the last row; their outputs are dropped).  The
+  // lane copies its 16 logits bytes of each block into the L slot and reads back the
+  // same bytes.
   const uint16_t* lsrc[kScPBlocks];
   float mL[kScPBlocks];
 #pragma unroll
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
     }
   };
 
-  constexpr int FI = kScRB / 2, FJ = kScTB / 2;
+  constexpr int FI = kScRB / 2, FJ = kScTB / 2;   // a 2 x 2 grid of 128 x 128 wave tiles
   const int wr = wv & 1, wt = wv >> 1;
   f32x4 acc[FI][FJ];
 #pragma unroll
@@ -180,16 +182,19 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Copy order per wave: A(0), L(0), A(1); then in step s: L(s + 1), A(s + 2).  Before
-  // p(s + 1) is made, vmcnt <= kScACopies leaves only A(s + 2) in flight, so L(s + 1) and
-  // every earlier copy (A(s + 1)) have landed; the barrier at the top of step s + 1 then
-  // publishes A(s + 1) and p(s + 1) of all waves and retires every read of the slots
-  // that step refills (A: step s - 1's; L and p: step s - 1's, read at its end).
-  issue_a(0);
+  // Copy order per wave: L(0), A(0), L(1), A(1); then at the top of step s: L(s + 2),
+  // A(s + 2) -- both two steps ahead.  Before p(s + 1) is made, vmcnt <= kScStepCopies
+  // leaves only step s's copies in flight, so L(s + 1) and A(s + 1) (issued at the top of
+  // step s - 1) have landed; the barrier at the top of step s + 1 then publishes A(s + 1)
+  // and p(s + 1) of all waves and retires every read of the slots step s + 1 refills
+  // (A and p: read by step s's MFMAs; L: read when p(s) was made).
+  constexpr int kScStepCopies = kScACopies + kScPBlocks;
   issue_l(0);
+  issue_a(0);
   if (nk > 1) {
+    issue_l(1);
     issue_a(1);
-    vm_wait<kScACopies>();
+    vm_wait<kScStepCopies>();
   } else {
     vm_wait<0>();
   }
@@ -199,8 +204,10 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
   u32x4 A[FI], Bh[2], Bl[2];
   for (int s = 0; s < nk; ++s) {
     lds_sync();
-    if (s + 1 < nk) issue_l(s + 1);
-    if (s + 2 < nk) issue_a(s + 2);
+    if (s + 2 < nk) {
+      issue_l(s + 2);
+      issue_a(s + 2);
+    }
     const lds_char* sa = la + (s % kScASlots) * kScABytes + lane * 16;
     const lds_char* sp = lp + (s % kScPSlots) * kScPBytes + lane * 16;
 #pragma unroll
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void sc_embed_gemm(ScArgs a) {
       for (int i = 0; i < FI; ++i) acc[i][j] = mfma16x2(A[i], Bh[j & 1], A[i], Bl[j & 1], acc[i][j]);
     }
     if (s + 1 < nk) {
-      if (s + 2 < nk) vm_wait<kScACopies>();
+      if (s + 2 < nk) vm_wait<kScStepCopies>();
       else vm_wait<0>();
       make_p(s + 1);
     }
@@ -308,7 +315,7 @@ void launch_sc_embed(const uint16_t* logits, const float2* stats, const uint16_t
   a.kslice = sc_kslice(K, a.nsplit);
   const int total = a.n_row_tiles * a.n_tok_tiles * a.nsplit;
   const int blocks = kXcd * ((total + kXcd - 1) / kXcd);
-  launch_kernel(sc_embed_gemm, dim3(blocks), dim3(256), (size_t)kScLds, s, nullptr, a);
+  launch_kernel(sc_embed_gemm, dim3(blocks), dim3(64 * kScWaves), (size_t)kScLds, s, nullptr, a);
 }
 
 void launch_sc_reduce(const float* part, int nsplit, const float2* stats, int M, int N, uint16_t* u_fm,
