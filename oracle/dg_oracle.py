@@ -39,6 +39,9 @@ in the design notes of the repository):
     when commit_all (the last step of a block).
   * Self-conditioning: z = SwiGLU(softmax(L) E) from a step's logits, added to the
     canvas rows' input at the next step (0 at the first).
+  * Mixed batches: each sequence runs its own pass (denoising, or the causal KV update
+    of a finished canvas) in one batch; serving cycles each sequence through N steps and
+    an append.
   * Uniform ("multinomial") variant: the canvas starts as uniformly random tokens;
     every position is a candidate at every step; accepted positions take their
     argmax and the rest are re-noised uniformly (Philox4x64-10 tokens).
@@ -625,6 +628,87 @@ def generate_block_annealed(cfg, weights: dict, kv: KVCache, batch: int, max_ste
     if append:
         prefill_kv(cfg, weights, kv, canvas, rnd)
     return canvas, done_at
+
+
+# --------------------------------------------------------------------------------------
+# Mixed batches and continuous batching
+# --------------------------------------------------------------------------------------
+#
+# DiffusionGemma Technical Report §6 (eliminating CPU-GPU synchronisation; multi-user
+# throughput): a served batch holds two kinds of forward pass -- denoising steps, and KV
+# cache updates (the causal encoding of a finished canvas) -- that need different attention
+# masks and may share one batch; a per-sequence causal-attention flag selects the mask.
+# Rows of different sequences never interact, so the plain definition of a mixed batch is
+# every sequence's own pass.  Readings for the serving loop: each sequence cycles through
+# N denoising steps of an all-[MASK] canvas (t_s = 1 - s/N, the entropy-bounded sampler,
+# the last step commits every remaining position) and one pass that appends the finished
+# canvas, after which its canvas starts again all-[MASK]; a sequence's phase is the step it
+# is at (N: the append); the schedule is fixed, so nothing needs the device's state.
+
+
+def _kv_one(kv: KVCache, b: int) -> KVCache:
+    one = KVCache.__new__(KVCache)
+    one.cfg, one.batch = kv.cfg, 1
+    one.k = [[kv.k[l][b]] for l in range(len(kv.k))]
+    one.v = [[kv.v[l][b]] for l in range(len(kv.v))]
+    one.len = [kv.len[b]]
+    return one
+
+
+def _kv_put(kv: KVCache, b: int, one: KVCache) -> None:
+    for l in range(len(kv.k)):
+        kv.k[l][b] = one.k[l][0]
+        kv.v[l][b] = one.v[l][0]
+    kv.len[b] = one.len[0]
+
+
+def mixed_step(cfg, weights: dict, kv: KVCache, tokens: np.ndarray, encode, t, rnd: bool = True) -> np.ndarray:
+    """One batch of both kinds of pass: sequence b with encode[b] runs the causal encoder over
+    its C tokens and appends their K/V (prefill_kv); every other one runs the denoising pass
+    over its canvas at its own time t[b] (denoise_step).  Returns logits [B][C][V] (NaN on
+    the rows of encoding sequences)."""
+    tokens = np.asarray(tokens)
+    B, C = tokens.shape
+    logits = np.full((B, C, cfg.vocab), np.nan)
+    for b in range(B):
+        one = _kv_one(kv, b)
+        if encode[b]:
+            prefill_kv(cfg, weights, one, tokens[b:b + 1], rnd)
+        else:
+            logits[b] = denoise_step(cfg, weights, one, tokens[b:b + 1], float(t[b]), rnd)[0]
+        _kv_put(kv, b, one)
+    return logits
+
+
+def serve(cfg, weights: dict, kv: KVCache, batch: int, steps: int, gamma: float, n_passes: int, phase,
+          rnd: bool = True):
+    """Continuous batching of block generation: n_passes mixed passes, sequence b starting at
+    phase[b] in [0, steps) with an all-[MASK] canvas (a later start shortens only its first
+    canvas, which still ends with the commit-all step).  Each pass runs every sequence's
+    current phase in one mixed_step (denoising at t = 1 - phase/steps, or the append at
+    phase = steps), then the sampler on each denoising sequence (sample_eb; commit_all at
+    phase steps - 1); an appended canvas is recorded and restarts all-[MASK].  Returns
+    (canvas [B][C], finished: per sequence the list of appended canvases, phase [B])."""
+    C, V = cfg.canvas, cfg.vocab
+    phase = np.array(phase, dtype=np.int64).copy()
+    assert ((phase >= 0) & (phase < steps)).all(), "a sequence starts at a denoising step"
+    canvas = np.full((batch, C), cfg.mask_id, dtype=np.int64)
+    finished = [[] for _ in range(batch)]
+    for _ in range(n_passes):
+        enc = phase == steps
+        t = np.where(enc, 0.0, 1.0 - phase / steps)
+        logits = mixed_step(cfg, weights, kv, canvas, enc, t, rnd)
+        stored = bf16(logits) if rnd else logits
+        for b in range(batch):
+            if enc[b]:
+                finished[b].append(canvas[b].copy())
+                canvas[b] = cfg.mask_id
+            else:
+                new, *_ = sample_eb(stored[b:b + 1], canvas[b:b + 1], gamma, bool(phase[b] == steps - 1),
+                                    cfg.mask_id)
+                canvas[b] = new[0]
+        phase = (phase + 1) % (steps + 1)
+    return canvas, finished, phase
 
 
 # --------------------------------------------------------------------------------------
