@@ -628,6 +628,61 @@ def long_context_line(packed, args):
             "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]}}
 
 
+CONC_BATCHES = (1, 2, 4, 8, 16)
+CONC_BLOCKS = 2
+
+
+def concurrency_line(packed, args):
+    """Multi-user throughput against the number of concurrent sequences (Technical Report
+    §6, multi-user throughput): the 30-layer model, each sequence with its own 1024-token
+    random prompt, whole blocks of 12 steps + the KV append.  Two schedules per batch size:
+    lockstep (every sequence in the same step; the append is a pass of its own) and
+    staggered continuous batching (dg_serve: sequences spread over the 13 phases, every
+    pass mixing denoising sequences with one or more sequences appending their finished
+    canvas, with the per-sequence causal flag).  tok/s = committed canvas tokens / wall."""
+    import torch
+    from discrete_diffusion_block_amd import dg, synth
+    cfg = synth.CONFIGS["full"]
+    C, V, P, N = cfg.canvas, cfg.vocab, args.prompt, args.denoise_steps
+    Bmax = max(CONC_BATCHES)
+    max_ctx = int(math.ceil((P + C * (2 * CONC_BLOCKS + 4)) / 64.0) * 64)
+    eng = dg.Engine(cfg, packed, max_batch=Bmax, max_ctx=max_ctx, packed=True)
+    logits = torch.empty(Bmax, C, V, dtype=torch.bfloat16, device="cuda")
+    nm = torch.empty(Bmax, dtype=torch.int32, device="cuda")
+    rows = []
+    for B in CONC_BATCHES:
+        eng.reset()
+        eng.prefill_kv(synth.make_prompt(cfg, B, P, device="cuda"))
+        canvas = torch.empty(B, C, dtype=torch.int32, device="cuda")
+        lg, n = logits[:B], nm[:B]
+        eng.generate_block(canvas, N, args.gamma, True, lg, n)          # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(CONC_BLOCKS):
+            eng.generate_block(canvas, N, args.gamma, True, lg, n)
+        torch.cuda.synchronize()
+        lock = B * C * CONC_BLOCKS / (time.perf_counter() - t0)
+        eng.reset()
+        eng.prefill_kv(synth.make_prompt(cfg, B, P, device="cuda"))
+        canvas.fill_(V)
+        phase = [(b * N) // B for b in range(B)]
+        dg.dg_serve(eng.ctx, eng.kv, canvas, N, args.gamma, N + 1, phase, lg, n, eng.ws)   # warm-up cycle
+        count = [0] * B
+        out = torch.empty(B, 1, C, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dg.dg_serve(eng.ctx, eng.kv, canvas, N, args.gamma, CONC_BLOCKS * (N + 1), phase, lg, n, eng.ws, out, count)
+        torch.cuda.synchronize()
+        stag = sum(count) * C / (time.perf_counter() - t0)
+        rows.append({"batch": B, "lockstep_tok_s": round(lock, 1), "staggered_tok_s": round(stag, 1)})
+        log(f"concurrency {B}: lockstep {lock:.0f}, staggered {stag:.0f} tok/s")
+    eng.close()
+    return {"workload": f"multi-user throughput of the 30-layer model: batch B of independent sequences, "
+                        f"{P}-token prompts, {N} steps + append per {C}-token block, gamma {args.gamma}; lockstep "
+                        f"blocks vs staggered continuous batching with mixed denoise/append passes",
+            "unit": "tok/s", "blocks_per_sequence": CONC_BLOCKS, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -804,6 +859,7 @@ def main():
         "long_context_batch8": None,
         "uniform_variant": None,
         "self_conditioning": None,
+        "concurrency": None,
         "cpu_baseline": None,
     }
     if not args.no_extras:
@@ -824,6 +880,12 @@ def main():
             out["long_context_batch8"] = long_context_line(packed, args)
         except Exception as exc:  # report, but never lose the headline
             out["long_context_batch8"] = {"error": repr(exc)}
+        torch.cuda.empty_cache()
+        log("concurrency sweep...")
+        try:
+            out["concurrency"] = concurrency_line(packed, args)
+        except Exception as exc:  # report, but never lose the headline
+            out["concurrency"] = {"error": repr(exc)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)...")
         try:

@@ -247,7 +247,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws, bool self_cond) 
   ws->att_po = cv.take<float>((size_t)kAttnMaxSplitRows * qd);
   ws->att_pml = cv.take<float2>((size_t)kAttnMaxSplitRows * c.n_q_heads);
   ws->rope = cv.take<float2>(M * (c.head_dim / 2));
-  ws->temb = cv.take<float>(c.d_model);
+  ws->temb = cv.take<float>((size_t)batch * c.d_model);
   ws->r = cv.take<float>(M * c.n_experts);
   ws->ids = cv.take<int32_t>(M * c.top_k);
   ws->wts = cv.take<float>(M * c.top_k);
@@ -329,7 +329,7 @@ KvLayer kv_layer(const dg_ctx* ctx, const dg_kv* kv, int l) {
 // [MASK] -- the only rows the sampler reads -- and leaves the other logits rows as
 // they were.
 dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const int32_t* tokens,
-                   float t, uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false,
+                   uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false,
                    const float* z = nullptr) {
   const dg_config& c = ctx->cfg;
   const int M = g.batch * g.n;
@@ -337,10 +337,10 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
   const float eps = c.rms_eps;
   const int nl = c.n_layers;
   SideFork sf(ctx);
-  DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, t, g.denoise ? ws.temb : nullptr,
+  DG_TIMED(ctx, DG_K_PREP, launch_prep(g, hd, c.rope_theta, ws.rope, d, g.denoise ? ws.temb : nullptr,
                                        ws.counters, kPassCounters, s));
   DG_TIMED(ctx, DG_K_EMBED,
-           launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, g.denoise ? z : nullptr,
+           launch_embed_norm(tokens, ctx->embed, g.denoise ? ws.temb : nullptr, g.denoise ? z : nullptr, g.n, g.enc,
                              ctx->layers[0].attn_norm, eps, ws.x, ws.h, M, d, c.vocab, s));
   for (int l = 0; l < nl; ++l) {
     const dg_layer_weights& L = ctx->layers[l];
@@ -387,12 +387,15 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
                              c.expert_ffn, d, ws.Y, s));
     if (fork) (void)hipStreamWaitEvent(s, sf.join, 0);
     const float* next_gain = (l + 1 < nl) ? ctx->layers[l + 1].attn_norm : (g.denoise ? ctx->final_norm : nullptr);
-    const bool compact = masked_head && g.denoise && l == nl - 1;
+    // the head's rows: those of the denoising sequences (all of them, or only their
+    // [MASK] rows), compacted when that is not every row
+    const bool compact = (masked_head || g.enc != 0) && g.denoise && l == nl - 1;
     DG_TIMED(ctx, DG_K_COMBINE,
              launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h,
-                            compact ? tokens : nullptr, c.vocab, compact ? ws.rows : nullptr, ws.counters, s));
+                            compact && masked_head ? tokens : nullptr, c.vocab, g.enc, g.n,
+                            compact ? ws.rows : nullptr, ws.counters, s));
   }
-  const bool compact = masked_head && g.denoise;
+  const bool compact = (masked_head || g.enc != 0) && g.denoise;
   if (g.denoise)
     DG_TIMED(ctx, DG_K_HEAD, launch_gemm_head(ws.h, ctx->embed, logits, M, c.vocab, d,
                                               compact ? ws.counters : nullptr, compact ? ws.rows : nullptr, s));
@@ -423,13 +426,15 @@ dg_status denoise_impl(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canvas, in
   g.batch = batch;
   g.n = ctx->cfg.canvas;
   g.denoise = 1;
+  g.enc = 0;
   for (int b = 0; b < batch; ++b) {
     if (kv->len[b] + ctx->cfg.canvas > ctx->cfg.max_ctx)
       return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + canvas %d exceeds max_ctx %d", b,
                   (long long)kv->len[b], ctx->cfg.canvas, ctx->cfg.max_ctx);
     g.len[b] = (int)kv->len[b];
+    g.t[b] = t;
   }
-  return run_pass(ctx, kv, g, d_canvas, t, d_logits, ws, s, masked_head, z);
+  return run_pass(ctx, kv, g, d_canvas, d_logits, ws, s, masked_head, z);
 }
 
 // Self-conditioning signal z (and u = p̂₀ E in fp32 when u_out is given) of the
@@ -461,9 +466,10 @@ dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batc
       g.batch = batch;
       g.n = std::min(chunk, n - s0);
       g.denoise = 0;
+      g.enc = all_sequences(batch);
       for (int b = 0; b < batch; ++b) g.len[b] = (int)kv->len[b] + s0;
       // a chunk's tokens are a strided slice when batch > 1; only batch == 1 can chunk in place
-      dg_status st = run_pass(ctx, kv, g, d_tokens + s0, 0.f, nullptr, ws, s);
+      dg_status st = run_pass(ctx, kv, g, d_tokens + s0, nullptr, ws, s);
       if (st != DG_OK) return st;
     }
   } else {
@@ -474,13 +480,14 @@ dg_status prefill_impl(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batc
         g.batch = 1;
         g.n = std::min(chunk, n - s0);
         g.denoise = 0;
+        g.enc = 1;
         g.len[0] = (int)kv->len[b] + s0;
         dg_kv one = *kv;
         const size_t seq_k = (size_t)ctx->cfg.n_kv_heads * ctx->cfg.max_ctx * ctx->cfg.head_dim;
         // view of sequence b: offset the cache base by b sequences within each layer
         one.k = kv->k + (size_t)b * seq_k;
         one.v = kv->v + (size_t)b * seq_k;
-        dg_status st = run_pass(ctx, &one, g, d_tokens + (size_t)b * n + s0, 0.f, nullptr, ws, s);
+        dg_status st = run_pass(ctx, &one, g, d_tokens + (size_t)b * n + s0, nullptr, ws, s);
         if (st != DG_OK) return st;
       }
     }
@@ -504,8 +511,11 @@ struct SampleOpts {
   int draw = 0;
 };
 
+// commit: bit b set = sequence b commits every candidate row (the last step of its block)
+uint64_t commit_mask(bool all) { return all ? ~0ull : 0ull; }
+
 dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
-                      float gamma, int commit_all, float* d_entropy, int32_t* d_argmax,
+                      float gamma, uint64_t commit, float* d_entropy, int32_t* d_argmax,
                       int32_t* d_n_masked, const Ws& ws, hipStream_t s, const dg_ctx* ctx = nullptr,
                       const SampleOpts& o = SampleOpts{}) {
   DG_TIMED(ctx, DG_K_SAMPLE_PASS1,
@@ -513,7 +523,7 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
                                   o.uniform ? o.done_step : nullptr, ws.part, ws.part_arg, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT,
            launch_eb_select(ws.part, ws.part_arg, sample_chunks(vocab), nullptr, nullptr, d_canvas, batch,
-                            canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax,
+                            canvas, vocab, gamma, commit, d_entropy, d_argmax, d_n_masked, o.prev_amax,
                             o.e_stop, o.step, o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin,
                             ws.skstar, o.uniform, o.seed, o.draw, s));
   // sequences whose decision the fast entropies could not certify: canonical entropy
@@ -523,7 +533,7 @@ dg_status sample_impl(const uint16_t* d_logits, int32_t* d_canvas, int batch, in
                                  ws.sflag, ws.shf, ws.swin, ws.cpart, s));
   DG_TIMED(ctx, DG_K_SAMPLE_SELECT_CANON,
            launch_eb_select_canon(ws.cpart, sample_chunks(vocab), d_canvas, batch, canvas, vocab, gamma,
-                                  commit_all, d_entropy, d_argmax, d_n_masked, o.prev_amax, o.e_stop, o.step,
+                                  commit, d_entropy, d_argmax, d_n_masked, o.prev_amax, o.e_stop, o.step,
                                   o.done_step, ws.sflag, ws.smoved, ws.samax, ws.shf, ws.swin, ws.skstar,
                                   o.uniform, o.seed, o.draw, s));
   return check_launch("sampler");
@@ -576,7 +586,7 @@ dg_status sample_checked(const uint16_t* d_logits, int32_t* d_canvas, int batch,
   Carver cv{base};
   Ws ws;
   carve_sampler(cv, batch, canvas, vocab, &ws);
-  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax, d_n, ws,
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_mask(commit_all), d_entropy, d_argmax, d_n, ws,
                      (hipStream_t)stream, nullptr, o);
 }
 
@@ -634,7 +644,7 @@ dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
       st = self_cond_impl(ctx, d_logits, batch, ws.sc_z, nullptr, ws, s);
       if (st != DG_OK) return st;
     }
-    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == max_steps - 1, nullptr,
+    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, commit_mask(step == max_steps - 1), nullptr,
                      nullptr, d_n, ws, s, ctx, o);
     if (st != DG_OK) return st;
   }
@@ -821,7 +831,7 @@ dg_status dg_sample_eb(const uint16_t* d_logits, int32_t* d_canvas, int batch, i
   Carver cv{base};
   Ws ws;
   carve_sampler(cv, batch, canvas, vocab, &ws);
-  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, d_entropy, d_argmax,
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_mask(commit_all), d_entropy, d_argmax,
                      d_n_masked, ws, (hipStream_t)stream);
 }
 
@@ -870,7 +880,7 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     const float t = 1.0f - (float)step / (float)steps;
     st = denoise_impl(ctx, kv, d_canvas, batch, t, d_logits, ws, s, /*masked_head=*/true);
     if (st != DG_OK) return st;
-    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, step == steps - 1, nullptr,
+    st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, commit_mask(step == steps - 1), nullptr,
                      nullptr, d_n_masked, ws, s, ctx);
     if (st != DG_OK) return st;
   }
@@ -892,6 +902,126 @@ dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, i
                                     void* d_ws, size_t ws_bytes, void* stream) {
   return generate_annealed(ctx, kv, d_canvas, batch, max_steps, gamma, tau_max, tau_min, e_stop, 1, seed,
                            append_kv, d_logits, d_n_open, d_done_step, d_ws, ws_bytes, stream);
+}
+
+dg_status dg_mixed_step(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batch, const int32_t* h_encode,
+                        const float* h_t, uint16_t* d_logits, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_tokens || !h_encode) return fail(DG_ERR_INVALID_ARG, "tokens or encode flags are NULL");
+  const dg_config& c = ctx->cfg;
+  PassGeom g{};
+  g.batch = batch;
+  g.n = c.canvas;
+  for (int b = 0; b < batch; ++b) {
+    if (kv->len[b] + c.canvas > c.max_ctx)
+      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + canvas %d exceeds max_ctx %d", b,
+                  (long long)kv->len[b], c.canvas, c.max_ctx);
+    g.len[b] = (int)kv->len[b];
+    if (h_encode[b]) {
+      g.enc |= 1ull << b;
+    } else {
+      if (!h_t || !d_logits) return fail(DG_ERR_INVALID_ARG, "a denoising sequence needs t and logits");
+      if (!(h_t[b] >= 0.f && h_t[b] <= 1.f)) return fail(DG_ERR_INVALID_ARG, "t[%d] must be in [0, 1]", b);
+      g.t[b] = h_t[b];
+      g.denoise = 1;
+    }
+  }
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  st = run_pass(ctx, kv, g, d_tokens, d_logits, ws, (hipStream_t)stream);
+  if (st != DG_OK) return st;
+  for (int b = 0; b < batch; ++b)
+    if (h_encode[b]) kv->len[b] += c.canvas;
+  return DG_OK;
+}
+
+dg_status dg_sample_eb_seq(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                           float gamma, const int32_t* h_commit_all, float* d_entropy, int32_t* d_argmax,
+                           int32_t* d_n_masked, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!h_commit_all) return fail(DG_ERR_INVALID_ARG, "commit flags are NULL");
+  if (batch < 1 || batch > DG_MAX_BATCH) return fail(DG_ERR_INVALID_ARG, "batch must be in [1, %d]", DG_MAX_BATCH);
+  size_t need = 0;
+  dg_status st = dg_sample_workspace_size(batch, canvas, vocab, &need);
+  if (st != DG_OK) return st;
+  if (!d_logits || !d_canvas || !d_n_masked || !d_ws) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  if (ws_bytes < need) return fail(DG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  uint64_t commit = 0;
+  for (int b = 0; b < batch; ++b)
+    if (h_commit_all[b]) commit |= 1ull << b;
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d_ws) + kAlign - 1) / kAlign * kAlign);
+  Carver cv{base};
+  Ws ws;
+  carve_sampler(cv, batch, canvas, vocab, &ws);
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit, d_entropy, d_argmax, d_n_masked, ws,
+                     (hipStream_t)stream);
+}
+
+dg_status dg_serve(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps, float gamma, int n_passes,
+                   int32_t* h_phase, uint16_t* d_logits, int32_t* d_n_masked, int32_t* d_out, int out_blocks,
+                   int32_t* h_out_count, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_canvas || !d_logits || !d_n_masked || !h_phase) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (steps < 1 || n_passes < 0) return fail(DG_ERR_INVALID_ARG, "steps must be >= 1 and n_passes >= 0");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  if (d_out && (out_blocks < 1 || !h_out_count))
+    return fail(DG_ERR_INVALID_ARG, "an output ring needs out_blocks >= 1 and the block counts");
+  const dg_config& c = ctx->cfg;
+  for (int b = 0; b < batch; ++b) {
+    if (h_phase[b] < 0 || h_phase[b] > steps) return fail(DG_ERR_INVALID_ARG, "phase[%d] outside [0, steps]", b);
+    if (d_out && h_out_count[b] < 0) return fail(DG_ERR_INVALID_ARG, "out_count[%d] < 0", b);
+    // the appends this call makes, plus one canvas of denoising scratch after the last
+    const int64_t first = (steps - h_phase[b] + (steps + 1)) % (steps + 1);   // passes to its next append
+    const int64_t appends = n_passes > first ? 1 + (n_passes - 1 - first) / (steps + 1) : 0;
+    if (kv->len[b] + (appends + 1) * c.canvas > c.max_ctx)
+      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + %lld appended canvases exceeds max_ctx %d", b,
+                  (long long)kv->len[b], (long long)appends, c.max_ctx);
+  }
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  for (int p = 0; p < n_passes; ++p) {
+    PassGeom g{};
+    g.batch = batch;
+    g.n = c.canvas;
+    uint64_t commit = 0;
+    SeqOffsets off{};
+    for (int b = 0; b < batch; ++b) {
+      g.len[b] = (int)kv->len[b];
+      if (h_phase[b] == steps) {
+        g.enc |= 1ull << b;
+        if (d_out) off.v[b] = ((int64_t)b * out_blocks + h_out_count[b] % out_blocks) * c.canvas;
+      } else {
+        g.t[b] = 1.0f - (float)h_phase[b] / (float)steps;
+        g.denoise = 1;
+        if (h_phase[b] == steps - 1) commit |= 1ull << b;
+      }
+    }
+    st = run_pass(ctx, kv, g, d_canvas, d_logits, ws, s, /*masked_head=*/true);
+    if (st != DG_OK) return st;
+    if (g.denoise) {
+      // the appending sequences' canvases hold no [MASK] row: the sampler leaves them alone
+      st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, commit, nullptr, nullptr, d_n_masked, ws,
+                       s, ctx);
+      if (st != DG_OK) return st;
+    }
+    if (g.enc) {
+      DG_TIMED(ctx, DG_K_FILL, launch_serve_finish(d_canvas, batch, c.canvas, c.vocab, g.enc, d_out, off, s));
+      for (int b = 0; b < batch; ++b)
+        if ((g.enc >> b) & 1) {
+          kv->len[b] += c.canvas;
+          if (d_out) ++h_out_count[b];
+        }
+    }
+    for (int b = 0; b < batch; ++b) h_phase[b] = (h_phase[b] + 1) % (steps + 1);
+  }
+  return check_launch("serve");
 }
 
 dg_status dg_generate_block_sc(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
@@ -1007,7 +1137,7 @@ dg_status dg_test_sample_eb_profiled(dg_ctx* ctx, const uint16_t* d_logits, int3
   Carver cv{base};
   Ws ws;
   carve_sampler(cv, batch, canvas, vocab, &ws);
-  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_all, nullptr, nullptr, d_n_masked, ws,
+  return sample_impl(d_logits, d_canvas, batch, canvas, vocab, gamma, commit_mask(commit_all), nullptr, nullptr, d_n_masked, ws,
                      (hipStream_t)stream, ctx);
 }
 
@@ -1053,7 +1183,7 @@ dg_status dg_test_eb_select(const float* d_entropy, const int32_t* d_argmax, int
       vocab < 1 || gamma != gamma)
     return fail(DG_ERR_INVALID_ARG, "bad selection arguments");
   launch_eb_select(nullptr, nullptr, 0, d_entropy, d_argmax, d_canvas, batch, canvas, vocab, gamma,
-                   commit_all, nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, nullptr, nullptr,
+                   commit_mask(commit_all), nullptr, nullptr, d_n_masked, nullptr, -1.0f, 0, nullptr, nullptr, nullptr,
                    nullptr, nullptr, nullptr, nullptr, 0, 0, 0, (hipStream_t)stream);
   return check_launch("eb select");
 }

@@ -16,9 +16,14 @@ namespace dg {
 struct PassGeom {
   int batch;
   int n;
-  int denoise;               // 1: bidirectional canvas over the cached prefix; 0: causal encoder
+  int denoise;               // 1: some sequence denoises its canvas (the pass ends in the head)
+  uint64_t enc;              // bit b: sequence b runs the causal encoder (prefill / KV update);
+                             // the others the bidirectional denoiser over the cached prefix
   int len[DG_MAX_BATCH];
+  float t[DG_MAX_BATCH];     // denoising time of each denoising sequence
 };
+__host__ __device__ inline bool seq_encodes(const PassGeom& g, int b) { return (g.enc >> b) & 1; }
+inline uint64_t all_sequences(int batch) { return batch >= 64 ? ~0ull : ((1ull << batch) - 1); }
 
 // KV-cache view of one layer.
 struct KvLayer {
@@ -71,21 +76,26 @@ inline void raise_lds_limit(LdsLimit& st, const void* fn, int bytes) {
 
 // ---- embed / norm / prep ----
 // also clears zero[0 .. nzero)
-void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
+void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d,
                  float* temb, int32_t* zero, int nzero, hipStream_t s);
-// z (optional): the self-conditioning signal, fp32 row-major [M][d], added with temb
+// temb (optional): [batch][d], sequence b's timestep embedding, added to the rows of the
+// sequences whose bit in enc is clear (rows m = b * n + i); z (optional): the
+// self-conditioning signal, fp32 row-major [M][d], added to the same rows
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb, const float* z,
-                       const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
-                       hipStream_t s);
+                       int n, uint64_t enc, const float* gain, float eps, float* x, uint16_t* h, int M, int d,
+                       int vocab, hipStream_t s);
 // h: fragment-major; h_rm (optional): the same values row-major [M][d]
 void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, uint16_t* h_rm, int M,
                     int d, hipStream_t s, hipEvent_t done = nullptr);
 // rows_out given: only the [MASK] rows of canvas (mask id mask_id) are normed,
 // compacted into h (the order of arrival); rows_out lists their row indices and
 // *count (zero on entry) their number
+// rows_out given: only the rows of sequences whose bit in skip is clear (rows m = b * n +
+// i), and of those only the [MASK] rows when canvas is given, are normed, compacted
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
-                    const int32_t* canvas, int mask_id, int32_t* rows_out, int32_t* count, hipStream_t s);
+                    const int32_t* canvas, int mask_id, uint64_t skip, int n, int32_t* rows_out, int32_t* count,
+                    hipStream_t s);
 
 // ---- dense GEMMs ----
 // y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).
@@ -165,10 +175,11 @@ void launch_uniform_canvas(int32_t* canvas, int batch, int C, int vocab, uint64_
 // passes below); decided sequences get flag[b] = 0.  uniform: every row of a sequence
 // whose done_step is 0 is a candidate, and the decided sequences' rows outside the
 // accepted set take the uniformly random tokens of (seed, draw); done_step is set when
-// the stop fires or commit_all.
+// the stop fires or its commit bit is set.  commit: bit b set = sequence b commits every
+// candidate row (the last step of a block).
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
-                      float gamma, int commit_all, float* H_out, int32_t* amax_out,
+                      float gamma, uint64_t commit, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                       int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
                       int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s);
@@ -181,7 +192,7 @@ void launch_canon_partials(const uint16_t* logits, const int32_t* canvas, int ba
                            const float2* win, ulonglong2* cpart, hipStream_t s);
 // Pass 4: the decision of the flagged sequences on the canonical entropy.
 void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
-                            float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
+                            float gamma, uint64_t commit, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                             int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
                             int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s);
@@ -200,6 +211,14 @@ void launch_sc_embed(const uint16_t* logits, const float2* stats, const uint16_t
 void launch_sc_reduce(const float* part, int nsplit, const float2* stats, int M, int N, uint16_t* u_fm,
                       float* u_out, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
+// A per-sequence element offset, passed by value.
+struct SeqOffsets {
+  int64_t v[DG_MAX_BATCH];
+};
+// For each sequence with its bit in enc set: copy its canvas row to out + off.v[b] (out
+// may be NULL) and refill the row with mask_id.
+void launch_serve_finish(int32_t* canvas, int batch, int C, int32_t mask_id, uint64_t enc, int32_t* out,
+                         const SeqOffsets& off, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 }  // namespace dg

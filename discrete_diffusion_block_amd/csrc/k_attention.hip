@@ -81,6 +81,7 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
   const int pair = unit / (a.nsplit * a.wg_per_pair);
   const int b = pair / kv.hkv, kvh = pair - b * kv.hkv;
   const int n = g.n, len = g.len[b];
+  const bool den = !seq_encodes(g, b);        // this sequence denoises (else: causal encoder)
   const int ngroups = a.grp * a.qt32;
   const int rg0 = wgp * NWV;
   const int rg = rg0 + w;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
 
   // key range of the workgroup (the union over its waves' queries), in 64-key stages
   int lo_t, hi_t;
-  if (g.denoise) {
+  if (den) {
     lo_t = kv.window > 0 ? max(0, len - kv.window) : 0;
     hi_t = len + n;
   } else {
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
   int lo_q[2], hi_q[2];                       // visible key range of each of the lane's queries
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (g.denoise) {
+    if (den) {
       lo_q[qb] = lo_t;
       hi_q[qb] = hi_t;
     } else {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
         }
       }
     // lane holds keys kc0 + 32 ch + 8 gq + e (e = 0..7: bb = e / 4, row e % 4) for query r
-    const bool nomask = g.denoise ? (kc0 >= lo_t && kc0 + kAttnStageKeys <= hi_t)
+    const bool nomask = den ? (kc0 >= lo_t && kc0 + kAttnStageKeys <= hi_t)
                                   : (kc0 + kAttnStageKeys - 1 <= p_first &&
                                      (kv.window == 0 || p_last - kc0 < kv.window));
     u32x4 ph[2][2], pl[2][2];
@@ -344,7 +345,7 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   // CU, keep at least two 64-key stages per split, and stay within the partial buffer
   int max_keys = 0;
   for (int bb = 0; bb < g.batch; ++bb) {
-    const int keys = g.denoise ? (kv.window > 0 ? min(g.len[bb], kv.window) : g.len[bb]) + g.n
+    const int keys = !seq_encodes(g, bb) ? (kv.window > 0 ? min(g.len[bb], kv.window) : g.len[bb]) + g.n
                                : (kv.window > 0 ? min(g.len[bb] + g.n, kv.window + 63) : g.len[bb] + g.n);
     max_keys = max(max_keys, keys);
   }

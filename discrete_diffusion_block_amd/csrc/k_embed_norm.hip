@@ -12,15 +12,16 @@ namespace dg {
 
 // rope_tab[m][i] = (cos, sin)(pos(m) * theta^(-2i/hd)), computed in fp64 so that
 // positions in the tens of thousands keep full fp32 accuracy.
-// temb[j] = sin(1000 t f_j) (j < d/2), cos(1000 t f_{j-d/2}) (j >= d/2), f_j = 10000^(-j/(d/2)).
+// temb[b][j] = sin(1000 t_b f_j) (j < d/2), cos(1000 t_b f_{j-d/2}) (j >= d/2), f_j =
+// 10000^(-j/(d/2)), t_b sequence b's denoising time.
 // Workgroup 0 also clears the pass's counters zero[0 .. nzero).
-__global__ void prep_kernel(PassGeom g, int hd, float theta, float2* rope_tab, int d, float t,
+__global__ void prep_kernel(PassGeom g, int hd, float theta, float2* rope_tab, int d,
                             float* temb, int32_t* zero, int nzero) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   const int half = hd / 2;
   const int M = g.batch * g.n;
-  const long total = (long)M * half + (temb ? d : 0);
+  const long total = (long)M * half + (temb ? (long)g.batch * d : 0);
   for (long idx = blockIdx.x * (long)blockDim.x + threadIdx.x; idx < total;
        idx += (long)gridDim.x * blockDim.x) {
     if (idx < (long)M * half) {
@@ -30,20 +31,21 @@ __global__ void prep_kernel(PassGeom g, int hd, float theta, float2* rope_tab, i
       const double ang = pos * pow((double)theta, -2.0 * i / hd);
       rope_tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
     } else {
-      const int j = (int)(idx - (long)M * half);
+      const long e = idx - (long)M * half;
+      const int b = (int)(e / d), j = (int)(e - (long)b * d);
       const int hh = d / 2;
       const int jj = j < hh ? j : j - hh;
-      const double a = 1000.0 * (double)t * pow(10000.0, -(double)jj / hh);
-      temb[j] = (float)(j < hh ? sin(a) : cos(a));
+      const double a = 1000.0 * (double)g.t[b] * pow(10000.0, -(double)jj / hh);
+      temb[e] = (float)(j < hh ? sin(a) : cos(a));
     }
   }
 }
 
-void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d, float t,
+void launch_prep(const PassGeom& g, int hd, float theta, float2* rope_tab, int d,
                  float* temb, int32_t* zero, int nzero, hipStream_t s) {
-  const long total = (long)g.batch * g.n * (hd / 2) + (temb ? d : 0);
+  const long total = (long)g.batch * g.n * (hd / 2) + (temb ? (long)g.batch * d : 0);
   const int blocks = (int)std::min<long>((total + 255) / 256, 4096);
-  launch_kernel(prep_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, nullptr, g, hd, theta, rope_tab, d, t,
+  launch_kernel(prep_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, s, nullptr, g, hd, theta, rope_tab, d,
                 temb, zero, nzero);
 }
 
@@ -79,13 +81,20 @@ __device__ __forceinline__ void norm_row(const float* xr, const float* gain, flo
   }
 }
 
-// x[m] = E[token] (+ temb) (+ z[m], the self-conditioning signal), then the first RMSNorm.
+// x[m] = E[token] (+ temb of its sequence) (+ z[m], the self-conditioning signal) -- the
+// two added only on the rows of denoising sequences -- then the first RMSNorm.
 __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens, const uint16_t* embed,
-                                                         const float* temb, const float* z, const float* gain,
-                                                         float eps, float* x, uint16_t* h, int d,
-                                                         int vocab) {
+                                                         const float* temb, const float* z, int n, uint64_t enc,
+                                                         const float* gain, float eps, float* x, uint16_t* h,
+                                                         int d, int vocab) {
   __shared__ float red[16];
   const int m = blockIdx.x;
+  const int b = m / n;
+  if ((enc >> b) & 1) {                // a row of an encoding sequence: the token alone
+    temb = nullptr;
+    z = nullptr;
+  }
+  if (temb) temb += (size_t)b * d;
   // ids outside [0, V] (V = [MASK]) are clamped so a bad id can never read past the table
   const int tok = min(max(tokens[m], 0), vocab);
   float* xr = x + (size_t)m * d;
@@ -121,10 +130,10 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tokens,
 static int row_threads(int d) { return std::min(1024, std::max(64, (d / 8 + 63) / 64 * 64)); }
 
 void launch_embed_norm(const int32_t* tokens, const uint16_t* embed, const float* temb, const float* z,
-                       const float* gain, float eps, float* x, uint16_t* h, int M, int d, int vocab,
-                       hipStream_t s) {
-  launch_kernel(embed_norm_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, tokens, embed, temb, z, gain, eps, x,
-                h, d, vocab);
+                       int n, uint64_t enc, const float* gain, float eps, float* x, uint16_t* h, int M, int d,
+                       int vocab, hipStream_t s) {
+  launch_kernel(embed_norm_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, tokens, embed, temb, z, n, enc,
+                gain, eps, x, h, d, vocab);
 }
 
 __global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* x, const float* gain, float eps,
@@ -151,9 +160,10 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
 
 // x[m] += ys[m] (the shared expert), then += sum_j w[m][j] * Y[inv[m*k + j]]
 // (j ascending), then h[m] = norm(x[m]) * next_gain.  With rows_out given (the
-// last layer of a pass whose head only needs the [MASK] rows of canvas), only
-// those rows are normed, each into the next free h row i taken from *count
-// (zero on entry; it ends as the number of [MASK] rows), with rows_out[i] = m.
+// last layer of a pass whose head needs only some rows: those of the denoising
+// sequences -- skip has the bits of the others -- and, with canvas given, only their
+// [MASK] rows), only those rows are normed, each into the next free h row i taken
+// from *count (zero on entry; it ends as the number of rows kept), with rows_out[i] = m.
 // The order of the compacted rows varies from run to run; every logits row the
 // head computes from them does not depend on it.
 __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys, const float* Y,
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
                                                       const int32_t* inv, int k, int d,
                                                       const float* next_gain, float eps,
                                                       uint16_t* h, const int32_t* canvas, int mask_id,
-                                                      int32_t* rows_out, int32_t* count) {
+                                                      uint64_t skip, int n, int32_t* rows_out, int32_t* count) {
   __shared__ float red[16];
   __shared__ int out_row;
   __shared__ int slot[16];
@@ -192,7 +202,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
   }
   if (!next_gain) return;
   if (rows_out) {
-    if (canvas[m] != mask_id) return;   // uniform per workgroup
+    if ((skip >> (m / n)) & 1) return;                 // uniform per workgroup
+    if (canvas && canvas[m] != mask_id) return;
     if (threadIdx.x == 0) {
       const int i = atomicAdd(count, 1);
       rows_out[i] = m;
@@ -207,9 +218,30 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
 
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
-                    const int32_t* canvas, int mask_id, int32_t* rows_out, int32_t* count, hipStream_t s) {
+                    const int32_t* canvas, int mask_id, uint64_t skip, int n, int32_t* rows_out, int32_t* count,
+                    hipStream_t s) {
   launch_kernel(combine_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h,
-                canvas, mask_id, rows_out, count);
+                canvas, mask_id, skip, n, rows_out, count);
+}
+
+// End of a serving pass: every sequence whose bit in enc is set has just appended its
+// finished canvas; its canvas row is copied to out + off.v[b] (when out is given) and
+// refilled with [MASK] for its next block.
+__global__ void serve_finish_kernel(int32_t* canvas, int C, int32_t mask_id, uint64_t enc, int32_t* out,
+                                    SeqOffsets off) {
+  const int b = blockIdx.y;
+  if (!((enc >> b) & 1)) return;   // uniform per workgroup
+  int32_t* row = canvas + (size_t)b * C;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < C; i += gridDim.x * 256) {
+    if (out) out[off.v[b] + i] = row[i];
+    row[i] = mask_id;
+  }
+}
+
+void launch_serve_finish(int32_t* canvas, int batch, int C, int32_t mask_id, uint64_t enc, int32_t* out,
+                         const SeqOffsets& off, hipStream_t s) {
+  launch_kernel(serve_finish_kernel, dim3((C + 255) / 256, batch), dim3(256), 0, s, nullptr, canvas, C, mask_id,
+                enc, out, off);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {

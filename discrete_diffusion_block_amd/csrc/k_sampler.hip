@@ -397,7 +397,7 @@ struct SelArgs {
   int32_t* canvas;
   int C, vocab;
   float gamma;
-  int commit_all;
+  uint64_t commit;           // bit b: sequence b commits (accepts) every candidate row
   float* H_out;
   int32_t* amax_out;
   int32_t* n_masked;
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
     int ks;
     if (MODE == SEL_CANON && A.flag[b] == 2) {
       ks = A.kstar_ws[b];                     // certain; the ranking above settled the order
-    } else if (A.commit_all || stop || n == 0) {
+    } else if (((A.commit >> b) & 1) || stop || n == 0) {
       ks = n;
     } else {
       // running fp64 sum in rank order (S_k of the first k rows); k_nat = the number
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(1024) void eb_select_kernel(SelArgs A) {
     if (decided) {
       A.n_masked[b] = n - ks;
       // complete: no [MASK] left; in the uniform variant, the stop fired or the last step
-      const bool complete = A.uniform ? (n > 0 && (A.commit_all || stop)) : n - ks == 0;
+      const bool complete = A.uniform ? (n > 0 && (((A.commit >> b) & 1) || stop)) : n - ks == 0;
       if (A.done_step && complete && A.done_step[b] == 0) A.done_step[b] = A.step + 1;
     }
   }
@@ -658,7 +658,7 @@ static void run_select(const SelArgs& a, int batch, hipStream_t s) {
 
 void launch_eb_select(const float4* part, const int* part_arg, int nchunks, const float* H_in,
                       const int32_t* amax_in, int32_t* canvas, int batch, int C, int vocab,
-                      float gamma, int commit_all, float* H_out, int32_t* amax_out,
+                      float gamma, uint64_t commit, float* H_out, int32_t* amax_out,
                       int32_t* n_masked, int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                       int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
                       int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s) {
@@ -667,7 +667,7 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
   a.part = part; a.part_arg = part_arg; a.nchunks = nchunks;
   a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
   a.H_in = H_in; a.amax_in = amax_in;
-  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
+  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit = commit;
   a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
   a.prev_amax = prev_amax; a.e_stop = e_stop; a.step = step; a.done_step = done_step;
   a.flag = flag; a.moved = moved; a.amax_ws = amax_ws;
@@ -676,7 +676,7 @@ void launch_eb_select(const float4* part, const int* part_arg, int nchunks, cons
 }
 
 void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canvas, int batch, int C, int vocab,
-                            float gamma, int commit_all, float* H_out, int32_t* amax_out, int32_t* n_masked,
+                            float gamma, uint64_t commit, float* H_out, int32_t* amax_out, int32_t* n_masked,
                             int32_t* prev_amax, float e_stop, int step, int32_t* done_step,
                             int32_t* flag, int32_t* moved, int32_t* amax_ws, float* Hf_ws, float2* win,
                             int32_t* kstar_ws, int uniform, uint64_t seed, int draw, hipStream_t s) {
@@ -684,7 +684,7 @@ void launch_eb_select_canon(const ulonglong2* cpart, int nchunks, int32_t* canva
   a.uniform = uniform; a.seed = seed; a.draw = draw;
   a.cpart = cpart; a.nchunks = nchunks;
   a.Hf_ws = Hf_ws; a.win = win; a.kstar_ws = kstar_ws;
-  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit_all = commit_all;
+  a.canvas = canvas; a.C = C; a.vocab = vocab; a.gamma = gamma; a.commit = commit;
   a.H_out = H_out; a.amax_out = amax_out; a.n_masked = n_masked;
   a.prev_amax = prev_amax; a.e_stop = e_stop; a.step = step; a.done_step = done_step;
   a.flag = flag; a.moved = moved; a.amax_ws = amax_ws;

@@ -93,6 +93,9 @@ def lib():
             "dg_denoise_step_sc": [vp, C.POINTER(KV), vp, i32, f32, vp, vp, vp, sz, vp],
             "dg_generate_block_sc": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, i32, u64, i32, vp, vp,
                                      vp, vp, sz, vp],
+            "dg_mixed_step": [vp, C.POINTER(KV), vp, i32, vp, vp, vp, vp, sz, vp],
+            "dg_sample_eb_seq": [vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp],
+            "dg_serve": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp],
             "dg_packed_elems": [i32, i32, C.POINTER(sz)],
             "dg_pack_weight": [i32, vp, vp, i32, i32, i32, i32, vp],
             "dg_profile_begin": [vp, i32, C.c_uint32],
@@ -277,6 +280,43 @@ def dg_generate_block_sc(ctx, kv: KV, canvas: torch.Tensor, max_steps: int, gamm
                                       float(tau_max), float(tau_min), float(e_stop), int(bool(uniform)),
                                       int(seed) & (2 ** 64 - 1), int(bool(append_kv)), _p(logits), _p(n),
                                       _p(done_step), _p(ws), ws.numel(), _stream(stream)))
+
+
+def _i32_array(values):
+    vals = [int(v) for v in values]
+    return (C.c_int32 * len(vals))(*vals)
+
+
+def dg_mixed_step(ctx, kv: KV, tokens: torch.Tensor, encode, t, logits: Optional[torch.Tensor], ws: torch.Tensor,
+                  stream=None):
+    b = tokens.shape[0]
+    enc = _i32_array(encode)
+    tt = (C.c_float * b)(*[float(x) for x in t])
+    _check(lib().dg_mixed_step(ctx, C.byref(kv), _p(tokens), b, enc, tt, _p(logits), _p(ws), ws.numel(),
+                               _stream(stream)))
+
+
+def dg_sample_eb_seq(logits: torch.Tensor, canvas: torch.Tensor, gamma: float, commit_all, n_masked: torch.Tensor,
+                     ws: torch.Tensor, entropy: Optional[torch.Tensor] = None, argmax: Optional[torch.Tensor] = None,
+                     stream=None):
+    b, c, v = logits.shape
+    _check(lib().dg_sample_eb_seq(_p(logits), _p(canvas), b, c, v, float(gamma), _i32_array(commit_all), _p(entropy),
+                                  _p(argmax), _p(n_masked), _p(ws), ws.numel(), _stream(stream)))
+
+
+def dg_serve(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, n_passes: int, phase: list,
+             logits: torch.Tensor, n_masked: torch.Tensor, ws: torch.Tensor, out: Optional[torch.Tensor] = None,
+             out_count: Optional[list] = None, stream=None):
+    """phase (and out_count, with out [batch][out_blocks][C]) are lists updated in place."""
+    b = canvas.shape[0]
+    ph = _i32_array(phase)
+    cnt = _i32_array(out_count) if out_count is not None else None
+    _check(lib().dg_serve(ctx, C.byref(kv), _p(canvas), b, steps, float(gamma), n_passes, ph, _p(logits),
+                          _p(n_masked), _p(out), out.shape[1] if out is not None else 0, cnt, _p(ws), ws.numel(),
+                          _stream(stream)))
+    phase[:] = list(ph)
+    if out_count is not None:
+        out_count[:] = list(cnt)
 
 
 def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_kv: bool,
@@ -536,6 +576,16 @@ class Engine:
                           done_step, seed, draw, n_open, entropy=None, argmax=None, stream=None):
         dg_sample_eb_uniform(logits, canvas, gamma, commit_all, temperature, e_stop, prev_argmax, step, done_step,
                              seed, draw, n_open, self.ws, entropy, argmax, stream)
+
+    def mixed_step(self, tokens, encode, t, logits, stream=None):
+        dg_mixed_step(self.ctx, self.kv, tokens, encode, t, logits, self.ws, stream)
+
+    def sample_eb_seq(self, logits, canvas, gamma, commit_all, n_masked, entropy=None, argmax=None, stream=None):
+        dg_sample_eb_seq(logits, canvas, gamma, commit_all, n_masked, self.ws, entropy, argmax, stream)
+
+    def serve(self, canvas, steps, gamma, n_passes, phase, logits, n_masked, out=None, out_count=None, stream=None):
+        dg_serve(self.ctx, self.kv, canvas, steps, gamma, n_passes, phase, logits, n_masked, self.ws, out, out_count,
+                 stream)
 
     def self_cond(self, logits, z, u=None, stream=None):
         dg_self_cond(self.ctx, logits, z, self.ws, u, stream)

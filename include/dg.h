@@ -336,6 +336,47 @@ dg_status dg_generate_block_sc(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int ba
                                int append_kv, uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step,
                                void* d_ws, size_t ws_bytes, void* stream);
 
+/* ---- mixed batches and continuous batching (Technical Report §6, eliminating CPU-GPU
+ * synchronisation; multi-user throughput) ----
+ * A served batch holds two kinds of forward pass -- denoising steps and KV-cache updates
+ * (the causal encoding of a finished canvas) -- that need different attention masks; a
+ * per-sequence causal flag selects the mask, so both run in one pass. */
+
+/* One pass over `batch` sequences of C tokens (d_tokens int32 [batch][C]): sequence b with
+ * h_encode[b] != 0 runs the causal encoder and appends the K/V of its C tokens (kv->len[b]
+ * += C, as dg_prefill_kv); every other one runs the denoising pass over its canvas at time
+ * h_t[b] in [0, 1] (as dg_denoise_step) and gets the logits rows of its canvas.  The head
+ * computes only the rows of the denoising sequences; the logits rows of the encoding ones
+ * are left as they were.  h_encode, h_t: host arrays [batch] (h_t and d_logits may be NULL
+ * when every sequence encodes).  Errors as for dg_denoise_step and dg_prefill_kv. */
+dg_status dg_mixed_step(dg_ctx* ctx, dg_kv* kv, const int32_t* d_tokens, int batch, const int32_t* h_encode,
+                        const float* h_t, uint16_t* d_logits, void* d_ws, size_t ws_bytes, void* stream);
+
+/* dg_sample_eb with a commit-all flag per sequence (h_commit_all, host int32 [batch],
+ * batch <= DG_MAX_BATCH): the sequences at the last step of their block commit every
+ * [MASK] row, the others follow the entropy bound.  A sequence with no [MASK] row (one
+ * whose canvas is being appended) is left unchanged. */
+dg_status dg_sample_eb_seq(const uint16_t* d_logits, int32_t* d_canvas, int batch, int canvas, int vocab,
+                           float gamma, const int32_t* h_commit_all, float* d_entropy, int32_t* d_argmax,
+                           int32_t* d_n_masked, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Continuous batching of block generation: n_passes mixed passes over `batch` sequences,
+ * each cycling through `steps` denoising steps of its canvas (t = 1 - phase/steps, the
+ * entropy-bounded sampler with gamma, every remaining [MASK] row committed at phase
+ * steps - 1) and one pass (phase == steps) that appends the finished canvas, whose canvas
+ * row then restarts all-[MASK].  h_phase (host int32 [batch], in/out): each sequence's
+ * phase in [0, steps], advanced by n_passes (mod steps + 1); d_canvas must hold the state
+ * that phase implies (at a sequence's first call: all [MASK] at a phase below steps).  The
+ * schedule is fixed on the host, so the loop enqueues every pass without waiting.
+ * d_out (int32 [batch][out_blocks][C], may be NULL): sequence b's finished canvases in
+ * a ring, block i of sequence b at slot i % out_blocks, i counted in h_out_count[b] (host
+ * int32 [batch], in/out).  d_logits: bf16 [batch][C][V] scratch; d_n_masked: int32 [batch].
+ * Errors: DG_ERR_INVALID_ARG for bad phases or sizes, DG_ERR_KV_CAPACITY when the
+ * appends of the call would pass max_ctx (checked before anything is enqueued). */
+dg_status dg_serve(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int steps, float gamma, int n_passes,
+                   int32_t* h_phase, uint16_t* d_logits, int32_t* d_n_masked, int32_t* d_out, int out_blocks,
+                   int32_t* h_out_count, void* d_ws, size_t ws_bytes, void* stream);
+
 /* ---- measurement helpers (diagnostics; not thread-safe) ---- */
 
 /* Kernel kinds the engine launches, for per-kind event timing. */

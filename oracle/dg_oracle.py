@@ -662,33 +662,38 @@ def _kv_put(kv: KVCache, b: int, one: KVCache) -> None:
     kv.len[b] = one.len[0]
 
 
-def mixed_step(cfg, weights: dict, kv: KVCache, tokens: np.ndarray, encode, t, rnd: bool = True) -> np.ndarray:
+def mixed_step(cfg, weights: dict, kv: KVCache, tokens: np.ndarray, encode, t, rnd: bool = True,
+               trace: Optional[list] = None) -> np.ndarray:
     """One batch of both kinds of pass: sequence b with encode[b] runs the causal encoder over
     its C tokens and appends their K/V (prefill_kv); every other one runs the denoising pass
     over its canvas at its own time t[b] (denoise_step).  Returns logits [B][C][V] (NaN on
-    the rows of encoding sequences)."""
+    the rows of encoding sequences).  trace (optional): one list per sequence, as for
+    prefill_kv and denoise_step."""
     tokens = np.asarray(tokens)
     B, C = tokens.shape
     logits = np.full((B, C, cfg.vocab), np.nan)
     for b in range(B):
         one = _kv_one(kv, b)
+        tr = [trace[b]] if trace is not None else None
         if encode[b]:
-            prefill_kv(cfg, weights, one, tokens[b:b + 1], rnd)
+            prefill_kv(cfg, weights, one, tokens[b:b + 1], rnd, trace=tr)
         else:
-            logits[b] = denoise_step(cfg, weights, one, tokens[b:b + 1], float(t[b]), rnd)[0]
+            logits[b] = denoise_step(cfg, weights, one, tokens[b:b + 1], float(t[b]), rnd, trace=tr)[0]
         _kv_put(kv, b, one)
     return logits
 
 
 def serve(cfg, weights: dict, kv: KVCache, batch: int, steps: int, gamma: float, n_passes: int, phase,
-          rnd: bool = True):
+          rnd: bool = True, record: Optional[list] = None):
     """Continuous batching of block generation: n_passes mixed passes, sequence b starting at
     phase[b] in [0, steps) with an all-[MASK] canvas (a later start shortens only its first
     canvas, which still ends with the commit-all step).  Each pass runs every sequence's
     current phase in one mixed_step (denoising at t = 1 - phase/steps, or the append at
     phase = steps), then the sampler on each denoising sequence (sample_eb; commit_all at
     phase steps - 1); an appended canvas is recorded and restarts all-[MASK].  Returns
-    (canvas [B][C], finished: per sequence the list of appended canvases, phase [B])."""
+    (canvas [B][C], finished: per sequence the list of appended canvases, phase [B]).
+    record (optional) gets per pass: the canvas and phases it started from, the encode
+    flags and times, and the routing trace."""
     C, V = cfg.canvas, cfg.vocab
     phase = np.array(phase, dtype=np.int64).copy()
     assert ((phase >= 0) & (phase < steps)).all(), "a sequence starts at a denoising step"
@@ -697,7 +702,11 @@ def serve(cfg, weights: dict, kv: KVCache, batch: int, steps: int, gamma: float,
     for _ in range(n_passes):
         enc = phase == steps
         t = np.where(enc, 0.0, 1.0 - phase / steps)
-        logits = mixed_step(cfg, weights, kv, canvas, enc, t, rnd)
+        tr = [[] for _ in range(batch)] if record is not None else None
+        if record is not None:
+            record.append({"canvas_in": canvas.copy(), "phase": phase.copy(), "encode": enc.copy(), "t": t.copy(),
+                           "trace": tr})
+        logits = mixed_step(cfg, weights, kv, canvas, enc, t, rnd, trace=tr)
         stored = bf16(logits) if rnd else logits
         for b in range(batch):
             if enc[b]:
