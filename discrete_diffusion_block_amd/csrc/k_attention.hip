@@ -284,7 +284,12 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
 }
 
 // Merge of the split-KV partials: one thread per 8 output features of one (sequence,
-// head, query); the splits are combined in split order.
+// head, query); the splits are combined in split order.  Every load a thread needs is
+// issued before the first is used (the split count is bounded by kAttnMaxSplits and the
+// loops are unrolled over that bound), so the merge costs about one memory round trip
+// rather than one per split.
+constexpr int kAttnMaxSplits = 16;
+
 template <int HD>
 __global__ __launch_bounds__(256) void attention_merge_kernel(const float* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml, int nsplit,
@@ -301,20 +306,31 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const float* __res
   const int head = (int)(rr % hq), b = (int)(rr / hq);
   const size_t base = ((size_t)b * hq + head) * npad32 + iq;
   const size_t stride = (size_t)batch * hq * npad32;
+  float2 ml[kAttnMaxSplits];
+  f32x4 v0[kAttnMaxSplits], v1[kAttnMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplits; ++s) {
+    if (s < nsplit) {
+      ml[s] = part_ml[s * stride + base];
+      const float* po = part_o + (s * stride + base) * HD + c8;
+      v0[s] = *reinterpret_cast<const f32x4*>(po);
+      v1[s] = *reinterpret_cast<const f32x4*>(po + 4);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[s * stride + base].x);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplits; ++s)
+    if (s < nsplit) M = fmaxf(M, ml[s].x);
   float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = part_ml[s * stride + base];
-    if (ml.x == -INFINITY) continue;
-    const float f = exp2f(ml.x - M);
-    L += ml.y * f;
-    const float* po = part_o + (s * stride + base) * HD + c8;
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(po), v1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplits; ++s) {
+    if (s >= nsplit || ml[s].x == -INFINITY) continue;
+    const float f = exp2f(ml[s].x - M);
+    L += ml[s].y * f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[e] += v0[e] * f;
-      acc[4 + e] += v1[e] * f;
+      acc[e] += v0[s][e] * f;
+      acc[4 + e] += v1[s][e] * f;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -353,6 +369,7 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   int nsplit = (512 + base_wgs - 1) / base_wgs;
   nsplit = min(nsplit, max(1, stages / 2));
   nsplit = min(nsplit, max(1, kAttnMaxSplitRows / (g.batch * a.qt32 * 32)));
+  nsplit = min(nsplit, kAttnMaxSplits);
   if (!part_o) nsplit = 1;
   a.nsplit = max(1, nsplit);
   const long units = (long)base_wgs * a.nsplit;
