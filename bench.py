@@ -510,6 +510,51 @@ def uniform_line(eng, cfg, args, logits):
             "warmup": UNIFORM_WARMUP}
 
 
+STOP_BUDGET, STOP_BLOCKS, STOP_WARMUP = 48, 2, 1
+
+
+def stop_line(eng, cfg, args, logits):
+    """Adaptive stopping (Technical Report §3.3, Fig. 5: about 12 effective steps of a
+    budget of 48): blocks of the headline workload with a budget of 48 steps and the stop
+    on, e_stop 1e30 (a sequence stops at the first step whose [MASK] rows all keep their
+    argmax; the random-init model's entropies, ~log V, never pass a realistic threshold).
+    The generator skips the passes after completion, so a block costs its completion step
+    plus at most one pass.  The warm-up block counts the passes that ran with the
+    library's launch profiler; the timed blocks run without it."""
+    import torch
+    from discrete_diffusion_block_amd import dg
+    C = cfg.canvas
+    canvas = torch.empty(1, C, dtype=torch.int32, device="cuda")
+    nm = torch.empty(1, dtype=torch.int32, device="cuda")
+    done = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def block():
+        eng.generate_block_ex(canvas, STOP_BUDGET, args.gamma, 1.0, 1.0, 1e30, True, logits, nm, done)
+    dg.dg_profile_begin(eng.ctx, 256, kinds=["prep"])
+    block()
+    passes = dg.dg_profile_end(eng.ctx)["prep"][1] - 1
+    for _ in range(STOP_WARMUP - 1):
+        block()
+    torch.cuda.synchronize()
+    steps_seen = []
+    t0 = time.perf_counter()
+    for _ in range(STOP_BLOCKS):
+        block()
+        steps_seen.append(done)         # read after the clock stops
+        done = torch.empty_like(done)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert nm.item() == 0
+    return {"workload": f"headline workload with the adaptive stop: budget {STOP_BUDGET} steps, gamma {args.gamma}, "
+                        f"tau 1, e_stop 1e30 (stop at the first step whose [MASK] argmaxes all repeat), passes "
+                        f"after completion skipped, KV append, batch 1",
+            "value": round(C * STOP_BLOCKS / wall, 1), "unit": "tok/s",
+            "ms_per_block": round(wall * 1e3 / STOP_BLOCKS, 2),
+            "completion_steps": [int(d.item()) for d in steps_seen],
+            "passes_run_first_block": passes, "budget": STOP_BUDGET, "blocks": STOP_BLOCKS,
+            "warmup": STOP_WARMUP}
+
+
 SC_REPS, SC_BLOCKS, SC_WARMUP = 10, 3, 1
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
@@ -739,7 +784,8 @@ def main():
         return
     cfg = synth.CONFIGS["full"]
     C, V = cfg.canvas, cfg.vocab
-    n_blocks = args.warmup + args.steps + 4 + UNIFORM_BLOCKS + UNIFORM_WARMUP + SC_BLOCKS + SC_WARMUP
+    n_blocks = (args.warmup + args.steps + 4 + UNIFORM_BLOCKS + UNIFORM_WARMUP + SC_BLOCKS + SC_WARMUP
+                + STOP_BLOCKS + STOP_WARMUP)
     max_ctx = int(math.ceil((args.prompt + C * n_blocks) / 64.0) * 64)
     t0 = time.time()
     w = synth.make_weights(cfg, device="cuda")
@@ -858,6 +904,7 @@ def main():
         "spread_routing": None,
         "long_context_batch8": None,
         "uniform_variant": None,
+        "adaptive_stop": None,
         "self_conditioning": None,
         "concurrency": None,
         "cpu_baseline": None,
@@ -869,6 +916,10 @@ def main():
         out["spread_routing"] = spread_line(eng, cfg, args.spread_distinct, reps, args.prompt)
         log("uniform-noise variant...")
         out["uniform_variant"] = uniform_line(eng, cfg, args, logits)
+        log("adaptive stop...")
+        out["adaptive_stop"] = stop_line(eng, cfg, args, logits)
+        log(f"adaptive stop: completion steps {out['adaptive_stop']['completion_steps']}, "
+            f"{out['adaptive_stop']['value']} tok/s")
         log("self-conditioning...")
         out["self_conditioning"] = selfcond_line(eng, cfg, args, logits)
         packed = eng.weights

@@ -1,6 +1,8 @@
 // C ABI of the engine: argument validation, workspace carving and the
 // per-pass kernel schedule.  Everything is enqueued on the caller's stream;
-// nothing here synchronises, allocates device memory or reads back.
+// nothing here allocates device memory.  Only the block generators with the
+// adaptive stop on read back (a few words of pinned host memory, two steps
+// behind the device) and wait on the device for them.
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -24,6 +26,8 @@ struct Prof {
   std::vector<int> kind;
   size_t used = 0;
 };
+
+struct StopProbe;
 
 struct dg_ctx {
   dg_config cfg;
@@ -54,6 +58,24 @@ struct dg_ctx {
   // Forced routing (test tap, not thread-safe): when set, layer l of every pass
   // takes its expert ids from force_ids + l * M * k instead of the router's top-k.
   const int32_t* force_ids = nullptr;
+  // Stop probes of the block generators (see StopProbe), one per call in flight;
+  // guarded by ev_mu.
+  mutable std::vector<StopProbe*> probes;
+};
+
+// Host view of the adaptive stop inside one block-generator call.  After the
+// sampler of step s the generator copies the per-sequence completion steps into
+// pinned host memory (slot s % kStopLag) and records an event; before it enqueues
+// step s it waits for the event of step s - kStopLag and ends the loop once every
+// sequence is complete.  The device then runs at most one pass after the stop (the
+// one already enqueued), and the host stays kStopLag steps ahead of the device.
+constexpr int kStopLag = 2;
+struct StopProbe {
+  int dev = -1;
+  bool busy = false;
+  int32_t* host = nullptr;                 // pinned [kStopLag][DG_MAX_BATCH]
+  hipEvent_t ev[kStopLag] = {};
+  bool recorded[kStopLag] = {};
 };
 
 namespace {
@@ -148,6 +170,57 @@ struct SideFork {
   }
   SideFork(const SideFork&) = delete;
   SideFork& operator=(const SideFork&) = delete;
+};
+
+// A probe for the current device whose earlier copies have all landed (a probe
+// given back by an earlier call may still have a copy in flight on that call's
+// stream, which must not land in this call's slots), or a new one; NULL when none
+// can be made (the generator then runs every step).
+StopProbe* acquire_probe(const dg_ctx* c) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(c->ev_mu);
+  for (StopProbe* p : c->probes) {
+    if (p->busy || p->dev != dev) continue;
+    bool idle = true;
+    for (int i = 0; i < kStopLag; ++i)
+      if (p->recorded[i] && hipEventQuery(p->ev[i]) != hipSuccess) idle = false;
+    if (idle) {
+      p->busy = true;
+      return p;
+    }
+  }
+  (void)hipGetLastError();
+  StopProbe* p = new (std::nothrow) StopProbe;
+  if (!p) return nullptr;
+  p->dev = dev;
+  bool ok = hipHostMalloc((void**)&p->host, sizeof(int32_t) * kStopLag * DG_MAX_BATCH, hipHostMallocDefault) ==
+            hipSuccess;
+  for (int i = 0; ok && i < kStopLag; ++i) ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    for (int i = 0; i < kStopLag; ++i)
+      if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
+    if (p->host) (void)hipHostFree(p->host);
+    delete p;
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  p->busy = true;
+  c->probes.push_back(p);
+  return p;
+}
+
+struct ProbeLease {
+  const dg_ctx* c;
+  StopProbe* p;
+  ProbeLease(const dg_ctx* c_, bool want) : c(c_), p(want ? acquire_probe(c_) : nullptr) {}
+  ~ProbeLease() {
+    if (!p) return;
+    std::lock_guard<std::mutex> lk(c->ev_mu);
+    p->busy = false;
+  }
+  ProbeLease(const ProbeLease&) = delete;
+  ProbeLease& operator=(const ProbeLease&) = delete;
 };
 
 constexpr int kPrefillChunk = 512;   // tokens per sequence per encoder pass
@@ -623,7 +696,18 @@ dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_canvas, c.vocab, (size_t)batch * c.canvas, s));
   DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(ws.prev_amax, -1, (size_t)batch * c.canvas, s));
   DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(d_done_step, 0, (size_t)batch, s));
+  // with the adaptive stop on, the passes after every canvas is complete are skipped
+  ProbeLease probe(ctx, e_stop >= 0.0f && max_steps > kStopLag);
   for (int step = 0; step < max_steps; ++step) {
+    if (probe.p && step >= kStopLag) {
+      const int slot = step % kStopLag;   // written after the sampler of step - kStopLag
+      const hipError_t e = hipEventSynchronize(probe.p->ev[slot]);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "stop probe: %s", hipGetErrorString(e));
+      const int32_t* h = probe.p->host + slot * DG_MAX_BATCH;
+      bool all = true;
+      for (int b = 0; b < batch; ++b) all = all && h[b] != 0;
+      if (all) break;
+    }
     const float t = 1.0f - (float)step / (float)max_steps;
     SampleOpts o;
     o.temperature = tau_min + (tau_max - tau_min) * t;
@@ -647,6 +731,14 @@ dg_status generate_annealed(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     st = sample_impl(d_logits, d_canvas, batch, c.canvas, c.vocab, gamma, commit_mask(step == max_steps - 1), nullptr,
                      nullptr, d_n, ws, s, ctx, o);
     if (st != DG_OK) return st;
+    if (probe.p && step + kStopLag < max_steps) {   // read before step + kStopLag is enqueued
+      const int slot = step % kStopLag;
+      hipError_t e = hipMemcpyAsync(probe.p->host + slot * DG_MAX_BATCH, d_done_step, sizeof(int32_t) * batch,
+                                    hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipEventRecord(probe.p->ev[slot], s);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "stop probe: %s", hipGetErrorString(e));
+      probe.p->recorded[slot] = true;
+    }
   }
   if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
   return DG_OK;
@@ -721,6 +813,14 @@ void dg_destroy(dg_ctx* ctx) {
   for (auto& e : ctx->ev_all) {
     (void)hipEventDestroy(e.first);
     (void)hipEventDestroy(e.second);
+  }
+  for (StopProbe* p : ctx->probes) {
+    for (int i = 0; i < kStopLag; ++i) {
+      if (p->recorded[i]) (void)hipEventSynchronize(p->ev[i]);   // its copy lands before the memory goes
+      (void)hipEventDestroy(p->ev[i]);
+    }
+    (void)hipHostFree(p->host);
+    delete p;
   }
   delete ctx;
 }

@@ -250,8 +250,14 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
  * at once; the last step commits whatever is left.  d_done_step (int32 [batch],
  * out): the number of steps after which each canvas was complete.  The previous
  * argmax lives in the workspace.  Once a canvas is complete its later steps change
- * nothing, but their denoising passes still run: nothing is skipped on the device
- * and the host never waits. */
+ * nothing.  With the stop on (e_stop >= 0) and max_steps > 2 the call skips them:
+ * after each step's sampler it copies d_done_step into pinned host memory, and
+ * before it enqueues step s it waits for the copy of step s - 2 and ends the step
+ * loop (then runs the append pass) once every sequence is complete, so at most one
+ * pass runs after the last canvas completes.  The host then blocks until the device
+ * is within two steps of the call's end; such a call cannot be captured into a
+ * graph.  With the stop off the host never waits.  The skipped steps would change
+ * neither the canvas, d_n_masked, d_done_step nor the KV cache. */
 dg_status dg_generate_block_ex(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
                                float gamma, float tau_max, float tau_min, float e_stop,
                                int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
@@ -298,7 +304,9 @@ dg_status dg_sample_eb_uniform(const uint16_t* d_logits, int32_t* d_canvas, int 
  * complete when the stop fires or after the last step and is not changed afterwards.
  * Then the append pass if append_kv.  d_n_open: int32 [batch] (0 at the end);
  * d_done_step: int32 [batch], the number of steps after which each canvas was
- * complete.  Errors as for dg_generate_block_ex. */
+ * complete.  With the stop on, the steps after every canvas is complete are skipped
+ * as in dg_generate_block_ex; d_logits then holds the last pass that ran (its rows of
+ * complete canvases are scratch either way).  Errors as for dg_generate_block_ex. */
 dg_status dg_generate_block_uniform(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps,
                                     float gamma, float tau_max, float tau_min, float e_stop, uint64_t seed,
                                     int append_kv, uint16_t* d_logits, int32_t* d_n_open,
@@ -330,7 +338,8 @@ dg_status dg_denoise_step_sc(dg_ctx* ctx, const dg_kv* kv, const int32_t* d_canv
 /* dg_generate_block_ex (uniform = 0) or dg_generate_block_uniform (uniform = 1, with
  * seed) with self-conditioning: step 0 runs with z = 0, and after every step but the
  * last z is recomputed from that step's logits for the next one; the head computes
- * every canvas row at every step.  z lives in the workspace. */
+ * every canvas row at every step.  z lives in the workspace.  With the stop on, the
+ * steps after every canvas is complete are skipped as in dg_generate_block_ex. */
 dg_status dg_generate_block_sc(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int max_steps, float gamma,
                                float tau_max, float tau_min, float e_stop, int uniform, uint64_t seed,
                                int append_kv, uint16_t* d_logits, int32_t* d_n, int32_t* d_done_step,
