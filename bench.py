@@ -30,10 +30,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+# the translation unit of each counted kernel kind (its launcher included) and the
+# headers every kernel source includes
+KIND_SOURCES = {"moe_gate_up": "k_moe.hip", "moe_down": "k_moe.hip", "head": "k_gemm.hip",
+                "sample_pass1": "k_sampler.hip", "attention": "k_attention.hip"}
+
+
+def kernel_source_digest(kind: str = "moe_gate_up") -> str:
+    """Digest of the sources that define one kernel kind: a traffic measurement stays
+    valid while they are unchanged (host-side runtime changes do not touch it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "discrete_diffusion_block_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("dg_common.h", "dg_internal.h", KIND_SOURCES[kind]):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -305,7 +313,7 @@ def write_traffic(fetch_txt: str, write_txt: str, kind: str, counts_json: str) -
     name = f"dg::{kind}_kernel"
     hw = int(round((fe[name] * fs + wr[name] * ws) * 1024))
     alg = cj.get(f"{kind}_bytes_per_launch")
-    t = {"kernel": kind, "source_digest": kernel_source_digest(),
+    t = {"kernel": kind, "source_digest": kernel_source_digest(kind),
          "bytes_per_launch": hw,
          "algorithmic_bytes_per_launch": alg,
          "traffic_over_algorithmic": round(hw / alg, 3) if alg else None,
@@ -854,7 +862,8 @@ def main():
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
-        if t.get("kernel") == dom and t.get("source_digest") == kernel_source_digest():
+        if (t.get("kernel") == dom and dom in KIND_SOURCES
+                and t.get("source_digest") == kernel_source_digest(dom)):
             traffic = t.get("bytes_per_launch")
     roofline = roofline_obj(bound, unit, avg_ms, amount, dom_launches, dom, traffic)
     if not used:
