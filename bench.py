@@ -228,9 +228,13 @@ def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prom
                     bench_json: str = None) -> str:
     """Per-kernel launch statistics from the rocprofv3 kernel-trace CSV under root of a
     `bench.py --steps S --warmup W` run: the denoising passes of the S timed blocks.
-    Passes start at the engine's prep kernel; the prompt prefill takes the first
-    ceil(prompt / 512) passes, then each block runs denoise_steps denoising passes (the
-    ones that end in the vocabulary head) and one append pass.  bench_json: that same
+    Passes start at the engine's prep kernel.  The run's passes, in order: the prompt
+    prefill (ceil(prompt / 512) passes); W warm-up blocks of denoise_steps denoising
+    passes (the ones that end in the vocabulary head) and one append pass each; a
+    2-block dg_generate_blocks call (2 * denoise_steps passes, the first block's append
+    inside the second block's first pass, then the last append); the timed S-block
+    call (S * denoise_steps passes + one append); S blocks as one call each; the
+    profiled block; then the roofline passes.  bench_json: that same
     run's JSON line, whose roofline figure (the dominant kind's algorithmic bytes per
     launch over the run's last denoise_steps passes, from their own expert counts) is
     divided by the trace's average duration of the same launches."""
@@ -245,8 +249,8 @@ def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prom
     starts = [i for i, r in enumerate(rows) if "prep_kernel" in r["Kernel_Name"]] + [len(rows)]
     passes = [rows[a:b] for a, b in zip(starts[:-1], starts[1:])]
     per_block = denoise_steps + 1
-    first = -(-prompt // 512) + warmup * per_block
-    timed = passes[first:first + steps * per_block]
+    first = -(-prompt // 512) + warmup * per_block + (2 * denoise_steps + 1)
+    timed = passes[first:first + steps * denoise_steps + 1]
     denoise = [p for p in timed if any("head_gemm" in r["Kernel_Name"] for r in p)]
     agg = collections.defaultdict(list)
     for p in denoise:
@@ -266,7 +270,7 @@ def summarize_trace(root: str, warmup: int, steps: int, denoise_steps: int, prom
     # which bench.py times the dominant kind with HIP events (the roofline figure of its
     # JSON line); they precede the sampler and the secondary workloads' passes
     heads = [p for p in passes if sum("head_gemm" in r["Kernel_Name"] for r in p) == 1 and len(p) > 300]
-    roof = heads[steps * denoise_steps + warmup * denoise_steps + denoise_steps:][:denoise_steps]
+    roof = heads[(warmup + 2 + 2 * steps + 1) * denoise_steps:][:denoise_steps]
     ragg = collections.defaultdict(list)
     for p in roof:
         for r in p:
@@ -792,7 +796,7 @@ def main():
         return
     cfg = synth.CONFIGS["full"]
     C, V = cfg.canvas, cfg.vocab
-    n_blocks = (args.warmup + args.steps + 4 + UNIFORM_BLOCKS + UNIFORM_WARMUP + SC_BLOCKS + SC_WARMUP
+    n_blocks = (args.warmup + 2 * args.steps + 2 + 4 + UNIFORM_BLOCKS + UNIFORM_WARMUP + SC_BLOCKS + SC_WARMUP
                 + STOP_BLOCKS + STOP_WARMUP)
     max_ctx = int(math.ceil((args.prompt + C * n_blocks) / 64.0) * 64)
     t0 = time.time()
@@ -813,21 +817,37 @@ def main():
         eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole blocks
+    # ---- timed region: K whole blocks, each generated and appended to the cache, in
+    # one dg_generate_blocks call (each block's append shares a pass with the next
+    # block's first denoising step; the last block's append runs on its own)
+    blocks = torch.empty(args.steps, 1, C, dtype=torch.int32, device="cuda")
+    eng.generate_blocks(blocks[:2], args.denoise_steps, args.gamma, True, logits, nm)   # warm-up of the call
+    L0 = eng.lengths[0]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+    eng.generate_blocks(blocks, args.denoise_steps, args.gamma, True, logits, nm)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    assert nm.item() == 0
+    assert nm.item() == 0 and (blocks != V).all()
     ms_per_block = wall * 1000.0 / args.steps
     value = C * args.steps / wall
     log(f"{args.steps} blocks: {wall * 1e3:.1f} ms wall, {gpu_ms:.1f} ms GPU -> {value:.0f} tok/s")
+    # the same blocks (the cache rewound to the same length: generation is deterministic)
+    # as one dg_generate_block call each, the append as its own pass
+    eng.kv.len[0] = L0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
+        same = torch.equal(canvas, blocks[j, 0]) if j == 0 else same
+    torch.cuda.synchronize()
+    per_call_tok_s = C * args.steps / (time.perf_counter() - t0)
+    assert eng.lengths[0] == L0 + C * args.steps and torch.equal(canvas, blocks[-1, 0]) and same
+    log(f"  the same blocks, one dg_generate_block call each: {per_call_tok_s:.0f} tok/s")
 
     # ---- one more block with per-launch HIP events (same stream, same work)
     dg.dg_profile_begin(eng.ctx, 20000)
@@ -896,15 +916,19 @@ def main():
         "data": "synthetic (random-init N(0,0.02) bf16 weights, uniform-random 1024-token prompt)",
         "config": {"workload": "full 256-token block generation: 30 MoE layers d2816, 16q/8kv x128, "
                                "128 experts top-8 (F 704) + shared (F 2112), vocab 262144 tied, "
-                               "1024-token prompt, 12 steps, gamma 2.0, batch 1; the random-init router sends "
+                               f"1024-token prompt, {args.steps} consecutive blocks of 12 steps, gamma 2.0, batch 1, "
+                               "every block generated and appended to the KV cache (dg_generate_blocks: each "
+                               "append shares a pass with the next block's first denoising step, bit-identical "
+                               "to separate passes); the random-init router sends "
                                f"the all-[MASK] canvas to ~{experts} of the 128 experts per layer, so the MoE "
                                "streams that many experts' weights (a trained model spreads to ~84: see "
                                "spread_routing)",
                    "global_batch": 1, "seq_len": args.prompt, "canvas": C,
                    "denoise_steps": args.denoise_steps, "parallelism": "single GPU"},
+        "per_block_call_tok_s": round(per_call_tok_s, 1),
         "denoise_step_ms": round(denoise_ms, 3),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 3),
-        "tokens_per_forward": round(C / (args.denoise_steps + 1), 3),
+        "tokens_per_forward": round(C * args.steps / (args.denoise_steps * args.steps + 1), 3),
         "experts_used_per_layer_mean": experts,
         "profiled_block_ms": round(prof_block_ms, 3),
         "kernel_ms_per_block": {k: round(v[0], 3) for k, v in prof.items() if v[1]},

@@ -320,7 +320,7 @@ size_t carve(const dg_config& c, int batch, char* base, Ws* ws, bool self_cond) 
   ws->att_po = cv.take<float>((size_t)kAttnMaxSplitRows * qd);
   ws->att_pml = cv.take<float2>((size_t)kAttnMaxSplitRows * c.n_q_heads);
   ws->rope = cv.take<float2>(M * (c.head_dim / 2));
-  ws->temb = cv.take<float>((size_t)batch * c.d_model);
+  ws->temb = cv.take<float>((size_t)DG_MAX_BATCH * c.d_model);   // a fused block pass has 2 sequences per slot
   ws->r = cv.take<float>(M * c.n_experts);
   ws->ids = cv.take<int32_t>(M * c.top_k);
   ws->wts = cv.take<float>(M * c.top_k);
@@ -401,10 +401,31 @@ KvLayer kv_layer(const dg_ctx* ctx, const dg_kv* kv, int l) {
 // masked_head (denoise passes): the head computes only the rows whose canvas token is
 // [MASK] -- the only rows the sampler reads -- and leaves the other logits rows as
 // they were.
+// split > 0 (a fused block pass): the pass's first `split` sequences are KV updates and
+// the others denoising canvases; attention runs as one launch per group (each with the
+// key splitting it gets in a pass of its own), and the head's output rows count from
+// the first denoising row.
+PassGeom sub_geom(const PassGeom& g, int s0, int s1) {
+  PassGeom h{};
+  h.batch = s1 - s0;
+  h.n = g.n;
+  h.enc = (g.enc >> s0) & all_sequences(s1 - s0);
+  h.denoise = h.enc != all_sequences(s1 - s0);
+  for (int b = s0; b < s1; ++b) {
+    h.len[b - s0] = g.len[b];
+    h.t[b - s0] = g.t[b];
+    h.kvshift[b - s0] = g.kvshift[b] - s0;   // the same cache sequence: (b - s0) - h.kvshift = b - g.kvshift
+  }
+  return h;
+}
+
 dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const int32_t* tokens,
                    uint16_t* logits, const Ws& ws, hipStream_t s, bool masked_head = false,
-                   const float* z = nullptr) {
+                   const float* z = nullptr, int split = 0) {
   const dg_config& c = ctx->cfg;
+  for (int b = 0; b < g.batch; ++b)
+    if (kv_seq(g, b) < 0 || kv_seq(g, b) >= c.max_batch)
+      return fail(DG_ERR_INVALID_ARG, "pass sequence %d maps to cache sequence %d", b, kv_seq(g, b));
   const int M = g.batch * g.n;
   const int d = c.d_model, hq = c.n_q_heads, hd = c.head_dim, E = c.n_experts, k = c.top_k;
   const float eps = c.rms_eps;
@@ -422,8 +443,18 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     // In the encoder only the keys/values are observable; the last layer's
     // attention output and FFN feed nothing, so they are not computed.
     if (!g.denoise && l == nl - 1) break;
-    DG_TIMED(ctx, kvl.window == 0 ? DG_K_ATTENTION_GLOBAL : DG_K_ATTENTION,
-             launch_attention(ws.q, hq, kvl, g, ws.o, ws.att_po, ws.att_pml, s));
+    if (split > 0 && split < g.batch) {
+      const size_t q_seq = (size_t)hq * ((g.n + 15) & ~15) * hd;    // one sequence's q
+      for (int part = 0; part < 2; ++part) {
+        const int s0 = part ? split : 0, s1 = part ? g.batch : split;
+        DG_TIMED(ctx, kvl.window == 0 ? DG_K_ATTENTION_GLOBAL : DG_K_ATTENTION,
+                 launch_attention(ws.q + s0 * q_seq, hq, kvl, sub_geom(g, s0, s1),
+                                  ws.o + (size_t)s0 * g.n * hq * hd, ws.att_po, ws.att_pml, s));
+      }
+    } else {
+      DG_TIMED(ctx, kvl.window == 0 ? DG_K_ATTENTION_GLOBAL : DG_K_ATTENTION,
+               launch_attention(ws.q, hq, kvl, g, ws.o, ws.att_po, ws.att_pml, s));
+    }
     DG_TIMED(ctx, DG_K_O_PROJ, launch_gemm_f32(ws.o, L.w_o, ws.x, M, d, hq * hd, /*add=*/true, s));
     // The shared expert depends only on h: it runs on the side stream while the
     // routed experts' routing chain (small, latency-bound kernels) runs here.  It
@@ -466,7 +497,7 @@ dg_status run_pass(const dg_ctx* ctx, const dg_kv* kv, const PassGeom& g, const 
     DG_TIMED(ctx, DG_K_COMBINE,
              launch_combine(ws.x, ws.ys, ws.Y, ws.wts, ws.inv, M, k, d, next_gain, eps, ws.h,
                             compact && masked_head ? tokens : nullptr, c.vocab, g.enc, g.n,
-                            compact ? ws.rows : nullptr, ws.counters, s));
+                            compact ? ws.rows : nullptr, ws.counters, split * g.n, s));
   }
   const bool compact = (masked_head || g.enc != 0) && g.denoise;
   if (g.denoise)
@@ -985,6 +1016,68 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
     if (st != DG_OK) return st;
   }
   if (append_kv) return prefill_impl(ctx, kv, d_canvas, batch, c.canvas, ws, s);
+  return DG_OK;
+}
+
+dg_status dg_generate_blocks(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int n_blocks, int steps,
+                             float gamma, int append_last, uint16_t* d_logits, int32_t* d_n_masked, void* d_ws,
+                             size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DG_ERR_INVALID_ARG, "ctx is NULL");
+  dg_status st = check_kv(ctx, kv, batch);
+  if (st != DG_OK) return st;
+  if (!d_canvas || !d_logits || !d_n_masked) return fail(DG_ERR_INVALID_ARG, "NULL pointer");
+  if (steps < 1 || n_blocks < 1) return fail(DG_ERR_INVALID_ARG, "steps and n_blocks must be >= 1");
+  if (gamma != gamma) return fail(DG_ERR_INVALID_ARG, "gamma is NaN");
+  const dg_config& c = ctx->cfg;
+  const int C = c.canvas;
+  for (int b = 0; b < batch; ++b)
+    if (kv->len[b] + (int64_t)n_blocks * C > c.max_ctx)
+      return fail(DG_ERR_KV_CAPACITY, "sequence %d: len %lld + %d blocks of %d exceeds max_ctx %d", b,
+                  (long long)kv->len[b], n_blocks, C, c.max_ctx);
+  Ws ws;
+  st = get_ws(ctx, batch, d_ws, ws_bytes, &ws);
+  if (st != DG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the append of block j - 1 and the first step of block j share one pass when both
+  // fit the workspace's rows and the pass's sequence slots
+  const bool fuse = 2 * C <= std::max(C, kPrefillChunk) && 2 * batch <= DG_MAX_BATCH;
+  for (int j = 0; j < n_blocks; ++j) {
+    int32_t* cv = d_canvas + (size_t)j * batch * C;
+    DG_TIMED(ctx, DG_K_FILL, launch_fill_i32(cv, c.vocab, (size_t)batch * C, s));
+    for (int step = 0; step < steps; ++step) {
+      const float t = 1.0f - (float)step / (float)steps;
+      if (step == 0 && j > 0 && fuse) {
+        // sequences 0 .. batch-1: the causal append of block j - 1 at len; sequences
+        // batch .. 2 batch-1: block j's canvas at len + C, in the same cache sequences
+        PassGeom g{};
+        g.batch = 2 * batch;
+        g.n = C;
+        g.denoise = 1;
+        g.enc = all_sequences(batch);
+        for (int b = 0; b < batch; ++b) {
+          g.len[b] = (int)kv->len[b];
+          g.len[batch + b] = (int)kv->len[b] + C;
+          g.t[batch + b] = t;
+          g.kvshift[batch + b] = batch;
+        }
+        st = run_pass(ctx, kv, g, d_canvas + (size_t)(j - 1) * batch * C, d_logits, ws, s, /*masked_head=*/true,
+                      nullptr, /*split=*/batch);
+        if (st != DG_OK) return st;
+        for (int b = 0; b < batch; ++b) kv->len[b] += C;
+      } else {
+        if (step == 0 && j > 0) {
+          st = prefill_impl(ctx, kv, d_canvas + (size_t)(j - 1) * batch * C, batch, C, ws, s);
+          if (st != DG_OK) return st;
+        }
+        st = denoise_impl(ctx, kv, cv, batch, t, d_logits, ws, s, /*masked_head=*/true);
+        if (st != DG_OK) return st;
+      }
+      st = sample_impl(d_logits, cv, batch, C, c.vocab, gamma, commit_mask(step == steps - 1), nullptr, nullptr,
+                       d_n_masked, ws, s, ctx);
+      if (st != DG_OK) return st;
+    }
+  }
+  if (append_last) return prefill_impl(ctx, kv, d_canvas + (size_t)(n_blocks - 1) * batch * C, batch, C, ws, s);
   return DG_OK;
 }
 

@@ -21,7 +21,11 @@ struct PassGeom {
                              // the others the bidirectional denoiser over the cached prefix
   int len[DG_MAX_BATCH];
   float t[DG_MAX_BATCH];     // denoising time of each denoising sequence
+  int kvshift[DG_MAX_BATCH]; // pass sequence b keeps its keys/values in cache sequence
+                             // b - kvshift[b] (0: its own; a pass may run two segments of
+                             // one cached sequence as two pass sequences)
 };
+__host__ __device__ inline int kv_seq(const PassGeom& g, int b) { return b - g.kvshift[b]; }
 __host__ __device__ inline bool seq_encodes(const PassGeom& g, int b) { return (g.enc >> b) & 1; }
 inline uint64_t all_sequences(int batch) { return batch >= 64 ? ~0ull : ((1ull << batch) - 1); }
 
@@ -95,7 +99,7 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
                     const int32_t* canvas, int mask_id, uint64_t skip, int n, int32_t* rows_out, int32_t* count,
-                    hipStream_t s);
+                    int row_base, hipStream_t s);
 
 // ---- dense GEMMs ----
 // y = x . w^T with fp32 output (store) or fp32 accumulate into y (add).

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
   // the wave's whole 32-query range, for deciding which stages need no mask at all
   const int p_first = len + q0, p_last = len + min(q0 + 31, n - 1);
 
-  const uint16_t* kbase = kv.k + ((size_t)b * kv.hkv + kvh) * (size_t)kv.max_ctx * HD;
-  const uint16_t* vbase = kv.vt + ((size_t)b * kv.hkv + kvh) * (size_t)HD * kv.max_ctx;
+  const uint16_t* kbase = kv.k + ((size_t)kv_seq(g, b) * kv.hkv + kvh) * (size_t)kv.max_ctx * HD;
+  const uint16_t* vbase = kv.vt + ((size_t)kv_seq(g, b) * kv.hkv + kvh) * (size_t)HD * kv.max_ctx;
   // stage st: K chunks 2 st, 2 st + 1 (contiguous), then V chunks 2 st, 2 st + 1
   auto issue = [&](int st, int slot) {
     char* dst = ring + slot * STAGE;

@@ -163,7 +163,8 @@ void launch_rmsnorm(const float* x, const float* gain, float eps, uint16_t* h, u
 // last layer of a pass whose head needs only some rows: those of the denoising
 // sequences -- skip has the bits of the others -- and, with canvas given, only their
 // [MASK] rows), only those rows are normed, each into the next free h row i taken
-// from *count (zero on entry; it ends as the number of rows kept), with rows_out[i] = m.
+// from *count (zero on entry; it ends as the number of rows kept), with
+// rows_out[i] = m - row_base (the head's output row).
 // The order of the compacted rows varies from run to run; every logits row the
 // head computes from them does not depend on it.
 __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys, const float* Y,
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
                                                       const int32_t* inv, int k, int d,
                                                       const float* next_gain, float eps,
                                                       uint16_t* h, const int32_t* canvas, int mask_id,
-                                                      uint64_t skip, int n, int32_t* rows_out, int32_t* count) {
+                                                      uint64_t skip, int n, int32_t* rows_out, int32_t* count,
+                                                      int row_base) {
   __shared__ float red[16];
   __shared__ int out_row;
   __shared__ int slot[16];
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
     if (canvas && canvas[m] != mask_id) return;
     if (threadIdx.x == 0) {
       const int i = atomicAdd(count, 1);
-      rows_out[i] = m;
+      rows_out[i] = m - row_base;
       out_row = i;
     }
     __syncthreads();
@@ -219,9 +221,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(float* x, const float* ys
 void launch_combine(float* x, const float* ys, const float* Y, const float* wts, const int32_t* inv,
                     int M, int k, int d, const float* next_gain, float eps, uint16_t* h,
                     const int32_t* canvas, int mask_id, uint64_t skip, int n, int32_t* rows_out, int32_t* count,
-                    hipStream_t s) {
+                    int row_base, hipStream_t s) {
   launch_kernel(combine_kernel, dim3(M), dim3(row_threads(d)), 0, s, nullptr, x, ys, Y, wts, inv, k, d, next_gain, eps, h,
-                canvas, mask_id, skip, n, rows_out, count);
+                canvas, mask_id, skip, n, rows_out, count, row_base);
 }
 
 // End of a serving pass: every sequence whose bit in enc is set has just appended its

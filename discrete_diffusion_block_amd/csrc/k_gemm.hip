@@ -97,13 +97,13 @@ __device__ __forceinline__ void epilogue(const DenseArgs& a, int blk0, int m, co
           *reinterpret_cast<uint32_t*>(base + fm_index(ii, p + half, hd)) = pack_bf2(y2, y3);
         } else {
           const int kh = head - a.hq;
-          uint16_t* base = a.kv.k + ((size_t)b * a.kv.hkv + kh) * (size_t)a.kv.max_ctx * hd;
+          uint16_t* base = a.kv.k + ((size_t)kv_seq(a.g, b) * a.kv.hkv + kh) * (size_t)a.kv.max_ctx * hd;
           *reinterpret_cast<uint32_t*>(base + k_index(pos, p, hd)) = pack_bf2(y0, y1);
           *reinterpret_cast<uint32_t*>(base + k_index(pos, p + half, hd)) = pack_bf2(y2, y3);
         }
       } else {
         const int vh = head - a.hq - a.kv.hkv;
-        uint16_t* base = a.kv.vt + ((size_t)b * a.kv.hkv + vh) * (size_t)hd * a.kv.max_ctx;
+        uint16_t* base = a.kv.vt + ((size_t)kv_seq(a.g, b) * a.kv.hkv + vh) * (size_t)hd * a.kv.max_ctx;
         base[v_index(pos, p, hd)] = f2bf(x0);
         base[v_index(pos, p + 1, hd)] = f2bf(x1);
         base[v_index(pos, p + half, hd)] = f2bf(x2);

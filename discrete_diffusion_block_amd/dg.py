@@ -80,6 +80,7 @@ def lib():
             "dg_sample_eb": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp],
             "dg_sample_eb_noalloc": [vp, vp, i32, i32, i32, f32, i32, vp, vp, vp, vp],
             "dg_generate_block": [vp, C.POINTER(KV), vp, i32, i32, f32, i32, vp, vp, vp, sz, vp],
+            "dg_generate_blocks": [vp, C.POINTER(KV), vp, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp],
             "dg_sample_eb_ex": [vp, vp, i32, i32, i32, f32, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, sz,
                                 vp],
             "dg_generate_block_ex": [vp, C.POINTER(KV), vp, i32, i32, f32, f32, f32, f32, i32, vp, vp, vp,
@@ -326,6 +327,14 @@ def dg_generate_block(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: floa
                                    _stream(stream)))
 
 
+def dg_generate_blocks(ctx, kv: KV, canvas: torch.Tensor, steps: int, gamma: float, append_last: bool,
+                       logits: torch.Tensor, n_masked: torch.Tensor, ws: torch.Tensor, stream=None):
+    """canvas: int32 [n_blocks][batch][C] (out)."""
+    _check(lib().dg_generate_blocks(ctx, C.byref(kv), _p(canvas), canvas.shape[1], canvas.shape[0], steps,
+                                    float(gamma), int(bool(append_last)), _p(logits), _p(n_masked), _p(ws),
+                                    ws.numel(), _stream(stream)))
+
+
 def dg_packed_elems(rows: int, cols: int) -> int:
     n = C.c_size_t()
     _check(lib().dg_packed_elems(rows, cols, C.byref(n)))
@@ -562,6 +571,9 @@ class Engine:
         off = dg_workspace_moe_counts(self.ctx, self.max_batch)
         n = self.cfg.n_layers * self.cfg.n_experts
         return self.ws[off:off + 4 * n].view(torch.int32).view(self.cfg.n_layers, self.cfg.n_experts)
+
+    def generate_blocks(self, canvas, steps, gamma, append_last, logits, n_masked, stream=None):
+        dg_generate_blocks(self.ctx, self.kv, canvas, steps, gamma, append_last, logits, n_masked, self.ws, stream)
 
     def generate_block(self, canvas, steps, gamma, append_kv, logits, n_masked, stream=None):
         dg_generate_block(self.ctx, self.kv, canvas, steps, gamma, append_kv, logits, n_masked,

@@ -242,6 +242,22 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
                             float gamma, int append_kv, uint16_t* d_logits, int32_t* d_n_masked,
                             void* d_ws, size_t ws_bytes, void* stream);
 
+/* n_blocks consecutive blocks per sequence (Technical Report §3.1–§3.3, the block
+ * loop): block j fills d_canvas + j * batch * C (int32 [n_blocks][batch][C], out) as
+ * dg_generate_block does, and its KV append runs fused into block j + 1's first
+ * denoising pass: one pass over 2 * batch * C rows in which the first batch * C rows
+ * (block j, causal, at len) write their keys/values before the attention of every
+ * layer and the other rows (block j + 1's canvas, at len + C) attend to them.  Every
+ * row's arithmetic is that of the separate passes, so canvases, logits and the KV
+ * cache equal n_blocks calls of dg_generate_block(append_kv = 1) bit for bit (when
+ * C > 256 or 2 * batch > DG_MAX_BATCH the passes stay separate).  The last block is
+ * appended by its own pass if append_last.  d_logits and d_n_masked as for
+ * dg_generate_block (the last block's).  Errors: as dg_generate_block, and
+ * DG_ERR_KV_CAPACITY when len + n_blocks * C exceeds max_ctx. */
+dg_status dg_generate_blocks(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch, int n_blocks, int steps,
+                             float gamma, int append_last, uint16_t* d_logits, int32_t* d_n_masked,
+                             void* d_ws, size_t ws_bytes, void* stream);
+
 /* dg_generate_block with the Technical Report's default sampler (§3.3) on the
  * absorbing canvas: up to max_steps steps at t_s = 1 - s/max_steps, entropies at
  * the temperature tau_min + (tau_max - tau_min) t_s (annealed linearly from tau_max
