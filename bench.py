@@ -522,16 +522,20 @@ def uniform_line(eng, cfg, args, logits):
             "warmup": UNIFORM_WARMUP}
 
 
-STOP_BUDGET, STOP_BLOCKS, STOP_WARMUP = 48, 2, 1
+STOP_BUDGET, STOP_BLOCKS, STOP_WARMUP, STOP_GAMMA = 48, 2, 1, 128.0
 
 
 def stop_line(eng, cfg, args, logits):
     """Adaptive stopping (Technical Report §3.3, Fig. 5: about 12 effective steps of a
-    budget of 48): blocks of the headline workload with a budget of 48 steps and the stop
-    on, e_stop 1e30 (a sequence stops at the first step whose [MASK] rows all keep their
-    argmax; the random-init model's entropies, ~log V, never pass a realistic threshold).
-    The generator skips the passes after completion, so a block costs its completion step
-    plus at most one pass.  The warm-up block counts the passes that ran with the
+    budget of 48): blocks of the headline model with a budget of 48 steps and the stop on,
+    e_stop 1e30 (a sequence stops at the first step whose [MASK] rows all keep their
+    argmax; the random-init model's entropies, ~log V, never pass a realistic threshold),
+    and gamma 128 (about ten rows per step at those entropies).  On random-init weights
+    the argmaxes keep moving, so the canvas completes through the entropy budget rather
+    than the stop; either way the generator skips the passes after completion, and a
+    block costs its completion step plus at most one pass.  Every run starts its blocks right after the prompt (the cache
+    rewound to the prompt's length), so the blocks, and where the stop fires, are the
+    same from run to run.  The warm-up block counts the passes that ran with the
     library's launch profiler; the timed blocks run without it."""
     import torch
     from discrete_diffusion_block_amd import dg
@@ -539,15 +543,18 @@ def stop_line(eng, cfg, args, logits):
     canvas = torch.empty(1, C, dtype=torch.int32, device="cuda")
     nm = torch.empty(1, dtype=torch.int32, device="cuda")
     done = torch.empty(1, dtype=torch.int32, device="cuda")
+    L_saved = eng.lengths[0]
 
     def block():
-        eng.generate_block_ex(canvas, STOP_BUDGET, args.gamma, 1.0, 1.0, 1e30, True, logits, nm, done)
+        eng.generate_block_ex(canvas, STOP_BUDGET, STOP_GAMMA, 1.0, 1.0, 1e30, True, logits, nm, done)
+    eng.kv.len[0] = args.prompt
     dg.dg_profile_begin(eng.ctx, 256, kinds=["prep"])
     block()
     passes = dg.dg_profile_end(eng.ctx)["prep"][1] - 1
     for _ in range(STOP_WARMUP - 1):
         block()
     torch.cuda.synchronize()
+    eng.kv.len[0] = args.prompt
     steps_seen = []
     t0 = time.perf_counter()
     for _ in range(STOP_BLOCKS):
@@ -557,9 +564,11 @@ def stop_line(eng, cfg, args, logits):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert nm.item() == 0
-    return {"workload": f"headline workload with the adaptive stop: budget {STOP_BUDGET} steps, gamma {args.gamma}, "
+    eng.kv.len[0] = max(L_saved, eng.lengths[0])
+    return {"workload": f"headline model with the adaptive stop: budget {STOP_BUDGET} steps, gamma {STOP_GAMMA}, "
                         f"tau 1, e_stop 1e30 (stop at the first step whose [MASK] argmaxes all repeat), passes "
-                        f"after completion skipped, KV append, batch 1",
+                        f"after completion skipped, KV append, batch 1; {STOP_BLOCKS} consecutive blocks right after "
+                        f"the {args.prompt}-token prompt",
             "value": round(C * STOP_BLOCKS / wall, 1), "unit": "tok/s",
             "ms_per_block": round(wall * 1e3 / STOP_BLOCKS, 2),
             "completion_steps": [int(d.item()) for d in steps_seen],
@@ -843,10 +852,10 @@ def main():
     t0 = time.perf_counter()
     for j in range(args.steps):
         eng.generate_block(canvas, args.denoise_steps, args.gamma, True, logits, nm)
-        same = torch.equal(canvas, blocks[j, 0]) if j == 0 else same
+        same = torch.equal(canvas[0], blocks[j, 0]) if j == 0 else same
     torch.cuda.synchronize()
     per_call_tok_s = C * args.steps / (time.perf_counter() - t0)
-    assert eng.lengths[0] == L0 + C * args.steps and torch.equal(canvas, blocks[-1, 0]) and same
+    assert eng.lengths[0] == L0 + C * args.steps and torch.equal(canvas[0], blocks[-1, 0]) and same
     log(f"  the same blocks, one dg_generate_block call each: {per_call_tok_s:.0f} tok/s")
 
     # ---- one more block with per-launch HIP events (same stream, same work)
