@@ -191,6 +191,123 @@ __global__ __launch_bounds__(64 * NW) void dense_gemm(DenseArgs a) {
   }
 }
 
+// Wide-tile dense GEMM for passes of many rows (several sequences, or long prefill
+// chunks): a workgroup owns 256 weight rows x 128 tokens, with both operands staged
+// through LDS by direct global->LDS copies (weights in a three-step ring, two steps
+// ahead; token tiles in a two-step ring) and read by all four waves.  Wave w computes
+// weight rows 64w .. 64w + 63 against the 128 tokens over the whole K, so each
+// operand byte from L2 feeds 128 or 256 outputs instead of the small tile's 64.  The
+// epilogues are the small tile's, fed one 16-token column (4 weight blocks) at a time.
+// Every output accumulates its k steps in order in one wave, which differs from the
+// small tile's four interleaved K partials; launch_* picks this kernel by the row
+// count alone (kWideMinRows), so a pass's results depend only on its shape.
+constexpr int kWideRB = 16, kWideTB = 8, kWideKT = 2;
+constexpr int kWideWSlots = 3, kWideXSlots = 2;
+constexpr int kWideWBytes = kWideRB * kWideKT * 1024, kWideXBytes = kWideTB * kWideKT * 1024;
+constexpr int kWideLds = kWideWSlots * kWideWBytes + kWideXSlots * kWideXBytes;
+constexpr int kWideWCopies = kWideRB * kWideKT / 4;   // per wave per step
+constexpr int kWideMinRows = 2048;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void dense_wide_gemm(DenseArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char ring[];
+  constexpr int WI = kWideRB / 4, NB = kWideTB;        // MFMA blocks per wave (rows x tokens)
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int n_row = (a.nblk + kWideRB - 1) / kWideRB, n_tok = (a.M + 16 * kWideTB - 1) / (16 * kWideTB);
+  // the token tiles of one weight tile take consecutive ranks on one XCD (shared weights in its L2)
+  const int b = blockIdx.x, rank = b / kXcd;
+  const int row_tile = (rank / n_tok) * kXcd + b % kXcd, tok_tile = rank % n_tok;
+  if (row_tile >= n_row) return;   // uniform per workgroup
+  const int rb0 = row_tile * kWideRB, tb0 = tok_tile * kWideTB;
+  const int mblocks = (a.M + 15) >> 4;
+  const int nk = a.K / (32 * kWideKT);
+  constexpr int WB = kWideRB / 4, XB = kWideTB / 4;
+  const uint16_t* wsrc[WB];
+  const uint16_t* xsrc[XB];
+  // blocks past the matrix re-read its last block (their outputs are dropped)
+#pragma unroll
+  for (int u = 0; u < WB; ++u) wsrc[u] = a.w + fm_tile(min(rb0 + wv * WB + u, a.nblk - 1), 0, a.K, lane);
+#pragma unroll
+  for (int u = 0; u < XB; ++u) xsrc[u] = a.x + fm_tile(min(tb0 + wv * XB + u, mblocks - 1), 0, a.K, lane);
+  char* const wring = ring;
+  char* const xring = ring + kWideWSlots * kWideWBytes;
+  auto issue_w = [&](int step) {
+    char* dst = wring + (step % kWideWSlots) * kWideWBytes + wv * WB * kWideKT * 1024;
+#pragma unroll
+    for (int u = 0; u < WB; ++u)
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t)
+        tile_to_lds<false>(wsrc[u] + (step * kWideKT + t) * 512, dst + (u * kWideKT + t) * 1024);
+  };
+  auto issue_x = [&](int step) {
+    char* dst = xring + (step % kWideXSlots) * kWideXBytes + wv * XB * kWideKT * 1024;
+#pragma unroll
+    for (int u = 0; u < XB; ++u)
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t)
+        tile_to_lds<false>(xsrc[u] + (step * kWideKT + t) * 512, dst + (u * kWideKT + t) * 1024);
+  };
+  lds_char* const lw = lds_launder(wring);
+  lds_char* const lx = lds_launder(xring);
+  f32x4 acc[WI][NB];
+#pragma unroll
+  for (int i = 0; i < WI; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Copy order: W(0), X(0), W(1), then after step s's barrier X(s + 1), W(s + 2).  At
+  // the top of step s the wave's copies of X(s) and W(s) have landed once at most the
+  // W(s + 1) batch that follows X(s) is in flight; the barrier then makes every wave's
+  // copies visible and retires all reads of the slots refilled next (they held step
+  // s - 1).
+  issue_w(0);
+  issue_x(0);
+  if (nk > 1) issue_w(1);
+  u32x4 A[WI][kWideKT], B[2][kWideKT];
+  for (int s = 0; s < nk; ++s) {
+    if (s + 1 < nk) vm_wait<kWideWCopies>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + 1 < nk) issue_x(s + 1);
+    if (s + 2 < nk) issue_w(s + 2);
+    const lds_char* sw = lw + (s % kWideWSlots) * kWideWBytes + lane * 16;
+    const lds_char* sx = lx + (s % kWideXSlots) * kWideXBytes + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t) A[i][t] = ld16_lds(sw + ((wv * WI + i) * kWideKT + t) * 1024);
+    auto readB = [&](int j) {
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t) B[j & 1][t] = ld16_lds(sx + (j * kWideKT + t) * 1024);
+    };
+    readB(0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j + 1 < NB) readB(j + 1);   // one token column ahead
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < WI; ++i) acc[i][j] = mfma16x2(A[i][0], B[j & 1][0], A[i][1], B[j & 1][1], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    f32x4 v[WI];
+#pragma unroll
+    for (int i = 0; i < WI; ++i) v[i] = acc[i][j];
+    epilogue<EPI, WI>(a, rb0 + wv * WI, (tb0 + j) * 16 + r, v, g);
+  }
+}
+
+template <int EPI>
+static void run_wide(const DenseArgs& a, hipStream_t s, hipEvent_t done = nullptr) {
+  static LdsLimit limit;   // the rings exceed the default dynamic-LDS limit
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&dense_wide_gemm<EPI>), kWideLds);
+  const int n_row = (a.nblk + kWideRB - 1) / kWideRB, n_tok = (a.M + 16 * kWideTB - 1) / (16 * kWideTB);
+  const int blocks = kXcd * ((n_row + kXcd - 1) / kXcd) * n_tok;
+  launch_kernel(dense_wide_gemm<EPI>, dim3(blocks), dim3(256), kWideLds, s, done, a);
+}
+
 template <int WN, int WM, int EPI, int NW = 4>
 static void run_dense(const DenseArgs& a, hipStream_t s, hipEvent_t done = nullptr) {
   const int n_tiles = (a.nblk + WN - 1) / WN, m_tiles = (a.M + 16 * WM - 1) / (16 * WM);
@@ -207,8 +324,14 @@ void launch_gemm_f32(const uint16_t* x, const uint16_t* w, float* y, int M, int 
   a.nblk = (N + 15) / 16;
   a.yf = y; a.ldy = N;
   // tile shapes measured at the 256-token canvas: narrow outputs (the router)
-  // want many small workgroups, wide ones 64 x 64 tiles
-  if (add) {
+  // want many small workgroups, wide ones 64 x 64 tiles; passes of many rows take
+  // the wide tile
+  if (N > 256 && M >= kWideMinRows) {
+    if (add)
+      run_wide<EPI_ADD_F32>(a, s, done);
+    else
+      run_wide<EPI_STORE_F32>(a, s, done);
+  } else if (add) {
     if (N <= 256)
       run_dense<1, 1, EPI_ADD_F32>(a, s, done);
     else
@@ -229,7 +352,10 @@ void launch_qkv_rope(const uint16_t* h, const uint16_t* w_qkv, int M, int K, int
   a.N = (hq + 2 * kv.hkv) * kv.hd;
   a.nblk = a.N / 16;
   a.hq = hq; a.hd = kv.hd; a.kv = kv; a.g = g; a.rope = rope_tab; a.q_out = q_out;
-  run_dense<4, 4, EPI_QKV>(a, s);
+  if (M >= kWideMinRows)
+    run_wide<EPI_QKV>(a, s);
+  else
+    run_dense<4, 4, EPI_QKV>(a, s);
 }
 
 void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int F, int K,
@@ -242,7 +368,10 @@ void launch_gemm_swiglu(const uint16_t* h, const uint16_t* w_gate_up, int M, int
   // registers per lane, which leaves room on every CU for the routing kernels and
   // the expert GEMMs that run beside this one (the 32-row tile at 232 registers put
   // two workgroups on each CU and took the registers those kernels need)
-  run_dense<4, 4, EPI_SWIGLU>(a, s);
+  if (M >= kWideMinRows)
+    run_wide<EPI_SWIGLU>(a, s);
+  else
+    run_dense<4, 4, EPI_SWIGLU>(a, s);
 }
 
 // ---------------------------------------------------------------- LM head

@@ -173,13 +173,15 @@ void launch_forced_route(const float* r, int M, int E, int k, const int32_t* for
 // perm[slot] = token (-1 on padding), inv[a] = slot; items lists the
 // (expert, first token) of every kMoeGroup-token group.
 //
-// Wave w owns the contiguous assignment range [w*per, (w+1)*per) and walks it 64 at
-// a time; the lanes holding one expert find each other by ballots on the id's bits,
-// which gives each assignment its rank among them.  A first walk counts every
-// expert per wave (no workgroup barrier inside the walk: each count is updated by
-// one lane of its wave), a one-wave prefix scan turns the totals into offsets, and
-// a second walk writes slot = offset of (wave, expert) + running rank.  The ids are
-// staged in LDS when they fit.
+// Wave w owns the contiguous assignment range [w*per, (w+1)*per).  A first walk
+// counts every expert per wave (LDS atomic additions: counts do not depend on their
+// order), a one-wave prefix scan turns the totals into offsets, a scan across the
+// waves gives each (wave, expert) its first slot, and a second walk, 64 assignments
+// at a time, writes slot = that slot + running rank, where the lanes holding one
+// expert find each other by ballots on the id's bits, which gives each assignment
+// its rank among them.  The ids are staged in LDS when at most CAP of them come
+// (sids: dynamic LDS the launch sizes to the ids, so a small batch holds little LDS
+// on the CU it shares with the concurrent shared-expert GEMM).
 template <int NW, int CAP>
 struct RouteLds {
   int base[256];
@@ -187,7 +189,6 @@ struct RouteLds {
   int ibase2[256];
   int tot[256];
   int wcnt[NW][256];
-  int ids[CAP];
 };
 
 // Lanes of this wave holding the same expert id e (8 bits; e < 0: no assignment):
@@ -210,7 +211,7 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
                             int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                             int2* __restrict__ items, int32_t* __restrict__ n_items,
                             int2* __restrict__ items2, int32_t* __restrict__ n_items2,
-                            int32_t* __restrict__ cnt_log, RouteLds<NW, CAP>& L) {
+                            int32_t* __restrict__ cnt_log, RouteLds<NW, CAP>& L, int* sids) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < NW * E; i += NT) L.wcnt[i / E][i % E] = 0;
@@ -224,18 +225,17 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
       if (tid + u * NT < A) v[u] = ids[tid + u * NT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (tid + u * NT < A) L.ids[tid + u * NT] = v[u];
+      if (tid + u * NT < A) sids[tid + u * NT] = v[u];
   }
   __syncthreads();
   const int per = ((A + NW - 1) / NW + 63) & ~63;
   const int w0 = min(A, wv * per), w1 = min(A, w0 + per);
-  auto id_at = [&](int a) { return a < w1 ? (staged ? L.ids[a] : ids[a]) : -1; };
+  auto id_at = [&](int a) { return a < w1 ? (staged ? sids[a] : ids[a]) : -1; };
   int* wc = L.wcnt[wv];
+  // per-wave histogram (counts only: the order of the LDS additions does not matter)
   for (int c = w0; c < w1; c += 64) {
     const int e = id_at(c + lane);
-    int rank, tot;
-    same_expert(e, lane, rank, tot);
-    if (e >= 0 && rank == tot - 1) wc[e] += tot;
+    if (e >= 0) atomicAdd(&wc[e], 1);
   }
   __syncthreads();
   if (wv == 0) {
@@ -293,13 +293,20 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
       int it2 = L.ibase2[e];
       for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup2) items2[it2++] = make_int2(e, t0);
     }
-    // per-wave running slot of expert e: its offset plus the earlier waves' counts
-    int run = L.base[e];
-    for (int w2 = 0; w2 < NW; ++w2) {
-      const int c = L.wcnt[w2][e];
-      L.wcnt[w2][e] = run;
-      run += c;
+  }
+  // per-wave running slot of expert e: its offset plus the earlier waves' counts, a
+  // scan over NW consecutive lanes (one lane group per expert, one lane per wave)
+  static_assert(NW <= 64 && (NW & (NW - 1)) == 0, "waves: a power of two");
+  for (int i0 = 0; i0 < E * NW; i0 += NT) {
+    const int i = i0 + tid, e = i / NW, w2 = i % NW;   // a lane group never straddles E * NW
+    const int c = i < E * NW ? L.wcnt[w2][e] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const int t = __shfl_up(incl, o, NW);
+      if (w2 >= o) incl += t;
     }
+    if (i < E * NW) L.wcnt[w2][e] = L.base[e] + incl - c;
   }
   __syncthreads();
   for (int c = w0; c < w1; c += 64) {
@@ -315,7 +322,7 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   }
 }
 
-constexpr int kRouteIds = 4096;   // ids staged in LDS (16 KiB)
+constexpr int kRouteIds = 16384;  // most ids staged in LDS (64 KiB: batch 8 of 256-token canvases, top-8)
 
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
@@ -328,15 +335,19 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ n_items2,
                                                      int32_t* __restrict__ cnt_log) {
   __shared__ RouteLds<16, kRouteIds> L;
+  extern __shared__ int sids[];   // A ids when A <= kRouteIds, else none
   route_block<16, kRouteIds>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log,
-                             L);
+                             L, sids);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int2* items2,
                   int32_t* n_items2, int32_t* cnt_log, hipStream_t s) {
-  launch_kernel(route_kernel, dim3(1), dim3(1024), 0, s, nullptr, ids, M * k, k, E, moe_max_slots(M, k, E),
-                cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
+  static LdsLimit limit;   // static part + up to 64 KiB of staged ids exceeds the default limit
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&route_kernel), kRouteIds * 4);
+  const int A = M * k, staged = A <= kRouteIds ? A : 0;
+  launch_kernel(route_kernel, dim3(1), dim3(1024), (size_t)staged * 4, s, nullptr, ids, A, k, E,
+                moe_max_slots(M, k, E), cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs

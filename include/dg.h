@@ -249,8 +249,11 @@ dg_status dg_generate_block(dg_ctx* ctx, dg_kv* kv, int32_t* d_canvas, int batch
  * (block j, causal, at len) write their keys/values before the attention of every
  * layer and the other rows (block j + 1's canvas, at len + C) attend to them.  Every
  * row's arithmetic is that of the separate passes, so canvases, logits and the KV
- * cache equal n_blocks calls of dg_generate_block(append_kv = 1) bit for bit (when
- * C > 256 or 2 * batch > DG_MAX_BATCH the passes stay separate).  The last block is
+ * cache equal n_blocks calls of dg_generate_block(append_kv = 1) bit for bit, as long
+ * as the fused pass (2 * batch * C rows) and the separate ones fall on the same side
+ * of 2048 rows, where the dense GEMMs change tile shape and with it their fp32
+ * summation order (always so for batch 1 and 2 at C = 256).  When C > 256 or
+ * 2 * batch > DG_MAX_BATCH the passes stay separate.  The last block is
  * appended by its own pass if append_last.  d_logits and d_n_masked as for
  * dg_generate_block (the last block's).  Errors: as dg_generate_block, and
  * DG_ERR_KV_CAPACITY when len + n_blocks * C exceeds max_ctx. */

@@ -24,7 +24,9 @@ def _bf16(shape, seed, scale=1.0):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4, 64), (37, 100, 128), (256, 4096, 2816), (300, 132, 704),
-                                   (16, 2816, 2112), (1024, 512, 256)])
+                                   (16, 2816, 2112), (1024, 512, 256),
+                                   # passes of >= 2048 rows take the wide tile (256 weight rows x 128 tokens)
+                                   (2048, 4096, 2816), (2100, 4224, 2816), (2200, 300, 192)])
 def test_gemm_matches_fp64(M, N, K):
     print(f"gemm M={M} N={N} K={K}", flush=True)
     x, w = _bf16((M, K), 1), _bf16((N, K), 2, 0.05)
@@ -336,7 +338,8 @@ def test_sampler_ragged_vocab_and_cross_chunk_ties():
 
 
 @pytest.mark.parametrize("M,E,k", [(256, 128, 8), (512, 128, 8), (33, 8, 2), (1000, 16, 3), (7, 4, 4),
-                                   (4096, 256, 16), (300, 100, 5), (257, 128, 16)])
+                                   (4096, 256, 16), (300, 100, 5), (257, 128, 16),
+                                   (2048, 128, 8), (1100, 128, 16)])   # 16384 ids: staged; 17600: not
 def test_routing_sort_bit_exact(M, E, k):
     """Top-k ids bit-exact vs the oracle; the counting sort is a stable, padded grouping."""
     print(f"route M={M} E={E} k={k}", flush=True)

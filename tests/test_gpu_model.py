@@ -98,6 +98,22 @@ def test_prefill_kv_matches_oracle(tiny):
     eng.close(); eng2.close(); eng3.close()
 
 
+def test_wide_tile_prefill_matches_oracle(tiny):
+    """A prefill pass of 4 x 512 rows runs its dense GEMMs on the wide tile (passes of
+    2048 rows or more): the QKV + RoPE epilogue writing K/V of every sequence, the
+    residual adds and the shared expert's SwiGLU and store.  Its K/V match the oracle's
+    as the small-tile passes do, routing teacher-forced."""
+    cfg, w_np, w_gpu, _ = tiny
+    print("tiny prefill of 4 x 512 tokens (wide-tile dense GEMMs)", flush=True)
+    prompt = synth.make_prompt(cfg, 4, 512, seed=23)
+    eng = dg.Engine(cfg, w_gpu, max_batch=4, max_ctx=576)
+    kv = _prefill_forced(eng, cfg, w_np, prompt)
+    assert eng.lengths[:4] == [512] * 4
+    for b in range(4):
+        _kv_compare(eng, kv, 0, 512, b=b, bref=b)
+    eng.close()
+
+
 def test_teacher_forced_steps(tiny):
     """Each step consumes the oracle's canvas and routing, so divergence cannot compound."""
     cfg, w_np, w_gpu, prompt = tiny
