@@ -179,9 +179,8 @@ void launch_forced_route(const float* r, int M, int E, int k, const int32_t* for
 // waves gives each (wave, expert) its first slot, and a second walk, 64 assignments
 // at a time, writes slot = that slot + running rank, where the lanes holding one
 // expert find each other by ballots on the id's bits, which gives each assignment
-// its rank among them.  The ids are staged in LDS when at most CAP of them come
-// (sids: dynamic LDS the launch sizes to the ids, so a small batch holds little LDS
-// on the CU it shares with the concurrent shared-expert GEMM).
+// its rank among them.  The ids are staged in LDS (sids) when at most CAP of them
+// come.
 template <int NW, int CAP>
 struct RouteLds {
   int base[256];
@@ -322,8 +321,14 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   }
 }
 
-constexpr int kRouteIds = 16384;  // most ids staged in LDS (64 KiB: batch 8 of 256-token canvases, top-8)
+// Ids staged in LDS: up to kRouteIdsSmall in a static array (a batch-1 canvas: 2048),
+// up to kRouteIds in dynamic LDS sized to the launch (batch 8 of 256-token canvases,
+// top-8: 64 KiB), beyond that read from memory.  The small kernel keeps the staging
+// loop short and holds little LDS on the CU it shares with the side stream's
+// shared-expert GEMM.
+constexpr int kRouteIdsSmall = 4096, kRouteIds = 16384;
 
+template <int CAP>
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ poff,
@@ -334,20 +339,28 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int2* __restrict__ items2,
                                                      int32_t* __restrict__ n_items2,
                                                      int32_t* __restrict__ cnt_log) {
-  __shared__ RouteLds<16, kRouteIds> L;
-  extern __shared__ int sids[];   // A ids when A <= kRouteIds, else none
-  route_block<16, kRouteIds>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log,
-                             L, sids);
+  constexpr bool kStatic = CAP <= kRouteIdsSmall;
+  __shared__ RouteLds<16, CAP> L;
+  __shared__ int st_ids[kStatic ? CAP : 1];
+  extern __shared__ int dyn_ids[];   // the large kernel: A ids when A <= CAP, else none
+  route_block<16, CAP>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log,
+                       L, kStatic ? st_ids : dyn_ids);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int2* items2,
                   int32_t* n_items2, int32_t* cnt_log, hipStream_t s) {
+  const int A = M * k, P = moe_max_slots(M, k, E);
+  if (A <= kRouteIdsSmall) {
+    launch_kernel(route_kernel<kRouteIdsSmall>, dim3(1), dim3(1024), 0, s, nullptr, ids, A, k, E, P, cnt, poff,
+                  perm, inv, items, n_items, items2, n_items2, cnt_log);
+    return;
+  }
   static LdsLimit limit;   // static part + up to 64 KiB of staged ids exceeds the default limit
-  raise_lds_limit(limit, reinterpret_cast<const void*>(&route_kernel), kRouteIds * 4);
-  const int A = M * k, staged = A <= kRouteIds ? A : 0;
-  launch_kernel(route_kernel, dim3(1), dim3(1024), (size_t)staged * 4, s, nullptr, ids, A, k, E,
-                moe_max_slots(M, k, E), cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&route_kernel<kRouteIds>), kRouteIds * 4);
+  const int staged = A <= kRouteIds ? A : 0;
+  launch_kernel(route_kernel<kRouteIds>, dim3(1), dim3(1024), (size_t)staged * 4, s, nullptr, ids, A, k, E, P,
+                cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
