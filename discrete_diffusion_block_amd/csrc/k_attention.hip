@@ -49,8 +49,8 @@ struct AttnArgs {
 
 constexpr int kAttnStageKeys = 64;
 
-template <int HD, int NWV>
-__global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
+template <int HD, int NWV, int RING>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a) {
   constexpr int NC = HD / 32;                 // k-steps of the score MFMA
   constexpr int NB = HD / 16;                 // 16-row output blocks of hd
   constexpr int KCH = 2 * NC * 1024;          // bytes of one 32-key K chunk (2 key blocks x NC tiles)
@@ -58,7 +58,8 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
   constexpr int STAGE = 2 * (KCH + VCH);      // one 64-key stage: K chunk 0, K chunk 1, V chunk 0, V chunk 1
   constexpr int COPIES = STAGE / 1024 / NWV;  // 1 KiB copies per wave per stage
   static_assert(STAGE % (1024 * NWV) == 0, "whole copies per wave");
-  extern __shared__ __attribute__((aligned(1024))) char ring[];   // [2][STAGE]
+  static_assert(RING == 2 || RING == 3, "stages in the ring");
+  extern __shared__ __attribute__((aligned(1024))) char ring[];   // [RING][STAGE]
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,12 +159,20 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
   const float scale = 1.4426950408889634f / sqrtf((float)HD);   // softmax in log2 units
   lds_char* const lr = lds_launder(ring);
 
-  if (s_begin < s_end) issue(s_begin, 0);
+  // RING - 1 stages in flight: stage st is copied RING - 1 iterations ahead of its use.
+  // At the top of iteration st the wave's later copies are those of the stages after
+  // st already issued (at most RING - 2 of them); waiting until only they remain lands
+  // stage st, and the barrier makes every wave's copies visible and retires all reads
+  // of the slot refilled next (stage st - 1's).
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j)
+    if (s_begin + j < s_end) issue(s_begin + j, j);
   for (int st = s_begin; st < s_end; ++st) {
-    const int slot = (st - s_begin) & 1;
-    vm_wait<0>();
-    __builtin_amdgcn_s_barrier();             // stage st visible; stage st - 1's slot free
-    if (st + 1 < s_end) issue(st + 1, slot ^ 1);
+    const int slot = (st - s_begin) % RING;
+    if (RING == 3 && st + 1 < s_end) vm_wait<COPIES>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (st + RING - 1 < s_end) issue(st + RING - 1, (st + RING - 1 - s_begin) % RING);
     if (!active) continue;
     const lds_char* sk = lr + slot * STAGE + lane * 16;
     const lds_char* sv = sk + 2 * KCH;
@@ -201,19 +210,24 @@ __global__ __launch_bounds__(64 * NWV) void attention_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float v = s[qb][ch][e >> 2][e & 3] * scale;
           const int key = kc0 + 32 * ch + 8 * gq + e;
-          const float x = (nomask || (key >= lo_q[qb] && key < hi_q[qb])) ? v : -INFINITY;
+          // branch-free: a select per key, no short-circuit control flow
+          const bool vis = nomask | ((key >= lo_q[qb]) & (key < hi_q[qb]));
+          const float x = vis ? v : -INFINITY;
           sv16[8 * ch + e] = x;
           cmax = fmaxf(cmax, x);
         }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
       const float m_new = fmaxf(m_run[qb], cmax);
-      alpha[qb] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[qb] - m_new);
+      // v_exp_f32 directly (results below 2^-126 flush to zero; exp2(-inf) = 0, so a
+      // masked key needs no select once the subtracted max is finite)
+      const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[qb] = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
       float p[16];
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = (sv16[e] == -INFINITY) ? 0.f : exp2f(sv16[e] - m_new);
+        p[e] = __builtin_amdgcn_exp2f(sv16[e] - m_sub);
         ps += p[e];
       }
       l_part[qb] = l_part[qb] * alpha[qb] + ps;
@@ -343,12 +357,12 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const float* __res
   *reinterpret_cast<u32x4*>(o + fm_index(m, head * HD + c8, hq * HD)) = out;
 }
 
-template <int HD, int NWV>
-static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
-                          float* part_o, float2* part_ml, hipStream_t s) {
+template <int HD, int NWV, int RING>
+static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, int max_keys,
+                          uint16_t* o, float* part_o, float2* part_ml, hipStream_t s) {
   constexpr int STAGE = 2 * (2 * (HD / 32) * 1024 + (HD / 16) * 1024);
   static LdsLimit limit;
-  raise_lds_limit(limit, reinterpret_cast<const void*>(&attention_kernel<HD, NWV>), 2 * STAGE);
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&attention_kernel<HD, NWV, RING>), RING * STAGE);
   AttnArgs a{};
   a.q = q; a.o = o; a.part_o = part_o; a.part_ml = part_ml;
   a.kv = kv; a.g = g; a.hq = hq;
@@ -359,12 +373,6 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   const int base_wgs = pairs * a.wg_per_pair;
   // split the key range when the pairs alone leave CUs idle: aim at ~2 workgroups per
   // CU, keep at least two 64-key stages per split, and stay within the partial buffer
-  int max_keys = 0;
-  for (int bb = 0; bb < g.batch; ++bb) {
-    const int keys = !seq_encodes(g, bb) ? (kv.window > 0 ? min(g.len[bb], kv.window) : g.len[bb]) + g.n
-                               : (kv.window > 0 ? min(g.len[bb] + g.n, kv.window + 63) : g.len[bb] + g.n);
-    max_keys = max(max_keys, keys);
-  }
   const int stages = (max_keys + kAttnStageKeys - 1) / kAttnStageKeys + 1;
   int nsplit = (512 + base_wgs - 1) / base_wgs;
   nsplit = min(nsplit, max(1, stages / 2));
@@ -374,7 +382,7 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   a.nsplit = max(1, nsplit);
   const long units = (long)base_wgs * a.nsplit;
   const int blocks = (int)(kXcd * ((units + kXcd - 1) / kXcd));
-  launch_kernel(attention_kernel<HD, NWV>, dim3(blocks), dim3(64 * NWV), 2 * STAGE, s, nullptr, a);
+  launch_kernel(attention_kernel<HD, NWV, RING>, dim3(blocks), dim3(64 * NWV), RING * STAGE, s, nullptr, a);
   if (a.nsplit > 1) {
     const long threads = (long)g.batch * hq * g.n * (HD / 8);
     launch_kernel(attention_merge_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, nullptr,
@@ -382,12 +390,32 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   }
 }
 
+// Long key ranges (global layers over a long prefix) take their own workgroup shape.
+constexpr int kAttnLongKeys = 4096, kAttnWavesLong = 4, kAttnRingLong = 2;
+
 void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
                       float* part_o, float2* part_ml, hipStream_t s) {
+  int max_keys = 0;   // the longest key range of any sequence of the pass
+  for (int bb = 0; bb < g.batch; ++bb) {
+    const int keys = !seq_encodes(g, bb) ? (kv.window > 0 ? min(g.len[bb], kv.window) : g.len[bb]) + g.n
+                               : (kv.window > 0 ? min(g.len[bb] + g.n, kv.window + 63) : g.len[bb] + g.n);
+    max_keys = max(max_keys, keys);
+  }
+  constexpr int NWL = kAttnWavesLong, RL = kAttnRingLong;
+  const bool lng = max_keys >= kAttnLongKeys;
   switch (kv.hd) {
-    case 32: run_attention<32, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
-    case 64: run_attention<64, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
-    default: run_attention<128, 4>(q, hq, kv, g, o, part_o, part_ml, s); break;
+    case 32:
+      if (lng) run_attention<32, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      else run_attention<32, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      break;
+    case 64:
+      if (lng) run_attention<64, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      else run_attention<64, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      break;
+    default:
+      if (lng) run_attention<128, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      else run_attention<128, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      break;
   }
 }
 
