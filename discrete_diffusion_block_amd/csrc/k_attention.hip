@@ -390,8 +390,10 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   }
 }
 
-// Long key ranges (global layers over a long prefix) take their own workgroup shape.
-constexpr int kAttnLongKeys = 4096, kAttnWavesLong = 4, kAttnRingLong = 2;
+// Long key ranges (global layers over a long prefix) take their own workgroup shape:
+// 8 waves share each K/V stage (half the copies per query) and the ring holds three
+// stages, so each copy is issued two stages ahead of its use.
+constexpr int kAttnLongKeys = 4096, kAttnWavesLong = 8, kAttnRingLong = 3;
 
 void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
                       float* part_o, float2* part_ml, hipStream_t s) {

@@ -60,11 +60,24 @@ def _kv_compare(eng, kv_ref, lo, hi, b=0, bref=0):
             assert np.abs(d).max() <= KV_ABS, float(np.abs(d).max())
 
 
+PREFILL_CHUNK = 512   # the library's prefill pass length: forced ids are indexed per pass
+
+
 def _prefill_forced(eng, cfg, w_np, prompt):
-    """Oracle prefill (with its trace), then the engine's prefill routed like it."""
+    """Oracle prefill (with its trace), then the engine's prefill routed like it.  A
+    single-sequence prompt longer than one prefill pass goes in pass-sized calls, each
+    forced with its own tokens' expert ids."""
     kv = O.KVCache(cfg, prompt.shape[0])
     tr = [[] for _ in range(prompt.shape[0])]
     O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
+    n = prompt.shape[1]
+    if prompt.shape[0] == 1 and n > PREFILL_CHUNK:
+        for s0 in range(0, n, PREFILL_CHUNK):
+            s1 = min(n, s0 + PREFILL_CHUNK)
+            with forced_routing(eng, forced_ids(tr, cfg.n_layers, s0, s1)):
+                eng.prefill_kv(prompt[:, s0:s1].contiguous().cuda())
+        return kv
+    assert n <= PREFILL_CHUNK, "one forced pass per call"
     with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
         eng.prefill_kv(prompt.cuda())
     return kv
@@ -263,6 +276,32 @@ def test_short_window_and_global_layers(tiny, global_every):
     with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
         eng.denoise_step(canvas.cuda(), 0.7, logits)
     err = np.abs(to_np_bf16(logits)[0] - ref[0]).max()
+    assert err <= LOGIT_TOL, err
+    eng.close()
+
+
+def test_long_prefix_global_layer(tiny):
+    """A 4200-token prompt with layer 1 global (layer 0: a 24-token window): the later
+    prefill chunks (causal) and the denoising pass attend over more than 4096 keys on
+    the global layer, which takes the long-range attention shape (8 waves sharing each
+    K/V stage, a three-stage ring).  K/V after prefill and the logits of one denoising
+    step against the oracle."""
+    cfg0, w_np, w_gpu, _ = tiny
+    cfg = dataclasses.replace(cfg0, window=24, global_every=2)
+    V, C = cfg.vocab, cfg.canvas
+    print("tiny, 4200-token prompt, layer 1 global", flush=True)
+    prompt = synth.make_prompt(cfg, 1, 4200, seed=31)
+    eng = dg.Engine(cfg, w_gpu, max_batch=1, max_ctx=4288)
+    kv = _prefill_forced(eng, cfg, w_np, prompt)
+    _kv_compare(eng, kv, 0, 4200)
+    canvas = synth.make_masked_canvas(C, V, 20, seed=3).reshape(1, C)
+    tr = [[]]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), 0.7, trace=tr)
+    logits = torch.empty(1, C, V, dtype=torch.bfloat16, device="cuda")
+    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+        eng.denoise_step(canvas.cuda(), 0.7, logits)
+    err = np.abs(to_np_bf16(logits)[0] - ref[0]).max()
+    print(f"  max |logit delta| {err:.2e}", flush=True)
     assert err <= LOGIT_TOL, err
     eng.close()
 
