@@ -9,11 +9,11 @@
 //
 // Work split.  A workgroup serves one (sequence, kv head) pair: NWV waves, each
 // owning 32 query rows (two 16-row MFMA blocks) of one q head of the pair's GQA
-// group, so the workgroup covers both q heads of a group and 64 queries of each.
-// Keys stream through LDS in 64-key stages (K and transposed V, copied straight
-// from the cache's fragment tiles into a two-stage ring by direct global->LDS
-// loads, one copy per workgroup) and every wave reads each stage: one K/V byte
-// from L2 feeds 128 query rows.  When the pairs alone give too few workgroups to
+// group (4 waves: both q heads of a group, 64 queries of each; 8 waves for long key
+// ranges).  Keys stream through LDS in 64-key stages (K and transposed V, copied
+// straight from the cache's fragment tiles into a RING-stage ring by direct
+// global->LDS loads, one copy per workgroup) and every wave reads each stage: one
+// K/V byte from L2 feeds 32 * NWV query rows.  When the pairs alone give too few workgroups to
 // fill the chip, the key range of each pair is split over several workgroups
 // (split-KV); each writes its unnormalised partial (max, sum, output) and a merge
 // kernel combines the splits in a fixed order.
