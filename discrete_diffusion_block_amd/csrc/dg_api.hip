@@ -1396,4 +1396,18 @@ dg_status dg_test_copy(const void* d_src, void* d_dst, size_t n_bytes, void* str
   return check_launch("copy");
 }
 
+dg_status dg_test_mfma_rate(int blocks, int iters, float* d_out, void* stream) {
+  if (!d_out || blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20))
+    return fail(DG_ERR_INVALID_ARG, "rate test needs 1..65536 blocks, 1..2^20 rounds and an output buffer");
+  launch_mfma_rate(blocks, iters, d_out, (hipStream_t)stream);
+  return check_launch("mfma rate");
+}
+
+dg_status dg_test_read_rate(const void* d_src, size_t n_bytes, int blocks, uint32_t* d_out, void* stream) {
+  if (!d_src || !d_out || n_bytes == 0 || n_bytes % 16 || blocks < 1 || blocks > 65536)
+    return fail(DG_ERR_INVALID_ARG, "read test needs buffers, a positive multiple of 16 bytes and 1..65536 blocks");
+  launch_read_rate(d_src, n_bytes, blocks, d_out, (hipStream_t)stream);
+  return check_launch("read rate");
+}
+
 }  // extern "C"

@@ -215,6 +215,10 @@ void launch_sc_embed(const uint16_t* logits, const float2* stats, const uint16_t
 void launch_sc_reduce(const float* part, int nsplit, const float2* stats, int M, int N, uint16_t* u_fm,
                       float* u_out, hipStream_t s);
 void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s);
+// blocks x 256 threads, iters rounds of 4 dependent MFMA pairs per wave; out: blocks * 256 floats
+void launch_mfma_rate(int blocks, int iters, float* out, hipStream_t s);
+// streaming read of n_bytes (multiple of 16) by blocks x 256 threads; out: blocks * 256 words
+void launch_read_rate(const void* src, size_t n_bytes, int blocks, uint32_t* out, hipStream_t s);
 // A per-sequence element offset, passed by value.
 struct SeqOffsets {
   int64_t v[DG_MAX_BATCH];

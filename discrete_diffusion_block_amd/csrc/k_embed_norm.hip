@@ -264,6 +264,57 @@ void launch_copy16(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
                 reinterpret_cast<u32x4*>(dst), n);
 }
 
+// Achievable bf16 MFMA rate: each wave runs iters rounds over kRateChains independent
+// accumulators, each round one dependent pair of v_mfma_f32_16x16x32_bf16 per
+// accumulator (the order in which this core issues MFMAs at full rate, as the GEMMs
+// do), on register operands (all ones: every element gains 32 per MFMA), with no
+// memory traffic; then each lane writes the sum of its accumulators --
+// kRateChains * 4 * 64 * iters exactly while that stays below 2^24 -- so the work
+// cannot be dropped and its count can be checked.
+constexpr int kRateChains = 4;
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* __restrict__ out) {
+  const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
+  const u32x4 a = {one2, one2, one2, one2};
+  f32x4 acc[kRateChains];
+#pragma unroll
+  for (int c = 0; c < kRateChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kRateChains; ++c) acc[c] = mfma16x2(a, a, a, a, acc[c]);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRateChains; ++c) sum += (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+void launch_mfma_rate(int blocks, int iters, float* out, hipStream_t s) {
+  launch_kernel(mfma_rate_kernel, dim3(blocks), dim3(256), 0, s, nullptr, iters, out);
+}
+
+// Achievable HBM read rate: thread t of the grid XORs the 16-byte words t, t + S,
+// t + 2S, ... (S = the grid's thread count) of src, four loads in flight per step, and
+// writes the first 32-bit lane of its XOR to out[t] (a checkable result: src filled
+// with one repeated word w gives w where the thread read an odd number of words).
+__global__ __launch_bounds__(256) void read_rate_kernel(const u32x4* __restrict__ src, size_t n,
+                                                        uint32_t* __restrict__ out) {
+  const size_t S = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t t = i;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (; i + 3 * S < n; i += 4 * S) {
+    const u32x4 a = src[i], b = src[i + S], c = src[i + 2 * S], d = src[i + 3 * S];
+    x ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n; i += S) x ^= src[i];
+  out[t] = x.x;
+}
+
+void launch_read_rate(const void* src, size_t n_bytes, int blocks, uint32_t* out, hipStream_t s) {
+  launch_kernel(read_rate_kernel, dim3(blocks), dim3(256), 0, s, nullptr, reinterpret_cast<const u32x4*>(src),
+                n_bytes / 16, out);
+}
+
 void launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
   launch_kernel(fill_i32_kernel, dim3(blocks), dim3(256), 0, s, nullptr, p, v, n);

@@ -109,6 +109,8 @@ def lib():
             "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
             "dg_test_copy": [vp, vp, C.c_size_t, vp],
+            "dg_test_mfma_rate": [i32, i32, vp, vp],
+            "dg_test_read_rate": [vp, C.c_size_t, i32, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -475,6 +477,19 @@ def dg_test_eb_select(entropy: torch.Tensor, argmax: torch.Tensor, canvas: torch
 def dg_test_copy(src: torch.Tensor, dst: torch.Tensor, n_bytes: int, stream=None) -> None:
     """Plain 16-byte-vector device copy (hardware byte-counter calibration)."""
     _check(lib().dg_test_copy(_p(src), _p(dst), n_bytes, _stream(stream)))
+
+
+def dg_test_mfma_rate(blocks: int, iters: int, out: torch.Tensor, stream=None) -> None:
+    """Register-only bf16 MFMA chains (achievable matrix-core rate); out: float32 [blocks * 256]."""
+    assert out.dtype == torch.float32 and out.numel() >= blocks * 256 and out.is_cuda
+    _check(lib().dg_test_mfma_rate(blocks, iters, _p(out), _stream(stream)))
+
+
+def dg_test_read_rate(src: torch.Tensor, n_bytes: int, blocks: int, out: torch.Tensor, stream=None) -> None:
+    """Streaming read of src (achievable HBM read rate); out: int32 [blocks * 256] (XOR words)."""
+    assert src.is_cuda and src.numel() * src.element_size() >= n_bytes
+    assert out.is_cuda and out.element_size() == 4 and out.numel() >= blocks * 256
+    _check(lib().dg_test_read_rate(_p(src), n_bytes, blocks, _p(out), _stream(stream)))
 
 
 def dg_test_gemm(x_packed: torch.Tensor, w_packed: torch.Tensor, y: torch.Tensor, M: int, N: int,

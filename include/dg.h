@@ -483,6 +483,23 @@ dg_status dg_test_gemm(const uint16_t* d_x, const uint16_t* d_w, float* d_y, int
  * hardware byte counters against which the other kernels are measured. */
 dg_status dg_test_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream);
 
+/* Achievable bf16 matrix-core rate, for reporting measured peaks beside the vendor
+ * figures: `blocks` workgroups of 256 threads; each wave issues `iters` rounds of 8
+ * v_mfma_f32_16x16x32_bf16 (16384 flop each; a dependent pair on each of 4
+ * accumulators) on register operands and touches no memory until it writes
+ * d_out[blocks * 256] (float, caller-owned): per lane 4 * 4 * 64 * iters, exact for
+ * iters < 2^14.  Work = blocks * 4 * 8 * iters * 16384 flop.  Errors: DG_ERR_INVALID_ARG for blocks outside 1..65536, iters outside
+ * 1..2^20 or a NULL d_out. */
+dg_status dg_test_mfma_rate(int blocks, int iters, float* d_out, void* stream);
+
+/* Achievable HBM read rate, for the same report: `blocks` workgroups of 256 threads
+ * stream d_src (n_bytes, a positive multiple of 16; caller-owned) once, thread t
+ * reading the 16-byte words t, t + S, t + 2S, ... (S = blocks * 256) four at a time,
+ * and write the first 32-bit lane of their XOR to d_out[t] (uint32 [blocks * 256],
+ * caller-owned).  Errors: DG_ERR_INVALID_ARG for NULL buffers, a byte count that is
+ * zero or not a multiple of 16, or blocks outside 1..65536. */
+dg_status dg_test_read_rate(const void* d_src, size_t n_bytes, int blocks, uint32_t* d_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

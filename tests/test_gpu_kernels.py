@@ -418,3 +418,33 @@ def test_sampler_adaptive_stop_vs_oracle():
     assert np.max(np.abs(Hg[1][masked1] - Ho)) <= 2e-5
     np.testing.assert_array_equal(d_prev.cpu().numpy(), am.cpu().numpy())   # this step's argmax, -1 elsewhere
     np.testing.assert_array_equal(am.cpu().numpy(), ref_a)
+
+
+def test_mfma_rate_tap_counts_its_work():
+    """The matrix-core rate tap runs every MFMA it is asked for: all-ones operands add 32
+    per MFMA to each accumulator element, two MFMAs per accumulator per round, so each
+    lane's checksum is 4 accumulators x 4 elements x 64 x rounds, exactly."""
+    print("mfma rate tap", flush=True)
+    for blocks, iters in ((3, 1), (37, 1000)):
+        out = torch.full((blocks * 256,), -1.0, device="cuda")
+        dg.dg_test_mfma_rate(blocks, iters, out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 4 * 4 * 64 * iters), (blocks, iters, out.unique()[:4].tolist())
+
+
+def test_read_rate_tap_reads_every_word():
+    """The streaming-read tap visits every 16-byte word once: with src one repeated
+    word, thread t's XOR is that word when it read an odd number of words (t, t + S,
+    ... below n), else zero."""
+    print("read rate tap", flush=True)
+    for blocks, nwords in ((2, 3000), (5, 1280), (3, 7)):
+        w = 0x5A17C3E1
+        src = torch.full((nwords * 4,), w, dtype=torch.int32, device="cuda")
+        out = torch.full((blocks * 256,), -1, dtype=torch.int32, device="cuda")
+        dg.dg_test_read_rate(src, nwords * 16, blocks, out)
+        torch.cuda.synchronize()
+        S = blocks * 256
+        t = np.arange(S)
+        reads = np.maximum(0, (nwords - t + S - 1) // S)
+        want = np.where(reads % 2 == 1, w, 0).astype(np.int32)
+        np.testing.assert_array_equal(out.cpu().numpy(), want)
