@@ -943,7 +943,12 @@ def main():
         if (t.get("kernel") == dom and dom in KIND_SOURCES
                 and t.get("source_digest") == kernel_source_digest(dom)):
             traffic = t.get("bytes_per_launch")
+    log("achievable peaks (streaming read, copy, register-only MFMA)...")
+    peaks = achievable_peaks()
+    ceiling = peaks["hbm_read_gbs"] if unit == "GB/s" else peaks["mfma_bf16_tflops"]
     roofline = roofline_obj(bound, unit, avg_ms, amount, dom_launches, dom, traffic)
+    roofline["measured_ceiling"] = ceiling
+    roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceiling, 4)
     if not used:
         used = [sum(1 for c in row if c > 0) for row in eng.moe_counts().cpu().tolist()]
     experts = round(sum(used) / len(used), 1)
@@ -1001,8 +1006,7 @@ def main():
         "cpu_baseline": None,
         "achievable_peaks": None,
     }
-    log("achievable peaks (copy, register-only MFMA)...")
-    out["achievable_peaks"] = achievable_peaks()
+    out["achievable_peaks"] = peaks
     if not args.no_extras:
         log("sampler on rotating buffers...")
         out["sampler_roofline"] = sampler_roofline(eng, cfg, args.gamma)
