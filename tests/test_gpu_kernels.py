@@ -341,12 +341,17 @@ def test_sampler_ragged_vocab_and_cross_chunk_ties():
                                    (4096, 256, 16), (300, 100, 5), (257, 128, 16),
                                    (2048, 128, 8), (1100, 128, 16)])   # ids: up to 4096 staged in static LDS; 4112, 16384 in dynamic LDS; 17600, 65536 read from memory
 def test_routing_sort_bit_exact(M, E, k):
-    """Top-k ids bit-exact vs the oracle; the counting sort is a stable, padded grouping."""
+    """Top-k ids bit-exact vs the oracle (ties, signed zeros, -inf and NaN rows among
+    them); the counting sort is a stable, padded grouping."""
     print(f"route M={M} E={E} k={k}", flush=True)
     g = torch.Generator().manual_seed(M + E)
     r = torch.randn(M, E, generator=g)
     r[::2] = torch.round(r[::2] * 2) / 2                    # exact ties
     r[5:40] = r[5]                                           # identical rows: all route alike
+    r[1] = 0.0                                               # a row of all-equal logits
+    r[2, ::2] = -0.0                                         # signed zeros tie with +0
+    r[3, : E // 2] = float("-inf")
+    r[4, :5] = float("nan")                                  # NaN ranks as -inf
     out = {k2: v.cpu() for k2, v in dg.dg_test_route(r.cuda(), k).items()}
     ref_ids, ref_w = O.router_topk(r.double().numpy(), k)
     np.testing.assert_array_equal(out["ids"].numpy(), ref_ids)
