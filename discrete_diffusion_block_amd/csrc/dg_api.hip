@@ -1358,14 +1358,15 @@ dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_
 
 dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
                         int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
-                        int32_t* d_items, int32_t* d_n_items, void* stream) {
+                        int32_t* d_items, int32_t* d_n_items, int32_t* d_items2, int32_t* d_n_items2,
+                        void* stream) {
   if (!d_r || !d_ids || !d_w || !d_cnt || !d_poff || !d_perm || !d_inv || !d_items || !d_n_items ||
-      M < 1 || E < 4 || E > 256 || E % 4 || k < 1 || k > 16 || k > E)
+      !d_items2 || !d_n_items2 || M < 1 || E < 4 || E > 256 || E % 4 || k < 1 || k > 16 || k > E)
     return fail(DG_ERR_INVALID_ARG, "bad routing arguments");
   hipStream_t s = (hipStream_t)stream;
   launch_topk(d_r, M, E, k, d_ids, d_w, s);
   launch_route(d_ids, M, k, E, d_cnt, d_poff, d_perm, d_inv, reinterpret_cast<int2*>(d_items), d_n_items,
-               nullptr, nullptr, nullptr, s);
+               reinterpret_cast<int2*>(d_items2), d_n_items2, nullptr, s);
   return check_launch("route");
 }
 

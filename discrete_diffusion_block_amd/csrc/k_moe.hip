@@ -289,8 +289,14 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
     int it = L.ibase[e];
     for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup) items[it++] = make_int2(e, t0);
     if (items2) {
+      // the expert's 16-token blocks dealt into its items as evenly as they go (at
+      // most kMoeGroup2 tokens each); .y packs the item's token range [t0, t1)
+      const int c = L.tot[e], ni = (c + kMoeGroup2 - 1) / kMoeGroup2, nb = (c + 15) >> 4;
       int it2 = L.ibase2[e];
-      for (int t0 = 0; t0 < L.tot[e]; t0 += kMoeGroup2) items2[it2++] = make_int2(e, t0);
+      for (int i = 0; i < ni; ++i) {
+        const int b0 = i * nb / ni, b1 = (i + 1) * nb / ni;
+        items2[it2++] = make_int2(e, 16 * b0 | min(c, 16 * b1) << 16);
+      }
     }
   }
   // per-wave running slot of expert e: its offset plus the earlier waves' counts, a
@@ -367,9 +373,11 @@ void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
-// Grouped expert GEMMs.  A workgroup owns one work item (expert e and a group of
-// its tokens: up to kMoeGroup2 = 128 for the gate/up GEMM, kMoeGroup = 64 for the
-// down GEMM) and a tile of output features.  The gate/up GEMM (K = d_model) stages
+// Grouped expert GEMMs.  A workgroup owns one work item (expert e and a range of
+// up to kMoeGroup2 = 128 of its tokens: an expert's 16-token blocks are dealt evenly
+// into its items, so 146 tokens make items of 80 and 66 rather than 128 and 18, and
+// no workgroup streams a weight tile for a handful of tokens) and a tile of output
+// features.  The gate/up GEMM (K = d_model) stages
 // weight and token fragment tiles through LDS rings by direct global->LDS copies
 // and computes a 128-row x 128-token tile; the down GEMM
 // (K = F, short) gives each wave 32 output rows over the whole K loop, with its
@@ -422,11 +430,11 @@ static_assert(kMoeGroup2 == 16 * kGuTB, "one token block per wave");
 
 template <bool STREAM>
 __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const uint16_t* h_rm,
-                                                 const int32_t* perm, int slot0, int t0, int ne, int F,
+                                                 const int32_t* perm, int slot0, int t0, int t1, int F,
                                                  int f0, int d, int lane, int wv, uint16_t* A,
                                                  char* ring) {
   constexpr int WI = 4, WJ = 2;                      // MFMA blocks per wave (rows x tokens)
-  const int ntb = min(kGuTB, (ne - t0 + 15) >> 4);   // token blocks of this item (>= 1)
+  const int ntb = min(kGuTB, (t1 - t0 + 15) >> 4);   // token blocks of this item [t0, t1) (>= 1)
   const int nk = d / (32 * kGuKT);
   const bool has_x = wv < ntb;                       // this wave copies a token block
   const uint16_t* wsrc = wgu_e + fm_tile(2 * f0 + wv, 0, d, lane);
@@ -524,7 +532,7 @@ __device__ __forceinline__ void gate_up_tile_lds(const uint16_t* wgu_e, const ui
   for (int j = 0; j < WJ; ++j) {
     const int tb = wt * WJ + j;
     const int t = t0 + 16 * tb + r;
-    if (tb >= ntb || t >= ne) continue;
+    if (tb >= ntb || t >= t1) continue;
 #pragma unroll
     for (int i = 0; i < WI; i += 2) {
       const f32x4 G = acc[i][j], U = acc[i + 1][j];
@@ -551,14 +559,14 @@ __global__ __launch_bounds__(64 * kGuWaves) void moe_gate_up_kernel(const uint16
   int item, fb;
   if (!xcd_item_schedule(*n_items, F / (16 * kGuRB / 2), &item, &fb)) return;
   const int2 it = items[item];
-  const int e = it.x, t0 = it.y;
-  const int ne = cnt[e], slot0 = poff[e] + t0;
+  const int e = it.x, t0 = it.y & 0xffff, t1 = it.y >> 16;
+  const int slot0 = poff[e] + t0;
   const uint16_t* wgu_e = wgu + (size_t)e * 2 * F * d;
   // an expert with a single work item streams its weights (read by no other item)
-  if (ne <= kMoeGroup2)
-    gate_up_tile_lds<true>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+  if (cnt[e] <= kMoeGroup2)
+    gate_up_tile_lds<true>(wgu_e, h_rm, perm, slot0, t0, t1, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
   else
-    gate_up_tile_lds<false>(wgu_e, h_rm, perm, slot0, t0, ne, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
+    gate_up_tile_lds<false>(wgu_e, h_rm, perm, slot0, t0, t1, F, fb * (kGuRB / 2), d, lane, wv, A, ring);
 }
 
 void launch_moe_gate_up(const uint16_t* h_rm, const int32_t* perm, const uint16_t* w_gate_up,
@@ -585,7 +593,7 @@ static_assert(kMoeGroup2 == 128, "eight token blocks per down work item");
 
 template <bool STREAM, int NT>
 __device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* A, int slot0, int t0,
-                                          int ne, int F, int d, int n0, int lane, int wv, float* Y,
+                                          int t1, int F, int d, int n0, int lane, int wv, float* Y,
                                           char* ring) {
   const int nblk = d >> 4;
   const int nk = F / (32 * kGuKT);                // >= 1 (F % 64 == 0)
@@ -659,7 +667,7 @@ __device__ __forceinline__ void down_tile(const uint16_t* wd_e, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int t = t0 + 16 * j + rr;
-    if (t >= ne) continue;
+    if (t >= t1) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if (rb0 + i < nblk)
@@ -680,15 +688,16 @@ __global__ __launch_bounds__(256) void moe_down_kernel(const uint16_t* __restric
   int item, nb;
   if (!xcd_item_schedule(*n_items, (d + kDownRows - 1) / kDownRows, &item, &nb)) return;
   const int2 it = items[item];
-  const int e = it.x, t0 = it.y;
-  const int ne = cnt[e], slot0 = poff[e] + t0;
+  const int e = it.x, t0 = it.y & 0xffff, t1 = it.y >> 16;
+  const int slot0 = poff[e] + t0;
   const int n0 = nb * kDownRows;
   const uint16_t* wd_e = wd + (size_t)e * d * F;
-  const int nt = min(8, (ne - t0 + 15) >> 4);
+  const int nt = min(8, (t1 - t0 + 15) >> 4);
+  const bool single = cnt[e] <= kMoeGroup2;
   // an expert with a single work item streams its weights (read by no other item)
 #define DOWN_TILE(NT)                                                                            \
-  (ne <= kMoeGroup2 ? down_tile<true, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring)  \
-                    : down_tile<false, NT>(wd_e, A, slot0, t0, ne, F, d, n0, lane, wv, Y, ring))
+  (single ? down_tile<true, NT>(wd_e, A, slot0, t0, t1, F, d, n0, lane, wv, Y, ring)            \
+          : down_tile<false, NT>(wd_e, A, slot0, t0, t1, F, d, n0, lane, wv, Y, ring))
   switch (nt) {
     case 1: DOWN_TILE(1); break;
     case 2: DOWN_TILE(2); break;

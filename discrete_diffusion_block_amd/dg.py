@@ -106,7 +106,7 @@ def lib():
             "dg_test_force_routing": [vp, vp],
             "dg_test_sample_eb_profiled": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, sz, vp],
             "dg_test_eb_select": [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp],
-            "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "dg_test_route": [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "dg_test_gemm": [vp, vp, vp, i32, i32, i32, vp],
             "dg_test_copy": [vp, vp, C.c_size_t, vp],
             "dg_test_mfma_rate": [i32, i32, vp, vp],
@@ -460,10 +460,12 @@ def dg_test_route(r: torch.Tensor, k: int, stream=None) -> dict:
            "perm": torch.empty(A + 15 * E, dtype=torch.int32, device=dev),
            "inv": torch.empty(A, dtype=torch.int32, device=dev),
            "items": torch.empty((A + 31) // 32 + E, 2, dtype=torch.int32, device=dev),
-           "n_items": torch.empty(1, dtype=torch.int32, device=dev)}
+           "n_items": torch.empty(1, dtype=torch.int32, device=dev),
+           "items2": torch.empty((A + 127) // 128 + E, 2, dtype=torch.int32, device=dev),
+           "n_items2": torch.empty(1, dtype=torch.int32, device=dev)}
     _check(lib().dg_test_route(_p(r), M, E, k, _p(out["ids"]), _p(out["w"]), _p(out["cnt"]),
                                _p(out["poff"]), _p(out["perm"]), _p(out["inv"]), _p(out["items"]),
-                               _p(out["n_items"]), _stream(stream)))
+                               _p(out["n_items"]), _p(out["items2"]), _p(out["n_items2"]), _stream(stream)))
     return out
 
 

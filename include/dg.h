@@ -461,10 +461,15 @@ dg_status dg_test_router_topk(const float* d_r, int M, int E, int k, int32_t* d_
  * padded slot offsets); perm int32 [M*k + 15E] (token of each padded slot, -1 on
  * padding); inv int32 [M*k] (slot of assignment m*k+j); items int32x2
  * [(M*k+63)/64 + E] -- (expert, first token) of every group of up to 64 of an
- * expert's tokens, experts ascending -- and n_items int32 [1]. */
+ * expert's tokens, experts ascending -- and n_items int32 [1]; items2 int32x2
+ * [(M*k+127)/128 + E] and n_items2 int32 [1] -- the expert GEMMs' work items: an
+ * expert with c tokens gets n = ceil(c/128) items, item i holding its 16-token
+ * blocks [floor(i*b/n), floor((i+1)*b/n)) of b = ceil(c/16), as (expert,
+ * t0 | t1 << 16) with [t0, t1) the item's tokens. */
 dg_status dg_test_route(const float* d_r, int M, int E, int k, int32_t* d_ids, float* d_w,
                         int32_t* d_cnt, int32_t* d_poff, int32_t* d_perm, int32_t* d_inv,
-                        int32_t* d_items, int32_t* d_n_items, void* stream);
+                        int32_t* d_items, int32_t* d_n_items, int32_t* d_items2, int32_t* d_n_items2,
+                        void* stream);
 
 /* Entropy-bounded selection alone on given fp32 entropies and argmax ids:
  * same rule and outputs as dg_sample_eb, with d_entropy and d_argmax as inputs

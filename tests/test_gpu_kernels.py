@@ -371,6 +371,16 @@ def test_routing_sort_bit_exact(M, E, k):
     items = out["items"].numpy()[:out["n_items"].item()]
     want = [(e, t0) for e in range(E) for t0 in range(0, cnt[e], dg.MOE_GROUP)]
     assert [tuple(x) for x in items] == want
+    # expert GEMM items: each expert's 16-token blocks dealt evenly into ceil(c / 128) items
+    want2 = []
+    for e in range(E):
+        n, b = -(-cnt[e] // 128), -(-cnt[e] // 16)
+        for i in range(n):
+            t0, t1 = 16 * (i * b // n), min(cnt[e], 16 * ((i + 1) * b // n))
+            assert 0 < t1 - t0 <= 128
+            want2.append((e, t0 | t1 << 16))
+    items2 = out["items2"].numpy()[:out["n_items2"].item()]
+    assert [tuple(x) for x in items2] == want2
 
 
 @pytest.mark.parametrize("tau", [0.5, 0.8])
