@@ -180,7 +180,7 @@ void launch_forced_route(const float* r, int M, int E, int k, const int32_t* for
 // at a time, writes slot = that slot + running rank, where the lanes holding one
 // expert find each other by ballots on the id's bits, which gives each assignment
 // its rank among them.  The ids are staged in LDS (sids) when at most CAP of them
-// come.
+// come (CAP > 0), else both walks read them from memory.
 template <int NW, int CAP>
 struct RouteLds {
   int base[256];
@@ -215,16 +215,18 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < NW * E; i += NT) L.wcnt[i / E][i % E] = 0;
   for (int i = tid; i < P; i += NT) perm[i] = -1;
-  const bool staged = A <= CAP;
-  if (staged) {
-    constexpr int U = (CAP + NT - 1) / NT;   // every load in flight at once
-    int v[U];
+  const bool staged = CAP > 0 && A <= CAP;
+  if constexpr (CAP > 0) {
+    if (staged) {
+      constexpr int U = (CAP + NT - 1) / NT;   // every load in flight at once
+      int v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (tid + u * NT < A) v[u] = ids[tid + u * NT];
+      for (int u = 0; u < U; ++u)
+        if (tid + u * NT < A) v[u] = ids[tid + u * NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (tid + u * NT < A) sids[tid + u * NT] = v[u];
+      for (int u = 0; u < U; ++u)
+        if (tid + u * NT < A) sids[tid + u * NT] = v[u];
+    }
   }
   __syncthreads();
   const int per = ((A + NW - 1) / NW + 63) & ~63;
@@ -327,13 +329,15 @@ __device__ void route_block(const int32_t* __restrict__ ids, int A, int k, int E
   }
 }
 
-// Ids staged in LDS: up to kRouteIdsSmall in a static array (a batch-1 canvas: 2048),
-// up to kRouteIds in dynamic LDS sized to the launch (batch 8 of 256-token canvases,
-// top-8: 64 KiB), beyond that read from memory.  The small kernel keeps the staging
-// loop short and holds little LDS on the CU it shares with the side stream's
-// shared-expert GEMM.
-constexpr int kRouteIdsSmall = 4096, kRouteIds = 16384;
+// Up to kRouteIdsSmall ids (a batch-1 canvas: 2048; a fused two-sequence pass: 4096)
+// are staged in a static LDS array; more are read from memory (L2) in both walks.
+// Larger passes run beside the side stream's wide-tile shared-expert GEMM, which
+// holds 128 KiB of LDS on its CUs: a sort workgroup that also staged its 16384 ids
+// (84 KiB in all) could start only on a CU with that much free and waited for one
+// (~47 us per launch at batch 8); at 20 KiB it starts at once.
+constexpr int kRouteIdsSmall = 4096;
 
+// CAP > 0: up to CAP ids staged in LDS; CAP == 0: ids read from memory
 template <int CAP>
 __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__ ids, int A, int k,
                                                      int E, int P, int32_t* __restrict__ cnt,
@@ -345,28 +349,22 @@ __global__ __launch_bounds__(1024) void route_kernel(const int32_t* __restrict__
                                                      int2* __restrict__ items2,
                                                      int32_t* __restrict__ n_items2,
                                                      int32_t* __restrict__ cnt_log) {
-  constexpr bool kStatic = CAP <= kRouteIdsSmall;
   __shared__ RouteLds<16, CAP> L;
-  __shared__ int st_ids[kStatic ? CAP : 1];
-  extern __shared__ int dyn_ids[];   // the large kernel: A ids when A <= CAP, else none
+  __shared__ int st_ids[CAP > 0 ? CAP : 1];
   route_block<16, CAP>(ids, A, k, E, P, cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log,
-                       L, kStatic ? st_ids : dyn_ids);
+                       L, st_ids);
 }
 
 void launch_route(const int32_t* ids, int M, int k, int E, int32_t* cnt, int32_t* poff,
                   int32_t* perm, int32_t* inv, int2* items, int32_t* n_items, int2* items2,
                   int32_t* n_items2, int32_t* cnt_log, hipStream_t s) {
   const int A = M * k, P = moe_max_slots(M, k, E);
-  if (A <= kRouteIdsSmall) {
+  if (A <= kRouteIdsSmall)
     launch_kernel(route_kernel<kRouteIdsSmall>, dim3(1), dim3(1024), 0, s, nullptr, ids, A, k, E, P, cnt, poff,
                   perm, inv, items, n_items, items2, n_items2, cnt_log);
-    return;
-  }
-  static LdsLimit limit;   // static part + up to 64 KiB of staged ids exceeds the default limit
-  raise_lds_limit(limit, reinterpret_cast<const void*>(&route_kernel<kRouteIds>), kRouteIds * 4);
-  const int staged = A <= kRouteIds ? A : 0;
-  launch_kernel(route_kernel<kRouteIds>, dim3(1), dim3(1024), (size_t)staged * 4, s, nullptr, ids, A, k, E, P,
-                cnt, poff, perm, inv, items, n_items, items2, n_items2, cnt_log);
+  else
+    launch_kernel(route_kernel<0>, dim3(1), dim3(1024), 0, s, nullptr, ids, A, k, E, P, cnt, poff, perm, inv,
+                  items, n_items, items2, n_items2, cnt_log);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs

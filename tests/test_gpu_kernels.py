@@ -339,7 +339,7 @@ def test_sampler_ragged_vocab_and_cross_chunk_ties():
 
 @pytest.mark.parametrize("M,E,k", [(256, 128, 8), (512, 128, 8), (33, 8, 2), (1000, 16, 3), (7, 4, 4),
                                    (4096, 256, 16), (300, 100, 5), (257, 128, 16),
-                                   (2048, 128, 8), (1100, 128, 16)])   # ids: up to 4096 staged in static LDS; 4112, 16384 in dynamic LDS; 17600, 65536 read from memory
+                                   (2048, 128, 8), (1100, 128, 16)])   # ids: up to 4096 staged in LDS; 4112, 16384, 17600, 65536 read from memory
 def test_routing_sort_bit_exact(M, E, k):
     """Top-k ids bit-exact vs the oracle (ties, signed zeros, -inf and NaN rows among
     them); the counting sort is a stable, padded grouping."""
