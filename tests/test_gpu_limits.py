@@ -1,0 +1,77 @@
+"""The boundary's stated limits, each on a narrow model the oracle finishes quickly: a
+canvas of 1024 (the largest), a batch of DG_MAX_BATCH = 64 sequences, and 256 experts with
+top-16 routing and head dim 64.  Each case prefills its prompts and runs one
+teacher-forced denoising step against the oracle (routing forced to the oracle's expert
+ids, as in the other model tests): logits within 3e-2, and the entropy-bounded selection
+the engine makes on its own logits equal to the oracle's selection on the same logits."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from discrete_diffusion_block_amd import dg, synth
+from oracle import dg_oracle as O
+from gpu_util import forced_ids, forced_routing, require_gpu, to_np_bf16
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 3e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+CASES = {
+    "canvas 1024": (dict(canvas=1024), 1, 64),
+    "batch 64": (dict(canvas=32), 64, 16),
+    "256 experts top-16, head dim 64": (dict(n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=256, top_k=16,
+                                             expert_ffn=64, shared_ffn=64), 1, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_limits_teacher_forced_step(name):
+    over, batch, prompt_len = CASES[name]
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], **over)
+    C, V = cfg.canvas, cfg.vocab
+    print(f"limits: {name} (batch {batch}, canvas {C}, {cfg.n_experts} experts top-{cfg.top_k}, "
+          f"head dim {cfg.head_dim})", flush=True)
+    w_cpu = synth.make_weights(cfg)
+    w_np = O.to_numpy_weights(w_cpu)
+    w_gpu = {"embed": w_cpu["embed"].cuda(), "final_norm": w_cpu["final_norm"].cuda(),
+             "layers": [{k: v.cuda() for k, v in lw.items()} for lw in w_cpu["layers"]]}
+    g = torch.Generator().manual_seed(len(name))
+    prompt = torch.randint(0, V, (batch, prompt_len), generator=g, dtype=torch.int32)
+    max_ctx = ((prompt_len + C) + 63) // 64 * 64
+    eng = dg.Engine(cfg, w_gpu, max_batch=batch, max_ctx=max_ctx)
+    kv = O.KVCache(cfg, batch)
+    tr = [[] for _ in range(batch)]
+    O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
+    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+        eng.prefill_kv(prompt.cuda())
+    canvas = torch.full((batch, C), cfg.mask_id, dtype=torch.int32)
+    keep = torch.rand(batch, C, generator=g) < 0.3                 # some committed tokens
+    canvas[keep] = torch.randint(0, V, (int(keep.sum()),), generator=g, dtype=torch.int32)
+    tr = [[] for _ in range(batch)]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), 0.7, trace=tr)
+    logits = torch.empty(batch, C, V, dtype=torch.bfloat16, device="cuda")
+    d_canvas = canvas.cuda()
+    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+        eng.denoise_step(d_canvas, 0.7, logits)
+    torch.cuda.synchronize()
+    lg = to_np_bf16(logits)
+    masked = canvas.numpy() == cfg.mask_id
+    err = np.abs(lg - ref)[masked].max()
+    print(f"  max |logit delta| on [MASK] rows {err:.2e}", flush=True)
+    assert err <= LOGIT_TOL, err
+    # the selection on the engine's own logits equals the oracle's on the same logits
+    nm = torch.empty(batch, dtype=torch.int32, device="cuda")
+    eng.sample_eb(logits, d_canvas, 2.0, False, nm)
+    torch.cuda.synchronize()
+    want = O.sample_eb(lg, canvas.numpy(), 2.0, False, cfg.mask_id)
+    np.testing.assert_array_equal(d_canvas.cpu().numpy(), want[0])
+    np.testing.assert_array_equal(nm.cpu().numpy(), want[3])
+    eng.close()
