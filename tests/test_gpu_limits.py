@@ -1,6 +1,7 @@
 """The boundary's stated limits, each on a narrow model the oracle finishes quickly: a
-canvas of 1024 (the largest), a batch of DG_MAX_BATCH = 64 sequences, and 256 experts with
-top-16 routing and head dim 64.  Each case prefills its prompts and runs one
+canvas of 1024 (the largest), a batch of DG_MAX_BATCH = 64 sequences, 256 experts with
+top-16 routing and head dim 64, and a sequence with an empty prefix beside one with a
+prompt.  Each case prefills its prompts and runs one
 teacher-forced denoising step against the oracle (routing forced to the oracle's expert
 ids, as in the other model tests): logits within 3e-2, and the entropy-bounded selection
 the engine makes on its own logits equal to the oracle's selection on the same logits."""
@@ -74,4 +75,48 @@ def test_limits_teacher_forced_step(name):
     want = O.sample_eb(lg, canvas.numpy(), 2.0, False, cfg.mask_id)
     np.testing.assert_array_equal(d_canvas.cpu().numpy(), want[0])
     np.testing.assert_array_equal(nm.cpu().numpy(), want[3])
+    eng.close()
+
+
+def test_empty_prefix_beside_a_prompt():
+    """A sequence with nothing cached (length 0: its canvas attends to itself only) in one
+    pass with a sequence holding a 40-token prompt."""
+    cfg = synth.CONFIGS["tiny"]
+    C, V = cfg.canvas, cfg.vocab
+    print("limits: empty prefix beside a 40-token prompt (batch 2)", flush=True)
+    w_cpu = synth.make_weights(cfg)
+    w_np = O.to_numpy_weights(w_cpu)
+    w_gpu = {"embed": w_cpu["embed"].cuda(), "final_norm": w_cpu["final_norm"].cuda(),
+             "layers": [{k: v.cuda() for k, v in lw.items()} for lw in w_cpu["layers"]]}
+    prompt = synth.make_prompt(cfg, 2, 40)
+    eng = dg.Engine(cfg, w_gpu, max_batch=2, max_ctx=128)
+    kvp = O.KVCache(cfg, 2)
+    tr = [[], []]
+    O.prefill_kv(cfg, w_np, kvp, prompt.numpy(), trace=tr)
+    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+        eng.prefill_kv(prompt.cuda())
+    eng.kv.len[0] = 0                              # sequence 0: nothing cached
+    kv = O.KVCache(cfg, 2)
+    for l in range(cfg.n_layers):
+        kv.k[l] = [kvp.k[l][0][:0], kvp.k[l][1]]
+        kv.v[l] = [kvp.v[l][0][:0], kvp.v[l][1]]
+    kv.len = [0, 40]
+    canvas = torch.full((2, C), cfg.mask_id, dtype=torch.int32)
+    canvas[1, 5] = 11
+    tr = [[], []]
+    ref = O.denoise_step(cfg, w_np, kv, canvas.numpy(), 0.8, trace=tr)
+    logits = torch.empty(2, C, V, dtype=torch.bfloat16, device="cuda")
+    d_canvas = canvas.cuda()
+    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+        eng.denoise_step(d_canvas, 0.8, logits)
+    torch.cuda.synchronize()
+    lg = to_np_bf16(logits)
+    err = np.abs(lg - ref)[canvas.numpy() == cfg.mask_id].max()
+    print(f"  max |logit delta| on [MASK] rows {err:.2e}", flush=True)
+    assert err <= LOGIT_TOL, err
+    nm = torch.empty(2, dtype=torch.int32, device="cuda")
+    eng.sample_eb(logits, d_canvas, 1.0, False, nm)
+    torch.cuda.synchronize()
+    want = O.sample_eb(lg, canvas.numpy(), 1.0, False, cfg.mask_id)
+    np.testing.assert_array_equal(d_canvas.cpu().numpy(), want[0])
     eng.close()
