@@ -13,7 +13,10 @@
 // ranges).  Keys stream through LDS in 64-key stages (K and transposed V, copied
 // straight from the cache's fragment tiles into a RING-stage ring by direct
 // global->LDS loads, one copy per workgroup) and every wave reads each stage: one
-// K/V byte from L2 feeds 32 * NWV query rows.  When the pairs alone give too few workgroups to
+// K/V byte from L2 feeds 32 * NWV query rows.  Over long key ranges the loop is
+// pipelined: each iteration issues the next stage's score MFMAs before this stage's
+// softmax, so the matrix cores work while the VALU computes the exponentials (the same
+// arithmetic in the same order, so the same results).  When the pairs alone give too few workgroups to
 // fill the chip, the key range of each pair is split over several workgroups
 // (split-KV); each writes its unnormalised partial (max, sum, output) and a merge
 // kernel combines the splits in a fixed order.
@@ -49,7 +52,7 @@ struct AttnArgs {
 
 constexpr int kAttnStageKeys = 64;
 
-template <int HD, int NWV, int RING>
+template <int HD, int NWV, int RING, bool PIPE = false>
 __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a) {
   constexpr int NC = HD / 32;                 // k-steps of the score MFMA
   constexpr int NB = HD / 16;                 // 16-row output blocks of hd
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a
   constexpr int STAGE = 2 * (KCH + VCH);      // one 64-key stage: K chunk 0, K chunk 1, V chunk 0, V chunk 1
   constexpr int COPIES = STAGE / 1024 / NWV;  // 1 KiB copies per wave per stage
   static_assert(STAGE % (1024 * NWV) == 0, "whole copies per wave");
-  static_assert(RING == 2 || RING == 3, "stages in the ring");
+  static_assert(RING == 2 || RING == 3 || (PIPE && RING == 4), "stages in the ring");
   extern __shared__ __attribute__((aligned(1024))) char ring[];   // [RING][STAGE]
 
   const int lane = threadIdx.x & 63;
@@ -159,26 +162,13 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a
   const float scale = 1.4426950408889634f / sqrtf((float)HD);   // softmax in log2 units
   lds_char* const lr = lds_launder(ring);
 
-  // RING - 1 stages in flight: stage st is copied RING - 1 iterations ahead of its use.
-  // At the top of iteration st the wave's later copies are those of the stages after
-  // st already issued (at most RING - 2 of them); waiting until only they remain lands
-  // stage st, and the barrier makes every wave's copies visible and retires all reads
-  // of the slot refilled next (stage st - 1's).
-#pragma unroll
-  for (int j = 0; j < RING - 1; ++j)
-    if (s_begin + j < s_end) issue(s_begin + j, j);
-  for (int st = s_begin; st < s_end; ++st) {
-    const int slot = (st - s_begin) % RING;
-    if (RING == 3 && st + 1 < s_end) vm_wait<COPIES>();
-    else vm_wait<0>();
-    __builtin_amdgcn_s_barrier();
-    if (st + RING - 1 < s_end) issue(st + RING - 1, (st + RING - 1 - s_begin) % RING);
-    if (!active) continue;
-    const lds_char* sk = lr + slot * STAGE + lane * 16;
-    const lds_char* sv = sk + 2 * KCH;
-    const int kc0 = st * kAttnStageKeys;
+  // one stage's scores S^T = K . Q^T of both 32-key chunks for both query blocks
+  // (s[qb][chunk][bb]), then its online softmax and the P.V product; the two steps are
+  // separate so that the pipelined loop can issue the next stage's score MFMAs before
+  // this stage's softmax (the matrix cores work while the VALU runs the softmax)
+  auto scores = [&](int st, f32x4 (&s)[2][2][2]) {
+    const lds_char* sk = lr + ((st - s_begin) % RING) * STAGE + lane * 16;
     // scores of both 32-key chunks for both query blocks: s[qb][chunk][bb]
-    f32x4 s[2][2][2];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
@@ -194,6 +184,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a
           s[qb][ch][bb] = t;
         }
       }
+  };
+  auto softmax_pv = [&](int st, f32x4 (&s)[2][2][2]) {
+    const lds_char* sv = lr + ((st - s_begin) % RING) * STAGE + lane * 16 + 2 * KCH;
+    const int kc0 = st * kAttnStageKeys;
     // lane holds keys kc0 + 32 ch + 8 gq + e (e = 0..7: bb = e / 4, row e % 4) for query r
     const bool nomask = den ? (kc0 >= lo_t && kc0 + kAttnStageKeys <= hi_t)
                                   : (kc0 + kAttnStageKeys - 1 <= p_first &&
@@ -263,6 +257,54 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attention_kernel(AttnArgs a
           acc[qb][hb] = mfma16(vf, pl[qb][ch], acc[qb][hb]);
         }
       }
+    }
+  };
+
+  if constexpr (!PIPE) {
+    // RING - 1 stages in flight: stage st is copied RING - 1 iterations ahead of its use.
+    // At the top of iteration st the wave's later copies are those of the stages after
+    // st already issued (at most RING - 2 of them); waiting until only they remain lands
+    // stage st, and the barrier makes every wave's copies visible and retires all reads
+    // of the slot refilled next (stage st - 1's).
+#pragma unroll
+    for (int j = 0; j < RING - 1; ++j)
+      if (s_begin + j < s_end) issue(s_begin + j, j);
+    for (int st = s_begin; st < s_end; ++st) {
+      if (RING == 3 && st + 1 < s_end) vm_wait<COPIES>();
+      else vm_wait<0>();
+      __builtin_amdgcn_s_barrier();
+      if (st + RING - 1 < s_end) issue(st + RING - 1, (st + RING - 1 - s_begin) % RING);
+      if (!active) continue;
+      f32x4 sc[2][2][2];
+      scores(st, sc);
+      softmax_pv(st, sc);
+    }
+  } else {
+    // Pipelined: iteration st computes stage st + 1's scores, then stage st's softmax and
+    // P.V.  Four slots: stage st + 3 is copied in iteration st into the slot of stage
+    // st - 1, whose K (scores in iteration st - 2) and V (iteration st - 1) every wave has
+    // finished with at the barrier.  At the top of iteration st stage st + 1 must have
+    // landed: the only later copies are stage st + 2's (issued in iteration st - 1).
+    static_assert(RING == 4, "the pipelined loop keeps two stages ahead in four slots");
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (s_begin + j < s_end) issue(s_begin + j, j);
+    if (s_begin + 2 < s_end) vm_wait<2 * COPIES>();
+    else if (s_begin + 1 < s_end) vm_wait<COPIES>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    f32x4 sa[2][2][2], sb[2][2][2];
+    if (active && s_begin < s_end) scores(s_begin, sa);
+    for (int st = s_begin; st < s_end; ++st) {
+      if (st + 2 < s_end) vm_wait<COPIES>();
+      else vm_wait<0>();
+      __builtin_amdgcn_s_barrier();
+      if (st + 3 < s_end) issue(st + 3, (st + 3 - s_begin) % RING);
+      if (!active) continue;
+      if (st + 1 < s_end) scores(st + 1, sb);
+      softmax_pv(st, sa);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) (&sa[0][0][0])[i] = (&sb[0][0][0])[i];
     }
   }
   if (!active) return;
@@ -357,12 +399,12 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const float* __res
   *reinterpret_cast<u32x4*>(o + fm_index(m, head * HD + c8, hq * HD)) = out;
 }
 
-template <int HD, int NWV, int RING>
+template <int HD, int NWV, int RING, bool PIPE = false>
 static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, int max_keys,
                           uint16_t* o, float* part_o, float2* part_ml, hipStream_t s) {
   constexpr int STAGE = 2 * (2 * (HD / 32) * 1024 + (HD / 16) * 1024);
   static LdsLimit limit;
-  raise_lds_limit(limit, reinterpret_cast<const void*>(&attention_kernel<HD, NWV, RING>), RING * STAGE);
+  raise_lds_limit(limit, reinterpret_cast<const void*>(&attention_kernel<HD, NWV, RING, PIPE>), RING * STAGE);
   AttnArgs a{};
   a.q = q; a.o = o; a.part_o = part_o; a.part_ml = part_ml;
   a.kv = kv; a.g = g; a.hq = hq;
@@ -382,7 +424,7 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
   a.nsplit = max(1, nsplit);
   const long units = (long)base_wgs * a.nsplit;
   const int blocks = (int)(kXcd * ((units + kXcd - 1) / kXcd));
-  launch_kernel(attention_kernel<HD, NWV, RING>, dim3(blocks), dim3(64 * NWV), RING * STAGE, s, nullptr, a);
+  launch_kernel(attention_kernel<HD, NWV, RING, PIPE>, dim3(blocks), dim3(64 * NWV), RING * STAGE, s, nullptr, a);
   if (a.nsplit > 1) {
     const long threads = (long)g.batch * hq * g.n * (HD / 8);
     launch_kernel(attention_merge_kernel<HD>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, nullptr,
@@ -391,9 +433,10 @@ static void run_attention(const uint16_t* q, int hq, const KvLayer& kv, const Pa
 }
 
 // Long key ranges (global layers over a long prefix) take their own workgroup shape:
-// 8 waves share each K/V stage (half the copies per query) and the ring holds three
-// stages, so each copy is issued two stages ahead of its use.
-constexpr int kAttnLongKeys = 4096, kAttnWavesLong = 8, kAttnRingLong = 3;
+// 8 waves share each K/V stage (half the copies per query), and the pipelined loop
+// issues the next stage's score MFMAs before this stage's softmax, with four ring slots
+// so that each copy still goes out two stages ahead of its use.
+constexpr int kAttnLongKeys = 4096, kAttnWavesLong = 8, kAttnRingLong = 4;
 
 void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGeom& g, uint16_t* o,
                       float* part_o, float2* part_ml, hipStream_t s) {
@@ -407,15 +450,15 @@ void launch_attention(const uint16_t* q, int hq, const KvLayer& kv, const PassGe
   const bool lng = max_keys >= kAttnLongKeys;
   switch (kv.hd) {
     case 32:
-      if (lng) run_attention<32, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      if (lng) run_attention<32, NWL, RL, true>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       else run_attention<32, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       break;
     case 64:
-      if (lng) run_attention<64, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      if (lng) run_attention<64, NWL, RL, true>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       else run_attention<64, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       break;
     default:
-      if (lng) run_attention<128, NWL, RL>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
+      if (lng) run_attention<128, NWL, RL, true>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       else run_attention<128, 4, 2>(q, hq, kv, g, max_keys, o, part_o, part_ml, s);
       break;
   }

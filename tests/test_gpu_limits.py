@@ -1,8 +1,8 @@
 """The boundary's stated limits, each on a narrow model the oracle finishes quickly: a
 canvas of 1024 (the largest), a batch of DG_MAX_BATCH = 64 sequences, 256 experts with
-top-16 routing and head dim 64, and a sequence with an empty prefix beside one with a
-prompt.  Each case prefills its prompts and runs one
-teacher-forced denoising step against the oracle (routing forced to the oracle's expert
+top-16 routing and head dim 64, head dim 64 on the long-key attention shape, and a
+sequence with an empty prefix beside one with a prompt.  Each case prefills its prompts
+and runs one teacher-forced denoising step against the oracle (routing forced to the oracle's expert
 ids, as in the other model tests): logits within 3e-2, and the entropy-bounded selection
 the engine makes on its own logits equal to the oracle's selection on the same logits."""
 import dataclasses
@@ -30,7 +30,11 @@ CASES = {
     "batch 64": (dict(canvas=32), 64, 16),
     "256 experts top-16, head dim 64": (dict(n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=256, top_k=16,
                                              expert_ffn=64, shared_ffn=64), 1, 64),
+    # the long-key attention shape (over 4096 keys on the global layer) at head dim 64
+    "head dim 64, global layer over 4200 keys": (dict(n_q_heads=4, n_kv_heads=2, head_dim=64, window=24,
+                                                      global_every=2), 1, 4200),
 }
+PREFILL_PASS = 512   # the library's prefill pass length: forced ids are indexed per pass
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -51,8 +55,15 @@ def test_limits_teacher_forced_step(name):
     kv = O.KVCache(cfg, batch)
     tr = [[] for _ in range(batch)]
     O.prefill_kv(cfg, w_np, kv, prompt.numpy(), trace=tr)
-    with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
-        eng.prefill_kv(prompt.cuda())
+    if prompt_len <= PREFILL_PASS:
+        with forced_routing(eng, forced_ids(tr, cfg.n_layers)):
+            eng.prefill_kv(prompt.cuda())
+    else:                                          # one call per pass, each forced with its own rows
+        assert batch == 1
+        for s0 in range(0, prompt_len, PREFILL_PASS):
+            s1 = min(prompt_len, s0 + PREFILL_PASS)
+            with forced_routing(eng, forced_ids(tr, cfg.n_layers, s0, s1)):
+                eng.prefill_kv(prompt[:, s0:s1].contiguous().cuda())
     canvas = torch.full((batch, C), cfg.mask_id, dtype=torch.int32)
     keep = torch.rand(batch, C, generator=g) < 0.3                 # some committed tokens
     canvas[keep] = torch.randint(0, V, (int(keep.sum()),), generator=g, dtype=torch.int32)

@@ -284,7 +284,7 @@ def test_long_prefix_global_layer(tiny):
     """A 4200-token prompt with layer 1 global (layer 0: a 24-token window): the later
     prefill chunks (causal) and the denoising pass attend over more than 4096 keys on
     the global layer, which takes the long-range attention shape (8 waves sharing each
-    K/V stage, a three-stage ring).  K/V after prefill and the logits of one denoising
+    K/V stage, the pipelined four-slot ring).  K/V after prefill and the logits of one denoising
     step against the oracle."""
     cfg0, w_np, w_gpu, _ = tiny
     cfg = dataclasses.replace(cfg0, window=24, global_every=2)
